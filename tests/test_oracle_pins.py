@@ -1,0 +1,489 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Each test checks the oracle against something other than itself: counts the
+pages print, closed forms, special cases that reduce to a textbook model,
+library routines, or brute force written out with plain loops.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import model as M
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# Schedule: 56 executions from 32 stored layers
+# --------------------------------------------------------------------------
+
+def _golden_schedule():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "schedule_9b.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        e, i, p, k = line.split()
+        rows.append((int(i), int(p), k))
+    return rows
+
+
+def test_schedule_9b_matches_pages():
+    cfg = M.nine_b_config()
+    s = M.schedule(cfg)
+    gold = _golden_schedule()
+    assert len(s) == 56 == len(gold)
+    assert [(i, p) for i, p, _ in gold] == s
+    kinds = ["F" if M.layer_is_full(cfg, i) else "L" for i, _ in s]
+    assert kinds == [k for _, _, k in gold]
+    assert kinds.count("F") == 14 and kinds.count("L") == 42
+    # 4 + 24 + 24 + 4
+    assert sum(1 for i, _ in s if i < 4) == 4
+    assert sum(1 for i, p in s if 4 <= i < 28 and p == 0) == 24
+    assert sum(1 for i, p in s if 4 <= i < 28 and p == 1) == 24
+    assert sum(1 for i, _ in s if i >= 28) == 4
+    assert len({i for i, _ in s}) == 32
+
+
+def test_schedule_tiny():
+    cfg = M.tiny_config()
+    s = M.schedule(cfg)
+    assert len(s) == 12
+    assert s == [(0, 0), (1, 0), (2, 0), (3, 0), (4, 0), (5, 0), (2, 1), (3, 1), (4, 1), (5, 1), (6, 0), (7, 0)]
+    assert sum(M.layer_is_full(cfg, i) for i, _ in s) == 3
+
+
+def test_oracle_counts_its_layer_calls():
+    cfg = M.tiny_config()
+    W = M.make_weights(cfg, 0)
+    toks = synth.uniform_int(1, synth.TID_TOKENS, (1, 16), cfg.vocab)
+    st = M.State()
+    M.forward(cfg, W, toks, state=st)
+    att = [c for c in st.calls if c[2] != "ffn"]
+    assert len(att) == 12 and len([c for c in st.calls if c[2] == "ffn"]) == 12
+    assert sum(1 for c in att if c[2] == "full") == 3
+    assert [(c[0], c[1]) for c in att] == M.schedule(cfg)
+    # one cache per (layer, pass): 3 KV slots and 9 linear states
+    assert len(st.kv) == 3 and len(st.lin) == 9
+
+
+# --------------------------------------------------------------------------
+# Looping: B(B(h)) equals the unrolled network with duplicated weights
+# --------------------------------------------------------------------------
+
+def _unrolled_weights(cfg_loop, W, cfg_un):
+    layers = []
+    L0, L1 = cfg_loop.loop_start, cfg_loop.loop_end
+    span = L1 - L0
+    for j in range(cfg_un.n_layers):
+        if j < L0:
+            src = j
+        elif j < L0 + cfg_loop.n_passes * span:
+            src = L0 + (j - L0) % span
+        else:
+            src = j - (cfg_loop.n_passes - 1) * span
+        layers.append(W.layer(src))
+    return M.Weights(cfg_un, layers, embed=W.embed, head=W.head)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_looped_equals_unrolled(dtype):
+    cfg = M.tiny_config(dtype=dtype)
+    W = M.make_weights(cfg, 0)
+    cfg_un = M.tiny_config(dtype=dtype, n_layers=12, loop_start=2, loop_end=10, n_passes=1)
+    Wu = _unrolled_weights(cfg, W, cfg_un)
+    toks = synth.uniform_int(1, synth.TID_TOKENS, (2, 24), cfg.vocab)
+    st_a, st_b = M.State(), M.State()
+    a = M.forward(cfg, W, toks[:, :20], state=st_a, all_logits=True)
+    b = M.forward(cfg_un, Wu, toks[:, :20], state=st_b, all_logits=True)
+    assert np.array_equal(a, b)
+    # per-pass caches: continuing both gives the same decode rows
+    for t in range(20, 24):
+        da = M.forward(cfg, W, toks[:, t:t + 1], state=st_a)
+        db = M.forward(cfg_un, Wu, toks[:, t:t + 1], state=st_b)
+        assert np.array_equal(da, db)
+
+
+def test_shared_cache_across_passes_would_differ():
+    """One cache per (layer, pass) is forced (A13): sharing a KV cache between
+    the passes changes the decode result, so the looped model is not B(B(h))."""
+    cfg = M.tiny_config()
+    W = M.make_weights(cfg, 0)
+    toks = synth.uniform_int(1, synth.TID_TOKENS, (1, 9), cfg.vocab)
+    ref = M.forward(cfg, W, toks, all_logits=True)[:, -1]
+
+    st = M.State()
+    M.forward(cfg, W, toks[:, :8], state=st)
+    # merge: make pass 1 use pass 0's cache (the wrong reading)
+    for (layer, p) in list(st.kv):
+        if p == 1:
+            st.kv[(layer, 1)] = st.kv[(layer, 0)]
+    bad = M.forward(cfg, W, toks[:, 8:], state=st)
+    assert M.max_row_rel_err(bad, ref) > 1e-6
+
+
+# --------------------------------------------------------------------------
+# Sinkhorn
+# --------------------------------------------------------------------------
+
+def test_sinkhorn_columns_exact_and_equal_logits():
+    rng = np.random.default_rng(0)
+    A = np.exp(rng.normal(size=(1000, 2, 2)) * 2)
+    for k in (1, 5, 20):
+        S = M.sinkhorn(A, k)
+        assert np.abs(S.sum(axis=-2) - 1).max() < 1e-14
+    S = M.sinkhorn(np.ones((2, 2)) * 7.3, 20)
+    assert np.array_equal(S, np.full((2, 2), 0.5))
+
+
+def test_sinkhorn_closed_form_limit():
+    """A positive 2x2 matrix [[a, b], [c, d]] scales to the doubly stochastic
+    [[p, 1-p], [1-p, p]] with the same cross-ratio, p = sqrt(ad)/(sqrt(ad)+sqrt(bc))."""
+    rng = np.random.default_rng(1)
+    for _ in range(50):
+        A = np.exp(rng.normal(size=(2, 2)) * 1.5)
+        a, b, c, d = A.ravel()
+        p = math.sqrt(a * d) / (math.sqrt(a * d) + math.sqrt(b * c))
+        S = M.sinkhorn(A, 400)
+        assert np.abs(S - np.array([[p, 1 - p], [1 - p, p]])).max() < 1e-5
+
+
+def test_sinkhorn_contraction_rate():
+    """Row-sum error contracts by tanh^2(|ln theta| / 4) per iteration, theta
+    the cross-ratio ad/(bc) (Birkhoff-Hopf rate for 2x2)."""
+    rng = np.random.default_rng(2)
+    for s in (0.8, 1.5, 2.5):
+        A = np.exp(rng.normal(size=(2, 2)) * s)
+        a, b, c, d = A.ravel()
+        rate = math.tanh(abs(math.log(a * d / (b * c))) / 4) ** 2
+        if rate < 0.05:
+            continue
+        errs = [np.abs(M.sinkhorn(A, k).sum(-1) - 1).max() for k in range(1, 41)]
+        ks = [k for k in range(len(errs) - 1) if errs[k + 1] > 1e-13]
+        k = ks[-1]
+        assert abs(errs[k + 1] / errs[k] - rate) < 2e-3 * max(rate, 1e-3) + 1e-6
+        assert all(errs[j + 1] <= errs[j] * rate * (1 + 1e-6) for j in range(len(errs) - 1) if errs[j + 1] > 1e-9)
+
+
+def test_sinkhorn_20_within_1e3_on_tiny_maps():
+    """The 1e-3 doubly-stochastic check holds for every map of the tiny model."""
+    cfg = M.tiny_config()
+    W = M.make_weights(cfg, 0)
+    rng = np.random.default_rng(3)
+    for layer in range(cfg.loop_start, cfg.loop_end):
+        L = W.layer(layer)
+        for s in (0, 1):
+            X = rng.normal(size=(512, 2, cfg.hidden))
+            _, _, res, _ = M.mhc_maps(X, L.mhc_w[s], L.mhc_b[s], 20, cfg.rms_eps)
+            assert np.abs(res.sum(-1) - 1).max() < 1e-3
+            assert np.abs(res.sum(-2) - 1).max() < 1e-12
+
+
+# --------------------------------------------------------------------------
+# mHC
+# --------------------------------------------------------------------------
+
+def test_mhc_maps_against_loops():
+    rng = np.random.default_rng(4)
+    C = 8
+    X = rng.normal(size=(3, 2, C))
+    w = rng.normal(size=(8, 2 * C)) * 0.3
+    b = rng.normal(size=8) * 0.3
+    pre, post, res, logits = M.mhc_maps(X, w, b, 20, 1e-6)
+    for t in range(3):
+        v = [X[t, 0, c] for c in range(C)] + [X[t, 1, c] for c in range(C)]
+        ms = sum(x * x for x in v) / len(v)
+        r = math.sqrt(ms + 1e-6)
+        l = [sum(w[j, i] * v[i] / r for i in range(2 * C)) + b[j] for j in range(8)]
+        assert np.allclose(logits[t], l, rtol=1e-12, atol=1e-12)
+        assert np.allclose(pre[t], [1 / (1 + math.exp(-l[0])), 1 / (1 + math.exp(-l[1]))])
+        assert np.allclose(post[t], [2 / (1 + math.exp(-l[2])), 2 / (1 + math.exp(-l[3]))])
+        m = max(l[4:8])
+        A = [[math.exp(l[4] - m), math.exp(l[5] - m)], [math.exp(l[6] - m), math.exp(l[7] - m)]]
+        for _ in range(20):
+            A = [[A[i][j] / (A[i][0] + A[i][1]) for j in range(2)] for i in range(2)]
+            A = [[A[i][j] / (A[0][j] + A[1][j]) for j in range(2)] for i in range(2)]
+        assert np.allclose(res[t], A, rtol=1e-12, atol=1e-14)
+
+
+def _identity_mhc(W, cfg):
+    for layer in range(cfg.loop_start, cfg.loop_end):
+        L = W.layer(layer)
+        L.mhc_w = [np.zeros_like(L.mhc_w[0]), np.zeros_like(L.mhc_w[1])]
+        bias = np.array([0, 0, 0, 0, 30, -30, -30, 30], np.float64)
+        L.mhc_b = [bias.copy(), bias.copy()]
+
+
+def test_mhc_identity_reduces_to_plain_transformer():
+    """W = 0, b = (0,0,0,0,+30,-30,-30,+30) gives H_pre = (1/2, 1/2),
+    H_post = (1, 1), H_res = I (to e^-60): the looped model is then exactly the
+    plain pre-norm residual transformer of its 12 executions, which the oracle
+    computes on its separate plain path."""
+    cfg = M.tiny_config()
+    W = M.make_weights(cfg, 0)
+    _identity_mhc(W, cfg)
+    cfg_plain = M.tiny_config(n_layers=12, loop_start=0, loop_end=0, n_passes=1)
+    Wp = _unrolled_weights(cfg, W, M.tiny_config(n_layers=12, loop_start=2, loop_end=10, n_passes=1))
+    Wp = M.Weights(cfg_plain, [Wp.layer(j) for j in range(12)], embed=W.embed, head=W.head)
+    toks = synth.uniform_int(1, synth.TID_TOKENS, (1, 32), cfg.vocab)
+    a = M.forward(cfg, W, toks, all_logits=True)
+    b = M.forward(cfg_plain, Wp, toks, all_logits=True)
+    assert M.max_row_rel_err(a, b) < 1e-12
+
+
+def test_mhc_site_textbook_mix():
+    """With constant maps the write-back is the 2x2 mix of the streams plus the
+    scaled output; checked element by element."""
+    cfg = M.tiny_config(hidden=4)
+    rng = np.random.default_rng(5)
+    X = rng.normal(size=(1, 1, 2, 4))
+    w = np.zeros((8, 8))
+    b = np.array([0.3, -0.2, 0.1, 0.5, 1.0, -1.0, 0.2, 0.4])
+    gamma = np.ones(4)
+    ys = []
+
+    def f(u):
+        ys.append(u.copy())
+        return 2.0 * u
+    out = M.mhc_site(cfg, X, w, b, gamma, f)
+    p0, p1 = 1 / (1 + math.exp(-0.3)), 1 / (1 + math.exp(0.2))
+    q0, q1 = 2 / (1 + math.exp(-0.1)), 2 / (1 + math.exp(-0.5))
+    _, _, res, _ = M.mhc_maps(X, w, b, 20, cfg.rms_eps)
+    x_in = [p0 * X[0, 0, 0, c] + p1 * X[0, 0, 1, c] for c in range(4)]
+    r = math.sqrt(sum(v * v for v in x_in) / 4 + cfg.rms_eps)
+    u = [v / r for v in x_in]
+    assert np.allclose(ys[0][0, 0], u)
+    for i in range(2):
+        for c in range(4):
+            want = res[0, 0, i, 0] * X[0, 0, 0, c] + res[0, 0, i, 1] * X[0, 0, 1, c] + (q0, q1)[i] * 2 * u[c]
+            assert abs(out[0, 0, i, c] - want) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Full attention
+# --------------------------------------------------------------------------
+
+def _attn_brute(q, k, v, pos0):
+    B, T, Hq, d = q.shape
+    S, Hkv = k.shape[1], k.shape[2]
+    out = np.zeros_like(q, dtype=np.float64)
+    for b in range(B):
+        for t in range(T):
+            for j in range(Hq):
+                kv = j // (Hq // Hkv)
+                sc = []
+                for tau in range(pos0 + t + 1):
+                    sc.append(sum(q[b, t, j, i] * k[b, tau, kv, i] for i in range(d)) / math.sqrt(d))
+                m = max(sc)
+                e = [math.exp(s - m) for s in sc]
+                Z = sum(e)
+                for i in range(d):
+                    out[b, t, j, i] = sum(e[tau] * v[b, tau, kv, i] for tau in range(len(e))) / Z
+    return out
+
+
+@pytest.mark.parametrize("pos0", [0, 3])
+def test_full_attention_brute_force(pos0):
+    rng = np.random.default_rng(6)
+    B, T, Hq, Hkv, d = 2, 5, 4, 2, 3
+    q = rng.normal(size=(B, T, Hq, d))
+    k = rng.normal(size=(B, pos0 + T, Hkv, d))
+    v = rng.normal(size=(B, pos0 + T, Hkv, d))
+    assert np.allclose(M.full_attention(q, k, v, pos0), _attn_brute(q, k, v, pos0), atol=1e-12)
+
+
+def test_full_attention_special_cases():
+    rng = np.random.default_rng(7)
+    q = rng.normal(size=(1, 6, 4, 8))
+    k = rng.normal(size=(1, 6, 2, 8))
+    v = rng.normal(size=(1, 6, 2, 8))
+    o = M.full_attention(q, k, v, 0)
+    assert np.allclose(o[0, 0, 0], v[0, 0, 0]) and np.allclose(o[0, 0, 3], v[0, 0, 1])
+    keq = np.repeat(k[:, :1], 6, axis=1)
+    o = M.full_attention(q, keq, v, 0)
+    for t in range(6):
+        assert np.allclose(o[0, t, 0], v[0, :t + 1, 0].mean(0))
+    # GQA equals MHA with each KV head repeated for its group
+    o1 = M.full_attention(q, k, v, 0)
+    o2 = M.full_attention(q, np.repeat(k, 2, axis=2), np.repeat(v, 2, axis=2), 0)
+    assert np.allclose(o1, o2, atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Linear attention
+# --------------------------------------------------------------------------
+
+def _phi(x):
+    return math.expm1(x) + 1.0 if x <= 0 else x + 1.0   # elu(x) + 1, elu with alpha = 1
+
+
+def _lin_brute(q, k, v, S0, z0, eps):
+    B, T, Hq, d = q.shape
+    Hkv = k.shape[2]
+    out = np.zeros((B, T, Hq, d))
+    for b in range(B):
+        for j in range(Hq):
+            h = j // (Hq // Hkv)
+            for t in range(T):
+                fq = [_phi(x) for x in q[b, t, j]]
+                num = [sum(fq[i] * S0[b, h, i, c] for i in range(d)) for c in range(d)]
+                den = sum(fq[i] * z0[b, h, i] for i in range(d)) + eps
+                for tau in range(t + 1):
+                    fk = [_phi(x) for x in k[b, tau, h]]
+                    wgt = sum(fq[i] * fk[i] for i in range(d))
+                    den += wgt
+                    for c in range(d):
+                        num[c] += wgt * v[b, tau, h, c]
+                out[b, t, j] = [n / den for n in num]
+    return out
+
+
+def test_linear_attention_brute_force_with_state():
+    rng = np.random.default_rng(8)
+    B, T, Hq, Hkv, d = 2, 6, 4, 2, 4
+    q, k = rng.normal(size=(B, T, Hq, d)), rng.normal(size=(B, T, Hkv, d))
+    v = rng.normal(size=(B, T, Hkv, d))
+    S0 = rng.normal(size=(B, Hkv, d, d))
+    z0 = np.abs(rng.normal(size=(B, Hkv, d))) + 1
+    o, S, z = M.linear_attention(q, k, v, S0, z0, 1e-6)
+    assert np.allclose(o, _lin_brute(q, k, v, S0, z0, 1e-6), atol=1e-12)
+    fk = np.vectorize(_phi)(k)
+    assert np.allclose(S, S0 + np.einsum("bthi,bthj->bhij", fk, v))
+    assert np.allclose(z, z0 + fk.sum(1))
+
+
+@pytest.mark.parametrize("chunk", [1, 16, 64])
+def test_linear_attention_chunked_form(chunk):
+    """Chunk-parallel form: per chunk, inter-chunk term from the state at the
+    chunk start plus the causal intra-chunk term, equals the recurrence."""
+    rng = np.random.default_rng(9)
+    B, T, Hq, Hkv, d = 1, 100, 4, 2, 8
+    q, k, v = (rng.normal(size=(B, T, Hq, d)), rng.normal(size=(B, T, Hkv, d)),
+               rng.normal(size=(B, T, Hkv, d)))
+    ref, Sref, zref = M.linear_attention(q, k, v, np.zeros((B, Hkv, d, d)), np.zeros((B, Hkv, d)), 1e-6)
+    fq, fk = M.elu_plus_one(q), M.elu_plus_one(k)
+    g = Hq // Hkv
+    S = np.zeros((B, Hkv, d, d))
+    z = np.zeros((B, Hkv, d))
+    out = np.zeros_like(ref)
+    for c0 in range(0, T, chunk):
+        c1 = min(T, c0 + chunk)
+        for j in range(Hq):
+            h = j // g
+            Q, K, V = fq[0, c0:c1, j], fk[0, c0:c1, h], v[0, c0:c1, h]
+            A = np.tril(Q @ K.T)
+            num = Q @ S[0, h] + A @ V
+            den = Q @ z[0, h] + A.sum(1) + 1e-6
+            out[0, c0:c1, j] = num / den[:, None]
+        S = S + np.einsum("bthi,bthj->bhij", fk[:, c0:c1], v[:, c0:c1])
+        z = z + fk[:, c0:c1].sum(1)
+    assert np.allclose(out, ref, atol=1e-11)
+    assert np.allclose(S, Sref) and np.allclose(z, zref)
+
+
+def test_linear_attention_convex_combination():
+    rng = np.random.default_rng(10)
+    q, k, v = rng.normal(size=(1, 40, 2, 6)), rng.normal(size=(1, 40, 2, 6)), rng.normal(size=(1, 40, 2, 6))
+    o, _, _ = M.linear_attention(q, k, v, np.zeros((1, 2, 6, 6)), np.zeros((1, 2, 6)), 0.0)
+    for t in range(40):
+        lo = v[0, :t + 1].min(0)
+        hi = v[0, :t + 1].max(0)
+        assert np.all(o[0, t] >= lo - 1e-12) and np.all(o[0, t] <= hi + 1e-12)
+    assert np.allclose(o[0, 0], v[0, 0])
+
+
+# --------------------------------------------------------------------------
+# Dense pieces against textbook loops; bf16 rounding against a library
+# --------------------------------------------------------------------------
+
+def test_rmsnorm_swiglu_elu_against_loops():
+    rng = np.random.default_rng(11)
+    x = rng.normal(size=(3, 5))
+    g = rng.normal(size=5)
+    r = M.rmsnorm(x, g, 1e-6)
+    for t in range(3):
+        ms = sum(v * v for v in x[t]) / 5
+        assert np.allclose(r[t], [g[c] * x[t, c] / math.sqrt(ms + 1e-6) for c in range(5)])
+    cfg = M.tiny_config(hidden=4, ffn=3)
+    u = rng.normal(size=(2, 4))
+    gu = rng.normal(size=(6, 4))
+    dn = rng.normal(size=(4, 3))
+    y = M.swiglu_ffn(cfg, u, gu, dn)
+    for t in range(2):
+        gate = [sum(gu[f, c] * u[t, c] for c in range(4)) for f in range(3)]
+        up = [sum(gu[3 + f, c] * u[t, c] for c in range(4)) for f in range(3)]
+        inter = [gate[f] / (1 + math.exp(-gate[f])) * up[f] for f in range(3)]
+        want = [sum(dn[c, f] * inter[f] for f in range(3)) for c in range(4)]
+        assert np.allclose(y[t], want)
+    xs = np.linspace(-6, 6, 101)
+    assert np.allclose(M.elu_plus_one(xs), [_phi(v) for v in xs], rtol=1e-15)
+
+
+def test_round_bf16_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(12)
+    x = np.concatenate([rng.normal(size=100000) * 10 ** rng.uniform(-5, 5, size=100000),
+                        np.array([0.0, -0.0, 1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -9, 65504.0])])
+    x32 = x.astype(np.float32)
+    want = torch.from_numpy(x32).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.array_equal(M.round_bf16(x32).astype(np.float32), want)
+    assert np.array_equal(synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(x32)), want)
+
+
+# --------------------------------------------------------------------------
+# Decode / chunking / batch independence
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["fp32"])
+def test_prefill_then_decode_equals_forward(dtype):
+    cfg = M.tiny_config(dtype=dtype)
+    W = M.make_weights(cfg, 0)
+    toks = synth.uniform_int(1, synth.TID_TOKENS, (2, 20), cfg.vocab)
+    full = M.forward(cfg, W, toks, all_logits=True)
+    st = M.State()
+    M.forward(cfg, W, toks[:, :16], state=st)
+    for t in range(16, 20):
+        d = M.forward(cfg, W, toks[:, t:t + 1], state=st)
+        assert M.max_row_rel_err(d, full[:, t]) < 1e-12
+    # chunked prefill equals one-shot
+    st2 = M.State()
+    a = M.forward(cfg, W, toks[:, :7], state=st2, all_logits=True)
+    b = M.forward(cfg, W, toks[:, 7:], state=st2, all_logits=True)
+    assert M.max_row_rel_err(np.concatenate([a, b], 1), full) < 1e-12
+    # batch rows are independent
+    one = M.forward(cfg, W, toks[1:2], all_logits=True)
+    assert M.max_row_rel_err(one, full[1:2]) < 1e-12
+
+
+def test_bf16_storage_points_are_bf16():
+    cfg = M.tiny_config(dtype="bf16")
+    W = M.make_weights(cfg, 0)
+    toks = synth.uniform_int(1, synth.TID_TOKENS, (1, 8), cfg.vocab)
+    h = M.forward(cfg, W, toks, hidden_out=True)
+    assert np.array_equal(M.round_bf16(h), h)
+
+
+# --------------------------------------------------------------------------
+# Synthetic input generator
+# --------------------------------------------------------------------------
+
+def test_splitmix64_known_answers():
+    """First outputs of SplitMix64 seeded with 0, as published with the reference
+    implementation (Vigna)."""
+    out = [int(x) for x in synth.splitmix64_outputs(0, 0, 3)]
+    assert out == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_synth_moments_and_slices():
+    x = synth.normal_f32(0, 77, (1 << 20,))
+    assert abs(x.mean()) < 5e-3 and abs(x.std() - 1) < 5e-3 and np.abs(x).max() <= 3.4642
+    y = synth.normal_f32(0, 77, (1000,), start=5000)
+    assert np.array_equal(y, x[5000:6000])
+    big = synth.normal_f32(0, 78, (3 << 22,))          # threaded path
+    assert np.array_equal(big[(1 << 22) - 5:(1 << 22) + 5],
+                          synth.normal_f32(0, 78, (10,), start=(1 << 22) - 5))
+    t = synth.uniform_int(1, 3, (100000,), 248320)
+    assert t.min() >= 0 and t.max() < 248320 and abs(t.mean() / 248320 - 0.5) < 0.01
