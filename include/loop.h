@@ -1,0 +1,190 @@
+/*
+ * loop.h - C ABI of libloop.so: the forward pass (prefill and decode) of a
+ * looped weight-shared decoder on one AMD Instinct MI355X (gfx950).
+ *
+ * What is computed.  The model stores n_layers decoder layers.  Layers
+ * [0, loop_start) run once, the block [loop_start, loop_end) runs n_passes
+ * times with every pass fed the previous pass's output, and layers
+ * [loop_end, n_layers) and the output head finish (pages: "SenseTime's Loop-9B
+ * runs its own layers twice, and gets a deeper model for free", section "The
+ * trick: run the middle of the network twice"; "How Does SenseNova-Loop Get
+ * More Depth Without More Parameters?", section "What is the looped decoder in
+ * SenseNova-Loop?").  The Loop-9B shape is 32 stored layers, block [4, 28)
+ * twice: 56 layer executions.  The loop range, the pass count and the
+ * hyper-connection parameters are part of the model's execution config, which
+ * a compatible engine must load and honour (same page, section "How do you
+ * run SenseNova-Loop-9B-Preview?"): they are fields of loop_config below.
+ *
+ * Inside the block the hidden state is two residual streams X0, X1 joined by
+ * hyper-connection maps (section "What does two-stream mHC do?").  Every
+ * sublayer (attention, then FFN) of a looped layer is one site with learned
+ * float32 parameters W [8][2C], b [8]:
+ *   x_hat = [X0, X1] / rms([X0, X1]);  l = W x_hat + b
+ *   H_pre = sigmoid(l0, l1), H_post = 2 sigmoid(l2, l3),
+ *   H_res = Sinkhorn_iters(exp([[l4, l5], [l6, l7]] - max))  (rows, then columns)
+ *   u = RMSNorm(H_pre0 X0 + H_pre1 X1; gamma);  y = f(u)
+ *   X_i <- sum_j H_res[i][j] X_j + H_post[i] y
+ * The streams are entered as two copies of h before the first looped layer
+ * and left as their mean after the last pass.  Outside the block every layer
+ * is two pre-norm residual sublayers h <- h + f(RMSNorm(h; gamma)).
+ * Attention follows a period of attn_period layers: layer i is full causal
+ * softmax attention when i % attn_period == attn_period - 1 and causal linear
+ * attention otherwise ("How does the hybrid attention pattern work?").  The
+ * linear attention uses the elu+1 feature map with normaliser la_eps; each
+ * (layer, pass) owns its own KV cache or linear state.  The FFN is SwiGLU.
+ * The pages leave these internals open; the choices above are this library's
+ * documented reading.
+ *
+ * Conventions.
+ *  - All tensors are row-major.  "dtype" means float (LOOP_FP32) or bf16
+ *    (LOOP_BF16) for the whole backbone; RMSNorm gains and the mHC
+ *    parameters are always float32; logits are always float32.
+ *  - Device pointers are HIP device memory owned by the caller, 16-byte
+ *    aligned (torch and hipMalloc allocations are 256-byte aligned), valid
+ *    for as long as the calls that use them run.
+ *  - Every call is asynchronous on the given stream (a hipStream_t passed as
+ *    void*; NULL = the default stream).  Calls that share a state must be
+ *    issued on one stream, in order.
+ *  - Results are deterministic: no floating-point atomics are used.
+ *  - Return codes are LOOP_OK (0) or a negative loop_status; a failed call
+ *    has launched nothing and changed no state.  loop_last_error() gives a
+ *    message for the calling thread.  Device-side input errors (a token id
+ *    out of range) are flagged in the state and read by loop_state_check().
+ */
+#ifndef LOOP_H
+#define LOOP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  LOOP_OK = 0,
+  LOOP_ERR_INVALID_ARG = -1,  /* null pointer or a value out of range */
+  LOOP_ERR_SHAPE = -2,        /* shapes the kernels do not support */
+  LOOP_ERR_ALIGN = -3,        /* a pointer not 16-byte aligned */
+  LOOP_ERR_CAPACITY = -4,     /* batch or positions beyond the state's capacity */
+  LOOP_ERR_WORKSPACE = -5,    /* workspace smaller than loop_workspace_bytes() */
+  LOOP_ERR_NO_DEVICE = -6,    /* no HIP device */
+  LOOP_ERR_HIP = -7,          /* a HIP runtime call failed */
+  LOOP_ERR_DEVICE_FLAG = -8,  /* loop_state_check(): a device-side input error was flagged */
+  LOOP_ERR_STATE = -9         /* decode before any prefill, or a state of another model */
+} loop_status;
+
+enum { LOOP_FP32 = 0, LOOP_BF16 = 1 };
+
+/* loop_prefill flags */
+enum {
+  LOOP_ALL_LOGITS = 1,  /* logits for every position [B][S][V] (default: last position [B][V]) */
+  LOOP_HIDDEN_OUT = 2,  /* return the final residual h [B][S][C] in dtype instead of logits */
+  LOOP_CONTINUE = 4     /* append to the state's sequences (chunked prefill) instead of restarting */
+};
+
+typedef struct loop_config {
+  int vocab;           /* V */
+  int hidden;          /* C; a multiple of 8, at most 4096 */
+  int ffn;             /* F (SwiGLU width) */
+  int n_heads;         /* Hq query heads */
+  int n_kv_heads;      /* Hkv KV heads; Hq % Hkv == 0, Hq / Hkv <= 8 */
+  int head_dim;        /* d: 64 or 128 (bf16 needs 128) */
+  int n_layers;        /* stored layers */
+  int loop_start;      /* first looped layer */
+  int loop_end;        /* one past the last looped layer */
+  int n_passes;        /* >= 1 */
+  int sinkhorn_iters;  /* Sinkhorn iterations of H_res (20 for Loop-9B) */
+  int attn_period;     /* layer i is full attention iff i % attn_period == attn_period - 1 */
+  float rms_eps;       /* RMSNorm epsilon (mHC rms included) */
+  float la_eps;        /* linear-attention normaliser epsilon */
+  int dtype;           /* LOOP_FP32 or LOOP_BF16 */
+} loop_config;
+
+typedef struct loop_layer_weights {
+  const float* attn_norm;  /* [C] */
+  const float* ffn_norm;   /* [C] */
+  const void* qkv;         /* [(Hq + 2 Hkv) d][C]: q rows, then k rows, then v rows */
+  const void* o;           /* [C][Hq d] */
+  const void* gate_up;     /* [2F][C]: gate rows, then up rows */
+  const void* down;        /* [C][F] */
+  const float* mhc_w[2];   /* looped layers only: [8][2C] per site (0 = attention, 1 = FFN) */
+  const float* mhc_b[2];   /* looped layers only: [8] per site */
+} loop_layer_weights;
+
+typedef struct loop_weights {
+  const void* embed;               /* [V][C] */
+  const float* final_norm;         /* [C] */
+  const void* head;                /* [V][C] (untied) */
+  const loop_layer_weights* layers;  /* host array of n_layers entries (copied) */
+  int n_layers;
+} loop_weights;
+
+typedef struct loop_model loop_model;  /* host object: config, weight pointers, schedule */
+typedef struct loop_state loop_state;  /* host handle on caller-owned device state */
+
+/* Validates the config and records the weight pointers (no copy, no launch).
+ * Errors: INVALID_ARG, SHAPE, ALIGN, NO_DEVICE. */
+int loop_model_create(const loop_config* cfg, const loop_weights* w, loop_model** out);
+int loop_model_destroy(loop_model* m);
+
+/* The execution schedule: for e < n, layer[e], pass[e] and kind[e] (1 = full,
+ * 0 = linear) and slot[e] (index among full or among linear executions).
+ * Any output array may be NULL; *n receives the number of executions. */
+int loop_model_schedule(const loop_model* m, int max, int* layer, int* pass, int* kind, int* slot, int* n);
+
+/* Device bytes of a state for `batch` sequences of up to `max_seq` positions:
+ * a 256-byte header, then per full-attention execution K [batch][Hkv][S_max][d]
+ * and V^T [batch][Hkv][d][S_max] (dtype), then per linear execution
+ * S [batch][Hkv][d][d] and z [batch][Hkv][d] (float32); S_max is max_seq
+ * rounded up to a multiple of 64. */
+int loop_state_bytes(const loop_model* m, int batch, int max_seq, size_t* bytes);
+
+/* Device bytes of the workspace for one call over up to `max_tokens` new
+ * positions in total (batch x positions per sequence) of `batch` sequences
+ * whose state holds up to `max_seq` positions. */
+int loop_workspace_bytes(const loop_model* m, int batch, int max_tokens, int max_seq, size_t* bytes);
+
+/* Wraps caller-owned device memory (>= loop_state_bytes) as a state of length 0.
+ * The memory is not cleared; a prefill without LOOP_CONTINUE ignores its
+ * contents.  Clear the header once (hipMemset to 0) before the first
+ * loop_state_check(). */
+int loop_state_create(const loop_model* m, void* state_dev, size_t bytes, int batch, int max_seq, loop_state** out);
+int loop_state_destroy(loop_state* st);
+int loop_state_length(const loop_state* st, int* length);
+/* Declares that every sequence holds `length` valid positions (for example
+ * after filling the regions directly); 0 <= length <= max_seq. */
+int loop_state_set_length(loop_state* st, int length);
+/* Device pointer and byte size of one region of the state: kind 0 = K, 1 = V^T
+ * (slot = full-attention execution index), 2 = S, 3 = z (slot = linear
+ * execution index), 4 = header (slot ignored; word 0 = error flags). */
+int loop_state_region(const loop_state* st, int kind, int slot, void** ptr, size_t* bytes);
+/* Synchronises the stream, reads and clears the device error word.
+ * Returns LOOP_OK or LOOP_ERR_DEVICE_FLAG (token id out of range: row 0 used). */
+int loop_state_check(loop_state* st, void* stream);
+
+/* Prefill of B sequences of S new positions each (B <= state batch).
+ * tokens_dev: int32 [B][S] (or NULL with embeds_dev: dtype [B][S][C]).
+ * out_dev: float32 logits [B][V] (last position), [B][S][V] with
+ * LOOP_ALL_LOGITS, or dtype h [B][S][C] with LOOP_HIDDEN_OUT.
+ * Without LOOP_CONTINUE the sequences restart at position 0; with it they
+ * continue at the state's length.  The state's length grows by S.
+ * Errors: INVALID_ARG, ALIGN, CAPACITY, WORKSPACE, HIP. */
+int loop_prefill(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes,
+                 const int32_t* tokens_dev, const void* embeds_dev, int B, int S,
+                 unsigned flags, void* out_dev, void* stream);
+
+/* One decode step: one new token per sequence, tokens_dev int32 [B]; logits
+ * float32 [B][V].  Appends one position to every KV cache and updates every
+ * linear state.  Errors: as loop_prefill, plus STATE when the state is empty. */
+int loop_decode_step(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes,
+                     const int32_t* tokens_dev, int B, float* logits_dev, void* stream);
+
+const char* loop_status_string(int status);
+const char* loop_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOOP_H */

@@ -1,0 +1,520 @@
+// Loop driver and C ABI (include/loop.h).
+//
+// The driver owns no device memory.  It turns the execution config into a
+// schedule table, one entry per layer execution (stored layer, pass, kind,
+// per-(layer, pass) cache slot), and walks it, enqueueing the kernels of every
+// sublayer on the caller's stream.  Each shared layer's weights are read once
+// per pass: the block [loop_start, loop_end) is walked n_passes times with the
+// same weight pointers.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/loop.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+bool misaligned(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct Exec {
+  int layer, pass, full, slot;
+};
+
+constexpr int DEC_SPLIT = 256;   // keys per decode-attention split
+constexpr int LIN_CHUNK = 64;
+
+}  // namespace
+
+struct loop_model {
+  loop_config cfg;
+  std::vector<loop_layer_weights> layers;
+  const void* embed;
+  const float* final_norm;
+  const void* head;
+  std::vector<Exec> sched;
+  int n_full = 0, n_lin = 0;
+  int es = 4;
+  int cu = 0;
+  bool in_loop(int i) const { return i >= cfg.loop_start && i < cfg.loop_end; }
+  int qkv_rows() const { return (cfg.n_heads + 2 * cfg.n_kv_heads) * cfg.head_dim; }
+};
+
+struct loop_state {
+  const loop_model* m;
+  char* base;
+  size_t bytes;
+  int batch, max_seq, S_max;
+  int length;
+  std::vector<size_t> koff, voff, soff, zoff;
+};
+
+namespace {
+
+struct WsLayout {
+  size_t h, X, u, y, qkv, attn, inter, maps, lin, dec, total;
+};
+
+WsLayout ws_layout(const loop_model* m, int batch, int max_tokens, int max_seq) {
+  const loop_config& c = m->cfg;
+  const size_t T = (size_t)max_tokens, C = c.hidden, es = m->es;
+  WsLayout w{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align256(bytes); return o; };
+  w.h = take(T * C * es);
+  w.X = take(T * 2 * C * es);
+  w.u = take(T * C * es);
+  w.y = take(T * C * es);
+  w.qkv = take(T * m->qkv_rows() * es);
+  w.attn = take(T * c.n_heads * c.head_dim * es);
+  w.inter = take(T * c.ffn * es);
+  w.maps = take(2 * T * 8 * sizeof(float));
+  const size_t chunks = (T + LIN_CHUNK - 1) / LIN_CHUNK + (size_t)batch;
+  w.lin = take(chunks * c.n_kv_heads * ((size_t)c.head_dim * c.head_dim + c.head_dim) * sizeof(float));
+  const size_t S_max = ((size_t)max_seq + 63) / 64 * 64;
+  const size_t nsplit = (S_max + DEC_SPLIT - 1) / DEC_SPLIT;
+  w.dec = take((size_t)batch * c.n_heads * nsplit * (c.head_dim + 2) * sizeof(float));
+  w.total = off;
+  return w;
+}
+
+int check_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return LOOP_OK;
+  return fail(LOOP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* loop_status_string(int s) {
+  switch (s) {
+    case LOOP_OK: return "ok";
+    case LOOP_ERR_INVALID_ARG: return "invalid argument";
+    case LOOP_ERR_SHAPE: return "unsupported shape";
+    case LOOP_ERR_ALIGN: return "misaligned pointer";
+    case LOOP_ERR_CAPACITY: return "capacity exceeded";
+    case LOOP_ERR_WORKSPACE: return "workspace too small";
+    case LOOP_ERR_NO_DEVICE: return "no HIP device";
+    case LOOP_ERR_HIP: return "HIP runtime error";
+    case LOOP_ERR_DEVICE_FLAG: return "device-side input error";
+    case LOOP_ERR_STATE: return "invalid state";
+  }
+  return "unknown status";
+}
+
+const char* loop_last_error(void) { return g_err.c_str(); }
+
+int loop_model_create(const loop_config* cfg, const loop_weights* w, loop_model** out) {
+  if (!cfg || !w || !out) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  *out = nullptr;
+  const loop_config& c = *cfg;
+  if (c.vocab <= 0 || c.hidden <= 0 || c.ffn <= 0 || c.n_heads <= 0 || c.n_kv_heads <= 0 ||
+      c.head_dim <= 0 || c.n_layers <= 0)
+    return fail(LOOP_ERR_INVALID_ARG, "sizes must be positive");
+  if (c.loop_start < 0 || c.loop_start > c.loop_end || c.loop_end > c.n_layers)
+    return fail(LOOP_ERR_INVALID_ARG, "loop range [%d, %d) not inside [0, %d]", c.loop_start, c.loop_end, c.n_layers);
+  if (c.n_passes < 1) return fail(LOOP_ERR_INVALID_ARG, "n_passes must be >= 1");
+  if (c.sinkhorn_iters < 0 || c.attn_period < 1) return fail(LOOP_ERR_INVALID_ARG, "sinkhorn_iters / attn_period");
+  if (!(c.rms_eps > 0.f) || !(c.la_eps >= 0.f)) return fail(LOOP_ERR_INVALID_ARG, "eps");
+  if (c.dtype != LOOP_FP32 && c.dtype != LOOP_BF16) return fail(LOOP_ERR_INVALID_ARG, "dtype");
+  if (w->n_layers != c.n_layers || !w->layers) return fail(LOOP_ERR_INVALID_ARG, "weights: layer count");
+  if (c.n_heads % c.n_kv_heads || c.n_heads / c.n_kv_heads > 8)
+    return fail(LOOP_ERR_SHAPE, "n_heads must be a multiple of n_kv_heads, at most 8 per group");
+  if (c.hidden % 8 || c.hidden > 4096) return fail(LOOP_ERR_SHAPE, "hidden must be a multiple of 8, <= 4096");
+  if (c.head_dim != 64 && c.head_dim != 128) return fail(LOOP_ERR_SHAPE, "head_dim must be 64 or 128");
+  const int qkv_rows = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
+  if (c.dtype == LOOP_BF16) {
+    if (c.head_dim != 128) return fail(LOOP_ERR_SHAPE, "bf16 needs head_dim 128");
+    if (c.hidden % 256 || qkv_rows % 256 || c.vocab % 256 || (c.n_heads * c.head_dim) % 128 || c.ffn % 128)
+      return fail(LOOP_ERR_SHAPE, "bf16 GEMM tiles need hidden, qkv rows, vocab %% 256 == 0 and ffn %% 128 == 0");
+  } else {
+    if (c.ffn % 8 || (c.n_heads * c.head_dim) % 8) return fail(LOOP_ERR_SHAPE, "fp32 widths must be multiples of 8");
+  }
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return fail(LOOP_ERR_NO_DEVICE, "no HIP device");
+
+  auto* m = new loop_model();
+  m->cfg = c;
+  m->es = c.dtype == LOOP_BF16 ? 2 : 4;
+  m->embed = w->embed;
+  m->final_norm = w->final_norm;
+  m->head = w->head;
+  m->layers.assign(w->layers, w->layers + c.n_layers);
+  auto bad = [&](const char* what, int i) {
+    delete m;
+    return fail(LOOP_ERR_INVALID_ARG, "weights: %s missing (layer %d)", what, i);
+  };
+  if (!m->embed || !m->final_norm || !m->head) return bad("embed/final_norm/head", -1);
+  if (misaligned(m->embed) || misaligned(m->final_norm) || misaligned(m->head)) {
+    delete m;
+    return fail(LOOP_ERR_ALIGN, "weights: global tensor not 16-byte aligned");
+  }
+  for (int i = 0; i < c.n_layers; ++i) {
+    const loop_layer_weights& L = m->layers[i];
+    if (!L.attn_norm || !L.ffn_norm || !L.qkv || !L.o || !L.gate_up || !L.down) return bad("layer tensor", i);
+    const void* ps[6] = {L.attn_norm, L.ffn_norm, L.qkv, L.o, L.gate_up, L.down};
+    for (const void* p : ps)
+      if (misaligned(p)) { delete m; return fail(LOOP_ERR_ALIGN, "weights: layer %d tensor not 16-byte aligned", i); }
+    if (m->in_loop(i)) {
+      for (int s = 0; s < 2; ++s) {
+        if (!L.mhc_w[s] || !L.mhc_b[s]) return bad("mhc parameters", i);
+        if (misaligned(L.mhc_w[s])) { delete m; return fail(LOOP_ERR_ALIGN, "weights: mhc_w not 16-byte aligned"); }
+      }
+    }
+  }
+  // schedule: [0, ls) once, [ls, le) n_passes times, [le, L) once
+  auto push = [&](int i, int p) {
+    const int full = (i % c.attn_period) == c.attn_period - 1;
+    m->sched.push_back({i, p, full, full ? m->n_full++ : m->n_lin++});
+  };
+  for (int i = 0; i < c.loop_start; ++i) push(i, 0);
+  for (int p = 0; p < c.n_passes; ++p)
+    for (int i = c.loop_start; i < c.loop_end; ++i) push(i, p);
+  for (int i = c.loop_end; i < c.n_layers; ++i) push(i, 0);
+  m->cu = lk::device_cu_count();
+  if (m->cu <= 0) m->cu = 256;
+  *out = m;
+  return LOOP_OK;
+}
+
+int loop_model_destroy(loop_model* m) {
+  delete m;
+  return LOOP_OK;
+}
+
+int loop_model_schedule(const loop_model* m, int max, int* layer, int* pass, int* kind, int* slot, int* n) {
+  if (!m || !n) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  *n = (int)m->sched.size();
+  for (int e = 0; e < *n && e < max; ++e) {
+    if (layer) layer[e] = m->sched[e].layer;
+    if (pass) pass[e] = m->sched[e].pass;
+    if (kind) kind[e] = m->sched[e].full;
+    if (slot) slot[e] = m->sched[e].slot;
+  }
+  return LOOP_OK;
+}
+
+static void state_offsets(const loop_model* m, int batch, int max_seq, std::vector<size_t>* k, std::vector<size_t>* v,
+                          std::vector<size_t>* s, std::vector<size_t>* z, size_t* total) {
+  const loop_config& c = m->cfg;
+  const size_t S_max = ((size_t)max_seq + 63) / 64 * 64;
+  const size_t kv = (size_t)batch * c.n_kv_heads * S_max * c.head_dim * m->es;
+  const size_t sb = (size_t)batch * c.n_kv_heads * c.head_dim * c.head_dim * sizeof(float);
+  const size_t zb = (size_t)batch * c.n_kv_heads * c.head_dim * sizeof(float);
+  size_t off = 256;
+  for (int i = 0; i < m->n_full; ++i) {
+    if (k) k->push_back(off);
+    off += align256(kv);
+    if (v) v->push_back(off);
+    off += align256(kv);
+  }
+  for (int i = 0; i < m->n_lin; ++i) {
+    if (s) s->push_back(off);
+    off += align256(sb);
+    if (z) z->push_back(off);
+    off += align256(zb);
+  }
+  *total = off;
+}
+
+int loop_state_bytes(const loop_model* m, int batch, int max_seq, size_t* bytes) {
+  if (!m || !bytes) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (batch <= 0 || max_seq <= 0) return fail(LOOP_ERR_INVALID_ARG, "batch and max_seq must be positive");
+  state_offsets(m, batch, max_seq, nullptr, nullptr, nullptr, nullptr, bytes);
+  return LOOP_OK;
+}
+
+int loop_workspace_bytes(const loop_model* m, int batch, int max_tokens, int max_seq, size_t* bytes) {
+  if (!m || !bytes) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (batch <= 0 || max_tokens <= 0 || max_seq <= 0) return fail(LOOP_ERR_INVALID_ARG, "sizes must be positive");
+  *bytes = ws_layout(m, batch, max_tokens, max_seq).total;
+  return LOOP_OK;
+}
+
+int loop_state_create(const loop_model* m, void* state_dev, size_t bytes, int batch, int max_seq, loop_state** out) {
+  if (!m || !state_dev || !out) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  *out = nullptr;
+  if (batch <= 0 || max_seq <= 0) return fail(LOOP_ERR_INVALID_ARG, "batch and max_seq must be positive");
+  if (misaligned(state_dev)) return fail(LOOP_ERR_ALIGN, "state not 16-byte aligned");
+  auto* st = new loop_state();
+  size_t need = 0;
+  state_offsets(m, batch, max_seq, &st->koff, &st->voff, &st->soff, &st->zoff, &need);
+  if (bytes < need) {
+    delete st;
+    return fail(LOOP_ERR_CAPACITY, "state has %zu bytes, needs %zu", bytes, need);
+  }
+  st->m = m;
+  st->base = (char*)state_dev;
+  st->bytes = bytes;
+  st->batch = batch;
+  st->max_seq = max_seq;
+  st->S_max = (max_seq + 63) / 64 * 64;
+  st->length = 0;
+  *out = st;
+  return LOOP_OK;
+}
+
+int loop_state_destroy(loop_state* st) {
+  delete st;
+  return LOOP_OK;
+}
+
+int loop_state_length(const loop_state* st, int* length) {
+  if (!st || !length) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  *length = st->length;
+  return LOOP_OK;
+}
+
+int loop_state_set_length(loop_state* st, int length) {
+  if (!st) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (length < 0 || length > st->max_seq) return fail(LOOP_ERR_CAPACITY, "length %d outside [0, %d]", length, st->max_seq);
+  st->length = length;
+  return LOOP_OK;
+}
+
+int loop_state_region(const loop_state* st, int kind, int slot, void** ptr, size_t* bytes) {
+  if (!st || !ptr) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  const loop_model* m = st->m;
+  const loop_config& c = m->cfg;
+  size_t off = 0, sz = 0;
+  const size_t kv = (size_t)st->batch * c.n_kv_heads * st->S_max * c.head_dim * m->es;
+  switch (kind) {
+    case 0: case 1:
+      if (slot < 0 || slot >= m->n_full) return fail(LOOP_ERR_INVALID_ARG, "full slot %d out of range", slot);
+      off = kind == 0 ? st->koff[slot] : st->voff[slot];
+      sz = kv;
+      break;
+    case 2: case 3:
+      if (slot < 0 || slot >= m->n_lin) return fail(LOOP_ERR_INVALID_ARG, "linear slot %d out of range", slot);
+      off = kind == 2 ? st->soff[slot] : st->zoff[slot];
+      sz = (size_t)st->batch * c.n_kv_heads * c.head_dim * (kind == 2 ? c.head_dim : 1) * sizeof(float);
+      break;
+    case 4:
+      off = 0;
+      sz = 256;
+      break;
+    default:
+      return fail(LOOP_ERR_INVALID_ARG, "region kind %d", kind);
+  }
+  *ptr = st->base + off;
+  if (bytes) *bytes = sz;
+  return LOOP_OK;
+}
+
+int loop_state_check(loop_state* st, void* stream) {
+  if (!st) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t word = 0;
+  int r = check_hip(hipMemcpyAsync(&word, st->base, sizeof word, hipMemcpyDeviceToHost, s), "read error word");
+  if (r) return r;
+  r = check_hip(hipStreamSynchronize(s), "synchronize");
+  if (r) return r;
+  if (word) {
+    r = check_hip(hipMemsetAsync(st->base, 0, sizeof word, s), "clear error word");
+    if (r) return r;
+    r = check_hip(hipStreamSynchronize(s), "synchronize");
+    if (r) return r;
+    return fail(LOOP_ERR_DEVICE_FLAG, "device flagged input error 0x%x (token id out of range)", word);
+  }
+  return LOOP_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+#define LAUNCH(call, what)                                   \
+  do {                                                       \
+    hipError_t e_ = (call);                                  \
+    if (e_ != hipSuccess) return check_hip(e_, what);        \
+  } while (0)
+
+int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, const int32_t* tokens,
+            const void* embeds, int B, int S, unsigned flags, void* out, hipStream_t s, bool decode) {
+  const loop_config& c = m->cfg;
+  if (!st || st->m != m) return fail(LOOP_ERR_STATE, "state does not belong to this model");
+  if (!workspace || !out || (!tokens && !embeds)) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (B <= 0 || S <= 0) return fail(LOOP_ERR_INVALID_ARG, "B and S must be positive");
+  if (misaligned(workspace) || misaligned(out) || misaligned(embeds)) return fail(LOOP_ERR_ALIGN, "misaligned buffer");
+  if (B > st->batch) return fail(LOOP_ERR_CAPACITY, "batch %d exceeds the state's %d", B, st->batch);
+  if (decode && st->length == 0) return fail(LOOP_ERR_STATE, "decode before prefill");
+  const int pos0 = (decode || (flags & LOOP_CONTINUE)) ? st->length : 0;
+  if ((long)pos0 + S > st->max_seq)
+    return fail(LOOP_ERR_CAPACITY, "positions %d + %d exceed max_seq %d", pos0, S, st->max_seq);
+  const int T = B * S;
+  const WsLayout L = ws_layout(m, B, T, st->max_seq);
+  if (ws_bytes < L.total) return fail(LOOP_ERR_WORKSPACE, "workspace %zu bytes, needs %zu", ws_bytes, L.total);
+
+  char* ws = (char*)workspace;
+  void* h = ws + L.h;
+  void* X = ws + L.X;
+  void* u = ws + L.u;
+  void* y = ws + L.y;
+  void* qkv = ws + L.qkv;
+  void* attn = ws + L.attn;
+  void* inter = ws + L.inter;
+  float* maps[2] = {(float*)(ws + L.maps), (float*)(ws + L.maps) + (size_t)T * 8};
+  float* lin_scr = (float*)(ws + L.lin);
+  float* dec_part = (float*)(ws + L.dec);
+  const int dt = c.dtype == LOOP_BF16 ? lk::DT_BF16 : lk::DT_F32;
+  const int C = c.hidden, Hq = c.n_heads, Hkv = c.n_kv_heads, d = c.head_dim;
+  const int qkv_rows = m->qkv_rows();
+  const int mhc_grid = T < 2 * m->cu ? T : 2 * m->cu;
+
+  // embedding
+  if (tokens) {
+    LAUNCH(lk::embed(dt, tokens, m->embed, c.vocab, C, T, h, (uint32_t*)st->base, s), "embed");
+  } else {
+    LAUNCH(hipMemcpyAsync(h, embeds, (size_t)T * C * m->es, hipMemcpyDeviceToDevice, s), "copy embeds");
+  }
+
+  auto norm = [&](const void* yin, const float* gamma) {
+    lk::NormArgs a{dt, T, C, yin, h, gamma, u, c.rms_eps};
+    return lk::add_rmsnorm(a, s);
+  };
+  int mp = 0;   // maps[mp] holds the maps of the current mHC site
+  auto mhc = [&](int mode, const void* yin, const float* w, const float* b, const float* gamma) {
+    lk::MhcArgs a{};
+    a.dt = dt; a.mode = mode; a.T = T; a.C = C; a.iters = c.sinkhorn_iters; a.eps = c.rms_eps;
+    a.y = yin; a.h = h; a.X = X;
+    a.maps_in = maps[mp];
+    a.maps_out = maps[mp ^ 1];
+    a.w = w; a.b = b; a.gamma = gamma; a.u = u; a.grid = mhc_grid;
+    hipError_t e = lk::mhc(a, s);
+    if (mode != lk::MHC_EXIT) mp ^= 1;
+    return e;
+  };
+  auto gemm = [&](int epi, const void* A, long lda, int M, const void* Bw, int N, int K, void* Cout, long ldc) {
+    lk::GemmArgs g{};
+    g.dt = dt; g.epi = epi; g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda; g.B = Bw; g.ldb = K; g.C = Cout; g.ldc = ldc;
+    return g;
+  };
+
+  const auto& sched = m->sched;
+  const int E = (int)sched.size();
+  {
+    const loop_layer_weights& L0 = m->layers[sched[0].layer];
+    if (m->in_loop(sched[0].layer)) {
+      LAUNCH(mhc(lk::MHC_ENTER, nullptr, L0.mhc_w[0], L0.mhc_b[0], L0.attn_norm), "mhc enter");
+    } else {
+      LAUNCH(norm(nullptr, L0.attn_norm), "rmsnorm");
+    }
+  }
+  for (int e = 0; e < E; ++e) {
+    const Exec& ex = sched[e];
+    const loop_layer_weights& W = m->layers[ex.layer];
+    const bool looped = m->in_loop(ex.layer);
+    // ---- attention sublayer
+    if (ex.full) {
+      lk::GemmArgs g = gemm(lk::EPI_QKV, u, C, T, W.qkv, qkv_rows, C, qkv, qkv_rows);
+      g.q_cols = Hq * d; g.n_kv = Hkv; g.head_dim = d;
+      g.kcache = st->base + st->koff[ex.slot];
+      g.vcache = st->base + st->voff[ex.slot];
+      g.S_call = S; g.pos0 = pos0; g.S_max = st->S_max;
+      LAUNCH(lk::gemm(g, s), "qkv gemm");
+      lk::AttnArgs a{};
+      a.dt = dt; a.B = B; a.S_call = S; a.pos0 = pos0; a.S_max = st->S_max; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+      a.q = qkv; a.ldq = qkv_rows; a.kcache = g.kcache; a.vcache = g.vcache; a.out = attn; a.ldo = Hq * d;
+      if (decode && dt == lk::DT_BF16) {
+        a.part = dec_part; a.split_len = DEC_SPLIT; a.n_split = (pos0 + S + DEC_SPLIT - 1) / DEC_SPLIT;
+        LAUNCH(lk::attn_decode(a, s), "decode attention");
+      } else {
+        LAUNCH(lk::attn_prefill(a, s), "prefill attention");
+      }
+    } else {
+      lk::GemmArgs g = gemm(lk::EPI_STORE, u, C, T, W.qkv, qkv_rows, C, qkv, qkv_rows);
+      LAUNCH(lk::gemm(g, s), "qkv gemm");
+      lk::LinArgs a{};
+      a.dt = dt; a.B = B; a.S_call = S; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.eps = c.la_eps;
+      a.qkv = qkv; a.ld = qkv_rows;
+      a.S = (float*)(st->base + st->soff[ex.slot]);
+      a.z = (float*)(st->base + st->zoff[ex.slot]);
+      a.init_zero = pos0 == 0;
+      a.out = attn; a.ldo = Hq * d; a.scratch = lin_scr; a.chunk = LIN_CHUNK;
+      if (S <= 16) { LAUNCH(lk::lin_decode(a, s), "linear attention (recurrent)"); }
+      else { LAUNCH(lk::lin_prefill(a, s), "linear attention (chunked)"); }
+    }
+    LAUNCH(lk::gemm(gemm(lk::EPI_STORE, attn, Hq * d, T, W.o, C, Hq * d, y, C), s), "o gemm");
+    // ---- attention -> FFN transition
+    if (looped) {
+      LAUNCH(mhc(lk::MHC_MID, y, W.mhc_w[1], W.mhc_b[1], W.ffn_norm), "mhc");
+    } else {
+      LAUNCH(norm(y, W.ffn_norm), "add+rmsnorm");
+    }
+    // ---- FFN sublayer
+    {
+      lk::GemmArgs g = gemm(lk::EPI_SWIGLU, u, C, T, W.gate_up, 2 * c.ffn, C, inter, c.ffn);
+      g.F = c.ffn;
+      LAUNCH(lk::gemm(g, s), "gate/up gemm");
+    }
+    LAUNCH(lk::gemm(gemm(lk::EPI_STORE, inter, c.ffn, T, W.down, C, c.ffn, y, C), s), "down gemm");
+    // ---- transition to the next execution (or the final norm)
+    const bool has_next = e + 1 < E;
+    const loop_layer_weights* Wn = has_next ? &m->layers[sched[e + 1].layer] : nullptr;
+    const bool next_looped = has_next && m->in_loop(sched[e + 1].layer);
+    const float* gamma_next = has_next ? Wn->attn_norm : m->final_norm;
+    if (looped) {
+      if (next_looped) {
+        LAUNCH(mhc(lk::MHC_MID, y, Wn->mhc_w[0], Wn->mhc_b[0], gamma_next), "mhc");
+      } else {
+        LAUNCH(mhc(lk::MHC_EXIT, y, nullptr, nullptr, gamma_next), "mhc exit");
+      }
+    } else if (next_looped) {
+      LAUNCH(mhc(lk::MHC_ENTER, y, Wn->mhc_w[0], Wn->mhc_b[0], gamma_next), "mhc enter");
+    } else {
+      LAUNCH(norm(y, gamma_next), "add+rmsnorm");
+    }
+  }
+  // ---- output
+  if (flags & LOOP_HIDDEN_OUT) {
+    LAUNCH(hipMemcpyAsync(out, h, (size_t)T * C * m->es, hipMemcpyDeviceToDevice, s), "copy hidden");
+  } else if (flags & LOOP_ALL_LOGITS) {
+    LAUNCH(lk::gemm(gemm(lk::EPI_F32, u, C, T, m->head, c.vocab, C, out, c.vocab), s), "head gemm");
+  } else {
+    const char* last = (const char*)u + (size_t)(S - 1) * C * m->es;
+    LAUNCH(lk::gemm(gemm(lk::EPI_F32, last, (long)S * C, B, m->head, c.vocab, C, out, c.vocab), s), "head gemm");
+  }
+  st->length = pos0 + S;
+  return LOOP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int loop_prefill(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, const int32_t* tokens_dev,
+                 const void* embeds_dev, int B, int S, unsigned flags, void* out_dev, void* stream) {
+  if (!m) return fail(LOOP_ERR_INVALID_ARG, "null model");
+  if (flags & ~(unsigned)(LOOP_ALL_LOGITS | LOOP_HIDDEN_OUT | LOOP_CONTINUE))
+    return fail(LOOP_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  return forward(m, st, workspace, ws_bytes, tokens_dev, embeds_dev, B, S, flags, out_dev, (hipStream_t)stream, false);
+}
+
+int loop_decode_step(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, const int32_t* tokens_dev,
+                     int B, float* logits_dev, void* stream) {
+  if (!m) return fail(LOOP_ERR_INVALID_ARG, "null model");
+  if (!tokens_dev) return fail(LOOP_ERR_INVALID_ARG, "null tokens");
+  return forward(m, st, workspace, ws_bytes, tokens_dev, nullptr, B, 1, 0, logits_dev, (hipStream_t)stream, true);
+}
+
+}  // extern "C"

@@ -1,0 +1,400 @@
+// Causal softmax attention with grouped KV heads over a per-(layer, pass) KV
+// cache slot.  Cache layout: K [B][Hkv][S_max][d], V transposed [B][Hkv][d][S_max],
+// so that both operands of both products are read with the contraction axis
+// contiguous.
+//
+// * attn_prefill_mfma (bf16, d = 128): flash-style.  One workgroup per
+//   (32-query block, KV head, sequence); wave w serves query head
+//   kvh * G + w, so the G heads of a group share every K / V tile in LDS.
+//   Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
+//   which leaves each lane with one query column; the probabilities feed
+//   O^T = V^T P^T directly from registers.  Online softmax in fp32 (base 2).
+// * attn_decode_mfma (bf16, d = 128, up to 16 query columns = heads x new
+//   tokens): split-K over the cache, v_mfma_f32_16x16x32_bf16, operands read
+//   straight from the cache, then a combine kernel.
+// * attn_f32: plain kernel for the fp32 configuration.
+#include "common.h"
+#include "kernels.h"
+
+namespace lk {
+
+constexpr float LOG2E = 1.4426950408889634f;
+
+// ------------------------------------------------------------------ prefill, bf16
+constexpr int PQ = 32;    // queries per wave
+constexpr int PK = 64;    // keys per tile
+constexpr int PD = 128;   // head dim
+
+// K tile [64 keys][128 d] in 16-byte chunks, chunk c of row r at c ^ (r & 15).
+DEV int ksw(int r, int c) { return r * PD + ((c ^ (r & 15)) << 3); }
+// V^T tile [128 d][64 keys] in 8-byte units, unit u of row r at u ^ (r & 15).
+DEV int vsw(int r, int u) { return r * PK + ((u ^ (r & 15)) << 2); }
+
+template <int NTHR>
+__global__ __launch_bounds__(NTHR, 1) void attn_prefill_mfma(AttnArgs a) {
+  extern __shared__ __align__(16) bf16_t smem[];
+  const int G = a.Hq / a.Hkv;
+  constexpr int nthr = NTHR;
+  bf16_t* Ks = smem;                  // [2][PK * PD]
+  bf16_t* Vs = smem + 2 * PK * PD;    // [2][PD * PK]
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int qb = gridDim.x - 1 - blockIdx.x;   // long rows first
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int j = kvh * G + min(wid, G - 1);
+  const int q0 = qb * PQ;
+  const int h = lane >> 5, col = lane & 31;
+  const int m = q0 + col;
+  const bool qvalid = m < a.S_call;
+  const int qpos = a.pos0 + m;
+  const int kv_end = a.pos0 + min(q0 + PQ, a.S_call);
+  const int ntiles = (kv_end + PK - 1) / PK;
+
+  const bf16_t* Q = (const bf16_t*)a.q + (size_t)(b * a.S_call + min(m, a.S_call - 1)) * a.ldq + j * PD;
+  bf16x8_t qf[8];
+  if (wid < G) {
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) qf[ds] = as_bf16x8(*(const uint4*)(Q + ds * 16 + h * 8));
+  }
+
+  const bf16_t* Kg = (const bf16_t*)a.kcache + ((size_t)(b * a.Hkv + kvh) * a.S_max) * PD;
+  const bf16_t* Vg = (const bf16_t*)a.vcache + ((size_t)(b * a.Hkv + kvh) * PD) * a.S_max;
+
+  // cooperative tile load: 1024 16-byte chunks of K and 1024 of V^T
+  constexpr int per = 1024 / nthr;   // 4 (256 threads) or 2 (512 threads)
+  uint4 rk[4], rv[4];
+  auto gload = [&](int kt) {
+    const int k0 = kt * PK;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      const int cidx = tid + i * nthr;
+      const int kr = cidx >> 4, kc = cidx & 15;       // K: row (key), chunk
+      const int key = k0 + kr;
+      rk[i] = *(const uint4*)(Kg + (size_t)min(key, a.S_max - 1) * PD + kc * 8);
+      const int vr = cidx >> 3, vc = cidx & 7;        // V^T: row (d), chunk of 8 keys
+      const int key0 = k0 + vc * 8;
+      uint4 v = *(const uint4*)(Vg + (size_t)vr * a.S_max + min(key0, a.S_max - 8));
+      if (key0 + 8 > kv_end) {
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (key0 + e >= kv_end) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        v = make_uint4(w[0], w[1], w[2], w[3]);
+      }
+      rv[i] = v;
+    }
+  };
+  auto sstore = [&](int buf) {
+    bf16_t* ks = Ks + buf * PK * PD;
+    bf16_t* vs = Vs + buf * PD * PK;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+      const int cidx = tid + i * nthr;
+      const int kr = cidx >> 4, kc = cidx & 15;
+      *(uint4*)(ks + ksw(kr, kc)) = rk[i];
+      const int vr = cidx >> 3, vc = cidx & 7;
+      *(uint2*)(vs + vsw(vr, 2 * vc)) = make_uint2(rv[i].x, rv[i].y);
+      *(uint2*)(vs + vsw(vr, 2 * vc + 1)) = make_uint2(rv[i].z, rv[i].w);
+    }
+  };
+
+  f32x16_t o[4];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float mrun = -INFINITY, lrun = 0.f;
+  const float sc = LOG2E / sqrtf((float)PD);
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < ntiles) gload(kt + 1);
+    const bf16_t* ks = Ks + cur * PK * PD;
+    const bf16_t* vs = Vs + cur * PD * PK;
+    if (wid < G) {
+      f32x16_t st[2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[c][r] = 0.f;
+#pragma unroll
+        for (int ds = 0; ds < 8; ++ds) {
+          const bf16x8_t kf = as_bf16x8(*(const uint4*)(ks + ksw(c * 32 + col, ds * 2 + h)));
+          st[c] = mfma32(kf, qf[ds], st[c]);
+        }
+      }
+      // st[c][r]: key kt*64 + c*32 + (r/4)*8 + h*4 + r%4, query column `col`
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt * PK + c * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+          const float v = (key <= qpos && key < kv_end) ? st[c][r] * sc : -INFINITY;
+          st[c][r] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mnew = fmaxf(mrun, tmax);
+      const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
+      float psum = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = (mnew == -INFINITY) ? 0.f : exp2f(st[c][r] - mnew);
+          st[c][r] = p;
+          psum += p;
+        }
+      lrun = lrun * alpha + psum;
+      mrun = mnew;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        const int c = mm >> 1, half = mm & 1;
+        uint32_t pw[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          pw[e] = (uint32_t)f2bf(st[c][half * 8 + 2 * e]) | ((uint32_t)f2bf(st[c][half * 8 + 2 * e + 1]) << 16);
+        const bf16x8_t pf = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+        const int kbase = c * 32 + half * 16 + h * 4;   // keys kbase+0..3 and kbase+8..11
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const int r = db * 32 + col;
+          const uint2 lo = *(const uint2*)(vs + vsw(r, kbase >> 2));
+          const uint2 hi = *(const uint2*)(vs + vsw(r, (kbase + 8) >> 2));
+          o[db] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pf, o[db]);
+        }
+      }
+    }
+    if (kt + 1 < ntiles) sstore(cur ^ 1);
+    __syncthreads();
+  }
+  if (wid < G && qvalid) {
+    const float ltot = lrun + __shfl_xor(lrun, 32, 64);
+    const float inv = 1.0f / ltot;
+    bf16_t* O = (bf16_t*)a.out + (size_t)(b * a.S_call + m) * a.ldo + j * PD;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + g4 * 8 + h * 4;
+        const uint32_t w0 = (uint32_t)f2bf(o[db][g4 * 4] * inv) | ((uint32_t)f2bf(o[db][g4 * 4 + 1] * inv) << 16);
+        const uint32_t w1 = (uint32_t)f2bf(o[db][g4 * 4 + 2] * inv) | ((uint32_t)f2bf(o[db][g4 * 4 + 3] * inv) << 16);
+        *(uint2*)(O + d0) = make_uint2(w0, w1);
+      }
+  }
+}
+
+// ------------------------------------------------------------------ decode, bf16
+// One wave per (split, KV head, sequence).  Query columns c < ncol are
+// (token t = c / G, head kvh*G + c % G).  A round covers 64 keys: four S^T
+// blocks of 16 keys whose rows are ordered so that, for PV step kk, lane group
+// g holds the probabilities of keys 32kk + 8g + 0..7, matching a contiguous
+// 16-byte read of V^T.
+__global__ __launch_bounds__(64) void attn_decode_mfma(AttnArgs a) {
+  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int G = a.Hq / a.Hkv;
+  const int ncol = G * a.S_call;
+  const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
+  const bool cvalid = c < ncol;
+  const int tq = cvalid ? c / G : 0, jq = kvh * G + (cvalid ? c % G : 0);
+  const int kv_len = a.pos0 + a.S_call;           // keys [0, kv_len) exist
+  const int lim = a.pos0 + tq + 1;                 // visible to this column
+  const int k_begin = s * a.split_len;
+  const int k_end = min(k_begin + a.split_len, kv_len);
+
+  const bf16_t* Q = (const bf16_t*)a.q + (size_t)(b * a.S_call + tq) * a.ldq + jq * PD;
+  bf16x8_t qf[4];
+  const uint4 zero = make_uint4(0, 0, 0, 0);
+#pragma unroll
+  for (int ds = 0; ds < 4; ++ds) qf[ds] = as_bf16x8(cvalid ? *(const uint4*)(Q + ds * 32 + g * 8) : zero);
+
+  const bf16_t* Kg = (const bf16_t*)a.kcache + ((size_t)(b * a.Hkv + kvh) * a.S_max) * PD;
+  const bf16_t* Vg = (const bf16_t*)a.vcache + ((size_t)(b * a.Hkv + kvh) * PD) * a.S_max;
+  const float sc = LOG2E / sqrtf((float)PD);
+
+  f32x4_t o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float mrun = -INFINITY, lrun = 0.f;
+
+  for (int k0 = k_begin; k0 < k_end; k0 += 64) {
+    f32x4_t st[4];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      st[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const int key = k0 + 32 * (sb >> 1) + (c >> 2) * 8 + (sb & 1) * 4 + (c & 3);
+      const bf16_t* kr = Kg + (size_t)key * PD + g * 8;
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) st[sb] = mfma16(as_bf16x8(*(const uint4*)(kr + ds * 32)), qf[ds], st[sb]);
+    }
+    // st[sb][i]: column c, key k0 + 32*(sb/2) + 8g + 4*(sb%2) + i
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = k0 + 32 * (sb >> 1) + 8 * g + 4 * (sb & 1) + i;
+        const float v = (key < lim && key < k_end) ? st[sb][i] * sc : -INFINITY;
+        st[sb][i] = v;
+        tmax = fmaxf(tmax, v);
+      }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float mnew = fmaxf(mrun, tmax);
+    const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
+    float psum = 0.f;
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = (mnew == -INFINITY) ? 0.f : exp2f(st[sb][i] - mnew);
+        st[sb][i] = p;
+        psum += p;
+      }
+    lrun = lrun * alpha + psum;
+    mrun = mnew;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) o[db] *= alpha;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      uint32_t pw[4];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        pw[e] = (uint32_t)f2bf(st[2 * kk][2 * e]) | ((uint32_t)f2bf(st[2 * kk][2 * e + 1]) << 16);
+        pw[2 + e] = (uint32_t)f2bf(st[2 * kk + 1][2 * e]) | ((uint32_t)f2bf(st[2 * kk + 1][2 * e + 1]) << 16);
+      }
+      const bf16x8_t pf = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      const int key0 = k0 + 32 * kk + 8 * g;
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        uint4 v = *(const uint4*)(Vg + (size_t)(db * 16 + c) * a.S_max + key0);
+        if (key0 + 8 > k_end) {
+          uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (key0 + e >= k_end) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+          v = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+        o[db] = mfma16(as_bf16x8(v), pf, o[db]);
+      }
+    }
+  }
+  // partial row sums of a column live in 4 lane groups
+  float ltot = lrun + __shfl_xor(lrun, 16, 64);
+  ltot += __shfl_xor(ltot, 32, 64);
+  if (cvalid) {
+    float* P = a.part + ((((size_t)(b * a.S_call + tq) * a.Hq + jq) * a.n_split) + s) * (PD + 2);
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+      *(float4*)(P + db * 16 + g * 4) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
+    if (g == 0) { P[PD] = mrun; P[PD + 1] = ltot; }
+  }
+}
+
+// out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
+template <typename T>
+__global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
+  const int row = blockIdx.x;                   // (b * S_call + t) * Hq + j
+  const int dd = threadIdx.x;
+  const float* P = a.part + (size_t)row * a.n_split * (a.d + 2);
+  float M = -INFINITY;
+  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, P[s * (a.d + 2) + a.d]);
+  float L = 0.f, acc = 0.f;
+  for (int s = 0; s < a.n_split; ++s) {
+    const float ms = P[s * (a.d + 2) + a.d];
+    const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+    L += P[s * (a.d + 2) + a.d + 1] * w;
+    if (dd < a.d) acc += P[s * (a.d + 2) + dd] * w;
+  }
+  const int tok = row / a.Hq, j = row % a.Hq;
+  if (dd < a.d) st1((T*)a.out + (size_t)tok * a.ldo + j * a.d + dd, acc / L);
+}
+
+// ------------------------------------------------------------------ fp32
+// One thread per (query, head); keys in order; online softmax.  Writes either
+// the final output (n_split == 0) or split partials in the decode layout.
+template <int D>
+__global__ __launch_bounds__(64) void attn_f32(AttnArgs a) {
+  const int t = blockIdx.x * 64 + threadIdx.x;
+  const int j = blockIdx.y, b = blockIdx.z;
+  if (t >= a.S_call) return;
+  const int G = a.Hq / a.Hkv, kvh = j / G;
+  const float* q = (const float*)a.q + (size_t)(b * a.S_call + t) * a.ldq + j * D;
+  const float* K = (const float*)a.kcache + ((size_t)(b * a.Hkv + kvh) * a.S_max) * D;
+  const float* V = (const float*)a.vcache + ((size_t)(b * a.Hkv + kvh) * D) * a.S_max;
+  float qr[D], o[D];
+  const float sc = 1.0f / sqrtf((float)D);
+#pragma unroll
+  for (int i = 0; i < D; ++i) { qr[i] = q[i]; o[i] = 0.f; }
+  float m = -INFINITY, l = 0.f;
+  const int last = a.pos0 + t;
+  for (int key = 0; key <= last; ++key) {
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) s += qr[i] * K[(size_t)key * D + i];
+    s *= sc;
+    const float mn = fmaxf(m, s);
+    const float al = expf(m - mn), p = expf(s - mn);
+    l = l * al + p;
+#pragma unroll
+    for (int i = 0; i < D; ++i) o[i] = o[i] * al + p * V[(size_t)i * a.S_max + key];
+    m = mn;
+  }
+  float* out = (float*)a.out + (size_t)(b * a.S_call + t) * a.ldo + j * D;
+#pragma unroll
+  for (int i = 0; i < D; ++i) out[i] = o[i] / l;
+}
+
+static hipError_t launch_f32(const AttnArgs& a, hipStream_t s) {
+  dim3 grid((a.S_call + 63) / 64, a.Hq, a.B);
+  if (a.d == 64) attn_f32<64><<<grid, 64, 0, s>>>(a);
+  else if (a.d == 128) attn_f32<128><<<grid, 64, 0, s>>>(a);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t attn_prefill(const AttnArgs& a, hipStream_t s) {
+  if (a.S_call <= 0 || a.B <= 0) return hipSuccess;
+  if (a.dt == DT_F32) return launch_f32(a, s);
+  const int G = a.Hq / a.Hkv;
+  if (a.d != PD || G < 1 || G > 8 || a.Hq % a.Hkv || a.S_max % 64) return hipErrorInvalidValue;
+  const int threads = G <= 4 ? 256 : 512;
+  const int lds = 2 * 2 * PK * PD * 2;   // 64 KB
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_mfma<256>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)attn_prefill_mfma<512>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  dim3 grid((a.S_call + PQ - 1) / PQ, a.Hkv, a.B);
+  if (threads == 256) attn_prefill_mfma<256><<<grid, 256, lds, s>>>(a);
+  else attn_prefill_mfma<512><<<grid, 512, lds, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t attn_decode(const AttnArgs& a, hipStream_t s) {
+  if (a.S_call <= 0 || a.B <= 0) return hipSuccess;
+  if (a.dt == DT_F32) return launch_f32(a, s);
+  const int G = a.Hq / a.Hkv;
+  if (a.d != PD || a.Hq % a.Hkv || G * a.S_call > 16 || a.S_max % 64 || a.split_len % 64) return hipErrorInvalidValue;
+  const int kv_len = a.pos0 + a.S_call;
+  if ((long)a.n_split * a.split_len < kv_len) return hipErrorInvalidValue;
+  dim3 grid(a.n_split, a.Hkv, a.B);
+  attn_decode_mfma<<<grid, 64, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  attn_combine<bf16_t><<<a.B * a.S_call * a.Hq, 128, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace lk

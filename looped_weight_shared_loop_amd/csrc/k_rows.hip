@@ -1,0 +1,290 @@
+// Row kernels: embedding gather, residual add + RMSNorm outside the looped
+// block, and the fused two-stream hyper-connection (mHC) transition inside it.
+#include "common.h"
+#include "kernels.h"
+
+namespace lk {
+
+// ------------------------------------------------------------------ embed
+template <typename T>
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
+                                                    const T* __restrict__ table, int vocab, int C,
+                                                    T* __restrict__ h, uint32_t* err) {
+  const int r = blockIdx.x;
+  int tok = tokens[r];
+  if (tok < 0 || tok >= vocab) {
+    if (threadIdx.x == 0) atomicOr(err, 1u);
+    tok = 0;
+  }
+  const T* src = table + (size_t)tok * C;
+  T* dst = h + (size_t)r * C;
+  for (int i = threadIdx.x * 8; i < C; i += blockDim.x * 8) {
+    float v[8];
+    ld8(src + i, v);
+    st8(dst + i, v);
+  }
+}
+
+hipError_t embed(int dt, const int32_t* tokens, const void* table, int vocab, int C, int T,
+                 void* h, uint32_t* err, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  if (dt == DT_BF16)
+    embed_kernel<bf16_t><<<T, 256, 0, s>>>(tokens, (const bf16_t*)table, vocab, C, (bf16_t*)h, err);
+  else
+    embed_kernel<float><<<T, 256, 0, s>>>(tokens, (const float*)table, vocab, C, (float*)h, err);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ block sum
+// Sums NV values over the block; `red` holds [2][16 waves][NV] floats and is
+// used by token parity so one barrier per token suffices.
+template <int NV>
+DEV void block_sum(float* v, float (*red)[16][12], int par) {
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = wave_sum(v[i]);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) red[par][wid][i] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = 0.f;
+  for (int w = 0; w < nw; ++w) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) v[i] += red[par][w][i];
+  }
+}
+
+// ------------------------------------------------------------------ add + RMSNorm
+template <typename T, int MAXV>
+__global__ __launch_bounds__(256) void add_rmsnorm_kernel(NormArgs a) {
+  __shared__ float red[2][16][12];
+  const int C = a.C, nv = C / 8;
+  const T* y = (const T*)a.y;
+  T* h = (T*)a.h;
+  T* u = (T*)a.u;
+  const int r = blockIdx.x;
+  float x[MAXV][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) {
+    const int vi = threadIdx.x + k * blockDim.x;
+    if (vi < nv) {
+      ld8(h + (size_t)r * C + vi * 8, x[k]);
+      if (y) {
+        float yv[8];
+        ld8(y + (size_t)r * C + vi * 8, yv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[k][e] = round_to(x[k][e] + yv[e], (T*)nullptr);
+        st8(h + (size_t)r * C + vi * 8, x[k]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[k][e] * x[k][e];
+    }
+  }
+  float tot[1] = {ss};
+  block_sum<1>(tot, red, 0);
+  const float inv = 1.0f / sqrtf(tot[0] / (float)C + a.eps);
+#pragma unroll
+  for (int k = 0; k < MAXV; ++k) {
+    const int vi = threadIdx.x + k * blockDim.x;
+    if (vi < nv) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = a.gamma[vi * 8 + e] * x[k][e] * inv;
+      st8(u + (size_t)r * C + vi * 8, o);
+    }
+  }
+}
+
+hipError_t add_rmsnorm(const NormArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  if (a.C % 8 || a.C > 8192) return hipErrorInvalidValue;
+  const int nv = a.C / 8;
+  const int threads = nv >= 256 ? 256 : ((nv + 63) / 64) * 64;
+  if (a.dt == DT_BF16)
+    add_rmsnorm_kernel<bf16_t, 4><<<a.T, threads, 0, s>>>(a);
+  else
+    add_rmsnorm_kernel<float, 4><<<a.T, threads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ mHC
+// One thread owns 8 consecutive channels c of both streams and keeps its
+// slice of the next site's projection W (8 x 16 floats) in registers for the
+// whole persistent loop over tokens, so W is read from memory once per block.
+//
+// Per token:  X'_i = sum_j H_res[i][j] X_j + H_post[i] y   (bf16-rounded, stored)
+//             l = W vec(X') / rms(vec(X')) + b ; maps of the next site
+//             u = gamma * x_in / rms(x_in), x_in = H_pre0 X'_0 + H_pre1 X'_1
+// rms(x_in) comes from the three stream sums already reduced for l:
+//   sum x_in^2 = p0^2 S00 + 2 p0 p1 S01 + p1^2 S11.
+DEV void mhc_maps_from_logits(const float* l, int iters, float* m) {
+  m[0] = 1.0f / (1.0f + expf(-l[0]));
+  m[1] = 1.0f / (1.0f + expf(-l[1]));
+  m[2] = 2.0f / (1.0f + expf(-l[2]));
+  m[3] = 2.0f / (1.0f + expf(-l[3]));
+  const float mx = fmaxf(fmaxf(l[4], l[5]), fmaxf(l[6], l[7]));
+  float a = expf(l[4] - mx), b = expf(l[5] - mx), c = expf(l[6] - mx), d = expf(l[7] - mx);
+  for (int it = 0; it < iters; ++it) {
+    const float r0 = a + b, r1 = c + d;
+    a = a / r0; b = b / r0; c = c / r1; d = d / r1;
+    const float c0 = a + c, c1 = b + d;
+    a = a / c0; c = c / c0; b = b / c1; d = d / c1;
+  }
+  m[4] = a; m[5] = b; m[6] = c; m[7] = d;
+}
+
+template <typename T>
+__global__ __launch_bounds__(512) void mhc_kernel(MhcArgs a) {
+  __shared__ float red[2][16][12];
+  const int C = a.C, nv = C / 8;
+  const int v = threadIdx.x;
+  const bool act = v < nv;
+  const int c0 = act ? v * 8 : 0;
+  T* X = (T*)a.X;
+  T* h = (T*)a.h;
+  T* u = (T*)a.u;
+  const T* y = (const T*)a.y;
+  const int mode = a.mode;
+
+  float w[8][16];
+  float bias[8];
+  float g[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    bias[j] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) w[j][e] = 0.f;
+  }
+  if (mode != MHC_EXIT && act) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      ld8(a.w + (size_t)j * 2 * C + c0, &w[j][0]);
+      ld8(a.w + (size_t)j * 2 * C + C + c0, &w[j][8]);
+      bias[j] = a.b[j];
+    }
+  }
+  if (act) ld8(a.gamma + c0, g);
+
+  int par = 0;
+  for (int t = blockIdx.x; t < a.T; t += gridDim.x, par ^= 1) {
+    float x0[8], x1[8];
+    if (act) {
+      if (mode == MHC_ENTER) {
+        ld8(h + (size_t)t * C + c0, x0);
+        if (y) {
+          float yv[8];
+          ld8(y + (size_t)t * C + c0, yv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x0[e] = round_to(x0[e] + yv[e], (T*)nullptr);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x1[e] = x0[e];
+        st8(X + ((size_t)t * 2) * C + c0, x0);
+        st8(X + ((size_t)t * 2 + 1) * C + c0, x1);
+      } else {
+        float p[8], q[8], yv[8];
+        ld8(X + ((size_t)t * 2) * C + c0, p);
+        ld8(X + ((size_t)t * 2 + 1) * C + c0, q);
+        ld8(y + (size_t)t * C + c0, yv);
+        const float* mi = a.maps_in + (size_t)t * 8;
+        const float po0 = mi[2], po1 = mi[3], r00 = mi[4], r01 = mi[5], r10 = mi[6], r11 = mi[7];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          x0[e] = round_to(r00 * p[e] + r01 * q[e] + po0 * yv[e], (T*)nullptr);
+          x1[e] = round_to(r10 * p[e] + r11 * q[e] + po1 * yv[e], (T*)nullptr);
+        }
+        if (mode == MHC_MID) {
+          st8(X + ((size_t)t * 2) * C + c0, x0);
+          st8(X + ((size_t)t * 2 + 1) * C + c0, x1);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) { x0[e] = 0.f; x1[e] = 0.f; }
+    }
+
+    if (mode == MHC_EXIT) {
+      float hv[8];
+      float ss = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        hv[e] = round_to(0.5f * (x0[e] + x1[e]), (T*)nullptr);
+        ss += hv[e] * hv[e];
+      }
+      if (act) st8(h + (size_t)t * C + c0, hv);
+      float tot[1] = {ss};
+      block_sum<1>(tot, red, par);
+      const float inv = 1.0f / sqrtf(tot[0] / (float)C + a.eps);
+      if (act) {
+        float o[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = g[e] * hv[e] * inv;
+        st8(u + (size_t)t * C + c0, o);
+      }
+      continue;
+    }
+
+    float acc[11];
+#pragma unroll
+    for (int i = 0; i < 11; ++i) acc[i] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[0] += x0[e] * x0[e];
+      acc[1] += x1[e] * x1[e];
+      acc[2] += x0[e] * x1[e];
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s += w[j][e] * x0[e] + w[j][8 + e] * x1[e];
+      acc[3 + j] = s;
+    }
+    block_sum<11>(acc, red, par);
+    const float inv = 1.0f / sqrtf((acc[0] + acc[1]) / (float)(2 * C) + a.eps);
+    float l[8], m[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) l[j] = acc[3 + j] * inv + bias[j];
+    mhc_maps_from_logits(l, a.iters, m);
+    if (threadIdx.x == 0) {
+      float* mo = a.maps_out + (size_t)t * 8;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) mo[j] = m[j];
+    }
+    const float p0 = m[0], p1 = m[1];
+    const float ssin = p0 * p0 * acc[0] + 2.f * p0 * p1 * acc[2] + p1 * p1 * acc[1];
+    const float invu = 1.0f / sqrtf(fmaxf(ssin, 0.f) / (float)C + a.eps);
+    if (act) {
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = g[e] * (p0 * x0[e] + p1 * x1[e]) * invu;
+      st8(u + (size_t)t * C + c0, o);
+    }
+  }
+}
+
+hipError_t mhc(const MhcArgs& a, hipStream_t s) {
+  if (a.T <= 0) return hipSuccess;
+  if (a.C % 8 || a.C / 8 > 512) return hipErrorInvalidValue;
+  const int nv = a.C / 8;
+  const int threads = ((nv + 63) / 64) * 64;
+  int grid = a.grid > 0 ? a.grid : a.T;
+  if (grid > a.T) grid = a.T;
+  if (a.dt == DT_BF16)
+    mhc_kernel<bf16_t><<<grid, threads, 0, s>>>(a);
+  else
+    mhc_kernel<float><<<grid, threads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return n;
+}
+
+}  // namespace lk

@@ -1,0 +1,91 @@
+// Internal launch interface between the loop driver and the gfx950 kernels.
+// Not part of the public C ABI (that is include/loop.h).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace lk {
+
+enum Dt { DT_F32 = 0, DT_BF16 = 1 };
+
+// ---------------------------------------------------------------- row kernels
+hipError_t embed(int dt, const int32_t* tokens, const void* table, int vocab, int C, int T,
+                 void* h, uint32_t* err_word, hipStream_t s);
+
+// h <- h + y (if y), u <- RMSNorm(h; gamma).  In place on h.
+struct NormArgs {
+  int dt, T, C;
+  const void* y;
+  void* h;
+  const float* gamma;
+  void* u;
+  float eps;
+};
+hipError_t add_rmsnorm(const NormArgs& a, hipStream_t s);
+
+// Fused two-stream hyper-connection transition (write-back of one site, then
+// maps, read and RMSNorm of the next site).
+enum MhcMode { MHC_ENTER = 0, MHC_MID = 1, MHC_EXIT = 2 };
+struct MhcArgs {
+  int dt, mode, T, C, iters;
+  float eps;
+  const void* y;         // output of the sublayer just run (nullable on ENTER)
+  void* h;               // ENTER: residual in; EXIT: residual out
+  void* X;               // [T][2][C] streams, updated in place
+  const float* maps_in;  // [T][8] maps of the site being written back (MID, EXIT)
+  float* maps_out;       // [T][8] maps of the next site (ENTER, MID)
+  const float* w;        // [8][2C] projection of the next site (ENTER, MID)
+  const float* b;        // [8]
+  const float* gamma;    // [C] RMSNorm gain of the next sublayer
+  void* u;               // [T][C] normed input of the next sublayer
+  int grid;              // persistent grid size (0: one block per token)
+};
+hipError_t mhc(const MhcArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- GEMM
+enum Epi { EPI_STORE = 0, EPI_F32 = 1, EPI_QKV = 2, EPI_SWIGLU = 3 };
+struct GemmArgs {
+  int dt, epi;
+  int M, N, K;          // C[M, N] = A[M, K] . B[N, K]^T; SWIGLU: N = 2F B rows, F outputs
+  const void* A; long lda;
+  const void* B; long ldb;
+  void* C; long ldc;
+  // EPI_QKV: columns [0, q_cols) -> C; [q_cols, q_cols + kv) -> K cache; then V cache
+  int q_cols, n_kv, head_dim;
+  void* kcache;          // [B][Hkv][S_max][d]
+  void* vcache;          // [B][Hkv][d][S_max] (transposed)
+  int S_call, pos0, S_max;  // row m is sequence m / S_call at position pos0 + m % S_call
+  int F;                 // EPI_SWIGLU: up rows start at row F of B
+};
+hipError_t gemm(const GemmArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- attention
+struct AttnArgs {
+  int dt, B, S_call, pos0, S_max, Hq, Hkv, d;
+  const void* q; long ldq;         // token m: q + m * ldq, head j at + j * d
+  const void* kcache;              // [B][Hkv][S_max][d]
+  const void* vcache;              // [B][Hkv][d][S_max]
+  void* out; long ldo;             // token m: out + m * ldo, head j at + j * d
+  float* part; int n_split, split_len;   // decode: [B][Hq][n_split][d + 2] fp32
+};
+hipError_t attn_prefill(const AttnArgs& a, hipStream_t s);
+hipError_t attn_decode(const AttnArgs& a, hipStream_t s);
+
+// ---------------------------------------------------------------- linear attention
+struct LinArgs {
+  int dt, B, S_call, Hq, Hkv, d;
+  float eps;
+  const void* qkv; long ld;        // q at column 0, k at Hq*d, v at (Hq+Hkv)*d
+  float* S; float* z;              // [B][Hkv][d][d], [B][Hkv][d] fp32
+  int init_zero;                   // treat the incoming state as zero
+  void* out; long ldo;
+  float* scratch; int chunk;       // prefill: [B*Hkv][n_chunk][d*d + d]
+};
+hipError_t lin_prefill(const LinArgs& a, hipStream_t s);
+hipError_t lin_decode(const LinArgs& a, hipStream_t s);
+size_t lin_scratch_floats(int B, int Hkv, int d, int S_call, int chunk);
+
+int device_cu_count();
+
+}  // namespace lk

@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point
+include/loop.h declares, and rejects bad configurations before touching a
+device.  No compute call is made (no GPU here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "loop.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(loop_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("loop_model_create", "loop_prefill", "loop_decode_step", "loop_state_bytes",
+              "loop_workspace_bytes", "loop_state_create", "loop_last_error"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    from looped_weight_shared_loop_amd import _abi
+    lib = ctypes.CDLL(_abi.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing
+    assert set(_declared()) == set(_abi.SYMBOLS), "binding and header disagree"
+
+
+def test_synth_library_exports():
+    from synth import device
+    lib = ctypes.CDLL(device.LIB_PATH)
+    assert hasattr(lib, "synth_fill_normal4") and hasattr(lib, "synth_fill_uniform_int")
+
+
+def _cfg(**kw):
+    from looped_weight_shared_loop_amd import ModelConfig
+    base = dict(vocab=512, hidden=256, ffn=768, n_heads=4, n_kv_heads=4, head_dim=64, n_layers=8,
+                loop_start=2, loop_end=6, dtype="fp32")
+    base.update(kw)
+    return ModelConfig(**base)
+
+
+def _create(cfg, n_layers=None):
+    from looped_weight_shared_loop_amd import _abi as A
+    layers = (A.loop_layer_weights * cfg.n_layers)()
+    w = A.loop_weights(16, 16, 16, ctypes.cast(layers, ctypes.POINTER(A.loop_layer_weights)),
+                       cfg.n_layers if n_layers is None else n_layers)
+    return A.loop_model_create(cfg.to_c(), w)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(loop_start=5, loop_end=3), -1),
+    (dict(loop_end=9), -1),
+    (dict(n_passes=0), -1),
+    (dict(attn_period=0), -1),
+    (dict(rms_eps=0.0), -1),
+    (dict(n_kv_heads=3), -2),
+    (dict(n_heads=32, n_kv_heads=2), -2),
+    (dict(hidden=260), -2),
+    (dict(hidden=8192), -2),
+    (dict(head_dim=96), -2),
+    (dict(dtype="bf16"), -2),                 # bf16 needs head_dim 128
+    (dict(dtype="bf16", head_dim=128, hidden=200), -2),
+])
+def test_create_rejects_bad_configs(kw, code):
+    from looped_weight_shared_loop_amd import LoopError
+    with pytest.raises(LoopError) as e:
+        _create(_cfg(**kw))
+    assert e.value.code == code
+
+
+def test_create_layer_count_mismatch():
+    from looped_weight_shared_loop_amd import LoopError
+    with pytest.raises(LoopError) as e:
+        _create(_cfg(), n_layers=7)
+    assert e.value.code == -1
+
+
+def test_create_without_device_reports_no_device():
+    torch = pytest.importorskip("torch")
+    if torch.cuda.is_available():
+        pytest.skip("a device is present")
+    from looped_weight_shared_loop_amd import LoopError
+    with pytest.raises(LoopError) as e:
+        _create(_cfg())
+    assert e.value.code == -6
+    with pytest.raises(LoopError) as e:
+        _create(_cfg(dtype="bf16", vocab=248320, hidden=4096, ffn=12288, n_heads=32, n_kv_heads=8,
+                     head_dim=128, n_layers=32, loop_start=4, loop_end=28))
+    assert e.value.code == -6
+
+
+def test_status_strings_and_null_arguments():
+    from looped_weight_shared_loop_amd import _abi as A
+    lib = A.lib()
+    for code in range(0, -10, -1):
+        assert A.loop_status_string(code) not in ("", "unknown status")
+    assert A.loop_status_string(-42) == "unknown status"
+    assert lib.loop_model_create(None, None, None) == A.LOOP_ERR_INVALID_ARG
+    assert "null" in A.loop_last_error()
+    assert lib.loop_prefill(None, None, None, 0, None, None, 1, 1, 0, None, None) == A.LOOP_ERR_INVALID_ARG
+    assert lib.loop_decode_step(None, None, None, 0, None, 1, None, None) == A.LOOP_ERR_INVALID_ARG
+    assert lib.loop_state_bytes(None, 1, 1, None) == A.LOOP_ERR_INVALID_ARG

@@ -1,0 +1,199 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Tolerances (max over rows of ||g - r||_inf / ||r||_inf):
+  fp32 configurations  1e-5  (float32 arithmetic against the float64 oracle)
+  bf16 configurations  2e-2  (both sides round to bf16 at the same storage
+                              points; the GPU also rounds the attention
+                              probabilities to bf16 for the P.V product)
+"""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_common import build_pair, mini_bf16_config, need_gpu, rel, to_dev_tokens, tokens, torch
+
+pytestmark = pytest.mark.gpu
+
+FP32_TOL = 1e-5
+BF16_TOL = 2e-2
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+# ------------------------------------------------------------------ inputs
+def test_synth_device_matches_host():
+    need_gpu()
+    from synth import device as sd
+    t = torch.empty(3 << 20, dtype=torch.bfloat16, device="cuda")
+    sd.fill_tensor_normal(t, 0, 123, 0.02)
+    host = synth.f32_to_bf16_bits(synth.normal_f32(0, 123, (3 << 20,), 0.02))
+    got = t.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, host)
+    f = torch.empty(1 << 20, dtype=torch.float32, device="cuda")
+    sd.fill_tensor_normal(f, 2, 7, 1.0, start=12345, absval=True)
+    assert np.array_equal(f.cpu().numpy(), synth.abs_normal_f32(2, 7, (1 << 20,), 1.0, start=12345))
+    i = torch.empty(100000, dtype=torch.int32, device="cuda")
+    sd.fill_tensor_uniform_int(i, 1, synth.TID_TOKENS, 248320)
+    assert np.array_equal(i.cpu().numpy(), synth.uniform_int(1, synth.TID_TOKENS, (100000,), 248320))
+    # 4-D strided fill (transposed V layout)
+    B, H, L, d, Smax = 2, 3, 40, 8, 64
+    v = torch.zeros(B, H, d, Smax, dtype=torch.bfloat16, device="cuda")
+    sd.fill_normal4(v.data_ptr(), True, (B, H, L, d), (H * d * Smax, d * Smax, 1, Smax), 2, 99, 1.0,
+                    stream=torch.cuda.current_stream().cuda_stream)
+    ref = synth.normal_bf16_as_f32(2, 99, (B, H, L, d))
+    assert np.array_equal(v.float().cpu().numpy()[:, :, :, :L], ref.transpose(0, 1, 3, 2))
+
+
+# ------------------------------------------------------------------ tiny fp32
+@pytest.mark.parametrize("variant", ["tiny", "tiny_gqa"])
+def test_tiny_fp32_all_logits(variant):
+    ocfg = oracle.tiny_config() if variant == "tiny" else oracle.tiny_config(n_kv_heads=2)
+    model, Wo = build_pair(ocfg)
+    toks = tokens(1, 128, ocfg.vocab)
+    _say("tiny fp32", variant, "B=1 S=128")
+    ref = oracle.forward(ocfg, Wo, toks, all_logits=True)
+    st = model.new_state(1, 128)
+    got = model.prefill(st, to_dev_tokens(toks), all_logits=True)
+    torch.cuda.synchronize()
+    err = rel(got.cpu().numpy(), ref)
+    _say("rel err", err)
+    assert err < FP32_TOL
+    assert st.length == 128
+
+
+def test_tiny_fp32_decode_and_chunked():
+    ocfg = oracle.tiny_config(n_kv_heads=2)
+    model, Wo = build_pair(ocfg)
+    B, S, K = 3, 70, 5
+    toks = tokens(B, S + K, ocfg.vocab, seed=3)
+    full = oracle.forward(ocfg, Wo, toks, all_logits=True)
+    st = model.new_state(B, S + K)
+    last = model.prefill(st, to_dev_tokens(toks[:, :S]))
+    assert rel(last.cpu().numpy(), full[:, S - 1]) < FP32_TOL
+    for k in range(K):
+        d = model.decode_step(st, to_dev_tokens(toks[:, S + k]))
+        err = rel(d.cpu().numpy(), full[:, S + k])
+        _say("decode step", k, err)
+        assert err < FP32_TOL
+    # chunked prefill (the second chunk continues the first)
+    st2 = model.new_state(B, S + K)
+    a = model.prefill(st2, to_dev_tokens(toks[:, :33]), all_logits=True)
+    b = model.prefill(st2, to_dev_tokens(toks[:, 33:S]), all_logits=True, cont=True)
+    got = np.concatenate([a.cpu().numpy(), b.cpu().numpy()], axis=1)
+    assert rel(got, full[:, :S]) < FP32_TOL
+
+
+def test_tiny_fp32_hidden_out_with_embeds():
+    ocfg = oracle.tiny_config()
+    model, Wo = build_pair(ocfg)
+    emb = synth.normal_f32(1, synth.TID_EMBEDS_IN, (2, 48, ocfg.hidden))
+    ref = oracle.forward(ocfg, Wo, embeds=emb, hidden_out=True)
+    st = model.new_state(2, 48)
+    got = model.prefill(st, embeds=torch.from_numpy(emb).cuda(), hidden_out=True)
+    assert rel(got.cpu().numpy(), ref) < FP32_TOL
+
+
+# ------------------------------------------------------------------ bf16 (MFMA kernels)
+def test_mini_bf16_prefill_decode():
+    ocfg = mini_bf16_config()
+    model, Wo = build_pair(ocfg)
+    B, S, K = 2, 100, 3
+    toks = tokens(B, S + K, ocfg.vocab, seed=5)
+    _say("mini bf16 B=2 S=100")
+    ost = oracle.State()
+    ref = oracle.forward(ocfg, Wo, toks[:, :S], state=ost, all_logits=True)
+    st = model.new_state(B, 256)
+    got = model.prefill(st, to_dev_tokens(toks[:, :S]), all_logits=True)
+    err = rel(got.cpu().numpy(), ref)
+    _say("prefill rel err", err)
+    assert err < BF16_TOL
+    for k in range(K):
+        r = oracle.forward(ocfg, Wo, toks[:, S + k:S + k + 1], state=ost)
+        g = model.decode_step(st, to_dev_tokens(toks[:, S + k]))
+        err = rel(g.cpu().numpy(), r)
+        _say("decode", k, err)
+        assert err < BF16_TOL
+
+
+def test_mini_bf16_deterministic_and_looped_equals_unrolled():
+    """Same inputs give bitwise-identical logits; and the looped model equals
+    the unrolled one whose repeated layers point at the same weights."""
+    L = need_gpu()
+    ocfg = mini_bf16_config()
+    gcfg = L.ModelConfig(**vars_of(ocfg))
+    W = L.random_weights(gcfg, 0)
+    model = L.LoopModel(gcfg, W)
+    toks = to_dev_tokens(tokens(2, 90, ocfg.vocab, seed=6))
+    st = model.new_state(2, 128)
+    a = model.prefill(st, toks, all_logits=True).clone()
+    b = model.prefill(st, toks, all_logits=True).clone()
+    assert torch.equal(a, b)
+    ucfg = L.ModelConfig(**{**vars_of(ocfg), "n_layers": 12, "loop_start": 2, "loop_end": 10, "n_passes": 1})
+    Wu = {"embed": W["embed"], "head": W["head"], "final_norm": W["final_norm"]}
+    for j in range(12):
+        src = j if j < 2 else (2 + (j - 2) % 4 if j < 10 else j - 4)
+        for k, v in W.items():
+            if k.startswith(f"layers.{src}."):
+                Wu[f"layers.{j}." + k.split(".", 2)[2]] = v
+    un = L.LoopModel(ucfg, Wu)
+    stu = un.new_state(2, 128)
+    c = un.prefill(stu, toks, all_logits=True)
+    assert torch.equal(a, c)
+    # decode continues bitwise-equal (one cache per (layer, pass))
+    nt = to_dev_tokens(tokens(2, 1, ocfg.vocab, seed=7)[:, 0])
+    assert torch.equal(model.decode_step(st, nt), un.decode_step(stu, nt))
+
+
+def vars_of(ocfg):
+    return dict(vocab=ocfg.vocab, hidden=ocfg.hidden, ffn=ocfg.ffn, n_heads=ocfg.n_heads,
+                n_kv_heads=ocfg.n_kv_heads, head_dim=ocfg.head_dim, n_layers=ocfg.n_layers,
+                loop_start=ocfg.loop_start, loop_end=ocfg.loop_end, n_passes=ocfg.n_passes,
+                sinkhorn_iters=ocfg.sinkhorn_iters, attn_period=ocfg.attn_period, rms_eps=ocfg.rms_eps,
+                la_eps=ocfg.la_eps, dtype=ocfg.dtype)
+
+
+def test_group_9b_width_hidden_out():
+    """One [linear x3, full] group at hidden 4096 / FFN 12288 / 32q-8kv x 128,
+    looped twice under two-stream mHC, inputs N(0, 1), at a reduced length."""
+    ocfg = oracle.group_config()
+    S = 200
+    _say("group 9B width S=", S)
+    model, Wo = build_pair(ocfg, cache_layers=4)
+    emb = synth.normal_bf16_as_f32(1, synth.TID_EMBEDS_IN, (1, S, ocfg.hidden))
+    ref = oracle.forward(ocfg, Wo, embeds=emb, hidden_out=True)
+    st = model.new_state(1, S)
+    got = model.prefill(st, embeds=torch.from_numpy(emb).to(torch.bfloat16).cuda(), hidden_out=True)
+    err = rel(got.float().cpu().numpy(), ref)
+    _say("group rel err", err)
+    assert err < BF16_TOL
+
+
+# ------------------------------------------------------------------ error paths
+def test_error_paths():
+    L = need_gpu()
+    ocfg = oracle.tiny_config()
+    model, _ = build_pair(ocfg)
+    st = model.new_state(2, 64)
+    with pytest.raises(L.LoopError) as e:
+        model.decode_step(st, to_dev_tokens(np.zeros(2, np.int32)))
+    assert e.value.code == -9
+    with pytest.raises(L.LoopError) as e:
+        model.prefill(st, to_dev_tokens(np.zeros((2, 65), np.int32)))
+    assert e.value.code == -4
+    with pytest.raises(L.LoopError) as e:
+        model.prefill(st, to_dev_tokens(np.zeros((3, 8), np.int32)))
+    assert e.value.code == -4
+    assert st.length == 0
+    bad = np.zeros((2, 8), np.int32)
+    bad[1, 3] = ocfg.vocab + 5
+    model.prefill(st, to_dev_tokens(bad))
+    with pytest.raises(L.LoopError) as e:
+        st.check()
+    assert e.value.code == -8
+    st.check()   # cleared
