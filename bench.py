@@ -1,0 +1,268 @@
+"""Throughput of the looped decoder forward pass on one MI355X.
+
+A step is one prefill of the Loop-9B-shaped model (32 stored layers, block
+[4, 28) run twice: 56 layer executions; hidden 4096, FFN 12288, 32 q / 8 kv
+heads of 128, vocabulary 248,320) over B=1, S=32,768 synthetic token ids,
+through every step of the path (embed, 56 executions with two-stream mHC,
+linear and full attention, SwiGLU, final norm, head on the last position).
+The same run also times a decode step of B=32 sequences holding 32,768
+pre-filled positions each, the dominant kernel on its own (HIP events on the
+stream it runs on), and the CPU oracle on a bounded sample.
+
+Prints ONE JSON line.  Inputs and weights are synthetic random-init values
+already resident in HBM when a timed region starts.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "looped-decoder tokens/sec (56 layer execs, 9B shape): prefill + decode; % roofline"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+NINE_B = dict(vocab=248320, hidden=4096, ffn=12288, n_heads=32, n_kv_heads=8, head_dim=128,
+              n_layers=32, loop_start=4, loop_end=28, n_passes=2, dtype="bf16")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def prefill_flops(cfg, S, B=1):
+    """Algorithmic FLOPs of one prefill: 2 * params * tokens for every GEMM
+    execution, 2 S^2 d Hq per causal full-attention execution (QK^T and PV,
+    causal half), the recurrent linear-attention cost (per token per
+    execution: S update 2 d^2 Hkv, readout 2 d^2 Hq, normaliser ~2 d (Hq+Hkv)),
+    and the head on the emitted rows."""
+    C, F, d, Hq, Hkv = cfg["hidden"], cfg["ffn"], cfg["head_dim"], cfg["n_heads"], cfg["n_kv_heads"]
+    per_layer = (Hq + 2 * Hkv) * d * C + C * Hq * d + 2 * F * C + C * F
+    n_exec = cfg["loop_start"] + cfg["n_passes"] * (cfg["loop_end"] - cfg["loop_start"]) + \
+        (cfg["n_layers"] - cfg["loop_end"])
+    n_full = 0
+    for i in list(range(cfg["loop_start"])) + list(range(cfg["loop_start"], cfg["loop_end"])) * cfg["n_passes"] + \
+            list(range(cfg["loop_end"], cfg["n_layers"])):
+        n_full += (i % 4 == 3)
+    T = B * S
+    gemm = 2.0 * per_layer * T * n_exec
+    attn = n_full * B * 2.0 * S * S * d * Hq
+    lin = (n_exec - n_full) * T * (2.0 * d * d * Hkv + 2.0 * d * d * Hq + 2.0 * d * (Hq + Hkv))
+    head = 2.0 * cfg["vocab"] * C * B
+    return gemm + attn + lin + head, gemm, attn, lin
+
+
+def decode_bytes(cfg, B, ctx):
+    """Bytes one decode step must move: every layer execution's weights (the
+    shared block twice), the head, every KV cache (K and V of `ctx` positions),
+    every linear state read and written."""
+    C, F, d, Hq, Hkv, V = cfg["hidden"], cfg["ffn"], cfg["head_dim"], cfg["n_heads"], cfg["n_kv_heads"], cfg["vocab"]
+    per_layer = ((Hq + 2 * Hkv) * d * C + C * Hq * d + 2 * F * C + C * F) * 2
+    n_exec, n_full = 56, 14
+    w = per_layer * n_exec + V * C * 2
+    kv = n_full * B * Hkv * ctx * d * 2 * 2
+    lin = (n_exec - n_full) * B * Hkv * (d * d + d) * 4 * 2
+    return w + kv + lin, w, kv, lin
+
+
+def time_prefill(L, torch, model, S, steps, warmup):
+    import synth
+    from synth import device as sd
+    st = model.new_state(1, S)
+    toks = torch.empty(1, S, dtype=torch.int32, device="cuda")
+    sd.fill_tensor_uniform_int(toks, 1, synth.TID_TOKENS, model.cfg.vocab)
+    model.workspace(1, S, S)
+    for i in range(warmup):
+        model.prefill(st, toks)
+        torch.cuda.synchronize()
+        log(f"prefill warmup {i + 1}/{warmup} done")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        out = model.prefill(st, toks)
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / steps
+    log(f"prefill: {ms:.1f} ms/step (events), wall {wall / steps * 1e3:.1f} ms/step")
+    st.check()
+    assert torch.isfinite(out).all().item()
+    st.close()
+    return ms
+
+
+def time_dominant_gemm(L, torch, S, iters=10):
+    """The SwiGLU gate/up projection at the prefill shape: M = 32768 tokens,
+    N = 2 x 12288 weight rows, K = 4096 (the largest GEMM, 44% of the FLOPs)."""
+    from looped_weight_shared_loop_amd import _abi as A
+    from synth import device as sd
+    M, F, K = S, NINE_B["ffn"], NINE_B["hidden"]
+    a = torch.empty(M, K, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty(2 * F, K, dtype=torch.bfloat16, device="cuda")
+    c = torch.empty(M, F, dtype=torch.bfloat16, device="cuda")
+    sd.fill_tensor_normal(a, 3, 1, 1.0)
+    sd.fill_tensor_normal(b, 3, 2, 0.02)
+    stream = torch.cuda.current_stream().cuda_stream
+    for _ in range(2):
+        A.loop_op_gemm(A.LOOP_BF16, A.LOOP_EPI_SWIGLU, M, 2 * F, K, a.data_ptr(), K, b.data_ptr(), K, c.data_ptr(),
+                       F, F, stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        A.loop_op_gemm(A.LOOP_BF16, A.LOOP_EPI_SWIGLU, M, 2 * F, K, a.data_ptr(), K, b.data_ptr(), K, c.data_ptr(),
+                       F, F, stream)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    flops = 2.0 * M * 2 * F * K
+    log(f"gate/up GEMM: {ms:.3f} ms/launch, {flops / ms / 1e9:.1f} TFLOP/s")
+    del a, b, c
+    return ms, flops
+
+
+def time_decode(L, torch, model, B, ctx, steps, warmup):
+    import synth
+    from synth import device as sd
+    from looped_weight_shared_loop_amd import _abi as A
+    st = model.new_state(B, ctx + warmup + steps + 1)
+    cfg = model.cfg
+    Hkv, d = cfg.n_kv_heads, cfg.head_dim
+    S_max = (st.max_seq + 63) // 64 * 64
+    stream = torch.cuda.current_stream().cuda_stream
+    sched = model.schedule()
+    n_full = sum(1 for e in sched if e[2] == 1)
+    n_lin = len(sched) - n_full
+    for slot in range(n_full):      # K [B][Hkv][S_max][d], V^T [B][Hkv][d][S_max], positions < ctx
+        kp, _ = st.region(A.REGION_K, slot)
+        vp, _ = st.region(A.REGION_VT, slot)
+        sd.fill_normal4(kp, True, (B, Hkv, ctx, d), (Hkv * S_max * d, S_max * d, d, 1), 2, synth.tid_kv(slot, "k"),
+                        1.0, stream=stream)
+        sd.fill_normal4(vp, True, (B, Hkv, ctx, d), (Hkv * d * S_max, d * S_max, 1, S_max), 2,
+                        synth.tid_kv(slot, "v"), 1.0, stream=stream)
+    for slot in range(n_lin):
+        sp, _ = st.region(A.REGION_S, slot)
+        zp, _ = st.region(A.REGION_Z, slot)
+        sd.fill_normal4(sp, False, (1, 1, 1, B * Hkv * d * d), (0, 0, 0, 1), 2, synth.tid_linstate(slot, "S"), 1.0,
+                        stream=stream)
+        sd.fill_normal4(zp, False, (1, 1, 1, B * Hkv * d), (0, 0, 0, 1), 2, synth.tid_linstate(slot, "z"), 1.0,
+                        absval=True, stream=stream)
+    st.set_length(ctx)
+    toks = torch.empty(warmup + steps, B, dtype=torch.int32, device="cuda")
+    sd.fill_tensor_uniform_int(toks, 1, synth.TID_TOKENS + 100, cfg.vocab)
+    model.workspace(B, B, st.max_seq)
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        model.decode_step(st, toks[i])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        out = model.decode_step(st, toks[warmup + i])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    st.check()
+    assert torch.isfinite(out).all().item()
+    log(f"decode B={B} ctx={ctx}: {ms:.2f} ms/step")
+    st.close()
+    return ms
+
+
+def cpu_baseline(seq=128):
+    """The oracle as it stands, on host cores, on a bounded sample: one 4-layer
+    group [linear x3, full] at full 9B width looped twice (8 of the 56 layer
+    executions) over `seq` tokens; scaled to a 56-execution tokens/s."""
+    import numpy as np
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 0) for i in threadpool_info()] or [os.cpu_count()])
+    except Exception:
+        cores = len(os.sched_getaffinity(0))
+    cfg = oracle.group_config()
+    W = oracle.make_weights(cfg, 0, cache_layers=4)
+    for i in range(cfg.n_layers):
+        W.layer(i)                          # generate outside the timed region
+    emb = synth.normal_bf16_as_f32(1, synth.TID_EMBEDS_IN, (1, seq, cfg.hidden))
+    t0 = time.perf_counter()
+    oracle.forward(cfg, W, embeds=emb, hidden_out=True)
+    dt = time.perf_counter() - t0
+    per_token_56 = dt / seq * 56.0 / 8.0
+    log(f"oracle sample: {dt:.1f} s for {seq} tokens x 8 executions")
+    return {"value": round(1.0 / per_token_56, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"float64 oracle, one 9B-width group [lin,lin,lin,full] looped twice (8 of 56 executions), "
+                      f"B=1 S={seq}, {dt:.1f} s; scaled by 8/56 to the 56-execution model (head excluded)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--seq", type=int, default=32768)
+    ap.add_argument("--decode-batch", type=int, default=32)
+    ap.add_argument("--decode-ctx", type=int, default=32768)
+    ap.add_argument("--decode-steps", type=int, default=16)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-seq", type=int, default=128)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only (no cross-GPU path); run with --gpus 1", flush=True)
+        sys.exit(2)
+
+    import torch
+    import looped_weight_shared_loop_amd as L
+
+    cfg = L.ModelConfig(**NINE_B)
+    log("generating random-init 9B-shape weights on the device")
+    model = L.LoopModel(cfg, L.random_weights(cfg, 0))
+    torch.cuda.synchronize()
+
+    S = args.seq
+    ms = time_prefill(L, torch, model, S, args.steps, args.warmup)
+    flops, gemm_f, attn_f, lin_f = prefill_flops(NINE_B, S)
+    tok_s = S / (ms / 1e3)
+    tflops = flops / (ms / 1e3) / 1e12
+
+    g_ms, g_flops = time_dominant_gemm(L, torch, S)
+    g_tflops = g_flops / (g_ms / 1e3) / 1e12
+
+    result = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"Loop-9B-shape looped prefill (56 layer executions, 14 full-attention), "
+                               f"B=1, S={S}, last-position logits", "batch": 1, "seq_len": S},
+        "prefill": {"tflops": round(tflops, 1), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                    "algorithmic_tflop": round(flops / 1e12, 2), "gemm_tflop": round(gemm_f / 1e12, 2),
+                    "attention_tflop": round(attn_f / 1e12, 2), "linear_tflop": round(lin_f / 1e12, 3)},
+        "roofline": {"kernel": "gemm_mfma_kernel (SwiGLU gate/up, M=%d N=24576 K=4096)" % S, "bound": "mfma",
+                     "achieved": round(g_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "avg_launch_ms": round(g_ms, 4)},
+    }
+    if not args.no_decode:
+        dms = time_decode(L, torch, model, args.decode_batch, args.decode_ctx, args.decode_steps, 3)
+        tot, w, kv, lin = decode_bytes(NINE_B, args.decode_batch, args.decode_ctx)
+        gbs = tot / (dms / 1e3) / 1e9
+        result["decode"] = {"tokens_per_s": round(args.decode_batch / (dms / 1e3), 1), "ms_per_step": round(dms, 3),
+                            "batch": args.decode_batch, "context": args.decode_ctx,
+                            "algorithmic_gb_per_step": round(tot / 1e9, 2), "achieved_gbs": round(gbs, 1),
+                            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seq)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

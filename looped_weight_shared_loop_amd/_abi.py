@@ -75,7 +75,25 @@ SYMBOLS = {
     "loop_decode_step": (c_int, [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_int, c_void_p, c_void_p]),
     "loop_status_string": (ctypes.c_char_p, [c_int]),
     "loop_last_error": (ctypes.c_char_p, []),
+    # op level (include/loop_ops.h)
+    "loop_op_gemm": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, ctypes.c_long, c_void_p, ctypes.c_long,
+                             c_void_p, ctypes.c_long, c_int, c_void_p]),
+    "loop_op_add_rmsnorm": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p]),
+    "loop_op_mhc": (c_int, [c_int, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
+                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+    "loop_op_attention": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, ctypes.c_long,
+                                  c_void_p, c_void_p, c_void_p, ctypes.c_long, c_void_p]),
+    "loop_op_attention_decode_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
+    "loop_op_attention_decode": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p,
+                                         ctypes.c_long, c_void_p, c_void_p, c_void_p, ctypes.c_long, c_void_p,
+                                         c_size_t, c_void_p]),
+    "loop_op_linear_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
+    "loop_op_linear": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_void_p, ctypes.c_long,
+                               c_void_p, c_void_p, c_int, c_void_p, ctypes.c_long, c_void_p, c_size_t, c_void_p]),
 }
+
+LOOP_EPI_STORE, LOOP_EPI_F32, LOOP_EPI_SWIGLU = 0, 1, 3
+LOOP_MHC_ENTER, LOOP_MHC_MID, LOOP_MHC_EXIT = 0, 1, 2
 
 _lib = None
 
@@ -182,3 +200,48 @@ def loop_decode_step(m, st, ws_ptr: int, ws_bytes: int, tokens_ptr: int, B: int,
                      stream: int) -> None:
     _check(lib().loop_decode_step(m, st, c_void_p(ws_ptr), ws_bytes, c_void_p(tokens_ptr), B,
                                   c_void_p(logits_ptr), c_void_p(stream)), "loop_decode_step")
+
+
+# ---------------------------------------------------------------- op level
+
+def _p(x):
+    return None if x is None else c_void_p(x)
+
+
+def loop_op_gemm(dtype, epi, M, N, K, A, lda, B, ldb, C, ldc, F, stream) -> None:
+    _check(lib().loop_op_gemm(dtype, epi, M, N, K, _p(A), lda, _p(B), ldb, _p(C), ldc, F, _p(stream)), "loop_op_gemm")
+
+
+def loop_op_add_rmsnorm(dtype, T, C, y, h, gamma, u, eps, stream) -> None:
+    _check(lib().loop_op_add_rmsnorm(dtype, T, C, _p(y), _p(h), _p(gamma), _p(u), eps, _p(stream)),
+           "loop_op_add_rmsnorm")
+
+
+def loop_op_mhc(dtype, mode, T, C, iters, eps, y, h, X, maps_in, maps_out, w, b, gamma, u, stream) -> None:
+    _check(lib().loop_op_mhc(dtype, mode, T, C, iters, eps, _p(y), _p(h), _p(X), _p(maps_in), _p(maps_out), _p(w),
+                             _p(b), _p(gamma), _p(u), _p(stream)), "loop_op_mhc")
+
+
+def loop_op_attention(dtype, B, S, pos0, S_max, Hq, Hkv, d, q, ldq, k, v, out, ldo, stream) -> None:
+    _check(lib().loop_op_attention(dtype, B, S, pos0, S_max, Hq, Hkv, d, _p(q), ldq, _p(k), _p(v), _p(out), ldo,
+                                   _p(stream)), "loop_op_attention")
+
+
+def loop_op_attention_decode_bytes(B, S, Hq, d, S_max) -> int:
+    return lib().loop_op_attention_decode_bytes(B, S, Hq, d, S_max)
+
+
+def loop_op_attention_decode(dtype, B, S, pos0, S_max, Hq, Hkv, d, q, ldq, k, v, out, ldo, scratch, nbytes,
+                             stream) -> None:
+    _check(lib().loop_op_attention_decode(dtype, B, S, pos0, S_max, Hq, Hkv, d, _p(q), ldq, _p(k), _p(v), _p(out),
+                                          ldo, _p(scratch), nbytes, _p(stream)), "loop_op_attention_decode")
+
+
+def loop_op_linear_bytes(B, S, Hkv, d) -> int:
+    return lib().loop_op_linear_bytes(B, S, Hkv, d)
+
+
+def loop_op_linear(dtype, chunked, B, S, Hq, Hkv, d, eps, qkv, ld, S_state, z_state, init_zero, out, ldo, scratch,
+                   nbytes, stream) -> None:
+    _check(lib().loop_op_linear(dtype, chunked, B, S, Hq, Hkv, d, eps, _p(qkv), ld, _p(S_state), _p(z_state),
+                                init_zero, _p(out), ldo, _p(scratch), nbytes, _p(stream)), "loop_op_linear")

@@ -21,7 +21,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wno-unused-result"]
 
-LOOP_SOURCES = ["k_rows.hip", "k_gemm.hip", "k_attn.hip", "k_lin.hip", "driver.cpp"]
+LOOP_SOURCES = ["k_rows.hip", "k_gemm.hip", "k_attn.hip", "k_lin.hip", "driver.cpp", "ops.cpp"]
 
 
 def _run(cmd):

@@ -7,6 +7,8 @@ typedef uint16_t bf16_t;
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 #define DEV __device__ __forceinline__
 
@@ -67,6 +69,9 @@ DEV float wave_max(float v) {
 }
 
 DEV bf16x8_t as_bf16x8(uint4 q) { return __builtin_bit_cast(bf16x8_t, q); }
+DEV bf16x8_t as_bf16x8(u32x4_t q) { return __builtin_bit_cast(bf16x8_t, q); }
+DEV u32x4_t ldv4(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
+DEV void stv4(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 
 DEV f32x16_t mfma32(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);

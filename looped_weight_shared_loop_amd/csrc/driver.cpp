@@ -15,13 +15,14 @@
 #include <vector>
 
 #include "../../include/loop.h"
+#include "abi_util.h"
 #include "kernels.h"
 
 namespace {
-
 thread_local std::string g_err;
+}  // namespace
 
-int fail(int code, const char* fmt, ...) {
+int lp_fail(int code, const char* fmt, ...) {
   char buf[512];
   va_list ap;
   va_start(ap, fmt);
@@ -31,7 +32,9 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
-bool misaligned(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+namespace {
+
+bool misaligned(const void* p) { return lp_misaligned(p); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -98,7 +101,7 @@ WsLayout ws_layout(const loop_model* m, int batch, int max_tokens, int max_seq) 
 
 int check_hip(hipError_t e, const char* what) {
   if (e == hipSuccess) return LOOP_OK;
-  return fail(LOOP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return lp_fail(LOOP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
 }  // namespace
@@ -124,33 +127,33 @@ const char* loop_status_string(int s) {
 const char* loop_last_error(void) { return g_err.c_str(); }
 
 int loop_model_create(const loop_config* cfg, const loop_weights* w, loop_model** out) {
-  if (!cfg || !w || !out) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (!cfg || !w || !out) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
   *out = nullptr;
   const loop_config& c = *cfg;
   if (c.vocab <= 0 || c.hidden <= 0 || c.ffn <= 0 || c.n_heads <= 0 || c.n_kv_heads <= 0 ||
       c.head_dim <= 0 || c.n_layers <= 0)
-    return fail(LOOP_ERR_INVALID_ARG, "sizes must be positive");
+    return lp_fail(LOOP_ERR_INVALID_ARG, "sizes must be positive");
   if (c.loop_start < 0 || c.loop_start > c.loop_end || c.loop_end > c.n_layers)
-    return fail(LOOP_ERR_INVALID_ARG, "loop range [%d, %d) not inside [0, %d]", c.loop_start, c.loop_end, c.n_layers);
-  if (c.n_passes < 1) return fail(LOOP_ERR_INVALID_ARG, "n_passes must be >= 1");
-  if (c.sinkhorn_iters < 0 || c.attn_period < 1) return fail(LOOP_ERR_INVALID_ARG, "sinkhorn_iters / attn_period");
-  if (!(c.rms_eps > 0.f) || !(c.la_eps >= 0.f)) return fail(LOOP_ERR_INVALID_ARG, "eps");
-  if (c.dtype != LOOP_FP32 && c.dtype != LOOP_BF16) return fail(LOOP_ERR_INVALID_ARG, "dtype");
-  if (w->n_layers != c.n_layers || !w->layers) return fail(LOOP_ERR_INVALID_ARG, "weights: layer count");
+    return lp_fail(LOOP_ERR_INVALID_ARG, "loop range [%d, %d) not inside [0, %d]", c.loop_start, c.loop_end, c.n_layers);
+  if (c.n_passes < 1) return lp_fail(LOOP_ERR_INVALID_ARG, "n_passes must be >= 1");
+  if (c.sinkhorn_iters < 0 || c.attn_period < 1) return lp_fail(LOOP_ERR_INVALID_ARG, "sinkhorn_iters / attn_period");
+  if (!(c.rms_eps > 0.f) || !(c.la_eps >= 0.f)) return lp_fail(LOOP_ERR_INVALID_ARG, "eps");
+  if (c.dtype != LOOP_FP32 && c.dtype != LOOP_BF16) return lp_fail(LOOP_ERR_INVALID_ARG, "dtype");
+  if (w->n_layers != c.n_layers || !w->layers) return lp_fail(LOOP_ERR_INVALID_ARG, "weights: layer count");
   if (c.n_heads % c.n_kv_heads || c.n_heads / c.n_kv_heads > 8)
-    return fail(LOOP_ERR_SHAPE, "n_heads must be a multiple of n_kv_heads, at most 8 per group");
-  if (c.hidden % 8 || c.hidden > 4096) return fail(LOOP_ERR_SHAPE, "hidden must be a multiple of 8, <= 4096");
-  if (c.head_dim != 64 && c.head_dim != 128) return fail(LOOP_ERR_SHAPE, "head_dim must be 64 or 128");
+    return lp_fail(LOOP_ERR_SHAPE, "n_heads must be a multiple of n_kv_heads, at most 8 per group");
+  if (c.hidden % 8 || c.hidden > 4096) return lp_fail(LOOP_ERR_SHAPE, "hidden must be a multiple of 8, <= 4096");
+  if (c.head_dim != 64 && c.head_dim != 128) return lp_fail(LOOP_ERR_SHAPE, "head_dim must be 64 or 128");
   const int qkv_rows = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
   if (c.dtype == LOOP_BF16) {
-    if (c.head_dim != 128) return fail(LOOP_ERR_SHAPE, "bf16 needs head_dim 128");
+    if (c.head_dim != 128) return lp_fail(LOOP_ERR_SHAPE, "bf16 needs head_dim 128");
     if (c.hidden % 256 || qkv_rows % 256 || c.vocab % 256 || (c.n_heads * c.head_dim) % 128 || c.ffn % 128)
-      return fail(LOOP_ERR_SHAPE, "bf16 GEMM tiles need hidden, qkv rows, vocab %% 256 == 0 and ffn %% 128 == 0");
+      return lp_fail(LOOP_ERR_SHAPE, "bf16 GEMM tiles need hidden, qkv rows, vocab %% 256 == 0 and ffn %% 128 == 0");
   } else {
-    if (c.ffn % 8 || (c.n_heads * c.head_dim) % 8) return fail(LOOP_ERR_SHAPE, "fp32 widths must be multiples of 8");
+    if (c.ffn % 8 || (c.n_heads * c.head_dim) % 8) return lp_fail(LOOP_ERR_SHAPE, "fp32 widths must be multiples of 8");
   }
   int ndev = 0;
-  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return fail(LOOP_ERR_NO_DEVICE, "no HIP device");
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) return lp_fail(LOOP_ERR_NO_DEVICE, "no HIP device");
 
   auto* m = new loop_model();
   m->cfg = c;
@@ -161,23 +164,23 @@ int loop_model_create(const loop_config* cfg, const loop_weights* w, loop_model*
   m->layers.assign(w->layers, w->layers + c.n_layers);
   auto bad = [&](const char* what, int i) {
     delete m;
-    return fail(LOOP_ERR_INVALID_ARG, "weights: %s missing (layer %d)", what, i);
+    return lp_fail(LOOP_ERR_INVALID_ARG, "weights: %s missing (layer %d)", what, i);
   };
   if (!m->embed || !m->final_norm || !m->head) return bad("embed/final_norm/head", -1);
   if (misaligned(m->embed) || misaligned(m->final_norm) || misaligned(m->head)) {
     delete m;
-    return fail(LOOP_ERR_ALIGN, "weights: global tensor not 16-byte aligned");
+    return lp_fail(LOOP_ERR_ALIGN, "weights: global tensor not 16-byte aligned");
   }
   for (int i = 0; i < c.n_layers; ++i) {
     const loop_layer_weights& L = m->layers[i];
     if (!L.attn_norm || !L.ffn_norm || !L.qkv || !L.o || !L.gate_up || !L.down) return bad("layer tensor", i);
     const void* ps[6] = {L.attn_norm, L.ffn_norm, L.qkv, L.o, L.gate_up, L.down};
     for (const void* p : ps)
-      if (misaligned(p)) { delete m; return fail(LOOP_ERR_ALIGN, "weights: layer %d tensor not 16-byte aligned", i); }
+      if (misaligned(p)) { delete m; return lp_fail(LOOP_ERR_ALIGN, "weights: layer %d tensor not 16-byte aligned", i); }
     if (m->in_loop(i)) {
       for (int s = 0; s < 2; ++s) {
         if (!L.mhc_w[s] || !L.mhc_b[s]) return bad("mhc parameters", i);
-        if (misaligned(L.mhc_w[s])) { delete m; return fail(LOOP_ERR_ALIGN, "weights: mhc_w not 16-byte aligned"); }
+        if (misaligned(L.mhc_w[s])) { delete m; return lp_fail(LOOP_ERR_ALIGN, "weights: mhc_w not 16-byte aligned"); }
       }
     }
   }
@@ -202,7 +205,7 @@ int loop_model_destroy(loop_model* m) {
 }
 
 int loop_model_schedule(const loop_model* m, int max, int* layer, int* pass, int* kind, int* slot, int* n) {
-  if (!m || !n) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (!m || !n) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
   *n = (int)m->sched.size();
   for (int e = 0; e < *n && e < max; ++e) {
     if (layer) layer[e] = m->sched[e].layer;
@@ -237,30 +240,30 @@ static void state_offsets(const loop_model* m, int batch, int max_seq, std::vect
 }
 
 int loop_state_bytes(const loop_model* m, int batch, int max_seq, size_t* bytes) {
-  if (!m || !bytes) return fail(LOOP_ERR_INVALID_ARG, "null argument");
-  if (batch <= 0 || max_seq <= 0) return fail(LOOP_ERR_INVALID_ARG, "batch and max_seq must be positive");
+  if (!m || !bytes) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (batch <= 0 || max_seq <= 0) return lp_fail(LOOP_ERR_INVALID_ARG, "batch and max_seq must be positive");
   state_offsets(m, batch, max_seq, nullptr, nullptr, nullptr, nullptr, bytes);
   return LOOP_OK;
 }
 
 int loop_workspace_bytes(const loop_model* m, int batch, int max_tokens, int max_seq, size_t* bytes) {
-  if (!m || !bytes) return fail(LOOP_ERR_INVALID_ARG, "null argument");
-  if (batch <= 0 || max_tokens <= 0 || max_seq <= 0) return fail(LOOP_ERR_INVALID_ARG, "sizes must be positive");
+  if (!m || !bytes) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (batch <= 0 || max_tokens <= 0 || max_seq <= 0) return lp_fail(LOOP_ERR_INVALID_ARG, "sizes must be positive");
   *bytes = ws_layout(m, batch, max_tokens, max_seq).total;
   return LOOP_OK;
 }
 
 int loop_state_create(const loop_model* m, void* state_dev, size_t bytes, int batch, int max_seq, loop_state** out) {
-  if (!m || !state_dev || !out) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (!m || !state_dev || !out) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
   *out = nullptr;
-  if (batch <= 0 || max_seq <= 0) return fail(LOOP_ERR_INVALID_ARG, "batch and max_seq must be positive");
-  if (misaligned(state_dev)) return fail(LOOP_ERR_ALIGN, "state not 16-byte aligned");
+  if (batch <= 0 || max_seq <= 0) return lp_fail(LOOP_ERR_INVALID_ARG, "batch and max_seq must be positive");
+  if (misaligned(state_dev)) return lp_fail(LOOP_ERR_ALIGN, "state not 16-byte aligned");
   auto* st = new loop_state();
   size_t need = 0;
   state_offsets(m, batch, max_seq, &st->koff, &st->voff, &st->soff, &st->zoff, &need);
   if (bytes < need) {
     delete st;
-    return fail(LOOP_ERR_CAPACITY, "state has %zu bytes, needs %zu", bytes, need);
+    return lp_fail(LOOP_ERR_CAPACITY, "state has %zu bytes, needs %zu", bytes, need);
   }
   st->m = m;
   st->base = (char*)state_dev;
@@ -279,32 +282,32 @@ int loop_state_destroy(loop_state* st) {
 }
 
 int loop_state_length(const loop_state* st, int* length) {
-  if (!st || !length) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (!st || !length) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
   *length = st->length;
   return LOOP_OK;
 }
 
 int loop_state_set_length(loop_state* st, int length) {
-  if (!st) return fail(LOOP_ERR_INVALID_ARG, "null argument");
-  if (length < 0 || length > st->max_seq) return fail(LOOP_ERR_CAPACITY, "length %d outside [0, %d]", length, st->max_seq);
+  if (!st) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (length < 0 || length > st->max_seq) return lp_fail(LOOP_ERR_CAPACITY, "length %d outside [0, %d]", length, st->max_seq);
   st->length = length;
   return LOOP_OK;
 }
 
 int loop_state_region(const loop_state* st, int kind, int slot, void** ptr, size_t* bytes) {
-  if (!st || !ptr) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (!st || !ptr) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
   const loop_model* m = st->m;
   const loop_config& c = m->cfg;
   size_t off = 0, sz = 0;
   const size_t kv = (size_t)st->batch * c.n_kv_heads * st->S_max * c.head_dim * m->es;
   switch (kind) {
     case 0: case 1:
-      if (slot < 0 || slot >= m->n_full) return fail(LOOP_ERR_INVALID_ARG, "full slot %d out of range", slot);
+      if (slot < 0 || slot >= m->n_full) return lp_fail(LOOP_ERR_INVALID_ARG, "full slot %d out of range", slot);
       off = kind == 0 ? st->koff[slot] : st->voff[slot];
       sz = kv;
       break;
     case 2: case 3:
-      if (slot < 0 || slot >= m->n_lin) return fail(LOOP_ERR_INVALID_ARG, "linear slot %d out of range", slot);
+      if (slot < 0 || slot >= m->n_lin) return lp_fail(LOOP_ERR_INVALID_ARG, "linear slot %d out of range", slot);
       off = kind == 2 ? st->soff[slot] : st->zoff[slot];
       sz = (size_t)st->batch * c.n_kv_heads * c.head_dim * (kind == 2 ? c.head_dim : 1) * sizeof(float);
       break;
@@ -313,7 +316,7 @@ int loop_state_region(const loop_state* st, int kind, int slot, void** ptr, size
       sz = 256;
       break;
     default:
-      return fail(LOOP_ERR_INVALID_ARG, "region kind %d", kind);
+      return lp_fail(LOOP_ERR_INVALID_ARG, "region kind %d", kind);
   }
   *ptr = st->base + off;
   if (bytes) *bytes = sz;
@@ -321,7 +324,7 @@ int loop_state_region(const loop_state* st, int kind, int slot, void** ptr, size
 }
 
 int loop_state_check(loop_state* st, void* stream) {
-  if (!st) return fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (!st) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
   hipStream_t s = (hipStream_t)stream;
   uint32_t word = 0;
   int r = check_hip(hipMemcpyAsync(&word, st->base, sizeof word, hipMemcpyDeviceToHost, s), "read error word");
@@ -333,7 +336,7 @@ int loop_state_check(loop_state* st, void* stream) {
     if (r) return r;
     r = check_hip(hipStreamSynchronize(s), "synchronize");
     if (r) return r;
-    return fail(LOOP_ERR_DEVICE_FLAG, "device flagged input error 0x%x (token id out of range)", word);
+    return lp_fail(LOOP_ERR_DEVICE_FLAG, "device flagged input error 0x%x (token id out of range)", word);
   }
   return LOOP_OK;
 }
@@ -351,18 +354,18 @@ namespace {
 int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, const int32_t* tokens,
             const void* embeds, int B, int S, unsigned flags, void* out, hipStream_t s, bool decode) {
   const loop_config& c = m->cfg;
-  if (!st || st->m != m) return fail(LOOP_ERR_STATE, "state does not belong to this model");
-  if (!workspace || !out || (!tokens && !embeds)) return fail(LOOP_ERR_INVALID_ARG, "null argument");
-  if (B <= 0 || S <= 0) return fail(LOOP_ERR_INVALID_ARG, "B and S must be positive");
-  if (misaligned(workspace) || misaligned(out) || misaligned(embeds)) return fail(LOOP_ERR_ALIGN, "misaligned buffer");
-  if (B > st->batch) return fail(LOOP_ERR_CAPACITY, "batch %d exceeds the state's %d", B, st->batch);
-  if (decode && st->length == 0) return fail(LOOP_ERR_STATE, "decode before prefill");
+  if (!st || st->m != m) return lp_fail(LOOP_ERR_STATE, "state does not belong to this model");
+  if (!workspace || !out || (!tokens && !embeds)) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (B <= 0 || S <= 0) return lp_fail(LOOP_ERR_INVALID_ARG, "B and S must be positive");
+  if (misaligned(workspace) || misaligned(out) || misaligned(embeds)) return lp_fail(LOOP_ERR_ALIGN, "misaligned buffer");
+  if (B > st->batch) return lp_fail(LOOP_ERR_CAPACITY, "batch %d exceeds the state's %d", B, st->batch);
+  if (decode && st->length == 0) return lp_fail(LOOP_ERR_STATE, "decode before prefill");
   const int pos0 = (decode || (flags & LOOP_CONTINUE)) ? st->length : 0;
   if ((long)pos0 + S > st->max_seq)
-    return fail(LOOP_ERR_CAPACITY, "positions %d + %d exceed max_seq %d", pos0, S, st->max_seq);
+    return lp_fail(LOOP_ERR_CAPACITY, "positions %d + %d exceed max_seq %d", pos0, S, st->max_seq);
   const int T = B * S;
   const WsLayout L = ws_layout(m, B, T, st->max_seq);
-  if (ws_bytes < L.total) return fail(LOOP_ERR_WORKSPACE, "workspace %zu bytes, needs %zu", ws_bytes, L.total);
+  if (ws_bytes < L.total) return lp_fail(LOOP_ERR_WORKSPACE, "workspace %zu bytes, needs %zu", ws_bytes, L.total);
 
   char* ws = (char*)workspace;
   void* h = ws + L.h;
@@ -504,16 +507,16 @@ extern "C" {
 
 int loop_prefill(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, const int32_t* tokens_dev,
                  const void* embeds_dev, int B, int S, unsigned flags, void* out_dev, void* stream) {
-  if (!m) return fail(LOOP_ERR_INVALID_ARG, "null model");
+  if (!m) return lp_fail(LOOP_ERR_INVALID_ARG, "null model");
   if (flags & ~(unsigned)(LOOP_ALL_LOGITS | LOOP_HIDDEN_OUT | LOOP_CONTINUE))
-    return fail(LOOP_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+    return lp_fail(LOOP_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
   return forward(m, st, workspace, ws_bytes, tokens_dev, embeds_dev, B, S, flags, out_dev, (hipStream_t)stream, false);
 }
 
 int loop_decode_step(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, const int32_t* tokens_dev,
                      int B, float* logits_dev, void* stream) {
-  if (!m) return fail(LOOP_ERR_INVALID_ARG, "null model");
-  if (!tokens_dev) return fail(LOOP_ERR_INVALID_ARG, "null tokens");
+  if (!m) return lp_fail(LOOP_ERR_INVALID_ARG, "null model");
+  if (!tokens_dev) return lp_fail(LOOP_ERR_INVALID_ARG, "null tokens");
   return forward(m, st, workspace, ws_bytes, tokens_dev, nullptr, B, 1, 0, logits_dev, (hipStream_t)stream, true);
 }
 

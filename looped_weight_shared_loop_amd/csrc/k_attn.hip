@@ -31,7 +31,7 @@ DEV int ksw(int r, int c) { return r * PD + ((c ^ (r & 15)) << 3); }
 DEV int vsw(int r, int u) { return r * PK + ((u ^ (r & 15)) << 2); }
 
 template <int NTHR>
-__global__ __launch_bounds__(NTHR, 1) void attn_prefill_mfma(AttnArgs a) {
+__global__ __launch_bounds__(NTHR, 2) void attn_prefill_mfma(AttnArgs a) {
   extern __shared__ __align__(16) bf16_t smem[];
   const int G = a.Hq / a.Hkv;
   constexpr int nthr = NTHR;
@@ -54,7 +54,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_prefill_mfma(AttnArgs a) {
   bf16x8_t qf[8];
   if (wid < G) {
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds) qf[ds] = as_bf16x8(*(const uint4*)(Q + ds * 16 + h * 8));
+    for (int ds = 0; ds < 8; ++ds) qf[ds] = as_bf16x8(ldv4(Q + ds * 16 + h * 8));
   }
 
   const bf16_t* Kg = (const bf16_t*)a.kcache + ((size_t)(b * a.Hkv + kvh) * a.S_max) * PD;
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_prefill_mfma(AttnArgs a) {
 
   // cooperative tile load: 1024 16-byte chunks of K and 1024 of V^T
   constexpr int per = 1024 / nthr;   // 4 (256 threads) or 2 (512 threads)
-  uint4 rk[4], rv[4];
+  u32x4_t rk[4], rv[4];
   auto gload = [&](int kt) {
     const int k0 = kt * PK;
 #pragma unroll
@@ -70,16 +70,14 @@ __global__ __launch_bounds__(NTHR, 1) void attn_prefill_mfma(AttnArgs a) {
       const int cidx = tid + i * nthr;
       const int kr = cidx >> 4, kc = cidx & 15;       // K: row (key), chunk
       const int key = k0 + kr;
-      rk[i] = *(const uint4*)(Kg + (size_t)min(key, a.S_max - 1) * PD + kc * 8);
+      rk[i] = ldv4(Kg + (size_t)min(key, a.S_max - 1) * PD + kc * 8);
       const int vr = cidx >> 3, vc = cidx & 7;        // V^T: row (d), chunk of 8 keys
       const int key0 = k0 + vc * 8;
-      uint4 v = *(const uint4*)(Vg + (size_t)vr * a.S_max + min(key0, a.S_max - 8));
+      u32x4_t v = ldv4(Vg + (size_t)vr * a.S_max + min(key0, a.S_max - 8));
       if (key0 + 8 > kv_end) {
-        uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-          if (key0 + e >= kv_end) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-        v = make_uint4(w[0], w[1], w[2], w[3]);
+          if (key0 + e >= kv_end) v[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
       }
       rv[i] = v;
     }
@@ -91,10 +89,10 @@ __global__ __launch_bounds__(NTHR, 1) void attn_prefill_mfma(AttnArgs a) {
     for (int i = 0; i < per; ++i) {
       const int cidx = tid + i * nthr;
       const int kr = cidx >> 4, kc = cidx & 15;
-      *(uint4*)(ks + ksw(kr, kc)) = rk[i];
+      stv4(ks + ksw(kr, kc), rk[i]);
       const int vr = cidx >> 3, vc = cidx & 7;
-      *(uint2*)(vs + vsw(vr, 2 * vc)) = make_uint2(rv[i].x, rv[i].y);
-      *(uint2*)(vs + vsw(vr, 2 * vc + 1)) = make_uint2(rv[i].z, rv[i].w);
+      *(u32x2_t*)(vs + vsw(vr, 2 * vc)) = u32x2_t{rv[i][0], rv[i][1]};
+      *(u32x2_t*)(vs + vsw(vr, 2 * vc + 1)) = u32x2_t{rv[i][2], rv[i][3]};
     }
   };
 
@@ -122,7 +120,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_prefill_mfma(AttnArgs a) {
         for (int r = 0; r < 16; ++r) st[c][r] = 0.f;
 #pragma unroll
         for (int ds = 0; ds < 8; ++ds) {
-          const bf16x8_t kf = as_bf16x8(*(const uint4*)(ks + ksw(c * 32 + col, ds * 2 + h)));
+          const bf16x8_t kf = as_bf16x8(ldv4(ks + ksw(c * 32 + col, ds * 2 + h)));
           st[c] = mfma32(kf, qf[ds], st[c]);
         }
       }
@@ -162,14 +160,14 @@ __global__ __launch_bounds__(NTHR, 1) void attn_prefill_mfma(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           pw[e] = (uint32_t)f2bf(st[c][half * 8 + 2 * e]) | ((uint32_t)f2bf(st[c][half * 8 + 2 * e + 1]) << 16);
-        const bf16x8_t pf = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+        const bf16x8_t pf = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
         const int kbase = c * 32 + half * 16 + h * 4;   // keys kbase+0..3 and kbase+8..11
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const int r = db * 32 + col;
-          const uint2 lo = *(const uint2*)(vs + vsw(r, kbase >> 2));
-          const uint2 hi = *(const uint2*)(vs + vsw(r, (kbase + 8) >> 2));
-          o[db] = mfma32(as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y)), pf, o[db]);
+          const u32x2_t lo = *(const u32x2_t*)(vs + vsw(r, kbase >> 2));
+          const u32x2_t hi = *(const u32x2_t*)(vs + vsw(r, (kbase + 8) >> 2));
+          o[db] = mfma32(as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), pf, o[db]);
         }
       }
     }
@@ -187,7 +185,7 @@ __global__ __launch_bounds__(NTHR, 1) void attn_prefill_mfma(AttnArgs a) {
         const int d0 = db * 32 + g4 * 8 + h * 4;
         const uint32_t w0 = (uint32_t)f2bf(o[db][g4 * 4] * inv) | ((uint32_t)f2bf(o[db][g4 * 4 + 1] * inv) << 16);
         const uint32_t w1 = (uint32_t)f2bf(o[db][g4 * 4 + 2] * inv) | ((uint32_t)f2bf(o[db][g4 * 4 + 3] * inv) << 16);
-        *(uint2*)(O + d0) = make_uint2(w0, w1);
+        *(u32x2_t*)(O + d0) = u32x2_t{w0, w1};
       }
   }
 }
@@ -212,9 +210,9 @@ __global__ __launch_bounds__(64) void attn_decode_mfma(AttnArgs a) {
 
   const bf16_t* Q = (const bf16_t*)a.q + (size_t)(b * a.S_call + tq) * a.ldq + jq * PD;
   bf16x8_t qf[4];
-  const uint4 zero = make_uint4(0, 0, 0, 0);
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int ds = 0; ds < 4; ++ds) qf[ds] = as_bf16x8(cvalid ? *(const uint4*)(Q + ds * 32 + g * 8) : zero);
+  for (int ds = 0; ds < 4; ++ds) qf[ds] = as_bf16x8(cvalid ? ldv4(Q + ds * 32 + g * 8) : zero);
 
   const bf16_t* Kg = (const bf16_t*)a.kcache + ((size_t)(b * a.Hkv + kvh) * a.S_max) * PD;
   const bf16_t* Vg = (const bf16_t*)a.vcache + ((size_t)(b * a.Hkv + kvh) * PD) * a.S_max;
@@ -233,7 +231,7 @@ __global__ __launch_bounds__(64) void attn_decode_mfma(AttnArgs a) {
       const int key = k0 + 32 * (sb >> 1) + (c >> 2) * 8 + (sb & 1) * 4 + (c & 3);
       const bf16_t* kr = Kg + (size_t)key * PD + g * 8;
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) st[sb] = mfma16(as_bf16x8(*(const uint4*)(kr + ds * 32)), qf[ds], st[sb]);
+      for (int ds = 0; ds < 4; ++ds) st[sb] = mfma16(as_bf16x8(ldv4(kr + ds * 32)), qf[ds], st[sb]);
     }
     // st[sb][i]: column c, key k0 + 32*(sb/2) + 8g + 4*(sb%2) + i
     float tmax = -INFINITY;
@@ -271,17 +269,15 @@ __global__ __launch_bounds__(64) void attn_decode_mfma(AttnArgs a) {
         pw[e] = (uint32_t)f2bf(st[2 * kk][2 * e]) | ((uint32_t)f2bf(st[2 * kk][2 * e + 1]) << 16);
         pw[2 + e] = (uint32_t)f2bf(st[2 * kk + 1][2 * e]) | ((uint32_t)f2bf(st[2 * kk + 1][2 * e + 1]) << 16);
       }
-      const bf16x8_t pf = as_bf16x8(make_uint4(pw[0], pw[1], pw[2], pw[3]));
+      const bf16x8_t pf = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
       const int key0 = k0 + 32 * kk + 8 * g;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        uint4 v = *(const uint4*)(Vg + (size_t)(db * 16 + c) * a.S_max + key0);
+        u32x4_t v = ldv4(Vg + (size_t)(db * 16 + c) * a.S_max + key0);
         if (key0 + 8 > k_end) {
-          uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            if (key0 + e >= k_end) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-          v = make_uint4(w[0], w[1], w[2], w[3]);
+            if (key0 + e >= k_end) v[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
         }
         o[db] = mfma16(as_bf16x8(v), pf, o[db]);
       }

@@ -1,7 +1,7 @@
 // Dense contractions of the looped decoder: C[M, N] = A[M, K] . B[N, K]^T.
 //
-// * gemm_mfma:   bf16, M > 32.  256x256x64 workgroup tile, 4 waves of
-//                128x128 (4x4 blocks of v_mfma_f32_32x32x16_bf16), LDS double
+// * gemm_mfma:   bf16, M > 32.  256x256x64 workgroup tile, 8 waves of
+//                128x64 (4x2 blocks of v_mfma_f32_32x32x16_bf16), LDS double
 //                buffer with an XOR swizzle of 16-byte chunks, XCD-aware tile
 //                order.  fp32 accumulation.
 // * gemm_skinny: bf16, M <= 32 (decode): streams B (the weights) once; each of
@@ -43,19 +43,23 @@ DEV void epi_one(const GemmArgs& a, int row, int col, float v) {
 }
 
 // ------------------------------------------------------------------ MFMA tile kernel
-constexpr int TBM = 256, TBN = 256, TBK = 64;
+// 256x256x64 workgroup tile, 512 threads = 8 waves as 2 (M) x 4 (N); each
+// wave owns a 128x64 sub-tile = 4x2 blocks of 32x32 (128 accumulators).
+// SwiGLU: the B tile holds, per wave, 32 gate rows and the 32 matching up
+// rows, so each wave emits 32 finished output columns (128 per workgroup).
+constexpr int TBM = 256, TBN = 256, TBK = 64, GT = 512;
 constexpr int GEMM_LDS = 2 * (TBM + TBN) * TBK * 2;   // 128 KB
 
 DEV int swz(int row, int chunk) { return row * TBK + ((chunk ^ (row & 7)) << 3); }
 
 template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a) {
+__global__ __launch_bounds__(GT, 1) void gemm_mfma_kernel(GemmArgs a) {
   extern __shared__ __align__(16) bf16_t smem[];
   bf16_t* As = smem;                       // [2][TBM][TBK]
   bf16_t* Bs = smem + 2 * TBM * TBK;       // [2][TBN][TBK]
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid >> 2, wn = wid & 3;
   const int num_m = (a.M + TBM - 1) / TBM;
   const int out_n = (EPI == EPI_SWIGLU) ? 128 : TBN;
   const int num_n = (EPI == EPI_SWIGLU ? a.F : a.N) / out_n;
@@ -77,53 +81,55 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a) {
   // Element offsets fit in 32 bits: the host checks M_tile*lda and N*ldb < 2^31.
   const bf16_t* A = (const bf16_t*)a.A + (long)m0 * a.lda;
   const bf16_t* B = (const bf16_t*)a.B;
-  const int lrow = tid >> 3, lchunk = tid & 7;
+  const int lrow = tid >> 3, lchunk = tid & 7;   // rows lrow + 64 i, i < 4
   const int mlast = a.M - 1 - m0;
-  int aoff[8], boff[8];
+  int aoff[4], boff[4];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = i * 32 + lrow;
+  for (int i = 0; i < 4; ++i) {
+    const int r = i * 64 + lrow;
     aoff[i] = min(r, mlast) * (int)a.lda + lchunk * 8;
     int br;
     if (EPI == EPI_SWIGLU) {
-      const int w = r >> 7, j = (r & 127) >> 5, c = r & 31;
-      br = (j < 2) ? (n0 + w * 64 + j * 32 + c) : (a.F + n0 + w * 64 + (j - 2) * 32 + c);
+      const int w = r >> 6, j = (r >> 5) & 1, c = r & 31;
+      br = (j == 0) ? (n0 + w * 32 + c) : (a.F + n0 + w * 32 + c);
     } else {
       br = n0 + r;
     }
     boff[i] = br * (int)a.ldb + lchunk * 8;
   }
 
-  uint4 ra[8], rb[8];
-  f32x16_t acc[4][4];
+  u32x4_t ra[4], rb[4];
+  f32x16_t acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int KT = a.K / TBK;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    ra[i] = *(const uint4*)(A + aoff[i]);
-    rb[i] = *(const uint4*)(B + boff[i]);
+  for (int i = 0; i < 4; ++i) {
+    ra[i] = ldv4(A + aoff[i]);
+    rb[i] = ldv4(B + boff[i]);
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    *(uint4*)(As + swz(i * 32 + lrow, lchunk)) = ra[i];
-    *(uint4*)(Bs + swz(i * 32 + lrow, lchunk)) = rb[i];
+  for (int i = 0; i < 4; ++i) {
+    stv4(As + swz(i * 64 + lrow, lchunk), ra[i]);
+    stv4(Bs + swz(i * 64 + lrow, lchunk), rb[i]);
   }
   __syncthreads();
 
+  const int arow = wm * 128 + (lane & 31);
+  const int brow = wn * 64 + (lane & 31);
   for (int kt = 0; kt < KT; ++kt) {
     const int cur = kt & 1;
     if (kt + 1 < KT) {
       const int k0 = (kt + 1) * TBK;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ra[i] = *(const uint4*)(A + aoff[i] + k0);
-        rb[i] = *(const uint4*)(B + boff[i] + k0);
+      for (int i = 0; i < 4; ++i) {
+        ra[i] = ldv4(A + aoff[i] + k0);
+        rb[i] = ldv4(B + boff[i] + k0);
       }
     }
     const bf16_t* as = As + cur * TBM * TBK;
@@ -131,29 +137,23 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
     for (int ks = 0; ks < TBK / 16; ++ks) {
       const int ch = ks * 2 + (lane >> 5);
-      bf16x8_t af[4], bfr[4];
+      bf16x8_t af[4], bfr[2];
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib) {
-        const int r = wm * 128 + ib * 32 + (lane & 31);
-        af[ib] = as_bf16x8(*(const uint4*)(as + swz(r, ch)));
-      }
+      for (int ib = 0; ib < 4; ++ib) af[ib] = as_bf16x8(ldv4(as + swz(arow + ib * 32, ch)));
 #pragma unroll
-      for (int jb = 0; jb < 4; ++jb) {
-        const int r = wn * 128 + jb * 32 + (lane & 31);
-        bfr[jb] = as_bf16x8(*(const uint4*)(bs + swz(r, ch)));
-      }
+      for (int jb = 0; jb < 2; ++jb) bfr[jb] = as_bf16x8(ldv4(bs + swz(brow + jb * 32, ch)));
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) acc[ib][jb] = mfma32(af[ib], bfr[jb], acc[ib][jb]);
+        for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma32(af[ib], bfr[jb], acc[ib][jb]);
     }
     if (kt + 1 < KT) {
       bf16_t* an = As + (cur ^ 1) * TBM * TBK;
       bf16_t* bn = Bs + (cur ^ 1) * TBN * TBK;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        *(uint4*)(an + swz(i * 32 + lrow, lchunk)) = ra[i];
-        *(uint4*)(bn + swz(i * 32 + lrow, lchunk)) = rb[i];
+      for (int i = 0; i < 4; ++i) {
+        stv4(an + swz(i * 64 + lrow, lchunk), ra[i]);
+        stv4(bn + swz(i * 64 + lrow, lchunk), rb[i]);
       }
     }
     __syncthreads();
@@ -164,25 +164,23 @@ __global__ __launch_bounds__(256, 1) void gemm_mfma_kernel(GemmArgs a) {
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wm * 128 + ib * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int col = n0 + wn * 32 + (lane & 31);
+        if (row < a.M) {
+          const float g = acc[ib][0][r], u = acc[ib][1][r];
+          st1((bf16_t*)a.C + (size_t)row * a.ldc + col, silu(g) * u);
+        }
+      }
+  } else {
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
       for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wm * 128 + ib * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
           const int col = n0 + wn * 64 + jb * 32 + (lane & 31);
-          if (row < a.M) {
-            const float g = acc[ib][jb][r], u = acc[ib][jb + 2][r];
-            st1((bf16_t*)a.C + (size_t)row * a.ldc + col, silu(g) * u);
-          }
-        }
-  } else {
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < 4; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * 128 + ib * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int col = n0 + wn * 128 + jb * 32 + (lane & 31);
           if (row < a.M) epi_one<bf16_t, EPI>(a, row, col, acc[ib][jb][r]);
         }
   }
@@ -213,21 +211,21 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a) {
   f32x16_t acc;
 #pragma unroll
   for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  const uint4 zero = make_uint4(0, 0, 0, 0);
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
   int s = 0;
   for (; s + 8 <= steps; s += 8) {
-    uint4 wv[8], xv[8];
+    u32x4_t wv[8], xv[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      wv[j] = *(const uint4*)(Bp + (s + j) * 8);
-      xv[j] = tok_ok ? *(const uint4*)(Ap + (s + j) * 8) : zero;
+      wv[j] = ldv4(Bp + (s + j) * 8);
+      xv[j] = tok_ok ? ldv4(Ap + (s + j) * 8) : zero;
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc = mfma32(as_bf16x8(wv[j]), as_bf16x8(xv[j]), acc);
   }
   for (; s < steps; ++s) {
-    const uint4 wv = *(const uint4*)(Bp + s * 8);
-    const uint4 xv = tok_ok ? *(const uint4*)(Ap + s * 8) : zero;
+    const u32x4_t wv = ldv4(Bp + s * 8);
+    const u32x4_t xv = tok_ok ? ldv4(Ap + s * 8) : zero;
     acc = mfma32(as_bf16x8(wv), as_bf16x8(xv), acc);
   }
   // acc: rows = B rows n = (i/4)*8 + h*4 + i%4, column = token (lane & 31)
@@ -350,7 +348,7 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
     attr_set = true;
   }
   const int blocks = ((a.M + TBM - 1) / TBM) * (ncols / out_n);
-  gemm_mfma_kernel<EPI><<<blocks, 256, GEMM_LDS, s>>>(a);
+  gemm_mfma_kernel<EPI><<<blocks, GT, GEMM_LDS, s>>>(a);
   return hipGetLastError();
 }
 

@@ -11,14 +11,18 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _declared():
-    text = open(os.path.join(ROOT, "include", "loop.h")).read()
-    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(loop_\w+)\s*\(", text, flags=re.M)))
+    names = set()
+    for h in ("loop.h", "loop_ops.h"):
+        text = open(os.path.join(ROOT, "include", h)).read()
+        names |= set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(loop_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
 
 
 def test_header_declares_the_entry_points():
     names = _declared()
     for n in ("loop_model_create", "loop_prefill", "loop_decode_step", "loop_state_bytes",
-              "loop_workspace_bytes", "loop_state_create", "loop_last_error"):
+              "loop_workspace_bytes", "loop_state_create", "loop_last_error", "loop_op_gemm", "loop_op_mhc",
+              "loop_op_attention", "loop_op_attention_decode", "loop_op_linear"):
         assert n in names
 
 
@@ -105,3 +109,21 @@ def test_status_strings_and_null_arguments():
     assert lib.loop_prefill(None, None, None, 0, None, None, 1, 1, 0, None, None) == A.LOOP_ERR_INVALID_ARG
     assert lib.loop_decode_step(None, None, None, 0, None, 1, None, None) == A.LOOP_ERR_INVALID_ARG
     assert lib.loop_state_bytes(None, 1, 1, None) == A.LOOP_ERR_INVALID_ARG
+
+
+def test_op_level_validation_without_device():
+    """Argument checks of the op-level entry points run before any launch."""
+    from looped_weight_shared_loop_amd import _abi as A
+    lib = A.lib()
+    assert lib.loop_op_gemm(7, 0, 1, 1, 1, None, 1, None, 1, None, 1, 0, None) == A.LOOP_ERR_INVALID_ARG
+    assert lib.loop_op_gemm(1, 0, 64, 256, 64, None, 64, None, 64, None, 256, 0, None) == A.LOOP_ERR_INVALID_ARG
+    assert lib.loop_op_gemm(1, 3, 64, 256, 64, 16, 64, 16, 64, 16, 128, 100, None) == A.LOOP_ERR_INVALID_ARG
+    assert lib.loop_op_gemm(1, 0, 64, 256, 64, 24, 64, 16, 64, 16, 256, 0, None) == A.LOOP_ERR_ALIGN
+    assert lib.loop_op_mhc(1, 9, 1, 8, 20, 1e-6, None, None, 16, None, None, None, None, 16, 16, None) == \
+        A.LOOP_ERR_INVALID_ARG
+    assert lib.loop_op_attention(1, 1, 10, 60, 64, 4, 2, 128, 16, 512, 16, 16, 16, 512, None) == \
+        A.LOOP_ERR_INVALID_ARG      # pos0 + S beyond S_max
+    assert lib.loop_op_linear(1, 1, 1, 8, 4, 3, 64, 1e-6, 16, 768, 16, 16, 0, 16, 256, 16, 1 << 20, None) == \
+        A.LOOP_ERR_INVALID_ARG      # Hq % Hkv
+    assert A.loop_op_attention_decode_bytes(32, 1, 32, 128, 32832) == 32 * 32 * 129 * 130 * 4
+    assert A.loop_op_linear_bytes(1, 100, 8, 128) == 2 * 8 * (128 * 128 + 128) * 4

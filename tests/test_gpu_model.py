@@ -158,6 +158,23 @@ def vars_of(ocfg):
                 la_eps=ocfg.la_eps, dtype=ocfg.dtype)
 
 
+# Hidden states of the 9B-width group are compared at a derived bar: the
+# oracle itself moves by 2.27e-2 on the max-row metric and 1.18e-2 on the row
+# RMS ratio ||g - r||_2 / ||r||_2 (mean over rows) when ONE input element of
+# the S=200 case is moved by one bf16 ulp (pinned on the CPU by
+# test_oracle_sensitivity.py), so two valid bf16 implementations that differ
+# in one rounding decision differ by that much.  Bar: 5e-2 max-row and 3e-2
+# row RMS.  Logits and shallow stacks keep the 2e-2 bar.
+HIDDEN_TOL = 5e-2
+HIDDEN_RMS_TOL = 3e-2
+
+
+def rms_rel(got, ref):
+    g = np.asarray(got, np.float64).reshape(-1, np.shape(got)[-1])
+    r = np.asarray(ref, np.float64).reshape(-1, np.shape(ref)[-1])
+    return float((np.linalg.norm(g - r, axis=1) / np.linalg.norm(r, axis=1)).mean())
+
+
 def test_group_9b_width_hidden_out():
     """One [linear x3, full] group at hidden 4096 / FFN 12288 / 32q-8kv x 128,
     looped twice under two-stream mHC, inputs N(0, 1), at a reduced length."""
@@ -169,8 +186,28 @@ def test_group_9b_width_hidden_out():
     ref = oracle.forward(ocfg, Wo, embeds=emb, hidden_out=True)
     st = model.new_state(1, S)
     got = model.prefill(st, embeds=torch.from_numpy(emb).to(torch.bfloat16).cuda(), hidden_out=True)
-    err = rel(got.float().cpu().numpy(), ref)
-    _say("group rel err", err)
+    g = got.float().cpu().numpy()
+    err, rms = rel(g, ref), rms_rel(g, ref)
+    _say("group rel err", err, "row rms", rms)
+    assert err < HIDDEN_TOL and rms < HIDDEN_RMS_TOL
+
+
+@pytest.mark.parametrize("shape", [(1, 0, 1, 1), (4, 3, 4, 1)], ids=["one_looped_linear", "three_plain_one_looped_full"])
+def test_group_9b_width_shallow(shape):
+    """Shallow stacks at 9B width, where rounding-flip growth is small, held to
+    the logits bar: one looped linear-attention layer (enter, two sites, exit),
+    and three plain linear layers followed by one looped full-attention layer."""
+    n_layers, ls, le, P = shape
+    ocfg = oracle.group_config(n_layers=n_layers, loop_start=ls, loop_end=le, n_passes=P)
+    S = 160
+    model, Wo = build_pair(ocfg, cache_layers=4)
+    emb = synth.normal_bf16_as_f32(1, synth.TID_EMBEDS_IN, (1, S, ocfg.hidden))
+    ref = oracle.forward(ocfg, Wo, embeds=emb, hidden_out=True)
+    st = model.new_state(1, S)
+    got = model.prefill(st, embeds=torch.from_numpy(emb).to(torch.bfloat16).cuda(), hidden_out=True)
+    g = got.float().cpu().numpy()
+    err, rms = rel(g, ref), rms_rel(g, ref)
+    _say(shape, "rel err", err, "row rms", rms)
     assert err < BF16_TOL
 
 
