@@ -27,8 +27,8 @@ constexpr int PD = 128;   // head dim
 
 // K tile [64 keys][128 d] in 16-byte chunks, chunk c of row r at c ^ (r & 15).
 DEV int ksw(int r, int c) { return r * PD + ((c ^ (r & 15)) << 3); }
-// V^T tile [128 d][64 keys] in 8-byte units, unit u of row r at u ^ (r & 15).
-DEV int vsw(int r, int u) { return r * PK + ((u ^ (r & 15)) << 2); }
+// V^T tile [128 d][64 keys] in 8-byte units, unit u of row r at u ^ ((r >> 1) & 15).
+DEV int vsw(int r, int u) { return r * PK + ((u ^ ((r >> 1) & 15)) << 2); }
 
 template <int NTHR>
 __global__ __launch_bounds__(NTHR, 2) void attn_prefill_mfma(AttnArgs a) {

@@ -1,9 +1,8 @@
 // Dense contractions of the looped decoder: C[M, N] = A[M, K] . B[N, K]^T.
 //
-// * gemm_mfma:   bf16, M > 32.  256x256x64 workgroup tile, 8 waves of
-//                128x64 (4x2 blocks of v_mfma_f32_32x32x16_bf16), LDS double
-//                buffer with an XOR swizzle of 16-byte chunks, XCD-aware tile
-//                order.  fp32 accumulation.
+// * gemm_dma:    bf16, M > 32.  256x256 workgroup tile, 8 waves of 128x64
+//                (v_mfma_f32_32x32x16_bf16), global -> LDS DMA through four
+//                LDS stages, XCD-aware tile order.  fp32 accumulation.
 // * gemm_skinny: bf16, M <= 32 (decode): streams B (the weights) once; each of
 //                8 waves takes 1/8 of K for a 32-row block of B, then the
 //                partial 32x32 blocks are summed in LDS in a fixed order.
@@ -43,31 +42,42 @@ DEV void epi_one(const GemmArgs& a, int row, int col, float v) {
 }
 
 // ------------------------------------------------------------------ MFMA tile kernel
-// 256x256x64 workgroup tile, 512 threads = 8 waves as 2 (M) x 4 (N); each
-// wave owns a 128x64 sub-tile = 4x2 blocks of 32x32 (128 accumulators).
-// SwiGLU: the B tile holds, per wave, 32 gate rows and the 32 matching up
-// rows, so each wave emits 32 finished output columns (128 per workgroup).
-constexpr int TBM = 256, TBN = 256, TBK = 64, GT = 512;
-constexpr int GEMM_LDS = 2 * (TBM + TBN) * TBK * 2;   // 128 KB
+// 256x256 workgroup tile; WN_ = 4: 8 waves as 2 (M) x 4 (N), each owning a
+// 128x64 sub-tile = 4x2 blocks of v_mfma_f32_32x32x16_bf16 (WN_ = 2: 4 waves
+// of 128x128).  Operands move global -> LDS with global_load_lds_dwordx4 (no
+// staging registers): BK = 32, four LDS stages, loads issued three tiles
+// ahead, LDS fragment reads one k-substep ahead of the MFMAs.  Each
+// wave-instruction writes 1 KB of LDS (lane l at +16 l): rows 16 b .. 16 b + 15
+// of one operand tile, 64 B each; 16-byte chunk c of row r sits at
+// c ^ ((r >> 2) & 3).  SwiGLU: a wave's B rows are JB/2 blocks of gate rows
+// then the JB/2 matching up-row blocks, so each wave emits finished output
+// columns (128 per workgroup).  Tiles are walked in an XCD-aware order.
+constexpr int TBM = 256, TBN = 256;
+constexpr int DBK = 32, DST = 4;
+constexpr int DSTAGE = (TBM + TBN) * DBK;            // elements per stage (32 KB)
+constexpr int GEMM_DMA_LDS = DST * DSTAGE * 2;       // 128 KB
 
-DEV int swz(int row, int chunk) { return row * TBK + ((chunk ^ (row & 7)) << 3); }
+DEV int dswz(int row, int chunk) { return row * DBK + ((chunk ^ ((row >> 2) & 3)) << 3); }
 
-template <int EPI>
-__global__ __launch_bounds__(GT, 1) void gemm_mfma_kernel(GemmArgs a) {
+DEV void dma16(const bf16_t* g, bf16_t* l) {
+  __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                   (void __attribute__((address_space(3)))*)l, 16, 0, 0);
+}
+
+template <int EPI, int WN_>
+__global__ __launch_bounds__(128 * WN_, 1) void gemm_dma_kernel(GemmArgs a) {
+  constexpr int JB = 8 / WN_, WCOL = 32 * JB;
+  constexpr int NBW = JB;                 // DMA blocks per wave per operand
   extern __shared__ __align__(16) bf16_t smem[];
-  bf16_t* As = smem;                       // [2][TBM][TBK]
-  bf16_t* Bs = smem + 2 * TBM * TBK;       // [2][TBN][TBK]
-
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 2, wn = wid & 3;
+  const int wm = wid / WN_, wn = wid % WN_;
   const int num_m = (a.M + TBM - 1) / TBM;
   const int out_n = (EPI == EPI_SWIGLU) ? 128 : TBN;
   const int num_n = (EPI == EPI_SWIGLU ? a.F : a.N) / out_n;
   const int nblk = num_m * num_n;
-
-  // XCD-aware order: consecutive hardware block ids go round-robin over the
-  // 8 XCDs; give each XCD a contiguous range of tiles, then walk tiles in
-  // groups of 8 row-tiles so neighbouring tiles share A and B panels in L2.
+  // Consecutive hardware block ids go round-robin over the 8 XCDs: give each
+  // XCD a contiguous range of tiles, then walk tiles in groups of 8 row-tiles
+  // so neighbouring tiles share A and B panels in that XCD's L2.
   int id = blockIdx.x;
   if (nblk % 8 == 0) id = (id & 7) * (nblk >> 3) + (id >> 3);
   const int GM = 8;
@@ -78,109 +88,125 @@ __global__ __launch_bounds__(GT, 1) void gemm_mfma_kernel(GemmArgs a) {
   const int tn = (id % group) / gsz;
   const int m0 = tm * TBM, n0 = tn * out_n;
 
-  // Element offsets fit in 32 bits: the host checks M_tile*lda and N*ldb < 2^31.
+  // Element offsets fit in 32 bits: the host checks 256*lda and N*ldb < 2^31.
   const bf16_t* A = (const bf16_t*)a.A + (long)m0 * a.lda;
   const bf16_t* B = (const bf16_t*)a.B;
-  const int lrow = tid >> 3, lchunk = tid & 7;   // rows lrow + 64 i, i < 4
+  // wave w issues blocks NBW w .. NBW w + NBW - 1 of A and of B: rows 16 blk + lane / 4
   const int mlast = a.M - 1 - m0;
-  int aoff[4], boff[4];
+  int aoff[NBW], boff[NBW], lofs[NBW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = i * 64 + lrow;
-    aoff[i] = min(r, mlast) * (int)a.lda + lchunk * 8;
+  for (int i = 0; i < NBW; ++i) {
+    const int blk = wid * NBW + i;
+    const int r = blk * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    aoff[i] = min(r, mlast) * (int)a.lda + c * 8;
     int br;
     if (EPI == EPI_SWIGLU) {
-      const int w = r >> 6, j = (r >> 5) & 1, c = r & 31;
-      br = (j == 0) ? (n0 + w * 32 + c) : (a.F + n0 + w * 32 + c);
+      const int w = r / WCOL, j = (r % WCOL) / 32, cc = r & 31;
+      const int oc = n0 + w * (WCOL / 2) + (j % (JB / 2)) * 32 + cc;
+      br = (j < JB / 2) ? oc : (a.F + oc);
     } else {
       br = n0 + r;
     }
-    boff[i] = br * (int)a.ldb + lchunk * 8;
+    boff[i] = br * (int)a.ldb + c * 8;
+    lofs[i] = blk * 512;   // elements: 1 KB per block
   }
-
-  u32x4_t ra[4], rb[4];
-  f32x16_t acc[4][2];
+  const int KT = a.K / DBK;
+  auto issue = [&](int kt) {
+    bf16_t* st = smem + (kt % DST) * DSTAGE;
+    const int k0 = kt * DBK;
+#pragma unroll
+    for (int i = 0; i < NBW; ++i) {
+      dma16(A + aoff[i] + k0, st + lofs[i]);
+      dma16(B + boff[i] + k0, st + TBM * DBK + lofs[i]);
+    }
+  };
+  f32x16_t acc[4][JB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < JB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int KT = a.K / TBK;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = ldv4(A + aoff[i]);
-    rb[i] = ldv4(B + boff[i]);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    stv4(As + swz(i * 64 + lrow, lchunk), ra[i]);
-    stv4(Bs + swz(i * 64 + lrow, lchunk), rb[i]);
-  }
-  __syncthreads();
-
+  for (int t = 0; t < DST - 1 && t < KT; ++t) issue(t);
   const int arow = wm * 128 + (lane & 31);
-  const int brow = wn * 64 + (lane & 31);
+  const int brow = wn * WCOL + (lane & 31);
+  // Software pipeline over k-substeps of 16: the fragments of the next
+  // substep are read from LDS while the MFMAs of the current one run.
+  bf16x8_t fa[2][4], fb[2][JB];
+  auto read_frags = [&](int kt, int ks, bf16x8_t (&xa)[4], bf16x8_t (&xb)[JB]) {
+    const bf16_t* as = smem + (kt % DST) * DSTAGE;
+    const bf16_t* bs = as + TBM * DBK;
+    const int ch = ks * 2 + (lane >> 5);
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) xa[ib] = as_bf16x8(ldv4(as + dswz(arow + ib * 32, ch)));
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) xb[jb] = as_bf16x8(ldv4(bs + dswz(brow + jb * 32, ch)));
+  };
+  auto mma = [&](const bf16x8_t (&xa)[4], const bf16x8_t (&xb)[JB]) {
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) acc[ib][jb] = mfma32(xa[ib], xb[jb], acc[ib][jb]);
+  };
+  // tile t is complete for this wave once at most 2 NBW * min(KT - 1 - t, 2) loads remain
+  auto wait_tile = [&](int t) {
+    if (NBW == 2) {
+      if (t + 2 < KT) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else if (t + 1 < KT) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    } else {
+      if (t + 2 < KT) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else if (t + 1 < KT) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+  };
+  wait_tile(0);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  if (DST - 1 < KT) issue(DST - 1);
+  read_frags(0, 0, fa[0], fb[0]);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
+    read_frags(kt, 1, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
     if (kt + 1 < KT) {
-      const int k0 = (kt + 1) * TBK;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = ldv4(A + aoff[i] + k0);
-        rb[i] = ldv4(B + boff[i] + k0);
-      }
+      // Each wave waits for its own loads of tile kt + 1; after the barrier
+      // the whole tile is in LDS and every wave has consumed its reads of
+      // stage (kt - 1) % DST, which the next issue overwrites.  No memory
+      // fence: that would drain the loads still in flight for later tiles.
+      wait_tile(kt + 1);
+      __builtin_amdgcn_s_barrier();
+      __atomic_signal_fence(__ATOMIC_SEQ_CST);
+      if (kt + DST < KT) issue(kt + DST);
+      read_frags(kt + 1, 0, fa[0], fb[0]);
     }
-    const bf16_t* as = As + cur * TBM * TBK;
-    const bf16_t* bs = Bs + cur * TBN * TBK;
-#pragma unroll
-    for (int ks = 0; ks < TBK / 16; ++ks) {
-      const int ch = ks * 2 + (lane >> 5);
-      bf16x8_t af[4], bfr[2];
-#pragma unroll
-      for (int ib = 0; ib < 4; ++ib) af[ib] = as_bf16x8(ldv4(as + swz(arow + ib * 32, ch)));
-#pragma unroll
-      for (int jb = 0; jb < 2; ++jb) bfr[jb] = as_bf16x8(ldv4(bs + swz(brow + jb * 32, ch)));
-#pragma unroll
-      for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) acc[ib][jb] = mfma32(af[ib], bfr[jb], acc[ib][jb]);
-    }
-    if (kt + 1 < KT) {
-      bf16_t* an = As + (cur ^ 1) * TBM * TBK;
-      bf16_t* bn = Bs + (cur ^ 1) * TBN * TBK;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        stv4(an + swz(i * 64 + lrow, lchunk), ra[i]);
-        stv4(bn + swz(i * 64 + lrow, lchunk), rb[i]);
-      }
-    }
-    __syncthreads();
+    mma(fa[1], fb[1]);
   }
 
-  // epilogue: lane holds column (lane & 31) and rows (r/4)*8 + (lane/32)*4 + r%4
   if (EPI == EPI_SWIGLU) {
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + ib * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-        const int col = n0 + wn * 32 + (lane & 31);
-        if (row < a.M) {
-          const float g = acc[ib][0][r], u = acc[ib][1][r];
-          st1((bf16_t*)a.C + (size_t)row * a.ldc + col, silu(g) * u);
+      for (int jb = 0; jb < JB / 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 128 + ib * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int col = n0 + wn * (WCOL / 2) + jb * 32 + (lane & 31);
+          if (row < a.M) {
+            const float g = acc[ib][jb][r], u = acc[ib][jb + JB / 2][r];
+            st1((bf16_t*)a.C + (size_t)row * a.ldc + col, silu(g) * u);
+          }
         }
-      }
   } else {
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-      for (int jb = 0; jb < 2; ++jb)
+      for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wm * 128 + ib * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int col = n0 + wn * 64 + jb * 32 + (lane & 31);
+          const int col = n0 + wn * WCOL + jb * 32 + (lane & 31);
           if (row < a.M) epi_one<bf16_t, EPI>(a, row, col, acc[ib][jb][r]);
         }
   }
@@ -322,6 +348,19 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs a) {
 }
 
 // ------------------------------------------------------------------ dispatch
+template <int EPI, int WN_>
+static hipError_t launch_dma(const GemmArgs& a, int blocks, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_dma_kernel<EPI, WN_>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_DMA_LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  gemm_dma_kernel<EPI, WN_><<<blocks, 128 * WN_, GEMM_DMA_LDS, s>>>(a);
+  return hipGetLastError();
+}
+
 template <int EPI>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 32) {
@@ -331,25 +370,14 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
     gemm_skinny_kernel<EPI><<<blocks, 512, 0, s>>>(a);
     return hipGetLastError();
   }
-  if (a.K % TBK) return hipErrorInvalidValue;
+  if (a.K % DBK) return hipErrorInvalidValue;
   if ((long)TBM * a.lda >= (1L << 31) || (long)(EPI == EPI_SWIGLU ? 2 * a.F : a.N) * a.ldb >= (1L << 31))
     return hipErrorInvalidValue;
   const int out_n = (EPI == EPI_SWIGLU) ? 128 : TBN;
   const int ncols = (EPI == EPI_SWIGLU) ? a.F : a.N;
   if (ncols % out_n) return hipErrorInvalidValue;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipSuccess;
-    const void* fns[4] = {(const void*)gemm_mfma_kernel<EPI_STORE>, (const void*)gemm_mfma_kernel<EPI_F32>,
-                          (const void*)gemm_mfma_kernel<EPI_QKV>, (const void*)gemm_mfma_kernel<EPI_SWIGLU>};
-    for (int i = 0; i < 4 && e == hipSuccess; ++i)
-      e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, GEMM_LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const int blocks = ((a.M + TBM - 1) / TBM) * (ncols / out_n);
-  gemm_mfma_kernel<EPI><<<blocks, GT, GEMM_LDS, s>>>(a);
-  return hipGetLastError();
+  return launch_dma<EPI, 4>(a, blocks, s);
 }
 
 template <int EPI>
