@@ -44,10 +44,14 @@ int loop_op_add_rmsnorm(int dtype, int T, int C, const void* y, void* h, const f
  *  ENTER: X = [h + y, h + y] (y may be NULL); maps_out, u for site (w, b, gamma).
  *  MID:   X <- H_res X + H_post y with maps_in; then maps_out and u for (w, b, gamma).
  *  EXIT:  X' = H_res X + H_post y; h = (X'0 + X'1) / 2; u = RMSNorm(h; gamma).
- * C <= 4096, C % 8 == 0. */
+ * C <= 4096, C % 8 == 0.  With bf16 and C % 256 == 0, ENTER and MID run the
+ * projection W x on the matrix cores when `scratch` (>= loop_op_mhc_bytes(C))
+ * is given: W is split there into bf16 high and low parts (about 16 mantissa
+ * bits of W, float32 accumulation); with scratch NULL a float32 path is used. */
+size_t loop_op_mhc_bytes(int C);
 int loop_op_mhc(int dtype, int mode, int T, int C, int sinkhorn_iters, float eps, const void* y, void* h, void* X,
                 const float* maps_in, float* maps_out, const float* w, const float* b, const float* gamma,
-                void* u, void* stream);
+                void* u, void* scratch, size_t scratch_bytes, void* stream);
 
 /* Causal softmax attention with grouped KV heads for S new positions (pos0 ..
  * pos0+S-1) of B sequences over a cache slot: K [B][Hkv][S_max][d],

@@ -79,8 +79,9 @@ SYMBOLS = {
     "loop_op_gemm": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, ctypes.c_long, c_void_p, ctypes.c_long,
                              c_void_p, ctypes.c_long, c_int, c_void_p]),
     "loop_op_add_rmsnorm": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p]),
+    "loop_op_mhc_bytes": (c_size_t, [c_int]),
     "loop_op_mhc": (c_int, [c_int, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
-                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p]),
+                            c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]),
     "loop_op_attention": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p, ctypes.c_long,
                                   c_void_p, c_void_p, c_void_p, ctypes.c_long, c_void_p]),
     "loop_op_attention_decode_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
@@ -217,9 +218,14 @@ def loop_op_add_rmsnorm(dtype, T, C, y, h, gamma, u, eps, stream) -> None:
            "loop_op_add_rmsnorm")
 
 
-def loop_op_mhc(dtype, mode, T, C, iters, eps, y, h, X, maps_in, maps_out, w, b, gamma, u, stream) -> None:
+def loop_op_mhc_bytes(C) -> int:
+    return lib().loop_op_mhc_bytes(C)
+
+
+def loop_op_mhc(dtype, mode, T, C, iters, eps, y, h, X, maps_in, maps_out, w, b, gamma, u, scratch, nbytes,
+                stream) -> None:
     _check(lib().loop_op_mhc(dtype, mode, T, C, iters, eps, _p(y), _p(h), _p(X), _p(maps_in), _p(maps_out), _p(w),
-                             _p(b), _p(gamma), _p(u), _p(stream)), "loop_op_mhc")
+                             _p(b), _p(gamma), _p(u), _p(scratch), nbytes, _p(stream)), "loop_op_mhc")
 
 
 def loop_op_attention(dtype, B, S, pos0, S_max, Hq, Hkv, d, q, ldq, k, v, out, ldo, stream) -> None:

@@ -73,7 +73,7 @@ struct loop_state {
 namespace {
 
 struct WsLayout {
-  size_t h, X, u, y, qkv, attn, inter, maps, lin, dec, total;
+  size_t h, X, u, y, qkv, attn, inter, maps, lin, dec, wsplit, total;
 };
 
 WsLayout ws_layout(const loop_model* m, int batch, int max_tokens, int max_seq) {
@@ -95,6 +95,7 @@ WsLayout ws_layout(const loop_model* m, int batch, int max_tokens, int max_seq) 
   const size_t S_max = ((size_t)max_seq + 63) / 64 * 64;
   const size_t nsplit = (S_max + DEC_SPLIT - 1) / DEC_SPLIT;
   w.dec = take((size_t)batch * c.n_heads * nsplit * (c.head_dim + 2) * sizeof(float));
+  w.wsplit = take((size_t)16 * 2 * C * sizeof(uint16_t));
   w.total = off;
   return w;
 }
@@ -402,6 +403,7 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
     a.maps_in = maps[mp];
     a.maps_out = maps[mp ^ 1];
     a.w = w; a.b = b; a.gamma = gamma; a.u = u; a.grid = mhc_grid;
+    a.wsplit = (lk::bf16_t*)(ws + L.wsplit);
     hipError_t e = lk::mhc(a, s);
     if (mode != lk::MHC_EXIT) mp ^= 1;
     return e;

@@ -227,6 +227,163 @@ __global__ __launch_bounds__(256) void lin_output(LinArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ chunk outputs, MFMA (d = 128)
+// One workgroup per (chunk, sequence, KV head) serves the G query heads of the
+// group, so S_c, z_c, phi(K) and V of the chunk are staged in LDS once.
+// Products use v_mfma_f32_16x16x4f32 (float32 operands, the state stays
+// float32).  Wave w owns chunk rows 16 w .. 16 w + 15.  In every product, lane
+// group g = lane / 16 carries the contiguous slice g * K/4 .. of the
+// contraction index on both operands (the sum is order-independent).
+//   A_g   = tril(phi(Q_g) phi(K)^T)                 [64 x 64]
+//   num_g = phi(Q_g) S_c + A_g V                      [64 x 128]
+//   den_g = phi(Q_g) z_c + rowsum(A_g) + eps
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+DEV f32x4v mfma_f32(float a, float b, f32x4v c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
+
+constexpr int LSP = 132;   // padded row of S^T and phi(K) (floats)
+constexpr int LAP = 68;    // padded row of V^T and A (floats)
+constexpr int LIN_MFMA_LDS = (128 * LSP + 64 * LSP + 128 * LAP + 64 * LAP + 128 + 64) * 4;
+
+template <typename T>
+__global__ __launch_bounds__(256, 1) void lin_output_mfma(LinArgs a) {
+  extern __shared__ float lsm[];
+  float* St = lsm;                  // [128][LSP]: St[j][k] = S_c[k][j]
+  float* Kf = St + 128 * LSP;       // [64][LSP]: phi(K)[tau][d]
+  float* Vt = Kf + 64 * LSP;        // [128][LAP]: Vt[j][tau] = V[tau][j]
+  float* Am = Vt + 128 * LAP;       // [64][LAP]: masked A of the current head
+  float* zc = Am + 64 * LAP;        // [128]
+  float* den = zc + 128;            // [64]
+  constexpr int D = 128;
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.Hkv, hk = bh % a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int nc = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  const T* base = (const T*)a.qkv;
+
+  {  // stage S_c^T, z_c, phi(K), V^T
+    const float* src = a.scratch + ((size_t)bh * nc + c) * (D * D + D);
+    for (int idx = tid; idx < D * D / 4; idx += 256) {
+      const int k = idx >> 5, j4 = (idx & 31) * 4;
+      const float4 v = reinterpret_cast<const float4*>(src)[idx];
+      St[(j4 + 0) * LSP + k] = v.x;
+      St[(j4 + 1) * LSP + k] = v.y;
+      St[(j4 + 2) * LSP + k] = v.z;
+      St[(j4 + 3) * LSP + k] = v.w;
+    }
+    if (tid < D) zc[tid] = src[D * D + tid];
+    for (int idx = tid; idx < LC * D / 8; idx += 256) {
+      const int t = idx >> 4, i8 = (idx & 15) * 8;
+      const int s = c * LC + t;
+      float kx[8], vx[8];
+      if (s < a.S_call) {
+        const T* row = base + (size_t)(b * a.S_call + s) * a.ld;
+        ld8(row + (a.Hq + hk) * D + i8, kx);
+        ld8(row + (a.Hq + a.Hkv + hk) * D + i8, vx);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) kx[e] = phi(kx[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { kx[e] = 0.f; vx[e] = 0.f; }
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        Kf[t * LSP + i8 + e] = kx[e];
+        Vt[(i8 + e) * LAP + t] = vx[e];
+      }
+    }
+  }
+  __syncthreads();
+
+  const int t_row = 16 * w + li;                // A-operand row of this lane
+  const int s_q = c * LC + t_row;
+  for (int hq = 0; hq < G; ++hq) {
+    const int j = hk * G + hq;
+    // phi(q) of row t_row, d in [32 g, 32 g + 32)
+    float q[32];
+    if (s_q < a.S_call) {
+      const T* row = base + (size_t)(b * a.S_call + s_q) * a.ld + j * D + 32 * g;
+#pragma unroll
+      for (int v8 = 0; v8 < 4; ++v8) {
+        ld8(row + 8 * v8, q + 8 * v8);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) q[8 * v8 + e] = phi(q[8 * v8 + e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 32; ++e) q[e] = 0.f;
+    }
+    // A blocks of this wave's rows: tau blocks nb <= w (later blocks are masked)
+    for (int nb = 0; nb < 4; ++nb) {
+      f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+      if (nb <= w) {
+        const float* kr = Kf + (16 * nb + li) * LSP + 32 * g;
+#pragma unroll
+        for (int s4 = 0; s4 < 8; ++s4) {
+          const float4 kv = *reinterpret_cast<const float4*>(kr + 4 * s4);
+          acc = mfma_f32(q[4 * s4 + 0], kv.x, acc);
+          acc = mfma_f32(q[4 * s4 + 1], kv.y, acc);
+          acc = mfma_f32(q[4 * s4 + 2], kv.z, acc);
+          acc = mfma_f32(q[4 * s4 + 3], kv.w, acc);
+        }
+      }
+      // acc[r]: row 16 w + 4 g + r, column tau = 16 nb + li
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * g + r, tau = 16 * nb + li;
+        Am[t * LAP + tau] = (tau <= t) ? acc[r] : 0.f;
+      }
+    }
+    __syncthreads();
+    {  // den for row t_row: phi(q) . z_c over the lane's slice + row sum of A over tau in [16 g, 16 g + 16)
+      float p = 0.f;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) p += q[e] * zc[32 * g + e];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) p += Am[t_row * LAP + 16 * g + e];
+      p += __shfl_xor(p, 16, 64);
+      p += __shfl_xor(p, 32, 64);
+      if (g == 0) den[t_row] = p + a.eps;
+    }
+    __syncthreads();
+    float dinv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dinv[r] = 1.0f / den[16 * w + 4 * g + r];
+    T* out = (T*)a.out;
+    for (int jb = 0; jb < 8; ++jb) {
+      f32x4v acc = {0.f, 0.f, 0.f, 0.f};
+      const float* sr = St + (16 * jb + li) * LSP + 32 * g;
+#pragma unroll
+      for (int s4 = 0; s4 < 8; ++s4) {
+        const float4 sv = *reinterpret_cast<const float4*>(sr + 4 * s4);
+        acc = mfma_f32(q[4 * s4 + 0], sv.x, acc);
+        acc = mfma_f32(q[4 * s4 + 1], sv.y, acc);
+        acc = mfma_f32(q[4 * s4 + 2], sv.z, acc);
+        acc = mfma_f32(q[4 * s4 + 3], sv.w, acc);
+      }
+      const float* ar = Am + t_row * LAP + 16 * g;
+      const float* vr = Vt + (16 * jb + li) * LAP + 16 * g;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const float4 av = *reinterpret_cast<const float4*>(ar + 4 * s4);
+        const float4 vv4 = *reinterpret_cast<const float4*>(vr + 4 * s4);
+        acc = mfma_f32(av.x, vv4.x, acc);
+        acc = mfma_f32(av.y, vv4.y, acc);
+        acc = mfma_f32(av.z, vv4.z, acc);
+        acc = mfma_f32(av.w, vv4.w, acc);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = 16 * w + 4 * g + r;
+        const int s = c * LC + t;
+        if (s < a.S_call) st1(out + (size_t)(b * a.S_call + s) * a.ldo + j * D + 16 * jb + li, acc[r] * dinv[r]);
+      }
+    }
+    __syncthreads();   // Am and den are rewritten by the next head
+  }
+}
+
 // ------------------------------------------------------------------ decode (recurrent)
 template <typename T, int D>
 __global__ __launch_bounds__(256) void lin_decode_kernel(LinArgs a) {
@@ -300,6 +457,9 @@ static hipError_t prefill_t(const LinArgs& a, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute((const void*)lin_delta<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)lin_output<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);
+    if (e == hipSuccess && D == 128)
+      e = hipFuncSetAttribute((const void*)lin_output_mfma<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              LIN_MFMA_LDS);
     if (e != hipSuccess) return e;
     attr = true;
   }
@@ -310,7 +470,8 @@ static hipError_t prefill_t(const LinArgs& a, hipStream_t s) {
   lin_scan<<<dim3((E + 255) / 256, BH), 256, 0, s>>>(a, nc);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  lin_output<T, D><<<dim3(nc, a.B * a.Hq), 256, lds3, s>>>(a);
+  if (D == 128) lin_output_mfma<T><<<dim3(nc, BH), 256, LIN_MFMA_LDS, s>>>(a);
+  else lin_output<T, D><<<dim3(nc, a.B * a.Hq), 256, lds3, s>>>(a);
   return hipGetLastError();
 }
 

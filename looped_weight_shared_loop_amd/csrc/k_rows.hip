@@ -266,9 +266,175 @@ __global__ __launch_bounds__(512) void mhc_kernel(MhcArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ mHC, MFMA (bf16)
+// For bf16 streams the 8 projections l = W vec(X') run on the matrix cores:
+// W (float32 [8][2C]) is split once per call into W_hi = bf16(W) and
+// W_lo = bf16(W - W_hi), stacked as 16 bf16 rows, so one
+// v_mfma_f32_16x16x32_bf16 yields hi and lo partial logits of 16 tokens
+// (l_j = col j + col j+8; about 16 mantissa bits of W, float32 accumulation).
+// A workgroup of 8 waves handles 16 tokens at a time; wave w owns channels
+// [w C/8, (w+1) C/8) of both streams, lane l owns token l % 16 and 8 channels
+// per 32-channel step.  The Sinkhorn maps are computed once per token (one
+// lane each), then every lane forms u from the X' it wrote.
+__global__ __launch_bounds__(256) void mhc_split_w(const float* __restrict__ w, bf16_t* __restrict__ ws, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
+    const float v = w[i];
+    const bf16_t hi = f2bf(v);
+    ws[i] = hi;                       // rows 0..7
+    ws[n + i] = f2bf(v - bf2f(hi));   // rows 8..15
+  }
+}
+
+__global__ __launch_bounds__(512) void mhc_mfma_kernel(MhcArgs a, const bf16_t* __restrict__ wsplit) {
+  __shared__ float red_acc[8][16][17];
+  __shared__ float red_s[8][16][3];
+  __shared__ float tl[16][17];
+  __shared__ float ts[16][3];
+  __shared__ float mp[16][3];
+  const int C = a.C, C2 = 2 * C;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  const int CW = C / 8, NS = CW / 32;
+  const int mode = a.mode;
+  bf16_t* X = (bf16_t*)a.X;
+  const bf16_t* hin = (const bf16_t*)a.h;
+  const bf16_t* y = (const bf16_t*)a.y;
+  bf16_t* u = (bf16_t*)a.u;
+  const int ntiles = (a.T + 15) / 16;
+  const bf16_t* wrow = wsplit + (size_t)li * C2;   // row li of [W_hi; W_lo]
+
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int t = tile * 16 + li;
+    const bool tv = t < a.T;
+    float po0 = 0.f, po1 = 0.f, r00 = 0.f, r01 = 0.f, r10 = 0.f, r11 = 0.f;
+    if (mode == MHC_MID && tv) {
+      const float* mi = a.maps_in + (size_t)t * 8;
+      po0 = mi[2]; po1 = mi[3]; r00 = mi[4]; r01 = mi[5]; r10 = mi[6]; r11 = mi[7];
+    }
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float s00 = 0.f, s11 = 0.f, s01 = 0.f;
+#pragma unroll 2
+    for (int j = 0; j < NS; ++j) {
+      const int cb = w * CW + 32 * j + 8 * g;
+      float x0[8], x1[8];
+      if (tv) {
+        if (mode == MHC_ENTER) {
+          ld8(hin + (size_t)t * C + cb, x0);
+          if (y) {
+            float yv[8];
+            ld8(y + (size_t)t * C + cb, yv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x0[e] = bf2f(f2bf(x0[e] + yv[e]));
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x1[e] = x0[e];
+        } else {
+          float p[8], q[8], yv[8];
+          ld8(X + ((size_t)t * 2) * C + cb, p);
+          ld8(X + ((size_t)t * 2 + 1) * C + cb, q);
+          ld8(y + (size_t)t * C + cb, yv);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            x0[e] = bf2f(f2bf(r00 * p[e] + r01 * q[e] + po0 * yv[e]));
+            x1[e] = bf2f(f2bf(r10 * p[e] + r11 * q[e] + po1 * yv[e]));
+          }
+        }
+        st8(X + ((size_t)t * 2) * C + cb, x0);
+        st8(X + ((size_t)t * 2 + 1) * C + cb, x1);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { x0[e] = 0.f; x1[e] = 0.f; }
+      }
+      uint32_t p0[4], p1[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        // exact: the values are already bf16
+        p0[e] = (__float_as_uint(x0[2 * e]) >> 16) | (__float_as_uint(x0[2 * e + 1]) & 0xFFFF0000u);
+        p1[e] = (__float_as_uint(x1[2 * e]) >> 16) | (__float_as_uint(x1[2 * e + 1]) & 0xFFFF0000u);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        s00 += x0[e] * x0[e];
+        s11 += x1[e] * x1[e];
+        s01 += x0[e] * x1[e];
+      }
+      const bf16x8_t w0 = as_bf16x8(ldv4(wrow + cb));
+      const bf16x8_t w1 = as_bf16x8(ldv4(wrow + C + cb));
+      acc = mfma16(as_bf16x8(u32x4_t{p0[0], p0[1], p0[2], p0[3]}), w0, acc);
+      acc = mfma16(as_bf16x8(u32x4_t{p1[0], p1[1], p1[2], p1[3]}), w1, acc);
+    }
+    // acc[r]: token 4 g + r, column li; the stream sums of token li are split over the 4 groups
+#pragma unroll
+    for (int r = 0; r < 4; ++r) red_acc[w][4 * g + r][li] = acc[r];
+    s00 += __shfl_xor(s00, 16, 64); s00 += __shfl_xor(s00, 32, 64);
+    s11 += __shfl_xor(s11, 16, 64); s11 += __shfl_xor(s11, 32, 64);
+    s01 += __shfl_xor(s01, 16, 64); s01 += __shfl_xor(s01, 32, 64);
+    if (g == 0) { red_s[w][li][0] = s00; red_s[w][li][1] = s11; red_s[w][li][2] = s01; }
+    __syncthreads();
+    if (tid < 256) {
+      const int ti = tid >> 4, cc = tid & 15;
+      float v = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 8; ++ww) v += red_acc[ww][ti][cc];
+      tl[ti][cc] = v;
+    } else if (tid < 256 + 48) {
+      const int ti = (tid - 256) / 3, k = (tid - 256) % 3;
+      float v = 0.f;
+#pragma unroll
+      for (int ww = 0; ww < 8; ++ww) v += red_s[ww][ti][k];
+      ts[ti][k] = v;
+    }
+    __syncthreads();
+    if (tid < 16) {
+      const int tt = tile * 16 + tid;
+      const float S00 = ts[tid][0], S11 = ts[tid][1], S01 = ts[tid][2];
+      const float inv = 1.0f / sqrtf((S00 + S11) / (float)C2 + a.eps);
+      float l[8], m[8];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) l[jj] = (tl[tid][jj] + tl[tid][jj + 8]) * inv + a.b[jj];
+      mhc_maps_from_logits(l, a.iters, m);
+      if (tt < a.T) {
+        float* mo = a.maps_out + (size_t)tt * 8;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) mo[jj] = m[jj];
+      }
+      const float ssin = m[0] * m[0] * S00 + 2.f * m[0] * m[1] * S01 + m[1] * m[1] * S11;
+      mp[tid][0] = m[0];
+      mp[tid][1] = m[1];
+      mp[tid][2] = 1.0f / sqrtf(fmaxf(ssin, 0.f) / (float)C + a.eps);
+    }
+    __syncthreads();
+    if (tv) {
+      const float q0 = mp[li][0], q1 = mp[li][1], iv = mp[li][2];
+      for (int j = 0; j < NS; ++j) {
+        const int cb = w * CW + 32 * j + 8 * g;
+        float x0[8], x1[8], gm[8], o[8];
+        ld8(X + ((size_t)t * 2) * C + cb, x0);      // X' written above by this thread
+        ld8(X + ((size_t)t * 2 + 1) * C + cb, x1);
+        ld8(a.gamma + cb, gm);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = gm[e] * (q0 * x0[e] + q1 * x1[e]) * iv;
+        st8(u + (size_t)t * C + cb, o);
+      }
+    }
+  }
+}
+
 hipError_t mhc(const MhcArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   if (a.C % 8 || a.C / 8 > 512) return hipErrorInvalidValue;
+  if (a.dt == DT_BF16 && a.mode != MHC_EXIT && a.C % 256 == 0 && a.wsplit) {
+    const int n = 8 * 2 * a.C;
+    mhc_split_w<<<(n + 255) / 256, 256, 0, s>>>(a.w, a.wsplit, n);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int ntiles = (a.T + 15) / 16;
+    const int cu = device_cu_count();
+    int grid = 3 * (cu > 0 ? cu : 256);
+    if (grid > ntiles) grid = ntiles;
+    mhc_mfma_kernel<<<grid, 512, 0, s>>>(a, a.wsplit);
+    return hipGetLastError();
+  }
   const int nv = a.C / 8;
   const int threads = ((nv + 63) / 64) * 64;
   int grid = a.grid > 0 ? a.grid : a.T;

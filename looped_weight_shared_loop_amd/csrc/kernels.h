@@ -7,6 +7,8 @@
 
 namespace lk {
 
+typedef uint16_t bf16_t;
+
 enum Dt { DT_F32 = 0, DT_BF16 = 1 };
 
 // ---------------------------------------------------------------- row kernels
@@ -40,6 +42,7 @@ struct MhcArgs {
   const float* gamma;    // [C] RMSNorm gain of the next sublayer
   void* u;               // [T][C] normed input of the next sublayer
   int grid;              // persistent grid size (0: one block per token)
+  bf16_t* wsplit;        // bf16 ENTER/MID: scratch of 16 x 2C bf16 for [W_hi; W_lo]
 };
 hipError_t mhc(const MhcArgs& a, hipStream_t s);
 

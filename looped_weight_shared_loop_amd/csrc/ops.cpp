@@ -60,9 +60,11 @@ int loop_op_add_rmsnorm(int dtype, int T, int C, const void* y, void* h, const f
   return launched(lk::add_rmsnorm(a, (hipStream_t)stream), "add_rmsnorm");
 }
 
+size_t loop_op_mhc_bytes(int C) { return C > 0 ? (size_t)16 * 2 * C * sizeof(uint16_t) : 0; }
+
 int loop_op_mhc(int dtype, int mode, int T, int C, int iters, float eps, const void* y, void* h, void* X,
                 const float* maps_in, float* maps_out, const float* w, const float* b, const float* gamma, void* u,
-                void* stream) {
+                void* scratch, size_t scratch_bytes, void* stream) {
   int dt;
   if (int r = dt_of(dtype, &dt)) return r;
   if (T < 0 || C <= 0 || iters < 0 || !X || !gamma || !u) return lp_fail(LOOP_ERR_INVALID_ARG, "arguments");
@@ -75,12 +77,14 @@ int loop_op_mhc(int dtype, int mode, int T, int C, int iters, float eps, const v
   } else {
     return lp_fail(LOOP_ERR_INVALID_ARG, "mode %d", mode);
   }
-  if (any_misaligned({y, h, X, w, gamma, u})) return lp_fail(LOOP_ERR_ALIGN, "misaligned");
+  if (any_misaligned({y, h, X, w, gamma, u, scratch})) return lp_fail(LOOP_ERR_ALIGN, "misaligned");
+  if (scratch && scratch_bytes < loop_op_mhc_bytes(C)) return lp_fail(LOOP_ERR_WORKSPACE, "mhc scratch too small");
   lk::MhcArgs a{};
   a.dt = dt; a.mode = mode; a.T = T; a.C = C; a.iters = iters; a.eps = eps; a.y = y; a.h = h; a.X = X;
   a.maps_in = maps_in; a.maps_out = maps_out; a.w = w; a.b = b; a.gamma = gamma; a.u = u;
   const int cu = lk::device_cu_count();
   a.grid = T < 2 * cu ? T : 2 * cu;
+  a.wsplit = (lk::bf16_t*)scratch;
   return launched(lk::mhc(a, (hipStream_t)stream), "mhc");
 }
 

@@ -119,8 +119,9 @@ def test_op_level_validation_without_device():
     assert lib.loop_op_gemm(1, 0, 64, 256, 64, None, 64, None, 64, None, 256, 0, None) == A.LOOP_ERR_INVALID_ARG
     assert lib.loop_op_gemm(1, 3, 64, 256, 64, 16, 64, 16, 64, 16, 128, 100, None) == A.LOOP_ERR_INVALID_ARG
     assert lib.loop_op_gemm(1, 0, 64, 256, 64, 24, 64, 16, 64, 16, 256, 0, None) == A.LOOP_ERR_ALIGN
-    assert lib.loop_op_mhc(1, 9, 1, 8, 20, 1e-6, None, None, 16, None, None, None, None, 16, 16, None) == \
+    assert lib.loop_op_mhc(1, 9, 1, 8, 20, 1e-6, None, None, 16, None, None, None, None, 16, 16, None, 0, None) == \
         A.LOOP_ERR_INVALID_ARG
+    assert A.loop_op_mhc_bytes(4096) == 16 * 8192 * 2
     assert lib.loop_op_attention(1, 1, 10, 60, 64, 4, 2, 128, 16, 512, 16, 16, 16, 512, None) == \
         A.LOOP_ERR_INVALID_ARG      # pos0 + S beyond S_max
     assert lib.loop_op_linear(1, 1, 1, 8, 4, 3, 64, 1e-6, 16, 768, 16, 16, 0, 16, 256, 16, 1 << 20, None) == \

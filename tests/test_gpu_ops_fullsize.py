@@ -1,0 +1,264 @@
+"""Full-size parity of each kernel family, in the launch configuration the
+9B-shape prefill and decode use, on sampled outputs the oracle recomputes one
+by one (inputs drawn on the device by the seeded generator and redrawn on the
+host for the sampled rows only).
+
+Bars (element-wise unless stated):
+  GEMM, float32 out   |g - r| <= 1e-5 * sum_k |a_k b_k|        (fp32 accumulation)
+  GEMM, bf16 out      |g - r| <= 2^-8 |r| + 1e-5 * sum_k |a_k b_k|  (one bf16 rounding)
+  mHC                 X' within 1 bf16 ulp (<= 2^-7 |x|), u within 2 ulp; maps within 1e-4
+  attention (bf16)    per query row ||g - r||_inf <= 2e-2 ||r||_inf (probabilities rounded to bf16)
+  linear attention    per row ||g - r||_inf <= 1e-2 ||r||_inf; state rel 1e-4
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import model as M
+from gpu_common import need_gpu, torch
+
+pytestmark = pytest.mark.gpu
+
+C, F, V = 4096, 12288, 248320
+HQ, HKV, D = 32, 8, 128
+QKV = (HQ + 2 * HKV) * D
+SEED = 7
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev_normal(shape, tid, std=1.0, dtype=None):
+    from synth import device as sd
+    t = torch.empty(shape, dtype=dtype or torch.bfloat16, device="cuda")
+    sd.fill_tensor_normal(t, SEED, tid, std)
+    return t
+
+
+def _host_rows(tid, ncols, rows, std=1.0, bf16=True):
+    f = synth.normal_bf16_as_f32 if bf16 else synth.normal_f32
+    return np.stack([f(SEED, tid, (ncols,), std, start=int(r) * ncols) for r in rows]).astype(np.float64)
+
+
+def _bf16(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+# ------------------------------------------------------------------ GEMM
+@pytest.mark.parametrize("name,M,N,K,epi", [
+    ("qkv", 32768, QKV, C, 0), ("o", 32768, C, HQ * D, 0), ("gate_up", 32768, 2 * F, C, 3),
+    ("down", 32768, C, F, 0), ("head_last_rows", 32, V, C, 1), ("head_all_rows", 2048, V, C, 1),
+    ("decode_gate_up", 32, 2 * F, C, 3), ("decode_down", 32, C, F, 0),
+])
+def test_gemm_full_size_sampled(name, M, N, K, epi):
+    need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    print(f"gemm {name} M={M} N={N} K={K}", flush=True)
+    a = _dev_normal((M, K), 11)
+    b = _dev_normal((N, K), 12, 0.02)
+    ncol = N // 2 if epi == 3 else N
+    c = torch.empty(M, ncol, dtype=torch.float32 if epi == 1 else torch.bfloat16, device="cuda")
+    A.loop_op_gemm(A.LOOP_BF16, epi, M, N, K, a.data_ptr(), K, b.data_ptr(), K, c.data_ptr(), ncol,
+                   N // 2 if epi == 3 else 0, _stream())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(hash(name) & 0xFFFF)
+    rows = np.unique(np.concatenate([rng.integers(0, M, 24), [0, M - 1]]))
+    cols = np.unique(np.concatenate([rng.integers(0, ncol, 24), [0, ncol - 1]]))
+    Ar = _host_rows(11, K, rows)
+    got = c[torch.from_numpy(rows).cuda()][:, torch.from_numpy(cols).cuda()].float().cpu().numpy()
+    if epi == 3:
+        Bg = _host_rows(12, K, cols, 0.02)
+        Bu = _host_rows(12, K, cols + ncol, 0.02)
+        g, u = Ar @ Bg.T, Ar @ Bu.T
+        ref = g / (1 + np.exp(-g)) * u
+        scale = (np.abs(Ar) @ np.abs(Bg).T) * np.abs(u) + (np.abs(Ar) @ np.abs(Bu).T) * np.abs(g) + 1e-30
+        bound = 2.0 ** -8 * np.abs(ref) + 2e-5 * scale
+    else:
+        Br = _host_rows(12, K, cols, 0.02)
+        ref = Ar @ Br.T
+        scale = np.abs(Ar) @ np.abs(Br).T
+        bound = 1e-5 * scale + (2.0 ** -8 * np.abs(ref) if epi == 0 else 0.0)
+    assert np.all(np.abs(got - ref) <= bound), float((np.abs(got - ref) / bound).max())
+
+
+# ------------------------------------------------------------------ mHC
+def test_mhc_isolated_full_size_sampled():
+    """2 streams x 4096 bf16 for 65,536 tokens, per-token map logits N(0, 1)
+    (maps from the oracle's definition), layer output y ~ N(0, 1)."""
+    need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    T = 65536
+    X = _dev_normal((T, 2, C), 21)
+    X0 = X.clone()
+    y = _dev_normal((T, C), 22)
+    logits_in = synth.normal_f32(SEED, 23, (T, 8))
+    pre_i = 1 / (1 + np.exp(-logits_in[:, 0:2].astype(np.float64)))
+    post_i = 2 / (1 + np.exp(-logits_in[:, 2:4].astype(np.float64)))
+    R = logits_in[:, 4:8].astype(np.float64).reshape(T, 2, 2)
+    res_i = M.sinkhorn(np.exp(R - R.max(axis=(1, 2), keepdims=True)), 20)
+    maps_in = np.concatenate([pre_i, post_i, res_i.reshape(T, 4)], 1).astype(np.float32)
+    mi = torch.from_numpy(maps_in).cuda()
+    mo = torch.empty(T, 8, dtype=torch.float32, device="cuda")
+    w = _dev_normal((8, 2 * C), 24, 0.02, torch.float32)
+    bb = _dev_normal((8,), 25, 0.02, torch.float32)
+    gamma = torch.ones(C, dtype=torch.float32, device="cuda")
+    u = torch.empty(T, C, dtype=torch.bfloat16, device="cuda")
+    nb = A.loop_op_mhc_bytes(C)
+    scr = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    A.loop_op_mhc(A.LOOP_BF16, A.LOOP_MHC_MID, T, C, 20, 1e-6, y.data_ptr(), None, X.data_ptr(), mi.data_ptr(),
+                  mo.data_ptr(), w.data_ptr(), bb.data_ptr(), gamma.data_ptr(), u.data_ptr(), scr.data_ptr(), nb,
+                  _stream())
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    toks = np.unique(np.concatenate([rng.integers(0, T, 48), [0, T - 1]]))
+    tt = torch.from_numpy(toks).cuda()
+    x_old = _bf16(X0[tt])
+    y_h = _bf16(y[tt])
+    W = w.cpu().numpy().astype(np.float64)
+    Bv = bb.cpu().numpy().astype(np.float64)
+    mi_s = maps_in[toks].astype(np.float64)
+    Xn = M.round_bf16(np.einsum("tij,tjc->tic", mi_s[:, 4:8].reshape(-1, 2, 2), x_old)
+                      + mi_s[:, 2:4, None] * y_h[:, None, :])
+    pre, post, res, _ = M.mhc_maps(Xn, W, Bv, 20, 1e-6)
+    x_in = pre[:, 0:1] * Xn[:, 0] + pre[:, 1:2] * Xn[:, 1]
+    u_ref = M.rmsnorm(x_in, np.ones(C), 1e-6)
+    gX = _bf16(X[tt])
+    # both sides round to bf16 once; they may land one ulp (<= 2^-7 |x|) apart
+    dX = np.abs(gX - Xn) / np.maximum(2.0 ** -7 * np.abs(Xn), 1e-30)
+    print("mhc X' max diff in ulp bound:", float(dX.max()), "flips:", int((gX != Xn).sum()), flush=True)
+    assert dX.max() <= 1.0
+    gm = mo[tt].cpu().numpy().astype(np.float64)
+    ref_maps = np.concatenate([pre, post, res.reshape(-1, 4)], 1)
+    assert np.abs(gm - ref_maps).max() < 1e-4
+    assert np.abs(gm[:, 4:8].reshape(-1, 2, 2).sum(1) - 1).max() < 1e-5     # columns
+    gu = _bf16(u[tt])
+    assert np.all(np.abs(gu - u_ref) <= 2.0 ** -6 * np.abs(u_ref) + 1e-3)
+
+
+# ------------------------------------------------------------------ attention
+def test_full_attention_prefill_full_size_sampled():
+    """One full-attention execution of the 32K prefill: B=1, S=32768, 32 q / 8 kv heads."""
+    need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    S = 32768
+    q = _dev_normal((S, QKV), 31)            # q columns of the QKV output row
+    k = _dev_normal((1, HKV, S, D), 32)
+    vt = torch.empty(1, HKV, D, S, dtype=torch.bfloat16, device="cuda")
+    from synth import device as sd
+    sd.fill_normal4(vt.data_ptr(), True, (1, HKV, S, D), (HKV * D * S, D * S, 1, S), SEED, 33, 1.0,
+                    stream=_stream())
+    out = torch.empty(S, HQ * D, dtype=torch.bfloat16, device="cuda")
+    A.loop_op_attention(A.LOOP_BF16, 1, S, 0, S, HQ, HKV, D, q.data_ptr(), QKV, k.data_ptr(), vt.data_ptr(),
+                        out.data_ptr(), HQ * D, _stream())
+    torch.cuda.synchronize()
+    for pos, head in [(0, 0), (31, 5), (4095, 13), (20000, 30), (S - 1, 31), (S - 1, 2)]:
+        kvh = head // (HQ // HKV)
+        qr = synth.normal_bf16_as_f32(SEED, 31, (QKV,), start=pos * QKV)[head * D:(head + 1) * D]
+        K = synth.normal_bf16_as_f32(SEED, 32, (pos + 1, D), start=(kvh * S) * D)
+        Vv = synth.normal_bf16_as_f32(SEED, 33, (pos + 1, D), start=(kvh * S) * D)
+        ref = M.full_attention(qr[None, None, None, :], K[None, :, None, :], Vv[None, :, None, :], pos)[0, 0, 0]
+        got = out[pos, head * D:(head + 1) * D].float().cpu().numpy()
+        err = np.abs(got - ref).max() / np.abs(ref).max()
+        print("attn", pos, head, err, flush=True)
+        assert err < 2e-2
+
+
+def test_decode_attention_full_size_sampled():
+    """B=32 sequences of 32,768 cached positions + 1 new, 8 KV heads."""
+    need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    from synth import device as sd
+    B, ctx = 32, 32768
+    Smax = 32832
+    kc = torch.zeros(B, HKV, Smax, D, dtype=torch.bfloat16, device="cuda")
+    vt = torch.zeros(B, HKV, D, Smax, dtype=torch.bfloat16, device="cuda")
+    L = ctx + 1
+    sd.fill_normal4(kc.data_ptr(), True, (B, HKV, L, D), (HKV * Smax * D, Smax * D, D, 1), SEED, 41, 1.0,
+                    stream=_stream())
+    sd.fill_normal4(vt.data_ptr(), True, (B, HKV, L, D), (HKV * D * Smax, D * Smax, 1, Smax), SEED, 42, 1.0,
+                    stream=_stream())
+    q = _dev_normal((B, QKV), 43)
+    out = torch.empty(B, HQ * D, dtype=torch.bfloat16, device="cuda")
+    nb = A.loop_op_attention_decode_bytes(B, 1, HQ, D, Smax)
+    scr = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    A.loop_op_attention_decode(A.LOOP_BF16, B, 1, ctx, Smax, HQ, HKV, D, q.data_ptr(), QKV, kc.data_ptr(),
+                               vt.data_ptr(), out.data_ptr(), HQ * D, scr.data_ptr(), nb, _stream())
+    torch.cuda.synchronize()
+    for b, head in [(0, 0), (7, 9), (31, 31), (16, 4)]:
+        kvh = head // (HQ // HKV)
+        qr = synth.normal_bf16_as_f32(SEED, 43, (QKV,), start=b * QKV)[head * D:(head + 1) * D]
+        base = ((b * HKV + kvh) * L) * D
+        K = synth.normal_bf16_as_f32(SEED, 41, (L, D), start=base)
+        Vv = synth.normal_bf16_as_f32(SEED, 42, (L, D), start=base)
+        ref = M.full_attention(qr[None, None, None, :], K[None, :, None, :], Vv[None, :, None, :], ctx)[0, 0, 0]
+        got = out[b, head * D:(head + 1) * D].float().cpu().numpy()
+        err = np.abs(got - ref).max() / np.abs(ref).max()
+        print("decode attn", b, head, err, flush=True)
+        assert err < 2e-2
+
+
+# ------------------------------------------------------------------ linear attention
+def test_linear_attention_chunked_full_size_sampled():
+    """One linear-attention execution of the 32K prefill, fresh state: outputs
+    of one KV group at sampled positions, and the final state of that group,
+    against the oracle's recurrence."""
+    need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    S = 32768
+    qkv = _dev_normal((S, QKV), 51)
+    out = torch.empty(S, HQ * D, dtype=torch.bfloat16, device="cuda")
+    St = torch.zeros(HKV, D, D, dtype=torch.float32, device="cuda")
+    zt = torch.zeros(HKV, D, dtype=torch.float32, device="cuda")
+    nb = A.loop_op_linear_bytes(1, S, HKV, D)
+    scr = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    A.loop_op_linear(A.LOOP_BF16, 1, 1, S, HQ, HKV, D, 1e-6, qkv.data_ptr(), QKV, St.data_ptr(), zt.data_ptr(), 1,
+                     out.data_ptr(), HQ * D, scr.data_ptr(), nb, _stream())
+    torch.cuda.synchronize()
+    kvh = 5
+    heads = list(range(kvh * 4, kvh * 4 + 4))
+    rows = synth.normal_bf16_as_f32(SEED, 51, (S, QKV))
+    q = rows[:, [h * D + i for h in heads for i in range(D)]].reshape(1, S, 4, D)
+    k = rows[:, (HQ + kvh) * D:(HQ + kvh + 1) * D].reshape(1, S, 1, D)
+    v = rows[:, (HQ + HKV + kvh) * D:(HQ + HKV + kvh + 1) * D].reshape(1, S, 1, D)
+    del rows
+    sample = [0, 1, 63, 64, 65, 1000, 4097, 16383, 20000, S - 1]
+    o, Sf, zf = M.linear_attention(q, k, v, np.zeros((1, 1, D, D)), np.zeros((1, 1, D)), 1e-6)
+    for t in sample:
+        for hi, h in enumerate(heads):
+            got = out[t, h * D:(h + 1) * D].float().cpu().numpy()
+            ref = o[0, t, hi]
+            assert np.abs(got - ref).max() <= 1e-2 * np.abs(ref).max(), (t, h)
+    gS = St[kvh].cpu().numpy()
+    assert np.abs(gS - Sf[0, 0]).max() <= 1e-4 * np.abs(Sf[0, 0]).max()
+    assert np.abs(zt[kvh].cpu().numpy() - zf[0, 0]).max() <= 1e-4 * np.abs(zf[0, 0]).max()
+
+
+def test_linear_attention_decode_prefilled_state():
+    """B=32 decode with pre-filled states S ~ N(0, 1), z = |N(0, 1)| (all outputs)."""
+    need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    B = 32
+    qkv = _dev_normal((B, QKV), 61)
+    S0 = _dev_normal((B, HKV, D, D), 62, 1.0, torch.float32)
+    from synth import device as sd
+    z0 = torch.empty(B, HKV, D, dtype=torch.float32, device="cuda")
+    sd.fill_tensor_normal(z0, SEED, 63, 1.0, absval=True)
+    S_host = S0.cpu().numpy().astype(np.float64)
+    z_host = z0.cpu().numpy().astype(np.float64)
+    out = torch.empty(B, HQ * D, dtype=torch.bfloat16, device="cuda")
+    A.loop_op_linear(A.LOOP_BF16, 0, B, 1, HQ, HKV, D, 1e-6, qkv.data_ptr(), QKV, S0.data_ptr(), z0.data_ptr(), 0,
+                     out.data_ptr(), HQ * D, None, 0, _stream())
+    torch.cuda.synchronize()
+    rows = synth.normal_bf16_as_f32(SEED, 61, (B, QKV))
+    q = rows[:, :HQ * D].reshape(B, 1, HQ, D)
+    k = rows[:, HQ * D:(HQ + HKV) * D].reshape(B, 1, HKV, D)
+    v = rows[:, (HQ + HKV) * D:].reshape(B, 1, HKV, D)
+    o, Sf, zf = M.linear_attention(q, k, v, S_host, z_host, 1e-6)
+    got = out.float().cpu().numpy().reshape(B, HQ, D)
+    ref = o[:, 0]
+    # the denominator of a pre-filled state can be small: compare per row
+    err = np.abs(got - ref).max(-1) / np.abs(ref).max(-1)
+    assert err.max() < 2e-2, err.max()
+    assert np.abs(S0.cpu().numpy() - Sf).max() <= 1e-5 * np.abs(Sf).max()
