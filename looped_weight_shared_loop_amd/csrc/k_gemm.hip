@@ -45,7 +45,7 @@ DEV void epi_one(const GemmArgs& a, int row, int col, float v) {
 // 256x256 workgroup tile; WN_ = 4: 8 waves as 2 (M) x 4 (N), each owning a
 // 128x64 sub-tile = 4x2 blocks of v_mfma_f32_32x32x16_bf16 (WN_ = 2: 4 waves
 // of 128x128).  Operands move global -> LDS with global_load_lds_dwordx4 (no
-// staging registers): BK = 32, four LDS stages, loads issued three tiles
+// staging registers): BK = 32, five LDS stages, loads issued four tiles
 // ahead, LDS fragment reads one k-substep ahead of the MFMAs.  Each
 // wave-instruction writes 1 KB of LDS (lane l at +16 l): rows 16 b .. 16 b + 15
 // of one operand tile, 64 B each; 16-byte chunk c of row r sits at
@@ -53,9 +53,9 @@ DEV void epi_one(const GemmArgs& a, int row, int col, float v) {
 // then the JB/2 matching up-row blocks, so each wave emits finished output
 // columns (128 per workgroup).  Tiles are walked in an XCD-aware order.
 constexpr int TBM = 256, TBN = 256;
-constexpr int DBK = 32, DST = 4;
+constexpr int DBK = 32, DST = 5;
 constexpr int DSTAGE = (TBM + TBN) * DBK;            // elements per stage (32 KB)
-constexpr int GEMM_DMA_LDS = DST * DSTAGE * 2;       // 128 KB
+constexpr int GEMM_DMA_LDS = DST * DSTAGE * 2;       // 160 KB
 
 DEV int dswz(int row, int chunk) { return row * DBK + ((chunk ^ ((row >> 2) & 3)) << 3); }
 
@@ -112,9 +112,13 @@ __global__ __launch_bounds__(128 * WN_, 1) void gemm_dma_kernel(GemmArgs a) {
     lofs[i] = blk * 512;   // elements: 1 KB per block
   }
   const int KT = a.K / DBK;
+  // Tiles past the end re-read the last tile into a stage nobody reads
+  // again, so every iteration issues the same number of loads and the
+  // steady-state loop has no branches (a branch merge makes the compiler
+  // drain all outstanding LDS reads).
   auto issue = [&](int kt) {
     bf16_t* st = smem + (kt % DST) * DSTAGE;
-    const int k0 = kt * DBK;
+    const int k0 = min(kt, KT - 1) * DBK;
 #pragma unroll
     for (int i = 0; i < NBW; ++i) {
       dma16(A + aoff[i] + k0, st + lofs[i]);
@@ -129,7 +133,6 @@ __global__ __launch_bounds__(128 * WN_, 1) void gemm_dma_kernel(GemmArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  for (int t = 0; t < DST - 1 && t < KT; ++t) issue(t);
   const int arow = wm * 128 + (lane & 31);
   const int brow = wn * WCOL + (lane & 31);
   // Software pipeline over k-substeps of 16: the fragments of the next
@@ -150,39 +153,59 @@ __global__ __launch_bounds__(128 * WN_, 1) void gemm_dma_kernel(GemmArgs a) {
 #pragma unroll
       for (int jb = 0; jb < JB; ++jb) acc[ib][jb] = mfma32(xa[ib], xb[jb], acc[ib][jb]);
   };
-  // tile t is complete for this wave once at most 2 NBW * min(KT - 1 - t, 2) loads remain
-  auto wait_tile = [&](int t) {
-    if (NBW == 2) {
-      if (t + 2 < KT) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else if (t + 1 < KT) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    } else {
-      if (t + 2 < KT) asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-      else if (t + 1 < KT) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
+  // Tile j is issued (into stage j % DST) right after the barrier of iteration
+  // j - DST + 1.  That barrier guarantees only that every wave has CONSUMED its
+  // reads of tile j - DST (their MFMAs ran in the previous iteration), so the
+  // issue targets exactly that tile's stage; the stage of the tile being read
+  // in this iteration is never written.  Before waiting for tile j at
+  // iteration j - 1, the tiles j + 1 .. j + DST - 3 may stay in flight:
+  // (DST - 3) * 2 NBW loads (the prologue waits for tile 0 with DST - 2 tiles
+  // issued behind it... i.e. (DST - 2) * 2 NBW remaining).
+  static_assert(DST == 5, "wait counts below assume five stages");
+  auto wait_prologue = [&]() {
+    if (NBW == 2) asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
   };
-  wait_tile(0);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  if (DST - 1 < KT) issue(DST - 1);
+  auto wait_tile = [&]() {
+    if (NBW == 2) asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+  };
+  // After the barrier every wave's own loads of the waited tile have landed
+  // (the wait above), so the whole tile is in LDS.  No memory fence: that
+  // would drain the loads still in flight for later tiles.
+  auto sync = [&]() {
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+  for (int t = 0; t < DST - 1; ++t) issue(t);
+  wait_prologue();
+  sync();
   read_frags(0, 0, fa[0], fb[0]);
-  for (int kt = 0; kt < KT; ++kt) {
+  // Interleave the 4 + JB fragment reads of the next substep one-to-one with
+  // the MFMAs of the current one, MFMA first (scheduling groups: MFMA, DS read).
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4 + JB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * JB - (4 + JB), 0);
+  };
+  for (int kt = 0; kt + 1 < KT; ++kt) {
     read_frags(kt, 1, fa[1], fb[1]);
     mma(fa[0], fb[0]);
-    if (kt + 1 < KT) {
-      // Each wave waits for its own loads of tile kt + 1; after the barrier
-      // the whole tile is in LDS and every wave has consumed its reads of
-      // stage (kt - 1) % DST, which the next issue overwrites.  No memory
-      // fence: that would drain the loads still in flight for later tiles.
-      wait_tile(kt + 1);
-      __builtin_amdgcn_s_barrier();
-      __atomic_signal_fence(__ATOMIC_SEQ_CST);
-      if (kt + DST < KT) issue(kt + DST);
-      read_frags(kt + 1, 0, fa[0], fb[0]);
-    }
+    interleave();
+    wait_tile();
+    sync();
+    issue(kt + DST - 1);      // into the stage of tile kt - 1, consumed before this barrier
+    read_frags(kt + 1, 0, fa[0], fb[0]);
     mma(fa[1], fb[1]);
+    interleave();
   }
+  read_frags(KT - 1, 1, fa[1], fb[1]);
+  mma(fa[0], fb[0]);
+  mma(fa[1], fb[1]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
 
   if (EPI == EPI_SWIGLU) {
 #pragma unroll

@@ -125,10 +125,14 @@ def test_mhc_isolated_full_size_sampled():
     x_in = pre[:, 0:1] * Xn[:, 0] + pre[:, 1:2] * Xn[:, 1]
     u_ref = M.rmsnorm(x_in, np.ones(C), 1e-6)
     gX = _bf16(X[tt])
-    # both sides round to bf16 once; they may land one ulp (<= 2^-7 |x|) apart
-    dX = np.abs(gX - Xn) / np.maximum(2.0 ** -7 * np.abs(Xn), 1e-30)
-    print("mhc X' max diff in ulp bound:", float(dX.max()), "flips:", int((gX != Xn).sum()), flush=True)
-    assert dX.max() <= 1.0
+    # Both sides round once to bf16 and may land one ulp (<= 2^-7 |x|) apart;
+    # when the three terms cancel, the float32 sum itself carries an error of
+    # a few float32 ulps of the largest term.
+    terms = (np.abs(mi_s[:, 4:8].reshape(-1, 2, 2)) @ np.abs(x_old)) + np.abs(mi_s[:, 2:4, None] * y_h[:, None, :])
+    bound = 2.0 ** -7 * np.abs(Xn) + 4 * 2.0 ** -24 * terms
+    print("mhc X' worst diff / bound:", float((np.abs(gX - Xn) / bound).max()),
+          "flips:", int((gX != Xn).sum()), flush=True)
+    assert np.all(np.abs(gX - Xn) <= bound)
     gm = mo[tt].cpu().numpy().astype(np.float64)
     ref_maps = np.concatenate([pre, post, res.reshape(-1, 4)], 1)
     assert np.abs(gm - ref_maps).max() < 1e-4
