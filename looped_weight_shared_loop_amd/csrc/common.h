@@ -14,11 +14,14 @@ typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 DEV float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// Round to nearest, ties to even (inputs are finite).
-DEV bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Round to nearest, ties to even: one v_cvt_pk_bf16_f32.
+DEV bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
+// Two floats to a packed bf16 pair (a in the low half).
+DEV uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 DEV float round_to(float v, bf16_t*) { return bf2f(f2bf(v)); }
@@ -49,7 +52,7 @@ DEV void ld8(const float* p, float* v) {
 DEV void st8(bf16_t* p, const float* v) {
   uint32_t w[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f2bf(v[2 * i]) | ((uint32_t)f2bf(v[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) w[i] = pack_bf16x2(v[2 * i], v[2 * i + 1]);
   *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 DEV void st8(float* p, const float* v) {

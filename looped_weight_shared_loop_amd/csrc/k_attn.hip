@@ -124,42 +124,55 @@ __global__ __launch_bounds__(NTHR, 2) void attn_prefill_mfma(AttnArgs a) {
           st[c] = mfma32(kf, qf[ds], st[c]);
         }
       }
-      // st[c][r]: key kt*64 + c*32 + (r/4)*8 + h*4 + r%4, query column `col`
+      // st[c][r]: key kt*64 + c*32 + (r/4)*8 + h*4 + r%4, query column `col`.
+      // Only tiles reaching past the first query of the block need the mask.
+      const bool diag = kt * PK + PK - 1 > a.pos0 + q0;
       float tmax = -INFINITY;
+      if (diag) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kt * PK + c * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-          const float v = (key <= qpos && key < kv_end) ? st[c][r] * sc : -INFINITY;
-          st[c][r] = v;
-          tmax = fmaxf(tmax, v);
-        }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt * PK + c * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
+            const float v = (key <= qpos && key < kv_end) ? st[c][r] : -INFINITY;
+            st[c][r] = v;
+            tmax = fmaxf(tmax, v);
+          }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[c][r]);
+      }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sc;     // scaled (base-2) units
       const float mnew = fmaxf(mrun, tmax);
-      const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
+      const float mfin = (mnew == -INFINITY) ? 0.f : mnew;
       float psum = 0.f;
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = (mnew == -INFINITY) ? 0.f : exp2f(st[c][r] - mnew);
+          const float p = exp2f(fmaf(st[c][r], sc, -mfin));
           st[c][r] = p;
           psum += p;
         }
-      lrun = lrun * alpha + psum;
+      // O and l are rescaled only when some lane's running max moved.
+      if (__any(mnew > mrun)) {
+        const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
+        lrun *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      }
+      lrun += psum;
       mrun = mnew;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm) {
         const int c = mm >> 1, half = mm & 1;
         uint32_t pw[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          pw[e] = (uint32_t)f2bf(st[c][half * 8 + 2 * e]) | ((uint32_t)f2bf(st[c][half * 8 + 2 * e + 1]) << 16);
+        for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(st[c][half * 8 + 2 * e], st[c][half * 8 + 2 * e + 1]);
         const bf16x8_t pf = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
         const int kbase = c * 32 + half * 16 + h * 4;   // keys kbase+0..3 and kbase+8..11
 #pragma unroll
@@ -183,8 +196,8 @@ __global__ __launch_bounds__(NTHR, 2) void attn_prefill_mfma(AttnArgs a) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int d0 = db * 32 + g4 * 8 + h * 4;
-        const uint32_t w0 = (uint32_t)f2bf(o[db][g4 * 4] * inv) | ((uint32_t)f2bf(o[db][g4 * 4 + 1] * inv) << 16);
-        const uint32_t w1 = (uint32_t)f2bf(o[db][g4 * 4 + 2] * inv) | ((uint32_t)f2bf(o[db][g4 * 4 + 3] * inv) << 16);
+        const uint32_t w0 = pack_bf16x2(o[db][g4 * 4] * inv, o[db][g4 * 4 + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(o[db][g4 * 4 + 2] * inv, o[db][g4 * 4 + 3] * inv);
         *(u32x2_t*)(O + d0) = u32x2_t{w0, w1};
       }
   }
@@ -266,8 +279,8 @@ __global__ __launch_bounds__(64) void attn_decode_mfma(AttnArgs a) {
       uint32_t pw[4];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        pw[e] = (uint32_t)f2bf(st[2 * kk][2 * e]) | ((uint32_t)f2bf(st[2 * kk][2 * e + 1]) << 16);
-        pw[2 + e] = (uint32_t)f2bf(st[2 * kk + 1][2 * e]) | ((uint32_t)f2bf(st[2 * kk + 1][2 * e + 1]) << 16);
+        pw[e] = pack_bf16x2(st[2 * kk][2 * e], st[2 * kk][2 * e + 1]);
+        pw[2 + e] = pack_bf16x2(st[2 * kk + 1][2 * e], st[2 * kk + 1][2 * e + 1]);
       }
       const bf16x8_t pf = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
       const int key0 = k0 + 32 * kk + 8 * g;
