@@ -27,12 +27,40 @@ METRIC = "looped-decoder tokens/sec (56 layer execs, 9B shape): prefill + decode
 PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
+# HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs
+# of `bench.py --profile-dominant` (FETCH_SIZE, then WRITE_SIZE, KiB per
+# dispatch), each scaled by the same counter's reading for a plain 1 GiB
+# device copy in that run.  Valid only for the kernel source it was taken on:
+# the hash of k_gemm.hip + common.h must match, else traffic is reported null.
+DOMINANT_COUNTERS = {"source_sha256_16": "8398e4ceba1dba96", "fetch_kib": 4723267.1, "write_kib": 786432.0,
+                     "copy_fetch_kib": 524316.7, "copy_write_kib": 1048576.0}
+
 NINE_B = dict(vocab=248320, hidden=4096, ffn=12288, n_heads=32, n_kv_heads=8, head_dim=128,
               n_layers=32, loop_start=4, loop_end=28, n_passes=2, dtype="bf16")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("k_gemm.hip", "common.h"):
+        with open(os.path.join(ROOT, "looped_weight_shared_loop_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def dominant_traffic():
+    """Measured HBM bytes per launch of the dominant kernel, or None when the
+    kernel source differs from the one the counters were read on."""
+    c = DOMINANT_COUNTERS
+    if gemm_source_hash() != c["source_sha256_16"]:
+        return None
+    fetch = c["fetch_kib"] * 1024 * ((1 << 30) / (c["copy_fetch_kib"] * 1024))
+    write = c["write_kib"] * 1024 * ((1 << 30) / (c["copy_write_kib"] * 1024))
+    return fetch + write
 
 
 def prefill_flops(cfg, S, B=1):
@@ -214,7 +242,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=16)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-seq", type=int, default=128)
+    ap.add_argument("--cpu-seq", type=int, default=1024)
+    ap.add_argument("--profile-dominant", action="store_true",
+                    help="only a 1 GiB device copy (counter scale reference) and 3 launches of the dominant kernel")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only (no cross-GPU path); run with --gpus 1", flush=True)
@@ -222,6 +252,17 @@ def main():
 
     import torch
     import looped_weight_shared_loop_amd as L
+
+    if args.profile_dominant:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")     # 1 GiB
+        dst = torch.empty_like(src)
+        dst.copy_(src)                                                   # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+        time_dominant_gemm(L, torch, args.seq, iters=3)
+        torch.cuda.synchronize()
+        print(json.dumps({"profile_dominant": "done", "copy_bytes": 1 << 30}), flush=True)
+        return
 
     cfg = L.ModelConfig(**NINE_B)
     log("generating random-init 9B-shape weights on the device")
@@ -236,6 +277,7 @@ def main():
 
     g_ms, g_flops = time_dominant_gemm(L, torch, S)
     g_tflops = g_flops / (g_ms / 1e3) / 1e12
+    traffic = dominant_traffic()
 
     result = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -246,9 +288,11 @@ def main():
         "prefill": {"tflops": round(tflops, 1), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                     "algorithmic_tflop": round(flops / 1e12, 2), "gemm_tflop": round(gemm_f / 1e12, 2),
                     "attention_tflop": round(attn_f / 1e12, 2), "linear_tflop": round(lin_f / 1e12, 3)},
-        "roofline": {"kernel": "gemm_mfma_kernel (SwiGLU gate/up, M=%d N=24576 K=4096)" % S, "bound": "mfma",
+        "roofline": {"kernel": "gemm_dma_kernel<EPI_SWIGLU> (gate/up, M=%d N=24576 K=4096)" % S, "bound": "mfma",
                      "achieved": round(g_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": (None if S != 32768 or traffic is None else round(traffic)),
+                     "algorithmic_bytes": (S * 4096 + 24576 * 4096 + S * 12288) * 2,
                      "avg_launch_ms": round(g_ms, 4)},
     }
     if not args.no_decode:

@@ -50,6 +50,35 @@ def test_synth_device_matches_host():
     assert np.array_equal(v.float().cpu().numpy()[:, :, :, :L], ref.transpose(0, 1, 3, 2))
 
 
+# ------------------------------------------------------------------ schedule
+@pytest.mark.parametrize("which", ["tiny", "nine_b"])
+def test_library_schedule_matches_oracle(which):
+    """The driver's execution table against the oracle's schedule: 56 (9B) or
+    12 (tiny) executions, full attention exactly at stored index % 4 == 3, and
+    one KV or linear-state slot per (layer, pass)."""
+    L = need_gpu()
+    from gpu_common import lib_config
+    ocfg = oracle.tiny_config() if which == "tiny" else oracle.nine_b_config()
+    gcfg = lib_config(ocfg)
+    # schedule only: every weight pointer may name one placeholder buffer (nothing is launched)
+    ph = torch.zeros(64, dtype=torch.float32, device="cuda")
+    names = ["embed", "final_norm", "head"]
+    for i in range(gcfg.n_layers):
+        names += [f"layers.{i}.{n}" for n in ("attn_norm", "ffn_norm", "qkv", "o", "gate_up", "down",
+                                              "mhc_w0", "mhc_b0", "mhc_w1", "mhc_b1")]
+    model = L.LoopModel(gcfg, {n: ph for n in names})
+    got = model.schedule()
+    ref = oracle.schedule(ocfg)
+    assert [(l, p) for (l, p, _, _) in got] == ref
+    assert len(got) == (56 if which == "nine_b" else 12)
+    assert all(k == (1 if l % 4 == 3 else 0) for (l, _, k, _) in got)
+    full_slots = [s for (_, _, k, s) in got if k == 1]
+    lin_slots = [s for (_, _, k, s) in got if k == 0]
+    assert full_slots == list(range(len(full_slots))) and lin_slots == list(range(len(lin_slots)))
+    if which == "nine_b":
+        assert (len(full_slots), len(lin_slots)) == (14, 42)
+
+
 # ------------------------------------------------------------------ tiny fp32
 @pytest.mark.parametrize("variant", ["tiny", "tiny_gqa"])
 def test_tiny_fp32_all_logits(variant):
