@@ -140,13 +140,13 @@ def time_dominant_gemm(L, torch, S, iters=10):
     stream = torch.cuda.current_stream().cuda_stream
     for _ in range(2):
         A.loop_op_gemm(A.LOOP_BF16, A.LOOP_EPI_SWIGLU, M, 2 * F, K, a.data_ptr(), K, b.data_ptr(), K, c.data_ptr(),
-                       F, F, stream)
+                       F, F, stream, None, 0)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(iters):
         A.loop_op_gemm(A.LOOP_BF16, A.LOOP_EPI_SWIGLU, M, 2 * F, K, a.data_ptr(), K, b.data_ptr(), K, c.data_ptr(),
-                       F, F, stream)
+                       F, F, stream, None, 0)
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / iters

@@ -27,11 +27,16 @@ enum { LOOP_MHC_ENTER = 0, LOOP_MHC_MID = 1, LOOP_MHC_EXIT = 2 };
  * fp32 accumulation (the QKV, O, gate/up, down and head projections).
  * epi STORE: C dtype [M][N]; F32: C float32 [M][N]; SWIGLU: B holds gate rows
  * [0, F) then up rows [F, 2F) (N = 2F) and C dtype [M][F] = silu(A.Bg^T) * (A.Bu^T).
- * bf16 needs K % 64 == 0 (M > 32) or K % 128 == 0 (M <= 32) and N (F for
- * SWIGLU) a multiple of 256 (M > 32; 128 for SWIGLU) or 32 (M <= 32; 16).
- * Errors: INVALID_ARG, SHAPE, ALIGN, HIP. */
+ * bf16 with M > 32 needs K % 32 == 0 and N (F for SWIGLU) a multiple of 256
+ * (128 for SWIGLU); bf16 with M <= 32 (the decode shape) needs K % 256 == 0.
+ * For M <= 32, `scratch` of loop_op_gemm_bytes() bytes (device, caller-owned,
+ * contents arbitrary) lets K be split over workgroups when the output tiles
+ * alone cannot fill the device; the partial sums are added in a fixed order,
+ * so results are deterministic.  scratch NULL: no split (same kernel, one
+ * workgroup per tile).  Errors: INVALID_ARG, SHAPE, ALIGN, WORKSPACE, HIP. */
+size_t loop_op_gemm_bytes(int dtype, int epi, int M, int N, int K, int F);
 int loop_op_gemm(int dtype, int epi, int M, int N, int K, const void* A, long lda, const void* B, long ldb,
-                 void* C, long ldc, int F, void* stream);
+                 void* C, long ldc, int F, void* scratch, size_t scratch_bytes, void* stream);
 
 /* Residual add + RMSNorm outside the looped block: h <- h + y (y may be NULL),
  * u <- gamma * h / sqrt(mean(h^2) + eps).  h, y, u dtype [T][C]; gamma float32 [C]. */
@@ -62,8 +67,11 @@ int loop_op_mhc(int dtype, int mode, int T, int C, int sinkhorn_iters, float eps
 int loop_op_attention(int dtype, int B, int S, int pos0, int S_max, int Hq, int Hkv, int d, const void* q, long ldq,
                       const void* kcache, const void* vcache, void* out, long ldo, void* stream);
 
-/* The decode form (split over the cache, then a combine): same contract, for
- * Hq / Hkv * S <= 16; needs `scratch` of loop_op_attention_decode_bytes(). */
+/* The decode form: same contract, for Hq / Hkv * S <= 16.  The cache is split
+ * over workgroups only as far as needed to fill the device (none at B * Hkv >=
+ * the CU count); several splits are merged by a second kernel through
+ * `scratch` (caller-owned, loop_op_attention_decode_bytes() bytes, an upper
+ * bound for any Hkv and any pos0 + S <= S_max). */
 size_t loop_op_attention_decode_bytes(int B, int S, int Hq, int d, int S_max);
 int loop_op_attention_decode(int dtype, int B, int S, int pos0, int S_max, int Hq, int Hkv, int d, const void* q,
                              long ldq, const void* kcache, const void* vcache, void* out, long ldo, void* scratch,

@@ -76,8 +76,9 @@ SYMBOLS = {
     "loop_status_string": (ctypes.c_char_p, [c_int]),
     "loop_last_error": (ctypes.c_char_p, []),
     # op level (include/loop_ops.h)
+    "loop_op_gemm_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int, c_int]),
     "loop_op_gemm": (c_int, [c_int, c_int, c_int, c_int, c_int, c_void_p, ctypes.c_long, c_void_p, ctypes.c_long,
-                             c_void_p, ctypes.c_long, c_int, c_void_p]),
+                             c_void_p, ctypes.c_long, c_int, c_void_p, c_size_t, c_void_p]),
     "loop_op_add_rmsnorm": (c_int, [c_int, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p, c_float, c_void_p]),
     "loop_op_mhc_bytes": (c_size_t, [c_int]),
     "loop_op_mhc": (c_int, [c_int, c_int, c_int, c_int, c_int, c_float, c_void_p, c_void_p, c_void_p, c_void_p,
@@ -209,8 +210,13 @@ def _p(x):
     return None if x is None else c_void_p(x)
 
 
-def loop_op_gemm(dtype, epi, M, N, K, A, lda, B, ldb, C, ldc, F, stream) -> None:
-    _check(lib().loop_op_gemm(dtype, epi, M, N, K, _p(A), lda, _p(B), ldb, _p(C), ldc, F, _p(stream)), "loop_op_gemm")
+def loop_op_gemm_bytes(dtype, epi, M, N, K, F) -> int:
+    return lib().loop_op_gemm_bytes(dtype, epi, M, N, K, F)
+
+
+def loop_op_gemm(dtype, epi, M, N, K, A, lda, B, ldb, C, ldc, F, stream, scratch=None, scratch_bytes=0) -> None:
+    _check(lib().loop_op_gemm(dtype, epi, M, N, K, _p(A), lda, _p(B), ldb, _p(C), ldc, F, _p(scratch), scratch_bytes,
+                              _p(stream)), "loop_op_gemm")
 
 
 def loop_op_add_rmsnorm(dtype, T, C, y, h, gamma, u, eps, stream) -> None:

@@ -8,6 +8,7 @@
 // same weight pointers.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -42,7 +43,6 @@ struct Exec {
   int layer, pass, full, slot;
 };
 
-constexpr int DEC_SPLIT = 256;   // keys per decode-attention split
 constexpr int LIN_CHUNK = 64;
 
 }  // namespace
@@ -73,7 +73,7 @@ struct loop_state {
 namespace {
 
 struct WsLayout {
-  size_t h, X, u, y, qkv, attn, inter, maps, lin, dec, wsplit, total;
+  size_t h, X, u, y, qkv, attn, inter, maps, lin, dec, wsplit, skinny, skinny_bytes, total;
 };
 
 WsLayout ws_layout(const loop_model* m, int batch, int max_tokens, int max_seq) {
@@ -92,10 +92,27 @@ WsLayout ws_layout(const loop_model* m, int batch, int max_tokens, int max_seq) 
   w.maps = take(2 * T * 8 * sizeof(float));
   const size_t chunks = (T + LIN_CHUNK - 1) / LIN_CHUNK + (size_t)batch;
   w.lin = take(chunks * c.n_kv_heads * ((size_t)c.head_dim * c.head_dim + c.head_dim) * sizeof(float));
-  const size_t S_max = ((size_t)max_seq + 63) / 64 * 64;
-  const size_t nsplit = (S_max + DEC_SPLIT - 1) / DEC_SPLIT;
-  w.dec = take((size_t)batch * c.n_heads * nsplit * (c.head_dim + 2) * sizeof(float));
+  // decode-attention partials: a call with B' <= batch sequences uses
+  // B' * Hq * n_split(B') rows of d + 2 floats
+  const int S_max = (max_seq + 63) / 64 * 64;
+  size_t dec_rows = 0;
+  for (int b = 1; b <= batch; ++b)
+    dec_rows = std::max(dec_rows, (size_t)b * c.n_heads * lk::decode_max_splits(b, c.n_kv_heads, S_max, m->cu));
+  w.dec = take(dec_rows * (c.head_dim + 2) * sizeof(float));
   w.wsplit = take((size_t)16 * 2 * C * sizeof(uint16_t));
+  // split-K scratch of the decode-shaped GEMMs (the largest plan of the five projections)
+  size_t sk = 0;
+  if (c.dtype == LOOP_BF16 && max_tokens <= 32) {
+    const lk::SkinnyPlan p[5] = {
+        lk::skinny_plan(lk::EPI_QKV, m->qkv_rows(), C, 0, m->cu),
+        lk::skinny_plan(lk::EPI_STORE, C, c.n_heads * c.head_dim, 0, m->cu),
+        lk::skinny_plan(lk::EPI_SWIGLU, 2 * c.ffn, C, c.ffn, m->cu),
+        lk::skinny_plan(lk::EPI_STORE, C, c.ffn, 0, m->cu),
+        lk::skinny_plan(lk::EPI_F32, c.vocab, C, 0, m->cu)};
+    for (const auto& q : p) sk = std::max(sk, q.bytes);
+  }
+  w.skinny = take(sk);
+  w.skinny_bytes = sk;
   w.total = off;
   return w;
 }
@@ -408,6 +425,20 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
     if (mode != lk::MHC_EXIT) mp ^= 1;
     return e;
   };
+  // decode-shaped GEMMs split K over workgroups when the workspace holds the scratch
+  auto run_gemm = [&](lk::GemmArgs g) {
+    g.ksplit = 1;
+    g.skinny_rb = 4;
+    if (g.dt == lk::DT_BF16 && g.M <= 32) {
+      const lk::SkinnyPlan p = lk::skinny_plan(g.epi, g.N, g.K, g.F, m->cu);
+      g.skinny_rb = p.rb;
+      if (p.ksplit > 1 && p.bytes <= L.skinny_bytes) {
+        g.ksplit = p.ksplit;
+        g.part = (float*)(ws + L.skinny);
+      }
+    }
+    return lk::gemm(g, s);
+  };
   auto gemm = [&](int epi, const void* A, long lda, int M, const void* Bw, int N, int K, void* Cout, long ldc) {
     lk::GemmArgs g{};
     g.dt = dt; g.epi = epi; g.M = M; g.N = N; g.K = K;
@@ -436,19 +467,20 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
       g.kcache = st->base + st->koff[ex.slot];
       g.vcache = st->base + st->voff[ex.slot];
       g.S_call = S; g.pos0 = pos0; g.S_max = st->S_max;
-      LAUNCH(lk::gemm(g, s), "qkv gemm");
+      LAUNCH(run_gemm(g), "qkv gemm");
       lk::AttnArgs a{};
       a.dt = dt; a.B = B; a.S_call = S; a.pos0 = pos0; a.S_max = st->S_max; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
       a.q = qkv; a.ldq = qkv_rows; a.kcache = g.kcache; a.vcache = g.vcache; a.out = attn; a.ldo = Hq * d;
       if (decode && dt == lk::DT_BF16) {
-        a.part = dec_part; a.split_len = DEC_SPLIT; a.n_split = (pos0 + S + DEC_SPLIT - 1) / DEC_SPLIT;
+        const lk::DecodePlan dp = lk::decode_plan(B, Hkv, pos0 + S, m->cu);
+        a.part = dec_part; a.split_len = dp.split_len; a.n_split = dp.n_split;
         LAUNCH(lk::attn_decode(a, s), "decode attention");
       } else {
         LAUNCH(lk::attn_prefill(a, s), "prefill attention");
       }
     } else {
       lk::GemmArgs g = gemm(lk::EPI_STORE, u, C, T, W.qkv, qkv_rows, C, qkv, qkv_rows);
-      LAUNCH(lk::gemm(g, s), "qkv gemm");
+      LAUNCH(run_gemm(g), "qkv gemm");
       lk::LinArgs a{};
       a.dt = dt; a.B = B; a.S_call = S; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.eps = c.la_eps;
       a.qkv = qkv; a.ld = qkv_rows;
@@ -459,7 +491,7 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
       if (S <= 16) { LAUNCH(lk::lin_decode(a, s), "linear attention (recurrent)"); }
       else { LAUNCH(lk::lin_prefill(a, s), "linear attention (chunked)"); }
     }
-    LAUNCH(lk::gemm(gemm(lk::EPI_STORE, attn, Hq * d, T, W.o, C, Hq * d, y, C), s), "o gemm");
+    LAUNCH(run_gemm(gemm(lk::EPI_STORE, attn, Hq * d, T, W.o, C, Hq * d, y, C)), "o gemm");
     // ---- attention -> FFN transition
     if (looped) {
       LAUNCH(mhc(lk::MHC_MID, y, W.mhc_w[1], W.mhc_b[1], W.ffn_norm), "mhc");
@@ -470,9 +502,9 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
     {
       lk::GemmArgs g = gemm(lk::EPI_SWIGLU, u, C, T, W.gate_up, 2 * c.ffn, C, inter, c.ffn);
       g.F = c.ffn;
-      LAUNCH(lk::gemm(g, s), "gate/up gemm");
+      LAUNCH(run_gemm(g), "gate/up gemm");
     }
-    LAUNCH(lk::gemm(gemm(lk::EPI_STORE, inter, c.ffn, T, W.down, C, c.ffn, y, C), s), "down gemm");
+    LAUNCH(run_gemm(gemm(lk::EPI_STORE, inter, c.ffn, T, W.down, C, c.ffn, y, C)), "down gemm");
     // ---- transition to the next execution (or the final norm)
     const bool has_next = e + 1 < E;
     const loop_layer_weights* Wn = has_next ? &m->layers[sched[e + 1].layer] : nullptr;
@@ -494,10 +526,10 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
   if (flags & LOOP_HIDDEN_OUT) {
     LAUNCH(hipMemcpyAsync(out, h, (size_t)T * C * m->es, hipMemcpyDeviceToDevice, s), "copy hidden");
   } else if (flags & LOOP_ALL_LOGITS) {
-    LAUNCH(lk::gemm(gemm(lk::EPI_F32, u, C, T, m->head, c.vocab, C, out, c.vocab), s), "head gemm");
+    LAUNCH(run_gemm(gemm(lk::EPI_F32, u, C, T, m->head, c.vocab, C, out, c.vocab)), "head gemm");
   } else {
     const char* last = (const char*)u + (size_t)(S - 1) * C * m->es;
-    LAUNCH(lk::gemm(gemm(lk::EPI_F32, last, (long)S * C, B, m->head, c.vocab, C, out, c.vocab), s), "head gemm");
+    LAUNCH(run_gemm(gemm(lk::EPI_F32, last, (long)S * C, B, m->head, c.vocab, C, out, c.vocab)), "head gemm");
   }
   st->length = pos0 + S;
   return LOOP_OK;

@@ -10,8 +10,9 @@
 //   which leaves each lane with one query column; the probabilities feed
 //   O^T = V^T P^T directly from registers.  Online softmax in fp32 (base 2).
 // * attn_decode_mfma (bf16, d = 128, up to 16 query columns = heads x new
-//   tokens): split-K over the cache, v_mfma_f32_16x16x32_bf16, operands read
-//   straight from the cache, then a combine kernel.
+//   tokens): eight waves per (split, KV head, sequence), splits only as many
+//   as needed to fill the device, v_mfma_f32_16x16x32_bf16, operands read
+//   straight from the cache; a combine kernel when there are several splits.
 // * attn_f32: plain kernel for the fp32 configuration.
 #include "common.h"
 #include "kernels.h"
@@ -204,16 +205,44 @@ __global__ __launch_bounds__(NTHR, 2) void attn_prefill_mfma(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ decode, bf16
-// One wave per (split, KV head, sequence).  Query columns c < ncol are
-// (token t = c / G, head kvh*G + c % G).  A round covers 64 keys: four S^T
-// blocks of 16 keys whose rows are ordered so that, for PV step kk, lane group
-// g holds the probabilities of keys 32kk + 8g + 0..7, matching a contiguous
-// 16-byte read of V^T.
-__global__ __launch_bounds__(64) void attn_decode_mfma(AttnArgs a) {
+// One workgroup of DW waves per (split, KV head, sequence); wave w takes the
+// 64-key rounds w, w + DW, ... of the split, so the waves stream neighbouring
+// cache lines together.  Query columns c < ncol are (token t = c / G, head
+// kvh*G + c % G).  A round loads its K rows and its V^T columns at once
+// (32 KB per wave in flight), then computes four S^T blocks of 16 keys whose
+// rows are ordered so that, for PV step kk, lane group g holds the
+// probabilities of keys 32kk + 8g + 0..7, matching a contiguous 16-byte read
+// of V^T.  The waves' (max, sum, O) are merged in LDS by a fixed tree
+// (w + 4 into w, then w + 2, then w + 1).  A single split writes the output;
+// several splits write fp32 partials for attn_combine.
+constexpr int DW = 8;
+
+DecodePlan decode_plan(int B, int Hkv, int kv_len, int cu) {
+  DecodePlan p{};
+  const int groups = B * Hkv > 0 ? B * Hkv : 1;
+  int want = (cu + groups - 1) / groups;
+  if (want < 1) want = 1;
+  int len = (kv_len + want - 1) / want;
+  len = (len + 63) / 64 * 64;
+  if (len < 64) len = 64;
+  p.split_len = len;
+  p.n_split = (kv_len + len - 1) / len;
+  return p;
+}
+
+int decode_max_splits(int B, int Hkv, int S_max, int cu) {
+  const int groups = B * Hkv > 0 ? B * Hkv : 1;
+  const int want = (cu + groups - 1) / groups;
+  const int cap = (S_max + 63) / 64;
+  return want < 1 ? 1 : (want < cap ? want : cap);
+}
+
+__global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
+  __shared__ float mrg[DW / 2][16][PD + 2];   // o[0..127], max, sum per column
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
   const int ncol = G * a.S_call;
-  const int lane = threadIdx.x, g = lane >> 4, c = lane & 15;
+  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const bool cvalid = c < ncol;
   const int tq = cvalid ? c / G : 0, jq = kvh * G + (cvalid ? c % G : 0);
   const int kv_len = a.pos0 + a.S_call;           // keys [0, kv_len) exist
@@ -236,15 +265,28 @@ __global__ __launch_bounds__(64) void attn_decode_mfma(AttnArgs a) {
   for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lrun = 0.f;
 
-  for (int k0 = k_begin; k0 < k_end; k0 += 64) {
+  for (int k0 = k_begin + wid * 64; k0 < k_end; k0 += DW * 64) {
+    // loads of the whole round first: K rows (S^T operand) and V^T (PV operand).
+    // Keys past k_end stay inside the slot (S_max % 64 == 0) and are masked.
+    u32x4_t kf[4][4], vf[2][8];
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb) {
+      const int key = k0 + 32 * (sb >> 1) + (c >> 2) * 8 + (sb & 1) * 4 + (c & 3);
+      const bf16_t* kr = Kg + (size_t)key * PD + g * 8;
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) kf[sb][ds] = ldv4(kr + ds * 32);
+    }
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int db = 0; db < 8; ++db) vf[kk][db] = ldv4(Vg + (size_t)(db * 16 + c) * a.S_max + k0 + 32 * kk + 8 * g);
+
     f32x4_t st[4];
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
       st[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const int key = k0 + 32 * (sb >> 1) + (c >> 2) * 8 + (sb & 1) * 4 + (c & 3);
-      const bf16_t* kr = Kg + (size_t)key * PD + g * 8;
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) st[sb] = mfma16(as_bf16x8(ldv4(kr + ds * 32)), qf[ds], st[sb]);
+      for (int ds = 0; ds < 4; ++ds) st[sb] = mfma16(as_bf16x8(kf[sb][ds]), qf[ds], st[sb]);
     }
     // st[sb][i]: column c, key k0 + 32*(sb/2) + 8g + 4*(sb%2) + i
     float tmax = -INFINITY;
@@ -282,11 +324,13 @@ __global__ __launch_bounds__(64) void attn_decode_mfma(AttnArgs a) {
         pw[e] = pack_bf16x2(st[2 * kk][2 * e], st[2 * kk][2 * e + 1]);
         pw[2 + e] = pack_bf16x2(st[2 * kk + 1][2 * e], st[2 * kk + 1][2 * e + 1]);
       }
+      // probabilities of masked keys are exactly 0, but V there may hold any
+      // bits (a NaN pattern would poison 0 * v): clear V past the end
       const bf16x8_t pf = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
       const int key0 = k0 + 32 * kk + 8 * g;
 #pragma unroll
       for (int db = 0; db < 8; ++db) {
-        u32x4_t v = ldv4(Vg + (size_t)(db * 16 + c) * a.S_max + key0);
+        u32x4_t v = vf[kk][db];
         if (key0 + 8 > k_end) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
@@ -296,16 +340,53 @@ __global__ __launch_bounds__(64) void attn_decode_mfma(AttnArgs a) {
       }
     }
   }
-  // partial row sums of a column live in 4 lane groups
+  // full row sum of a column (its four lane groups)
   float ltot = lrun + __shfl_xor(lrun, 16, 64);
   ltot += __shfl_xor(ltot, 32, 64);
-  if (cvalid) {
-    float* P = a.part + ((((size_t)(b * a.S_call + tq) * a.Hq + jq) * a.n_split) + s) * (PD + 2);
+
+  // merge waves: step h = 4, 2, 1: waves [h, 2h) hand their state to w - h
+  for (int h = DW / 2; h >= 1; h >>= 1) {
+    if (wid >= h && wid < 2 * h) {
+      float* slot = &mrg[wid - h][c][0];
 #pragma unroll
-    for (int db = 0; db < 8; ++db)
-      *(float4*)(P + db * 16 + g * 4) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
-    if (g == 0) { P[PD] = mrun; P[PD + 1] = ltot; }
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) slot[db * 16 + g * 4 + i] = o[db][i];
+      if (g == 0) { slot[PD] = mrun; slot[PD + 1] = ltot; }
+    }
+    __syncthreads();
+    if (wid < h) {
+      const float* slot = &mrg[wid][c][0];
+      const float m2 = slot[PD], l2 = slot[PD + 1];
+      const float M = fmaxf(mrun, m2);
+      const float a1 = (mrun == -INFINITY) ? 0.f : exp2f(mrun - M);
+      const float a2 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - M);
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[db][i] = o[db][i] * a1 + slot[db * 16 + g * 4 + i] * a2;
+      ltot = ltot * a1 + l2 * a2;
+      mrun = M;
+    }
+    __syncthreads();
   }
+  if (wid != 0 || !cvalid) return;
+  if (a.n_split == 1) {
+    const float inv = 1.f / ltot;
+    bf16_t* O = (bf16_t*)a.out + (size_t)(b * a.S_call + tq) * a.ldo + jq * PD;
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const uint32_t w0 = pack_bf16x2(o[db][0] * inv, o[db][1] * inv);
+      const uint32_t w1 = pack_bf16x2(o[db][2] * inv, o[db][3] * inv);
+      *(u32x2_t*)(O + db * 16 + g * 4) = u32x2_t{w0, w1};
+    }
+    return;
+  }
+  float* P = a.part + ((((size_t)(b * a.S_call + tq) * a.Hq + jq) * a.n_split) + s) * (PD + 2);
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+    *(float4*)(P + db * 16 + g * 4) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
+  if (g == 0) { P[PD] = mrun; P[PD + 1] = ltot; }
 }
 
 // out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
@@ -399,9 +480,9 @@ hipError_t attn_decode(const AttnArgs& a, hipStream_t s) {
   const int kv_len = a.pos0 + a.S_call;
   if ((long)a.n_split * a.split_len < kv_len) return hipErrorInvalidValue;
   dim3 grid(a.n_split, a.Hkv, a.B);
-  attn_decode_mfma<<<grid, 64, 0, s>>>(a);
+  attn_decode_mfma<<<grid, 64 * DW, 0, s>>>(a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || a.n_split == 1) return e;
   attn_combine<bf16_t><<<a.B * a.S_call * a.Hq, 128, 0, s>>>(a);
   return hipGetLastError();
 }

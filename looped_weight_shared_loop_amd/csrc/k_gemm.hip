@@ -1,11 +1,12 @@
 // Dense contractions of the looped decoder: C[M, N] = A[M, K] . B[N, K]^T.
 //
 // * gemm_dma:    bf16, M > 32.  256x256 workgroup tile, 8 waves of 128x64
-//                (v_mfma_f32_32x32x16_bf16), global -> LDS DMA through four
+//                (v_mfma_f32_32x32x16_bf16), global -> LDS DMA through five
 //                LDS stages, XCD-aware tile order.  fp32 accumulation.
-// * gemm_skinny: bf16, M <= 32 (decode): streams B (the weights) once; each of
-//                8 waves takes 1/8 of K for a 32-row block of B, then the
-//                partial 32x32 blocks are summed in LDS in a fixed order.
+// * gemm_skinny: bf16, M <= 32 (decode): streams B (the weights) once; 64- or
+//                128-row tiles, K split over 4 waves and, when the tiles cannot fill
+//                the device, over workgroups (partials summed in index order
+//                by a second kernel).
 // * gemm_f32:    fp32 configuration: LDS-tiled FMA kernel.
 // All share one epilogue: plain bf16/fp32 store, fp32 logits, the QKV split
 // that writes K and V into a per-(layer, pass) cache slot, or SwiGLU.
@@ -236,72 +237,186 @@ __global__ __launch_bounds__(128 * WN_, 1) void gemm_dma_kernel(GemmArgs a) {
 }
 
 // ------------------------------------------------------------------ skinny (M <= 32)
-// Block of 32 B rows (SwiGLU: 16 gate + 16 matching up rows); 8 waves split K.
-// MFMA A operand = B rows (weights), B operand = the <= 32 activation rows.
-// Lane l: B row (l & 31), token (l & 31); its half h = l >> 5 owns a
-// contiguous half of the wave's K range, 8 k per MFMA (the contraction index
-// is permuted identically on both operands, which leaves the sum unchanged).
-template <int EPI>
-__global__ __launch_bounds__(512) void gemm_skinny_kernel(GemmArgs a) {
-  __shared__ float red[8][32][33];
+// Decode shape: the weights B are streamed once, the <= 32 activation rows are
+// the MFMA's other operand.  A workgroup owns a tile of R = 32 RB B rows
+// (SwiGLU: R/2 gate rows and the R/2 matching up rows) and 1/ksplit of K; its
+// 4 waves split that K range again.  Wave operands for v_mfma_f32_32x32x16_bf16: A = B rows
+// (lane l: row l & 31), B = tokens (lane l: token l & 31).  Per 64-wide k step
+// lane half h = l >> 5 loads 64 contiguous bytes (k + 32 h .. k + 32 h + 31) of
+// its row, so each row's 128 B line is fetched whole; MFMA j contracts chunk j
+// of both halves, and both operands use the same k order, which leaves the
+// dot products unchanged.  The four waves are reduced in LDS in a fixed order.
+// ksplit == 1: the workgroup applies the epilogue.  ksplit > 1: it stores its
+// fp32 partial tile and gemm_skinny_reduce (the next kernel on the stream, so
+// the kernel boundary orders the partials) adds the ksplit partials in index
+// order and applies the epilogue: results do not depend on scheduling.
+constexpr int SK_THREADS = 256;
+
+// Tile height: 64 rows (two waves per SIMD fit) unless the 128-row tiles alone
+// give four workgroups per CU (the head), where the wider A reuse wins.  K is
+// split in powers of two while the grid has fewer than two workgroups per CU
+// and each wave keeps at least 256 of K.
+SkinnyPlan skinny_plan(int epi, int N, int K, int F, int cu) {
+  SkinnyPlan p{};
+  auto tiles_of = [&](int rb) {
+    const int rows = 32 * rb;
+    return (epi == EPI_SWIGLU) ? (F + rows / 2 - 1) / (rows / 2) : (N + rows - 1) / rows;
+  };
+  p.rb = (long)tiles_of(4) >= 4L * cu ? 4 : 2;
+  p.tiles = tiles_of(p.rb);
+  p.ksplit = 1;
+  while ((long)p.tiles * p.ksplit < 2L * cu && K % (p.ksplit * 2 * 4 * 64) == 0 && K / (p.ksplit * 2 * 4) >= 256)
+    p.ksplit *= 2;
+  if (p.ksplit > 1) p.bytes = (size_t)p.tiles * p.ksplit * 32 * 32 * p.rb * sizeof(float);
+  return p;
+}
+
+template <int RB>
+DEV void sk_load(const bf16_t* const* Bp, const bf16_t* Ap, bool tok_ok, int k, u32x4_t (&bw)[RB][4],
+                 u32x4_t (&xw)[4]) {
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bw[rb][j] = ldv4(Bp[rb] + k + j * 8);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) xw[j] = tok_ok ? ldv4(Ap + k + j * 8) : zero;
+}
+
+template <int RB>
+DEV void sk_mma(const u32x4_t (&bw)[RB][4], const u32x4_t (&xw)[4], f32x16_t (&acc)[RB]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) acc[rb] = mfma32(as_bf16x8(bw[rb][j]), as_bf16x8(xw[j]), acc[rb]);
+}
+
+template <int EPI, int RB>
+DEV void sk_epilogue(const GemmArgs& a, int tile, int m, int j, float v, float vup) {
+  constexpr int R = 32 * RB;
+  if (EPI == EPI_SWIGLU) {
+    const int col = tile * (R / 2) + j;
+    if (col < a.F) st1((bf16_t*)a.C + (size_t)m * a.ldc + col, silu(v) * vup);
+  } else {
+    const int col = tile * R + j;
+    if (col < a.N) epi_one<bf16_t, EPI>(a, m, col, v);
+  }
+}
+
+template <int EPI, int RB>
+__global__ __launch_bounds__(SK_THREADS) void gemm_skinny_kernel(GemmArgs a) {
+  constexpr int R = 32 * RB;
+  __shared__ float red[2][32][R + 1];      // [slot][token][tile row]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int nb = blockIdx.x;
+  const int ks = a.ksplit;
+  const int tile = blockIdx.x / ks, kpart = blockIdx.x - tile * ks;
   const int r = lane & 31, h = lane >> 5;
-  int brow;
-  if (EPI == EPI_SWIGLU) brow = (r < 16) ? (nb * 16 + r) : (a.F + nb * 16 + (r - 16));
-  else brow = nb * 32 + r;
-  const int KW = a.K / 8;
-  const int kbeg = wid * KW + h * (KW / 2);
-  const int steps = KW / 16;
-  const bf16_t* Bp = (const bf16_t*)a.B + (size_t)brow * a.ldb + kbeg;
+  const int Kw = a.K / (ks * 4);
+  const int kbeg = (kpart * 4 + wid) * Kw + h * 32;
+  const bf16_t* Bp[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    int n;
+    if (EPI == EPI_SWIGLU) {
+      const int j = tile * (R / 2) + (rb % (RB / 2)) * 32 + r;       // output column
+      n = j < a.F ? ((rb < RB / 2) ? j : a.F + j) : 0;
+    } else {
+      n = tile * R + rb * 32 + r;
+      n = n < a.N ? n : 0;
+    }
+    Bp[rb] = (const bf16_t*)a.B + (size_t)n * a.ldb + kbeg;
+  }
   const bool tok_ok = r < a.M;
   const bf16_t* Ap = (const bf16_t*)a.A + (size_t)(tok_ok ? r : 0) * a.lda + kbeg;
 
-  f32x16_t acc;
+  f32x16_t acc[RB];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) acc[i] = 0.f;
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-  int s = 0;
-  for (; s + 8 <= steps; s += 8) {
-    u32x4_t wv[8], xv[8];
+  for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      wv[j] = ldv4(Bp + (s + j) * 8);
-      xv[j] = tok_ok ? ldv4(Ap + (s + j) * 8) : zero;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) acc = mfma32(as_bf16x8(wv[j]), as_bf16x8(xv[j]), acc);
+    for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
+  // two register sets: loads for step k + 64 are in flight during step k's MFMAs
+  u32x4_t bw0[RB][4], xw0[4], bw1[RB][4], xw1[4];
+  sk_load<RB>(Bp, Ap, tok_ok, 0, bw0, xw0);
+  int k = 0;
+  for (; k + 128 <= Kw; k += 128) {
+    sk_load<RB>(Bp, Ap, tok_ok, k + 64, bw1, xw1);
+    sk_mma<RB>(bw0, xw0, acc);
+    if (k + 128 < Kw) sk_load<RB>(Bp, Ap, tok_ok, k + 128, bw0, xw0);
+    sk_mma<RB>(bw1, xw1, acc);
   }
-  for (; s < steps; ++s) {
-    const u32x4_t wv = ldv4(Bp + s * 8);
-    const u32x4_t xv = tok_ok ? ldv4(Ap + s * 8) : zero;
-    acc = mfma32(as_bf16x8(wv), as_bf16x8(xv), acc);
-  }
-  // acc: rows = B rows n = (i/4)*8 + h*4 + i%4, column = token (lane & 31)
+  if (k < Kw) sk_mma<RB>(bw0, xw0, acc);
+
+  // acc[rb][i]: tile row rb*32 + (i/4)*8 + h*4 + i%4, token r.  Sum the waves
+  // as (w0 + w2) + (w1 + w3).
+  auto put = [&](int slot) {
 #pragma unroll
-  for (int i = 0; i < 16; ++i) red[wid][(i >> 2) * 8 + h * 4 + (i & 3)][lane & 31] = acc[i];
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red[slot][r][rb * 32 + (i >> 2) * 8 + h * 4 + (i & 3)] = acc[rb][i];
+  };
+  auto add = [&](int slot) {
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[rb][i] += red[slot][r][rb * 32 + (i >> 2) * 8 + h * 4 + (i & 3)];
+  };
+  if (wid >= 2) put(wid - 2);
   __syncthreads();
-  if (EPI == EPI_SWIGLU) {
-    const int m = tid >> 4, c = tid & 15;
-    if (m < a.M) {
-      float g = 0.f, u = 0.f;
-#pragma unroll
-      for (int w = 0; w < 8; ++w) { g += red[w][c][m]; u += red[w][16 + c][m]; }
-      st1((bf16_t*)a.C + (size_t)m * a.ldc + nb * 16 + c, silu(g) * u);
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int idx = tid * 2 + e;
-      const int m = idx >> 5, c = idx & 31;
-      if (m < a.M) {
-        float v = 0.f;
-#pragma unroll
-        for (int w = 0; w < 8; ++w) v += red[w][c][m];
-        epi_one<bf16_t, EPI>(a, m, nb * 32 + c, v);
-      }
-    }
+  if (wid < 2) add(wid);
+  __syncthreads();
+  if (wid == 1) put(0);
+  __syncthreads();
+  if (wid == 0) { add(0); put(0); }
+  __syncthreads();
+
+  // element e of the tile: token e / R, tile row e % R (coalesced along rows)
+  const int M = a.M;
+  if (ks > 1) {
+    float* mine = a.part + (size_t)blockIdx.x * 32 * R;
+    for (int e = tid; e < M * R; e += SK_THREADS) mine[e] = red[0][e / R][e % R];
+    return;
   }
+  if (EPI == EPI_SWIGLU) {
+    constexpr int H = R / 2;
+    for (int e = tid; e < M * H; e += SK_THREADS)
+      sk_epilogue<EPI, RB>(a, tile, e / H, e % H, red[0][e / H][e % H], red[0][e / H][H + e % H]);
+  } else {
+    for (int e = tid; e < M * R; e += SK_THREADS)
+      sk_epilogue<EPI, RB>(a, tile, e / R, e % R, red[0][e / R][e % R], 0.f);
+  }
+}
+
+// One thread per output (token m, output column): the ksplit partials of its
+// tile in index order, then the epilogue.
+template <int EPI, int RB>
+__global__ __launch_bounds__(256) void gemm_skinny_reduce(GemmArgs a) {
+  constexpr int R = 32 * RB;
+  constexpr int per_tile = (EPI == EPI_SWIGLU) ? R / 2 : R;
+  const int tiles = (EPI == EPI_SWIGLU) ? (a.F + per_tile - 1) / per_tile : (a.N + R - 1) / R;
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= a.M * tiles * per_tile) return;
+  const int m = i / (tiles * per_tile), c = i - m * tiles * per_tile;
+  const int tile = c / per_tile, j = c - tile * per_tile;
+  const int ks = a.ksplit;
+  const float* p = a.part + (size_t)tile * ks * 32 * R + m * R + j;
+  float v = 0.f, vup = 0.f;
+  for (int q = 0; q < ks; ++q) {
+    v += p[(size_t)q * 32 * R];
+    if (EPI == EPI_SWIGLU) vup += p[(size_t)q * 32 * R + R / 2];
+  }
+  sk_epilogue<EPI, RB>(a, tile, m, j, v, vup);
+}
+
+template <int EPI, int RB>
+static hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
+  constexpr int R = 32 * RB;
+  const int tiles = (EPI == EPI_SWIGLU) ? (a.F + R / 2 - 1) / (R / 2) : (a.N + R - 1) / R;
+  gemm_skinny_kernel<EPI, RB><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
+  if (a.ksplit > 1) {
+    const long outs = (long)a.M * tiles * (EPI == EPI_SWIGLU ? R / 2 : R);
+    gemm_skinny_reduce<EPI, RB><<<(int)((outs + 255) / 256), 256, 0, s>>>(a);
+  }
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ fp32 kernel
@@ -387,11 +502,11 @@ static hipError_t launch_dma(const GemmArgs& a, int blocks, hipStream_t s) {
 template <int EPI>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 32) {
-    if (a.K % 128) return hipErrorInvalidValue;
-    const int blocks = (EPI == EPI_SWIGLU) ? a.F / 16 : a.N / 32;
-    if ((EPI == EPI_SWIGLU ? a.F % 16 : a.N % 32)) return hipErrorInvalidValue;
-    gemm_skinny_kernel<EPI><<<blocks, 512, 0, s>>>(a);
-    return hipGetLastError();
+    if (a.ksplit < 1 || a.K % (a.ksplit * 4 * 64)) return hipErrorInvalidValue;
+    if (a.ksplit > 1 && !a.part) return hipErrorInvalidValue;
+    if (a.skinny_rb == 2) return launch_skinny<EPI, 2>(a, s);
+    if (a.skinny_rb == 4) return launch_skinny<EPI, 4>(a, s);
+    return hipErrorInvalidValue;
   }
   if (a.K % DBK) return hipErrorInvalidValue;
   if ((long)TBM * a.lda >= (1L << 31) || (long)(EPI == EPI_SWIGLU ? 2 * a.F : a.N) * a.ldb >= (1L << 31))

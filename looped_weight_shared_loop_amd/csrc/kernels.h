@@ -60,8 +60,18 @@ struct GemmArgs {
   void* vcache;          // [B][Hkv][d][S_max] (transposed)
   int S_call, pos0, S_max;  // row m is sequence m / S_call at position pos0 + m % S_call
   int F;                 // EPI_SWIGLU: up rows start at row F of B
+  // M <= 32: split-K plan (skinny_plan) and its scratch; ksplit 1 needs none.
+  int ksplit;
+  int skinny_rb;         // 32-row blocks per tile (2 or 4)
+  float* part;           // [tiles * ksplit][32][32 * skinny_rb] fp32 partial sums
 };
 hipError_t gemm(const GemmArgs& a, hipStream_t s);
+
+// Decode-shaped (M <= 32) GEMM plan: 128 weight rows per workgroup tile (SwiGLU:
+// 64 gate + 64 up rows), K split over `ksplit` workgroups when the tiles alone
+// cannot fill the device.  `bytes` = partial sums (0 when ksplit == 1).
+struct SkinnyPlan { int rb, tiles, ksplit; size_t bytes; };
+SkinnyPlan skinny_plan(int epi, int N, int K, int F, int cu);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {
@@ -70,10 +80,16 @@ struct AttnArgs {
   const void* kcache;              // [B][Hkv][S_max][d]
   const void* vcache;              // [B][Hkv][d][S_max]
   void* out; long ldo;             // token m: out + m * ldo, head j at + j * d
-  float* part; int n_split, split_len;   // decode: [B][Hq][n_split][d + 2] fp32
+  float* part; int n_split, split_len;   // decode: [B][Hq][n_split][d + 2] fp32 (n_split > 1)
 };
 hipError_t attn_prefill(const AttnArgs& a, hipStream_t s);
 hipError_t attn_decode(const AttnArgs& a, hipStream_t s);
+// Decode split of the cache: as few splits as fill `cu` workgroups over the
+// B * Hkv (sequence, KV head) pairs, each a multiple of 64 keys.
+struct DecodePlan { int split_len, n_split; };
+DecodePlan decode_plan(int B, int Hkv, int kv_len, int cu);
+// upper bound of n_split over kv_len <= S_max
+int decode_max_splits(int B, int Hkv, int S_max, int cu);
 
 // ---------------------------------------------------------------- linear attention
 struct LinArgs {

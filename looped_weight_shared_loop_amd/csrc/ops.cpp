@@ -26,15 +26,19 @@ bool any_misaligned(std::initializer_list<const void*> ps) {
   return false;
 }
 
-constexpr int DEC_SPLIT = 256;
 constexpr int LIN_CHUNK = 64;
 
 }  // namespace
 
 extern "C" {
 
+size_t loop_op_gemm_bytes(int dtype, int epi, int M, int N, int K, int F) {
+  if (dtype != LOOP_BF16 || M <= 0 || M > 32 || N <= 0 || K <= 0) return 0;
+  return lk::skinny_plan(epi, N, K, F, lk::device_cu_count()).bytes;
+}
+
 int loop_op_gemm(int dtype, int epi, int M, int N, int K, const void* A, long lda, const void* B, long ldb, void* C,
-                 long ldc, int F, void* stream) {
+                 long ldc, int F, void* scratch, size_t scratch_bytes, void* stream) {
   int dt;
   if (int r = dt_of(dtype, &dt)) return r;
   if (!A || !B || !C) return lp_fail(LOOP_ERR_INVALID_ARG, "null pointer");
@@ -43,10 +47,23 @@ int loop_op_gemm(int dtype, int epi, int M, int N, int K, const void* A, long ld
   if (M < 0 || N <= 0 || K <= 0 || lda < K || ldb < K) return lp_fail(LOOP_ERR_INVALID_ARG, "sizes");
   if (epi == LOOP_EPI_SWIGLU && (F <= 0 || N != 2 * F || ldc < F)) return lp_fail(LOOP_ERR_INVALID_ARG, "swiglu sizes");
   if (epi != LOOP_EPI_SWIGLU && ldc < N) return lp_fail(LOOP_ERR_INVALID_ARG, "ldc");
-  if (any_misaligned({A, B, C}) || lda % 8 || ldb % 8) return lp_fail(LOOP_ERR_ALIGN, "operands must be 16-byte aligned");
+  if (any_misaligned({A, B, C, scratch}) || lda % 8 || ldb % 8)
+    return lp_fail(LOOP_ERR_ALIGN, "operands must be 16-byte aligned");
   lk::GemmArgs g{};
   g.dt = dt; g.epi = epi; g.M = M; g.N = N; g.K = K; g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
   g.F = F;
+  g.ksplit = 1;
+  g.skinny_rb = 4;
+  if (dt == lk::DT_BF16 && M > 0 && M <= 32) {
+    const lk::SkinnyPlan p = lk::skinny_plan(epi, N, K, F, lk::device_cu_count());
+    g.skinny_rb = p.rb;
+    if (p.ksplit > 1 && scratch) {
+      if (scratch_bytes < p.bytes)
+        return lp_fail(LOOP_ERR_WORKSPACE, "gemm scratch %zu bytes, needs %zu", scratch_bytes, p.bytes);
+      g.ksplit = p.ksplit;
+      g.part = (float*)scratch;
+    }
+  }
   return launched(lk::gemm(g, (hipStream_t)stream), "gemm");
 }
 
@@ -111,7 +128,8 @@ int loop_op_attention(int dtype, int B, int S, int pos0, int S_max, int Hq, int 
 
 size_t loop_op_attention_decode_bytes(int B, int S, int Hq, int d, int S_max) {
   if (B <= 0 || S <= 0 || Hq <= 0 || d <= 0 || S_max <= 0) return 0;
-  const size_t nsplit = ((size_t)S_max + DEC_SPLIT - 1) / DEC_SPLIT;
+  // bound over every KV-head count: the split count only falls as Hkv grows
+  const size_t nsplit = (size_t)lk::decode_max_splits(B, 1, S_max, lk::device_cu_count());
   return (size_t)B * S * Hq * nsplit * (d + 2) * sizeof(float);
 }
 
@@ -124,9 +142,10 @@ int loop_op_attention_decode(int dtype, int B, int S, int pos0, int S_max, int H
   if (!scratch || scratch_bytes < loop_op_attention_decode_bytes(B, S, Hq, d, S_max))
     return lp_fail(LOOP_ERR_WORKSPACE, "decode attention scratch too small");
   if (lp_misaligned(scratch)) return lp_fail(LOOP_ERR_ALIGN, "misaligned scratch");
+  const lk::DecodePlan dp = lk::decode_plan(B, Hkv, pos0 + S, lk::device_cu_count());
   a.part = (float*)scratch;
-  a.split_len = DEC_SPLIT;
-  a.n_split = (pos0 + S + DEC_SPLIT - 1) / DEC_SPLIT;
+  a.split_len = dp.split_len;
+  a.n_split = dp.n_split;
   return launched(lk::attn_decode(a, (hipStream_t)stream), "decode attention");
 }
 

@@ -115,10 +115,14 @@ def test_op_level_validation_without_device():
     """Argument checks of the op-level entry points run before any launch."""
     from looped_weight_shared_loop_amd import _abi as A
     lib = A.lib()
-    assert lib.loop_op_gemm(7, 0, 1, 1, 1, None, 1, None, 1, None, 1, 0, None) == A.LOOP_ERR_INVALID_ARG
-    assert lib.loop_op_gemm(1, 0, 64, 256, 64, None, 64, None, 64, None, 256, 0, None) == A.LOOP_ERR_INVALID_ARG
-    assert lib.loop_op_gemm(1, 3, 64, 256, 64, 16, 64, 16, 64, 16, 128, 100, None) == A.LOOP_ERR_INVALID_ARG
-    assert lib.loop_op_gemm(1, 0, 64, 256, 64, 24, 64, 16, 64, 16, 256, 0, None) == A.LOOP_ERR_ALIGN
+    assert lib.loop_op_gemm(7, 0, 1, 1, 1, None, 1, None, 1, None, 1, 0, None, 0, None) == A.LOOP_ERR_INVALID_ARG
+    assert lib.loop_op_gemm(1, 0, 64, 256, 64, None, 64, None, 64, None, 256, 0, None, 0, None) == A.LOOP_ERR_INVALID_ARG
+    assert lib.loop_op_gemm(1, 3, 64, 256, 64, 16, 64, 16, 64, 16, 128, 100, None, 0, None) == A.LOOP_ERR_INVALID_ARG
+    assert lib.loop_op_gemm(1, 0, 64, 256, 64, 24, 64, 16, 64, 16, 256, 0, None, 0, None) == A.LOOP_ERR_ALIGN
+    assert lib.loop_op_gemm(1, 0, 8, 256, 256, 16, 256, 16, 256, 16, 256, 0, 24, 64, None) == A.LOOP_ERR_ALIGN
+    # fp32 and prefill shapes need no split-K scratch
+    assert lib.loop_op_gemm_bytes(0, 0, 8, 4096, 4096, 0) == 0
+    assert lib.loop_op_gemm_bytes(1, 0, 64, 4096, 4096, 0) == 0
     assert lib.loop_op_mhc(1, 9, 1, 8, 20, 1e-6, None, None, 16, None, None, None, None, 16, 16, None, 0, None) == \
         A.LOOP_ERR_INVALID_ARG
     assert A.loop_op_mhc_bytes(4096) == 16 * 8192 * 2

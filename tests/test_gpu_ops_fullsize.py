@@ -47,21 +47,31 @@ def _bf16(t):
 
 
 # ------------------------------------------------------------------ GEMM
-@pytest.mark.parametrize("name,M,N,K,epi", [
-    ("qkv", 32768, QKV, C, 0), ("o", 32768, C, HQ * D, 0), ("gate_up", 32768, 2 * F, C, 3),
-    ("down", 32768, C, F, 0), ("head_last_rows", 32, V, C, 1), ("head_all_rows", 2048, V, C, 1),
-    ("decode_gate_up", 32, 2 * F, C, 3), ("decode_down", 32, C, F, 0),
+@pytest.mark.parametrize("name,M,N,K,epi,split", [
+    ("qkv", 32768, QKV, C, 0, False), ("o", 32768, C, HQ * D, 0, False), ("gate_up", 32768, 2 * F, C, 3, False),
+    ("down", 32768, C, F, 0, False), ("head_last_rows", 32, V, C, 1, True), ("head_all_rows", 2048, V, C, 1, False),
+    ("decode_gate_up", 32, 2 * F, C, 3, True), ("decode_down", 32, C, F, 0, True),
+    ("decode_o", 32, C, HQ * D, 0, True), ("decode_qkv_m7", 7, QKV, C, 0, True),
+    ("decode_down_nosplit", 32, C, F, 0, False), ("decode_gate_up_m1_nosplit", 1, 2 * F, C, 3, False),
 ])
-def test_gemm_full_size_sampled(name, M, N, K, epi):
+def test_gemm_full_size_sampled(name, M, N, K, epi, split):
+    """9B-shape projections; M <= 32 is the decode kernel, with K split over
+    workgroups (scratch given) or one workgroup per 128-row tile."""
     need_gpu()
     from looped_weight_shared_loop_amd import _abi as A
-    print(f"gemm {name} M={M} N={N} K={K}", flush=True)
+    print(f"gemm {name} M={M} N={N} K={K} split={split}", flush=True)
     a = _dev_normal((M, K), 11)
     b = _dev_normal((N, K), 12, 0.02)
     ncol = N // 2 if epi == 3 else N
     c = torch.empty(M, ncol, dtype=torch.float32 if epi == 1 else torch.bfloat16, device="cuda")
-    A.loop_op_gemm(A.LOOP_BF16, epi, M, N, K, a.data_ptr(), K, b.data_ptr(), K, c.data_ptr(), ncol,
-                   N // 2 if epi == 3 else 0, _stream())
+    Fa = N // 2 if epi == 3 else 0
+    nbytes = A.loop_op_gemm_bytes(A.LOOP_BF16, epi, M, N, K, Fa) if split else 0
+    if split and name.startswith("decode"):
+        assert nbytes > 0          # these shapes do split on a 256-CU device
+    scr = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    for _ in range(2):             # the second call runs on the counters the first one left
+        A.loop_op_gemm(A.LOOP_BF16, epi, M, N, K, a.data_ptr(), K, b.data_ptr(), K, c.data_ptr(), ncol, Fa,
+                       _stream(), scr.data_ptr() if nbytes else None, nbytes)
     torch.cuda.synchronize()
     rng = np.random.default_rng(hash(name) & 0xFFFF)
     rows = np.unique(np.concatenate([rng.integers(0, M, 24), [0, M - 1]]))
@@ -169,13 +179,18 @@ def test_full_attention_prefill_full_size_sampled():
         assert err < 2e-2
 
 
-def test_decode_attention_full_size_sampled():
-    """B=32 sequences of 32,768 cached positions + 1 new, 8 KV heads."""
+@pytest.mark.parametrize("B,ctx,samples", [
+    (32, 32768, [(0, 0), (7, 9), (31, 31), (16, 4)]),     # one split per (sequence, KV head)
+    (2, 5001, [(0, 0), (1, 13), (1, 31)]),                # several splits, ragged last split
+    (1, 37, [(0, 0), (0, 30)]),                           # fewer keys than one round
+])
+def test_decode_attention_full_size_sampled(B, ctx, samples):
+    """B sequences of ctx cached positions + 1 new, 8 KV heads of 128."""
     need_gpu()
     from looped_weight_shared_loop_amd import _abi as A
     from synth import device as sd
-    B, ctx = 32, 32768
-    Smax = 32832
+    print(f"decode attention B={B} ctx={ctx}", flush=True)
+    Smax = (ctx + 1 + 63) // 64 * 64
     kc = torch.zeros(B, HKV, Smax, D, dtype=torch.bfloat16, device="cuda")
     vt = torch.zeros(B, HKV, D, Smax, dtype=torch.bfloat16, device="cuda")
     L = ctx + 1
@@ -190,7 +205,7 @@ def test_decode_attention_full_size_sampled():
     A.loop_op_attention_decode(A.LOOP_BF16, B, 1, ctx, Smax, HQ, HKV, D, q.data_ptr(), QKV, kc.data_ptr(),
                                vt.data_ptr(), out.data_ptr(), HQ * D, scr.data_ptr(), nb, _stream())
     torch.cuda.synchronize()
-    for b, head in [(0, 0), (7, 9), (31, 31), (16, 4)]:
+    for b, head in samples:
         kvh = head // (HQ // HKV)
         qr = synth.normal_bf16_as_f32(SEED, 43, (QKV,), start=b * QKV)[head * D:(head + 1) * D]
         base = ((b * HKV + kvh) * L) * D
