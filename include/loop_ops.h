@@ -49,10 +49,11 @@ int loop_op_add_rmsnorm(int dtype, int T, int C, const void* y, void* h, const f
  *  ENTER: X = [h + y, h + y] (y may be NULL); maps_out, u for site (w, b, gamma).
  *  MID:   X <- H_res X + H_post y with maps_in; then maps_out and u for (w, b, gamma).
  *  EXIT:  X' = H_res X + H_post y; h = (X'0 + X'1) / 2; u = RMSNorm(h; gamma).
- * C <= 4096, C % 8 == 0.  With bf16 and C % 256 == 0, ENTER and MID run the
- * projection W x on the matrix cores when `scratch` (>= loop_op_mhc_bytes(C))
- * is given: W is split there into bf16 high and low parts (about 16 mantissa
- * bits of W, float32 accumulation); with scratch NULL a float32 path is used. */
+ * C <= 4096, C % 8 == 0.  With bf16, C % 256 == 0 and T >= 256, ENTER and
+ * MID run the projection W x on the matrix cores when `scratch` (>=
+ * loop_op_mhc_bytes(C)) is given: W is split there into bf16 high and low
+ * parts (about 16 mantissa bits of W, float32 accumulation); otherwise (fewer
+ * tokens, or scratch NULL) a float32 path with one workgroup per token runs. */
 size_t loop_op_mhc_bytes(int C);
 int loop_op_mhc(int dtype, int mode, int T, int C, int sinkhorn_iters, float eps, const void* y, void* h, void* X,
                 const float* maps_in, float* maps_out, const float* w, const float* b, const float* gamma,

@@ -286,6 +286,8 @@ __global__ __launch_bounds__(256) void mhc_split_w(const float* __restrict__ w, 
 }
 
 __global__ __launch_bounds__(512) void mhc_mfma_kernel(MhcArgs a, const bf16_t* __restrict__ wsplit) {
+  constexpr int NSMAX = 16;                 // C <= 4096: 32-channel steps per wave
+  constexpr int GRP = 2;                    // steps whose loads are issued together
   __shared__ float red_acc[8][16][17];
   __shared__ float red_s[8][16][3];
   __shared__ float tl[16][17];
@@ -302,6 +304,7 @@ __global__ __launch_bounds__(512) void mhc_mfma_kernel(MhcArgs a, const bf16_t* 
   bf16_t* u = (bf16_t*)a.u;
   const int ntiles = (a.T + 15) / 16;
   const bf16_t* wrow = wsplit + (size_t)li * C2;   // row li of [W_hi; W_lo]
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
 
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     const int t = tile * 16 + li;
@@ -311,57 +314,81 @@ __global__ __launch_bounds__(512) void mhc_mfma_kernel(MhcArgs a, const bf16_t* 
       const float* mi = a.maps_in + (size_t)t * 8;
       po0 = mi[2]; po1 = mi[3]; r00 = mi[4]; r01 = mi[5]; r10 = mi[6]; r11 = mi[7];
     }
+    const size_t tr = tv ? (size_t)t : 0;
+    const bf16_t* X0r = X + (tr * 2) * C + w * CW + 8 * g;
+    const bf16_t* X1r = X0r + C;
+    const bf16_t* Hr = hin + tr * C + w * CW + 8 * g;
+    const bf16_t* Yr = (y ? y + tr * C : nullptr) + w * CW + 8 * g;
+    // X' of this lane's token and channels stays in registers (bf16 pairs)
+    u32x4_t xs0[NSMAX], xs1[NSMAX];
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     float s00 = 0.f, s11 = 0.f, s01 = 0.f;
-#pragma unroll 2
-    for (int j = 0; j < NS; ++j) {
-      const int cb = w * CW + 32 * j + 8 * g;
-      float x0[8], x1[8];
-      if (tv) {
-        if (mode == MHC_ENTER) {
-          ld8(hin + (size_t)t * C + cb, x0);
-          if (y) {
-            float yv[8];
-            ld8(y + (size_t)t * C + cb, yv);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x0[e] = bf2f(f2bf(x0[e] + yv[e]));
-          }
+    for (int j0 = 0; j0 < NSMAX; j0 += GRP) {
+      if (j0 < NS) {
+        u32x4_t la[GRP], lb[GRP], lc[GRP];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) x1[e] = x0[e];
-        } else {
-          float p[8], q[8], yv[8];
-          ld8(X + ((size_t)t * 2) * C + cb, p);
-          ld8(X + ((size_t)t * 2 + 1) * C + cb, q);
-          ld8(y + (size_t)t * C + cb, yv);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            x0[e] = bf2f(f2bf(r00 * p[e] + r01 * q[e] + po0 * yv[e]));
-            x1[e] = bf2f(f2bf(r10 * p[e] + r11 * q[e] + po1 * yv[e]));
+        for (int k = 0; k < GRP; ++k) {
+          const int off = 32 * (j0 + k);
+          if (mode == MHC_ENTER) {
+            la[k] = tv ? ldv4(Hr + off) : zero;
+            lc[k] = (tv && y) ? ldv4(Yr + off) : zero;
+          } else {
+            la[k] = tv ? ldv4(X0r + off) : zero;
+            lb[k] = tv ? ldv4(X1r + off) : zero;
+            lc[k] = tv ? ldv4(Yr + off) : zero;
           }
         }
-        st8(X + ((size_t)t * 2) * C + cb, x0);
-        st8(X + ((size_t)t * 2 + 1) * C + cb, x1);
-      } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { x0[e] = 0.f; x1[e] = 0.f; }
-      }
-      uint32_t p0[4], p1[4];
+        for (int k = 0; k < GRP; ++k) {
+          const int j = j0 + k;
+          float x0[8], x1[8];
+          if (mode == MHC_ENTER) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // exact: the values are already bf16
-        p0[e] = (__float_as_uint(x0[2 * e]) >> 16) | (__float_as_uint(x0[2 * e + 1]) & 0xFFFF0000u);
-        p1[e] = (__float_as_uint(x1[2 * e]) >> 16) | (__float_as_uint(x1[2 * e + 1]) & 0xFFFF0000u);
-      }
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t wa = la[k][e >> 1], wc = lc[k][e >> 1];
+              const float hv = __uint_as_float((e & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
+              const float yv = __uint_as_float((e & 1) ? (wc & 0xFFFF0000u) : (wc << 16));
+              x0[e] = bf2f(f2bf(hv + yv));   // y absent: adds 0
+              x1[e] = x0[e];
+            }
+          } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        s00 += x0[e] * x0[e];
-        s11 += x1[e] * x1[e];
-        s01 += x0[e] * x1[e];
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t wa = la[k][e >> 1], wb = lb[k][e >> 1], wc = lc[k][e >> 1];
+              const float p = __uint_as_float((e & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
+              const float q = __uint_as_float((e & 1) ? (wb & 0xFFFF0000u) : (wb << 16));
+              const float yv = __uint_as_float((e & 1) ? (wc & 0xFFFF0000u) : (wc << 16));
+              x0[e] = bf2f(f2bf(r00 * p + r01 * q + po0 * yv));
+              x1[e] = bf2f(f2bf(r10 * p + r11 * q + po1 * yv));
+            }
+          }
+          u32x4_t p0, p1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            // exact: the values are already bf16
+            p0[e] = (__float_as_uint(x0[2 * e]) >> 16) | (__float_as_uint(x0[2 * e + 1]) & 0xFFFF0000u);
+            p1[e] = (__float_as_uint(x1[2 * e]) >> 16) | (__float_as_uint(x1[2 * e + 1]) & 0xFFFF0000u);
+          }
+          xs0[j] = p0;
+          xs1[j] = p1;
+          if (tv) {
+            stv4(X + (tr * 2) * C + w * CW + 32 * j + 8 * g, p0);
+            stv4(X + (tr * 2 + 1) * C + w * CW + 32 * j + 8 * g, p1);
+          }
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            s00 += x0[e] * x0[e];
+            s11 += x1[e] * x1[e];
+            s01 += x0[e] * x1[e];
+          }
+          const int cb = w * CW + 32 * j + 8 * g;
+          const bf16x8_t w0 = as_bf16x8(ldv4(wrow + cb));
+          const bf16x8_t w1 = as_bf16x8(ldv4(wrow + C + cb));
+          acc = mfma16(as_bf16x8(p0), w0, acc);
+          acc = mfma16(as_bf16x8(p1), w1, acc);
+        }
       }
-      const bf16x8_t w0 = as_bf16x8(ldv4(wrow + cb));
-      const bf16x8_t w1 = as_bf16x8(ldv4(wrow + C + cb));
-      acc = mfma16(as_bf16x8(u32x4_t{p0[0], p0[1], p0[2], p0[3]}), w0, acc);
-      acc = mfma16(as_bf16x8(u32x4_t{p1[0], p1[1], p1[2], p1[3]}), w1, acc);
     }
     // acc[r]: token 4 g + r, column li; the stream sums of token li are split over the 4 groups
 #pragma unroll
@@ -406,24 +433,35 @@ __global__ __launch_bounds__(512) void mhc_mfma_kernel(MhcArgs a, const bf16_t* 
     __syncthreads();
     if (tv) {
       const float q0 = mp[li][0], q1 = mp[li][1], iv = mp[li][2];
-      for (int j = 0; j < NS; ++j) {
-        const int cb = w * CW + 32 * j + 8 * g;
-        float x0[8], x1[8], gm[8], o[8];
-        ld8(X + ((size_t)t * 2) * C + cb, x0);      // X' written above by this thread
-        ld8(X + ((size_t)t * 2 + 1) * C + cb, x1);
-        ld8(a.gamma + cb, gm);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = gm[e] * (q0 * x0[e] + q1 * x1[e]) * iv;
-        st8(u + (size_t)t * C + cb, o);
+      for (int j = 0; j < NSMAX; ++j) {
+        if (j < NS) {
+          const int cb = w * CW + 32 * j + 8 * g;
+          float gm[8], o[8];
+          ld8(a.gamma + cb, gm);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const uint32_t wa = xs0[j][e >> 1], wb = xs1[j][e >> 1];
+            const float x0 = __uint_as_float((e & 1) ? (wa & 0xFFFF0000u) : (wa << 16));
+            const float x1 = __uint_as_float((e & 1) ? (wb & 0xFFFF0000u) : (wb << 16));
+            o[e] = gm[e] * (q0 * x0 + q1 * x1) * iv;
+          }
+          st8(u + (size_t)t * C + cb, o);
+        }
       }
     }
+    __syncthreads();    // LDS reuse by the next tile
   }
 }
+
+constexpr int MHC_MFMA_MIN_T = 256;
 
 hipError_t mhc(const MhcArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   if (a.C % 8 || a.C / 8 > 512) return hipErrorInvalidValue;
-  if (a.dt == DT_BF16 && a.mode != MHC_EXIT && a.C % 256 == 0 && a.wsplit) {
+  // 16-token tiles on the matrix cores pay off once there are enough tiles;
+  // fewer tokens (decode) take one workgroup per token with W in registers
+  if (a.dt == DT_BF16 && a.mode != MHC_EXIT && a.C % 256 == 0 && a.wsplit && a.T >= MHC_MFMA_MIN_T) {
     const int n = 8 * 2 * a.C;
     mhc_split_w<<<(n + 255) / 256, 256, 0, s>>>(a.w, a.wsplit, n);
     hipError_t e = hipGetLastError();
