@@ -242,7 +242,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=16)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--cpu-seq", type=int, default=1024)
+    ap.add_argument("--cpu-seq", type=int, default=1536)
     ap.add_argument("--profile-dominant", action="store_true",
                     help="only a 1 GiB device copy (counter scale reference) and 3 launches of the dominant kernel")
     args = ap.parse_args()

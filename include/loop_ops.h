@@ -63,8 +63,8 @@ int loop_op_mhc(int dtype, int mode, int T, int C, int sinkhorn_iters, float eps
  * pos0+S-1) of B sequences over a cache slot: K [B][Hkv][S_max][d],
  * V^T [B][Hkv][d][S_max] holding positions 0 .. pos0+S-1.  q: token (b, s) at
  * q + (b*S + s)*ldq, head j at + j*d; out likewise with ldo.  Query head j
- * reads KV head j / (Hq / Hkv); scale 1/sqrt(d).  bf16 needs d == 128 and
- * S_max % 64 == 0. */
+ * reads KV head j / (Hq / Hkv); scale 1/sqrt(d).  bf16 needs d == 128,
+ * Hq / Hkv in {1, 2, 4, 8} and S_max % 64 == 0. */
 int loop_op_attention(int dtype, int B, int S, int pos0, int S_max, int Hq, int Hkv, int d, const void* q, long ldq,
                       const void* kcache, const void* vcache, void* out, long ldo, void* stream);
 

@@ -84,3 +84,8 @@ DEV f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
 }
 
 DEV float silu(float x) { return x / (1.0f + expf(-x)); }
+// 2^x with the hardware instruction alone (about 1 ulp; results below
+// 2^-126 flush to zero): the softmax exponentials, where such tiny
+// probabilities do not matter, skip the denormal-range handling of exp2f.
+DEV float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+

@@ -165,6 +165,8 @@ int loop_model_create(const loop_config* cfg, const loop_weights* w, loop_model*
   const int qkv_rows = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
   if (c.dtype == LOOP_BF16) {
     if (c.head_dim != 128) return lp_fail(LOOP_ERR_SHAPE, "bf16 needs head_dim 128");
+    const int G = c.n_heads / c.n_kv_heads;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return lp_fail(LOOP_ERR_SHAPE, "bf16 needs n_heads / n_kv_heads in 1, 2, 4, 8");
     if (c.hidden % 256 || qkv_rows % 256 || c.vocab % 256 || (c.n_heads * c.head_dim) % 128 || c.ffn % 128)
       return lp_fail(LOOP_ERR_SHAPE, "bf16 GEMM tiles need hidden, qkv rows, vocab %% 256 == 0 and ffn %% 128 == 0");
   } else {

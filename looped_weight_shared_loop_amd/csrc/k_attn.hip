@@ -3,12 +3,13 @@
 // so that both operands of both products are read with the contraction axis
 // contiguous.
 //
-// * attn_prefill_mfma (bf16, d = 128): flash-style.  One workgroup per
-//   (32-query block, KV head, sequence); wave w serves query head
-//   kvh * G + w, so the G heads of a group share every K / V tile in LDS.
-//   Scores are computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16),
-//   which leaves each lane with one query column; the probabilities feed
-//   O^T = V^T P^T directly from registers.  Online softmax in fp32 (base 2).
+// * attn_prefill_dma (bf16, d = 128, Hq / Hkv in 1, 2, 4, 8): flash-style.
+//   One workgroup of eight waves per (256 / G queries, KV head, sequence);
+//   the G heads of a group and 8 / G query blocks of 32 share every K / V^T
+//   tile, which global -> LDS DMA brings in three tiles ahead.  Scores are
+//   computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16), which leaves
+//   each lane with one query column; the probabilities feed O^T = V^T P^T
+//   directly from registers.  Online softmax in fp32 (base 2).
 // * attn_decode_mfma (bf16, d = 128, up to 16 query columns = heads x new
 //   tokens): eight waves per (split, KV head, sequence), splits only as many
 //   as needed to fill the device, v_mfma_f32_16x16x32_bf16, operands read
@@ -22,79 +23,83 @@ namespace lk {
 constexpr float LOG2E = 1.4426950408889634f;
 
 // ------------------------------------------------------------------ prefill, bf16
-constexpr int PQ = 32;    // queries per wave
 constexpr int PK = 64;    // keys per tile
 constexpr int PD = 128;   // head dim
 
-// K tile [64 keys][128 d] in 16-byte chunks, chunk c of row r at c ^ (r & 15).
-DEV int ksw(int r, int c) { return r * PD + ((c ^ (r & 15)) << 3); }
-// V^T tile [128 d][64 keys] in 8-byte units, unit u of row r at u ^ ((r >> 1) & 15).
-DEV int vsw(int r, int u) { return r * PK + ((u ^ ((r >> 1) & 15)) << 2); }
+// ------------------------------------------------------------------ prefill, bf16, DMA
+// Eight waves per workgroup: wave w serves query head kvh*G + w % G for the
+// query sub-block w / G (32 queries), so one K / V^T tile in LDS serves
+// 32 * 8 / G queries of each of the G heads.  Tiles move global -> LDS with
+// global_load_lds_dwordx4 into a ring of four stages, three tiles ahead.
+// LDS layouts (16-byte units, swizzled against the 64 banks):
+//   K   [64 keys][128 d]:  unit c of row r at c ^ (r & 15)
+//   V^T [128 d][64 keys]:  unit u (keys 8u .. 8u + 7) of row r at u ^ ((r >> 1) & 7)
+// The score MFMA takes its K rows in the order kappa(rho), which swaps bits 2
+// and 3 of the row index, so that a lane's probabilities for PV step mm are the
+// eight consecutive keys 16 mm + 8 h .. + 7: one 16-byte read of V^T.
+constexpr int AQ_STAGE = 2 * PK * PD;          // elements per stage (K + V^T, 32 KB)
 
-template <int NTHR>
-__global__ __launch_bounds__(NTHR, 2) void attn_prefill_mfma(AttnArgs a) {
+DEV int kq_sw(int r, int c) { return r * PD + ((c ^ (r & 15)) << 3); }
+DEV int vq_sw(int r, int u) { return r * PK + ((u ^ ((r >> 1) & 7)) << 3); }
+
+constexpr int AQ_NW = 8;                       // waves per workgroup
+constexpr int AQ_NS = 4;                       // LDS stages
+constexpr int AQ_LDS = AQ_NS * AQ_STAGE * 2;   // 128 KB
+
+__global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
+  constexpr int NW = AQ_NW, AHEAD = AQ_NS - 1;
   extern __shared__ __align__(16) bf16_t smem[];
-  const int G = a.Hq / a.Hkv;
-  constexpr int nthr = NTHR;
-  bf16_t* Ks = smem;                  // [2][PK * PD]
-  bf16_t* Vs = smem + 2 * PK * PD;    // [2][PD * PK]
-
+  constexpr int NB = 16 / NW;                  // DMA blocks per wave per operand and tile
+  const int G = a.Hq / a.Hkv;                  // 1, 2, 4 or 8
+  const int QS = NW / G;                       // query sub-blocks per workgroup
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int qb = gridDim.x - 1 - blockIdx.x;   // long rows first
   const int kvh = blockIdx.y, b = blockIdx.z;
-  const int j = kvh * G + min(wid, G - 1);
-  const int q0 = qb * PQ;
+  const int j = kvh * G + wid % G;
+  const int q0 = qb * 32 * QS + (wid / G) * 32; // this wave's first query
   const int h = lane >> 5, col = lane & 31;
   const int m = q0 + col;
   const bool qvalid = m < a.S_call;
   const int qpos = a.pos0 + m;
-  const int kv_end = a.pos0 + min(q0 + PQ, a.S_call);
+  const int kv_end = a.pos0 + min((qb + 1) * 32 * QS, a.S_call);   // keys the workgroup needs
   const int ntiles = (kv_end + PK - 1) / PK;
+  const int wave_last = a.pos0 + min(q0 + 31, a.S_call - 1);       // last key this wave can see
 
   const bf16_t* Q = (const bf16_t*)a.q + (size_t)(b * a.S_call + min(m, a.S_call - 1)) * a.ldq + j * PD;
   bf16x8_t qf[8];
-  if (wid < G) {
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds) qf[ds] = as_bf16x8(ldv4(Q + ds * 16 + h * 8));
-  }
+  for (int ds = 0; ds < 8; ++ds) qf[ds] = as_bf16x8(ldv4(Q + ds * 16 + h * 8));
 
   const bf16_t* Kg = (const bf16_t*)a.kcache + ((size_t)(b * a.Hkv + kvh) * a.S_max) * PD;
   const bf16_t* Vg = (const bf16_t*)a.vcache + ((size_t)(b * a.Hkv + kvh) * PD) * a.S_max;
-
-  // cooperative tile load: 1024 16-byte chunks of K and 1024 of V^T
-  constexpr int per = 1024 / nthr;   // 4 (256 threads) or 2 (512 threads)
-  u32x4_t rk[4], rv[4];
-  auto gload = [&](int kt) {
-    const int k0 = kt * PK;
+  // DMA: per tile 16 K blocks of 4 rows and 16 V^T blocks of 8 rows; wave w
+  // issues blocks 2w and 2w + 1 of each.  Lane l writes LDS bytes 16 l .. of
+  // the block, so it fetches the global unit that the swizzle puts there.
+  int koff[NB], voff[NB], kl[NB], vl[NB];
 #pragma unroll
-    for (int i = 0; i < per; ++i) {
-      const int cidx = tid + i * nthr;
-      const int kr = cidx >> 4, kc = cidx & 15;       // K: row (key), chunk
-      const int key = k0 + kr;
-      rk[i] = ldv4(Kg + (size_t)min(key, a.S_max - 1) * PD + kc * 8);
-      const int vr = cidx >> 3, vc = cidx & 7;        // V^T: row (d), chunk of 8 keys
-      const int key0 = k0 + vc * 8;
-      u32x4_t v = ldv4(Vg + (size_t)vr * a.S_max + min(key0, a.S_max - 8));
-      if (key0 + 8 > kv_end) {
+  for (int i = 0; i < NB; ++i) {
+    const int blk = NB * wid + i;
+    const int kr = 4 * blk + (lane >> 4), ks = lane & 15;
+    koff[i] = kr * PD + ((ks ^ (kr & 15)) << 3);
+    kl[i] = blk * 512;
+    const int vr = 8 * blk + (lane >> 3), vs = lane & 7;
+    voff[i] = vr * a.S_max + ((vs ^ ((vr >> 1) & 7)) << 3);
+    vl[i] = PK * PD + blk * 512;
+  }
+  auto issue = [&](int kt) {
+    bf16_t* st = smem + (kt % AQ_NS) * AQ_STAGE;
+    const int k0 = min(kt, ntiles - 1) * PK;
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (key0 + e >= kv_end) v[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-      }
-      rv[i] = v;
+    for (int i = 0; i < NB; ++i) {
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Kg + (size_t)k0 * PD + koff[i]),
+                                       (void __attribute__((address_space(3)))*)(st + kl[i]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Vg + k0 + voff[i]),
+                                       (void __attribute__((address_space(3)))*)(st + vl[i]), 16, 0, 0);
     }
   };
-  auto sstore = [&](int buf) {
-    bf16_t* ks = Ks + buf * PK * PD;
-    bf16_t* vs = Vs + buf * PD * PK;
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-      const int cidx = tid + i * nthr;
-      const int kr = cidx >> 4, kc = cidx & 15;
-      stv4(ks + ksw(kr, kc), rk[i]);
-      const int vr = cidx >> 3, vc = cidx & 7;
-      *(u32x2_t*)(vs + vsw(vr, 2 * vc)) = u32x2_t{rv[i][0], rv[i][1]};
-      *(u32x2_t*)(vs + vsw(vr, 2 * vc + 1)) = u32x2_t{rv[i][2], rv[i][3]};
-    }
+  auto sync = [&]() {
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
 
   f32x16_t o[4];
@@ -104,91 +109,110 @@ __global__ __launch_bounds__(NTHR, 2) void attn_prefill_mfma(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
   float mrun = -INFINITY, lrun = 0.f;
   const float sc = LOG2E / sqrtf((float)PD);
+  // MFMA row rho of the score block reads K row kappa(rho) (bits 2 and 3 swapped)
+  const int krow = (col & 0x13) | ((col & 4) << 1) | ((col & 8) >> 1);
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < ntiles) gload(kt + 1);
-    const bf16_t* ks = Ks + cur * PK * PD;
-    const bf16_t* vs = Vs + cur * PD * PK;
-    if (wid < G) {
-      f32x16_t st[2];
+  static_assert(AQ_NS == 4 && NW == 8 && NB == 2, "wait counts below");
+  f32x16_t st[2];
+  auto scores = [&](int kt) {
+    const bf16_t* ks = smem + (kt % AQ_NS) * AQ_STAGE;
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < 2; ++c) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st[c][r] = 0.f;
+      for (int r = 0; r < 16; ++r) st[c][r] = 0.f;
 #pragma unroll
-        for (int ds = 0; ds < 8; ++ds) {
-          const bf16x8_t kf = as_bf16x8(ldv4(ks + ksw(c * 32 + col, ds * 2 + h)));
-          st[c] = mfma32(kf, qf[ds], st[c]);
-        }
+      for (int ds = 0; ds < 8; ++ds) {
+        const bf16x8_t kf = as_bf16x8(ldv4(ks + kq_sw(c * 32 + krow, ds * 2 + h)));
+        st[c] = mfma32(kf, qf[ds], st[c]);
       }
-      // st[c][r]: key kt*64 + c*32 + (r/4)*8 + h*4 + r%4, query column `col`.
-      // Only tiles reaching past the first query of the block need the mask.
-      const bool diag = kt * PK + PK - 1 > a.pos0 + q0;
-      float tmax = -INFINITY;
-      if (diag) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt * PK + c * 32 + (r >> 2) * 8 + h * 4 + (r & 3);
-            const float v = (key <= qpos && key < kv_end) ? st[c][r] : -INFINITY;
-            st[c][r] = v;
-            tmax = fmaxf(tmax, v);
-          }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[c][r]);
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sc;     // scaled (base-2) units
-      const float mnew = fmaxf(mrun, tmax);
-      const float mfin = (mnew == -INFINITY) ? 0.f : mnew;
-      float psum = 0.f;
+    }
+  };
+  auto softmax_pv = [&](int kt) {
+    const bf16_t* vs = smem + (kt % AQ_NS) * AQ_STAGE + PK * PD;
+    // st[c][r]: key kt*64 + 32c + 16(r/8) + 8h + r%8, query column `col`
+    const bool diag = kt * PK + PK - 1 > a.pos0 + q0;
+    float tmax = -INFINITY;
+    if (diag) {
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = exp2f(fmaf(st[c][r], sc, -mfin));
-          st[c][r] = p;
-          psum += p;
+          const int key = kt * PK + c * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
+          const float v = (key <= qpos && key < kv_end) ? st[c][r] : -INFINITY;
+          st[c][r] = v;
+          tmax = fmaxf(tmax, v);
         }
-      // O and l are rescaled only when some lane's running max moved.
-      if (__any(mnew > mrun)) {
-        const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
-        lrun *= alpha;
+    } else {
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[c][r]);
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sc;     // scaled (base-2) units
+    const float mnew = fmaxf(mrun, tmax);
+    const float mfin = (mnew == -INFINITY) ? 0.f : mnew;
+    float psum = 0.f;
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_hw(fmaf(st[c][r], sc, -mfin));
+        st[c][r] = p;
+        psum += p;
       }
-      lrun += psum;
-      mrun = mnew;
+    if (__any(mnew > mrun)) {
+      const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(mrun - mnew);
+      lrun *= alpha;
 #pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        const int c = mm >> 1, half = mm & 1;
-        uint32_t pw[4];
+      for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(st[c][half * 8 + 2 * e], st[c][half * 8 + 2 * e + 1]);
-        const bf16x8_t pf = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
-        const int kbase = c * 32 + half * 16 + h * 4;   // keys kbase+0..3 and kbase+8..11
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    }
+    lrun += psum;
+    mrun = mnew;
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const int r = db * 32 + col;
-          const u32x2_t lo = *(const u32x2_t*)(vs + vsw(r, kbase >> 2));
-          const u32x2_t hi = *(const u32x2_t*)(vs + vsw(r, (kbase + 8) >> 2));
-          o[db] = mfma32(as_bf16x8(u32x4_t{lo[0], lo[1], hi[0], hi[1]}), pf, o[db]);
-        }
+    for (int mm = 0; mm < 4; ++mm) {
+      const int c = mm >> 1, half = mm & 1;
+      uint32_t pw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(st[c][half * 8 + 2 * e], st[c][half * 8 + 2 * e + 1]);
+      const bf16x8_t pf = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8_t vf = as_bf16x8(ldv4(vs + vq_sw(db * 32 + col, 2 * mm + h)));
+        o[db] = mfma32(vf, pf, o[db]);
       }
     }
-    if (kt + 1 < ntiles) sstore(cur ^ 1);
-    __syncthreads();
+  };
+  for (int t = 0; t < AHEAD; ++t) issue(t);
+  for (int kt = 0; kt < ntiles; ++kt) {
+    // tile kt may leave the two later tiles (4 loads per wave each) in flight
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    sync();
+    issue(kt + AHEAD);   // into the stage read in iteration kt - 1, finished before the barrier
+    if (kt == ntiles - 1 && kv_end % PK) {
+      // keys kv_end .. of the last tile hold arbitrary bits: clear V^T there
+      // (their probabilities are 0, but 0 * NaN would not be)
+      bf16_t* vs = smem + (kt % AQ_NS) * AQ_STAGE + PK * PD;
+      const int lim = kv_end - kt * PK;
+      for (int idx = tid; idx < PD * 8; idx += 64 * NW) {
+        const int r = idx >> 3, u = idx & 7;
+        if (8 * u + 8 > lim) {
+          bf16_t* p = vs + vq_sw(r, u);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (8 * u + e >= lim) p[e] = 0;
+        }
+      }
+      sync();
+    }
+    if (kt * PK <= wave_last) {
+      scores(kt);
+      softmax_pv(kt);
+    }
   }
-  if (wid < G && qvalid) {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
+  if (qvalid) {
     const float ltot = lrun + __shfl_xor(lrun, 32, 64);
     const float inv = 1.0f / ltot;
     bf16_t* O = (bf16_t*)a.out + (size_t)(b * a.S_call + m) * a.ldo + j * PD;
@@ -302,13 +326,13 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
     tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
     tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
     const float mnew = fmaxf(mrun, tmax);
-    const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(mrun - mnew);
+    const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(mrun - mnew);
     float psum = 0.f;
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = (mnew == -INFINITY) ? 0.f : exp2f(st[sb][i] - mnew);
+        const float p = (mnew == -INFINITY) ? 0.f : exp2_hw(st[sb][i] - mnew);
         st[sb][i] = p;
         psum += p;
       }
@@ -359,8 +383,8 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
       const float* slot = &mrg[wid][c][0];
       const float m2 = slot[PD], l2 = slot[PD + 1];
       const float M = fmaxf(mrun, m2);
-      const float a1 = (mrun == -INFINITY) ? 0.f : exp2f(mrun - M);
-      const float a2 = (m2 == -INFINITY) ? 0.f : exp2f(m2 - M);
+      const float a1 = (mrun == -INFINITY) ? 0.f : exp2_hw(mrun - M);
+      const float a2 = (m2 == -INFINITY) ? 0.f : exp2_hw(m2 - M);
 #pragma unroll
       for (int db = 0; db < 8; ++db)
 #pragma unroll
@@ -400,7 +424,7 @@ __global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
   float L = 0.f, acc = 0.f;
   for (int s = 0; s < a.n_split; ++s) {
     const float ms = P[s * (a.d + 2) + a.d];
-    const float w = (ms == -INFINITY) ? 0.f : exp2f(ms - M);
+    const float w = (ms == -INFINITY) ? 0.f : exp2_hw(ms - M);
     L += P[s * (a.d + 2) + a.d + 1] * w;
     if (dd < a.d) acc += P[s * (a.d + 2) + dd] * w;
   }
@@ -455,20 +479,17 @@ hipError_t attn_prefill(const AttnArgs& a, hipStream_t s) {
   if (a.S_call <= 0 || a.B <= 0) return hipSuccess;
   if (a.dt == DT_F32) return launch_f32(a, s);
   const int G = a.Hq / a.Hkv;
-  if (a.d != PD || G < 1 || G > 8 || a.Hq % a.Hkv || a.S_max % 64) return hipErrorInvalidValue;
-  const int threads = G <= 4 ? 256 : 512;
-  const int lds = 2 * 2 * PK * PD * 2;   // 64 KB
+  if (a.d != PD || a.Hq % a.Hkv || !(G == 1 || G == 2 || G == 4 || G == 8) || a.S_max % 64)
+    return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_mfma<256>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)attn_prefill_mfma<512>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_dma, hipFuncAttributeMaxDynamicSharedMemorySize, AQ_LDS);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  dim3 grid((a.S_call + PQ - 1) / PQ, a.Hkv, a.B);
-  if (threads == 256) attn_prefill_mfma<256><<<grid, 256, lds, s>>>(a);
-  else attn_prefill_mfma<512><<<grid, 512, lds, s>>>(a);
+  const int qpw = 32 * (AQ_NW / G);   // queries per workgroup
+  dim3 grid((a.S_call + qpw - 1) / qpw, a.Hkv, a.B);
+  attn_prefill_dma<<<grid, 64 * AQ_NW, AQ_LDS, s>>>(a);
   return hipGetLastError();
 }
 

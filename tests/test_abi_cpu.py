@@ -69,6 +69,7 @@ def _create(cfg, n_layers=None):
     (dict(head_dim=96), -2),
     (dict(dtype="bf16"), -2),                 # bf16 needs head_dim 128
     (dict(dtype="bf16", head_dim=128, hidden=200), -2),
+    (dict(dtype="bf16", head_dim=128, hidden=256, n_heads=6, n_kv_heads=2), -2),   # group of 3 heads
 ])
 def test_create_rejects_bad_configs(kw, code):
     from looped_weight_shared_loop_amd import LoopError
