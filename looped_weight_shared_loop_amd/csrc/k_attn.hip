@@ -117,15 +117,17 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
   auto scores = [&](int kt) {
     const bf16_t* ks = smem + (kt % AQ_NS) * AQ_STAGE;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) st[c][r] = 0.f;
+    // the two 32-key blocks alternate, so consecutive MFMAs are independent
 #pragma unroll
-      for (int ds = 0; ds < 8; ++ds) {
+    for (int ds = 0; ds < 8; ++ds)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
         const bf16x8_t kf = as_bf16x8(ldv4(ks + kq_sw(c * 32 + krow, ds * 2 + h)));
         st[c] = mfma32(kf, qf[ds], st[c]);
       }
-    }
   };
   auto softmax_pv = [&](int kt) {
     const bf16_t* vs = smem + (kt % AQ_NS) * AQ_STAGE + PK * PD;

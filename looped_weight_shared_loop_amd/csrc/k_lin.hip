@@ -9,6 +9,8 @@
 //                the total becomes the outgoing state
 //   lin_output : per chunk and query head,
 //                o = (phi(Q) S_c + tril(phi(Q) phi(K)^T) V) / (phi(Q) z_c + rowsum + eps)
+// bf16 with d = 128 runs the same three steps on the matrix cores (lin_delta_bf,
+// lin_scan_t, lin_out_bf) with operands split into bf16 high and low parts.
 // Decode (a few tokens per sequence) runs the recurrence with S in registers.
 #include "common.h"
 #include "kernels.h"
@@ -18,6 +20,8 @@ namespace lk {
 constexpr int LC = 64;   // chunk length
 
 DEV float phi(float x) { return x > 0.f ? x + 1.0f : expf(x); }
+// the same with the hardware exponential (about 1 ulp), for the bf16 paths
+DEV float phi_hw(float x) { return x > 0.f ? x + 1.0f : exp2_hw(x * 1.4426950408889634f); }
 
 size_t lin_scratch_floats(int B, int Hkv, int d, int S_call, int chunk) {
   const int nc = (S_call + chunk - 1) / chunk;
@@ -227,160 +231,340 @@ __global__ __launch_bounds__(256) void lin_output(LinArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ chunk outputs, MFMA (d = 128)
-// One workgroup per (chunk, sequence, KV head) serves the G query heads of the
-// group, so S_c, z_c, phi(K) and V of the chunk are staged in LDS once.
-// Products use v_mfma_f32_16x16x4f32 (float32 operands, the state stays
-// float32).  Wave w owns chunk rows 16 w .. 16 w + 15.  In every product, lane
-// group g = lane / 16 carries the contiguous slice g * K/4 .. of the
-// contraction index on both operands (the sum is order-independent).
-//   A_g   = tril(phi(Q_g) phi(K)^T)                 [64 x 64]
-//   num_g = phi(Q_g) S_c + A_g V                      [64 x 128]
-//   den_g = phi(Q_g) z_c + rowsum(A_g) + eps
-typedef float f32x4v __attribute__((ext_vector_type(4)));
-DEV f32x4v mfma_f32(float a, float b, f32x4v c) { return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0); }
+// ------------------------------------------------------------------ bf16, d = 128, matrix cores
+// The same three steps on v_mfma_f32_32x32x16_bf16.  Every fp32 operand
+// (phi(q), phi(k), the state, the intra-chunk weights A) is split into a bf16
+// high part and the bf16 rounding of its remainder; a product takes
+// hi.hi + hi.lo + lo.hi (lo.lo, about 2^-16 of the term, is dropped), with
+// fp32 accumulation.  V is bf16 already and enters once.  Everything is
+// computed transposed (rows = output feature j or key tau, columns = token):
+// the chunk deltas and prefixes are stored as S^T [j][k].
+constexpr int LP = LC + 8;      // LDS pitch (elements) of [128][64] tiles
+constexpr int SP = 128 + 8;     // LDS pitch of [*][128] tiles
 
-constexpr int LSP = 132;   // padded row of S^T and phi(K) (floats)
-constexpr int LAP = 68;    // padded row of V^T and A (floats)
-constexpr int LIN_MFMA_LDS = (128 * LSP + 64 * LSP + 128 * LAP + 64 * LAP + 128 + 64) * 4;
+DEV void split_bf16(float x, bf16_t& hi, bf16_t& lo) {
+  hi = f2bf(x);
+  lo = f2bf(x - bf2f(hi));
+}
 
-template <typename T>
-__global__ __launch_bounds__(256, 1) void lin_output_mfma(LinArgs a) {
-  extern __shared__ float lsm[];
-  float* St = lsm;                  // [128][LSP]: St[j][k] = S_c[k][j]
-  float* Kf = St + 128 * LSP;       // [64][LSP]: phi(K)[tau][d]
-  float* Vt = Kf + 64 * LSP;        // [128][LAP]: Vt[j][tau] = V[tau][j]
-  float* Am = Vt + 128 * LAP;       // [64][LAP]: masked A of the current head
-  float* zc = Am + 64 * LAP;        // [128]
-  float* den = zc + 128;            // [64]
+// dS_c^T [j][k] = sum_tau V[tau][j] phi(K)[tau][k], dz_c = sum_tau phi(K)[tau]
+__global__ __launch_bounds__(256) void lin_delta_bf(LinArgs a) {
   constexpr int D = 128;
+  __shared__ __align__(16) bf16_t Kth[D * LP], Ktl[D * LP], Vt[D * LP];   // [feature][tau]
+  __shared__ float zp[16][D];
   const int c = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
-  const int G = a.Hq / a.Hkv;
   const int nc = gridDim.x;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int li = lane & 15, g = lane >> 4;
-  const T* base = (const T*)a.qkv;
-
-  {  // stage S_c^T, z_c, phi(K), V^T
-    const float* src = a.scratch + ((size_t)bh * nc + c) * (D * D + D);
-    for (int idx = tid; idx < D * D / 4; idx += 256) {
-      const int k = idx >> 5, j4 = (idx & 31) * 4;
-      const float4 v = reinterpret_cast<const float4*>(src)[idx];
-      St[(j4 + 0) * LSP + k] = v.x;
-      St[(j4 + 1) * LSP + k] = v.y;
-      St[(j4 + 2) * LSP + k] = v.z;
-      St[(j4 + 3) * LSP + k] = v.w;
+  const bf16_t* base = (const bf16_t*)a.qkv;
+  {
+    const int i8 = (tid & 15) * 8;          // this thread's 8 features
+    float zs[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    u32x4_t kraw[4], vraw[4];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int sq = min(c * LC + (tid >> 4) + 16 * s4, a.S_call - 1);
+      const bf16_t* row = base + (size_t)(b * a.S_call + sq) * a.ld;
+      kraw[s4] = ldv4(row + (a.Hq + hk) * D + i8);
+      vraw[s4] = ldv4(row + (a.Hq + a.Hkv + hk) * D + i8);
     }
-    if (tid < D) zc[tid] = src[D * D + tid];
-    for (int idx = tid; idx < LC * D / 8; idx += 256) {
-      const int t = idx >> 4, i8 = (idx & 15) * 8;
-      const int s = c * LC + t;
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int t = (tid >> 4) + 16 * s4;
+      const bool ok = c * LC + t < a.S_call;
       float kx[8], vx[8];
-      if (s < a.S_call) {
-        const T* row = base + (size_t)(b * a.S_call + s) * a.ld;
-        ld8(row + (a.Hq + hk) * D + i8, kx);
-        ld8(row + (a.Hq + a.Hkv + hk) * D + i8, vx);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) kx[e] = phi(kx[e]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { kx[e] = 0.f; vx[e] = 0.f; }
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t wk = kraw[s4][e >> 1], wv = vraw[s4][e >> 1];
+        kx[e] = ok ? phi(__uint_as_float((e & 1) ? (wk & 0xFFFF0000u) : (wk << 16))) : 0.f;
+        vx[e] = ok ? __uint_as_float((e & 1) ? (wv & 0xFFFF0000u) : (wv << 16)) : 0.f;
       }
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        Kf[t * LSP + i8 + e] = kx[e];
-        Vt[(i8 + e) * LAP + t] = vx[e];
+        zs[e] += kx[e];
+        bf16_t hi, lo;
+        split_bf16(kx[e], hi, lo);
+        Kth[(i8 + e) * LP + t] = hi;
+        Ktl[(i8 + e) * LP + t] = lo;
+        Vt[(i8 + e) * LP + t] = f2bf(vx[e]);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) zp[tid >> 4][i8 + e] = zs[e];
+  }
+  __syncthreads();
+  // wave w: rows j in [32 w, 32 w + 32), all four 32-column blocks of k
+  f32x16_t acc[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[kb][r] = 0.f;
+  const int rl = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int ks = 0; ks < LC / 16; ++ks) {
+    const int tc = ks * 16 + h * 8;
+    const bf16x8_t va = as_bf16x8(ldv4(Vt + (32 * w + rl) * LP + tc));
+    bf16x8_t kh[4], kl[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      kh[kb] = as_bf16x8(ldv4(Kth + (32 * kb + rl) * LP + tc));
+      kl[kb] = as_bf16x8(ldv4(Ktl + (32 * kb + rl) * LP + tc));
+    }
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) acc[kb] = mfma32(va, kh[kb], acc[kb]);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) acc[kb] = mfma32(va, kl[kb], acc[kb]);
+  }
+  float* out = a.scratch + ((size_t)bh * nc + c) * (D * D + D);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int j = 32 * w + (r >> 2) * 8 + h * 4 + (r & 3);
+      out[j * D + 32 * kb + rl] = acc[kb][r];
+    }
+  if (tid < D) {
+    float zt = 0.f;
+#pragma unroll
+    for (int g = 0; g < 16; ++g) zt += zp[g][tid];
+    out[D * D + tid] = zt;
+  }
+}
+
+// Exclusive prefix over chunks of the transposed deltas, seeded by the
+// incoming state S [k][j], z; the total becomes the outgoing state.
+__global__ __launch_bounds__(256) void lin_scan_t(LinArgs a, int nc) {
+  constexpr int D = 128, E = D * D + D, U = 8;
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  const int bh = blockIdx.y;
+  if (e >= E) return;
+  float* st = (e < D * D) ? (a.S + (size_t)bh * D * D + (e % D) * D + e / D) : (a.z + (size_t)bh * D + (e - D * D));
+  float run = a.init_zero ? 0.f : *st;
+  float* p = a.scratch + (size_t)bh * nc * E + e;
+  int c = 0;
+  for (; c + U <= nc; c += U) {
+    float t[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) t[u] = p[(size_t)(c + u) * E];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      p[(size_t)(c + u) * E] = run;
+      run += t[u];
+    }
+  }
+  for (; c < nc; ++c) {
+    const float t = p[(size_t)c * E];
+    p[(size_t)c * E] = run;
+    run += t;
+  }
+  *st = run;
+}
+
+// One workgroup per (chunk, sequence x KV head) and up to four query heads of
+// the group, two waves per head (one per 32-token column block).  Per head:
+//   A^T  = mask(phi(K) phi(Q)^T)          [64 tau x 64 t]
+//   num^T = S_c^T phi(Q)^T + V^T A^T      [128 j x 64 t]
+//   den  = phi(Q) z_c + column sums of A^T + eps
+constexpr int LIN_BF_LDS = (2 * 128 * SP + 2 * 64 * SP + 128 * LP) * 2 + 128 * 4;
+
+template <int NH>
+__global__ __launch_bounds__(128 * NH, 1) void lin_out_bf(LinArgs a) {
+  constexpr int D = 128;
+  constexpr int nthr = 128 * NH;            // two waves per query head (NH heads here)
+  extern __shared__ __align__(16) bf16_t lsb[];
+  bf16_t* Sth = lsb;                  // [128 j][SP]: S_c^T high part
+  bf16_t* Stl = Sth + 128 * SP;       // low part
+  bf16_t* Kh = Stl + 128 * SP;        // [64 tau][SP]: phi(K) high
+  bf16_t* Kl = Kh + 64 * SP;          // low
+  bf16_t* Vt = Kl + 64 * SP;          // [128 j][LP]: V^T
+  float* zc = (float*)(Vt + 128 * LP);
+  const int c = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / a.Hkv, hk = bh % a.Hkv;
+  const int nc = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int rl = lane & 31, h = lane >> 5;
+  const bf16_t* base = (const bf16_t*)a.qkv;
+  const int j_q = hk * (a.Hq / a.Hkv) + blockIdx.z * NH + (w >> 1);   // this wave's query head
+  const int tb = w & 1;                                               // and token block
+  const int sq_mine = c * LC + tb * 32 + rl;                          // this lane's token
+  // this lane's q fragments for all 8 k-steps, requested before the staging
+  // so that they arrive while it runs
+  u32x4_t qraw[8];
+  {
+    const bf16_t* qrow = base + (size_t)(b * a.S_call + min(sq_mine, a.S_call - 1)) * a.ld + j_q * D + h * 8;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) qraw[ks] = ldv4(qrow + ks * 16);
+  }
+  {  // stage S_c^T (split), z_c, phi(K) (split, zero past the end), V^T
+    const float* src = a.scratch + ((size_t)bh * nc + c) * (D * D + D);
+    constexpr int SPT = D * D / 4 / nthr;     // float4 per thread
+    constexpr int SB = SPT < 16 ? SPT : 16;   // issued together
+    constexpr int KPT = LC * D / 8 / nthr;    // 8-wide K / V items per thread
+    constexpr int KB = KPT < 4 ? KPT : 4;
+    if (tid < D) zc[tid] = src[D * D + tid];
+#pragma unroll
+    for (int k0 = 0; k0 < KPT; k0 += KB) {
+      u32x4_t kraw[KB], vraw[KB];
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const int idx = tid + (k0 + i) * nthr;
+        const int t = idx >> 4, i8 = (idx & 15) * 8;
+        const int sq = min(c * LC + t, a.S_call - 1);
+        const bf16_t* row = base + (size_t)(b * a.S_call + sq) * a.ld;
+        kraw[i] = ldv4(row + (a.Hq + hk) * D + i8);
+        vraw[i] = ldv4(row + (a.Hq + a.Hkv + hk) * D + i8);
+      }
+#pragma unroll
+      for (int i = 0; i < KB; ++i) {
+        const int idx = tid + (k0 + i) * nthr;
+        const int t = idx >> 4, i8 = (idx & 15) * 8;
+        const bool ok = c * LC + t < a.S_call;
+        bf16_t hi[8], lo[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t wk = kraw[i][e >> 1], wv = vraw[i][e >> 1];
+          const float kx = __uint_as_float((e & 1) ? (wk & 0xFFFF0000u) : (wk << 16));
+          split_bf16(ok ? phi_hw(kx) : 0.f, hi[e], lo[e]);
+          Vt[(i8 + e) * LP + t] = ok ? (bf16_t)((e & 1) ? (wv >> 16) : (wv & 0xFFFFu)) : (bf16_t)0;
+        }
+        u32x4_t ph, pl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ph[e] = hi[2 * e] | ((uint32_t)hi[2 * e + 1] << 16);
+          pl[e] = lo[2 * e] | ((uint32_t)lo[2 * e + 1] << 16);
+        }
+        stv4(Kh + t * SP + i8, ph);
+        stv4(Kl + t * SP + i8, pl);
+      }
+    }
+#pragma unroll
+    for (int s0 = 0; s0 < SPT; s0 += SB) {
+      float4 sv[SB];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) sv[i] = reinterpret_cast<const float4*>(src)[tid + (s0 + i) * nthr];
+#pragma unroll
+      for (int i = 0; i < SB; ++i) {
+        const int idx = tid + (s0 + i) * nthr;
+        const int j = idx >> 5, k4 = (idx & 31) * 4;
+        bf16_t hi[4], lo[4];
+        split_bf16(sv[i].x, hi[0], lo[0]);
+        split_bf16(sv[i].y, hi[1], lo[1]);
+        split_bf16(sv[i].z, hi[2], lo[2]);
+        split_bf16(sv[i].w, hi[3], lo[3]);
+        *(u32x2_t*)(Sth + j * SP + k4) = u32x2_t{hi[0] | ((uint32_t)hi[1] << 16), hi[2] | ((uint32_t)hi[3] << 16)};
+        *(u32x2_t*)(Stl + j * SP + k4) = u32x2_t{lo[0] | ((uint32_t)lo[1] << 16), lo[2] | ((uint32_t)lo[3] << 16)};
       }
     }
   }
   __syncthreads();
 
-  const int t_row = 16 * w + li;                // A-operand row of this lane
-  const int s_q = c * LC + t_row;
-  for (int hq = 0; hq < G; ++hq) {
-    const int j = hk * G + hq;
-    // phi(q) of row t_row, d in [32 g, 32 g + 32)
-    float q[32];
-    if (s_q < a.S_call) {
-      const T* row = base + (size_t)(b * a.S_call + s_q) * a.ld + j * D + 32 * g;
+  // num^T [128 j x 32 t] of this wave's token block and A^T blocks x <= tb
+  f32x16_t num[4], at[2];
 #pragma unroll
-      for (int v8 = 0; v8 < 4; ++v8) {
-        ld8(row + 8 * v8, q + 8 * v8);
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) q[8 * v8 + e] = phi(q[8 * v8 + e]);
-      }
-    } else {
+    for (int r = 0; r < 16; ++r) num[db][r] = 0.f;
 #pragma unroll
-      for (int e = 0; e < 32; ++e) q[e] = 0.f;
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) at[x][r] = 0.f;
+  const bool tok_ok = sq_mine < a.S_call;
+  float den = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const int dc = ks * 16 + h * 8;           // this lane's 8 features of the step
+    float x8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t wq = qraw[ks][e >> 1];
+      x8[e] = tok_ok ? phi_hw(__uint_as_float((e & 1) ? (wq & 0xFFFF0000u) : (wq << 16))) : 0.f;
+      den += x8[e] * zc[dc + e];
     }
-    // A blocks of this wave's rows: tau blocks nb <= w (later blocks are masked)
-    for (int nb = 0; nb < 4; ++nb) {
-      f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-      if (nb <= w) {
-        const float* kr = Kf + (16 * nb + li) * LSP + 32 * g;
+    u32x4_t ph, pl;
 #pragma unroll
-        for (int s4 = 0; s4 < 8; ++s4) {
-          const float4 kv = *reinterpret_cast<const float4*>(kr + 4 * s4);
-          acc = mfma_f32(q[4 * s4 + 0], kv.x, acc);
-          acc = mfma_f32(q[4 * s4 + 1], kv.y, acc);
-          acc = mfma_f32(q[4 * s4 + 2], kv.z, acc);
-          acc = mfma_f32(q[4 * s4 + 3], kv.w, acc);
+    for (int e = 0; e < 4; ++e) {
+      bf16_t h0, l0, h1, l1;
+      split_bf16(x8[2 * e], h0, l0);
+      split_bf16(x8[2 * e + 1], h1, l1);
+      ph[e] = h0 | ((uint32_t)h1 << 16);
+      pl[e] = l0 | ((uint32_t)l1 << 16);
+    }
+    const bf16x8_t qh = as_bf16x8(ph), ql = as_bf16x8(pl);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+      if (x <= tb) {
+        const bf16x8_t kh = as_bf16x8(ldv4(Kh + (32 * x + rl) * SP + dc));
+        const bf16x8_t kl = as_bf16x8(ldv4(Kl + (32 * x + rl) * SP + dc));
+        at[x] = mfma32(kh, qh, at[x]);
+        at[x] = mfma32(kh, ql, at[x]);
+        at[x] = mfma32(kl, qh, at[x]);
+      }
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const bf16x8_t sh = as_bf16x8(ldv4(Sth + (32 * db + rl) * SP + dc));
+      const bf16x8_t sl = as_bf16x8(ldv4(Stl + (32 * db + rl) * SP + dc));
+      num[db] = mfma32(sh, qh, num[db]);
+      num[db] = mfma32(sh, ql, num[db]);
+      num[db] = mfma32(sl, qh, num[db]);
+    }
+    __builtin_amdgcn_sched_barrier(0);   // keep the steps apart: bounded register use
+  }
+  // causal mask of the diagonal block: at[tb][r] holds tau = 32 tb + (r/4)*8 + 4h + r%4, t = 32 tb + rl
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+    if (x == tb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if ((r >> 2) * 8 + h * 4 + (r & 3) > rl) at[x][r] = 0.f;
+  // den: the two lane halves hold parts of phi(q) . z_c and of the column sums of A^T
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+    if (x <= tb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) den += at[x][r];
+  den += __shfl_xor(den, 32, 64);
+  // num^T += V^T A^T: k-step (x, half) covers tau 32x + 16half + {4h .. 4h+3, 8+4h .. 8+4h+3}
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+    if (x <= tb)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int t0 = 32 * x + 16 * half + 4 * h;
+        bf16x8_t vf[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const bf16_t* vr = Vt + (32 * db + rl) * LP;
+          const u32x2_t lo8 = *(const u32x2_t*)(vr + t0);
+          const u32x2_t hi8 = *(const u32x2_t*)(vr + t0 + 8);
+          vf[db] = as_bf16x8(u32x4_t{lo8[0], lo8[1], hi8[0], hi8[1]});
         }
+        u32x4_t ph, pl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bf16_t h0, l0, h1, l1;
+          split_bf16(at[x][half * 8 + 2 * e], h0, l0);
+          split_bf16(at[x][half * 8 + 2 * e + 1], h1, l1);
+          ph[e] = h0 | ((uint32_t)h1 << 16);
+          pl[e] = l0 | ((uint32_t)l1 << 16);
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) num[db] = mfma32(vf[db], as_bf16x8(ph), num[db]);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) num[db] = mfma32(vf[db], as_bf16x8(pl), num[db]);
       }
-      // acc[r]: row 16 w + 4 g + r, column tau = 16 nb + li
+  // out[t][j_q d + j] = num^T[j][t] / den[t]; lane: column t, rows j in runs of 4
+  if (tok_ok) {
+    const float inv = 1.0f / (den + a.eps);
+    bf16_t* orow = (bf16_t*)a.out + (size_t)(b * a.S_call + sq_mine) * a.ldo + j_q * D;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * g + r, tau = 16 * nb + li;
-        Am[t * LAP + tau] = (tau <= t) ? acc[r] : 0.f;
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int j0 = 32 * db + g4 * 8 + h * 4;
+        const uint32_t w0 = pack_bf16x2(num[db][g4 * 4] * inv, num[db][g4 * 4 + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(num[db][g4 * 4 + 2] * inv, num[db][g4 * 4 + 3] * inv);
+        *(u32x2_t*)(orow + j0) = u32x2_t{w0, w1};
       }
-    }
-    __syncthreads();
-    {  // den for row t_row: phi(q) . z_c over the lane's slice + row sum of A over tau in [16 g, 16 g + 16)
-      float p = 0.f;
-#pragma unroll
-      for (int e = 0; e < 32; ++e) p += q[e] * zc[32 * g + e];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) p += Am[t_row * LAP + 16 * g + e];
-      p += __shfl_xor(p, 16, 64);
-      p += __shfl_xor(p, 32, 64);
-      if (g == 0) den[t_row] = p + a.eps;
-    }
-    __syncthreads();
-    float dinv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) dinv[r] = 1.0f / den[16 * w + 4 * g + r];
-    T* out = (T*)a.out;
-    for (int jb = 0; jb < 8; ++jb) {
-      f32x4v acc = {0.f, 0.f, 0.f, 0.f};
-      const float* sr = St + (16 * jb + li) * LSP + 32 * g;
-#pragma unroll
-      for (int s4 = 0; s4 < 8; ++s4) {
-        const float4 sv = *reinterpret_cast<const float4*>(sr + 4 * s4);
-        acc = mfma_f32(q[4 * s4 + 0], sv.x, acc);
-        acc = mfma_f32(q[4 * s4 + 1], sv.y, acc);
-        acc = mfma_f32(q[4 * s4 + 2], sv.z, acc);
-        acc = mfma_f32(q[4 * s4 + 3], sv.w, acc);
-      }
-      const float* ar = Am + t_row * LAP + 16 * g;
-      const float* vr = Vt + (16 * jb + li) * LAP + 16 * g;
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) {
-        const float4 av = *reinterpret_cast<const float4*>(ar + 4 * s4);
-        const float4 vv4 = *reinterpret_cast<const float4*>(vr + 4 * s4);
-        acc = mfma_f32(av.x, vv4.x, acc);
-        acc = mfma_f32(av.y, vv4.y, acc);
-        acc = mfma_f32(av.z, vv4.z, acc);
-        acc = mfma_f32(av.w, vv4.w, acc);
-      }
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = 16 * w + 4 * g + r;
-        const int s = c * LC + t;
-        if (s < a.S_call) st1(out + (size_t)(b * a.S_call + s) * a.ldo + j * D + 16 * jb + li, acc[r] * dinv[r]);
-      }
-    }
-    __syncthreads();   // Am and den are rewritten by the next head
   }
 }
 
@@ -457,9 +641,6 @@ static hipError_t prefill_t(const LinArgs& a, hipStream_t s) {
     hipError_t e = hipFuncSetAttribute((const void*)lin_delta<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds1);
     if (e == hipSuccess)
       e = hipFuncSetAttribute((const void*)lin_output<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds3);
-    if (e == hipSuccess && D == 128)
-      e = hipFuncSetAttribute((const void*)lin_output_mfma<T>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              LIN_MFMA_LDS);
     if (e != hipSuccess) return e;
     attr = true;
   }
@@ -470,16 +651,46 @@ static hipError_t prefill_t(const LinArgs& a, hipStream_t s) {
   lin_scan<<<dim3((E + 255) / 256, BH), 256, 0, s>>>(a, nc);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (D == 128) lin_output_mfma<T><<<dim3(nc, BH), 256, LIN_MFMA_LDS, s>>>(a);
-  else lin_output<T, D><<<dim3(nc, a.B * a.Hq), 256, lds3, s>>>(a);
+  lin_output<T, D><<<dim3(nc, a.B * a.Hq), 256, lds3, s>>>(a);
   return hipGetLastError();
+}
+
+template <int NH>
+static hipError_t launch_out_bf(const LinArgs& a, int nc, int BH, hipStream_t s) {
+  static bool attr = false;
+  if (!attr) {
+    hipError_t e = hipFuncSetAttribute((const void*)lin_out_bf<NH>, hipFuncAttributeMaxDynamicSharedMemorySize, LIN_BF_LDS);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  // groups of eight heads take two workgroups of four
+  lin_out_bf<NH><<<dim3(nc, BH, a.Hq / a.Hkv / NH), 128 * NH, LIN_BF_LDS, s>>>(a);
+  return hipGetLastError();
+}
+
+static hipError_t prefill_bf128(const LinArgs& a, hipStream_t s) {
+  const int G = a.Hq / a.Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return hipErrorInvalidValue;
+  const int nc = (a.S_call + LC - 1) / LC;
+  const int BH = a.B * a.Hkv;
+  lin_delta_bf<<<dim3(nc, BH), 256, 0, s>>>(a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  lin_scan_t<<<dim3((128 * 128 + 128 + 255) / 256, BH), 256, 0, s>>>(a, nc);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (G) {
+    case 1: return launch_out_bf<1>(a, nc, BH, s);
+    case 2: return launch_out_bf<2>(a, nc, BH, s);
+    default: return launch_out_bf<4>(a, nc, BH, s);
+  }
 }
 
 hipError_t lin_prefill(const LinArgs& a, hipStream_t s) {
   if (a.S_call <= 0 || a.B <= 0) return hipSuccess;
   if (a.Hq % a.Hkv || a.Hq / a.Hkv > 8 || a.chunk != LC) return hipErrorInvalidValue;
   if (a.dt == DT_BF16) {
-    if (a.d == 128) return prefill_t<bf16_t, 128>(a, s);
+    if (a.d == 128) return prefill_bf128(a, s);
     if (a.d == 64) return prefill_t<bf16_t, 64>(a, s);
   } else {
     if (a.d == 128) return prefill_t<float, 128>(a, s);
