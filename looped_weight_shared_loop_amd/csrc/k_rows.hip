@@ -127,11 +127,14 @@ DEV void mhc_maps_from_logits(const float* l, int iters, float* m) {
   m[3] = 2.0f / (1.0f + expf(-l[3]));
   const float mx = fmaxf(fmaxf(l[4], l[5]), fmaxf(l[6], l[7]));
   float a = expf(l[4] - mx), b = expf(l[5] - mx), c = expf(l[6] - mx), d = expf(l[7] - mx);
+  // rows, then columns, each scaled by the hardware reciprocal of its sum
+  // (about 1 ulp; the iteration is a contraction, so these roundings do not
+  // accumulate)
   for (int it = 0; it < iters; ++it) {
-    const float r0 = a + b, r1 = c + d;
-    a = a / r0; b = b / r0; c = c / r1; d = d / r1;
-    const float c0 = a + c, c1 = b + d;
-    a = a / c0; c = c / c0; b = b / c1; d = d / c1;
+    const float i0 = __builtin_amdgcn_rcpf(a + b), i1 = __builtin_amdgcn_rcpf(c + d);
+    a *= i0; b *= i0; c *= i1; d *= i1;
+    const float j0 = __builtin_amdgcn_rcpf(a + c), j1 = __builtin_amdgcn_rcpf(b + d);
+    a *= j0; c *= j0; b *= j1; d *= j1;
   }
   m[4] = a; m[5] = b; m[6] = c; m[7] = d;
 }
