@@ -410,8 +410,14 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
     LAUNCH(hipMemcpyAsync(h, embeds, (size_t)T * C * m->es, hipMemcpyDeviceToDevice, s), "copy embeds");
   }
 
+  // Decode-shaped o and down projections leave their split-K partials in the
+  // workspace; the norm or mHC kernel that consumes y sums them (ypend).
+  lk::YPart ypend{};
   auto norm = [&](const void* yin, const float* gamma) {
-    lk::NormArgs a{dt, T, C, yin, h, gamma, u, c.rms_eps};
+    lk::NormArgs a{};
+    a.dt = dt; a.T = T; a.C = C; a.y = yin; a.h = h; a.gamma = gamma; a.u = u; a.eps = c.rms_eps;
+    if (yin) a.yp = ypend;
+    ypend = lk::YPart{};
     return lk::add_rmsnorm(a, s);
   };
   int mp = 0;   // maps[mp] holds the maps of the current mHC site
@@ -419,6 +425,8 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
     lk::MhcArgs a{};
     a.dt = dt; a.mode = mode; a.T = T; a.C = C; a.iters = c.sinkhorn_iters; a.eps = c.rms_eps;
     a.y = yin; a.h = h; a.X = X;
+    if (yin) a.yp = ypend;
+    ypend = lk::YPart{};
     a.maps_in = maps[mp];
     a.maps_out = maps[mp ^ 1];
     a.w = w; a.b = b; a.gamma = gamma; a.u = u; a.grid = mhc_grid;
@@ -428,7 +436,7 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
     return e;
   };
   // decode-shaped GEMMs split K over workgroups when the workspace holds the scratch
-  auto run_gemm = [&](lk::GemmArgs g) {
+  auto run_gemm = [&](lk::GemmArgs g, bool may_defer = false) {
     g.ksplit = 1;
     g.skinny_rb = 4;
     if (g.dt == lk::DT_BF16 && g.M <= 32) {
@@ -437,6 +445,10 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
       if (p.ksplit > 1 && p.bytes <= L.skinny_bytes) {
         g.ksplit = p.ksplit;
         g.part = (float*)(ws + L.skinny);
+        if (may_defer && g.epi == lk::EPI_STORE) {
+          g.defer_reduce = 1;
+          ypend = lk::YPart{g.part, p.ksplit, 32 * p.rb};
+        }
       }
     }
     return lk::gemm(g, s);
@@ -493,7 +505,7 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
       if (S <= 16) { LAUNCH(lk::lin_decode(a, s), "linear attention (recurrent)"); }
       else { LAUNCH(lk::lin_prefill(a, s), "linear attention (chunked)"); }
     }
-    LAUNCH(run_gemm(gemm(lk::EPI_STORE, attn, Hq * d, T, W.o, C, Hq * d, y, C)), "o gemm");
+    LAUNCH(run_gemm(gemm(lk::EPI_STORE, attn, Hq * d, T, W.o, C, Hq * d, y, C), decode), "o gemm");
     // ---- attention -> FFN transition
     if (looped) {
       LAUNCH(mhc(lk::MHC_MID, y, W.mhc_w[1], W.mhc_b[1], W.ffn_norm), "mhc");
@@ -506,7 +518,7 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
       g.F = c.ffn;
       LAUNCH(run_gemm(g), "gate/up gemm");
     }
-    LAUNCH(run_gemm(gemm(lk::EPI_STORE, inter, c.ffn, T, W.down, C, c.ffn, y, C)), "down gemm");
+    LAUNCH(run_gemm(gemm(lk::EPI_STORE, inter, c.ffn, T, W.down, C, c.ffn, y, C), decode), "down gemm");
     // ---- transition to the next execution (or the final norm)
     const bool has_next = e + 1 < E;
     const loop_layer_weights* Wn = has_next ? &m->layers[sched[e + 1].layer] : nullptr;

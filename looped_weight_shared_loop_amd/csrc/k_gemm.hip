@@ -412,7 +412,7 @@ static hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
   constexpr int R = 32 * RB;
   const int tiles = (EPI == EPI_SWIGLU) ? (a.F + R / 2 - 1) / (R / 2) : (a.N + R - 1) / R;
   gemm_skinny_kernel<EPI, RB><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
-  if (a.ksplit > 1) {
+  if (a.ksplit > 1 && !(a.defer_reduce && EPI == EPI_STORE)) {
     const long outs = (long)a.M * tiles * (EPI == EPI_SWIGLU ? R / 2 : R);
     gemm_skinny_reduce<EPI, RB><<<(int)((outs + 255) / 256), 256, 0, s>>>(a);
   }

@@ -57,6 +57,27 @@ DEV void block_sum(float* v, float (*red)[16][12], int par) {
 }
 
 // ------------------------------------------------------------------ add + RMSNorm
+// 8 channels c0 .. c0 + 7 (one GEMM tile) of token t of a sublayer output:
+// from y, or summed from the split-K partials and rounded like the stored y.
+template <typename T>
+DEV void ld8_y(const T* y, const YPart& yp, int t, int C, int c0, float* v) {
+  if (yp.part) {
+    const int R = yp.rows, tile = c0 / R, j = c0 - tile * R;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = 0.f;
+    for (int p = 0; p < yp.ks; ++p) {
+      const float4* q = reinterpret_cast<const float4*>(yp.part + ((size_t)(tile * yp.ks + p) * 32 + t) * R + j);
+      const float4 lo = q[0], hi = q[1];
+      v[0] += lo.x; v[1] += lo.y; v[2] += lo.z; v[3] += lo.w;
+      v[4] += hi.x; v[5] += hi.y; v[6] += hi.z; v[7] += hi.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = round_to(v[e], (T*)nullptr);
+    return;
+  }
+  ld8(y + (size_t)t * C + c0, v);
+}
+
 template <typename T, int MAXV>
 __global__ __launch_bounds__(256) void add_rmsnorm_kernel(NormArgs a) {
   __shared__ float red[2][16][12];
@@ -72,9 +93,9 @@ __global__ __launch_bounds__(256) void add_rmsnorm_kernel(NormArgs a) {
     const int vi = threadIdx.x + k * blockDim.x;
     if (vi < nv) {
       ld8(h + (size_t)r * C + vi * 8, x[k]);
-      if (y) {
+      if (y || a.yp.part) {
         float yv[8];
-        ld8(y + (size_t)r * C + vi * 8, yv);
+        ld8_y(y, a.yp, r, C, vi * 8, yv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[k][e] = round_to(x[k][e] + yv[e], (T*)nullptr);
         st8(h + (size_t)r * C + vi * 8, x[k]);
@@ -177,9 +198,9 @@ __global__ __launch_bounds__(512) void mhc_kernel(MhcArgs a) {
     if (act) {
       if (mode == MHC_ENTER) {
         ld8(h + (size_t)t * C + c0, x0);
-        if (y) {
+        if (y || a.yp.part) {
           float yv[8];
-          ld8(y + (size_t)t * C + c0, yv);
+          ld8_y(y, a.yp, t, C, c0, yv);
 #pragma unroll
           for (int e = 0; e < 8; ++e) x0[e] = round_to(x0[e] + yv[e], (T*)nullptr);
         }
@@ -191,7 +212,7 @@ __global__ __launch_bounds__(512) void mhc_kernel(MhcArgs a) {
         float p[8], q[8], yv[8];
         ld8(X + ((size_t)t * 2) * C + c0, p);
         ld8(X + ((size_t)t * 2 + 1) * C + c0, q);
-        ld8(y + (size_t)t * C + c0, yv);
+        ld8_y(y, a.yp, t, C, c0, yv);
         const float* mi = a.maps_in + (size_t)t * 8;
         const float po0 = mi[2], po1 = mi[3], r00 = mi[4], r01 = mi[5], r10 = mi[6], r11 = mi[7];
 #pragma unroll
@@ -465,6 +486,7 @@ hipError_t mhc(const MhcArgs& a, hipStream_t s) {
   // 16-token tiles on the matrix cores pay off once there are enough tiles;
   // fewer tokens (decode) take one workgroup per token with W in registers
   if (a.dt == DT_BF16 && a.mode != MHC_EXIT && a.C % 256 == 0 && a.wsplit && a.T >= MHC_MFMA_MIN_T) {
+    if (a.yp.part) return hipErrorInvalidValue;   // the tiled path reads y itself
     const int n = 8 * 2 * a.C;
     mhc_split_w<<<(n + 255) / 256, 256, 0, s>>>(a.w, a.wsplit, n);
     hipError_t e = hipGetLastError();

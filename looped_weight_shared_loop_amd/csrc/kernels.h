@@ -16,9 +16,19 @@ hipError_t embed(int dt, const int32_t* tokens, const void* table, int vocab, in
                  void* h, uint32_t* err_word, hipStream_t s);
 
 // h <- h + y (if y), u <- RMSNorm(h; gamma).  In place on h.
+// A bf16 [T][C] sublayer output that is still split-K partial sums of the
+// decode-shaped GEMM (tile of R output columns, ks partials of 32 rows):
+// element (t, c) = bf16(sum_p part[((c / R) * ks + p) * 32 + t) * R + c % R]),
+// the sum taken in index order as the GEMM's own reduction would.
+struct YPart {
+  const float* part;     // null: the output is stored in y
+  int ks, rows;
+};
+
 struct NormArgs {
   int dt, T, C;
   const void* y;
+  YPart yp;              // overrides y when yp.part is set (bf16, T <= 32)
   void* h;
   const float* gamma;
   void* u;
@@ -33,6 +43,7 @@ struct MhcArgs {
   int dt, mode, T, C, iters;
   float eps;
   const void* y;         // output of the sublayer just run (nullable on ENTER)
+  YPart yp;              // overrides y when yp.part is set (bf16, per-token path only)
   void* h;               // ENTER: residual in; EXIT: residual out
   void* X;               // [T][2][C] streams, updated in place
   const float* maps_in;  // [T][8] maps of the site being written back (MID, EXIT)
@@ -62,6 +73,7 @@ struct GemmArgs {
   int F;                 // EPI_SWIGLU: up rows start at row F of B
   // M <= 32: split-K plan (skinny_plan) and its scratch; ksplit 1 needs none.
   int ksplit;
+  int defer_reduce;      // ksplit > 1: leave the partials for the consumer (YPart)
   int skinny_rb;         // 32-row blocks per tile (2 or 4)
   float* part;           // [tiles * ksplit][32][32 * skinny_rb] fp32 partial sums
 };

@@ -73,7 +73,8 @@ int loop_op_add_rmsnorm(int dtype, int T, int C, const void* y, void* h, const f
   if (int r = dt_of(dtype, &dt)) return r;
   if (!h || !gamma || !u || T < 0 || C <= 0) return lp_fail(LOOP_ERR_INVALID_ARG, "arguments");
   if (any_misaligned({y, h, gamma, u})) return lp_fail(LOOP_ERR_ALIGN, "misaligned");
-  lk::NormArgs a{dt, T, C, y, h, gamma, u, eps};
+  lk::NormArgs a{};
+  a.dt = dt; a.T = T; a.C = C; a.y = y; a.h = h; a.gamma = gamma; a.u = u; a.eps = eps;
   return launched(lk::add_rmsnorm(a, (hipStream_t)stream), "add_rmsnorm");
 }
 

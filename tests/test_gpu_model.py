@@ -240,6 +240,32 @@ def test_group_9b_width_shallow(shape):
     assert err < BF16_TOL
 
 
+def test_9b_width_decode_shallow():
+    """Decode at 9B width, where the decode-shaped o and down projections split K
+    over workgroups and the following RMSNorm / mHC kernels sum the partials:
+    three plain linear layers and one looped full-attention layer, B=2, a
+    prefill of 40 positions, then three decode steps against the oracle's
+    recurrence (logits bar; the stack is shallow)."""
+    ocfg = oracle.group_config(vocab=1024, n_layers=4, loop_start=3, loop_end=4, n_passes=1)
+    model, Wo = build_pair(ocfg, cache_layers=4)
+    B, S, K = 2, 40, 3
+    toks = tokens(B, S + K, ocfg.vocab, seed=9)
+    _say("9B-width decode B=2 S=40")
+    ost = oracle.State()
+    ref = oracle.forward(ocfg, Wo, toks[:, :S], state=ost)
+    st = model.new_state(B, 128)
+    got = model.prefill(st, to_dev_tokens(toks[:, :S]))
+    err = rel(got.cpu().numpy(), ref)
+    _say("prefill (last position) rel err", err)
+    assert err < BF16_TOL
+    for k in range(K):
+        r = oracle.forward(ocfg, Wo, toks[:, S + k:S + k + 1], state=ost)
+        g = model.decode_step(st, to_dev_tokens(toks[:, S + k]))
+        err = rel(g.cpu().numpy(), r)
+        _say("decode", k, err)
+        assert err < BF16_TOL
+
+
 # ------------------------------------------------------------------ error paths
 def test_error_paths():
     L = need_gpu()
