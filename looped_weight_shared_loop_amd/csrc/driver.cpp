@@ -494,8 +494,10 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
       }
     } else {
       lk::GemmArgs g = gemm(lk::EPI_STORE, u, C, T, W.qkv, qkv_rows, C, qkv, qkv_rows);
-      LAUNCH(run_gemm(g), "qkv gemm");
+      LAUNCH(run_gemm(g, decode && S <= 16), "qkv gemm");
       lk::LinArgs a{};
+      a.qp = ypend;                    // set when the projection left partials
+      ypend = lk::YPart{};
       a.dt = dt; a.B = B; a.S_call = S; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.eps = c.la_eps;
       a.qkv = qkv; a.ld = qkv_rows;
       a.S = (float*)(st->base + st->soff[ex.slot]);

@@ -569,16 +569,34 @@ __global__ __launch_bounds__(128 * NH, 1) void lin_out_bf(LinArgs a) {
 }
 
 // ------------------------------------------------------------------ decode (recurrent)
+// One workgroup per (sequence x KV head); thread (row group rg, column jj)
+// keeps S[RPT rg .. RPT rg + RPT - 1][jj] in registers.  At decode shapes q, k
+// and v may be read straight from the QKV projection's split-K partials.
+constexpr int LDQ = 1;   // value-column groups per state (z is shared: one writer)
+
+template <typename T>
+DEV float ld_qkv(const LinArgs& a, int row, int col) {
+  if (a.qp.part) {
+    const int R = a.qp.rows, tile = col / R;
+    float v = 0.f;
+    for (int p = 0; p < a.qp.ks; ++p) v += a.qp.part[((size_t)(tile * a.qp.ks + p) * 32 + row) * R + (col - tile * R)];
+    return round_to(v, (T*)nullptr);
+  }
+  return ld1((const T*)a.qkv + (size_t)row * a.ld + col);
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void lin_decode_kernel(LinArgs a) {
-  constexpr int NRG = 256 / D;          // row groups
-  constexpr int RPT = D / NRG;          // rows per thread
-  __shared__ float fk[D], vv[D], fq[8][D], zs[D], dens[8];
-  __shared__ float red[NRG][8][D];
-  const int bh = blockIdx.x;
+  constexpr int NJ = D / LDQ;            // columns per workgroup (32 or 16)
+  constexpr int NRG = 256 / NJ;          // row groups (8 or 16)
+  constexpr int RPT = D / NRG;           // rows per thread (16 or 4)
+  __shared__ float fk[D], vv[NJ], fq[8][D], zs[D], dens[8];
+  __shared__ float red[NRG][8][NJ];
+  const int bh = blockIdx.x / LDQ, jq = blockIdx.x % LDQ;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int G = a.Hq / a.Hkv;
-  const int col = threadIdx.x % D, rg = threadIdx.x / D;
+  const int jj = threadIdx.x % NJ, rg = threadIdx.x / NJ;
+  const int col = jq * NJ + jj;
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
   float* Sg = a.S + (size_t)bh * D * D;
   float s[RPT];
@@ -586,17 +604,16 @@ __global__ __launch_bounds__(256) void lin_decode_kernel(LinArgs a) {
   for (int i = 0; i < RPT; ++i) s[i] = a.init_zero ? 0.f : Sg[(rg * RPT + i) * D + col];
   float zr = 0.f;
   if (threadIdx.x < D) zr = a.init_zero ? 0.f : a.z[(size_t)bh * D + threadIdx.x];
-  const T* base = (const T*)a.qkv;
   for (int t = 0; t < a.S_call; ++t) {
-    const T* row = base + (size_t)(b * a.S_call + t) * a.ld;
-    for (int idx = threadIdx.x; idx < (G + 2) * D; idx += 256) {
+    const int row = b * a.S_call + t;
+    for (int idx = threadIdx.x; idx < (G + 1) * D + NJ; idx += 256) {
       const int part = idx / D, i = idx % D;
-      if (part < G) fq[part][i] = phi(ld1(row + (hk * G + part) * D + i));
-      else if (part == G) fk[i] = phi(ld1(row + (a.Hq + hk) * D + i));
-      else vv[i] = ld1(row + (a.Hq + a.Hkv + hk) * D + i);
+      if (part < G) fq[part][i] = phi(ld_qkv<T>(a, row, (hk * G + part) * D + i));
+      else if (part == G) fk[i] = phi(ld_qkv<T>(a, row, (a.Hq + hk) * D + i));
+      else vv[i] = ld_qkv<T>(a, row, (a.Hq + a.Hkv + hk) * D + jq * NJ + i);
     }
     __syncthreads();
-    const float vj = vv[col];
+    const float vj = vv[jj];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) s[i] += fk[rg * RPT + i] * vj;
     if (threadIdx.x < D) { zr += fk[threadIdx.x]; zs[threadIdx.x] = zr; }
@@ -604,7 +621,7 @@ __global__ __launch_bounds__(256) void lin_decode_kernel(LinArgs a) {
       float p = 0.f;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) p += fq[g][rg * RPT + i] * s[i];
-      red[rg][g][col] = p;
+      red[rg][g][jj] = p;
     }
     __syncthreads();
     for (int g = wid; g < G; g += 4) {
@@ -614,19 +631,18 @@ __global__ __launch_bounds__(256) void lin_decode_kernel(LinArgs a) {
       if (lane == 0) dens[g] = p + a.eps;
     }
     __syncthreads();
-    T* orow = (T*)a.out + (size_t)(b * a.S_call + t) * a.ldo;
-    for (int idx = threadIdx.x; idx < G * D; idx += 256) {
-      const int g = idx / D, jj = idx % D;
+    T* orow = (T*)a.out + (size_t)row * a.ldo;
+    for (int idx = threadIdx.x; idx < G * NJ; idx += 256) {
+      const int g = idx / NJ, j = idx % NJ;
       float n = 0.f;
-#pragma unroll
-      for (int r = 0; r < NRG; ++r) n += red[r][g][jj];
-      st1(orow + (hk * G + g) * D + jj, n / dens[g]);
+      for (int r = 0; r < NRG; ++r) n += red[r][g][j];
+      st1(orow + (hk * G + g) * D + jq * NJ + j, n / dens[g]);
     }
     __syncthreads();
   }
 #pragma unroll
   for (int i = 0; i < RPT; ++i) Sg[(rg * RPT + i) * D + col] = s[i];
-  if (threadIdx.x < D) a.z[(size_t)bh * D + threadIdx.x] = zr;
+  if (jq == 0 && threadIdx.x < D) a.z[(size_t)bh * D + threadIdx.x] = zr;
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -702,7 +718,8 @@ hipError_t lin_prefill(const LinArgs& a, hipStream_t s) {
 hipError_t lin_decode(const LinArgs& a, hipStream_t s) {
   if (a.S_call <= 0 || a.B <= 0) return hipSuccess;
   if (a.Hq % a.Hkv || a.Hq / a.Hkv > 8) return hipErrorInvalidValue;
-  const int grid = a.B * a.Hkv;
+  if (a.qp.part && (a.dt != DT_BF16 || a.S_call != 1)) return hipErrorInvalidValue;
+  const int grid = a.B * a.Hkv * LDQ;
   if (a.dt == DT_BF16) {
     if (a.d == 128) lin_decode_kernel<bf16_t, 128><<<grid, 256, 0, s>>>(a);
     else if (a.d == 64) lin_decode_kernel<bf16_t, 64><<<grid, 256, 0, s>>>(a);

@@ -112,6 +112,7 @@ struct LinArgs {
   int init_zero;                   // treat the incoming state as zero
   void* out; long ldo;
   float* scratch; int chunk;       // prefill: [B*Hkv][n_chunk][d*d + d]
+  YPart qp;                        // decode: qkv still split-K partials (bf16, S_call == 1)
 };
 hipError_t lin_prefill(const LinArgs& a, hipStream_t s);
 hipError_t lin_decode(const LinArgs& a, hipStream_t s);
