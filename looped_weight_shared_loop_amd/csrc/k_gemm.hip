@@ -254,8 +254,8 @@ constexpr int SK_THREADS = 256;
 
 // Tile height: 64 rows (two waves per SIMD fit) unless the 128-row tiles alone
 // give four workgroups per CU (the head), where the wider A reuse wins.  K is
-// split in powers of two while the grid has fewer than two workgroups per CU
-// and each wave keeps at least 256 of K.
+// split in powers of two (at most 16) while the grid has fewer than two
+// workgroups per CU and each wave keeps at least 256 of K.
 SkinnyPlan skinny_plan(int epi, int N, int K, int F, int cu) {
   SkinnyPlan p{};
   auto tiles_of = [&](int rb) {
@@ -265,7 +265,8 @@ SkinnyPlan skinny_plan(int epi, int N, int K, int F, int cu) {
   p.rb = (long)tiles_of(4) >= 4L * cu ? 4 : 2;
   p.tiles = tiles_of(p.rb);
   p.ksplit = 1;
-  while ((long)p.tiles * p.ksplit < 2L * cu && K % (p.ksplit * 2 * 4 * 64) == 0 && K / (p.ksplit * 2 * 4) >= 256)
+  while (p.ksplit < 16 && (long)p.tiles * p.ksplit < 2L * cu && K % (p.ksplit * 2 * 4 * 64) == 0 &&
+         K / (p.ksplit * 2 * 4) >= 256)
     p.ksplit *= 2;
   if (p.ksplit > 1) p.bytes = (size_t)p.tiles * p.ksplit * 32 * 32 * p.rb * sizeof(float);
   return p;

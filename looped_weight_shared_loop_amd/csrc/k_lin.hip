@@ -578,8 +578,15 @@ template <typename T>
 DEV float ld_qkv(const LinArgs& a, int row, int col) {
   if (a.qp.part) {
     const int R = a.qp.rows, tile = col / R;
+    constexpr int KSMAX = 16;   // loads first, then the sum in index order
+    float x[KSMAX];
+#pragma unroll
+    for (int p = 0; p < KSMAX; ++p)
+      if (p < a.qp.ks) x[p] = a.qp.part[((size_t)(tile * a.qp.ks + p) * 32 + row) * R + (col - tile * R)];
     float v = 0.f;
-    for (int p = 0; p < a.qp.ks; ++p) v += a.qp.part[((size_t)(tile * a.qp.ks + p) * 32 + row) * R + (col - tile * R)];
+#pragma unroll
+    for (int p = 0; p < KSMAX; ++p)
+      if (p < a.qp.ks) v += x[p];
     return round_to(v, (T*)nullptr);
   }
   return ld1((const T*)a.qkv + (size_t)row * a.ld + col);
@@ -718,7 +725,7 @@ hipError_t lin_prefill(const LinArgs& a, hipStream_t s) {
 hipError_t lin_decode(const LinArgs& a, hipStream_t s) {
   if (a.S_call <= 0 || a.B <= 0) return hipSuccess;
   if (a.Hq % a.Hkv || a.Hq / a.Hkv > 8) return hipErrorInvalidValue;
-  if (a.qp.part && (a.dt != DT_BF16 || a.S_call != 1)) return hipErrorInvalidValue;
+  if (a.qp.part && (a.dt != DT_BF16 || a.S_call != 1 || a.qp.ks > 16)) return hipErrorInvalidValue;
   const int grid = a.B * a.Hkv * LDQ;
   if (a.dt == DT_BF16) {
     if (a.d == 128) lin_decode_kernel<bf16_t, 128><<<grid, 256, 0, s>>>(a);

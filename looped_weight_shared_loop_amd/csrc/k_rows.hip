@@ -65,11 +65,23 @@ DEV void ld8_y(const T* y, const YPart& yp, int t, int C, int c0, float* v) {
     const int R = yp.rows, tile = c0 / R, j = c0 - tile * R;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    for (int p = 0; p < yp.ks; ++p) {
-      const float4* q = reinterpret_cast<const float4*>(yp.part + ((size_t)(tile * yp.ks + p) * 32 + t) * R + j);
-      const float4 lo = q[0], hi = q[1];
-      v[0] += lo.x; v[1] += lo.y; v[2] += lo.z; v[3] += lo.w;
-      v[4] += hi.x; v[5] += hi.y; v[6] += hi.z; v[7] += hi.w;
+    // partial loads issued four at a time ahead of their sums (index order kept)
+    constexpr int PG = 4;
+    for (int p0 = 0; p0 < yp.ks; p0 += PG) {
+      float4 lo[PG], hi[PG];
+#pragma unroll
+      for (int p = 0; p < PG; ++p)
+        if (p0 + p < yp.ks) {
+          const float4* q = reinterpret_cast<const float4*>(yp.part + ((size_t)(tile * yp.ks + p0 + p) * 32 + t) * R + j);
+          lo[p] = q[0];
+          hi[p] = q[1];
+        }
+#pragma unroll
+      for (int p = 0; p < PG; ++p)
+        if (p0 + p < yp.ks) {
+          v[0] += lo[p].x; v[1] += lo[p].y; v[2] += lo[p].z; v[3] += lo[p].w;
+          v[4] += hi[p].x; v[5] += hi[p].y; v[6] += hi[p].z; v[7] += hi[p].w;
+        }
     }
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = round_to(v[e], (T*)nullptr);
