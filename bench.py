@@ -126,6 +126,30 @@ def time_prefill(L, torch, model, S, steps, warmup):
     return ms
 
 
+def time_long_prefill(L, torch, model, S_long, chunk):
+    """Chunked prefill of one sequence of S_long positions in chunks of `chunk`
+    (LOOP_CONTINUE), every chunk through all 56 executions; one timed pass."""
+    import synth
+    from synth import device as sd
+    st = model.new_state(1, S_long)
+    toks = torch.empty(1, S_long, dtype=torch.int32, device="cuda")
+    sd.fill_tensor_uniform_int(toks, 1, synth.TID_TOKENS + 200, model.cfg.vocab)
+    model.workspace(1, chunk, S_long)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for c in range(S_long // chunk):
+        out = model.prefill(st, toks[:, c * chunk:(c + 1) * chunk], cont=c > 0)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    st.check()
+    assert torch.isfinite(out).all().item()
+    log(f"chunked prefill S={S_long} (chunks of {chunk}): {ms:.1f} ms")
+    st.close()
+    return ms
+
+
 def time_dominant_gemm(L, torch, S, iters=10):
     """The SwiGLU gate/up projection at the prefill shape: M = 32768 tokens,
     N = 2 x 12288 weight rows, K = 4096 (the largest GEMM, 44% of the FLOPs)."""
@@ -241,6 +265,9 @@ def main():
     ap.add_argument("--decode-ctx", type=int, default=32768)
     ap.add_argument("--decode-steps", type=int, default=16)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--long-seq", type=int, default=262144,
+                    help="one chunked prefill of this many positions (0: skip)")
+    ap.add_argument("--long-chunk", type=int, default=32768)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seq", type=int, default=1536)
     ap.add_argument("--profile-dominant", action="store_true",
@@ -303,6 +330,14 @@ def main():
                             "batch": args.decode_batch, "context": args.decode_ctx,
                             "algorithmic_gb_per_step": round(tot / 1e9, 2), "achieved_gbs": round(gbs, 1),
                             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if args.long_seq > 0:
+        lms = time_long_prefill(L, torch, model, args.long_seq, args.long_chunk)
+        lf, lg, la, ll = prefill_flops(NINE_B, args.long_seq)
+        result["prefill_long"] = {"seq_len": args.long_seq, "chunk": args.long_chunk, "ms": round(lms, 1),
+                                  "tokens_per_s": round(args.long_seq / (lms / 1e3), 1),
+                                  "tflops": round(lf / (lms / 1e3) / 1e12, 1),
+                                  "mfma_frac": round(lf / (lms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                                  "algorithmic_tflop": round(lf / 1e12, 1), "attention_tflop": round(la / 1e12, 1)}
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seq)
     print(json.dumps(result), flush=True)

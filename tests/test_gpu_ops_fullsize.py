@@ -179,6 +179,42 @@ def test_full_attention_prefill_full_size_sampled():
         assert err < 2e-2
 
 
+def test_full_attention_chunk_continuation_sampled():
+    """A prefill chunk that continues a long cache (chunked prefill): 700 new
+    positions at pos0 = 30000 (not a tile multiple) over S_max = 30720, B=2."""
+    need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    from synth import device as sd
+    B, pos0, S = 2, 30000, 700
+    L = pos0 + S
+    Smax = (L + 63) // 64 * 64
+    q = _dev_normal((B * S, QKV), 34)
+    kc = torch.empty(B, HKV, Smax, D, dtype=torch.bfloat16, device="cuda")
+    vt = torch.empty(B, HKV, D, Smax, dtype=torch.bfloat16, device="cuda")
+    sd.fill_tensor_normal(kc, SEED, 99, 1.0)          # arbitrary values past the end
+    sd.fill_tensor_normal(vt, SEED, 98, 1.0)
+    sd.fill_normal4(kc.data_ptr(), True, (B, HKV, L, D), (HKV * Smax * D, Smax * D, D, 1), SEED, 35, 1.0,
+                    stream=_stream())
+    sd.fill_normal4(vt.data_ptr(), True, (B, HKV, L, D), (HKV * D * Smax, D * Smax, 1, Smax), SEED, 36, 1.0,
+                    stream=_stream())
+    out = torch.empty(B * S, HQ * D, dtype=torch.bfloat16, device="cuda")
+    A.loop_op_attention(A.LOOP_BF16, B, S, pos0, Smax, HQ, HKV, D, q.data_ptr(), QKV, kc.data_ptr(), vt.data_ptr(),
+                        out.data_ptr(), HQ * D, _stream())
+    torch.cuda.synchronize()
+    for b, t, head in [(0, 0, 0), (0, 63, 7), (1, 64, 12), (1, 699, 31), (0, 350, 20)]:
+        kvh = head // (HQ // HKV)
+        row = b * S + t
+        qr = synth.normal_bf16_as_f32(SEED, 34, (QKV,), start=row * QKV)[head * D:(head + 1) * D]
+        base = ((b * HKV + kvh) * L) * D
+        K = synth.normal_bf16_as_f32(SEED, 35, (pos0 + t + 1, D), start=base)
+        Vv = synth.normal_bf16_as_f32(SEED, 36, (pos0 + t + 1, D), start=base)
+        ref = M.full_attention(qr[None, None, None, :], K[None, :, None, :], Vv[None, :, None, :], pos0 + t)[0, 0, 0]
+        got = out[row, head * D:(head + 1) * D].float().cpu().numpy()
+        err = np.abs(got - ref).max() / np.abs(ref).max()
+        print("attn chunk", b, t, head, err, flush=True)
+        assert err < 2e-2
+
+
 @pytest.mark.parametrize("B,ctx,samples", [
     (32, 32768, [(0, 0), (7, 9), (31, 31), (16, 4)]),     # one split per (sequence, KV head)
     (2, 5001, [(0, 0), (1, 13), (1, 31)]),                # several splits, ragged last split
