@@ -113,8 +113,10 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
   const int krow = (col & 0x13) | ((col & 4) << 1) | ((col & 8) >> 1);
 
   static_assert(AQ_NS == 4 && NW == 8 && NB == 2, "wait counts below");
-  f32x16_t st[2];
-  auto scores = [&](int kt) {
+  // Software pipeline: the score MFMAs of tile kt + 1 are issued before the
+  // softmax and PV of tile kt, so the softmax VALU work runs while they execute.
+  f32x16_t sa[2], sb[2];                     // scores of the current / next tile
+  auto scores = [&](int kt, f32x16_t (&st)[2]) {
     const bf16_t* ks = smem + (kt % AQ_NS) * AQ_STAGE;
 #pragma unroll
     for (int c = 0; c < 2; ++c)
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
         st[c] = mfma32(kf, qf[ds], st[c]);
       }
   };
-  auto softmax_pv = [&](int kt) {
+  auto softmax_pv = [&](int kt, f32x16_t (&st)[2]) {
     const bf16_t* vs = smem + (kt % AQ_NS) * AQ_STAGE + PK * PD;
     // st[c][r]: key kt*64 + 32c + 16(r/8) + 8h + r%8, query column `col`
     const bool diag = kt * PK + PK - 1 > a.pos0 + q0;
@@ -186,32 +188,45 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
       }
     }
   };
-  for (int t = 0; t < AHEAD; ++t) issue(t);
-  for (int kt = 0; kt < ntiles; ++kt) {
-    // tile kt may leave the two later tiles (4 loads per wave each) in flight
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    sync();
-    issue(kt + AHEAD);   // into the stage read in iteration kt - 1, finished before the barrier
-    if (kt == ntiles - 1 && kv_end % PK) {
-      // keys kv_end .. of the last tile hold arbitrary bits: clear V^T there
-      // (their probabilities are 0, but 0 * NaN would not be)
-      bf16_t* vs = smem + (kt % AQ_NS) * AQ_STAGE + PK * PD;
-      const int lim = kv_end - kt * PK;
-      for (int idx = tid; idx < PD * 8; idx += 64 * NW) {
-        const int r = idx >> 3, u = idx & 7;
-        if (8 * u + 8 > lim) {
-          bf16_t* p = vs + vq_sw(r, u);
+  // keys kv_end .. of the last tile hold arbitrary bits: clear V^T there once
+  // the tile has landed, before any PV reads it (probabilities there are 0,
+  // but 0 * NaN would not be)
+  auto mask_tail = [&]() {
+    const int kt = ntiles - 1;
+    bf16_t* vs = smem + (kt % AQ_NS) * AQ_STAGE + PK * PD;
+    const int lim = kv_end - kt * PK;
+    for (int idx = tid; idx < PD * 8; idx += 64 * NW) {
+      const int r = idx >> 3, u = idx & 7;
+      if (8 * u + 8 > lim) {
+        bf16_t* p = vs + vq_sw(r, u);
 #pragma unroll
-          for (int e = 0; e < 8; ++e)
-            if (8 * u + e >= lim) p[e] = 0;
-        }
+        for (int e = 0; e < 8; ++e)
+          if (8 * u + e >= lim) p[e] = 0;
       }
-      sync();
     }
-    if (kt * PK <= wave_last) {
-      scores(kt);
-      softmax_pv(kt);
-    }
+  };
+  const bool ragged = kv_end % PK != 0;
+  for (int t = 0; t < AHEAD; ++t) issue(t);
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");    // tile 0 (4 loads) landed, tiles 1, 2 in flight
+  sync();
+  if (ntiles == 1 && ragged) { mask_tail(); sync(); }
+  scores(0, sa);
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    // even step: scores of kt + 1 into sb, softmax / PV of kt from sa
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // tile kt + 1 landed (tile kt + 2 may be in flight)
+    sync();
+    issue(kt + AHEAD);                       // into the stage of tile kt - 1, finished before this barrier
+    if (kt + 1 == ntiles - 1 && ragged) mask_tail();   // ordered before its PV by the next barrier
+    if ((kt + 1) * PK <= wave_last) scores(kt + 1, sb);   // wave-uniform: tiles past the
+    if (kt * PK <= wave_last) softmax_pv(kt, sa);           // wave's last query are skipped
+    if (kt + 1 >= ntiles) break;
+    // odd step: scores of kt + 2 into sa, softmax / PV of kt + 1 from sb
+    asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    sync();
+    issue(kt + 1 + AHEAD);
+    if (kt + 2 == ntiles - 1 && ragged) mask_tail();
+    if ((kt + 2) * PK <= wave_last) scores(kt + 2, sa);
+    if ((kt + 1) * PK <= wave_last) softmax_pv(kt + 1, sb);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
   if (qvalid) {
