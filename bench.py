@@ -228,6 +228,86 @@ def time_decode(L, torch, model, B, ctx, steps, warmup):
     return ms
 
 
+# one 9B-width group [linear x3, full] looped twice (8 executions); no embed or head
+GROUP = dict(NINE_B, vocab=1024, n_layers=4, loop_start=0, loop_end=4)
+MHC_BYTES_PER_TOKEN = 49184    # read X (2C), y (C); write X' (2C), u (C): bf16, C = 4096; + maps
+
+
+def time_mhc_isolated(torch, T=65536, iters=10):
+    """The mHC site kernel alone (mid-loop form) over T tokens of two 4096-wide
+    bf16 streams: read X and the sublayer output y, write X' = H_res X +
+    H_post y and u = RMSNorm(H_pre' X'), with the next site's maps from the
+    projection and 20 Sinkhorn iterations.  The incoming maps are synthetic
+    values in [0, 1) (they do not change the traffic)."""
+    import synth
+    from synth import device as sd
+    from looped_weight_shared_loop_amd import _abi as A
+    C = NINE_B["hidden"]
+    X = torch.empty(T, 2, C, dtype=torch.bfloat16, device="cuda")
+    y = torch.empty(T, C, dtype=torch.bfloat16, device="cuda")
+    u = torch.empty(T, C, dtype=torch.bfloat16, device="cuda")
+    w = torch.empty(8, 2 * C, dtype=torch.float32, device="cuda")
+    b = torch.empty(8, dtype=torch.float32, device="cuda")
+    sd.fill_tensor_normal(X, 4, 1, 1.0)
+    sd.fill_tensor_normal(y, 4, 2, 1.0)
+    sd.fill_tensor_normal(w, 4, 3, 0.02)
+    sd.fill_tensor_normal(b, 4, 4, 0.02)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(4)
+    maps_in = torch.rand(T, 8, device="cuda", generator=gen)
+    maps_out = torch.empty(T, 8, dtype=torch.float32, device="cuda")
+    gamma = torch.ones(C, dtype=torch.float32, device="cuda")
+    nb = A.loop_op_mhc_bytes(C)
+    scr = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    f = lambda: A.loop_op_mhc(A.LOOP_BF16, A.LOOP_MHC_MID, T, C, 20, 1e-6, y.data_ptr(), None, X.data_ptr(),
+                              maps_in.data_ptr(), maps_out.data_ptr(), w.data_ptr(), b.data_ptr(), gamma.data_ptr(),
+                              u.data_ptr(), scr.data_ptr(), nb, stream)
+    for _ in range(2):
+        f()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        f()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    assert torch.isfinite(maps_out).all().item()
+    log(f"mHC isolated T={T}: {ms:.3f} ms")
+    del X, y, u
+    return ms
+
+
+def time_group(L, torch, S=8192, iters=3):
+    """One 9B-width group [lin, lin, lin, full] looped twice under two-stream
+    mHC (8 executions), B=1, S=8192, inputs h ~ N(0, 1) passed as embeddings,
+    final hidden states returned (no embedding lookup, no head)."""
+    import synth
+    from synth import device as sd
+    cfg = L.ModelConfig(**GROUP)
+    model = L.LoopModel(cfg, L.random_weights(cfg, 0))
+    st = model.new_state(1, S)
+    emb = torch.empty(1, S, cfg.hidden, dtype=torch.bfloat16, device="cuda")
+    sd.fill_tensor_normal(emb, 1, synth.TID_EMBEDS_IN, 1.0)
+    model.workspace(1, S, S)
+    out = model.prefill(st, embeds=emb, hidden_out=True)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        out = model.prefill(st, embeds=emb, hidden_out=True)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / iters
+    st.check()
+    assert torch.isfinite(out).all().item()
+    log(f"group x2 S={S}: {ms:.2f} ms")
+    st.close()
+    model.close()
+    return ms
+
+
 def cpu_baseline(seq=128):
     """The oracle as it stands, on host cores, on a bounded sample: one 4-layer
     group [linear x3, full] at full 9B width looped twice (8 of the 56 layer
@@ -269,6 +349,8 @@ def main():
                     help="one chunked prefill of this many positions (0: skip)")
     ap.add_argument("--long-chunk", type=int, default=32768)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-parts", action="store_true",
+                    help="skip the mHC-isolated and one-group measurements")
     ap.add_argument("--cpu-seq", type=int, default=1536)
     ap.add_argument("--profile-dominant", action="store_true",
                     help="only a 1 GiB device copy (counter scale reference) and 3 launches of the dominant kernel")
@@ -338,6 +420,20 @@ def main():
                                   "tflops": round(lf / (lms / 1e3) / 1e12, 1),
                                   "mfma_frac": round(lf / (lms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
                                   "algorithmic_tflop": round(lf / 1e12, 1), "attention_tflop": round(la / 1e12, 1)}
+    if not args.no_parts:
+        mms = time_mhc_isolated(torch)
+        mgb = 65536 * MHC_BYTES_PER_TOKEN / (mms / 1e3) / 1e9
+        result["mhc_isolated"] = {"tokens": 65536, "ms": round(mms, 4), "algorithmic_gb": round(65536 * MHC_BYTES_PER_TOKEN / 1e9, 3),
+                                  "achieved_gbs": round(mgb, 1), "hbm_frac": round(mgb / PEAK_HBM_GBS, 4)}
+        del model
+        torch.cuda.empty_cache()
+        gms = time_group(L, torch)
+        _, gg, ga, gl = prefill_flops(GROUP, 8192)
+        gf = gg + ga + gl
+        result["group_x2"] = {"seq_len": 8192, "ms": round(gms, 3), "tokens_per_s": round(8192 / (gms / 1e3), 1),
+                              "algorithmic_tflop": round(gf / 1e12, 2),
+                              "tflops": round(gf / (gms / 1e3) / 1e12, 1),
+                              "mfma_frac": round(gf / (gms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seq)
     print(json.dumps(result), flush=True)

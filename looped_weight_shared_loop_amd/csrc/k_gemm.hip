@@ -304,7 +304,7 @@ DEV void sk_epilogue(const GemmArgs& a, int tile, int m, int j, float v, float v
   }
 }
 
-template <int EPI, int RB>
+template <int EPI, int RB, int D>
 __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_kernel(GemmArgs a) {
   constexpr int R = 32 * RB;
   __shared__ float red[2][32][R + 1];      // [slot][token][tile row]
@@ -335,17 +335,22 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_kernel(GemmArgs a) {
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
-  // two register sets: loads for step k + 64 are in flight during step k's MFMAs
-  u32x4_t bw0[RB][4], xw0[4], bw1[RB][4], xw1[4];
-  sk_load<RB>(Bp, Ap, tok_ok, 0, bw0, xw0);
-  int k = 0;
-  for (; k + 128 <= Kw; k += 128) {
-    sk_load<RB>(Bp, Ap, tok_ok, k + 64, bw1, xw1);
-    sk_mma<RB>(bw0, xw0, acc);
-    if (k + 128 < Kw) sk_load<RB>(Bp, Ap, tok_ok, k + 128, bw0, xw0);
-    sk_mma<RB>(bw1, xw1, acc);
+  // D register sets: the loads of the next D steps of 64 are in flight while a
+  // step's MFMAs run.  The launch guarantees Kw / 64 is a positive multiple of
+  // D, so the steady loop refills every set unconditionally and the last D
+  // steps drain without loads (no branch inside the pipeline).
+  u32x4_t bw[D][RB][4], xw[D][4];
+#pragma unroll
+  for (int d = 0; d < D; ++d) sk_load<RB>(Bp, Ap, tok_ok, d * 64, bw[d], xw[d]);
+  for (int k = 0; k + D * 64 < Kw; k += D * 64) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      sk_mma<RB>(bw[d], xw[d], acc);
+      sk_load<RB>(Bp, Ap, tok_ok, k + (D + d) * 64, bw[d], xw[d]);
+    }
   }
-  if (k < Kw) sk_mma<RB>(bw0, xw0, acc);
+#pragma unroll
+  for (int d = 0; d < D; ++d) sk_mma<RB>(bw[d], xw[d], acc);
 
   // acc[rb][i]: tile row rb*32 + (i/4)*8 + h*4 + i%4, token r.  Sum the waves
   // as (w0 + w2) + (w1 + w3).
@@ -412,7 +417,15 @@ template <int EPI, int RB>
 static hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
   constexpr int R = 32 * RB;
   const int tiles = (EPI == EPI_SWIGLU) ? (a.F + R / 2 - 1) / (R / 2) : (a.N + R - 1) / R;
-  gemm_skinny_kernel<EPI, RB><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
+  // steps of 64 per wave (K % (ksplit * 4 * 64) == 0 is checked by the caller)
+  const int steps = a.K / (a.ksplit * 4 * 64);
+  constexpr int DEEP = RB == 2 ? 4 : 2;   // four steps in flight fit the registers only at RB = 2
+  if (steps % DEEP == 0)
+    gemm_skinny_kernel<EPI, RB, DEEP><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
+  else if (steps % 2 == 0)
+    gemm_skinny_kernel<EPI, RB, 2><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
+  else
+    gemm_skinny_kernel<EPI, RB, 1><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
   if (a.ksplit > 1 && !(a.defer_reduce && EPI == EPI_STORE)) {
     const long outs = (long)a.M * tiles * (EPI == EPI_SWIGLU ? R / 2 : R);
     gemm_skinny_reduce<EPI, RB><<<(int)((outs + 255) / 256), 256, 0, s>>>(a);

@@ -504,9 +504,20 @@ hipError_t mhc(const MhcArgs& a, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int ntiles = (a.T + 15) / 16;
+    // Persistent grid: exactly the resident workgroups (a second wave of
+    // workgroups would start only after the first finished its tiles), then
+    // shrunk so that every workgroup gets the same number of tiles.
+    static int per_cu = 0;
+    if (per_cu == 0) {
+      int n = 0;
+      if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, mhc_mfma_kernel, 512, 0) != hipSuccess || n < 1) n = 1;
+      per_cu = n;
+    }
     const int cu = device_cu_count();
-    int grid = 3 * (cu > 0 ? cu : 256);
+    int grid = per_cu * (cu > 0 ? cu : 256);
     if (grid > ntiles) grid = ntiles;
+    const int per_wg = (ntiles + grid - 1) / grid;
+    grid = (ntiles + per_wg - 1) / per_wg;
     mhc_mfma_kernel<<<grid, 512, 0, s>>>(a, a.wsplit);
     return hipGetLastError();
   }

@@ -128,6 +128,48 @@ def test_tiny_fp32_hidden_out_with_embeds():
     assert rel(got.cpu().numpy(), ref) < FP32_TOL
 
 
+@pytest.mark.parametrize("passes,loop", [(1, (2, 6)), (3, (2, 6)), (4, (1, 5)), (3, (0, 8))])
+def test_tiny_fp32_pass_count_and_loop_range(passes, loop):
+    """The pass count and the loop range are execution-config fields: P = 1, 3
+    and 4 and other ranges match the oracle for prefill and the decode steps
+    after it (each (layer, pass) keeps its own KV cache or linear state)."""
+    ocfg = oracle.tiny_config(n_kv_heads=2, n_passes=passes, loop_start=loop[0], loop_end=loop[1])
+    model, Wo = build_pair(ocfg)
+    B, S, K = 2, 48, 2
+    toks = tokens(B, S + K, ocfg.vocab, seed=11 + passes)
+    _say("tiny fp32 passes", passes, "loop", loop)
+    full = oracle.forward(ocfg, Wo, toks, all_logits=True)
+    st = model.new_state(B, S + K)
+    got = model.prefill(st, to_dev_tokens(toks[:, :S]), all_logits=True)
+    assert rel(got.cpu().numpy(), full[:, :S]) < FP32_TOL
+    for k in range(K):
+        d = model.decode_step(st, to_dev_tokens(toks[:, S + k]))
+        assert rel(d.cpu().numpy(), full[:, S + k]) < FP32_TOL
+    n_exec = ocfg.loop_start + passes * (ocfg.loop_end - ocfg.loop_start) + ocfg.n_layers - ocfg.loop_end
+    assert len(model.schedule()) == n_exec
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_multi_token_verify_block(dtype):
+    """A block of k new tokens per sequence appended to a state (causal inside
+    the block, all rows' logits), as a speculative verify step would issue it,
+    equals the one-shot forward's rows; decoding then continues after it."""
+    ocfg = oracle.tiny_config(n_kv_heads=2) if dtype == "fp32" else mini_bf16_config()
+    tol = FP32_TOL if dtype == "fp32" else BF16_TOL
+    model, Wo = build_pair(ocfg)
+    B, S, k = 2, 40, 4
+    toks = tokens(B, S + k + 1, ocfg.vocab, seed=21)
+    _say("verify block", dtype, "S", S, "k", k)
+    full = oracle.forward(ocfg, Wo, toks, all_logits=True)
+    st = model.new_state(B, 64)
+    model.prefill(st, to_dev_tokens(toks[:, :S]))
+    blk = model.prefill(st, to_dev_tokens(toks[:, S:S + k]), all_logits=True, cont=True)
+    assert rel(blk.cpu().numpy(), full[:, S:S + k]) < tol
+    assert st.length == S + k
+    d = model.decode_step(st, to_dev_tokens(toks[:, S + k]))
+    assert rel(d.cpu().numpy(), full[:, S + k]) < tol
+
+
 # ------------------------------------------------------------------ bf16 (MFMA kernels)
 def test_mini_bf16_prefill_decode():
     ocfg = mini_bf16_config()
