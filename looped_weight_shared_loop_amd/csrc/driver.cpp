@@ -102,13 +102,15 @@ WsLayout ws_layout(const loop_model* m, int batch, int max_tokens, int max_seq) 
   w.wsplit = take((size_t)16 * 2 * C * sizeof(uint16_t));
   // split-K scratch of the decode-shaped GEMMs (the largest plan of the five projections)
   size_t sk = 0;
-  if (c.dtype == LOOP_BF16 && max_tokens <= 32) {
+  if (c.dtype == LOOP_BF16 && max_tokens <= 64) {
+    // the plan's partial size only grows with the token count (one or two blocks of 32)
+    const int M = max_tokens;
     const lk::SkinnyPlan p[5] = {
-        lk::skinny_plan(lk::EPI_QKV, m->qkv_rows(), C, 0, m->cu),
-        lk::skinny_plan(lk::EPI_STORE, C, c.n_heads * c.head_dim, 0, m->cu),
-        lk::skinny_plan(lk::EPI_SWIGLU, 2 * c.ffn, C, c.ffn, m->cu),
-        lk::skinny_plan(lk::EPI_STORE, C, c.ffn, 0, m->cu),
-        lk::skinny_plan(lk::EPI_F32, c.vocab, C, 0, m->cu)};
+        lk::skinny_plan(lk::EPI_QKV, M, m->qkv_rows(), C, 0, m->cu),
+        lk::skinny_plan(lk::EPI_STORE, M, C, c.n_heads * c.head_dim, 0, m->cu),
+        lk::skinny_plan(lk::EPI_SWIGLU, M, 2 * c.ffn, C, c.ffn, m->cu),
+        lk::skinny_plan(lk::EPI_STORE, M, C, c.ffn, 0, m->cu),
+        lk::skinny_plan(lk::EPI_F32, M, c.vocab, C, 0, m->cu)};
     for (const auto& q : p) sk = std::max(sk, q.bytes);
   }
   w.skinny = take(sk);
@@ -439,15 +441,15 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
   auto run_gemm = [&](lk::GemmArgs g, bool may_defer = false) {
     g.ksplit = 1;
     g.skinny_rb = 4;
-    if (g.dt == lk::DT_BF16 && g.M <= 32) {
-      const lk::SkinnyPlan p = lk::skinny_plan(g.epi, g.N, g.K, g.F, m->cu);
+    if (g.dt == lk::DT_BF16 && g.M <= 64) {
+      const lk::SkinnyPlan p = lk::skinny_plan(g.epi, g.M, g.N, g.K, g.F, m->cu);
       g.skinny_rb = p.rb;
       if (p.ksplit > 1 && p.bytes <= L.skinny_bytes) {
         g.ksplit = p.ksplit;
         g.part = (float*)(ws + L.skinny);
         if (may_defer && g.epi == lk::EPI_STORE) {
           g.defer_reduce = 1;
-          ypend = lk::YPart{g.part, p.ksplit, 32 * p.rb};
+          ypend = lk::YPart{g.part, p.ksplit, 32 * p.rb, 32 * p.tb};
         }
       }
     }

@@ -1,10 +1,10 @@
 // Dense contractions of the looped decoder: C[M, N] = A[M, K] . B[N, K]^T.
 //
-// * gemm_dma:    bf16, M > 32.  256x256 workgroup tile, 8 waves of 128x64
+// * gemm_dma:    bf16, M > 64.  256x256 workgroup tile, 8 waves of 128x64
 //                (v_mfma_f32_32x32x16_bf16), global -> LDS DMA through five
 //                LDS stages, XCD-aware tile order.  fp32 accumulation.
-// * gemm_skinny: bf16, M <= 32 (decode): streams B (the weights) once; 64- or
-//                128-row tiles, K split over 4 waves and, when the tiles cannot fill
+// * gemm_skinny: bf16, M <= 64 (decode): streams B (the weights) once for up to
+//                64 token rows; 64- or 128-row tiles, K split over 4 waves and, when the tiles cannot fill
 //                the device, over workgroups (partials summed in index order
 //                by a second kernel).
 // * gemm_f32:    fp32 configuration: LDS-tiled FMA kernel.
@@ -236,12 +236,14 @@ __global__ __launch_bounds__(128 * WN_, 1) void gemm_dma_kernel(GemmArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ skinny (M <= 32)
-// Decode shape: the weights B are streamed once, the <= 32 activation rows are
-// the MFMA's other operand.  A workgroup owns a tile of R = 32 RB B rows
-// (SwiGLU: R/2 gate rows and the R/2 matching up rows) and 1/ksplit of K; its
-// 4 waves split that K range again.  Wave operands for v_mfma_f32_32x32x16_bf16: A = B rows
-// (lane l: row l & 31), B = tokens (lane l: token l & 31).  Per 64-wide k step
+// ------------------------------------------------------------------ skinny (M <= 64)
+// Decode shape: the weights B are streamed once, the <= 64 activation rows
+// (one or two blocks of 32 tokens) are the MFMA's other operand.  A workgroup
+// owns a tile of R = 32 RB B rows (SwiGLU: R/2 gate rows and the R/2 matching
+// up rows) and 1/ksplit of K; its 4 waves split that K range again.  Wave
+// operands for v_mfma_f32_32x32x16_bf16: A = B rows (lane l: row l & 31),
+// B = tokens (lane l: token l & 31 of each block); every weight fragment
+// loaded feeds both token blocks.  Per 64-wide k step
 // lane half h = l >> 5 loads 64 contiguous bytes (k + 32 h .. k + 32 h + 31) of
 // its row, so each row's 128 B line is fetched whole; MFMA j contracts chunk j
 // of both halves, and both operands use the same k order, which leaves the
@@ -256,40 +258,45 @@ constexpr int SK_THREADS = 256;
 // give four workgroups per CU (the head), where the wider A reuse wins.  K is
 // split in powers of two (at most 16) while the grid has fewer than two
 // workgroups per CU and each wave keeps at least 256 of K.
-SkinnyPlan skinny_plan(int epi, int N, int K, int F, int cu) {
+SkinnyPlan skinny_plan(int epi, int M, int N, int K, int F, int cu) {
   SkinnyPlan p{};
   auto tiles_of = [&](int rb) {
     const int rows = 32 * rb;
     return (epi == EPI_SWIGLU) ? (F + rows / 2 - 1) / (rows / 2) : (N + rows - 1) / rows;
   };
-  p.rb = (long)tiles_of(4) >= 4L * cu ? 4 : 2;
+  p.tb = M > 32 ? 2 : 1;
+  p.rb = (p.tb == 1 && (long)tiles_of(4) >= 4L * cu) ? 4 : 2;
   p.tiles = tiles_of(p.rb);
   p.ksplit = 1;
   while (p.ksplit < 16 && (long)p.tiles * p.ksplit < 2L * cu && K % (p.ksplit * 2 * 4 * 64) == 0 &&
          K / (p.ksplit * 2 * 4) >= 256)
     p.ksplit *= 2;
-  if (p.ksplit > 1) p.bytes = (size_t)p.tiles * p.ksplit * 32 * 32 * p.rb * sizeof(float);
+  if (p.ksplit > 1) p.bytes = (size_t)p.tiles * p.ksplit * 32 * p.tb * 32 * p.rb * sizeof(float);
   return p;
 }
 
-template <int RB>
-DEV void sk_load(const bf16_t* const* Bp, const bf16_t* Ap, bool tok_ok, int k, u32x4_t (&bw)[RB][4],
-                 u32x4_t (&xw)[4]) {
+template <int RB, int TB>
+DEV void sk_load(const bf16_t* const* Bp, const bf16_t* const* Ap, const bool* tok_ok, int k, u32x4_t (&bw)[RB][4],
+                 u32x4_t (&xw)[TB][4]) {
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
     for (int j = 0; j < 4; ++j) bw[rb][j] = ldv4(Bp[rb] + k + j * 8);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) xw[j] = tok_ok ? ldv4(Ap + k + j * 8) : zero;
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xw[tb][j] = tok_ok[tb] ? ldv4(Ap[tb] + k + j * 8) : zero;
 }
 
-template <int RB>
-DEV void sk_mma(const u32x4_t (&bw)[RB][4], const u32x4_t (&xw)[4], f32x16_t (&acc)[RB]) {
+template <int RB, int TB>
+DEV void sk_mma(const u32x4_t (&bw)[RB][4], const u32x4_t (&xw)[TB][4], f32x16_t (&acc)[TB][RB]) {
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[rb] = mfma32(as_bf16x8(bw[rb][j]), as_bf16x8(xw[j]), acc[rb]);
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int tb = 0; tb < TB; ++tb) acc[tb][rb] = mfma32(as_bf16x8(bw[rb][j]), as_bf16x8(xw[tb][j]), acc[tb][rb]);
 }
 
 template <int EPI, int RB>
@@ -304,10 +311,10 @@ DEV void sk_epilogue(const GemmArgs& a, int tile, int m, int j, float v, float v
   }
 }
 
-template <int EPI, int RB, int D>
+template <int EPI, int RB, int D, int TB>
 __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_kernel(GemmArgs a) {
-  constexpr int R = 32 * RB;
-  __shared__ float red[2][32][R + 1];      // [slot][token][tile row]
+  constexpr int R = 32 * RB, TOK = 32 * TB;
+  __shared__ float red[2][TOK][R + 1];     // [slot][token][tile row]
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int ks = a.ksplit;
   const int tile = blockIdx.x / ks, kpart = blockIdx.x - tile * ks;
@@ -327,44 +334,56 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_kernel(GemmArgs a) {
     }
     Bp[rb] = (const bf16_t*)a.B + (size_t)n * a.ldb + kbeg;
   }
-  const bool tok_ok = r < a.M;
-  const bf16_t* Ap = (const bf16_t*)a.A + (size_t)(tok_ok ? r : 0) * a.lda + kbeg;
+  bool tok_ok[TB];
+  const bf16_t* Ap[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb) {
+    const int t = tb * 32 + r;
+    tok_ok[tb] = t < a.M;
+    Ap[tb] = (const bf16_t*)a.A + (size_t)(tok_ok[tb] ? t : 0) * a.lda + kbeg;
+  }
 
-  f32x16_t acc[RB];
+  f32x16_t acc[TB][RB];
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
+  for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[rb][i] = 0.f;
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[tb][rb][i] = 0.f;
   // D register sets: the loads of the next D steps of 64 are in flight while a
   // step's MFMAs run.  The launch guarantees Kw / 64 is a positive multiple of
   // D, so the steady loop refills every set unconditionally and the last D
   // steps drain without loads (no branch inside the pipeline).
-  u32x4_t bw[D][RB][4], xw[D][4];
+  u32x4_t bw[D][RB][4], xw[D][TB][4];
 #pragma unroll
-  for (int d = 0; d < D; ++d) sk_load<RB>(Bp, Ap, tok_ok, d * 64, bw[d], xw[d]);
+  for (int d = 0; d < D; ++d) sk_load<RB, TB>(Bp, Ap, tok_ok, d * 64, bw[d], xw[d]);
   for (int k = 0; k + D * 64 < Kw; k += D * 64) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      sk_mma<RB>(bw[d], xw[d], acc);
-      sk_load<RB>(Bp, Ap, tok_ok, k + (D + d) * 64, bw[d], xw[d]);
+      sk_mma<RB, TB>(bw[d], xw[d], acc);
+      sk_load<RB, TB>(Bp, Ap, tok_ok, k + (D + d) * 64, bw[d], xw[d]);
     }
   }
 #pragma unroll
-  for (int d = 0; d < D; ++d) sk_mma<RB>(bw[d], xw[d], acc);
+  for (int d = 0; d < D; ++d) sk_mma<RB, TB>(bw[d], xw[d], acc);
 
-  // acc[rb][i]: tile row rb*32 + (i/4)*8 + h*4 + i%4, token r.  Sum the waves
-  // as (w0 + w2) + (w1 + w3).
+  // acc[tb][rb][i]: tile row rb*32 + (i/4)*8 + h*4 + i%4, token 32 tb + r.
+  // Sum the waves as (w0 + w2) + (w1 + w3).
   auto put = [&](int slot) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) red[slot][r][rb * 32 + (i >> 2) * 8 + h * 4 + (i & 3)] = acc[rb][i];
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) red[slot][tb * 32 + r][rb * 32 + (i >> 2) * 8 + h * 4 + (i & 3)] = acc[tb][rb][i];
   };
   auto add = [&](int slot) {
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[rb][i] += red[slot][r][rb * 32 + (i >> 2) * 8 + h * 4 + (i & 3)];
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[tb][rb][i] += red[slot][tb * 32 + r][rb * 32 + (i >> 2) * 8 + h * 4 + (i & 3)];
   };
   if (wid >= 2) put(wid - 2);
   __syncthreads();
@@ -378,7 +397,7 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_kernel(GemmArgs a) {
   // element e of the tile: token e / R, tile row e % R (coalesced along rows)
   const int M = a.M;
   if (ks > 1) {
-    float* mine = a.part + (size_t)blockIdx.x * 32 * R;
+    float* mine = a.part + (size_t)blockIdx.x * TOK * R;
     for (int e = tid; e < M * R; e += SK_THREADS) mine[e] = red[0][e / R][e % R];
     return;
   }
@@ -394,9 +413,9 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_kernel(GemmArgs a) {
 
 // One thread per output (token m, output column): the ksplit partials of its
 // tile in index order, then the epilogue.
-template <int EPI, int RB>
+template <int EPI, int RB, int TB>
 __global__ __launch_bounds__(256) void gemm_skinny_reduce(GemmArgs a) {
-  constexpr int R = 32 * RB;
+  constexpr int R = 32 * RB, TOK = 32 * TB;
   constexpr int per_tile = (EPI == EPI_SWIGLU) ? R / 2 : R;
   const int tiles = (EPI == EPI_SWIGLU) ? (a.F + per_tile - 1) / per_tile : (a.N + R - 1) / R;
   const int i = blockIdx.x * 256 + threadIdx.x;
@@ -404,31 +423,32 @@ __global__ __launch_bounds__(256) void gemm_skinny_reduce(GemmArgs a) {
   const int m = i / (tiles * per_tile), c = i - m * tiles * per_tile;
   const int tile = c / per_tile, j = c - tile * per_tile;
   const int ks = a.ksplit;
-  const float* p = a.part + (size_t)tile * ks * 32 * R + m * R + j;
+  const float* p = a.part + (size_t)tile * ks * TOK * R + m * R + j;
   float v = 0.f, vup = 0.f;
   for (int q = 0; q < ks; ++q) {
-    v += p[(size_t)q * 32 * R];
-    if (EPI == EPI_SWIGLU) vup += p[(size_t)q * 32 * R + R / 2];
+    v += p[(size_t)q * TOK * R];
+    if (EPI == EPI_SWIGLU) vup += p[(size_t)q * TOK * R + R / 2];
   }
   sk_epilogue<EPI, RB>(a, tile, m, j, v, vup);
 }
 
-template <int EPI, int RB>
+template <int EPI, int RB, int TB>
 static hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
   constexpr int R = 32 * RB;
   const int tiles = (EPI == EPI_SWIGLU) ? (a.F + R / 2 - 1) / (R / 2) : (a.N + R - 1) / R;
   // steps of 64 per wave (K % (ksplit * 4 * 64) == 0 is checked by the caller)
   const int steps = a.K / (a.ksplit * 4 * 64);
-  constexpr int DEEP = RB == 2 ? 4 : 2;   // four steps in flight fit the registers only at RB = 2
+  // four steps in flight fit the registers only with 64 weight rows and 32 tokens
+  constexpr int DEEP = (RB == 2 && TB == 1) ? 4 : 2;
   if (steps % DEEP == 0)
-    gemm_skinny_kernel<EPI, RB, DEEP><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
+    gemm_skinny_kernel<EPI, RB, DEEP, TB><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
   else if (steps % 2 == 0)
-    gemm_skinny_kernel<EPI, RB, 2><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
+    gemm_skinny_kernel<EPI, RB, 2, TB><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
   else
-    gemm_skinny_kernel<EPI, RB, 1><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
+    gemm_skinny_kernel<EPI, RB, 1, TB><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
   if (a.ksplit > 1 && !(a.defer_reduce && EPI == EPI_STORE)) {
     const long outs = (long)a.M * tiles * (EPI == EPI_SWIGLU ? R / 2 : R);
-    gemm_skinny_reduce<EPI, RB><<<(int)((outs + 255) / 256), 256, 0, s>>>(a);
+    gemm_skinny_reduce<EPI, RB, TB><<<(int)((outs + 255) / 256), 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }
@@ -515,11 +535,15 @@ static hipError_t launch_dma(const GemmArgs& a, int blocks, hipStream_t s) {
 
 template <int EPI>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
-  if (a.M <= 32) {
+  if (a.M <= 64) {
     if (a.ksplit < 1 || a.K % (a.ksplit * 4 * 64)) return hipErrorInvalidValue;
     if (a.ksplit > 1 && !a.part) return hipErrorInvalidValue;
-    if (a.skinny_rb == 2) return launch_skinny<EPI, 2>(a, s);
-    if (a.skinny_rb == 4) return launch_skinny<EPI, 4>(a, s);
+    if (a.M > 32) {
+      if (a.skinny_rb == 2) return launch_skinny<EPI, 2, 2>(a, s);
+      return hipErrorInvalidValue;
+    }
+    if (a.skinny_rb == 2) return launch_skinny<EPI, 2, 1>(a, s);
+    if (a.skinny_rb == 4) return launch_skinny<EPI, 4, 1>(a, s);
     return hipErrorInvalidValue;
   }
   if (a.K % DBK) return hipErrorInvalidValue;

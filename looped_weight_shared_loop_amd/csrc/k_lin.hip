@@ -582,7 +582,7 @@ DEV float ld_qkv(const LinArgs& a, int row, int col) {
     float x[KSMAX];
 #pragma unroll
     for (int p = 0; p < KSMAX; ++p)
-      if (p < a.qp.ks) x[p] = a.qp.part[((size_t)(tile * a.qp.ks + p) * 32 + row) * R + (col - tile * R)];
+      if (p < a.qp.ks) x[p] = a.qp.part[((size_t)(tile * a.qp.ks + p) * a.qp.tok + row) * R + (col - tile * R)];
     float v = 0.f;
 #pragma unroll
     for (int p = 0; p < KSMAX; ++p)

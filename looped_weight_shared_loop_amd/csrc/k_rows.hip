@@ -72,7 +72,7 @@ DEV void ld8_y(const T* y, const YPart& yp, int t, int C, int c0, float* v) {
 #pragma unroll
       for (int p = 0; p < PG; ++p)
         if (p0 + p < yp.ks) {
-          const float4* q = reinterpret_cast<const float4*>(yp.part + ((size_t)(tile * yp.ks + p0 + p) * 32 + t) * R + j);
+          const float4* q = reinterpret_cast<const float4*>(yp.part + ((size_t)(tile * yp.ks + p0 + p) * yp.tok + t) * R + j);
           lo[p] = q[0];
           hi[p] = q[1];
         }

@@ -17,18 +17,19 @@ hipError_t embed(int dt, const int32_t* tokens, const void* table, int vocab, in
 
 // h <- h + y (if y), u <- RMSNorm(h; gamma).  In place on h.
 // A bf16 [T][C] sublayer output that is still split-K partial sums of the
-// decode-shaped GEMM (tile of R output columns, ks partials of 32 rows):
-// element (t, c) = bf16(sum_p part[((c / R) * ks + p) * 32 + t) * R + c % R]),
-// the sum taken in index order as the GEMM's own reduction would.
+// decode-shaped GEMM (tile of R output columns, ks partials of `tok` rows,
+// tok = 32 or 64): element (t, c) =
+// bf16(sum_p part[((c / R) * ks + p) * tok + t) * R + c % R]), the sum taken
+// in index order as the GEMM's own reduction would.
 struct YPart {
   const float* part;     // null: the output is stored in y
-  int ks, rows;
+  int ks, rows, tok;
 };
 
 struct NormArgs {
   int dt, T, C;
   const void* y;
-  YPart yp;              // overrides y when yp.part is set (bf16, T <= 32)
+  YPart yp;              // overrides y when yp.part is set (bf16, T <= yp.tok)
   void* h;
   const float* gamma;
   void* u;
@@ -71,19 +72,20 @@ struct GemmArgs {
   void* vcache;          // [B][Hkv][d][S_max] (transposed)
   int S_call, pos0, S_max;  // row m is sequence m / S_call at position pos0 + m % S_call
   int F;                 // EPI_SWIGLU: up rows start at row F of B
-  // M <= 32: split-K plan (skinny_plan) and its scratch; ksplit 1 needs none.
+  // M <= 64: split-K plan (skinny_plan) and its scratch; ksplit 1 needs none.
   int ksplit;
   int defer_reduce;      // ksplit > 1: leave the partials for the consumer (YPart)
-  int skinny_rb;         // 32-row blocks per tile (2 or 4)
-  float* part;           // [tiles * ksplit][32][32 * skinny_rb] fp32 partial sums
+  int skinny_rb;         // 32-row blocks per tile (2 or 4; 2 when M > 32)
+  float* part;           // [tiles * ksplit][32 tb][32 * skinny_rb] fp32 partial sums, tb = M > 32 ? 2 : 1
 };
 hipError_t gemm(const GemmArgs& a, hipStream_t s);
 
-// Decode-shaped (M <= 32) GEMM plan: 128 weight rows per workgroup tile (SwiGLU:
-// 64 gate + 64 up rows), K split over `ksplit` workgroups when the tiles alone
-// cannot fill the device.  `bytes` = partial sums (0 when ksplit == 1).
-struct SkinnyPlan { int rb, tiles, ksplit; size_t bytes; };
-SkinnyPlan skinny_plan(int epi, int N, int K, int F, int cu);
+// Decode-shaped (M <= 64) GEMM plan: 32 rb weight rows per workgroup tile
+// (SwiGLU: half gate, half up rows) against tb = 1 or 2 blocks of 32 token
+// rows, K split over `ksplit` workgroups when the tiles alone cannot fill the
+// device.  `bytes` = partial sums (0 when ksplit == 1).
+struct SkinnyPlan { int rb, tb, tiles, ksplit; size_t bytes; };
+SkinnyPlan skinny_plan(int epi, int M, int N, int K, int F, int cu);
 
 // ---------------------------------------------------------------- attention
 struct AttnArgs {

@@ -33,8 +33,8 @@ constexpr int LIN_CHUNK = 64;
 extern "C" {
 
 size_t loop_op_gemm_bytes(int dtype, int epi, int M, int N, int K, int F) {
-  if (dtype != LOOP_BF16 || M <= 0 || M > 32 || N <= 0 || K <= 0) return 0;
-  return lk::skinny_plan(epi, N, K, F, lk::device_cu_count()).bytes;
+  if (dtype != LOOP_BF16 || M <= 0 || M > 64 || N <= 0 || K <= 0) return 0;
+  return lk::skinny_plan(epi, M, N, K, F, lk::device_cu_count()).bytes;
 }
 
 int loop_op_gemm(int dtype, int epi, int M, int N, int K, const void* A, long lda, const void* B, long ldb, void* C,
@@ -54,8 +54,8 @@ int loop_op_gemm(int dtype, int epi, int M, int N, int K, const void* A, long ld
   g.F = F;
   g.ksplit = 1;
   g.skinny_rb = 4;
-  if (dt == lk::DT_BF16 && M > 0 && M <= 32) {
-    const lk::SkinnyPlan p = lk::skinny_plan(epi, N, K, F, lk::device_cu_count());
+  if (dt == lk::DT_BF16 && M > 0 && M <= 64) {
+    const lk::SkinnyPlan p = lk::skinny_plan(epi, M, N, K, F, lk::device_cu_count());
     g.skinny_rb = p.rb;
     if (p.ksplit > 1 && scratch) {
       if (scratch_bytes < p.bytes)

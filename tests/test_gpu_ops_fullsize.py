@@ -53,10 +53,14 @@ def _bf16(t):
     ("decode_gate_up", 32, 2 * F, C, 3, True), ("decode_down", 32, C, F, 0, True),
     ("decode_o", 32, C, HQ * D, 0, True), ("decode_qkv_m7", 7, QKV, C, 0, True),
     ("decode_down_nosplit", 32, C, F, 0, False), ("decode_gate_up_m1_nosplit", 1, 2 * F, C, 3, False),
+    # two blocks of 32 token rows against one weight read (two cohorts of a pipelined decode)
+    ("decode64_gate_up", 64, 2 * F, C, 3, True), ("decode64_o", 64, C, HQ * D, 0, True),
+    ("decode64_down_m45", 45, C, F, 0, True), ("head64_rows", 64, V, C, 1, True),
+    ("decode64_qkv_nosplit_m33", 33, QKV, C, 0, False),
 ])
 def test_gemm_full_size_sampled(name, M, N, K, epi, split):
-    """9B-shape projections; M <= 32 is the decode kernel, with K split over
-    workgroups (scratch given) or one workgroup per 128-row tile."""
+    """9B-shape projections; M <= 64 is the decode kernel, with K split over
+    workgroups (scratch given) or one workgroup per weight tile."""
     need_gpu()
     from looped_weight_shared_loop_amd import _abi as A
     print(f"gemm {name} M={M} N={N} K={K} split={split}", flush=True)
