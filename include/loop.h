@@ -136,8 +136,10 @@ int loop_model_schedule(const loop_model* m, int max, int* layer, int* pass, int
 /* Device bytes of a state for `batch` sequences of up to `max_seq` positions:
  * a 256-byte header, then per full-attention execution K [batch][Hkv][S_max][d]
  * and V^T [batch][Hkv][d][S_max] (dtype), then per linear execution
- * S [batch][Hkv][d][d] and z [batch][Hkv][d] (float32); S_max is max_seq
- * rounded up to a multiple of 64. */
+ * S [batch][Hkv][d][d] and z [batch][Hkv][d] (float32), then the parked
+ * cohorts of loop_decode_pipelined (X [batch][2][C], y [batch][C] in dtype,
+ * maps [batch][8] float32); regions start on 256-byte boundaries; S_max is
+ * max_seq rounded up to a multiple of 64. */
 int loop_state_bytes(const loop_model* m, int batch, int max_seq, size_t* bytes);
 
 /* Device bytes of the workspace for one call over up to `max_tokens` new
@@ -179,6 +181,39 @@ int loop_prefill(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes
  * linear state.  Errors: as loop_prefill, plus STATE when the state is empty. */
 int loop_decode_step(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes,
                      const int32_t* tokens_dev, int B, float* logits_dev, void* stream);
+
+/* Decode with the passes of the looped block co-scheduled over cohorts, so
+ * that every call reads each shared layer's weights once for several tokens'
+ * passes.  One page expects the shared block's weights to be fetched once
+ * and kept for the second pass ("SenseTime open-sourced its experimental
+ * SenseNova-Loop-9B-Preview" (frontword.com), section "Why parameter reuse
+ * matters for inference"); at 9.3 GB per block pass no cache holds them, and
+ * this schedule is what makes one weight read serve two passes.
+ *
+ * The state holds n_passes cohorts of B sequences: cohort g is sequences
+ * [g B, (g + 1) B) (state batch = n_passes x B, prefilled as usual).  A token
+ * enters its cohort with the layers before the block and pass 1 of the block,
+ * advances one pass per call (parked inside the block between calls), and
+ * leaves after the last pass with the layers after the block and the head.
+ * Cohorts enter in the order 0, 1, ..., n_passes - 1, 0, ...; a cohort can
+ * take its next token once its previous one has left.  Each call runs every
+ * stored layer of the block once over all cohorts' rows (each cohort on its own
+ * (layer, pass) KV cache or linear state and its own position).
+ *
+ * tokens_dev: int32 [B] for the entering cohort, or NULL (no cohort enters:
+ * drains the pipeline).  logits_dev: float32 [B][V], written for the cohort
+ * whose token leaves in this call.  cohorts (host int[2]): [0] the cohort
+ * that entered (-1: none), [1] the cohort whose logits were written (-1: none;
+ * the first n_passes - 1 calls after a prefill write none).  Results per
+ * token equal loop_decode_step's up to summation order.  The workspace is
+ * loop_workspace_bytes(m, n_passes x B, n_passes x B, max_seq).  While a
+ * cohort has a token in flight, loop_prefill and loop_decode_step return
+ * STATE; loop_state_set_length resets the pipeline (tokens in flight are
+ * dropped).  loop_state_length reports the smallest cohort length.
+ * Errors: INVALID_ARG, SHAPE (batch != n_passes x B), ALIGN, CAPACITY,
+ * WORKSPACE, STATE (nothing to run, a cohort not ready, or no prefill), HIP. */
+int loop_decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes,
+                          const int32_t* tokens_dev, int B, float* logits_dev, int* cohorts, void* stream);
 
 const char* loop_status_string(int status);
 const char* loop_last_error(void);

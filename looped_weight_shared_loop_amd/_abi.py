@@ -73,6 +73,8 @@ SYMBOLS = {
     "loop_prefill": (c_int, [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, c_int, c_int,
                              c_uint, c_void_p, c_void_p]),
     "loop_decode_step": (c_int, [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_int, c_void_p, c_void_p]),
+    "loop_decode_pipelined": (c_int, [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_int, c_void_p, c_void_p,
+                                      c_void_p]),
     "loop_status_string": (ctypes.c_char_p, [c_int]),
     "loop_last_error": (ctypes.c_char_p, []),
     # op level (include/loop_ops.h)
@@ -202,6 +204,14 @@ def loop_decode_step(m, st, ws_ptr: int, ws_bytes: int, tokens_ptr: int, B: int,
                      stream: int) -> None:
     _check(lib().loop_decode_step(m, st, c_void_p(ws_ptr), ws_bytes, c_void_p(tokens_ptr), B,
                                   c_void_p(logits_ptr), c_void_p(stream)), "loop_decode_step")
+
+
+def loop_decode_pipelined(m, st, ws_ptr: int, ws_bytes: int, tokens_ptr, B: int, logits_ptr, stream: int):
+    """Returns (entered cohort, cohort whose logits were written), -1 for none."""
+    info = (c_int * 2)(-1, -1)
+    _check(lib().loop_decode_pipelined(m, st, c_void_p(ws_ptr), ws_bytes, c_void_p(tokens_ptr), B,
+                                       c_void_p(logits_ptr), info, c_void_p(stream)), "loop_decode_pipelined")
+    return int(info[0]), int(info[1])
 
 
 # ---------------------------------------------------------------- op level

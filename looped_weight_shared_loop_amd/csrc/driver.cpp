@@ -68,6 +68,22 @@ struct loop_state {
   int batch, max_seq, S_max;
   int length;
   std::vector<size_t> koff, voff, soff, zoff;
+  // pipelined decode: cohort g holds sequences [g B, (g + 1) B), B = batch / n_passes.
+  // A cohort between calls is parked in the looped block: its streams X, its
+  // last sublayer output y and that site's maps (the pending write-back).
+  size_t park_x = 0, park_y = 0, park_maps = 0;
+  std::vector<int> pipe_next;   // pass the cohort runs at its next call; 0: no token in flight
+  std::vector<int> pipe_len;    // positions each cohort has completed
+  int pipe_enter = 0;           // cohort whose token enters next
+  bool pipe_idle() const {
+    for (size_t g = 0; g < pipe_next.size(); ++g)
+      if (pipe_next[g] != 0 || pipe_len[g] != length) return false;
+    return true;
+  }
+  void pipe_reset() {
+    for (size_t g = 0; g < pipe_next.size(); ++g) { pipe_next[g] = 0; pipe_len[g] = length; }
+    pipe_enter = 0;
+  }
 };
 
 namespace {
@@ -239,7 +255,7 @@ int loop_model_schedule(const loop_model* m, int max, int* layer, int* pass, int
 }
 
 static void state_offsets(const loop_model* m, int batch, int max_seq, std::vector<size_t>* k, std::vector<size_t>* v,
-                          std::vector<size_t>* s, std::vector<size_t>* z, size_t* total) {
+                          std::vector<size_t>* s, std::vector<size_t>* z, size_t* total, size_t* park = nullptr) {
   const loop_config& c = m->cfg;
   const size_t S_max = ((size_t)max_seq + 63) / 64 * 64;
   const size_t kv = (size_t)batch * c.n_kv_heads * S_max * c.head_dim * m->es;
@@ -258,6 +274,14 @@ static void state_offsets(const loop_model* m, int batch, int max_seq, std::vect
     if (z) z->push_back(off);
     off += align256(zb);
   }
+  // parked cohorts of the pipelined decode: X [batch][2][C], y [batch][C], maps [batch][8] fp32
+  const size_t C = c.hidden;
+  if (park) park[0] = off;
+  off += align256((size_t)batch * 2 * C * m->es);
+  if (park) park[1] = off;
+  off += align256((size_t)batch * C * m->es);
+  if (park) park[2] = off;
+  off += align256((size_t)batch * 8 * sizeof(float));
   *total = off;
 }
 
@@ -281,8 +305,8 @@ int loop_state_create(const loop_model* m, void* state_dev, size_t bytes, int ba
   if (batch <= 0 || max_seq <= 0) return lp_fail(LOOP_ERR_INVALID_ARG, "batch and max_seq must be positive");
   if (misaligned(state_dev)) return lp_fail(LOOP_ERR_ALIGN, "state not 16-byte aligned");
   auto* st = new loop_state();
-  size_t need = 0;
-  state_offsets(m, batch, max_seq, &st->koff, &st->voff, &st->soff, &st->zoff, &need);
+  size_t need = 0, park[3] = {0, 0, 0};
+  state_offsets(m, batch, max_seq, &st->koff, &st->voff, &st->soff, &st->zoff, &need, park);
   if (bytes < need) {
     delete st;
     return lp_fail(LOOP_ERR_CAPACITY, "state has %zu bytes, needs %zu", bytes, need);
@@ -294,6 +318,11 @@ int loop_state_create(const loop_model* m, void* state_dev, size_t bytes, int ba
   st->max_seq = max_seq;
   st->S_max = (max_seq + 63) / 64 * 64;
   st->length = 0;
+  st->park_x = park[0];
+  st->park_y = park[1];
+  st->park_maps = park[2];
+  st->pipe_next.assign(m->cfg.n_passes, 0);
+  st->pipe_len.assign(m->cfg.n_passes, 0);
   *out = st;
   return LOOP_OK;
 }
@@ -313,6 +342,7 @@ int loop_state_set_length(loop_state* st, int length) {
   if (!st) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
   if (length < 0 || length > st->max_seq) return lp_fail(LOOP_ERR_CAPACITY, "length %d outside [0, %d]", length, st->max_seq);
   st->length = length;
+  st->pipe_reset();
   return LOOP_OK;
 }
 
@@ -382,6 +412,8 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
   if (misaligned(workspace) || misaligned(out) || misaligned(embeds)) return lp_fail(LOOP_ERR_ALIGN, "misaligned buffer");
   if (B > st->batch) return lp_fail(LOOP_ERR_CAPACITY, "batch %d exceeds the state's %d", B, st->batch);
   if (decode && st->length == 0) return lp_fail(LOOP_ERR_STATE, "decode before prefill");
+  if (!st->pipe_idle())
+    return lp_fail(LOOP_ERR_STATE, "pipelined decode in progress (cohorts at different positions)");
   const int pos0 = (decode || (flags & LOOP_CONTINUE)) ? st->length : 0;
   if ((long)pos0 + S > st->max_seq)
     return lp_fail(LOOP_ERR_CAPACITY, "positions %d + %d exceed max_seq %d", pos0, S, st->max_seq);
@@ -550,6 +582,283 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
     LAUNCH(run_gemm(gemm(lk::EPI_F32, last, (long)S * C, B, m->head, c.vocab, C, out, c.vocab)), "head gemm");
   }
   st->length = pos0 + S;
+  st->pipe_reset();
+  return LOOP_OK;
+}
+
+// Decode with the passes of the looped block co-scheduled over n_passes
+// cohorts (cohort g = sequences [g B, (g + 1) B)).  A token enters its cohort
+// with the layers before the block and pass 1, advances one pass per call
+// (parked in the block between calls), and leaves after pass P with the
+// layers after the block and the head.  Every call runs each stored layer of
+// the block once for all cohorts' rows, so its weights are read once for up
+// to P tokens' passes; attention and linear attention run per cohort on the
+// cohort's own (layer, pass) slot and position.  Rows of a cohort with no
+// token in flight go through the shared projections and stream kernels as
+// don't-care rows whose results nothing reads.
+int decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, const int32_t* tokens, int B,
+                     float* logits, int* info, hipStream_t s) {
+  const loop_config& c = m->cfg;
+  const int G = c.n_passes;
+  if (!st || st->m != m) return lp_fail(LOOP_ERR_STATE, "state does not belong to this model");
+  if (!workspace || !info) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (B <= 0 || st->batch != G * B)
+    return lp_fail(LOOP_ERR_SHAPE, "pipelined decode needs a state of n_passes x cohort sequences (%d x %d != %d)", G,
+                   B, st->batch);
+  if (misaligned(workspace) || misaligned(logits)) return lp_fail(LOOP_ERR_ALIGN, "misaligned buffer");
+  info[0] = info[1] = -1;
+  std::vector<int> pass(G, 0);     // pass each cohort runs in this call (0: none)
+  for (int g = 0; g < G; ++g)
+    if (st->pipe_next[g] >= 2) pass[g] = st->pipe_next[g];
+  int e = -1;
+  if (tokens) {
+    e = st->pipe_enter;
+    if (st->pipe_next[e] != 0) return lp_fail(LOOP_ERR_STATE, "cohort %d still has a token in flight", e);
+    if (st->pipe_len[e] == 0) return lp_fail(LOOP_ERR_STATE, "decode before prefill");
+    pass[e] = 1;
+  }
+  int f = -1;
+  for (int g = 0; g < G; ++g)
+    if (pass[g] == G) f = g;
+  bool any = false;
+  for (int g = 0; g < G; ++g) any = any || pass[g] > 0;
+  if (!any) return lp_fail(LOOP_ERR_STATE, "no token to decode (no cohort in flight and no tokens given)");
+  if (f >= 0 && !logits) return lp_fail(LOOP_ERR_INVALID_ARG, "null logits");
+  for (int g = 0; g < G; ++g)
+    if (pass[g] && st->pipe_len[g] >= st->max_seq)
+      return lp_fail(LOOP_ERR_CAPACITY, "cohort %d is at max_seq %d", g, st->max_seq);
+  const int T = G * B;
+  const WsLayout L = ws_layout(m, T, T, st->max_seq);
+  if (ws_bytes < L.total) return lp_fail(LOOP_ERR_WORKSPACE, "workspace %zu bytes, needs %zu", ws_bytes, L.total);
+
+  char* ws = (char*)workspace;
+  const size_t es = m->es;
+  const int dt = c.dtype == LOOP_BF16 ? lk::DT_BF16 : lk::DT_F32;
+  const int C = c.hidden, Hq = c.n_heads, Hkv = c.n_kv_heads, d = c.head_dim, F = c.ffn;
+  const int qkv_rows = m->qkv_rows();
+  char* h = ws + L.h;
+  char* u = ws + L.u;
+  char* y = ws + L.y;
+  char* qkv = ws + L.qkv;
+  char* attn = ws + L.attn;
+  char* inter = ws + L.inter;
+  float* maps[2] = {(float*)(ws + L.maps), (float*)(ws + L.maps) + (size_t)T * 8};
+  float* lin_scr = (float*)(ws + L.lin);
+  float* dec_part = (float*)(ws + L.dec);
+  char* X = st->base + st->park_x;
+  char* parkY = st->base + st->park_y;
+  float* parkM = (float*)(st->base + st->park_maps);
+  const int ls = c.loop_start, le = c.loop_end, nl = le - ls;
+  auto rows = [&](char* p, int r, size_t width) { return p + (size_t)r * width * es; };
+
+  lk::YPart ypend{};
+  auto run_gemm = [&](lk::GemmArgs g, bool may_defer) {
+    g.ksplit = 1;
+    g.skinny_rb = 4;
+    if (g.dt == lk::DT_BF16 && g.M <= 64) {
+      const lk::SkinnyPlan p = lk::skinny_plan(g.epi, g.M, g.N, g.K, g.F, m->cu);
+      g.skinny_rb = p.rb;
+      if (p.ksplit > 1 && p.bytes <= L.skinny_bytes) {
+        g.ksplit = p.ksplit;
+        g.part = (float*)(ws + L.skinny);
+        if (may_defer && g.epi == lk::EPI_STORE) {
+          g.defer_reduce = 1;
+          ypend = lk::YPart{g.part, p.ksplit, 32 * p.rb, 32 * p.tb};
+        }
+      }
+    }
+    return lk::gemm(g, s);
+  };
+  auto gemm = [&](int epi, const void* A, long lda, int M, const void* Bw, int N, int K, void* Cout, long ldc) {
+    lk::GemmArgs g{};
+    g.dt = dt; g.epi = epi; g.M = M; g.N = N; g.K = K;
+    g.A = A; g.lda = lda; g.B = Bw; g.ldb = K; g.C = Cout; g.ldc = ldc;
+    return g;
+  };
+  // rows [r0, r0 + n): h <- h + y (y may be null), u <- RMSNorm(h; gamma)
+  auto norm = [&](int r0, int n, bool with_y, const float* gamma) {
+    lk::NormArgs a{};
+    a.dt = dt; a.T = n; a.C = C; a.y = with_y ? rows(y, r0, C) : nullptr; a.h = rows(h, r0, C); a.gamma = gamma;
+    a.u = rows(u, r0, C); a.eps = c.rms_eps;
+    if (with_y) a.yp = ypend;
+    ypend = lk::YPart{};
+    return lk::add_rmsnorm(a, s);
+  };
+  // one mHC transition on rows [r0, r0 + n)
+  auto mhc = [&](int mode, int r0, int n, const void* yin, bool use_ypend, const float* mi, float* mo,
+                 const float* w, const float* b, const float* gamma) {
+    lk::MhcArgs a{};
+    a.dt = dt; a.mode = mode; a.T = n; a.C = C; a.iters = c.sinkhorn_iters; a.eps = c.rms_eps;
+    a.y = yin; a.h = rows(h, r0, C); a.X = rows(X, r0, 2 * C);
+    if (use_ypend) a.yp = ypend;
+    ypend = lk::YPart{};
+    a.maps_in = mi ? mi + (size_t)r0 * 8 : nullptr;
+    a.maps_out = mo ? mo + (size_t)r0 * 8 : nullptr;
+    a.w = w; a.b = b; a.gamma = gamma; a.u = rows(u, r0, C);
+    a.grid = n < 2 * m->cu ? n : 2 * m->cu;
+    a.wsplit = (lk::bf16_t*)(ws + L.wsplit);
+    return lk::mhc(a, s);
+  };
+  // attention sublayer of stored layer `layer` on rows [r0, r0 + n); cohorts in
+  // `coh` (each a block of B rows inside the range) run their own execution
+  // `ex_of(g)` at position pipe_len[g]; the O projection leaves y (deferred
+  // when `defer_o`)
+  auto attention = [&](int layer, int r0, int n, const std::vector<int>& coh, const std::vector<const Exec*>& exs,
+                       bool defer_o) -> int {
+    const loop_layer_weights& W = m->layers[layer];
+    const bool full = exs[0]->full;
+    const bool fused = full && (int)coh.size() == 1 && n == B;
+    if (fused) {
+      // one cohort: K and V go into its slot from the projection's epilogue
+      const int g = coh[0];
+      lk::GemmArgs q = gemm(lk::EPI_QKV, rows(u, r0, C), C, n, W.qkv, qkv_rows, C, rows(qkv, r0, qkv_rows), qkv_rows);
+      q.q_cols = Hq * d; q.n_kv = Hkv; q.head_dim = d;
+      q.kcache = st->base + st->koff[exs[0]->slot] + (size_t)g * B * Hkv * st->S_max * d * es;
+      q.vcache = st->base + st->voff[exs[0]->slot] + (size_t)g * B * Hkv * d * st->S_max * es;
+      q.S_call = 1; q.pos0 = st->pipe_len[g]; q.S_max = st->S_max;
+      LAUNCH(run_gemm(q, false), "qkv gemm");
+    } else {
+      LAUNCH(run_gemm(gemm(lk::EPI_STORE, rows(u, r0, C), C, n, W.qkv, qkv_rows, C, rows(qkv, r0, qkv_rows),
+                           qkv_rows), false), "qkv gemm");
+    }
+    for (size_t i = 0; i < coh.size(); ++i) {
+      const int g = coh[i];
+      const Exec& ex = *exs[i];
+      const int pos = st->pipe_len[g];
+      char* qrow = rows(qkv, g * B, qkv_rows);
+      if (full) {
+        char* kc = st->base + st->koff[ex.slot] + (size_t)g * B * Hkv * st->S_max * d * es;
+        char* vc = st->base + st->voff[ex.slot] + (size_t)g * B * Hkv * d * st->S_max * es;
+        if (!fused)
+          LAUNCH(lk::kv_append(dt, qrow, qkv_rows, Hq * d, B, Hkv, d, kc, vc, st->S_max, pos, s), "kv append");
+        lk::AttnArgs a{};
+        a.dt = dt; a.B = B; a.S_call = 1; a.pos0 = pos; a.S_max = st->S_max; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+        a.q = qrow; a.ldq = qkv_rows; a.kcache = kc; a.vcache = vc; a.out = rows(attn, g * B, Hq * d);
+        a.ldo = Hq * d;
+        if (dt == lk::DT_BF16) {
+          const lk::DecodePlan dp = lk::decode_plan(B, Hkv, pos + 1, m->cu);
+          a.part = dec_part; a.split_len = dp.split_len; a.n_split = dp.n_split;
+          LAUNCH(lk::attn_decode(a, s), "decode attention");
+        } else {
+          LAUNCH(lk::attn_prefill(a, s), "attention");
+        }
+      } else {
+        lk::LinArgs a{};
+        a.dt = dt; a.B = B; a.S_call = 1; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.eps = c.la_eps;
+        a.qkv = qrow; a.ld = qkv_rows;
+        a.S = (float*)(st->base + st->soff[ex.slot]) + (size_t)g * B * Hkv * d * d;
+        a.z = (float*)(st->base + st->zoff[ex.slot]) + (size_t)g * B * Hkv * d;
+        a.init_zero = pos == 0;
+        a.out = rows(attn, g * B, Hq * d); a.ldo = Hq * d; a.scratch = lin_scr; a.chunk = LIN_CHUNK;
+        LAUNCH(lk::lin_decode(a, s), "linear attention (recurrent)");
+      }
+    }
+    LAUNCH(run_gemm(gemm(lk::EPI_STORE, rows(attn, r0, Hq * d), Hq * d, n, W.o, C, Hq * d, rows(y, r0, C), C),
+                    defer_o), "o gemm");
+    return LOOP_OK;
+  };
+  auto ffn = [&](int layer, int r0, int n, bool defer_down) -> int {
+    const loop_layer_weights& W = m->layers[layer];
+    lk::GemmArgs g = gemm(lk::EPI_SWIGLU, rows(u, r0, C), C, n, W.gate_up, 2 * F, C, rows(inter, r0, F), F);
+    g.F = F;
+    LAUNCH(run_gemm(g, false), "gate/up gemm");
+    LAUNCH(run_gemm(gemm(lk::EPI_STORE, rows(inter, r0, F), F, n, W.down, C, F, rows(y, r0, C), C), defer_down),
+           "down gemm");
+    return LOOP_OK;
+  };
+  // the plain (outside the block) layers of one cohort: rows [g B, (g + 1) B).
+  // On return y holds the last FFN output and h the residual before it.
+  auto plain_layers = [&](int g, int first, int last, bool defer_last) -> int {
+    for (int i = first; i < last; ++i) {
+      const int idx = i < ls ? i : ls + G * nl + (i - le);
+      const Exec& ex = m->sched[idx];
+      const loop_layer_weights& W = m->layers[i];
+      if (int r = attention(i, g * B, B, {g}, {&ex}, true)) return r;
+      LAUNCH(norm(g * B, B, true, W.ffn_norm), "add+rmsnorm");
+      if (int r = ffn(i, g * B, B, defer_last || i + 1 < last)) return r;
+      if (i + 1 < last) LAUNCH(norm(g * B, B, true, m->layers[i + 1].attn_norm), "add+rmsnorm");
+    }
+    return LOOP_OK;
+  };
+
+  // ---- the entering cohort: embedding and the layers before the block
+  if (e >= 0) {
+    LAUNCH(lk::embed(dt, tokens, m->embed, c.vocab, C, B, rows(h, e * B, C), (uint32_t*)st->base, s), "embed");
+    if (ls > 0) {
+      LAUNCH(norm(e * B, B, false, m->layers[0].attn_norm), "rmsnorm");
+      if (int r = plain_layers(e, 0, ls, true)) return r;
+    }
+  }
+  // ---- the block: every stored layer once, over all cohorts' rows
+  std::vector<int> coh;
+  for (int g = 0; g < G; ++g)
+    if (pass[g]) coh.push_back(g);
+  int mp = 1;     // maps[mp] holds the maps of the current site
+  {
+    const loop_layer_weights& W0 = m->layers[ls];
+    if (e >= 0)   // streams enter: X = [h + y, h + y]
+      LAUNCH(mhc(lk::MHC_ENTER, e * B, B, ls > 0 ? rows(y, e * B, C) : nullptr, ls > 0, nullptr, maps[1], W0.mhc_w[0],
+                 W0.mhc_b[0], W0.attn_norm), "mhc enter");
+    // every other cohort resumes from its park (cohorts with nothing in
+    // flight go along as don't-care rows)
+    for (int g = 0; g < G; ++g) {
+      if (g == e) continue;
+      int g1 = g;
+      while (g1 + 1 < G && g1 + 1 != e) ++g1;
+      LAUNCH(mhc(lk::MHC_MID, g * B, (g1 - g + 1) * B, rows(parkY, g * B, C), false, parkM, maps[1], W0.mhc_w[0],
+                 W0.mhc_b[0], W0.attn_norm), "mhc resume");
+      g = g1;
+    }
+  }
+  for (int i = ls; i < le; ++i) {
+    const loop_layer_weights& W = m->layers[i];
+    std::vector<const Exec*> exs;
+    for (int g : coh) exs.push_back(&m->sched[ls + (pass[g] - 1) * nl + (i - ls)]);
+    if (int r = attention(i, 0, T, coh, exs, true)) return r;
+    LAUNCH(mhc(lk::MHC_MID, 0, T, y, true, maps[mp], maps[mp ^ 1], W.mhc_w[1], W.mhc_b[1], W.ffn_norm), "mhc");
+    mp ^= 1;
+    const bool last = i + 1 == le;
+    if (int r = ffn(i, 0, T, !last)) return r;
+    if (!last) {
+      const loop_layer_weights& Wn = m->layers[i + 1];
+      LAUNCH(mhc(lk::MHC_MID, 0, T, y, true, maps[mp], maps[mp ^ 1], Wn.mhc_w[0], Wn.mhc_b[0], Wn.attn_norm), "mhc");
+      mp ^= 1;
+    }
+  }
+  // ---- leave the block: the cohort after pass P exits, the others park
+  for (int g : coh) {
+    if (g == f) continue;
+    LAUNCH(hipMemcpyAsync(rows(parkY, g * B, C), rows(y, g * B, C), (size_t)B * C * es, hipMemcpyDeviceToDevice, s),
+           "park y");
+    LAUNCH(hipMemcpyAsync(parkM + (size_t)g * B * 8, maps[mp] + (size_t)g * B * 8, (size_t)B * 8 * sizeof(float),
+                          hipMemcpyDeviceToDevice, s), "park maps");
+  }
+  if (f >= 0) {
+    const float* gamma = le < c.n_layers ? m->layers[le].attn_norm : m->final_norm;
+    LAUNCH(mhc(lk::MHC_EXIT, f * B, B, rows(y, f * B, C), false, maps[mp], nullptr, nullptr, nullptr, gamma),
+           "mhc exit");
+    if (le < c.n_layers) {
+      if (int r = plain_layers(f, le, c.n_layers, true)) return r;
+      LAUNCH(norm(f * B, B, true, m->final_norm), "add+rmsnorm");
+    }
+    LAUNCH(run_gemm(gemm(lk::EPI_F32, rows(u, f * B, C), C, B, m->head, c.vocab, C, logits, c.vocab), false),
+           "head gemm");
+  }
+  // ---- bookkeeping
+  for (int g : coh) {
+    if (g == f) {
+      st->pipe_next[g] = 0;
+      st->pipe_len[g] += 1;
+    } else {
+      st->pipe_next[g] = pass[g] + 1;
+    }
+  }
+  if (e >= 0) st->pipe_enter = (e + 1) % G;
+  int mn = st->pipe_len[0];
+  for (int g = 1; g < G; ++g) mn = std::min(mn, st->pipe_len[g]);
+  st->length = mn;
+  info[0] = e;
+  info[1] = f;
   return LOOP_OK;
 }
 
@@ -570,6 +879,12 @@ int loop_decode_step(loop_model* m, loop_state* st, void* workspace, size_t ws_b
   if (!m) return lp_fail(LOOP_ERR_INVALID_ARG, "null model");
   if (!tokens_dev) return lp_fail(LOOP_ERR_INVALID_ARG, "null tokens");
   return forward(m, st, workspace, ws_bytes, tokens_dev, nullptr, B, 1, 0, logits_dev, (hipStream_t)stream, true);
+}
+
+int loop_decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, const int32_t* tokens_dev,
+                          int B, float* logits_dev, int* cohorts, void* stream) {
+  if (!m) return lp_fail(LOOP_ERR_INVALID_ARG, "null model");
+  return decode_pipelined(m, st, workspace, ws_bytes, tokens_dev, B, logits_dev, cohorts, (hipStream_t)stream);
 }
 
 }  // extern "C"

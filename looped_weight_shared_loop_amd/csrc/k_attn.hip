@@ -525,4 +525,36 @@ hipError_t attn_decode(const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------------ KV append
+// Writes the K and V columns of B q|k|v rows (one new position per sequence,
+// already rounded to the storage type) at position `pos` of a cache slot,
+// K [B][Hkv][S_max][d] and V^T [B][Hkv][d][S_max]: the same values the fused
+// QKV epilogue stores, for callers whose projection covered several slots.
+template <typename T>
+__global__ __launch_bounds__(256) void kv_append_kernel(const T* __restrict__ qkv, long ld, int q_cols, int B,
+                                                        int Hkv, int d, T* __restrict__ kc, T* __restrict__ vc,
+                                                        int S_max, int pos) {
+  const int n = B * Hkv * d;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
+    const int b = i / (Hkv * d), r = i - b * Hkv * d, hk = r / d, dd = r - hk * d;
+    const T* row = qkv + (size_t)b * ld + q_cols;
+    kc[(((size_t)b * Hkv + hk) * S_max + pos) * d + dd] = row[hk * d + dd];
+    vc[(((size_t)b * Hkv + hk) * d + dd) * S_max + pos] = row[Hkv * d + hk * d + dd];
+  }
+}
+
+hipError_t kv_append(int dt, const void* qkv, long ld, int q_cols, int B, int Hkv, int d, void* kcache,
+                     void* vcache, int S_max, int pos, hipStream_t s) {
+  const int n = B * Hkv * d;
+  if (n <= 0) return hipSuccess;
+  const int grid = (n + 255) / 256;
+  if (dt == DT_BF16)
+    kv_append_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)qkv, ld, q_cols, B, Hkv, d, (bf16_t*)kcache,
+                                                  (bf16_t*)vcache, S_max, pos);
+  else
+    kv_append_kernel<float><<<grid, 256, 0, s>>>((const float*)qkv, ld, q_cols, B, Hkv, d, (float*)kcache,
+                                                 (float*)vcache, S_max, pos);
+  return hipGetLastError();
+}
+
 }  // namespace lk

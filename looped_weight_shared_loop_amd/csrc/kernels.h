@@ -98,6 +98,10 @@ struct AttnArgs {
 };
 hipError_t attn_prefill(const AttnArgs& a, hipStream_t s);
 hipError_t attn_decode(const AttnArgs& a, hipStream_t s);
+// K and V columns of B q|k|v rows (row stride ld, K from column q_cols) into a
+// cache slot at position pos (one new position per sequence).
+hipError_t kv_append(int dt, const void* qkv, long ld, int q_cols, int B, int Hkv, int d, void* kcache,
+                     void* vcache, int S_max, int pos, hipStream_t s);
 // Decode split of the cache: as few splits as fill `cu` workgroups over the
 // B * Hkv (sequence, KV head) pairs, each a multiple of 64 keys.
 struct DecodePlan { int split_len, n_split; };

@@ -223,6 +223,23 @@ class LoopModel:
                            out.data_ptr(), self._stream())
         return out
 
+    def decode_pipelined(self, state: LoopState, tokens: Optional[torch.Tensor], out: Optional[torch.Tensor] = None):
+        """One call of the pass-pipelined decode (the state holds n_passes
+        cohorts of B sequences).  tokens: int32 [B] for the entering cohort, or
+        None.  Returns (entered, left, logits): the cohorts that entered and
+        left (-1: none) and float32 [B][V] logits of the leaving cohort."""
+        G = self.cfg.n_passes
+        B = state.batch // G
+        if tokens is not None:
+            assert tokens.dtype == torch.int32 and tokens.is_contiguous() and int(tokens.shape[0]) == B
+        if out is None:
+            out = torch.empty(B, self.cfg.vocab, dtype=torch.float32, device=self.device)
+        ws = self.workspace(state.batch, state.batch, state.max_seq)
+        entered, left = A.loop_decode_pipelined(self.handle, state.handle, ws.data_ptr(), ws.numel(),
+                                                tokens.data_ptr() if tokens is not None else None, B,
+                                                out.data_ptr(), self._stream())
+        return entered, left, out
+
     def close(self) -> None:
         if self.handle:
             A.loop_model_destroy(self.handle)

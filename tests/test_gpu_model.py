@@ -170,6 +170,80 @@ def test_multi_token_verify_block(dtype):
     assert rel(d.cpu().numpy(), full[:, S + k]) < tol
 
 
+@pytest.mark.parametrize("dtype,passes,loop", [("fp32", 2, (2, 6)), ("fp32", 3, (2, 6)), ("fp32", 2, (0, 8)),
+                                                ("bf16", 2, (2, 6))])
+def test_pipelined_decode_matches_oracle(dtype, passes, loop):
+    """Decode with the block's passes co-scheduled over n_passes cohorts: every
+    token's logits (returned when it leaves, n_passes - 1 calls after it
+    entered) equal the one-shot forward's row; after the pipeline drains, the
+    cohorts are level and the ordinary decode step continues."""
+    if dtype == "fp32":
+        ocfg = oracle.tiny_config(n_kv_heads=2, n_passes=passes, loop_start=loop[0], loop_end=loop[1])
+        tol = FP32_TOL
+    else:
+        ocfg = mini_bf16_config(n_passes=passes, loop_start=loop[0], loop_end=loop[1])
+        tol = BF16_TOL
+    model, Wo = build_pair(ocfg)
+    G, Bc, S, K = passes, 2, 24, 3
+    toks = tokens(G * Bc, S + K + 1, ocfg.vocab, seed=31 + passes)
+    _say("pipelined decode", dtype, "passes", passes, "loop", loop)
+    full = oracle.forward(ocfg, Wo, toks, all_logits=True)
+    st = model.new_state(G * Bc, S + K + 1)
+    model.prefill(st, to_dev_tokens(toks[:, :S]))
+    sent, back = [0] * G, [0] * G
+    for t in range(K * G + G - 1):
+        e = t % G
+        tk = None
+        if t < K * G:
+            tk = to_dev_tokens(toks[e * Bc:(e + 1) * Bc, S + sent[e]])
+        entered, left, out = model.decode_pipelined(st, tk)
+        if tk is not None:
+            assert entered == e
+            sent[e] += 1
+        else:
+            assert entered == -1
+        if t < G - 1:
+            assert left == -1             # the pipeline is still filling
+        else:
+            assert left == (t - (G - 1)) % G
+            k = back[left]
+            err = rel(out.cpu().numpy(), full[left * Bc:(left + 1) * Bc, S + k])
+            _say("call", t, "cohort", left, "token", k, "rel err", err)
+            assert err < tol
+            back[left] += 1
+    assert back == [K] * G and st.length == S + K
+    d = model.decode_step(st, to_dev_tokens(toks[:, S + K]))
+    assert rel(d.cpu().numpy(), full[:, S + K]) < tol
+
+
+def test_pipelined_decode_state_rules():
+    """A prefill or an ordinary decode step is refused while a cohort has a
+    token in flight; resetting the length drops the pipeline."""
+    L = need_gpu()
+    ocfg = oracle.tiny_config(n_kv_heads=2)
+    model, _ = build_pair(ocfg)
+    st = model.new_state(4, 40)
+    toks = tokens(4, 12, ocfg.vocab, seed=41)
+    with pytest.raises(L.LoopError):                      # no prefill yet
+        model.decode_pipelined(st, to_dev_tokens(toks[:2, 0]))
+    model.prefill(st, to_dev_tokens(toks[:, :10]))
+    with pytest.raises(L.LoopError):                      # nothing in flight, nothing entering
+        model.decode_pipelined(st, None)
+    model.decode_pipelined(st, to_dev_tokens(toks[:2, 10]))
+    with pytest.raises(L.LoopError) as ei:
+        model.decode_step(st, to_dev_tokens(toks[:, 10]))
+    assert ei.value.code == -9
+    with pytest.raises(L.LoopError):
+        model.prefill(st, to_dev_tokens(toks[:, :10]))
+    st.set_length(10)
+    d = model.decode_step(st, to_dev_tokens(toks[:, 10]))
+    assert torch.isfinite(d).all().item()
+    bad = model.new_state(3, 40)                          # batch not a multiple of the pass count
+    model.prefill(bad, to_dev_tokens(toks[:3, :10]))
+    with pytest.raises(L.LoopError) as ei:
+        model.decode_pipelined(bad, to_dev_tokens(toks[:1, 10]))
+
+
 # ------------------------------------------------------------------ bf16 (MFMA kernels)
 def test_mini_bf16_prefill_decode():
     ocfg = mini_bf16_config()
