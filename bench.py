@@ -85,6 +85,17 @@ def prefill_flops(cfg, S, B=1):
     return gemm + attn + lin + head, gemm, attn, lin
 
 
+def decode_pipelined_bytes(cfg, B, ctx):
+    """Bytes one pass-pipelined call must move (B tokens leave per call): every
+    stored layer's weights once (the looped block serves all cohorts), the
+    head, and the same KV and linear-state traffic as a B-token decode step."""
+    tot, w, kv, lin = decode_bytes(cfg, B, ctx)
+    C, F, d, Hq, Hkv = cfg["hidden"], cfg["ffn"], cfg["head_dim"], cfg["n_heads"], cfg["n_kv_heads"]
+    per_layer = ((Hq + 2 * Hkv) * d * C + C * Hq * d + 2 * F * C + C * F) * 2
+    w1 = per_layer * cfg["n_layers"] + cfg["vocab"] * C * 2
+    return w1 + kv + lin, w1, kv, lin
+
+
 def decode_bytes(cfg, B, ctx):
     """Bytes one decode step must move: every layer execution's weights (the
     shared block twice), the head, every KV cache (K and V of `ctx` positions),
@@ -180,11 +191,12 @@ def time_dominant_gemm(L, torch, S, iters=10):
     return ms, flops
 
 
-def time_decode(L, torch, model, B, ctx, steps, warmup):
+def fill_decode_state(torch, model, st, B, ctx):
+    """Every KV cache slot and linear state of B sequences pre-filled as if
+    `ctx` positions had been processed: K, V ~ N(0, 1); S ~ N(0, 1), z = |N(0, 1)|."""
     import synth
     from synth import device as sd
     from looped_weight_shared_loop_amd import _abi as A
-    st = model.new_state(B, ctx + warmup + steps + 1)
     cfg = model.cfg
     Hkv, d = cfg.n_kv_heads, cfg.head_dim
     S_max = (st.max_seq + 63) // 64 * 64
@@ -207,6 +219,47 @@ def time_decode(L, torch, model, B, ctx, steps, warmup):
         sd.fill_normal4(zp, False, (1, 1, 1, B * Hkv * d), (0, 0, 0, 1), 2, synth.tid_linstate(slot, "z"), 1.0,
                         absval=True, stream=stream)
     st.set_length(ctx)
+
+
+def time_decode_pipelined(L, torch, model, B, ctx, calls, warmup):
+    """Pass-pipelined decode: n_passes cohorts of B sequences, each call runs
+    the looped block once for all cohorts' rows and returns one cohort's
+    logits (B tokens per call in steady state)."""
+    import synth
+    from synth import device as sd
+    G = model.cfg.n_passes
+    st = model.new_state(G * B, ctx + warmup + calls + 2)
+    fill_decode_state(torch, model, st, G * B, ctx)
+    toks = torch.empty(warmup + calls + G, B, dtype=torch.int32, device="cuda")
+    sd.fill_tensor_uniform_int(toks, 1, synth.TID_TOKENS + 300, model.cfg.vocab)
+    model.workspace(G * B, G * B, st.max_seq)
+    out = torch.empty(B, model.cfg.vocab, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    for i in range(G - 1 + warmup):           # fill the pipeline, then warm up
+        model.decode_pipelined(st, toks[i], out)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    left = []
+    e0.record()
+    for i in range(calls):
+        left.append(model.decode_pipelined(st, toks[G - 1 + warmup + i], out)[1])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / calls
+    assert all(x >= 0 for x in left)          # every timed call returned a cohort's logits
+    st.check()
+    assert torch.isfinite(out).all().item()
+    log(f"pipelined decode {G} x B={B} ctx={ctx}: {ms:.2f} ms/call")
+    st.close()
+    return ms
+
+
+def time_decode(L, torch, model, B, ctx, steps, warmup):
+    import synth
+    from synth import device as sd
+    st = model.new_state(B, ctx + warmup + steps + 1)
+    cfg = model.cfg
+    fill_decode_state(torch, model, st, B, ctx)
     toks = torch.empty(warmup + steps, B, dtype=torch.int32, device="cuda")
     sd.fill_tensor_uniform_int(toks, 1, synth.TID_TOKENS + 100, cfg.vocab)
     model.workspace(B, B, st.max_seq)
@@ -345,6 +398,7 @@ def main():
     ap.add_argument("--decode-ctx", type=int, default=32768)
     ap.add_argument("--decode-steps", type=int, default=16)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-pipelined", action="store_true", help="skip the pass-pipelined decode")
     ap.add_argument("--long-seq", type=int, default=262144,
                     help="one chunked prefill of this many positions (0: skip)")
     ap.add_argument("--long-chunk", type=int, default=32768)
@@ -412,6 +466,15 @@ def main():
                             "batch": args.decode_batch, "context": args.decode_ctx,
                             "algorithmic_gb_per_step": round(tot / 1e9, 2), "achieved_gbs": round(gbs, 1),
                             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if not args.no_decode and not args.no_pipelined:
+        pms = time_decode_pipelined(L, torch, model, args.decode_batch, args.decode_ctx, args.decode_steps, 2)
+        ptot, pw, _, _ = decode_pipelined_bytes(NINE_B, args.decode_batch, args.decode_ctx)
+        pgbs = ptot / (pms / 1e3) / 1e9
+        result["decode_pipelined"] = {
+            "cohorts": NINE_B["n_passes"], "cohort_batch": args.decode_batch, "context": args.decode_ctx,
+            "ms_per_call": round(pms, 3), "tokens_per_s": round(args.decode_batch / (pms / 1e3), 1),
+            "algorithmic_gb_per_call": round(ptot / 1e9, 2), "weight_gb_per_call": round(pw / 1e9, 2),
+            "achieved_gbs": round(pgbs, 1), "hbm_frac": round(pgbs / PEAK_HBM_GBS, 4)}
     if args.long_seq > 0:
         lms = time_long_prefill(L, torch, model, args.long_seq, args.long_chunk)
         lf, lg, la, ll = prefill_flops(NINE_B, args.long_seq)
