@@ -29,7 +29,7 @@ enum { LOOP_MHC_ENTER = 0, LOOP_MHC_MID = 1, LOOP_MHC_EXIT = 2 };
  * [0, F) then up rows [F, 2F) (N = 2F) and C dtype [M][F] = silu(A.Bg^T) * (A.Bu^T).
  * bf16 with M > 64 needs K % 32 == 0 and N (F for SWIGLU) a multiple of 256
  * (128 for SWIGLU); bf16 with M <= 64 (the decode shape: the weights are
- * streamed once for up to 64 token rows) needs K % 256 == 0.
+ * streamed once for up to 64 token rows) needs K % 64 == 0.
  * For M <= 64, `scratch` of loop_op_gemm_bytes() bytes (device, caller-owned,
  * contents arbitrary) lets K be split over workgroups when the output tiles
  * alone cannot fill the device; the partial sums are added in a fixed order,

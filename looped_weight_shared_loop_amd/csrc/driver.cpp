@@ -472,10 +472,8 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
   // decode-shaped GEMMs split K over workgroups when the workspace holds the scratch
   auto run_gemm = [&](lk::GemmArgs g, bool may_defer = false) {
     g.ksplit = 1;
-    g.skinny_rb = 4;
     if (g.dt == lk::DT_BF16 && g.M <= 64) {
       const lk::SkinnyPlan p = lk::skinny_plan(g.epi, g.M, g.N, g.K, g.F, m->cu);
-      g.skinny_rb = p.rb;
       if (p.ksplit > 1 && p.bytes <= L.skinny_bytes) {
         g.ksplit = p.ksplit;
         g.part = (float*)(ws + L.skinny);
@@ -654,10 +652,8 @@ int decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_b
   lk::YPart ypend{};
   auto run_gemm = [&](lk::GemmArgs g, bool may_defer) {
     g.ksplit = 1;
-    g.skinny_rb = 4;
     if (g.dt == lk::DT_BF16 && g.M <= 64) {
       const lk::SkinnyPlan p = lk::skinny_plan(g.epi, g.M, g.N, g.K, g.F, m->cu);
-      g.skinny_rb = p.rb;
       if (p.ksplit > 1 && p.bytes <= L.skinny_bytes) {
         g.ksplit = p.ksplit;
         g.part = (float*)(ws + L.skinny);

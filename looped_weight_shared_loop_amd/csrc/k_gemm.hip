@@ -4,12 +4,15 @@
 //                (v_mfma_f32_32x32x16_bf16), global -> LDS DMA through five
 //                LDS stages, XCD-aware tile order.  fp32 accumulation.
 // * gemm_skinny: bf16, M <= 64 (decode): streams B (the weights) once for up to
-//                64 token rows; 64- or 128-row tiles, K split over 4 waves and, when the tiles cannot fill
+//                64 token rows; 128-row tiles whose 4 waves split the rows and share the
+//                token operand through LDS; K split, when the tiles cannot fill
 //                the device, over workgroups (partials summed in index order
 //                by a second kernel).
 // * gemm_f32:    fp32 configuration: LDS-tiled FMA kernel.
 // All share one epilogue: plain bf16/fp32 store, fp32 logits, the QKV split
 // that writes K and V into a per-(layer, pass) cache slot, or SwiGLU.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -237,27 +240,17 @@ __global__ __launch_bounds__(128 * WN_, 1) void gemm_dma_kernel(GemmArgs a) {
 }
 
 // ------------------------------------------------------------------ skinny (M <= 64)
-// Decode shape: the weights B are streamed once, the <= 64 activation rows
-// (one or two blocks of 32 tokens) are the MFMA's other operand.  A workgroup
-// owns a tile of R = 32 RB B rows (SwiGLU: R/2 gate rows and the R/2 matching
-// up rows) and 1/ksplit of K; its 4 waves split that K range again.  Wave
-// operands for v_mfma_f32_32x32x16_bf16: A = B rows (lane l: row l & 31),
-// B = tokens (lane l: token l & 31 of each block); every weight fragment
-// loaded feeds both token blocks.  Per 64-wide k step
-// lane half h = l >> 5 loads 64 contiguous bytes (k + 32 h .. k + 32 h + 31) of
-// its row, so each row's 128 B line is fetched whole; MFMA j contracts chunk j
-// of both halves, and both operands use the same k order, which leaves the
-// dot products unchanged.  The four waves are reduced in LDS in a fixed order.
+// Decode shape: the weights are streamed once; the <= 64 token rows (one or two
+// blocks of 32) are the MFMA's other operand (gemm_skinny_rs_kernel below).
 // ksplit == 1: the workgroup applies the epilogue.  ksplit > 1: it stores its
 // fp32 partial tile and gemm_skinny_reduce (the next kernel on the stream, so
 // the kernel boundary orders the partials) adds the ksplit partials in index
 // order and applies the epilogue: results do not depend on scheduling.
 constexpr int SK_THREADS = 256;
 
-// Tile height: 64 rows (two waves per SIMD fit) unless the 128-row tiles alone
-// give four workgroups per CU (the head), where the wider A reuse wins.  K is
-// split in powers of two (at most 16) while the grid has fewer than two
-// workgroups per CU and each wave keeps at least 256 of K.
+// Tiles of 128 weight rows (SwiGLU: 64 output columns).  K is split in powers
+// of two (at most 16) while the grid has fewer than two workgroups per CU and
+// each workgroup keeps at least eight 64-wide k steps.
 SkinnyPlan skinny_plan(int epi, int M, int N, int K, int F, int cu) {
   SkinnyPlan p{};
   auto tiles_of = [&](int rb) {
@@ -265,38 +258,14 @@ SkinnyPlan skinny_plan(int epi, int M, int N, int K, int F, int cu) {
     return (epi == EPI_SWIGLU) ? (F + rows / 2 - 1) / (rows / 2) : (N + rows - 1) / rows;
   };
   p.tb = M > 32 ? 2 : 1;
-  p.rb = (p.tb == 1 && (long)tiles_of(4) >= 4L * cu) ? 4 : 2;
+  p.rb = 4;
   p.tiles = tiles_of(p.rb);
   p.ksplit = 1;
   while (p.ksplit < 16 && (long)p.tiles * p.ksplit < 2L * cu && K % (p.ksplit * 2 * 4 * 64) == 0 &&
-         K / (p.ksplit * 2 * 4) >= 256)
+         K / (p.ksplit * 2) >= 512)
     p.ksplit *= 2;
   if (p.ksplit > 1) p.bytes = (size_t)p.tiles * p.ksplit * 32 * p.tb * 32 * p.rb * sizeof(float);
   return p;
-}
-
-template <int RB, int TB>
-DEV void sk_load(const bf16_t* const* Bp, const bf16_t* const* Ap, const bool* tok_ok, int k, u32x4_t (&bw)[RB][4],
-                 u32x4_t (&xw)[TB][4]) {
-  const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) bw[rb][j] = ldv4(Bp[rb] + k + j * 8);
-#pragma unroll
-  for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xw[tb][j] = tok_ok[tb] ? ldv4(Ap[tb] + k + j * 8) : zero;
-}
-
-template <int RB, int TB>
-DEV void sk_mma(const u32x4_t (&bw)[RB][4], const u32x4_t (&xw)[TB][4], f32x16_t (&acc)[TB][RB]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int tb = 0; tb < TB; ++tb) acc[tb][rb] = mfma32(as_bf16x8(bw[rb][j]), as_bf16x8(xw[tb][j]), acc[tb][rb]);
 }
 
 template <int EPI, int RB>
@@ -308,106 +277,6 @@ DEV void sk_epilogue(const GemmArgs& a, int tile, int m, int j, float v, float v
   } else {
     const int col = tile * R + j;
     if (col < a.N) epi_one<bf16_t, EPI>(a, m, col, v);
-  }
-}
-
-template <int EPI, int RB, int D, int TB>
-__global__ __launch_bounds__(SK_THREADS) void gemm_skinny_kernel(GemmArgs a) {
-  constexpr int R = 32 * RB, TOK = 32 * TB;
-  __shared__ float red[2][TOK][R + 1];     // [slot][token][tile row]
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int ks = a.ksplit;
-  const int tile = blockIdx.x / ks, kpart = blockIdx.x - tile * ks;
-  const int r = lane & 31, h = lane >> 5;
-  const int Kw = a.K / (ks * 4);
-  const int kbeg = (kpart * 4 + wid) * Kw + h * 32;
-  const bf16_t* Bp[RB];
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    int n;
-    if (EPI == EPI_SWIGLU) {
-      const int j = tile * (R / 2) + (rb % (RB / 2)) * 32 + r;       // output column
-      n = j < a.F ? ((rb < RB / 2) ? j : a.F + j) : 0;
-    } else {
-      n = tile * R + rb * 32 + r;
-      n = n < a.N ? n : 0;
-    }
-    Bp[rb] = (const bf16_t*)a.B + (size_t)n * a.ldb + kbeg;
-  }
-  bool tok_ok[TB];
-  const bf16_t* Ap[TB];
-#pragma unroll
-  for (int tb = 0; tb < TB; ++tb) {
-    const int t = tb * 32 + r;
-    tok_ok[tb] = t < a.M;
-    Ap[tb] = (const bf16_t*)a.A + (size_t)(tok_ok[tb] ? t : 0) * a.lda + kbeg;
-  }
-
-  f32x16_t acc[TB][RB];
-#pragma unroll
-  for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[tb][rb][i] = 0.f;
-  // D register sets: the loads of the next D steps of 64 are in flight while a
-  // step's MFMAs run.  The launch guarantees Kw / 64 is a positive multiple of
-  // D, so the steady loop refills every set unconditionally and the last D
-  // steps drain without loads (no branch inside the pipeline).
-  u32x4_t bw[D][RB][4], xw[D][TB][4];
-#pragma unroll
-  for (int d = 0; d < D; ++d) sk_load<RB, TB>(Bp, Ap, tok_ok, d * 64, bw[d], xw[d]);
-  for (int k = 0; k + D * 64 < Kw; k += D * 64) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      sk_mma<RB, TB>(bw[d], xw[d], acc);
-      sk_load<RB, TB>(Bp, Ap, tok_ok, k + (D + d) * 64, bw[d], xw[d]);
-    }
-  }
-#pragma unroll
-  for (int d = 0; d < D; ++d) sk_mma<RB, TB>(bw[d], xw[d], acc);
-
-  // acc[tb][rb][i]: tile row rb*32 + (i/4)*8 + h*4 + i%4, token 32 tb + r.
-  // Sum the waves as (w0 + w2) + (w1 + w3).
-  auto put = [&](int slot) {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) red[slot][tb * 32 + r][rb * 32 + (i >> 2) * 8 + h * 4 + (i & 3)] = acc[tb][rb][i];
-  };
-  auto add = [&](int slot) {
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[tb][rb][i] += red[slot][tb * 32 + r][rb * 32 + (i >> 2) * 8 + h * 4 + (i & 3)];
-  };
-  if (wid >= 2) put(wid - 2);
-  __syncthreads();
-  if (wid < 2) add(wid);
-  __syncthreads();
-  if (wid == 1) put(0);
-  __syncthreads();
-  if (wid == 0) { add(0); put(0); }
-  __syncthreads();
-
-  // element e of the tile: token e / R, tile row e % R (coalesced along rows)
-  const int M = a.M;
-  if (ks > 1) {
-    float* mine = a.part + (size_t)blockIdx.x * TOK * R;
-    for (int e = tid; e < M * R; e += SK_THREADS) mine[e] = red[0][e / R][e % R];
-    return;
-  }
-  if (EPI == EPI_SWIGLU) {
-    constexpr int H = R / 2;
-    for (int e = tid; e < M * H; e += SK_THREADS)
-      sk_epilogue<EPI, RB>(a, tile, e / H, e % H, red[0][e / H][e % H], red[0][e / H][H + e % H]);
-  } else {
-    for (int e = tid; e < M * R; e += SK_THREADS)
-      sk_epilogue<EPI, RB>(a, tile, e / R, e % R, red[0][e / R][e % R], 0.f);
   }
 }
 
@@ -432,23 +301,156 @@ __global__ __launch_bounds__(256) void gemm_skinny_reduce(GemmArgs a) {
   sk_epilogue<EPI, RB>(a, tile, m, j, v, vup);
 }
 
-template <int EPI, int RB, int TB>
-static hipError_t launch_skinny(const GemmArgs& a, hipStream_t s) {
-  constexpr int R = 32 * RB;
-  const int tiles = (EPI == EPI_SWIGLU) ? (a.F + R / 2 - 1) / (R / 2) : (a.N + R - 1) / R;
-  // steps of 64 per wave (K % (ksplit * 4 * 64) == 0 is checked by the caller)
-  const int steps = a.K / (a.ksplit * 4 * 64);
-  // four steps in flight fit the registers only with 64 weight rows and 32 tokens
-  constexpr int DEEP = (RB == 2 && TB == 1) ? 4 : 2;
-  if (steps % DEEP == 0)
-    gemm_skinny_kernel<EPI, RB, DEEP, TB><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
-  else if (steps % 2 == 0)
-    gemm_skinny_kernel<EPI, RB, 2, TB><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
-  else
-    gemm_skinny_kernel<EPI, RB, 1, TB><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
+// ------------------------------------------------------------------ skinny, row split
+// Decode shape with the token operand shared: a workgroup owns 128 weight rows
+// (SwiGLU: 64 gate and the 64 matching up rows) and a k range; each of its four
+// waves owns one 32-row MFMA block (SwiGLU: 16 gate rows, then their 16 up
+// rows) over the whole range, so all four read the same token operand, which
+// moves global -> LDS once per 64-k step (DMA into a ring of D + 1 stages).
+// The weight rows stream into registers D steps ahead, as in the kernel above,
+// with the same k order inside a step (lane half h: k + 32 h .. + 31; MFMA j
+// takes chunk j of both halves, the token fragment the same chunks).
+// Token rows [TOK][64 k] in LDS: 16-byte unit c of row t at c ^ ((t >> 1) & 7).
+// ksplit > 1: fp32 partial tiles [blockIdx][TOK][128] in the logical column
+// order (SwiGLU: gate columns, then up columns), read by gemm_skinny_reduce<.., 4, TB>
+// or a YPart consumer; ksplit == 1: the epilogue is applied directly.
+template <int EPI, int TB, int D>
+__global__ __launch_bounds__(SK_THREADS) void gemm_skinny_rs_kernel(GemmArgs a) {
+  constexpr int R = 128, TOK = 32 * TB, NS = D + 1;
+  constexpr int RING = NS * TOK * 64 * 2, STAGE_OUT = TOK * (R + 1) * 4;
+  __shared__ __align__(16) char lds[RING > STAGE_OUT ? RING : STAGE_OUT];
+  bf16_t* As = (bf16_t*)lds;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int ks = a.ksplit;
+  const int tile = blockIdx.x / ks, kpart = blockIdx.x - tile * ks;
+  const int r = lane & 31, h = lane >> 5;
+  const int Kw = a.K / ks, kb = kpart * Kw;
+  const int nsteps = Kw / 64;
+  int n;
+  if (EPI == EPI_SWIGLU) {
+    const int j = tile * 64 + wid * 16 + (r & 15);                  // output column
+    n = j < a.F ? (r < 16 ? j : a.F + j) : 0;
+  } else {
+    n = tile * R + wid * 32 + r;
+    n = n < a.N ? n : 0;
+  }
+  const bf16_t* Bp = (const bf16_t*)a.B + (size_t)n * a.ldb + kb + h * 32;
+  // token DMA: per step TOK rows of 128 B = 4 TB blocks of 8 rows; wave w
+  // issues blocks w + 4 i.  Lane l of a block writes LDS unit l % 8 of row
+  // 8 blk + l / 8, so it fetches the global unit the swizzle puts there.
+  const bf16_t* Ag[TB];
+  int Al[TB];
+#pragma unroll
+  for (int i = 0; i < TB; ++i) {
+    const int blk = wid + 4 * i, t = 8 * blk + (lane >> 3);
+    const int c = (lane & 7) ^ ((t >> 1) & 7);
+    Ag[i] = (const bf16_t*)a.A + (size_t)min(t, a.M - 1) * a.lda + kb + c * 8;
+    Al[i] = blk * 512;
+  }
+  u32x4_t bw[D][4];
+  auto issue = [&](int st, u32x4_t (&w)[4]) {      // weights and tokens of step st
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = ldv4(Bp + st * 64 + j * 8);
+    bf16_t* dst = As + (st % NS) * (TOK * 64);
+#pragma unroll
+    for (int i = 0; i < TB; ++i)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Ag[i] + st * 64),
+                                       (void __attribute__((address_space(3)))*)(dst + Al[i]), 16, 0, 0);
+  };
+  f32x16_t acc[TB];
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[tb][i] = 0.f;
+  auto sync = [&]() {
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+  auto compute = [&](int st, const u32x4_t (&w)[4]) {
+    const bf16_t* src = As + (st % NS) * (TOK * 64);
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int t = tb * 32 + r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const u32x4_t x = ldv4(src + t * 64 + (((4 * h + j) ^ ((t >> 1) & 7)) << 3));
+        acc[tb] = mfma32(as_bf16x8(w[j]), as_bf16x8(x), acc[tb]);
+      }
+    }
+  };
+  // Group of step st = 4 weight loads then TB token DMAs.  Waiting until at
+  // most (D - 1 - q) groups are outstanding lands the oldest one; the barrier
+  // then makes every wave's token rows of that step visible, and also orders
+  // all reads of step st - 1 before the DMA that refills its stage.
+  constexpr int GS = 4 + TB;
+  static_assert(GS * (D - 1) <= 63, "vmcnt range");
+  auto wait_groups = [&](auto q) {
+    constexpr int N = GS * (D - 1 - decltype(q)::value);
+    asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d, bw[d]);
+  int st = 0;
+  for (; st + D < nsteps; st += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      wait_groups(std::integral_constant<int, 0>{});
+      sync();
+      compute(st + d, bw[d]);
+      issue(st + d + D, bw[d]);    // stage of step st + d - 1, read before the barrier above
+    }
+  }
+  // last D steps: no more loads, the outstanding groups drain one by one
+  wait_groups(std::integral_constant<int, 0>{}); sync(); compute(st, bw[0]);
+  if constexpr (D > 1) { wait_groups(std::integral_constant<int, 1>{}); sync(); compute(st + 1, bw[1]); }
+  if constexpr (D > 2) { wait_groups(std::integral_constant<int, 2>{}); sync(); compute(st + 2, bw[2]); }
+  if constexpr (D > 3) { wait_groups(std::integral_constant<int, 3>{}); sync(); compute(st + 3, bw[3]); }
+  static_assert(D <= 4, "drain above");
+
+  // accumulators -> LDS in the logical column order, then coalesced output
+  sync();                              // every wave is done with the token ring
+  float* out = (float*)lds;            // [TOK][R + 1]
+#pragma unroll
+  for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int wr = (i >> 2) * 8 + h * 4 + (i & 3);      // row inside the wave's block
+      int col;
+      if (EPI == EPI_SWIGLU) col = wr < 16 ? wid * 16 + wr : 64 + wid * 16 + (wr - 16);
+      else col = wid * 32 + wr;
+      out[(tb * 32 + r) * (R + 1) + col] = acc[tb][i];
+    }
+  __syncthreads();
+  const int M = a.M;
+  if (ks > 1) {
+    float* mine = a.part + (size_t)blockIdx.x * TOK * R;
+    for (int e = tid; e < M * R; e += SK_THREADS) mine[e] = out[(e / R) * (R + 1) + e % R];
+    return;
+  }
+  if (EPI == EPI_SWIGLU) {
+    for (int e = tid; e < M * 64; e += SK_THREADS) {
+      const int t = e / 64, j = e % 64, col = tile * 64 + j;
+      if (col < a.F)
+        st1((bf16_t*)a.C + (size_t)t * a.ldc + col, silu(out[t * (R + 1) + j]) * out[t * (R + 1) + 64 + j]);
+    }
+  } else {
+    for (int e = tid; e < M * R; e += SK_THREADS) {
+      const int t = e / R, j = e % R, col = tile * R + j;
+      if (col < a.N) epi_one<bf16_t, EPI>(a, t, col, out[t * (R + 1) + j]);
+    }
+  }
+}
+
+template <int EPI, int TB>
+static hipError_t launch_skinny_rs(const GemmArgs& a, hipStream_t s) {
+  const int tiles = (EPI == EPI_SWIGLU) ? (a.F + 63) / 64 : (a.N + 127) / 128;
+  const int steps = a.K / (a.ksplit * 64);
+  if (steps % 4 == 0) gemm_skinny_rs_kernel<EPI, TB, 4><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
+  else if (steps % 2 == 0) gemm_skinny_rs_kernel<EPI, TB, 2><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
+  else gemm_skinny_rs_kernel<EPI, TB, 1><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
   if (a.ksplit > 1 && !(a.defer_reduce && EPI == EPI_STORE)) {
-    const long outs = (long)a.M * tiles * (EPI == EPI_SWIGLU ? R / 2 : R);
-    gemm_skinny_reduce<EPI, RB, TB><<<(int)((outs + 255) / 256), 256, 0, s>>>(a);
+    const long outs = (long)a.M * tiles * (EPI == EPI_SWIGLU ? 64 : 128);
+    gemm_skinny_reduce<EPI, 4, TB><<<(int)((outs + 255) / 256), 256, 0, s>>>(a);
   }
   return hipGetLastError();
 }
@@ -536,15 +538,9 @@ static hipError_t launch_dma(const GemmArgs& a, int blocks, hipStream_t s) {
 template <int EPI>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 64) {
-    if (a.ksplit < 1 || a.K % (a.ksplit * 4 * 64)) return hipErrorInvalidValue;
+    if (a.ksplit < 1 || a.K % (a.ksplit * 64)) return hipErrorInvalidValue;
     if (a.ksplit > 1 && !a.part) return hipErrorInvalidValue;
-    if (a.M > 32) {
-      if (a.skinny_rb == 2) return launch_skinny<EPI, 2, 2>(a, s);
-      return hipErrorInvalidValue;
-    }
-    if (a.skinny_rb == 2) return launch_skinny<EPI, 2, 1>(a, s);
-    if (a.skinny_rb == 4) return launch_skinny<EPI, 4, 1>(a, s);
-    return hipErrorInvalidValue;
+    return a.M > 32 ? launch_skinny_rs<EPI, 2>(a, s) : launch_skinny_rs<EPI, 1>(a, s);
   }
   if (a.K % DBK) return hipErrorInvalidValue;
   if ((long)TBM * a.lda >= (1L << 31) || (long)(EPI == EPI_SWIGLU ? 2 * a.F : a.N) * a.ldb >= (1L << 31))

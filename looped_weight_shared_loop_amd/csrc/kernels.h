@@ -75,13 +75,12 @@ struct GemmArgs {
   // M <= 64: split-K plan (skinny_plan) and its scratch; ksplit 1 needs none.
   int ksplit;
   int defer_reduce;      // ksplit > 1: leave the partials for the consumer (YPart)
-  int skinny_rb;         // 32-row blocks per tile (2 or 4; 2 when M > 32)
-  float* part;           // [tiles * ksplit][32 tb][32 * skinny_rb] fp32 partial sums, tb = M > 32 ? 2 : 1
+  float* part;           // [tiles * ksplit][32 tb][128] fp32 partial sums, tb = M > 32 ? 2 : 1
 };
 hipError_t gemm(const GemmArgs& a, hipStream_t s);
 
-// Decode-shaped (M <= 64) GEMM plan: 32 rb weight rows per workgroup tile
-// (SwiGLU: half gate, half up rows) against tb = 1 or 2 blocks of 32 token
+// Decode-shaped (M <= 64) GEMM plan: 32 rb = 128 weight rows per workgroup
+// tile (SwiGLU: 64 gate and 64 up rows) against tb = 1 or 2 blocks of 32 token
 // rows, K split over `ksplit` workgroups when the tiles alone cannot fill the
 // device.  `bytes` = partial sums (0 when ksplit == 1).
 struct SkinnyPlan { int rb, tb, tiles, ksplit; size_t bytes; };

@@ -53,10 +53,8 @@ int loop_op_gemm(int dtype, int epi, int M, int N, int K, const void* A, long ld
   g.dt = dt; g.epi = epi; g.M = M; g.N = N; g.K = K; g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.C = C; g.ldc = ldc;
   g.F = F;
   g.ksplit = 1;
-  g.skinny_rb = 4;
   if (dt == lk::DT_BF16 && M > 0 && M <= 64) {
     const lk::SkinnyPlan p = lk::skinny_plan(epi, M, N, K, F, lk::device_cu_count());
-    g.skinny_rb = p.rb;
     if (p.ksplit > 1 && scratch) {
       if (scratch_bytes < p.bytes)
         return lp_fail(LOOP_ERR_WORKSPACE, "gemm scratch %zu bytes, needs %zu", scratch_bytes, p.bytes);
