@@ -302,6 +302,119 @@ __global__ __launch_bounds__(512) void mhc_kernel(MhcArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ mHC, few tokens, channel split
+// Decode-sized calls (T <= 64 tokens): one wave per (512-channel slice, token)
+// instead of one workgroup per token, so a site fills the device.
+//  A: the write-back (or the stream entry) of its slice, then the slice's
+//     share of the 8 projections and of the three stream sums, stored to
+//     part[t][slice][11];
+//  B: the slices' shares summed in slice order, the maps (every wave of the
+//     token computes them; slice 0 stores them), then u for its slice from
+//     the X' that A wrote (the kernel boundary orders the two).
+constexpr int MHC_SLICE = 512;
+
+DEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void mhc_slice_a(MhcArgs a, float* __restrict__ part) {
+  const int C = a.C, nsl = C / MHC_SLICE;
+  const int sl = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
+  const int c0 = sl * MHC_SLICE + lane * 8;
+  T* X = (T*)a.X;
+  const T* y = (const T*)a.y;
+  float x0[8], x1[8];
+  if (a.mode == MHC_ENTER) {
+    ld8((const T*)a.h + (size_t)t * C + c0, x0);
+    if (y || a.yp.part) {
+      float yv[8];
+      ld8_y(y, a.yp, t, C, c0, yv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x0[e] = round_to(x0[e] + yv[e], (T*)nullptr);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x1[e] = x0[e];
+  } else {
+    float p[8], q[8], yv[8];
+    ld8(X + ((size_t)t * 2) * C + c0, p);
+    ld8(X + ((size_t)t * 2 + 1) * C + c0, q);
+    ld8_y(y, a.yp, t, C, c0, yv);
+    const float* mi = a.maps_in + (size_t)t * 8;
+    const float po0 = mi[2], po1 = mi[3], r00 = mi[4], r01 = mi[5], r10 = mi[6], r11 = mi[7];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x0[e] = round_to(r00 * p[e] + r01 * q[e] + po0 * yv[e], (T*)nullptr);
+      x1[e] = round_to(r10 * p[e] + r11 * q[e] + po1 * yv[e], (T*)nullptr);
+    }
+  }
+  st8(X + ((size_t)t * 2) * C + c0, x0);
+  st8(X + ((size_t)t * 2 + 1) * C + c0, x1);
+  float acc[11];
+  acc[0] = acc[1] = acc[2] = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    acc[0] += x0[e] * x0[e];
+    acc[1] += x1[e] * x1[e];
+    acc[2] += x0[e] * x1[e];
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    float w0[8], w1[8];
+    ld8(a.w + (size_t)j * 2 * C + c0, w0);
+    ld8(a.w + (size_t)j * 2 * C + C + c0, w1);
+    float sj = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sj += w0[e] * x0[e] + w1[e] * x1[e];
+    acc[3 + j] = sj;
+  }
+#pragma unroll
+  for (int i = 0; i < 11; ++i) acc[i] = wave_sum(acc[i]);
+  if (lane < 11) {
+    float v = acc[0];
+#pragma unroll
+    for (int i = 1; i < 11; ++i) v = lane == i ? acc[i] : v;
+    part[((size_t)t * nsl + sl) * 11 + lane] = v;
+  }
+}
+
+template <typename T>
+__global__ __launch_bounds__(64) void mhc_slice_b(MhcArgs a, const float* __restrict__ part) {
+  const int C = a.C, nsl = C / MHC_SLICE;
+  const int sl = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
+  const int c0 = sl * MHC_SLICE + lane * 8;
+  float acc[11];
+#pragma unroll
+  for (int i = 0; i < 11; ++i) acc[i] = 0.f;
+  for (int q = 0; q < nsl; ++q) {
+    const float* pq = part + ((size_t)t * nsl + q) * 11;
+#pragma unroll
+    for (int i = 0; i < 11; ++i) acc[i] += pq[i];
+  }
+  const float inv = 1.0f / sqrtf((acc[0] + acc[1]) / (float)(2 * C) + a.eps);
+  float l[8], m[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) l[j] = acc[3 + j] * inv + a.b[j];
+  mhc_maps_from_logits(l, a.iters, m);
+  if (sl == 0 && lane == 0) {
+    float* mo = a.maps_out + (size_t)t * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mo[j] = m[j];
+  }
+  const float p0 = m[0], p1 = m[1];
+  const float ssin = p0 * p0 * acc[0] + 2.f * p0 * p1 * acc[2] + p1 * p1 * acc[1];
+  const float invu = 1.0f / sqrtf(fmaxf(ssin, 0.f) / (float)C + a.eps);
+  float x0[8], x1[8], g[8], o[8];
+  ld8((const T*)a.X + ((size_t)t * 2) * C + c0, x0);
+  ld8((const T*)a.X + ((size_t)t * 2 + 1) * C + c0, x1);
+  ld8(a.gamma + c0, g);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = g[e] * (p0 * x0[e] + p1 * x1[e]) * invu;
+  st8((T*)a.u + (size_t)t * C + c0, o);
+}
+
 // ------------------------------------------------------------------ mHC, MFMA (bf16)
 // For bf16 streams the 8 projections l = W vec(X') run on the matrix cores:
 // W (float32 [8][2C]) is split once per call into W_hi = bf16(W) and
@@ -496,7 +609,8 @@ hipError_t mhc(const MhcArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   if (a.C % 8 || a.C / 8 > 512) return hipErrorInvalidValue;
   // 16-token tiles on the matrix cores pay off once there are enough tiles;
-  // fewer tokens (decode) take one workgroup per token with W in registers
+  // decode-sized calls split the channels over waves (below); otherwise one
+  // workgroup per token with W in registers
   if (a.dt == DT_BF16 && a.mode != MHC_EXIT && a.C % 256 == 0 && a.wsplit && a.T >= MHC_MFMA_MIN_T) {
     if (a.yp.part) return hipErrorInvalidValue;   // the tiled path reads y itself
     const int n = 8 * 2 * a.C;
@@ -519,6 +633,19 @@ hipError_t mhc(const MhcArgs& a, hipStream_t s) {
     const int per_wg = (ntiles + grid - 1) / grid;
     grid = (ntiles + per_wg - 1) / per_wg;
     mhc_mfma_kernel<<<grid, 512, 0, s>>>(a, a.wsplit);
+    return hipGetLastError();
+  }
+  // few tokens: one wave per (512-channel slice, token), partial sums in the scratch
+  if (a.mode != MHC_EXIT && a.C % MHC_SLICE == 0 && a.T <= 64 && a.wsplit) {
+    float* part = (float*)a.wsplit;     // T * (C / 512) * 11 floats <= 16 * 2C bf16 for T <= 64
+    const dim3 grid(a.C / MHC_SLICE, a.T);
+    if (a.dt == DT_BF16) {
+      mhc_slice_a<bf16_t><<<grid, 64, 0, s>>>(a, part);
+      mhc_slice_b<bf16_t><<<grid, 64, 0, s>>>(a, part);
+    } else {
+      mhc_slice_a<float><<<grid, 64, 0, s>>>(a, part);
+      mhc_slice_b<float><<<grid, 64, 0, s>>>(a, part);
+    }
     return hipGetLastError();
   }
   const int nv = a.C / 8;
