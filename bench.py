@@ -254,12 +254,22 @@ def time_decode_pipelined(L, torch, model, B, ctx, calls, warmup):
     return ms
 
 
-def time_decode(L, torch, model, B, ctx, steps, warmup):
+def ragged_lengths(B, ctx):
+    """Per-sequence lengths of the ragged decode batch: spread over
+    [ctx / 2, ctx] by a fixed stride permutation (every length distinct)."""
+    half = ctx // 2
+    return [half + (b * 7919) % (half + 1) for b in range(B)]
+
+
+def time_decode(L, torch, model, B, ctx, steps, warmup, lengths=None):
     import synth
     from synth import device as sd
     st = model.new_state(B, ctx + warmup + steps + 1)
     cfg = model.cfg
     fill_decode_state(torch, model, st, B, ctx)
+    if lengths is not None:              # ragged: sequence b holds lengths[b] <= ctx positions
+        for b, n in enumerate(lengths):
+            st.set_seq_length(b, n)
     toks = torch.empty(warmup + steps, B, dtype=torch.int32, device="cuda")
     sd.fill_tensor_uniform_int(toks, 1, synth.TID_TOKENS + 100, cfg.vocab)
     model.workspace(B, B, st.max_seq)
@@ -276,7 +286,7 @@ def time_decode(L, torch, model, B, ctx, steps, warmup):
     ms = e0.elapsed_time(e1) / steps
     st.check()
     assert torch.isfinite(out).all().item()
-    log(f"decode B={B} ctx={ctx}: {ms:.2f} ms/step")
+    log(f"decode B={B} ctx={ctx}{' ragged' if lengths else ''}: {ms:.2f} ms/step")
     st.close()
     return ms
 
@@ -466,6 +476,18 @@ def main():
                             "batch": args.decode_batch, "context": args.decode_ctx,
                             "algorithmic_gb_per_step": round(tot / 1e9, 2), "achieved_gbs": round(gbs, 1),
                             "hbm_frac": round(gbs / PEAK_HBM_GBS, 4)}
+    if not args.no_decode:
+        lens = ragged_lengths(args.decode_batch, args.decode_ctx)
+        rms = time_decode(L, torch, model, args.decode_batch, args.decode_ctx, args.decode_steps, 3, lens)
+        _, w, _, lin = decode_bytes(NINE_B, args.decode_batch, args.decode_ctx)
+        _, _, kv1, _ = decode_bytes(NINE_B, 1, 1)             # K and V bytes of one position, all full slots
+        rtot = w + lin + kv1 * sum(lens)
+        rgbs = rtot / (rms / 1e3) / 1e9
+        result["decode_ragged"] = {"tokens_per_s": round(args.decode_batch / (rms / 1e3), 1),
+                                   "ms_per_step": round(rms, 3), "batch": args.decode_batch,
+                                   "lengths": f"{min(lens)}..{max(lens)}, mean {sum(lens) / len(lens):.0f}",
+                                   "algorithmic_gb_per_step": round(rtot / 1e9, 2), "achieved_gbs": round(rgbs, 1),
+                                   "hbm_frac": round(rgbs / PEAK_HBM_GBS, 4)}
     if not args.no_decode and not args.no_pipelined:
         pms = time_decode_pipelined(L, torch, model, args.decode_batch, args.decode_ctx, args.decode_steps, 2)
         ptot, pw, _, _ = decode_pipelined_bytes(NINE_B, args.decode_batch, args.decode_ctx)

@@ -138,8 +138,9 @@ int loop_model_schedule(const loop_model* m, int max, int* layer, int* pass, int
  * and V^T [batch][Hkv][d][S_max] (dtype), then per linear execution
  * S [batch][Hkv][d][d] and z [batch][Hkv][d] (float32), then the parked
  * cohorts of loop_decode_pipelined (X [batch][2][C], y [batch][C] in dtype,
- * maps [batch][8] float32); regions start on 256-byte boundaries; S_max is
- * max_seq rounded up to a multiple of 64. */
+ * maps [batch][8] float32), then the start positions of a ragged decode step
+ * (int32 [batch]); regions start on 256-byte boundaries; S_max is max_seq
+ * rounded up to a multiple of 64. */
 int loop_state_bytes(const loop_model* m, int batch, int max_seq, size_t* bytes);
 
 /* Device bytes of the workspace for one call over up to `max_tokens` new
@@ -153,10 +154,29 @@ int loop_workspace_bytes(const loop_model* m, int batch, int max_tokens, int max
  * loop_state_check(). */
 int loop_state_create(const loop_model* m, void* state_dev, size_t bytes, int batch, int max_seq, loop_state** out);
 int loop_state_destroy(loop_state* st);
+/* Every sequence of a state has its own length (the positions its KV caches
+ * and linear states hold).  Sequences of one state may differ (a ragged
+ * batch): loop_prefill_rows fills a subset, and loop_decode_step advances
+ * each sequence from its own length.  Ragged serving is the gap one page
+ * names for shared-weight loops ("SenseTime Open-Sources Loop-9B: Same
+ * Layers, Run Twice" (nvdium.com), its closing paragraphs on costs); the
+ * caches stay one contiguous slot per sequence (no paging).
+ *
+ * loop_state_length: the shortest sequence's length (the common length when
+ * all agree).  loop_state_seq_length: sequence `seq`'s length. */
 int loop_state_length(const loop_state* st, int* length);
-/* Declares that every sequence holds `length` valid positions (for example
- * after filling the regions directly); 0 <= length <= max_seq. */
+int loop_state_seq_length(const loop_state* st, int seq, int* length);
+/* Declares that every sequence (loop_state_set_length) or sequence `seq`
+ * (loop_state_set_seq_length) holds `length` valid positions, for example
+ * after filling the regions directly; 0 <= length <= max_seq.  Only the KV
+ * caches are indexed by position: a linear-attention state holds every
+ * position it has taken in, so a shorter length is only consistent once the
+ * caller has restored those regions (or with length 0, which the next
+ * prefill starts from).  Either call resets loop_decode_pipelined (tokens in
+ * flight are dropped).  Errors: INVALID_ARG (seq outside [0, batch)),
+ * CAPACITY. */
 int loop_state_set_length(loop_state* st, int length);
+int loop_state_set_seq_length(loop_state* st, int seq, int length);
 /* Device pointer and byte size of one region of the state: kind 0 = K, 1 = V^T
  * (slot = full-attention execution index), 2 = S, 3 = z (slot = linear
  * execution index), 4 = header (slot ignored; word 0 = error flags). */
@@ -170,15 +190,28 @@ int loop_state_check(loop_state* st, void* stream);
  * out_dev: float32 logits [B][V] (last position), [B][S][V] with
  * LOOP_ALL_LOGITS, or dtype h [B][S][C] with LOOP_HIDDEN_OUT.
  * Without LOOP_CONTINUE the sequences restart at position 0; with it they
- * continue at the state's length.  The state's length grows by S.
- * Errors: INVALID_ARG, ALIGN, CAPACITY, WORKSPACE, HIP. */
+ * continue at their length, which must be the same for all B (else STATE).
+ * Each sequence's length becomes its start position + S.
+ * Errors: INVALID_ARG, ALIGN, CAPACITY, WORKSPACE, STATE, HIP. */
 int loop_prefill(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes,
                  const int32_t* tokens_dev, const void* embeds_dev, int B, int S,
                  unsigned flags, void* out_dev, void* stream);
+/* loop_prefill over sequences [seq0, seq0 + B) of the state (their slots and
+ * lengths); the other sequences are untouched.  This is how a ragged batch is
+ * built: prompts of different lengths prefilled per group, then decoded
+ * together by loop_decode_step.  tokens/embeds/out are laid out as for
+ * loop_prefill with B rows.  Errors: as loop_prefill; INVALID_ARG when seq0
+ * lies outside [0, batch), CAPACITY when seq0 + B > batch. */
+int loop_prefill_rows(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, int seq0,
+                      const int32_t* tokens_dev, const void* embeds_dev, int B, int S,
+                      unsigned flags, void* out_dev, void* stream);
 
 /* One decode step: one new token per sequence, tokens_dev int32 [B]; logits
- * float32 [B][V].  Appends one position to every KV cache and updates every
- * linear state.  Errors: as loop_prefill, plus STATE when the state is empty. */
+ * float32 [B][V].  Sequence b in [0, B) takes its token at its own length
+ * (ragged batches allowed); appends one position to each of its KV caches
+ * and updates every linear state.  A ragged step first writes the B start
+ * positions into the state's position region (one small kernel launch).
+ * Errors: as loop_prefill, plus STATE when any of the B sequences is empty. */
 int loop_decode_step(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes,
                      const int32_t* tokens_dev, int B, float* logits_dev, void* stream);
 
@@ -209,7 +242,9 @@ int loop_decode_step(loop_model* m, loop_state* st, void* workspace, size_t ws_b
  * loop_workspace_bytes(m, n_passes x B, n_passes x B, max_seq).  While a
  * cohort has a token in flight, loop_prefill and loop_decode_step return
  * STATE; loop_state_set_length resets the pipeline (tokens in flight are
- * dropped).  loop_state_length reports the smallest cohort length.
+ * dropped).  Each cohort's sequences must share one length (else STATE when
+ * it enters); cohorts may differ.  A cohort's lengths grow when its token
+ * leaves, so loop_state_length reports the shortest cohort's length.
  * Errors: INVALID_ARG, SHAPE (batch != n_passes x B), ALIGN, CAPACITY,
  * WORKSPACE, STATE (nothing to run, a cohort not ready, or no prefill), HIP. */
 int loop_decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes,

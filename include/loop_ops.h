@@ -78,6 +78,16 @@ size_t loop_op_attention_decode_bytes(int B, int S, int Hq, int d, int S_max);
 int loop_op_attention_decode(int dtype, int B, int S, int pos0, int S_max, int Hq, int Hkv, int d, const void* q,
                              long ldq, const void* kcache, const void* vcache, void* out, long ldo, void* scratch,
                              size_t scratch_bytes, void* stream);
+/* loop_op_attention_decode for a ragged batch: sequence b's S new queries sit
+ * at positions pos_dev[b] .. pos_dev[b] + S - 1 (pos_dev: device int32 [B]).
+ * max_pos0 bounds every start (0 <= pos_dev[b] <= max_pos0, max_pos0 + S <=
+ * S_max): the split plan covers max_pos0 + S keys, and the kernels read each
+ * start clamped to [0, max_pos0], so no access leaves the slots even for
+ * starts outside that range (whose results are then not meaningful).  Same
+ * scratch as loop_op_attention_decode.  dtype float32 runs the scalar kernel. */
+int loop_op_attention_decode_ragged(int dtype, int B, int S, const int32_t* pos_dev, int max_pos0, int S_max, int Hq,
+                                    int Hkv, int d, const void* q, long ldq, const void* kcache, const void* vcache,
+                                    void* out, long ldo, void* scratch, size_t scratch_bytes, void* stream);
 
 /* Causal elu+1 linear attention for S new positions of B sequences from
  * qkv [B*S][ld] (q at column 0, k at Hq*d, v at (Hq+Hkv)*d), continuing the

@@ -68,10 +68,14 @@ SYMBOLS = {
     "loop_state_destroy": (c_int, [c_void_p]),
     "loop_state_length": (c_int, [c_void_p, POINTER(c_int)]),
     "loop_state_set_length": (c_int, [c_void_p, c_int]),
+    "loop_state_seq_length": (c_int, [c_void_p, c_int, POINTER(c_int)]),
+    "loop_state_set_seq_length": (c_int, [c_void_p, c_int, c_int]),
     "loop_state_region": (c_int, [c_void_p, c_int, c_int, POINTER(c_void_p), POINTER(c_size_t)]),
     "loop_state_check": (c_int, [c_void_p, c_void_p]),
     "loop_prefill": (c_int, [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_void_p, c_int, c_int,
                              c_uint, c_void_p, c_void_p]),
+    "loop_prefill_rows": (c_int, [c_void_p, c_void_p, c_void_p, c_size_t, c_int, c_void_p, c_void_p, c_int, c_int,
+                                  c_uint, c_void_p, c_void_p]),
     "loop_decode_step": (c_int, [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_int, c_void_p, c_void_p]),
     "loop_decode_pipelined": (c_int, [c_void_p, c_void_p, c_void_p, c_size_t, c_void_p, c_int, c_void_p, c_void_p,
                                       c_void_p]),
@@ -91,6 +95,9 @@ SYMBOLS = {
     "loop_op_attention_decode": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_void_p,
                                          ctypes.c_long, c_void_p, c_void_p, c_void_p, ctypes.c_long, c_void_p,
                                          c_size_t, c_void_p]),
+    "loop_op_attention_decode_ragged": (c_int, [c_int, c_int, c_int, c_void_p, c_int, c_int, c_int, c_int, c_int,
+                                                c_void_p, ctypes.c_long, c_void_p, c_void_p, c_void_p, ctypes.c_long,
+                                                c_void_p, c_size_t, c_void_p]),
     "loop_op_linear_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
     "loop_op_linear": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_void_p, ctypes.c_long,
                                c_void_p, c_void_p, c_int, c_void_p, ctypes.c_long, c_void_p, c_size_t, c_void_p]),
@@ -183,6 +190,16 @@ def loop_state_set_length(st, length: int) -> None:
     _check(lib().loop_state_set_length(st, length), "loop_state_set_length")
 
 
+def loop_state_seq_length(st, seq: int) -> int:
+    n = c_int()
+    _check(lib().loop_state_seq_length(st, seq, ctypes.byref(n)), "loop_state_seq_length")
+    return n.value
+
+
+def loop_state_set_seq_length(st, seq: int, length: int) -> None:
+    _check(lib().loop_state_set_seq_length(st, seq, length), "loop_state_set_seq_length")
+
+
 def loop_state_region(st, kind: int, slot: int):
     p = c_void_p()
     n = c_size_t()
@@ -198,6 +215,13 @@ def loop_prefill(m, st, ws_ptr: int, ws_bytes: int, tokens_ptr, embeds_ptr, B: i
                  out_ptr: int, stream: int) -> None:
     _check(lib().loop_prefill(m, st, c_void_p(ws_ptr), ws_bytes, c_void_p(tokens_ptr), c_void_p(embeds_ptr),
                               B, S, flags, c_void_p(out_ptr), c_void_p(stream)), "loop_prefill")
+
+
+def loop_prefill_rows(m, st, ws_ptr: int, ws_bytes: int, seq0: int, tokens_ptr, embeds_ptr, B: int, S: int,
+                      flags: int, out_ptr: int, stream: int) -> None:
+    _check(lib().loop_prefill_rows(m, st, c_void_p(ws_ptr), ws_bytes, seq0, c_void_p(tokens_ptr),
+                                   c_void_p(embeds_ptr), B, S, flags, c_void_p(out_ptr), c_void_p(stream)),
+           "loop_prefill_rows")
 
 
 def loop_decode_step(m, st, ws_ptr: int, ws_bytes: int, tokens_ptr: int, B: int, logits_ptr: int,
@@ -257,6 +281,13 @@ def loop_op_attention_decode(dtype, B, S, pos0, S_max, Hq, Hkv, d, q, ldq, k, v,
                              stream) -> None:
     _check(lib().loop_op_attention_decode(dtype, B, S, pos0, S_max, Hq, Hkv, d, _p(q), ldq, _p(k), _p(v), _p(out),
                                           ldo, _p(scratch), nbytes, _p(stream)), "loop_op_attention_decode")
+
+
+def loop_op_attention_decode_ragged(dtype, B, S, pos, max_pos0, S_max, Hq, Hkv, d, q, ldq, k, v, out, ldo, scratch,
+                                    nbytes, stream) -> None:
+    _check(lib().loop_op_attention_decode_ragged(dtype, B, S, _p(pos), max_pos0, S_max, Hq, Hkv, d, _p(q), ldq, _p(k),
+                                                 _p(v), _p(out), ldo, _p(scratch), nbytes, _p(stream)),
+           "loop_op_attention_decode_ragged")
 
 
 def loop_op_linear_bytes(B, S, Hkv, d) -> int:

@@ -66,23 +66,28 @@ struct loop_state {
   char* base;
   size_t bytes;
   int batch, max_seq, S_max;
-  int length;
+  std::vector<int> seq_len;     // positions each sequence holds (sequences may differ: ragged batch)
+  size_t pos_off = 0;           // int32 [batch] device copy of a ragged call's start positions
   std::vector<size_t> koff, voff, soff, zoff;
   // pipelined decode: cohort g holds sequences [g B, (g + 1) B), B = batch / n_passes.
   // A cohort between calls is parked in the looped block: its streams X, its
   // last sublayer output y and that site's maps (the pending write-back).
   size_t park_x = 0, park_y = 0, park_maps = 0;
   std::vector<int> pipe_next;   // pass the cohort runs at its next call; 0: no token in flight
-  std::vector<int> pipe_len;    // positions each cohort has completed
   int pipe_enter = 0;           // cohort whose token enters next
   bool pipe_idle() const {
     for (size_t g = 0; g < pipe_next.size(); ++g)
-      if (pipe_next[g] != 0 || pipe_len[g] != length) return false;
+      if (pipe_next[g] != 0) return false;
     return true;
   }
   void pipe_reset() {
-    for (size_t g = 0; g < pipe_next.size(); ++g) { pipe_next[g] = 0; pipe_len[g] = length; }
+    for (size_t g = 0; g < pipe_next.size(); ++g) pipe_next[g] = 0;
     pipe_enter = 0;
+  }
+  // shortest and longest length over sequences [s0, s0 + n)
+  void lengths(int s0, int n, int* mn, int* mx) const {
+    *mn = *mx = seq_len[s0];
+    for (int i = s0 + 1; i < s0 + n; ++i) { *mn = std::min(*mn, seq_len[i]); *mx = std::max(*mx, seq_len[i]); }
   }
 };
 
@@ -282,6 +287,9 @@ static void state_offsets(const loop_model* m, int batch, int max_seq, std::vect
   off += align256((size_t)batch * C * m->es);
   if (park) park[2] = off;
   off += align256((size_t)batch * 8 * sizeof(float));
+  // start positions of a ragged call, int32 [batch]
+  if (park) park[3] = off;
+  off += align256((size_t)batch * sizeof(int32_t));
   *total = off;
 }
 
@@ -305,7 +313,7 @@ int loop_state_create(const loop_model* m, void* state_dev, size_t bytes, int ba
   if (batch <= 0 || max_seq <= 0) return lp_fail(LOOP_ERR_INVALID_ARG, "batch and max_seq must be positive");
   if (misaligned(state_dev)) return lp_fail(LOOP_ERR_ALIGN, "state not 16-byte aligned");
   auto* st = new loop_state();
-  size_t need = 0, park[3] = {0, 0, 0};
+  size_t need = 0, park[4] = {0, 0, 0, 0};
   state_offsets(m, batch, max_seq, &st->koff, &st->voff, &st->soff, &st->zoff, &need, park);
   if (bytes < need) {
     delete st;
@@ -317,12 +325,12 @@ int loop_state_create(const loop_model* m, void* state_dev, size_t bytes, int ba
   st->batch = batch;
   st->max_seq = max_seq;
   st->S_max = (max_seq + 63) / 64 * 64;
-  st->length = 0;
+  st->seq_len.assign(batch, 0);
   st->park_x = park[0];
   st->park_y = park[1];
   st->park_maps = park[2];
+  st->pos_off = park[3];
   st->pipe_next.assign(m->cfg.n_passes, 0);
-  st->pipe_len.assign(m->cfg.n_passes, 0);
   *out = st;
   return LOOP_OK;
 }
@@ -334,14 +342,31 @@ int loop_state_destroy(loop_state* st) {
 
 int loop_state_length(const loop_state* st, int* length) {
   if (!st || !length) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
-  *length = st->length;
+  int mx;
+  st->lengths(0, st->batch, length, &mx);
   return LOOP_OK;
 }
 
 int loop_state_set_length(loop_state* st, int length) {
   if (!st) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
   if (length < 0 || length > st->max_seq) return lp_fail(LOOP_ERR_CAPACITY, "length %d outside [0, %d]", length, st->max_seq);
-  st->length = length;
+  st->seq_len.assign(st->batch, length);
+  st->pipe_reset();
+  return LOOP_OK;
+}
+
+int loop_state_seq_length(const loop_state* st, int seq, int* length) {
+  if (!st || !length) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (seq < 0 || seq >= st->batch) return lp_fail(LOOP_ERR_INVALID_ARG, "sequence %d outside [0, %d)", seq, st->batch);
+  *length = st->seq_len[seq];
+  return LOOP_OK;
+}
+
+int loop_state_set_seq_length(loop_state* st, int seq, int length) {
+  if (!st) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (seq < 0 || seq >= st->batch) return lp_fail(LOOP_ERR_INVALID_ARG, "sequence %d outside [0, %d)", seq, st->batch);
+  if (length < 0 || length > st->max_seq) return lp_fail(LOOP_ERR_CAPACITY, "length %d outside [0, %d]", length, st->max_seq);
+  st->seq_len[seq] = length;
   st->pipe_reset();
   return LOOP_OK;
 }
@@ -403,18 +428,30 @@ namespace {
     if (e_ != hipSuccess) return check_hip(e_, what);        \
   } while (0)
 
-int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, const int32_t* tokens,
+// Runs sequences [seq0, seq0 + B) of the state, S new positions each.  A
+// decode step takes every sequence at its own length (ragged rows read their
+// start positions from the state's device copy); a prefill starts the rows at
+// 0, or with LOOP_CONTINUE at their common length.
+int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, int seq0, const int32_t* tokens,
             const void* embeds, int B, int S, unsigned flags, void* out, hipStream_t s, bool decode) {
   const loop_config& c = m->cfg;
   if (!st || st->m != m) return lp_fail(LOOP_ERR_STATE, "state does not belong to this model");
   if (!workspace || !out || (!tokens && !embeds)) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
   if (B <= 0 || S <= 0) return lp_fail(LOOP_ERR_INVALID_ARG, "B and S must be positive");
   if (misaligned(workspace) || misaligned(out) || misaligned(embeds)) return lp_fail(LOOP_ERR_ALIGN, "misaligned buffer");
-  if (B > st->batch) return lp_fail(LOOP_ERR_CAPACITY, "batch %d exceeds the state's %d", B, st->batch);
-  if (decode && st->length == 0) return lp_fail(LOOP_ERR_STATE, "decode before prefill");
+  if (seq0 < 0 || seq0 >= st->batch) return lp_fail(LOOP_ERR_INVALID_ARG, "first sequence %d outside [0, %d)", seq0, st->batch);
+  if (B > st->batch - seq0)
+    return lp_fail(LOOP_ERR_CAPACITY, "sequences [%d, %d) exceed the state's %d", seq0, seq0 + B, st->batch);
   if (!st->pipe_idle())
-    return lp_fail(LOOP_ERR_STATE, "pipelined decode in progress (cohorts at different positions)");
-  const int pos0 = (decode || (flags & LOOP_CONTINUE)) ? st->length : 0;
+    return lp_fail(LOOP_ERR_STATE, "pipelined decode in progress (a cohort has a token in flight)");
+  int len_min, len_max;
+  st->lengths(seq0, B, &len_min, &len_max);
+  if (decode && len_min == 0) return lp_fail(LOOP_ERR_STATE, "decode before prefill");
+  if (!decode && (flags & LOOP_CONTINUE) && len_min != len_max)
+    return lp_fail(LOOP_ERR_STATE, "continued prefill over sequences of different lengths (%d..%d)", len_min, len_max);
+  // pos0: the (largest) first new position; ragged decode rows read their own
+  const int pos0 = (decode || (flags & LOOP_CONTINUE)) ? len_max : 0;
+  const bool ragged = decode && len_min != len_max;
   if ((long)pos0 + S > st->max_seq)
     return lp_fail(LOOP_ERR_CAPACITY, "positions %d + %d exceed max_seq %d", pos0, S, st->max_seq);
   const int T = B * S;
@@ -436,6 +473,15 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
   const int C = c.hidden, Hq = c.n_heads, Hkv = c.n_kv_heads, d = c.head_dim;
   const int qkv_rows = m->qkv_rows();
   const int mhc_grid = T < 2 * m->cu ? T : 2 * m->cu;
+  // per-sequence slices of the slots: the kernels index sequences from the base
+  const size_t kv_skip = (size_t)seq0 * Hkv * st->S_max * d * m->es;
+  const size_t s_skip = (size_t)seq0 * Hkv * d * d, z_skip = (size_t)seq0 * Hkv * d;
+  const int* pos_dev = nullptr;
+  if (ragged) {
+    int32_t* p = (int32_t*)(st->base + st->pos_off) + seq0;
+    LAUNCH(lk::set_i32(p, st->seq_len.data() + seq0, B, s), "positions");
+    pos_dev = p;
+  }
 
   // embedding
   if (tokens) {
@@ -510,12 +556,13 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
     if (ex.full) {
       lk::GemmArgs g = gemm(lk::EPI_QKV, u, C, T, W.qkv, qkv_rows, C, qkv, qkv_rows);
       g.q_cols = Hq * d; g.n_kv = Hkv; g.head_dim = d;
-      g.kcache = st->base + st->koff[ex.slot];
-      g.vcache = st->base + st->voff[ex.slot];
-      g.S_call = S; g.pos0 = pos0; g.S_max = st->S_max;
+      g.kcache = st->base + st->koff[ex.slot] + kv_skip;
+      g.vcache = st->base + st->voff[ex.slot] + kv_skip;
+      g.S_call = S; g.pos0 = pos0; g.S_max = st->S_max; g.pos_dev = pos_dev;
       LAUNCH(run_gemm(g), "qkv gemm");
       lk::AttnArgs a{};
       a.dt = dt; a.B = B; a.S_call = S; a.pos0 = pos0; a.S_max = st->S_max; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+      a.pos_dev = pos_dev;
       a.q = qkv; a.ldq = qkv_rows; a.kcache = g.kcache; a.vcache = g.vcache; a.out = attn; a.ldo = Hq * d;
       if (decode && dt == lk::DT_BF16) {
         const lk::DecodePlan dp = lk::decode_plan(B, Hkv, pos0 + S, m->cu);
@@ -532,8 +579,8 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
       ypend = lk::YPart{};
       a.dt = dt; a.B = B; a.S_call = S; a.Hq = Hq; a.Hkv = Hkv; a.d = d; a.eps = c.la_eps;
       a.qkv = qkv; a.ld = qkv_rows;
-      a.S = (float*)(st->base + st->soff[ex.slot]);
-      a.z = (float*)(st->base + st->zoff[ex.slot]);
+      a.S = (float*)(st->base + st->soff[ex.slot]) + s_skip;
+      a.z = (float*)(st->base + st->zoff[ex.slot]) + z_skip;
       a.init_zero = pos0 == 0;
       a.out = attn; a.ldo = Hq * d; a.scratch = lin_scr; a.chunk = LIN_CHUNK;
       if (S <= 16) { LAUNCH(lk::lin_decode(a, s), "linear attention (recurrent)"); }
@@ -579,8 +626,7 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, con
     const char* last = (const char*)u + (size_t)(S - 1) * C * m->es;
     LAUNCH(run_gemm(gemm(lk::EPI_F32, last, (long)S * C, B, m->head, c.vocab, C, out, c.vocab)), "head gemm");
   }
-  st->length = pos0 + S;
-  st->pipe_reset();
+  for (int b = seq0; b < seq0 + B; ++b) st->seq_len[b] = (decode ? st->seq_len[b] : pos0) + S;
   return LOOP_OK;
 }
 
@@ -612,7 +658,10 @@ int decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_b
   if (tokens) {
     e = st->pipe_enter;
     if (st->pipe_next[e] != 0) return lp_fail(LOOP_ERR_STATE, "cohort %d still has a token in flight", e);
-    if (st->pipe_len[e] == 0) return lp_fail(LOOP_ERR_STATE, "decode before prefill");
+    int mn, mx;
+    st->lengths(e * B, B, &mn, &mx);
+    if (mn == 0) return lp_fail(LOOP_ERR_STATE, "decode before prefill");
+    if (mn != mx) return lp_fail(LOOP_ERR_STATE, "cohort %d holds sequences of different lengths (%d..%d)", e, mn, mx);
     pass[e] = 1;
   }
   int f = -1;
@@ -623,7 +672,7 @@ int decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_b
   if (!any) return lp_fail(LOOP_ERR_STATE, "no token to decode (no cohort in flight and no tokens given)");
   if (f >= 0 && !logits) return lp_fail(LOOP_ERR_INVALID_ARG, "null logits");
   for (int g = 0; g < G; ++g)
-    if (pass[g] && st->pipe_len[g] >= st->max_seq)
+    if (pass[g] && st->seq_len[g * B] >= st->max_seq)
       return lp_fail(LOOP_ERR_CAPACITY, "cohort %d is at max_seq %d", g, st->max_seq);
   const int T = G * B;
   const WsLayout L = ws_layout(m, T, T, st->max_seq);
@@ -697,7 +746,7 @@ int decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_b
   };
   // attention sublayer of stored layer `layer` on rows [r0, r0 + n); cohorts in
   // `coh` (each a block of B rows inside the range) run their own execution
-  // `ex_of(g)` at position pipe_len[g]; the O projection leaves y (deferred
+  // `ex_of(g)` at the cohort's common length; the O projection leaves y (deferred
   // when `defer_o`)
   auto attention = [&](int layer, int r0, int n, const std::vector<int>& coh, const std::vector<const Exec*>& exs,
                        bool defer_o) -> int {
@@ -711,7 +760,7 @@ int decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_b
       q.q_cols = Hq * d; q.n_kv = Hkv; q.head_dim = d;
       q.kcache = st->base + st->koff[exs[0]->slot] + (size_t)g * B * Hkv * st->S_max * d * es;
       q.vcache = st->base + st->voff[exs[0]->slot] + (size_t)g * B * Hkv * d * st->S_max * es;
-      q.S_call = 1; q.pos0 = st->pipe_len[g]; q.S_max = st->S_max;
+      q.S_call = 1; q.pos0 = st->seq_len[g * B]; q.S_max = st->S_max;
       LAUNCH(run_gemm(q, false), "qkv gemm");
     } else {
       LAUNCH(run_gemm(gemm(lk::EPI_STORE, rows(u, r0, C), C, n, W.qkv, qkv_rows, C, rows(qkv, r0, qkv_rows),
@@ -720,7 +769,7 @@ int decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_b
     for (size_t i = 0; i < coh.size(); ++i) {
       const int g = coh[i];
       const Exec& ex = *exs[i];
-      const int pos = st->pipe_len[g];
+      const int pos = st->seq_len[g * B];
       char* qrow = rows(qkv, g * B, qkv_rows);
       if (full) {
         char* kc = st->base + st->koff[ex.slot] + (size_t)g * B * Hkv * st->S_max * d * es;
@@ -844,15 +893,12 @@ int decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_b
   for (int g : coh) {
     if (g == f) {
       st->pipe_next[g] = 0;
-      st->pipe_len[g] += 1;
+      for (int b = g * B; b < (g + 1) * B; ++b) st->seq_len[b] += 1;
     } else {
       st->pipe_next[g] = pass[g] + 1;
     }
   }
   if (e >= 0) st->pipe_enter = (e + 1) % G;
-  int mn = st->pipe_len[0];
-  for (int g = 1; g < G; ++g) mn = std::min(mn, st->pipe_len[g]);
-  st->length = mn;
   info[0] = e;
   info[1] = f;
   return LOOP_OK;
@@ -867,14 +913,25 @@ int loop_prefill(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes
   if (!m) return lp_fail(LOOP_ERR_INVALID_ARG, "null model");
   if (flags & ~(unsigned)(LOOP_ALL_LOGITS | LOOP_HIDDEN_OUT | LOOP_CONTINUE))
     return lp_fail(LOOP_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
-  return forward(m, st, workspace, ws_bytes, tokens_dev, embeds_dev, B, S, flags, out_dev, (hipStream_t)stream, false);
+  return forward(m, st, workspace, ws_bytes, 0, tokens_dev, embeds_dev, B, S, flags, out_dev, (hipStream_t)stream,
+                 false);
+}
+
+int loop_prefill_rows(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, int seq0,
+                      const int32_t* tokens_dev, const void* embeds_dev, int B, int S, unsigned flags, void* out_dev,
+                      void* stream) {
+  if (!m) return lp_fail(LOOP_ERR_INVALID_ARG, "null model");
+  if (flags & ~(unsigned)(LOOP_ALL_LOGITS | LOOP_HIDDEN_OUT | LOOP_CONTINUE))
+    return lp_fail(LOOP_ERR_INVALID_ARG, "unknown flags 0x%x", flags);
+  return forward(m, st, workspace, ws_bytes, seq0, tokens_dev, embeds_dev, B, S, flags, out_dev, (hipStream_t)stream,
+                 false);
 }
 
 int loop_decode_step(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, const int32_t* tokens_dev,
                      int B, float* logits_dev, void* stream) {
   if (!m) return lp_fail(LOOP_ERR_INVALID_ARG, "null model");
   if (!tokens_dev) return lp_fail(LOOP_ERR_INVALID_ARG, "null tokens");
-  return forward(m, st, workspace, ws_bytes, tokens_dev, nullptr, B, 1, 0, logits_dev, (hipStream_t)stream, true);
+  return forward(m, st, workspace, ws_bytes, 0, tokens_dev, nullptr, B, 1, 0, logits_dev, (hipStream_t)stream, true);
 }
 
 int loop_decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, const int32_t* tokens_dev,

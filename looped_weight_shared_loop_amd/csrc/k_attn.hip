@@ -286,8 +286,9 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
   const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const bool cvalid = c < ncol;
   const int tq = cvalid ? c / G : 0, jq = kvh * G + (cvalid ? c % G : 0);
-  const int kv_len = a.pos0 + a.S_call;           // keys [0, kv_len) exist
-  const int lim = a.pos0 + tq + 1;                 // visible to this column
+  const int pos0 = a.pos_dev ? min(max(a.pos_dev[b], 0), a.pos0) : a.pos0;   // this sequence's first new position
+  const int kv_len = pos0 + a.S_call;              // keys [0, kv_len) exist
+  const int lim = pos0 + tq + 1;                   // visible to this column
   const int k_begin = s * a.split_len;
   const int k_end = min(k_begin + a.split_len, kv_len);
 
@@ -466,7 +467,7 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < D; ++i) { qr[i] = q[i]; o[i] = 0.f; }
   float m = -INFINITY, l = 0.f;
-  const int last = a.pos0 + t;
+  const int last = (a.pos_dev ? min(max(a.pos_dev[b], 0), a.pos0) : a.pos0) + t;
   for (int key = 0; key <= last; ++key) {
     float s = 0.f;
 #pragma unroll
@@ -495,6 +496,7 @@ static hipError_t launch_f32(const AttnArgs& a, hipStream_t s) {
 hipError_t attn_prefill(const AttnArgs& a, hipStream_t s) {
   if (a.S_call <= 0 || a.B <= 0) return hipSuccess;
   if (a.dt == DT_F32) return launch_f32(a, s);
+  if (a.pos_dev) return hipErrorInvalidValue;   // one start position per call
   const int G = a.Hq / a.Hkv;
   if (a.d != PD || a.Hq % a.Hkv || !(G == 1 || G == 2 || G == 4 || G == 8) || a.S_max % 64)
     return hipErrorInvalidValue;

@@ -27,7 +27,8 @@ DEV void epi_qkv(const GemmArgs& a, int row, int col, float v) {
   }
   int cc = col - a.q_cols;
   const int kvn = a.n_kv * a.head_dim;
-  const int b = row / a.S_call, pos = a.pos0 + row % a.S_call;
+  const int b = row / a.S_call;
+  const int pos = (a.pos_dev ? min(max(a.pos_dev[b], 0), a.pos0) : a.pos0) + row % a.S_call;
   if (cc < kvn) {
     const int hk = cc / a.head_dim, dd = cc % a.head_dim;
     st1((T*)a.kcache + (((size_t)b * a.n_kv + hk) * a.S_max + pos) * a.head_dim + dd, v);

@@ -35,6 +35,24 @@ hipError_t embed(int dt, const int32_t* tokens, const void* table, int vocab, in
   return hipGetLastError();
 }
 
+struct I32Block { int32_t v[64]; };
+
+__global__ __launch_bounds__(64) void set_i32_kernel(int32_t* __restrict__ dst, I32Block b, int n) {
+  if ((int)threadIdx.x < n) dst[threadIdx.x] = b.v[threadIdx.x];
+}
+
+hipError_t set_i32(int32_t* dst, const int32_t* vals, int n, hipStream_t s) {
+  for (int i = 0; i < n; i += 64) {
+    const int k = n - i < 64 ? n - i : 64;
+    I32Block b{};
+    for (int j = 0; j < k; ++j) b.v[j] = vals[i + j];
+    set_i32_kernel<<<1, 64, 0, s>>>(dst + i, b, k);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 // ------------------------------------------------------------------ block sum
 // Sums NV values over the block; `red` holds [2][16 waves][NV] floats and is
 // used by token parity so one barrier per token suffices.

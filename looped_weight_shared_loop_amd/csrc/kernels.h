@@ -15,6 +15,10 @@ enum Dt { DT_F32 = 0, DT_BF16 = 1 };
 hipError_t embed(int dt, const int32_t* tokens, const void* table, int vocab, int C, int T,
                  void* h, uint32_t* err_word, hipStream_t s);
 
+// dst[0, n) <- vals[0, n) (host values passed as kernel arguments, so the
+// host array may be reused as soon as the call returns).
+hipError_t set_i32(int32_t* dst, const int32_t* vals, int n, hipStream_t s);
+
 // h <- h + y (if y), u <- RMSNorm(h; gamma).  In place on h.
 // A bf16 [T][C] sublayer output that is still split-K partial sums of the
 // decode-shaped GEMM (tile of R output columns, ks partials of `tok` rows,
@@ -71,6 +75,8 @@ struct GemmArgs {
   void* kcache;          // [B][Hkv][S_max][d]
   void* vcache;          // [B][Hkv][d][S_max] (transposed)
   int S_call, pos0, S_max;  // row m is sequence m / S_call at position pos0 + m % S_call
+  const int* pos_dev;    // non-null: sequence b starts at pos_dev[b] (ragged batch), read clamped
+                         // to [0, pos0]: pos0 then holds the largest start, which bounds the writes
   int F;                 // EPI_SWIGLU: up rows start at row F of B
   // M <= 64: split-K plan (skinny_plan) and its scratch; ksplit 1 needs none.
   int ksplit;
@@ -94,6 +100,9 @@ struct AttnArgs {
   const void* vcache;              // [B][Hkv][d][S_max]
   void* out; long ldo;             // token m: out + m * ldo, head j at + j * d
   float* part; int n_split, split_len;   // decode: [B][Hq][n_split][d + 2] fp32 (n_split > 1)
+  const int* pos_dev;              // decode: non-null: sequence b's new tokens start at pos_dev[b]
+                                   // (ragged batch), read clamped to [0, pos0]: pos0 then holds
+                                   // the largest start, which the split plan covers
 };
 hipError_t attn_prefill(const AttnArgs& a, hipStream_t s);
 hipError_t attn_decode(const AttnArgs& a, hipStream_t s);

@@ -148,6 +148,24 @@ int loop_op_attention_decode(int dtype, int B, int S, int pos0, int S_max, int H
   return launched(lk::attn_decode(a, (hipStream_t)stream), "decode attention");
 }
 
+int loop_op_attention_decode_ragged(int dtype, int B, int S, const int32_t* pos_dev, int max_pos0, int S_max, int Hq,
+                                    int Hkv, int d, const void* q, long ldq, const void* kcache, const void* vcache,
+                                    void* out, long ldo, void* scratch, size_t scratch_bytes, void* stream) {
+  if (!pos_dev) return lp_fail(LOOP_ERR_INVALID_ARG, "null positions");
+  lk::AttnArgs a;
+  if (int r = attn_common(dtype, B, S, max_pos0, S_max, Hq, Hkv, d, q, ldq, kcache, vcache, out, ldo, &a)) return r;
+  a.pos_dev = pos_dev;
+  if (dtype == LOOP_FP32) return launched(lk::attn_prefill(a, (hipStream_t)stream), "attention");
+  if (!scratch || scratch_bytes < loop_op_attention_decode_bytes(B, S, Hq, d, S_max))
+    return lp_fail(LOOP_ERR_WORKSPACE, "decode attention scratch too small");
+  if (lp_misaligned(scratch)) return lp_fail(LOOP_ERR_ALIGN, "misaligned scratch");
+  const lk::DecodePlan dp = lk::decode_plan(B, Hkv, max_pos0 + S, lk::device_cu_count());
+  a.part = (float*)scratch;
+  a.split_len = dp.split_len;
+  a.n_split = dp.n_split;
+  return launched(lk::attn_decode(a, (hipStream_t)stream), "decode attention");
+}
+
 size_t loop_op_linear_bytes(int B, int S, int Hkv, int d) {
   if (B <= 0 || S <= 0 || Hkv <= 0 || d <= 0) return 0;
   return lk::lin_scratch_floats(B, Hkv, d, S, LIN_CHUNK) * sizeof(float);

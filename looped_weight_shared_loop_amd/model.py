@@ -116,10 +116,21 @@ class LoopState:
 
     @property
     def length(self) -> int:
+        """The shortest sequence's length (the common one unless ragged)."""
         return A.loop_state_length(self.handle)
 
     def set_length(self, n: int) -> None:
         A.loop_state_set_length(self.handle, n)
+
+    def seq_length(self, seq: int) -> int:
+        return A.loop_state_seq_length(self.handle, seq)
+
+    def set_seq_length(self, seq: int, n: int) -> None:
+        A.loop_state_set_seq_length(self.handle, seq, n)
+
+    @property
+    def lengths(self):
+        return [self.seq_length(i) for i in range(self.batch)]
 
     def region(self, kind: int, slot: int):
         return A.loop_state_region(self.handle, kind, slot)
@@ -190,7 +201,9 @@ class LoopModel:
 
     def prefill(self, state: LoopState, tokens: Optional[torch.Tensor] = None, embeds: Optional[torch.Tensor] = None,
                 all_logits: bool = False, hidden_out: bool = False, cont: bool = False,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None, seq0: Optional[int] = None) -> torch.Tensor:
+        """Prefill of B sequences: [0, B), or [seq0, seq0 + B) of the state
+        when seq0 is given (the other sequences keep their lengths)."""
         src = tokens if tokens is not None else embeds
         B, S = int(src.shape[0]), int(src.shape[1])
         flags = (A.LOOP_ALL_LOGITS if all_logits else 0) | (A.LOOP_HIDDEN_OUT if hidden_out else 0) | \
@@ -209,8 +222,12 @@ class LoopModel:
             assert tokens.dtype == torch.int32 and tokens.is_contiguous()
         if embeds is not None:
             assert embeds.dtype == self.cfg.torch_dtype and embeds.is_contiguous()
-        A.loop_prefill(self.handle, state.handle, ws.data_ptr(), ws.numel(), tok_ptr, emb_ptr, B, S, flags,
-                       out.data_ptr(), self._stream())
+        if seq0 is None:
+            A.loop_prefill(self.handle, state.handle, ws.data_ptr(), ws.numel(), tok_ptr, emb_ptr, B, S, flags,
+                           out.data_ptr(), self._stream())
+        else:
+            A.loop_prefill_rows(self.handle, state.handle, ws.data_ptr(), ws.numel(), seq0, tok_ptr, emb_ptr, B, S,
+                                flags, out.data_ptr(), self._stream())
         return out
 
     def decode_step(self, state: LoopState, tokens: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:

@@ -244,6 +244,100 @@ def test_pipelined_decode_state_rules():
         model.decode_pipelined(bad, to_dev_tokens(toks[:1, 10]))
 
 
+# ------------------------------------------------------------------ ragged batches
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_ragged_batch_prefill_rows_and_decode(dtype):
+    """Sequences of one state at different lengths: rows [0, 2) prefilled to
+    20 positions, row 2 to 33 in two chunks (the second continues it), row 3
+    to 27; then decode steps advance all four together, each at its own
+    position.  Every logit row equals the oracle's forward over that
+    sequence alone."""
+    ocfg = oracle.tiny_config(n_kv_heads=2) if dtype == "fp32" else mini_bf16_config()
+    tol = FP32_TOL if dtype == "fp32" else BF16_TOL
+    model, Wo = build_pair(ocfg)
+    lens, K = [20, 20, 33, 27], 3
+    toks = tokens(4, max(lens) + K, ocfg.vocab, seed=51)
+    _say("ragged batch", dtype, "lengths", lens)
+    ref = [oracle.forward(ocfg, Wo, toks[b:b + 1, :lens[b] + K], all_logits=True)[0] for b in range(4)]
+    st = model.new_state(4, max(lens) + K)
+    got = model.prefill(st, to_dev_tokens(toks[:2, :20]))                      # rows 0, 1
+    assert rel(got.cpu().numpy(), np.stack([ref[0][19], ref[1][19]])) < tol
+    assert st.lengths == [20, 20, 0, 0] and st.length == 0
+    got = model.prefill(st, to_dev_tokens(toks[2:3, :21]), seq0=2, all_logits=True)
+    assert rel(got.cpu().numpy()[0], ref[2][:21]) < tol
+    got = model.prefill(st, to_dev_tokens(toks[2:3, 21:33]), seq0=2, cont=True, all_logits=True)
+    assert rel(got.cpu().numpy()[0], ref[2][21:33]) < tol
+    got = model.prefill(st, to_dev_tokens(toks[3:4, :27]), seq0=3)
+    assert rel(got.cpu().numpy()[0], ref[3][26]) < tol
+    assert st.lengths == [20, 20, 33, 27] and st.length == 20
+    for k in range(K):
+        step = np.array([toks[b, lens[b] + k] for b in range(4)], np.int32)
+        d = model.decode_step(st, to_dev_tokens(step)).cpu().numpy()
+        for b in range(4):
+            err = rel(d[b:b + 1], ref[b][lens[b] + k][None])
+            _say("step", k, "sequence", b, "position", lens[b] + k, "rel err", err)
+            assert err < tol
+    assert st.lengths == [l + K for l in lens]
+
+
+def test_ragged_batch_subset_decode_and_rules():
+    """A decode step over the first B sequences of a ragged state leaves the
+    rest untouched; continued prefills need equal lengths; sequence ranges and
+    empty sequences are refused; a pipelined cohort must be of one length."""
+    L = need_gpu()
+    ocfg = oracle.tiny_config(n_kv_heads=2)
+    model, Wo = build_pair(ocfg)
+    toks = tokens(4, 20, ocfg.vocab, seed=57)
+    ref = [oracle.forward(ocfg, Wo, toks[b:b + 1], all_logits=True)[0] for b in range(4)]
+    st = model.new_state(4, 40)
+    model.prefill(st, to_dev_tokens(toks[:2, :10]))
+    model.prefill(st, to_dev_tokens(toks[2:3, :12]), seq0=2)
+    with pytest.raises(L.LoopError) as ei:                      # sequence 3 is empty
+        model.decode_step(st, to_dev_tokens(toks[:, 12]))
+    assert ei.value.code == -9
+    with pytest.raises(L.LoopError) as ei:                      # rows of lengths 10 and 12
+        model.prefill(st, to_dev_tokens(toks[1:3, 12:14]), seq0=1, cont=True)
+    assert ei.value.code == -9
+    with pytest.raises(L.LoopError) as ei:
+        model.prefill(st, to_dev_tokens(toks[:1, :4]), seq0=4)
+    assert ei.value.code == -1
+    with pytest.raises(L.LoopError) as ei:
+        model.prefill(st, to_dev_tokens(toks[:2, :4]), seq0=3)
+    assert ei.value.code == -4
+    with pytest.raises(L.LoopError) as ei:
+        st.seq_length(4)
+    assert ei.value.code == -1
+    d = model.decode_step(st, to_dev_tokens(np.array([toks[0, 10], toks[1, 10], toks[2, 12]], np.int32)))
+    d = d.cpu().numpy()
+    assert rel(d[:2], np.stack([ref[0][10], ref[1][10]])) < FP32_TOL
+    assert rel(d[2:3], ref[2][12][None]) < FP32_TOL
+    assert st.lengths == [11, 11, 13, 0]
+    # cohorts of a pipelined decode (2 passes: rows [0, 2) and [2, 4)) need one length each
+    model.prefill(st, to_dev_tokens(toks[3:4, :11]), seq0=3)
+    assert st.lengths == [11, 11, 13, 11]
+    model.decode_pipelined(st, to_dev_tokens(toks[:2, 11]))    # cohort 0 enters
+    with pytest.raises(L.LoopError) as ei:
+        model.decode_pipelined(st, to_dev_tokens(toks[2:4, 11]))
+    assert ei.value.code == -9
+    entered, left, out = model.decode_pipelined(st, None)      # cohort 0 leaves
+    assert (entered, left) == (-1, 0)
+    assert rel(out.cpu().numpy(), np.stack([ref[0][11], ref[1][11]])) < FP32_TOL
+    assert st.lengths == [12, 12, 13, 11]
+    st.set_seq_length(3, 0)
+    assert st.seq_length(3) == 0
+    model.prefill(st, to_dev_tokens(toks[3:4, :13]), seq0=3)
+    # cohorts at lengths 12 and 13 share the calls
+    entered, left, out = model.decode_pipelined(st, to_dev_tokens(toks[:2, 12]))
+    assert (entered, left) == (0, -1)
+    entered, left, out = model.decode_pipelined(st, to_dev_tokens(toks[2:4, 13]))
+    assert (entered, left) == (1, 0)
+    assert rel(out.cpu().numpy(), np.stack([ref[0][12], ref[1][12]])) < FP32_TOL
+    entered, left, out = model.decode_pipelined(st, None)
+    assert (entered, left) == (-1, 1)
+    assert rel(out.cpu().numpy(), np.stack([ref[2][13], ref[3][13]])) < FP32_TOL
+    assert st.lengths == [13, 13, 14, 14]
+
+
 # ------------------------------------------------------------------ bf16 (MFMA kernels)
 def test_mini_bf16_prefill_decode():
     ocfg = mini_bf16_config()
