@@ -32,8 +32,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # dispatch), each scaled by the same counter's reading for a plain 1 GiB
 # device copy in that run.  Valid only for the kernel source it was taken on:
 # the hash of k_gemm.hip + common.h must match, else traffic is reported null.
-DOMINANT_COUNTERS = {"source_sha256_16": "18c89946696f6ccc", "fetch_kib": 4722856.7, "write_kib": 786432.0,
-                     "copy_fetch_kib": 524308.6, "copy_write_kib": 1048576.0}
+DOMINANT_COUNTERS = {"source_sha256_16": "2991f4ae966bf0d7", "fetch_kib": 4721210.1, "write_kib": 786717.5,
+                     "copy_fetch_kib": 524315.3, "copy_write_kib": 1048576.0}
 
 NINE_B = dict(vocab=248320, hidden=4096, ffn=12288, n_heads=32, n_kv_heads=8, head_dim=128,
               n_layers=32, loop_start=4, loop_end=28, n_passes=2, dtype="bf16")
@@ -461,7 +461,7 @@ def main():
         "prefill": {"tflops": round(tflops, 1), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                     "algorithmic_tflop": round(flops / 1e12, 2), "gemm_tflop": round(gemm_f / 1e12, 2),
                     "attention_tflop": round(attn_f / 1e12, 2), "linear_tflop": round(lin_f / 1e12, 3)},
-        "roofline": {"kernel": "gemm_dma_kernel<EPI_SWIGLU> (gate/up, M=%d N=24576 K=4096)" % S, "bound": "mfma",
+        "roofline": {"kernel": "gemm_w4_kernel<EPI_SWIGLU> (gate/up, M=%d N=24576 K=4096)" % S, "bound": "mfma",
                      "achieved": round(g_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": (None if S != 32768 or traffic is None else round(traffic)),

@@ -240,6 +240,223 @@ __global__ __launch_bounds__(128 * WN_, 1) void gemm_dma_kernel(GemmArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ MFMA tile kernel, 64-deep
+// 256x256 workgroup tile, four waves as 2 (M) x 2 (N), each owning 128x128 =
+// 4x4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).
+// A k step is 64 deep, so every operand row of a step is one whole 128-byte
+// line: a DMA instruction moves 8 rows (1 KB, lane l to +16 l), and the row's
+// eight 16-byte chunks sit at c ^ ((row >> 1) & 7): a fragment read takes one
+// chunk of 16 consecutive rows per 16 lanes, and with 64 four-byte banks two
+// rows span all banks, so the rows of one parity must use 8 distinct
+// positions.  Two 64 KB stages.  Within a step the fragments of substep
+// j + 1 are read while the MFMAs of substep j run.  The step's one barrier
+// sits before its last substep, whose fragments are already in registers: by
+// then every read of the stage has returned and the next step has landed, so
+// the next step's first reads overlap the last MFMAs.  The loads are issued
+// one after every second MFMA rather than in a burst (a burst stalls the
+// wave on a full load queue while its MFMA pipe idles): A of step kt + 2
+// during the last substep of step kt, into the stage just released, and B of
+// step kt + 2 during the first substep of step kt + 1.
+// Against the eight-wave, 32-deep kernel above this halves the L2 requests
+// (whole lines) and cuts LDS fragment reads by a third (128x128 per wave).
+// MFMA j of a step contracts k 16 j .. 16 j + 15 (lane half h reads chunk
+// 2 j + h), the same k sets in the same order as the kernel above.
+constexpr int WBK = 64, WST = 2;
+constexpr int WSTAGE = (TBM + TBN) * WBK;             // elements per stage (64 KB)
+constexpr int GEMM_W4_LDS = WST * WSTAGE * 2;         // 128 KB
+
+DEV int wswz(int row, int chunk) { return row * WBK + ((chunk ^ ((row >> 1) & 7)) << 3); }
+
+// 16 bytes per lane from a buffer (byte offset voff + soff) into LDS at lds + 16 lane.
+// Reads past num_records return zeros.
+DEV void dma16_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff, bf16_t* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, soff, 0, 0);
+}
+DEV __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, unsigned bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
+  constexpr int JB = 4, WCOL = 128;
+  constexpr int NB = 8;                    // DMA instructions per wave per operand per step
+  extern __shared__ __align__(16) bf16_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int num_m = (a.M + TBM - 1) / TBM;
+  const int out_n = (EPI == EPI_SWIGLU) ? 128 : TBN;
+  const int num_n = (EPI == EPI_SWIGLU ? a.F : a.N) / out_n;
+  const int nblk = num_m * num_n;
+  // XCD-aware tile order, as in the kernel above.
+  int id = blockIdx.x;
+  if (nblk % 8 == 0) id = (id & 7) * (nblk >> 3) + (id >> 3);
+  const int GM = 8;
+  const int group = GM * num_n;
+  const int first_m = (id / group) * GM;
+  const int gsz = min(num_m - first_m, GM);
+  const int tm = first_m + (id % group) % gsz;
+  const int tn = (id % group) / gsz;
+  const int m0 = tm * TBM, n0 = tn * out_n;
+
+  // Buffer views of this tile's A rows and of B; byte offsets fit in 32 bits
+  // (the host checks 256 lda and the B rows against 2^31 elements).
+  const int mlast = a.M - 1 - m0;
+  const __amdgpu_buffer_rsrc_t Ar = buf_rsrc((const bf16_t*)a.A + (long)m0 * a.lda,
+                                             (unsigned)(min(TBM, a.M - m0) * a.lda * 2));
+  const __amdgpu_buffer_rsrc_t Br = buf_rsrc(a.B, 0xFFFFFFF0u);
+  // wave w issues DMA blocks 8 w .. 8 w + 7 of each operand: rows 8 blk + lane / 8,
+  // LDS chunk lane % 8 holds global chunk (lane % 8) ^ ((row >> 1) & 7)
+  int aoff[NB], boff[NB];
+#pragma unroll
+  for (int i = 0; i < NB; ++i) {
+    const int blk = wid * NB + i;
+    const int r = blk * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    aoff[i] = (min(r, mlast) * (int)a.lda + c * 8) * 2;
+    int br;
+    if (EPI == EPI_SWIGLU) {
+      const int w = r / WCOL, j = (r % WCOL) / 32, cc = r & 31;
+      const int oc = n0 + w * (WCOL / 2) + (j % (JB / 2)) * 32 + cc;
+      br = (j < JB / 2) ? oc : (a.F + oc);
+    } else {
+      br = n0 + r;
+    }
+    boff[i] = (br * (int)a.ldb + c * 8) * 2;
+  }
+  const int KT = a.K / WBK;
+  // Steps past the end re-read the last step into the stage nobody reads
+  // again, so the loop body has no branch around its loads.
+  // one operand (op 0: A, op 1: B) of step kt: NB loads per wave
+  auto issue = [&](int kt, int op) {
+    bf16_t* st = smem + (kt & 1) * WSTAGE + op * TBM * WBK;
+    const int kb = min(kt, KT - 1) * WBK * 2;
+    if (op == 0) {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) dma16_buf(Ar, aoff[i], kb, st + (wid * NB + i) * 512);
+    } else {
+#pragma unroll
+      for (int i = 0; i < NB; ++i) dma16_buf(Br, boff[i], kb, st + (wid * NB + i) * 512);
+    }
+  };
+  f32x16_t acc[4][JB];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < JB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int arow = wm * 128 + (lane & 31);
+  const int brow = wn * WCOL + (lane & 31);
+  bf16x8_t fa[2][4], fb[2][JB];
+  auto read_frags = [&](int kt, int j, bf16x8_t (&xa)[4], bf16x8_t (&xb)[JB]) {
+    const bf16_t* as = smem + (kt & 1) * WSTAGE;
+    const bf16_t* bs = as + TBM * WBK;
+    const int ch = j * 2 + (lane >> 5);
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib) xa[ib] = as_bf16x8(ldv4(as + wswz(arow + ib * 32, ch)));
+#pragma unroll
+    for (int jb = 0; jb < JB; ++jb) xb[jb] = as_bf16x8(ldv4(bs + wswz(brow + jb * 32, ch)));
+  };
+  auto mma = [&](const bf16x8_t (&xa)[4], const bf16x8_t (&xb)[JB]) {
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb) acc[ib][jb] = mfma32(xa[ib], xb[jb], acc[ib][jb]);
+  };
+  // the 8 fragment reads of the next substep one-to-one with the first 8 of the 16 MFMAs
+  auto interleave = [&]() {
+#pragma unroll
+    for (int i = 0; i < 4 + JB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * JB - (4 + JB), 0);
+  };
+  // The 16 MFMAs of a substep with the NB loads of one operand of step kt,
+  // one load after every second MFMA (scheduling walls keep that order), so
+  // the wave never stalls on a burst of loads while its MFMA pipe idles.
+  auto mma_dma = [&](const bf16x8_t (&xa)[4], const bf16x8_t (&xb)[JB], int kt, int op) {
+    bf16_t* st = smem + (kt & 1) * WSTAGE + op * TBM * WBK;
+    const int kb = min(kt, KT - 1) * WBK * 2;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int ib = q >> 2, jb = q & 3;
+      acc[ib][jb] = mfma32(xa[ib], xb[jb], acc[ib][jb]);
+      if (q & 1) {
+        const int i = q >> 1;
+        if (op == 0) dma16_buf(Ar, aoff[i], kb, st + (wid * NB + i) * 512);
+        else dma16_buf(Br, boff[i], kb, st + (wid * NB + i) * 512);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
+  auto sync = [&]() {
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+  issue(0, 0);
+  issue(0, 1);
+  issue(1, 0);
+  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // step 0 landed (A of step 1 may fly)
+  sync();
+  read_frags(0, 0, fa[0], fb[0]);
+  for (int kt = 0; kt + 1 < KT; ++kt) {
+    // B of step kt + 1 into the stage of step kt - 1 (free since the last barrier)
+    read_frags(kt, 1, fa[1], fb[1]);
+    mma_dma(fa[0], fb[0], kt + 1, 1);
+    read_frags(kt, 2, fa[0], fb[0]);
+    mma(fa[1], fb[1]);
+    interleave();
+    read_frags(kt, 3, fa[1], fb[1]);
+    mma(fa[0], fb[0]);
+    interleave();
+    // Every read of this stage has returned (their registers feed the MFMAs
+    // below) and this wave's loads of step kt + 1 have landed; after the
+    // barrier the stage of step kt takes A of step kt + 2 while the last
+    // substep's MFMAs run.
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    sync();
+    read_frags(kt + 1, 0, fa[0], fb[0]);
+    mma_dma(fa[1], fb[1], kt + 2, 0);
+  }
+  read_frags(KT - 1, 1, fa[1], fb[1]);
+  mma(fa[0], fb[0]);
+  read_frags(KT - 1, 2, fa[0], fb[0]);
+  mma(fa[1], fb[1]);
+  read_frags(KT - 1, 3, fa[1], fb[1]);
+  mma(fa[0], fb[0]);
+  mma(fa[1], fb[1]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
+
+  if (EPI == EPI_SWIGLU) {
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < JB / 2; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 128 + ib * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int col = n0 + wn * (WCOL / 2) + jb * 32 + (lane & 31);
+          if (row < a.M) {
+            const float g = acc[ib][jb][r], u = acc[ib][jb + JB / 2][r];
+            st1((bf16_t*)a.C + (size_t)row * a.ldc + col, silu(g) * u);
+          }
+        }
+  } else {
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wm * 128 + ib * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+          const int col = n0 + wn * WCOL + jb * 32 + (lane & 31);
+          if (row < a.M) epi_one<bf16_t, EPI>(a, row, col, acc[ib][jb][r]);
+        }
+  }
+}
+
 // ------------------------------------------------------------------ skinny (M <= 64)
 // Decode shape: the weights are streamed once; the <= 64 token rows (one or two
 // blocks of 32) are the MFMA's other operand (gemm_skinny_rs_kernel below).
@@ -537,6 +754,19 @@ static hipError_t launch_dma(const GemmArgs& a, int blocks, hipStream_t s) {
 }
 
 template <int EPI>
+static hipError_t launch_w4(const GemmArgs& a, int blocks, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_w4_kernel<EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       GEMM_W4_LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  gemm_w4_kernel<EPI><<<blocks, 256, GEMM_W4_LDS, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int EPI>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 64) {
     if (a.ksplit < 1 || a.K % (a.ksplit * 64)) return hipErrorInvalidValue;
@@ -550,6 +780,7 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   const int ncols = (EPI == EPI_SWIGLU) ? a.F : a.N;
   if (ncols % out_n) return hipErrorInvalidValue;
   const int blocks = ((a.M + TBM - 1) / TBM) * (ncols / out_n);
+  if (a.K % WBK == 0) return launch_w4<EPI>(a, blocks, s);
   return launch_dma<EPI, 4>(a, blocks, s);
 }
 
