@@ -83,9 +83,12 @@ DEV f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-DEV float silu(float x) { return x / (1.0f + expf(-x)); }
 // 2^x with the hardware instruction alone (about 1 ulp; results below
 // 2^-126 flush to zero): the softmax exponentials, where such tiny
 // probabilities do not matter, skip the denormal-range handling of exp2f.
 DEV float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// x sigma(x) = x / (1 + e^-x) from the hardware 2^x and reciprocal (about
+// 1 ulp each): a few instructions instead of a library exponential and an
+// IEEE division.  Large negative x give 1 / inf = 0, so the result is 0.
+DEV float silu(float x) { return x * __builtin_amdgcn_rcpf(1.0f + exp2_hw(-1.4426950408889634f * x)); }
 

@@ -429,19 +429,34 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
   mma(fa[1], fb[1]);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
 
+  // Epilogue: each lane's stores go to one base pointer plus offsets that
+  // are the same for the whole wave (row step times ldc); rows past M are
+  // skipped.
+  const int lrow = wm * 128 + (lane >> 5) * 4, lcol = lane & 31;
+  const int rows_left = a.M - m0 - lrow;     // this lane's rows r < rows_left exist
   if (EPI == EPI_SWIGLU) {
+    bf16_t* Cl = (bf16_t*)a.C + ((size_t)(m0 + lrow)) * a.ldc + n0 + wn * (WCOL / 2) + lcol;
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
       for (int jb = 0; jb < JB / 2; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * 128 + ib * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int col = n0 + wn * (WCOL / 2) + jb * 32 + (lane & 31);
-          if (row < a.M) {
-            const float g = acc[ib][jb][r], u = acc[ib][jb + JB / 2][r];
-            st1((bf16_t*)a.C + (size_t)row * a.ldc + col, silu(g) * u);
-          }
+          const int dr = ib * 32 + (r >> 2) * 8 + (r & 3);
+          if (dr < rows_left)
+            st1(Cl + (long)dr * a.ldc + jb * 32, silu(acc[ib][jb][r]) * acc[ib][jb + JB / 2][r]);
+        }
+  } else if (EPI == EPI_STORE || EPI == EPI_F32) {
+    using T = typename std::conditional<EPI == EPI_F32, float, bf16_t>::type;
+    T* Cl = (T*)a.C + ((size_t)(m0 + lrow)) * a.ldc + n0 + wn * WCOL + lcol;
+#pragma unroll
+    for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int dr = ib * 32 + (r >> 2) * 8 + (r & 3);
+          if (dr < rows_left) st1(Cl + (long)dr * a.ldc + jb * 32, acc[ib][jb][r]);
         }
   } else {
 #pragma unroll
@@ -450,8 +465,8 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
       for (int jb = 0; jb < JB; ++jb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * 128 + ib * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-          const int col = n0 + wn * WCOL + jb * 32 + (lane & 31);
+          const int row = m0 + lrow + ib * 32 + (r >> 2) * 8 + (r & 3);
+          const int col = n0 + wn * WCOL + jb * 32 + lcol;
           if (row < a.M) epi_one<bf16_t, EPI>(a, row, col, acc[ib][jb][r]);
         }
   }
