@@ -281,7 +281,9 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
   constexpr int JB = 4, WCOL = 128;
   constexpr int NB = 8;                    // DMA instructions per wave per operand per step
   extern __shared__ __align__(16) bf16_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  // the wave index is uniform: as a scalar it keeps every LDS destination of
+  // the DMA (the M0 operand) in scalar registers, with no per-load readfirstlane
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid >> 1, wn = wid & 1;
   const int num_m = (a.M + TBM - 1) / TBM;
   const int out_n = (EPI == EPI_SWIGLU) ? 128 : TBN;
@@ -349,8 +351,9 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
   const int arow = wm * 128 + (lane & 31);
   const int brow = wn * WCOL + (lane & 31);
   bf16x8_t fa[2][4], fb[2][JB];
-  auto read_frags = [&](int kt, int j, bf16x8_t (&xa)[4], bf16x8_t (&xb)[JB]) {
-    const bf16_t* as = smem + (kt & 1) * WSTAGE;
+  // par: the stage, kt & 1, passed as a constant so LDS addresses fold into offsets
+  auto read_frags = [&](int par, int j, bf16x8_t (&xa)[4], bf16x8_t (&xb)[JB]) {
+    const bf16_t* as = smem + par * WSTAGE;
     const bf16_t* bs = as + TBM * WBK;
     const int ch = j * 2 + (lane >> 5);
 #pragma unroll
@@ -376,8 +379,8 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
   // The 16 MFMAs of a substep with the NB loads of one operand of step kt,
   // one load after every second MFMA (scheduling walls keep that order), so
   // the wave never stalls on a burst of loads while its MFMA pipe idles.
-  auto mma_dma = [&](const bf16x8_t (&xa)[4], const bf16x8_t (&xb)[JB], int kt, int op) {
-    bf16_t* st = smem + (kt & 1) * WSTAGE + op * TBM * WBK;
+  auto mma_dma = [&](const bf16x8_t (&xa)[4], const bf16x8_t (&xb)[JB], int kt, int par, int op) {
+    bf16_t* st = smem + par * WSTAGE + op * TBM * WBK;
     const int kb = min(kt, KT - 1) * WBK * 2;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
@@ -401,14 +404,14 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
   asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // step 0 landed (A of step 1 may fly)
   sync();
   read_frags(0, 0, fa[0], fb[0]);
-  for (int kt = 0; kt + 1 < KT; ++kt) {
+  auto step = [&](int kt, int par) {
     // B of step kt + 1 into the stage of step kt - 1 (free since the last barrier)
-    read_frags(kt, 1, fa[1], fb[1]);
-    mma_dma(fa[0], fb[0], kt + 1, 1);
-    read_frags(kt, 2, fa[0], fb[0]);
+    read_frags(par, 1, fa[1], fb[1]);
+    mma_dma(fa[0], fb[0], kt + 1, par ^ 1, 1);
+    read_frags(par, 2, fa[0], fb[0]);
     mma(fa[1], fb[1]);
     interleave();
-    read_frags(kt, 3, fa[1], fb[1]);
+    read_frags(par, 3, fa[1], fb[1]);
     mma(fa[0], fb[0]);
     interleave();
     // Every read of this stage has returned (their registers feed the MFMAs
@@ -417,14 +420,21 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
     // substep's MFMAs run.
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     sync();
-    read_frags(kt + 1, 0, fa[0], fb[0]);
-    mma_dma(fa[1], fb[1], kt + 2, 0);
+    read_frags(par ^ 1, 0, fa[0], fb[0]);
+    mma_dma(fa[1], fb[1], kt + 2, par, 0);
+  };
+  // steps 0 .. KT - 2, two per trip so that the stage of each is a constant
+  int kt = 0;
+  for (; kt + 2 < KT; kt += 2) {
+    step(kt, 0);
+    step(kt + 1, 1);
   }
-  read_frags(KT - 1, 1, fa[1], fb[1]);
+  if (kt + 1 < KT) step(kt++, 0);
+  read_frags(kt & 1, 1, fa[1], fb[1]);
   mma(fa[0], fb[0]);
-  read_frags(KT - 1, 2, fa[0], fb[0]);
+  read_frags(kt & 1, 2, fa[0], fb[0]);
   mma(fa[1], fb[1]);
-  read_frags(KT - 1, 3, fa[1], fb[1]);
+  read_frags(kt & 1, 3, fa[1], fb[1]);
   mma(fa[0], fb[0]);
   mma(fa[1], fb[1]);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
