@@ -52,7 +52,7 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
   constexpr int NB = 16 / NW;                  // DMA blocks per wave per operand and tile
   const int G = a.Hq / a.Hkv;                  // 1, 2, 4 or 8
   const int QS = NW / G;                       // query sub-blocks per workgroup
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qb = gridDim.x - 1 - blockIdx.x;   // long rows first
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int j = kvh * G + wid % G;
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
   const int ncol = G * a.S_call;
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
   const bool cvalid = c < ncol;
   const int tq = cvalid ? c / G : 0, jq = kvh * G + (cvalid ? c % G : 0);
   const int pos0 = a.pos_dev ? min(max(a.pos_dev[b], 0), a.pos0) : a.pos0;   // this sequence's first new position

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(128 * WN_, 1) void gemm_dma_kernel(GemmArgs a) {
   constexpr int JB = 8 / WN_, WCOL = 32 * JB;
   constexpr int NBW = JB;                 // DMA blocks per wave per operand
   extern __shared__ __align__(16) bf16_t smem[];
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wid / WN_, wn = wid % WN_;
   const int num_m = (a.M + TBM - 1) / TBM;
   const int out_n = (EPI == EPI_SWIGLU) ? 128 : TBN;

@@ -255,7 +255,7 @@ __global__ __launch_bounds__(256) void lin_delta_bf(LinArgs a) {
   const int c = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int nc = gridDim.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const bf16_t* base = (const bf16_t*)a.qkv;
   {
     const int i8 = (tid & 15) * 8;          // this thread's 8 features
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(128 * NH, 1) void lin_out_bf(LinArgs a) {
   const int c = blockIdx.x, bh = blockIdx.y;
   const int b = bh / a.Hkv, hk = bh % a.Hkv;
   const int nc = gridDim.x;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int rl = lane & 31, h = lane >> 5;
   const bf16_t* base = (const bf16_t*)a.qkv;
   const int j_q = hk * (a.Hq / a.Hkv) + blockIdx.z * NH + (w >> 1);   // this wave's query head
@@ -604,7 +604,7 @@ __global__ __launch_bounds__(256) void lin_decode_kernel(LinArgs a) {
   const int G = a.Hq / a.Hkv;
   const int jj = threadIdx.x % NJ, rg = threadIdx.x / NJ;
   const int col = jq * NJ + jj;
-  const int wid = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   float* Sg = a.S + (size_t)bh * D * D;
   float s[RPT];
 #pragma unroll

@@ -461,7 +461,7 @@ __global__ __launch_bounds__(512) void mhc_mfma_kernel(MhcArgs a, const bf16_t* 
   __shared__ float ts[16][3];
   __shared__ float mp[16][3];
   const int C = a.C, C2 = 2 * C;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int li = lane & 15, g = lane >> 4;
   const int CW = C / 8, NS = CW / 32;
   const int mode = a.mode;
