@@ -57,6 +57,10 @@ def _bf16(t):
     ("decode64_gate_up", 64, 2 * F, C, 3, True), ("decode64_o", 64, C, HQ * D, 0, True),
     ("decode64_down_m45", 45, C, F, 0, True), ("head64_rows", 64, V, C, 1, True),
     ("decode64_qkv_nosplit_m33", 33, QKV, C, 0, False),
+    # row counts that end inside a 256-row tile (the epilogue's row bound)
+    ("gate_up_rows1000", 1000, 2 * F, C, 3, False), ("head_rows300", 300, V, C, 1, False),
+    # K % 64 == 32: the 32-deep eight-wave kernel
+    ("qkv_k4064_rows4133", 4133, QKV, 4064, 0, False), ("gate_up_k4064_rows1000", 1000, 2 * 2048, 4064, 3, False),
 ])
 def test_gemm_full_size_sampled(name, M, N, K, epi, split):
     """9B-shape projections; M <= 64 is the decode kernel, with K split over
