@@ -469,16 +469,48 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
           if (dr < rows_left) st1(Cl + (long)dr * a.ldc + jb * 32, acc[ib][jb][r]);
         }
   } else {
+    // QKV: a tile wholly in the V columns writes V^T [.., d][S_max]: a lane's
+    // four consecutive rows are four consecutive positions of one column, so
+    // they go out as one 8-byte store (same sequence and 4-aligned positions
+    // when S_call and pos0 are multiples of 4)
+    const int kvn = a.n_kv * a.head_dim;
+    const bool vtile = EPI == EPI_QKV && n0 >= a.q_cols + kvn && !a.pos_dev && a.S_call % 4 == 0 &&
+                       a.pos0 % 4 == 0 && (a.head_dim & 31) == 0;
+    if (vtile) {
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
+      for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
+        for (int jb = 0; jb < JB; ++jb) {
+          const int cc = n0 + wn * WCOL + jb * 32 + lcol - a.q_cols - kvn;
+          const int hk = cc / a.head_dim, dd = cc - hk * a.head_dim;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = m0 + lrow + ib * 32 + (r >> 2) * 8 + (r & 3);
-          const int col = n0 + wn * WCOL + jb * 32 + lcol;
-          if (row < a.M) epi_one<bf16_t, EPI>(a, row, col, acc[ib][jb][r]);
+          for (int g = 0; g < 4; ++g) {
+            const int row = m0 + lrow + ib * 32 + g * 8;     // rows row .. row + 3
+            if (row + 3 < a.M) {
+              const int b = row / a.S_call, pos = a.pos0 + row - b * a.S_call;
+              bf16_t* dst = (bf16_t*)a.vcache + (((size_t)b * a.n_kv + hk) * a.head_dim + dd) * a.S_max + pos;
+              const uint32_t w0 = pack_bf16x2(acc[ib][jb][g * 4], acc[ib][jb][g * 4 + 1]);
+              const uint32_t w1 = pack_bf16x2(acc[ib][jb][g * 4 + 2], acc[ib][jb][g * 4 + 3]);
+              *(u32x2_t*)dst = u32x2_t{w0, w1};
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (row + e < a.M) epi_one<bf16_t, EPI>(a, row + e, n0 + wn * WCOL + jb * 32 + lcol, acc[ib][jb][g * 4 + e]);
+            }
+          }
         }
+    } else {
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = m0 + lrow + ib * 32 + (r >> 2) * 8 + (r & 3);
+            const int col = n0 + wn * WCOL + jb * 32 + lcol;
+            if (row < a.M) epi_one<bf16_t, EPI>(a, row, col, acc[ib][jb][r]);
+          }
+    }
   }
 }
 
