@@ -32,7 +32,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # dispatch), each scaled by the same counter's reading for a plain 1 GiB
 # device copy in that run.  Valid only for the kernel source it was taken on:
 # the hash of k_gemm.hip + common.h must match, else traffic is reported null.
-DOMINANT_COUNTERS = {"source_sha256_16": "a5df5d307f213ee9", "fetch_kib": 4724175.6, "write_kib": 786442.6,
+DOMINANT_COUNTERS = {"source_sha256_16": "866eab9dfacf468a", "fetch_kib": 4724175.6, "write_kib": 786442.6,
                      "copy_fetch_kib": 524315.6, "copy_write_kib": 1048576.0}
 
 NINE_B = dict(vocab=248320, hidden=4096, ffn=12288, n_heads=32, n_kv_heads=8, head_dim=128,
@@ -44,11 +44,17 @@ def log(*a):
 
 
 def gemm_source_hash():
+    """Hash of the GEMM sources with comments and blank space removed, so that
+    a change of comments alone keeps the measured counters valid."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("k_gemm.hip", "common.h"):
-        with open(os.path.join(ROOT, "looped_weight_shared_loop_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "looped_weight_shared_loop_amd", "csrc", f), encoding="utf-8") as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

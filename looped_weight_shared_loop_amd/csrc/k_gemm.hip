@@ -1,8 +1,11 @@
 // Dense contractions of the looped decoder: C[M, N] = A[M, K] . B[N, K]^T.
 //
-// * gemm_dma:    bf16, M > 64.  256x256 workgroup tile, 8 waves of 128x64
-//                (v_mfma_f32_32x32x16_bf16), global -> LDS DMA through five
-//                LDS stages, XCD-aware tile order.  fp32 accumulation.
+// * gemm_w4:     bf16, M > 64, K % 64 == 0 (every model shape).  256x256
+//                workgroup tile, 4 waves of 128x128 (v_mfma_f32_32x32x16_bf16),
+//                64-deep k steps of whole-line global -> LDS DMA into two
+//                stages, XCD-aware tile order.  fp32 accumulation.
+// * gemm_dma:    bf16, M > 64, K % 64 == 32.  The same tile with 8 waves of
+//                128x64 and 32-deep steps through five LDS stages.
 // * gemm_skinny: bf16, M <= 64 (decode): streams B (the weights) once for up to
 //                64 token rows; 128-row tiles whose 4 waves split the rows and share the
 //                token operand through LDS; K split, when the tiles cannot fill
