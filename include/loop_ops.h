@@ -27,8 +27,9 @@ enum { LOOP_MHC_ENTER = 0, LOOP_MHC_MID = 1, LOOP_MHC_EXIT = 2 };
  * fp32 accumulation (the QKV, O, gate/up, down and head projections).
  * epi STORE: C dtype [M][N]; F32: C float32 [M][N]; SWIGLU: B holds gate rows
  * [0, F) then up rows [F, 2F) (N = 2F) and C dtype [M][F] = silu(A.Bg^T) * (A.Bu^T).
- * bf16 with M > 64 needs K % 32 == 0 and N (F for SWIGLU) a multiple of 256
- * (128 for SWIGLU); bf16 with M <= 64 (the decode shape: the weights are
+ * bf16 with M > 64 needs K % 32 == 0, N (F for SWIGLU) a multiple of 256
+ * (128 for SWIGLU) and 256 output rows within 2^31 bytes (ldc < 2^21 for
+ * float32 output); bf16 with M <= 64 (the decode shape: the weights are
  * streamed once for up to 64 token rows) needs K % 64 == 0.
  * For M <= 64, `scratch` of loop_op_gemm_bytes() bytes (device, caller-owned,
  * contents arbitrary) lets K be split over workgroups when the output tiles

@@ -1,10 +1,11 @@
 // Dense contractions of the looped decoder: C[M, N] = A[M, K] . B[N, K]^T.
 //
-// * gemm_w4:     bf16, M > 64, K % 64 == 0 (every model shape).  256x256
+// * gemm_w4:     bf16, M > 64, K % 128 == 0 (every model shape).  256x256
 //                workgroup tile, 4 waves of 128x128 (v_mfma_f32_32x32x16_bf16),
 //                64-deep k steps of whole-line global -> LDS DMA into two
-//                stages, XCD-aware tile order.  fp32 accumulation.
-// * gemm_dma:    bf16, M > 64, K % 64 == 32.  The same tile with 8 waves of
+//                stages, persistent workgroups, XCD-aware tile order.  fp32
+//                accumulation.
+// * gemm_dma:    bf16, M > 64, other K % 32 == 0.  The same tile with 8 waves of
 //                128x64 and 32-deep steps through five LDS stages.
 // * gemm_skinny: bf16, M <= 64 (decode): streams B (the weights) once for up to
 //                64 token rows; 128-row tiles whose 4 waves split the rows and share the
@@ -252,14 +253,20 @@ __global__ __launch_bounds__(128 * WN_, 1) void gemm_dma_kernel(GemmArgs a) {
 // chunk of 16 consecutive rows per 16 lanes, and with 64 four-byte banks two
 // rows span all banks, so the rows of one parity must use 8 distinct
 // positions.  Two 64 KB stages.  Within a step the fragments of substep
-// j + 1 are read while the MFMAs of substep j run.  The step's one barrier
-// sits before its last substep, whose fragments are already in registers: by
-// then every read of the stage has returned and the next step has landed, so
-// the next step's first reads overlap the last MFMAs.  The loads are issued
-// one after every second MFMA rather than in a burst (a burst stalls the
-// wave on a full load queue while its MFMA pipe idles): A of step kt + 2
-// during the last substep of step kt, into the stage just released, and B of
-// step kt + 2 during the first substep of step kt + 1.
+// j + 1 are read while the MFMAs of substep j run, one read after each of
+// the first eight MFMAs.  The step's one barrier sits before its last
+// substep, whose fragments are already in registers: by then every read of
+// the stage has returned and the next step has landed, so the next step's
+// first reads overlap the last MFMAs.  The loads are issued one after every
+// second MFMA rather than in a burst (a burst stalls the wave on a full load
+// queue while its MFMA pipe idles): A of step kt + 2 during the last substep
+// of step kt, into the stage just released, and B of step kt + 2 during the
+// first substep of step kt + 1.  Scheduling walls after every MFMA fix this
+// order.  The kernel is persistent: workgroup b takes tiles b, b + G, ...
+// (G a multiple of 8, at most the CU count) as one stream of k steps, so
+// the loads of a tile's first steps go out during the previous tile's last
+// steps and the epilogue (branch-free buffer stores) runs with them in
+// flight.
 // Against the eight-wave, 32-deep kernel above this halves the L2 requests
 // (whole lines) and cuts LDS fragment reads by a third (128x128 per wave).
 // MFMA j of a step contracts k 16 j .. 16 j + 15 (lane half h reads chunk
@@ -292,69 +299,105 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
   const int out_n = (EPI == EPI_SWIGLU) ? 128 : TBN;
   const int num_n = (EPI == EPI_SWIGLU ? a.F : a.N) / out_n;
   const int nblk = num_m * num_n;
-  // XCD-aware tile order, as in the kernel above.
-  int id = blockIdx.x;
-  if (nblk % 8 == 0) id = (id & 7) * (nblk >> 3) + (id >> 3);
+  const int G = gridDim.x;                 // workgroup b takes tiles b, b + G, b + 2 G, ...
   const int GM = num_n <= 16 ? 4 : 8;     // measured: 4 suits the 4096-wide outputs, 8 the wider ones
-  const int group = GM * num_n;
-  const int first_m = (id / group) * GM;
-  const int gsz = min(num_m - first_m, GM);
-  const int tm = first_m + (id % group) % gsz;
-  const int tn = (id % group) / gsz;
-  const int m0 = tm * TBM, n0 = tn * out_n;
-
-  // Buffer views of this tile's A rows and of B; byte offsets fit in 32 bits
-  // (the host checks 256 lda and the B rows against 2^31 elements).
-  const int mlast = a.M - 1 - m0;
-  const __amdgpu_buffer_rsrc_t Ar = buf_rsrc((const bf16_t*)a.A + (long)m0 * a.lda,
-                                             (unsigned)(min(TBM, a.M - m0) * a.lda * 2));
-  const __amdgpu_buffer_rsrc_t Br = buf_rsrc(a.B, 0xFFFFFFF0u);
-  // wave w issues DMA blocks 8 w .. 8 w + 7 of each operand: rows 8 blk + lane / 8,
-  // LDS chunk lane % 8 holds global chunk (lane % 8) ^ ((row >> 1) & 7)
-  int aoff[NB], boff[NB];
-#pragma unroll
-  for (int i = 0; i < NB; ++i) {
-    const int blk = wid * NB + i;
-    const int r = blk * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    aoff[i] = (min(r, mlast) * (int)a.lda + c * 8) * 2;
-    int br;
-    if (EPI == EPI_SWIGLU) {
-      const int w = r / WCOL, j = (r % WCOL) / 32, cc = r & 31;
-      const int oc = n0 + w * (WCOL / 2) + (j % (JB / 2)) * 32 + cc;
-      br = (j < JB / 2) ? oc : (a.F + oc);
-    } else {
-      br = n0 + r;
-    }
-    boff[i] = (br * (int)a.ldb + c * 8) * 2;
-  }
+  // Launch-order tile t -> output block.  XCD-aware as in the kernel above:
+  // workgroup b runs on XCD b % 8 and G is a multiple of 8 (or covers every
+  // tile), so tile t runs on XCD t % 8 and each XCD walks a contiguous range.
+  auto tile_mn = [&](int t, int& m0, int& n0) {
+    int id = t;
+    if (nblk % 8 == 0) id = (id & 7) * (nblk >> 3) + (id >> 3);
+    const int group = GM * num_n;
+    const int first_m = (id / group) * GM;
+    const int gsz = min(num_m - first_m, GM);
+    m0 = (first_m + (id % group) % gsz) * TBM;
+    n0 = ((id % group) / gsz) * out_n;
+  };
   const int KT = a.K / WBK;
-  // Steps past the end re-read the last step into the stage nobody reads
-  // again, so the loop body has no branch around its loads.
-  // one operand (op 0: A, op 1: B) of step kt: NB loads per wave
-  auto issue = [&](int kt, int op) {
-    bf16_t* st = smem + (kt & 1) * WSTAGE + op * TBM * WBK;
-    const int kb = min(kt, KT - 1) * WBK * 2;
+
+  // The workgroup's steps form one stream over its tiles; the loads run ahead
+  // of the MFMAs on two cursors (A two steps ahead, B one), so the first
+  // steps of the next tile are in LDS by the time this tile's last MFMAs end
+  // and its epilogue runs.  A cursor past the last tile re-reads the last
+  // step into the stage nobody reads again, so the loop has no branch around
+  // its loads.
+  // Wave w issues DMA blocks 8 w .. 8 w + 7 of each operand: rows 8 blk + lane / 8,
+  // LDS chunk lane % 8 holds global chunk (lane % 8) ^ ((row >> 1) & 7).
+  // Buffer views of the tile's A rows and of B: byte offsets fit in 32 bits
+  // (the host checks 256 lda and the B rows against 2^31 elements).
+  int a_t = blockIdx.x, a_kt = 0, b_t = blockIdx.x, b_kt = 0;
+  __amdgpu_buffer_rsrc_t Ar;
+  const __amdgpu_buffer_rsrc_t Br = buf_rsrc(a.B, 0xFFFFFFF0u);
+  int aoff[NB], boff[NB];
+  auto set_a = [&](int t) {
+    int m0, n0;
+    tile_mn(t, m0, n0);
+    const int mlast = a.M - 1 - m0;
+    Ar = buf_rsrc((const bf16_t*)a.A + (long)m0 * a.lda, (unsigned)(min(TBM, a.M - m0) * a.lda * 2));
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int r = (wid * NB + i) * 8 + (lane >> 3);
+      aoff[i] = (min(r, mlast) * (int)a.lda + ((lane & 7) ^ ((r >> 1) & 7)) * 8) * 2;
+    }
+  };
+  auto set_b = [&](int t) {
+    int m0, n0;
+    tile_mn(t, m0, n0);
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int r = (wid * NB + i) * 8 + (lane >> 3);
+      int br;
+      if (EPI == EPI_SWIGLU) {
+        const int w = r / WCOL, j = (r % WCOL) / 32, cc = r & 31;
+        const int oc = n0 + w * (WCOL / 2) + (j % (JB / 2)) * 32 + cc;
+        br = (j < JB / 2) ? oc : (a.F + oc);
+      } else {
+        br = n0 + r;
+      }
+      boff[i] = (br * (int)a.ldb + ((lane & 7) ^ ((r >> 1) & 7)) * 8) * 2;
+    }
+  };
+  auto next_a = [&]() {
+    if (++a_kt == KT) {
+      if (a_t + G < nblk) {
+        a_t += G;
+        a_kt = 0;
+        set_a(a_t);
+      } else {
+        a_kt = KT - 1;
+      }
+    }
+  };
+  auto next_b = [&]() {
+    if (++b_kt == KT) {
+      if (b_t + G < nblk) {
+        b_t += G;
+        b_kt = 0;
+        set_b(b_t);
+      } else {
+        b_kt = KT - 1;
+      }
+    }
+  };
+  set_a(a_t);
+  set_b(b_t);
+  // one operand (op 0: A, op 1: B) at its cursor, NB loads per wave, into stage par
+  auto issue = [&](int par, int op) {
+    bf16_t* st = smem + par * WSTAGE + op * TBM * WBK;
     if (op == 0) {
 #pragma unroll
-      for (int i = 0; i < NB; ++i) dma16_buf(Ar, aoff[i], kb, st + (wid * NB + i) * 512);
+      for (int i = 0; i < NB; ++i) dma16_buf(Ar, aoff[i], a_kt * WBK * 2, st + (wid * NB + i) * 512);
     } else {
 #pragma unroll
-      for (int i = 0; i < NB; ++i) dma16_buf(Br, boff[i], kb, st + (wid * NB + i) * 512);
+      for (int i = 0; i < NB; ++i) dma16_buf(Br, boff[i], b_kt * WBK * 2, st + (wid * NB + i) * 512);
     }
   };
   f32x16_t acc[4][JB];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < JB; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int arow = wm * 128 + (lane & 31);
   const int brow = wn * WCOL + (lane & 31);
   bf16x8_t fa[2][4], fb[2][JB];
-  // par: the stage, kt & 1, passed as a constant so LDS addresses fold into offsets
+  // par: the stage, step & 1, passed as a constant so LDS addresses fold into offsets
   auto read_frags = [&](int par, int j, bf16x8_t (&xa)[4], bf16x8_t (&xb)[JB]) {
     const bf16_t* as = smem + par * WSTAGE;
     const bf16_t* bs = as + TBM * WBK;
@@ -364,157 +407,176 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
 #pragma unroll
     for (int jb = 0; jb < JB; ++jb) xb[jb] = as_bf16x8(ldv4(bs + wswz(brow + jb * 32, ch)));
   };
-  auto mma = [&](const bf16x8_t (&xa)[4], const bf16x8_t (&xb)[JB]) {
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb) acc[ib][jb] = mfma32(xa[ib], xb[jb], acc[ib][jb]);
-  };
-  // the 8 fragment reads of the next substep one-to-one with the first 8 of the 16 MFMAs
-  auto interleave = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4 + JB; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, 4 * JB - (4 + JB), 0);
-  };
-  // The 16 MFMAs of a substep with the NB loads of one operand of step kt,
-  // one load after every second MFMA (scheduling walls keep that order), so
-  // the wave never stalls on a burst of loads while its MFMA pipe idles.
-  auto mma_dma = [&](const bf16x8_t (&xa)[4], const bf16x8_t (&xb)[JB], int kt, int par, int op) {
-    bf16_t* st = smem + par * WSTAGE + op * TBM * WBK;
-    const int kb = min(kt, KT - 1) * WBK * 2;
+  // Load L of a step (L < 8: A block L, else B block L - 8) goes out after
+  // MFMA w of the step's load window: the last substep of the step two
+  // before (w 0..15, after that step's barrier has freed the stage), then
+  // the substeps of the step before (w 16..).  One load per LSP MFMAs; with
+  // LSP = 2 the A blocks fill the first part and the B blocks the first
+  // substep of the step before, so every load has at least two substeps to
+  // land before the barrier that waits for it (spreading them one per three
+  // MFMAs, into the second substep, measured slower on the wide shapes).
+  constexpr int LSP = 2;
+  static_assert(LSP >= 2 && LSP * (2 * NB - 1) < 48, "every load needs a slot before the third substep");
+  auto load_slot = [](int w) { return (w % LSP == 0 && w / LSP < 2 * NB) ? w / LSP : -1; };
+  // One substep: its 16 MFMAs (first: from zero accumulators), after MFMA
+  // q < 8 the fragment read q of the next substep (rd >= 0: substep rd of
+  // stage rpar), and the loads of window slots w0 + q (w0 >= 0) into stage
+  // lpar.  Scheduling walls keep this order.
+  auto substep = [&](const bf16x8_t (&xa)[4], const bf16x8_t (&xb)[JB], bool first, int rpar, int rd,
+                     bf16x8_t (&ya)[4], bf16x8_t (&yb)[JB], int w0, int lpar) {
+    const bf16_t* as = smem + rpar * WSTAGE;
+    const bf16_t* bs = as + TBM * WBK;
+    const int ch = rd * 2 + (lane >> 5);
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int ib = q >> 2, jb = q & 3;
-      acc[ib][jb] = mfma32(xa[ib], xb[jb], acc[ib][jb]);
-      if (q & 1) {
-        const int i = q >> 1;
-        if (op == 0) dma16_buf(Ar, aoff[i], kb, st + (wid * NB + i) * 512);
-        else dma16_buf(Br, boff[i], kb, st + (wid * NB + i) * 512);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      acc[ib][jb] = mfma32(xa[ib], xb[jb], first ? f32x16_t{} : acc[ib][jb]);
+      if (rd >= 0 && q < 4) ya[q] = as_bf16x8(ldv4(as + wswz(arow + q * 32, ch)));
+      if (rd >= 0 && q >= 4 && q < 4 + JB) yb[q - 4] = as_bf16x8(ldv4(bs + wswz(brow + (q - 4) * 32, ch)));
+      const int L = w0 >= 0 ? load_slot(w0 + q) : -1;
+      if (L >= 0 && L < NB)
+        dma16_buf(Ar, aoff[L], a_kt * WBK * 2, smem + lpar * WSTAGE + (wid * NB + L) * 512);
+      if (L >= NB)
+        dma16_buf(Br, boff[L - NB], b_kt * WBK * 2, smem + lpar * WSTAGE + TBM * WBK + (wid * NB + L - NB) * 512);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   auto sync = [&]() {
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
+  // A and B of stream step 0 into stage 0, then the loads of step 1 that
+  // belong to the window's first part (A blocks) into stage 1
   issue(0, 0);
+  next_a();
   issue(0, 1);
-  issue(1, 0);
-  asm volatile("s_waitcnt vmcnt(8)" ::: "memory");   // step 0 landed (A of step 1 may fly)
+  next_b();
+  constexpr int NA0 = (16 + LSP - 1) / LSP;    // slots w < 16
+#pragma unroll
+  for (int L = 0; L < NA0; ++L)
+    dma16_buf(Ar, aoff[L], a_kt * WBK * 2, smem + WSTAGE + (wid * NB + L) * 512);
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NA0) : "memory");   // step 0 landed
   sync();
   read_frags(0, 0, fa[0], fb[0]);
-  auto step = [&](int kt, int par) {
-    // B of step kt + 1 into the stage of step kt - 1 (free since the last barrier)
-    read_frags(par, 1, fa[1], fb[1]);
-    mma_dma(fa[0], fb[0], kt + 1, par ^ 1, 1);
-    read_frags(par, 2, fa[0], fb[0]);
-    mma(fa[1], fb[1]);
-    interleave();
-    read_frags(par, 3, fa[1], fb[1]);
-    mma(fa[0], fb[0]);
-    interleave();
+  // Stream step s of the stage par = s & 1.  The loads of step s + 1 (into
+  // the other stage, free since the last barrier) finish in the first two
+  // substeps; after the barrier the stage of step s takes the first loads of
+  // step s + 2 while the last substep's MFMAs run.  The first substep of
+  // step s + 1 is read during those MFMAs, except after a tile's last step
+  // (last), where it is read after the epilogue so that it does not hold
+  // registers across it.
+  auto step = [&](int par, bool first, bool last) {
+    substep(fa[0], fb[0], first, par, 1, fa[1], fb[1], 16, par ^ 1);
+    substep(fa[1], fb[1], false, par, 2, fa[0], fb[0], 32, par ^ 1);
+    next_a();
+    next_b();
+    substep(fa[0], fb[0], false, par, 3, fa[1], fb[1], -1, 0);
     // Every read of this stage has returned (their registers feed the MFMAs
-    // below) and this wave's loads of step kt + 1 have landed; after the
-    // barrier the stage of step kt takes A of step kt + 2 while the last
-    // substep's MFMAs run.
+    // below) and this wave's loads of step s + 1 have landed.
     asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
     sync();
-    read_frags(par ^ 1, 0, fa[0], fb[0]);
-    mma_dma(fa[1], fb[1], kt + 2, par, 0);
+    substep(fa[1], fb[1], false, par ^ 1, last ? -1 : 0, fa[0], fb[0], 0, par);
   };
-  // steps 0 .. KT - 2, two per trip so that the stage of each is a constant
-  int kt = 0;
-  for (; kt + 2 < KT; kt += 2) {
-    step(kt, 0);
-    step(kt + 1, 1);
-  }
-  if (kt + 1 < KT) step(kt++, 0);
-  read_frags(kt & 1, 1, fa[1], fb[1]);
-  mma(fa[0], fb[0]);
-  read_frags(kt & 1, 2, fa[0], fb[0]);
-  mma(fa[1], fb[1]);
-  read_frags(kt & 1, 3, fa[1], fb[1]);
-  mma(fa[0], fb[0]);
-  mma(fa[1], fb[1]);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
 
-  // Epilogue: each lane's stores go to one base pointer plus offsets that
-  // are the same for the whole wave (row step times ldc); rows past M are
-  // skipped.
-  const int lrow = wm * 128 + (lane >> 5) * 4, lcol = lane & 31;
-  const int rows_left = a.M - m0 - lrow;     // this lane's rows r < rows_left exist
-  if (EPI == EPI_SWIGLU) {
-    bf16_t* Cl = (bf16_t*)a.C + ((size_t)(m0 + lrow)) * a.ldc + n0 + wn * (WCOL / 2) + lcol;
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < JB / 2; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int dr = ib * 32 + (r >> 2) * 8 + (r & 3);
-          if (dr < rows_left)
-            st1(Cl + (long)dr * a.ldc + jb * 32, silu(acc[ib][jb][r]) * acc[ib][jb + JB / 2][r]);
-        }
-  } else if (EPI == EPI_STORE || EPI == EPI_F32) {
-    using T = typename std::conditional<EPI == EPI_F32, float, bf16_t>::type;
-    T* Cl = (T*)a.C + ((size_t)(m0 + lrow)) * a.ldc + n0 + wn * WCOL + lcol;
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-      for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int dr = ib * 32 + (r >> 2) * 8 + (r & 3);
-          if (dr < rows_left) st1(Cl + (long)dr * a.ldc + jb * 32, acc[ib][jb][r]);
-        }
-  } else {
-    // QKV: a tile wholly in the V columns writes V^T [.., d][S_max]: a lane's
-    // four consecutive rows are four consecutive positions of one column, so
-    // they go out as one 8-byte store (same sequence and 4-aligned positions
-    // when S_call and pos0 are multiples of 4)
-    const int kvn = a.n_kv * a.head_dim;
-    const bool vtile = EPI == EPI_QKV && n0 >= a.q_cols + kvn && !a.pos_dev && a.S_call % 4 == 0 &&
-                       a.pos0 % 4 == 0 && (a.head_dim & 31) == 0;
-    if (vtile) {
+  // Epilogue.  Plain stores (SwiGLU, bf16 or fp32 output, and QKV tiles
+  // wholly in the q columns) go through a buffer view of the tile's rows that
+  // ends at row M, so the hardware drops the rows past M and the stores need
+  // no branches: a lane's offset is its own column plus a row step that is
+  // the same for the whole wave.
+  auto epilogue = [&](int m0, int n0) {
+    const int lrow = wm * 128 + (lane >> 5) * 4, lcol = lane & 31;
+    if (EPI == EPI_SWIGLU || EPI == EPI_STORE || EPI == EPI_F32 || n0 + TBN <= a.q_cols) {
+      constexpr int ES = EPI == EPI_F32 ? 4 : 2;      // output element bytes
+      int ldcb = (int)a.ldc * ES;
+      // opaque here, so the 64 row offsets below are formed per tile rather
+      // than hoisted out of the tile loop, where they would hold registers
+      asm volatile("" : "+s"(ldcb));
+      const __amdgpu_buffer_rsrc_t Cr =
+          buf_rsrc((const char*)a.C + (size_t)m0 * ldcb, (unsigned)(min(TBM, a.M - m0) * ldcb));
+      const int lb = lrow * ldcb + (n0 + wn * (EPI == EPI_SWIGLU ? WCOL / 2 : WCOL) + lcol) * ES;
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb) {
-          const int cc = n0 + wn * WCOL + jb * 32 + lcol - a.q_cols - kvn;
-          const int hk = cc / a.head_dim, dd = cc - hk * a.head_dim;
+        for (int r = 0; r < 16; ++r) {
+          const int vo = lb + (ib * 32 + (r >> 2) * 8 + (r & 3)) * ldcb;
+          if (EPI == EPI_SWIGLU) {
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int row = m0 + lrow + ib * 32 + g * 8;     // rows row .. row + 3
-            if (row + 3 < a.M) {
-              const int b = row / a.S_call, pos = a.pos0 + row - b * a.S_call;
-              bf16_t* dst = (bf16_t*)a.vcache + (((size_t)b * a.n_kv + hk) * a.head_dim + dd) * a.S_max + pos;
-              const uint32_t w0 = pack_bf16x2(acc[ib][jb][g * 4], acc[ib][jb][g * 4 + 1]);
-              const uint32_t w1 = pack_bf16x2(acc[ib][jb][g * 4 + 2], acc[ib][jb][g * 4 + 3]);
-              *(u32x2_t*)dst = u32x2_t{w0, w1};
-            } else {
+            for (int jb = 0; jb < JB / 2; ++jb)
+              __builtin_amdgcn_raw_buffer_store_b16(f2bf(silu(acc[ib][jb][r]) * acc[ib][jb + JB / 2][r]), Cr,
+                                                    vo + jb * 32 * ES, 0, 0);
+          } else if (EPI == EPI_F32) {
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (row + e < a.M) epi_one<bf16_t, EPI>(a, row + e, n0 + wn * WCOL + jb * 32 + lcol, acc[ib][jb][g * 4 + e]);
-            }
+            for (int jb = 0; jb < JB; ++jb)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[ib][jb][r]), Cr, vo + jb * 32 * ES, 0, 0);
+          } else {
+#pragma unroll
+            for (int jb = 0; jb < JB; ++jb)
+              __builtin_amdgcn_raw_buffer_store_b16(f2bf(acc[ib][jb][r]), Cr, vo + jb * 32 * ES, 0, 0);
           }
         }
     } else {
+      // QKV: a tile wholly in the V columns writes V^T [.., d][S_max]: a lane's
+      // four consecutive rows are four consecutive positions of one column, so
+      // they go out as one 8-byte store (same sequence and 4-aligned positions
+      // when S_call and pos0 are multiples of 4)
+      const int kvn = a.n_kv * a.head_dim;
+      const bool vtile = EPI == EPI_QKV && n0 >= a.q_cols + kvn && !a.pos_dev && a.S_call % 4 == 0 &&
+                         a.pos0 % 4 == 0 && (a.head_dim & 31) == 0;
+      if (vtile) {
 #pragma unroll
-      for (int ib = 0; ib < 4; ++ib)
+        for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
-        for (int jb = 0; jb < JB; ++jb)
+          for (int jb = 0; jb < JB; ++jb) {
+            const int cc = n0 + wn * WCOL + jb * 32 + lcol - a.q_cols - kvn;
+            const int hk = cc / a.head_dim, dd = cc - hk * a.head_dim;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = m0 + lrow + ib * 32 + (r >> 2) * 8 + (r & 3);
-            const int col = n0 + wn * WCOL + jb * 32 + lcol;
-            if (row < a.M) epi_one<bf16_t, EPI>(a, row, col, acc[ib][jb][r]);
+            for (int g = 0; g < 4; ++g) {
+              const int row = m0 + lrow + ib * 32 + g * 8;     // rows row .. row + 3
+              if (row + 3 < a.M) {
+                const int b = row / a.S_call, pos = a.pos0 + row - b * a.S_call;
+                bf16_t* dst = (bf16_t*)a.vcache + (((size_t)b * a.n_kv + hk) * a.head_dim + dd) * a.S_max + pos;
+                const uint32_t w0 = pack_bf16x2(acc[ib][jb][g * 4], acc[ib][jb][g * 4 + 1]);
+                const uint32_t w1 = pack_bf16x2(acc[ib][jb][g * 4 + 2], acc[ib][jb][g * 4 + 3]);
+                *(u32x2_t*)dst = u32x2_t{w0, w1};
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (row + e < a.M)
+                    epi_one<bf16_t, EPI>(a, row + e, n0 + wn * WCOL + jb * 32 + lcol, acc[ib][jb][g * 4 + e]);
+              }
+            }
           }
+      } else {
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib)
+#pragma unroll
+          for (int jb = 0; jb < JB; ++jb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = m0 + lrow + ib * 32 + (r >> 2) * 8 + (r & 3);
+              const int col = n0 + wn * WCOL + jb * 32 + lcol;
+              if (row < a.M) epi_one<bf16_t, EPI>(a, row, col, acc[ib][jb][r]);
+            }
+      }
     }
+  };
+
+  // Tiles of this workgroup; KT is even (the host checks), so every tile
+  // starts on stage 0 and two steps per trip keep the stage of each a
+  // constant.
+  for (int t = blockIdx.x; t < nblk; t += G) {
+    step(0, true, false);
+    for (int kt = 1; kt + 2 < KT; kt += 2) {
+      step(1, false, false);
+      step(0, false, false);
+    }
+    step(1, false, true);
+    int m0, n0;
+    tile_mn(t, m0, n0);
+    epilogue(m0, n0);
+    read_frags(0, 0, fa[0], fb[0]);
   }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
 }
 
 // ------------------------------------------------------------------ skinny (M <= 64)
@@ -834,13 +896,18 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
     return a.M > 32 ? launch_skinny_rs<EPI, 2>(a, s) : launch_skinny_rs<EPI, 1>(a, s);
   }
   if (a.K % DBK) return hipErrorInvalidValue;
-  if ((long)TBM * a.lda >= (1L << 31) || (long)(EPI == EPI_SWIGLU ? 2 * a.F : a.N) * a.ldb >= (1L << 31))
+  if ((long)TBM * a.lda >= (1L << 31) || (long)(EPI == EPI_SWIGLU ? 2 * a.F : a.N) * a.ldb >= (1L << 31) ||
+      (long)TBM * a.ldc * 4 >= (1L << 31))
     return hipErrorInvalidValue;
   const int out_n = (EPI == EPI_SWIGLU) ? 128 : TBN;
   const int ncols = (EPI == EPI_SWIGLU) ? a.F : a.N;
   if (ncols % out_n) return hipErrorInvalidValue;
   const int blocks = ((a.M + TBM - 1) / TBM) * (ncols / out_n);
-  if (a.K % WBK == 0) return launch_w4<EPI>(a, blocks, s);
+  if (a.K % (2 * WBK) == 0) {
+    // persistent: one workgroup per CU (a multiple of 8, for the XCD order)
+    const int cu = device_cu_count() & ~7;
+    return launch_w4<EPI>(a, (cu > 0 && blocks > cu) ? cu : blocks, s);
+  }
   return launch_dma<EPI, 4>(a, blocks, s);
 }
 
