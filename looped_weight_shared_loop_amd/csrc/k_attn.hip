@@ -116,20 +116,29 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
   // Software pipeline: the score MFMAs of tile kt + 1 are issued before the
   // softmax and PV of tile kt, so the softmax VALU work runs while they execute.
   f32x16_t sa[2], sb[2];                     // scores of the current / next tile
+  // The two 32-key blocks alternate, so consecutive MFMAs are independent;
+  // the K fragments of chunk ds + SA are read while the MFMAs of chunk ds
+  // run (scheduling walls keep that order), so the MFMAs do not wait on the
+  // LDS latency.
+  constexpr int SA = 2;
   auto scores = [&](int kt, f32x16_t (&st)[2]) {
     const bf16_t* ks = smem + (kt % AQ_NS) * AQ_STAGE;
+    bf16x8_t kf[SA + 1][2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int ds = 0; ds < SA; ++ds)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) st[c][r] = 0.f;
-    // the two 32-key blocks alternate, so consecutive MFMAs are independent
+      for (int c = 0; c < 2; ++c) kf[ds][c] = as_bf16x8(ldv4(ks + kq_sw(c * 32 + krow, ds * 2 + h)));
 #pragma unroll
-    for (int ds = 0; ds < 8; ++ds)
+    for (int ds = 0; ds < 8; ++ds) {
+      if (ds + SA < 8) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const bf16x8_t kf = as_bf16x8(ldv4(ks + kq_sw(c * 32 + krow, ds * 2 + h)));
-        st[c] = mfma32(kf, qf[ds], st[c]);
+        for (int c = 0; c < 2; ++c)
+          kf[(ds + SA) % (SA + 1)][c] = as_bf16x8(ldv4(ks + kq_sw(c * 32 + krow, (ds + SA) * 2 + h)));
       }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) st[c] = mfma32(kf[ds % (SA + 1)][c], qf[ds], ds == 0 ? f32x16_t{} : st[c]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
   auto softmax_pv = [&](int kt, f32x16_t (&st)[2]) {
     const bf16_t* vs = smem + (kt % AQ_NS) * AQ_STAGE + PK * PD;
