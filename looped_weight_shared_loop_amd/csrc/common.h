@@ -60,14 +60,36 @@ DEV void st8(float* p, const float* v) {
   *reinterpret_cast<float4*>(p + 4) = make_float4(v[4], v[5], v[6], v[7]);
 }
 
+// v combined with v of lane l ^ 32 (l ^ 16) without an LDS round trip:
+// v_permlane32_swap (v_permlane16_swap) exchanges the odd 32- (16-) lane rows
+// of one copy of v with the even rows of another, so each lane ends up with
+// its own value in one copy and its partner's in the other.  Sum and max are
+// commutative, so the results equal those of a shuffle bit for bit.
+DEV void xswap32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+DEV void xswap16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+DEV float x32_sum(float v) { float a, b; xswap32(v, a, b); return a + b; }
+DEV float x32_max(float v) { float a, b; xswap32(v, a, b); return fmaxf(a, b); }
+DEV float x16_sum(float v) { float a, b; xswap16(v, a, b); return a + b; }
+DEV float x16_max(float v) { float a, b; xswap16(v, a, b); return fmaxf(a, b); }
+
 DEV float wave_sum(float v) {
+  v = x16_sum(x32_sum(v));
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  for (int o = 8; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
 DEV float wave_max(float v) {
+  v = x16_max(x32_max(v));
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  for (int o = 8; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
 }
 

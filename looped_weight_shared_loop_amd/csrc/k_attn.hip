@@ -161,7 +161,7 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[c][r]);
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64)) * sc;     // scaled (base-2) units
+    tmax = x32_max(tmax) * sc;     // scaled (base-2) units
     const float mnew = fmaxf(mrun, tmax);
     const float mfin = (mnew == -INFINITY) ? 0.f : mnew;
     float psum = 0.f;
@@ -239,7 +239,7 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
   if (qvalid) {
-    const float ltot = lrun + __shfl_xor(lrun, 32, 64);
+    const float ltot = x32_sum(lrun);
     const float inv = 1.0f / ltot;
     bf16_t* O = (bf16_t*)a.out + (size_t)(b * a.S_call + m) * a.ldo + j * PD;
 #pragma unroll
@@ -350,8 +350,7 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
         st[sb][i] = v;
         tmax = fmaxf(tmax, v);
       }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    tmax = x32_max(x16_max(tmax));
     const float mnew = fmaxf(mrun, tmax);
     const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(mrun - mnew);
     float psum = 0.f;
@@ -392,8 +391,7 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
     }
   }
   // full row sum of a column (its four lane groups)
-  float ltot = lrun + __shfl_xor(lrun, 16, 64);
-  ltot += __shfl_xor(ltot, 32, 64);
+  float ltot = x32_sum(x16_sum(lrun));
 
   // merge waves: step h = 4, 2, 1: waves [h, 2h) hand their state to w - h
   for (int h = DW / 2; h >= 1; h >>= 1) {

@@ -522,7 +522,7 @@ __global__ __launch_bounds__(128 * NH, 1) void lin_out_bf(LinArgs a) {
     if (x <= tb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) den += at[x][r];
-  den += __shfl_xor(den, 32, 64);
+  den = x32_sum(den);
   // num^T += V^T A^T: k-step (x, half) covers tau 32x + 16half + {4h .. 4h+3, 8+4h .. 8+4h+3}
 #pragma unroll
   for (int x = 0; x < 2; ++x)

@@ -331,12 +331,6 @@ __global__ __launch_bounds__(512) void mhc_kernel(MhcArgs a) {
 //     the X' that A wrote (the kernel boundary orders the two).
 constexpr int MHC_SLICE = 512;
 
-DEV float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 template <typename T>
 __global__ __launch_bounds__(64) void mhc_slice_a(MhcArgs a, float* __restrict__ part) {
   const int C = a.C, nsl = C / MHC_SLICE;
@@ -560,9 +554,9 @@ __global__ __launch_bounds__(512) void mhc_mfma_kernel(MhcArgs a, const bf16_t* 
     // acc[r]: token 4 g + r, column li; the stream sums of token li are split over the 4 groups
 #pragma unroll
     for (int r = 0; r < 4; ++r) red_acc[w][4 * g + r][li] = acc[r];
-    s00 += __shfl_xor(s00, 16, 64); s00 += __shfl_xor(s00, 32, 64);
-    s11 += __shfl_xor(s11, 16, 64); s11 += __shfl_xor(s11, 32, 64);
-    s01 += __shfl_xor(s01, 16, 64); s01 += __shfl_xor(s01, 32, 64);
+    s00 = x32_sum(x16_sum(s00));
+    s11 = x32_sum(x16_sum(s11));
+    s01 = x32_sum(x16_sum(s01));
     if (g == 0) { red_s[w][li][0] = s00; red_s[w][li][1] = s11; red_s[w][li][2] = s01; }
     __syncthreads();
     if (tid < 256) {
