@@ -115,6 +115,11 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
   static_assert(AQ_NS == 4 && NW == 8 && NB == 2, "wait counts below");
   // Software pipeline: the score MFMAs of tile kt + 1 are issued before the
   // softmax and PV of tile kt, so the softmax VALU work runs while they execute.
+  // The two waves of a SIMD reach the same phase together after each barrier;
+  // a wave raises its issue priority for its score MFMAs (and keeps a middle
+  // one through softmax and PV), so the SIMD's other wave fills the VALU
+  // slots rather than both waves alternating instruction by instruction
+  // (measured: 3% over equal priorities; results are unchanged).
   f32x16_t sa[2], sb[2];                     // scores of the current / next tile
   // The two 32-key blocks alternate, so consecutive MFMAs are independent;
   // the K fragments of chunk ds + SA are read while the MFMAs of chunk ds
@@ -226,16 +231,22 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
     sync();
     issue(kt + AHEAD);                       // into the stage of tile kt - 1, finished before this barrier
     if (kt + 1 == ntiles - 1 && ragged) mask_tail();   // ordered before its PV by the next barrier
+    __builtin_amdgcn_s_setprio(2);
     if ((kt + 1) * PK <= wave_last) scores(kt + 1, sb);   // wave-uniform: tiles past the
+    __builtin_amdgcn_s_setprio(1);
     if (kt * PK <= wave_last) softmax_pv(kt, sa);           // wave's last query are skipped
+    __builtin_amdgcn_s_setprio(0);
     if (kt + 1 >= ntiles) break;
     // odd step: scores of kt + 2 into sa, softmax / PV of kt + 1 from sb
     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     sync();
     issue(kt + 1 + AHEAD);
     if (kt + 2 == ntiles - 1 && ragged) mask_tail();
+    __builtin_amdgcn_s_setprio(2);
     if ((kt + 2) * PK <= wave_last) scores(kt + 2, sa);
+    __builtin_amdgcn_s_setprio(1);
     if ((kt + 1) * PK <= wave_last) softmax_pv(kt + 1, sb);
+    __builtin_amdgcn_s_setprio(0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
   if (qvalid) {
