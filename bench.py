@@ -32,7 +32,7 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # dispatch), each scaled by the same counter's reading for a plain 1 GiB
 # device copy in that run.  Valid only for the kernel source it was taken on:
 # the hash of k_gemm.hip + common.h must match, else traffic is reported null.
-DOMINANT_COUNTERS = {"source_sha256_16": "00c110947d4c57e3", "fetch_kib": 4929542.5, "write_kib": 807168.0,
+DOMINANT_COUNTERS = {"source_sha256_16": "fde6365338384f30", "fetch_kib": 4929292.1, "write_kib": 807168.0,
                      "copy_fetch_kib": 524315.0, "copy_write_kib": 1048576.0}
 
 NINE_B = dict(vocab=248320, hidden=4096, ffn=12288, n_heads=32, n_kv_heads=8, head_dim=128,
