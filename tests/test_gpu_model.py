@@ -431,14 +431,18 @@ def test_group_9b_width_hidden_out():
     assert err < HIDDEN_TOL and rms < HIDDEN_RMS_TOL
 
 
-@pytest.mark.parametrize("shape", [(1, 0, 1, 1), (4, 3, 4, 1)], ids=["one_looped_linear", "three_plain_one_looped_full"])
-def test_group_9b_width_shallow(shape):
+@pytest.mark.parametrize("shape,S", [((1, 0, 1, 1, 4), 160), ((4, 3, 4, 1, 4), 160), ((1, 0, 1, 1, 1), 2900)],
+                         ids=["one_looped_linear", "three_plain_one_looped_full", "one_looped_full_2900"])
+def test_group_9b_width_shallow(shape, S):
     """Shallow stacks at 9B width, where rounding-flip growth is small, held to
     the logits bar: one looped linear-attention layer (enter, two sites, exit),
-    and three plain linear layers followed by one looped full-attention layer."""
-    n_layers, ls, le, P = shape
-    ocfg = oracle.group_config(n_layers=n_layers, loop_start=ls, loop_end=le, n_passes=P)
-    S = 160
+    three plain linear layers followed by one looped full-attention layer, and
+    one looped full-attention layer (attention period 1) at S=2900.  There the
+    projections have 12 row tiles of 256 (the last one ragged), so the QKV
+    projection's 288 output tiles exceed the CU count and each persistent GEMM
+    workgroup writes q, K-cache and V-cache tiles in turn."""
+    n_layers, ls, le, P, period = shape
+    ocfg = oracle.group_config(n_layers=n_layers, loop_start=ls, loop_end=le, n_passes=P, attn_period=period)
     model, Wo = build_pair(ocfg, cache_layers=4)
     emb = synth.normal_bf16_as_f32(1, synth.TID_EMBEDS_IN, (1, S, ocfg.hidden))
     ref = oracle.forward(ocfg, Wo, embeds=emb, hidden_out=True)
@@ -446,7 +450,7 @@ def test_group_9b_width_shallow(shape):
     got = model.prefill(st, embeds=torch.from_numpy(emb).to(torch.bfloat16).cuda(), hidden_out=True)
     g = got.float().cpu().numpy()
     err, rms = rel(g, ref), rms_rel(g, ref)
-    _say(shape, "rel err", err, "row rms", rms)
+    _say(shape, S, "rel err", err, "row rms", rms)
     assert err < BF16_TOL
 
 
