@@ -485,15 +485,28 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
   // the same for the whole wave.
   auto epilogue = [&](int m0, int n0) {
     const int lrow = wm * 128 + (lane >> 5) * 4, lcol = lane & 31;
-    if (EPI == EPI_SWIGLU || EPI == EPI_STORE || EPI == EPI_F32 || n0 + TBN <= a.q_cols) {
+    // QKV tile wholly in the K columns, head_dim 128 (a wave's 128 columns are
+    // one KV head) and rows in one sequence: its K-cache rows [pos][d] are a
+    // plain row-major block, stored like the q tiles
+    int ksq = -1;
+    if (EPI == EPI_QKV && n0 >= a.q_cols && n0 + TBN <= a.q_cols + a.n_kv * a.head_dim && a.head_dim == WCOL &&
+        !a.pos_dev && m0 / a.S_call == (min(m0 + TBM, a.M) - 1) / a.S_call)
+      ksq = m0 / a.S_call;
+    if (EPI == EPI_SWIGLU || EPI == EPI_STORE || EPI == EPI_F32 || n0 + TBN <= a.q_cols || ksq >= 0) {
       constexpr int ES = EPI == EPI_F32 ? 4 : 2;      // output element bytes
-      int ldcb = (int)a.ldc * ES;
+      int ldcb = (int)(ksq >= 0 ? a.head_dim : a.ldc) * ES;
       // opaque here, so the 64 row offsets below are formed per tile rather
       // than hoisted out of the tile loop, where they would hold registers
       asm volatile("" : "+s"(ldcb));
-      const __amdgpu_buffer_rsrc_t Cr =
-          buf_rsrc((const char*)a.C + (size_t)m0 * ldcb, (unsigned)(min(TBM, a.M - m0) * ldcb));
-      const int lb = lrow * ldcb + (n0 + wn * (EPI == EPI_SWIGLU ? WCOL / 2 : WCOL) + lcol) * ES;
+      const char* base = (const char*)a.C + (size_t)m0 * ldcb;
+      int lb = lrow * ldcb + (n0 + wn * (EPI == EPI_SWIGLU ? WCOL / 2 : WCOL) + lcol) * ES;
+      if (ksq >= 0) {
+        const int hk = (n0 - a.q_cols) / WCOL + wn;
+        base = (const char*)a.kcache +
+               (((size_t)ksq * a.n_kv + hk) * a.S_max + a.pos0 + (m0 - ksq * a.S_call)) * (size_t)ldcb;
+        lb = lrow * ldcb + lcol * ES;
+      }
+      const __amdgpu_buffer_rsrc_t Cr = buf_rsrc(base, (unsigned)(min(TBM, a.M - m0) * ldcb));
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib)
 #pragma unroll
