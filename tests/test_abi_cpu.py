@@ -121,6 +121,10 @@ def test_op_level_validation_without_device():
     assert lib.loop_op_gemm(1, 3, 64, 256, 64, 16, 64, 16, 64, 16, 128, 100, None, 0, None) == A.LOOP_ERR_INVALID_ARG
     assert lib.loop_op_gemm(1, 0, 64, 256, 64, 24, 64, 16, 64, 16, 256, 0, None, 0, None) == A.LOOP_ERR_ALIGN
     assert lib.loop_op_gemm(1, 0, 8, 256, 256, 16, 256, 16, 256, 16, 256, 0, 24, 64, None) == A.LOOP_ERR_ALIGN
+    # prefill-shaped bf16 (M > 64): output widths off the 256-column tile, and 256 fp32
+    # output rows past 2^31 bytes (the tile's stores use 32-bit offsets), are shape errors
+    assert lib.loop_op_gemm(1, 0, 128, 300, 128, 16, 128, 16, 128, 16, 300, 0, None, 0, None) == A.LOOP_ERR_SHAPE
+    assert lib.loop_op_gemm(1, 1, 128, 256, 128, 16, 128, 16, 128, 16, 1 << 21, 0, None, 0, None) == A.LOOP_ERR_SHAPE
     # fp32 and prefill shapes need no split-K scratch
     assert lib.loop_op_gemm_bytes(0, 0, 8, 4096, 4096, 0) == 0
     assert lib.loop_op_gemm_bytes(1, 0, 64, 4096, 4096, 0) == 0
