@@ -426,7 +426,7 @@ def main():
                     help="only a 1 GiB device copy (counter scale reference) and 3 launches of the dominant kernel")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only (no cross-GPU path); run with --gpus 1", flush=True)
+        print("bench.py: the looped-decoder path runs on one GPU (it has no cross-GPU path); run with --gpus 1", flush=True)
         sys.exit(2)
 
     import torch
