@@ -167,7 +167,10 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
         for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[c][r]);
     }
     tmax = x32_max(tmax) * sc;     // scaled (base-2) units
-    const float mnew = fmaxf(mrun, tmax);
+    // the running max moves only when the tile's max exceeds it by more than
+    // 8: the probabilities stay below 2^8 and the result is the same softmax,
+    // with fewer rescales of O
+    const float mnew = tmax > mrun + 8.f ? tmax : mrun;
     const float mfin = (mnew == -INFINITY) ? 0.f : mnew;
     float psum = 0.f;
 #pragma unroll
