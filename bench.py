@@ -32,8 +32,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # dispatch), each scaled by the same counter's reading for a plain 1 GiB
 # device copy in that run.  Valid only for the kernel source it was taken on:
 # the hash of k_gemm.hip + common.h must match, else traffic is reported null.
-DOMINANT_COUNTERS = {"source_sha256_16": "101a8993efe0f4c4", "fetch_kib": 4930906.0, "write_kib": 807168.0,
-                     "copy_fetch_kib": 524315.2, "copy_write_kib": 1048576.0}
+DOMINANT_COUNTERS = {"source_sha256_16": "101a8993efe0f4c4", "fetch_kib": 4930203.2, "write_kib": 807168.0,
+                     "copy_fetch_kib": 524315.6, "copy_write_kib": 1048576.0}
 
 NINE_B = dict(vocab=248320, hidden=4096, ffn=12288, n_heads=32, n_kv_heads=8, head_dim=128,
               n_layers=32, loop_start=4, loop_end=28, n_passes=2, dtype="bf16")
