@@ -43,6 +43,11 @@ class Config:
     rms_eps: float = 1e-6         # A10
     la_eps: float = 1e-6          # A2
     dtype: str = "fp32"           # "fp32" or "bf16" (A15)
+    # bf16 configs round to bf16 at the storage points (A16).  False keeps
+    # float64 between the steps instead, on the same bf16-valued weights and
+    # inputs: the exact-arithmetic result that bf16 storage approximates,
+    # which measures how far rounding alone moves an output.
+    round_storage: bool = True
 
     @property
     def qkv_rows(self) -> int:
@@ -214,8 +219,11 @@ def round_bf16(x: np.ndarray) -> np.ndarray:
 
 
 def _store(cfg: Config, x: np.ndarray) -> np.ndarray:
-    """Value as the GPU path stores it: bf16 for bf16 configs, exact otherwise."""
-    return round_bf16(x) if cfg.dtype == "bf16" else np.asarray(x, dtype=np.float64)
+    """Value as the GPU path stores it: bf16 for bf16 configs (unless
+    ``round_storage`` is off), exact otherwise."""
+    if cfg.dtype == "bf16" and cfg.round_storage:
+        return round_bf16(x)
+    return np.asarray(x, dtype=np.float64)
 
 
 def rmsnorm(x: np.ndarray, gamma: np.ndarray, eps: float) -> np.ndarray:

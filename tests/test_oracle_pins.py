@@ -466,6 +466,29 @@ def test_bf16_storage_points_are_bf16():
     assert np.array_equal(M.round_bf16(h), h)
 
 
+def test_unrounded_storage_is_the_float64_definition():
+    """With storage rounding off, a bf16 configuration computes the plain
+    float64 definition on its bf16-valued weights: bit for bit the fp32
+    configuration's arithmetic on those same weights (so the unrounded run
+    that the derived bf16 bars measure against is exact arithmetic, not a
+    third rounding scheme).  Rounding on moves the result by a bf16-sized
+    amount, not more."""
+    cfg_r = M.tiny_config(dtype="bf16")
+    cfg_u = M.tiny_config(dtype="bf16", round_storage=False)
+    cfg_f = M.tiny_config(dtype="fp32")
+    W = M.make_weights(cfg_r, 0)
+    assert np.array_equal(M.round_bf16(W.layer(3).gate_up), W.layer(3).gate_up)   # bf16-valued weights
+    toks = synth.uniform_int(1, synth.TID_TOKENS, (2, 16), cfg_r.vocab)
+    u = M.forward(cfg_u, W, toks, all_logits=True)
+    f = M.forward(cfg_f, W, toks, all_logits=True)
+    assert np.array_equal(u, f)
+    r = M.forward(cfg_r, W, toks, all_logits=True)
+    err = M.max_row_rel_err(r, u)
+    assert 1e-4 < err < 5e-2
+    h = M.forward(cfg_u, W, toks, hidden_out=True)
+    assert not np.array_equal(M.round_bf16(h), h)
+
+
 # --------------------------------------------------------------------------
 # Synthetic input generator
 # --------------------------------------------------------------------------
