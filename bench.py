@@ -377,6 +377,61 @@ def time_group(L, torch, S=8192, iters=3):
     return ms
 
 
+TINY = dict(vocab=512, hidden=256, ffn=768, n_heads=4, n_kv_heads=4, head_dim=64, n_layers=8, loop_start=2,
+            loop_end=6, n_passes=2, dtype="fp32")
+
+
+def time_tiny(L, torch, S=128, iters=20):
+    """The tiny looped decoder (8 stored layers, block [2, 6) twice: 12
+    executions; fp32): latency of one B=1 prefill of S=128 tokens (last-row
+    logits) and of one decode step after it."""
+    import synth
+    from synth import device as sd
+    cfg = L.ModelConfig(**TINY)
+    model = L.LoopModel(cfg, L.random_weights(cfg, 0))
+    st = model.new_state(1, S + iters + 8)
+    toks = torch.empty(1, S + iters + 8, dtype=torch.int32, device="cuda")
+    sd.fill_tensor_uniform_int(toks, 1, synth.TID_TOKENS, cfg.vocab)
+    p = toks[:, :S].contiguous()
+    for _ in range(3):
+        model.prefill(st, p)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(iters):
+        model.prefill(st, p)
+    e1.record()
+    torch.cuda.synchronize()
+    pre_ms = e0.elapsed_time(e1) / iters
+    dec = [toks[:, S + i].contiguous() for i in range(iters + 2)]
+    model.decode_step(st, dec[0])
+    model.decode_step(st, dec[1])
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(iters):
+        model.decode_step(st, dec[2 + i])
+    e1.record()
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / iters
+    st.check()
+    log(f"tiny: prefill S={S} {pre_ms:.3f} ms, decode step {dec_ms:.3f} ms")
+    st.close()
+    model.close()
+    return pre_ms, dec_ms
+
+
+def cpu_tiny_oracle(S=128):
+    """The float64 oracle on the tiny configuration's full input (B=1, S=128)."""
+    import oracle
+    import synth
+    cfg = oracle.tiny_config()
+    W = oracle.make_weights(cfg, 0)
+    toks = synth.uniform_int(1, synth.TID_TOKENS, (1, S), cfg.vocab)
+    t0 = time.perf_counter()
+    oracle.forward(cfg, W, toks)
+    return time.perf_counter() - t0
+
+
 def cpu_baseline(seq=128):
     """The oracle as it stands, on host cores, on a bounded sample: one 4-layer
     group [linear x3, full] at full 9B width looped twice (8 of the 56 layer
@@ -399,9 +454,54 @@ def cpu_baseline(seq=128):
     dt = time.perf_counter() - t0
     per_token_56 = dt / seq * 56.0 / 8.0
     log(f"oracle sample: {dt:.1f} s for {seq} tokens x 8 executions")
+    tiny_s = cpu_tiny_oracle()
+    log(f"oracle, tiny config B=1 S=128: {tiny_s:.2f} s")
     return {"value": round(1.0 / per_token_56, 3), "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"float64 oracle, one 9B-width group [lin,lin,lin,full] looped twice (8 of 56 executions), "
-                      f"B=1 S={seq}, {dt:.1f} s; scaled by 8/56 to the 56-execution model (head excluded)"}
+                      f"B=1 S={seq}, {dt:.1f} s; scaled by 8/56 to the 56-execution model (head excluded)",
+            "tiny": {"config": "tiny looped decoder (12 executions, fp32), B=1 S=128, last-row logits",
+                     "oracle_s": round(tiny_s, 3), "tokens_per_s": round(128 / tiny_s, 1)}}
+
+
+PROFILE_MODES = ("dominant", "prefill", "decode", "mhc", "group", "long")
+
+
+def profile_run(L, torch, args):
+    """One instance of one workload after a 1 GiB device copy whose counter
+    readings scale the HBM counters (FETCH_SIZE, WRITE_SIZE) to bytes:
+      dominant  3 launches of the gate/up GEMM at M = 32768
+      prefill   one Loop-9B prefill, B=1, S=32,768 (after one untimed warm-up call)
+      decode    one decode step, B=32 at 32,768 pre-filled positions (after 2 warm-up steps)
+      mhc       the mHC site alone, 65,536 tokens, 3 launches
+      group     one 9B-width group looped twice, S=8,192 (after one warm-up call)
+      long      one chunked prefill of 262,144 positions (8 chunks of 32,768)
+    Prints the step it is in before each one, so a profiled run shows progress."""
+    src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")     # 1 GiB
+    dst = torch.empty_like(src)
+    dst.copy_(src)                                                   # reads 1 GiB, writes 1 GiB
+    torch.cuda.synchronize()
+    del src, dst
+    mode = args.profile
+    log(f"profile {mode}: copy done")
+    if mode == "dominant":
+        time_dominant_gemm(L, torch, args.seq, iters=3)
+    elif mode == "mhc":
+        time_mhc_isolated(torch, iters=3)
+    elif mode == "group":
+        time_group(L, torch, iters=1)
+    else:
+        cfg = L.ModelConfig(**NINE_B)
+        model = L.LoopModel(cfg, L.random_weights(cfg, 0))
+        torch.cuda.synchronize()
+        log(f"profile {mode}: weights ready")
+        if mode == "prefill":
+            time_prefill(L, torch, model, args.seq, 1, 1)
+        elif mode == "decode":
+            time_decode(L, torch, model, args.decode_batch, args.decode_ctx, 1, 2)
+        elif mode == "long":
+            time_long_prefill(L, torch, model, args.long_seq, args.long_chunk)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile": mode, "done": True, "copy_bytes": 1 << 30}), flush=True)
 
 
 def main():
@@ -424,6 +524,9 @@ def main():
     ap.add_argument("--cpu-seq", type=int, default=1536)
     ap.add_argument("--profile-dominant", action="store_true",
                     help="only a 1 GiB device copy (counter scale reference) and 3 launches of the dominant kernel")
+    ap.add_argument("--profile", choices=PROFILE_MODES, default=None,
+                    help="only a 1 GiB device copy (counter scale reference) and ONE run of this workload, "
+                         "for rocprofv3 kernel traces and counters per configuration")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: the looped-decoder path runs on one GPU (it has no cross-GPU path); run with --gpus 1", flush=True)
@@ -433,14 +536,9 @@ def main():
     import looped_weight_shared_loop_amd as L
 
     if args.profile_dominant:
-        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")     # 1 GiB
-        dst = torch.empty_like(src)
-        dst.copy_(src)                                                   # reads 1 GiB, writes 1 GiB
-        torch.cuda.synchronize()
-        del src, dst
-        time_dominant_gemm(L, torch, args.seq, iters=3)
-        torch.cuda.synchronize()
-        print(json.dumps({"profile_dominant": "done", "copy_bytes": 1 << 30}), flush=True)
+        args.profile = "dominant"
+    if args.profile:
+        profile_run(L, torch, args)
         return
 
     cfg = L.ModelConfig(**NINE_B)
@@ -525,6 +623,11 @@ def main():
                               "algorithmic_tflop": round(gf / 1e12, 2),
                               "tflops": round(gf / (gms / 1e3) / 1e12, 1),
                               "mfma_frac": round(gf / (gms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    if not args.no_parts:
+        tp, td = time_tiny(L, torch)
+        result["tiny"] = {"config": "tiny looped decoder (8 stored layers, block [2,6) x2 = 12 executions, fp32), "
+                                    "B=1", "prefill_s128_ms": round(tp, 4), "decode_step_ms": round(td, 4),
+                          "prefill_tokens_per_s": round(128 / (tp / 1e3), 1)}
     if not args.no_cpu:
         result["cpu_baseline"] = cpu_baseline(args.cpu_seq)
     print(json.dumps(result), flush=True)

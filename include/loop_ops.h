@@ -53,9 +53,10 @@ int loop_op_add_rmsnorm(int dtype, int T, int C, const void* y, void* h, const f
  *  EXIT:  X' = H_res X + H_post y; h = (X'0 + X'1) / 2; u = RMSNorm(h; gamma).
  * C <= 4096, C % 8 == 0.  With bf16, C % 256 == 0 and T >= 256, ENTER and
  * MID run the projection W x on the matrix cores when `scratch` (>=
- * loop_op_mhc_bytes(C)) is given: W is split there into bf16 high and low
- * parts (about 16 mantissa bits of W, float32 accumulation); otherwise (fewer
- * tokens, or scratch NULL) a float32 path with one workgroup per token runs. */
+ * loop_op_mhc_bytes(C)) is given: W is split there into three bf16 parts
+ * (high, middle, low; together within 2^-27 of W, so the projection equals a
+ * float32 one up to summation order); otherwise (fewer tokens, or scratch
+ * NULL) a float32 path with one workgroup per token runs. */
 size_t loop_op_mhc_bytes(int C);
 int loop_op_mhc(int dtype, int mode, int T, int C, int sinkhorn_iters, float eps, const void* y, void* h, void* X,
                 const float* maps_in, float* maps_out, const float* w, const float* b, const float* gamma,

@@ -120,7 +120,7 @@ WsLayout ws_layout(const loop_model* m, int batch, int max_tokens, int max_seq) 
   for (int b = 1; b <= batch; ++b)
     dec_rows = std::max(dec_rows, (size_t)b * c.n_heads * lk::decode_max_splits(b, c.n_kv_heads, S_max, m->cu));
   w.dec = take(dec_rows * (c.head_dim + 2) * sizeof(float));
-  w.wsplit = take((size_t)16 * 2 * C * sizeof(uint16_t));
+  w.wsplit = take((size_t)lk::MHC_WSPLIT_ROWS * 2 * C * sizeof(uint16_t));
   // split-K scratch of the decode-shaped GEMMs (the largest plan of the five projections)
   size_t sk = 0;
   if (c.dtype == LOOP_BF16 && max_tokens <= 64) {
@@ -192,6 +192,14 @@ int loop_model_create(const loop_config* cfg, const loop_weights* w, loop_model*
     if (G != 1 && G != 2 && G != 4 && G != 8) return lp_fail(LOOP_ERR_SHAPE, "bf16 needs n_heads / n_kv_heads in 1, 2, 4, 8");
     if (c.hidden % 256 || qkv_rows % 256 || c.vocab % 256 || (c.n_heads * c.head_dim) % 128 || c.ffn % 128)
       return lp_fail(LOOP_ERR_SHAPE, "bf16 GEMM tiles need hidden, qkv rows, vocab %% 256 == 0 and ffn %% 128 == 0");
+    // The bf16 GEMM tiles address a weight matrix and 256 rows of an operand
+    // with 32-bit element offsets, and 256 float32 logit rows with 32-bit
+    // byte offsets.  Checked here, so that no call can fail on a shape after
+    // it has launched part of a forward.
+    const long lim = 1L << 31, C = c.hidden, F = c.ffn, Q = (long)c.n_heads * c.head_dim;
+    if ((long)c.vocab * C >= lim || 2 * F * C >= lim || (long)qkv_rows * C >= lim || C * Q >= lim || C * F >= lim ||
+        256L * std::max(F, Q) >= lim || 256L * c.vocab * 4 >= lim)
+      return lp_fail(LOOP_ERR_SHAPE, "bf16 weight matrices need fewer than 2^31 elements and vocab < 2^21");
   } else {
     if (c.ffn % 8 || (c.n_heads * c.head_dim) % 8) return lp_fail(LOOP_ERR_SHAPE, "fp32 widths must be multiples of 8");
   }
@@ -623,8 +631,17 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, int
   } else if (flags & LOOP_ALL_LOGITS) {
     LAUNCH(run_gemm(gemm(lk::EPI_F32, u, C, T, m->head, c.vocab, C, out, c.vocab)), "head gemm");
   } else {
-    const char* last = (const char*)u + (size_t)(S - 1) * C * m->es;
-    LAUNCH(run_gemm(gemm(lk::EPI_F32, last, (long)S * C, B, m->head, c.vocab, C, out, c.vocab)), "head gemm");
+    // the last position of every sequence: with S > 1 its B rows are gathered
+    // into one contiguous block first (y is free once the final norm has read
+    // it), so the head reads rows of stride C whatever S is
+    const void* last = u;
+    if (S > 1) {
+      LAUNCH(hipMemcpy2DAsync(y, (size_t)C * m->es, (const char*)u + (size_t)(S - 1) * C * m->es,
+                              (size_t)S * C * m->es, (size_t)C * m->es, B, hipMemcpyDeviceToDevice, s),
+             "gather last rows");
+      last = y;
+    }
+    LAUNCH(run_gemm(gemm(lk::EPI_F32, last, C, B, m->head, c.vocab, C, out, c.vocab)), "head gemm");
   }
   for (int b = seq0; b < seq0 + B; ++b) st->seq_len[b] = (decode ? st->seq_len[b] : pos0) + S;
   return LOOP_OK;

@@ -429,10 +429,13 @@ __global__ __launch_bounds__(64) void mhc_slice_b(MhcArgs a, const float* __rest
 
 // ------------------------------------------------------------------ mHC, MFMA (bf16)
 // For bf16 streams the 8 projections l = W vec(X') run on the matrix cores:
-// W (float32 [8][2C]) is split once per call into W_hi = bf16(W) and
-// W_lo = bf16(W - W_hi), stacked as 16 bf16 rows, so one
-// v_mfma_f32_16x16x32_bf16 yields hi and lo partial logits of 16 tokens
-// (l_j = col j + col j+8; about 16 mantissa bits of W, float32 accumulation).
+// W (float32 [8][2C]) is split once per call into W_hi = bf16(W),
+// W_mid = bf16(W - W_hi) and W_lo = bf16(W - W_hi - W_mid), 24 bf16 rows
+// that carry W to within 2^-27 of its value (finer than float32's own
+// rounding): X' is bf16, so each product is exact and the projection equals
+// a float32 one up to the order of the float32 sums.  One
+// v_mfma_f32_16x16x32_bf16 takes [W_hi; W_mid] (columns j and j + 8), a
+// second one W_lo (columns j < 8); l_j = col j + col j+8 over both.
 // A workgroup of 8 waves handles 16 tokens at a time; wave w owns channels
 // [w C/8, (w+1) C/8) of both streams, lane l owns token l % 16 and 8 channels
 // per 32-channel step.  The Sinkhorn maps are computed once per token (one
@@ -441,8 +444,11 @@ __global__ __launch_bounds__(256) void mhc_split_w(const float* __restrict__ w, 
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
     const float v = w[i];
     const bf16_t hi = f2bf(v);
+    const float r1 = v - bf2f(hi);    // exact in float32
+    const bf16_t mid = f2bf(r1);
     ws[i] = hi;                       // rows 0..7
-    ws[n + i] = f2bf(v - bf2f(hi));   // rows 8..15
+    ws[n + i] = mid;                  // rows 8..15
+    ws[2 * n + i] = f2bf(r1 - bf2f(mid));   // rows 16..23
   }
 }
 
@@ -464,7 +470,9 @@ __global__ __launch_bounds__(512) void mhc_mfma_kernel(MhcArgs a, const bf16_t* 
   const bf16_t* y = (const bf16_t*)a.y;
   bf16_t* u = (bf16_t*)a.u;
   const int ntiles = (a.T + 15) / 16;
-  const bf16_t* wrow = wsplit + (size_t)li * C2;   // row li of [W_hi; W_lo]
+  const bf16_t* wrow = wsplit + (size_t)li * C2;   // row li of [W_hi; W_mid]
+  const bool has_lo = li < 8;
+  const bf16_t* wlo = wsplit + (size_t)(16 + (has_lo ? li : 0)) * C2;   // row li of W_lo
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 
   for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
@@ -482,7 +490,7 @@ __global__ __launch_bounds__(512) void mhc_mfma_kernel(MhcArgs a, const bf16_t* 
     const bf16_t* Yr = (y ? y + tr * C : nullptr) + w * CW + 8 * g;
     // X' of this lane's token and channels stays in registers (bf16 pairs)
     u32x4_t xs0[NSMAX], xs1[NSMAX];
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f}, acc_lo = {0.f, 0.f, 0.f, 0.f};
     float s00 = 0.f, s11 = 0.f, s01 = 0.f;
 #pragma unroll
     for (int j0 = 0; j0 < NSMAX; j0 += GRP) {
@@ -548,12 +556,17 @@ __global__ __launch_bounds__(512) void mhc_mfma_kernel(MhcArgs a, const bf16_t* 
           const bf16x8_t w1 = as_bf16x8(ldv4(wrow + C + cb));
           acc = mfma16(as_bf16x8(p0), w0, acc);
           acc = mfma16(as_bf16x8(p1), w1, acc);
+          const bf16x8_t v0 = as_bf16x8(has_lo ? ldv4(wlo + cb) : zero);
+          const bf16x8_t v1 = as_bf16x8(has_lo ? ldv4(wlo + C + cb) : zero);
+          acc_lo = mfma16(as_bf16x8(p0), v0, acc_lo);
+          acc_lo = mfma16(as_bf16x8(p1), v1, acc_lo);
         }
       }
     }
     // acc[r]: token 4 g + r, column li; the stream sums of token li are split over the 4 groups
+    // columns j < 8: hi + lo parts of logit j; columns j + 8: its mid part
 #pragma unroll
-    for (int r = 0; r < 4; ++r) red_acc[w][4 * g + r][li] = acc[r];
+    for (int r = 0; r < 4; ++r) red_acc[w][4 * g + r][li] = acc[r] + acc_lo[r];
     s00 = x32_sum(x16_sum(s00));
     s11 = x32_sum(x16_sum(s11));
     s01 = x32_sum(x16_sum(s01));
@@ -649,7 +662,7 @@ hipError_t mhc(const MhcArgs& a, hipStream_t s) {
   }
   // few tokens: one wave per (512-channel slice, token), partial sums in the scratch
   if (a.mode != MHC_EXIT && a.C % MHC_SLICE == 0 && a.T <= 64 && a.wsplit) {
-    float* part = (float*)a.wsplit;     // T * (C / 512) * 11 floats <= 16 * 2C bf16 for T <= 64
+    float* part = (float*)a.wsplit;     // T * (C / 512) * 11 floats <= 24 * 2C bf16 for T <= 64
     const dim3 grid(a.C / MHC_SLICE, a.T);
     if (a.dt == DT_BF16) {
       mhc_slice_a<bf16_t><<<grid, 64, 0, s>>>(a, part);

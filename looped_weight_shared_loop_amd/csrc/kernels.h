@@ -44,6 +44,9 @@ hipError_t add_rmsnorm(const NormArgs& a, hipStream_t s);
 // Fused two-stream hyper-connection transition (write-back of one site, then
 // maps, read and RMSNorm of the next site).
 enum MhcMode { MHC_ENTER = 0, MHC_MID = 1, MHC_EXIT = 2 };
+// rows of the bf16 split of an mHC projection W [8][2C]: high, middle and low parts
+constexpr int MHC_WSPLIT_ROWS = 24;
+
 struct MhcArgs {
   int dt, mode, T, C, iters;
   float eps;
@@ -58,7 +61,7 @@ struct MhcArgs {
   const float* gamma;    // [C] RMSNorm gain of the next sublayer
   void* u;               // [T][C] normed input of the next sublayer
   int grid;              // persistent grid size (0: one block per token)
-  bf16_t* wsplit;        // bf16 ENTER/MID: scratch of 16 x 2C bf16 for [W_hi; W_lo]
+  bf16_t* wsplit;        // bf16 ENTER/MID: scratch of MHC_WSPLIT_ROWS x 2C bf16 for [W_hi; W_mid; W_lo]
 };
 hipError_t mhc(const MhcArgs& a, hipStream_t s);
 

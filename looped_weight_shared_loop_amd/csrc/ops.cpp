@@ -76,7 +76,7 @@ int loop_op_add_rmsnorm(int dtype, int T, int C, const void* y, void* h, const f
   return launched(lk::add_rmsnorm(a, (hipStream_t)stream), "add_rmsnorm");
 }
 
-size_t loop_op_mhc_bytes(int C) { return C > 0 ? (size_t)16 * 2 * C * sizeof(uint16_t) : 0; }
+size_t loop_op_mhc_bytes(int C) { return C > 0 ? (size_t)lk::MHC_WSPLIT_ROWS * 2 * C * sizeof(uint16_t) : 0; }
 
 int loop_op_mhc(int dtype, int mode, int T, int C, int iters, float eps, const void* y, void* h, void* X,
                 const float* maps_in, float* maps_out, const float* w, const float* b, const float* gamma, void* u,

@@ -1,0 +1,84 @@
+"""The bf16 prefill attention keeps its running max in place until a key
+tile's max exceeds it by more than 8 (base 2), and rescales O only when it
+moves.  Inputs drawn as N(0, 1) never take that branch after the first tile,
+so here the scores are built to rise across the 64-key tiles: every key is
+k_tau = (s_tau + e_tau) u + n_tau, with u a unit vector, n_tau orthogonal to u,
+and every query q_t = a_t sqrt(d) u.  The score q_t . k_tau / sqrt(d) is then
+a_t (s_tau + e_tau): a per-tile level s (steps just under, just over and far
+over the threshold, and drops) plus a small spread e inside the tile.  The
+query scales a_t in [0.85, 1.15] put a step of 8.5 on either side of 8 for
+different queries.  Sampled rows are checked against the oracle's causal
+softmax attention (pages: "How Does SenseNova-Loop Get More Depth Without More
+Parameters?", section "How does the hybrid attention pattern work?"), per row
+at 2e-2 of the row's largest value, for a chunk from position 0 and a chunk
+continuing a cache.
+"""
+import numpy as np
+import pytest
+
+from oracle import model as M
+from gpu_common import need_gpu, torch
+
+pytestmark = pytest.mark.gpu
+
+D, HQ, HKV = 128, 8, 2
+LOG2E = 1.4426950408889634
+# per-tile step of the score level, base 2 (the first tile sets the level)
+STEPS2 = [0.0, 7.0, 9.0, 7.5, 8.5, 30.0, -25.0, 7.2, 9.5, 2.0, 7.8, 8.4, 40.0, 0.5, 7.6, 9.2,
+          8.0, 8.1, 7.9, 12.0, -3.0, 8.6, 7.4, 16.0]
+
+
+def _inputs(L, rng):
+    u = rng.standard_normal(D)
+    u /= np.linalg.norm(u)
+    level2 = np.cumsum(STEPS2)[np.arange(L) // 64] + rng.uniform(-0.3, 0.3, L)   # base 2
+    s = level2 / LOG2E
+    K = np.empty((HKV, L, D))
+    for h in range(HKV):
+        n = rng.standard_normal((L, D))
+        n -= np.outer(n @ u, u)                          # orthogonal to u
+        K[h] = s[:, None] * u[None, :] * (1.0 + 0.05 * h) + n
+    V = rng.standard_normal((HKV, L, D))
+    return u, M.round_bf16(K), M.round_bf16(V)
+
+
+@pytest.mark.parametrize("pos0,S", [(0, 1536), (600, 936)], ids=["from_zero", "continued_chunk"])
+def test_prefill_attention_rising_scores(pos0, S):
+    L = need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    rng = np.random.default_rng(1234 + pos0)
+    Lk = pos0 + S
+    assert Lk <= 64 * len(STEPS2)
+    Smax = (Lk + 63) // 64 * 64
+    u, K, V = _inputs(Lk, rng)
+    a = rng.uniform(0.85, 1.15, (S, HQ))
+    q = M.round_bf16(a[:, :, None] * np.sqrt(D) * u[None, None, :] + 0.01 * rng.standard_normal((S, HQ, D)))
+    print(f"rising-score attention pos0={pos0} S={S}", flush=True)
+    kc = np.zeros((1, HKV, Smax, D), np.float32)
+    vt = np.zeros((1, HKV, D, Smax), np.float32)
+    kc[0, :, :Lk] = K
+    vt[0, :, :, :Lk] = V.transpose(0, 2, 1)
+    to = lambda x: torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).cuda()
+    qd, kd, vd = to(q.reshape(S, HQ * D)), to(kc), to(vt)
+    out = torch.empty(S, HQ * D, dtype=torch.bfloat16, device="cuda")
+    A.loop_op_attention(A.LOOP_BF16, 1, S, pos0, Smax, HQ, HKV, D, qd.data_ptr(), HQ * D, kd.data_ptr(),
+                        vd.data_ptr(), out.data_ptr(), HQ * D, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().reshape(S, HQ, D)
+    # rows at tile ends and starts, around the continued chunk's start, and random ones
+    rows = sorted(set([0, 1, 31, 32, 63, 64, S - 1, S - 2] + [t for t in range(63, S, 64)] +
+                      list(rng.integers(0, S, 24))))
+    G = HQ // HKV
+    worst = 0.0
+    for t in rows:
+        for j in range(HQ):
+            kv = j // G
+            ref = M.full_attention(q[t, j][None, None, None, :], K[kv][None, :, None, :], V[kv][None, :, None, :],
+                                   pos0 + t)[0, 0, 0]
+            err = np.abs(got[t, j] - ref).max() / np.abs(ref).max()
+            worst = max(worst, err)
+            assert err < 2e-2, (t, j, err)
+    print("worst row error", worst, flush=True)
+    # the construction does move the max by more than 2^8 between tiles for these rows
+    lv = np.cumsum(STEPS2)
+    assert np.any(np.diff(lv[: (Lk + 63) // 64]) > 8.5)

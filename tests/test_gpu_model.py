@@ -6,6 +6,7 @@ Tolerances (max over rows of ||g - r||_inf / ||r||_inf):
                               points; the GPU also rounds the attention
                               probabilities to bf16 for the P.V product)
 """
+import os
 import sys
 
 import numpy as np
@@ -397,15 +398,18 @@ def vars_of(ocfg):
                 la_eps=ocfg.la_eps, dtype=ocfg.dtype)
 
 
-# Hidden states of the 9B-width group are compared at a derived bar: the
-# oracle itself moves by 2.27e-2 on the max-row metric and 1.18e-2 on the row
-# RMS ratio ||g - r||_2 / ||r||_2 (mean over rows) when ONE input element of
-# the S=200 case is moved by one bf16 ulp (pinned on the CPU by
-# test_oracle_sensitivity.py), so two valid bf16 implementations that differ
-# in one rounding decision differ by that much.  Bar: 5e-2 max-row and 3e-2
-# row RMS.  Logits and shallow stacks keep the 2e-2 bar.
-HIDDEN_TOL = 5e-2
-HIDDEN_RMS_TOL = 3e-2
+# Bars for bf16 results deep in the stack, derived rather than chosen.  The
+# oracle with bf16 storage (rounded at the same points as the GPU path) is
+# itself some distance from exact arithmetic on the same bf16-valued weights
+# and inputs (the oracle with storage rounding off); a one-ulp change of one
+# input moves the rounded oracle by about as much (eight sites measured by
+# tests/golden/make_golden.py: max-row 1.3-2.3e-2, row-RMS 1.0-1.2e-2 for the
+# group).  Two valid bf16 implementations differ by rounding decisions of that
+# size, so a GPU result is held to DERIVED_FACTOR times the rounded oracle's
+# own distance from the exact result, on the max-row and on the row-RMS
+# metric, with both reference results stored by that script.
+DERIVED_FACTOR = 1.5
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 def rms_rel(got, ref):
@@ -414,21 +418,73 @@ def rms_rel(got, ref):
     return float((np.linalg.norm(g - r, axis=1) / np.linalg.norm(r, axis=1)).mean())
 
 
+def _derived_check(tag, got, rounded, exact):
+    base_max, base_rms = rel(rounded, exact), rms_rel(rounded, exact)
+    e_max, e_rms = rel(got, exact), rms_rel(got, exact)
+    _say(tag, "GPU vs exact: max-row", e_max, "row-rms", e_rms, "| bf16 oracle vs exact:", base_max, base_rms,
+         "| GPU vs bf16 oracle:", rel(got, rounded), rms_rel(got, rounded))
+    assert e_max <= DERIVED_FACTOR * base_max, (e_max, base_max)
+    assert e_rms <= DERIVED_FACTOR * base_rms, (e_rms, base_rms)
+
+
 def test_group_9b_width_hidden_out():
     """One [linear x3, full] group at hidden 4096 / FFN 12288 / 32q-8kv x 128,
-    looped twice under two-stream mHC, inputs N(0, 1), at a reduced length."""
+    looped twice under two-stream mHC (8 executions), inputs N(0, 1), S=200,
+    against the stored oracle results at the derived bar."""
+    L = need_gpu()
+    import json
+    from gpu_common import lib_config
+    g = np.load(os.path.join(GOLDEN, "group9b_hidden.npz"))
+    rounded = synth.bf16_bits_to_f32(g["rounded_bf16_bits"]).astype(np.float64)
+    exact = g["unrounded"].astype(np.float64)
+    meta = json.loads(str(g["meta"]))
     ocfg = oracle.group_config()
-    S = 200
+    S = meta["S"]
     _say("group 9B width S=", S)
-    model, Wo = build_pair(ocfg, cache_layers=4)
+    model = L.LoopModel(lib_config(ocfg), L.random_weights(lib_config(ocfg), 0))
     emb = synth.normal_bf16_as_f32(1, synth.TID_EMBEDS_IN, (1, S, ocfg.hidden))
-    ref = oracle.forward(ocfg, Wo, embeds=emb, hidden_out=True)
     st = model.new_state(1, S)
     got = model.prefill(st, embeds=torch.from_numpy(emb).to(torch.bfloat16).cuda(), hidden_out=True)
-    g = got.float().cpu().numpy()
-    err, rms = rel(g, ref), rms_rel(g, ref)
-    _say("group rel err", err, "row rms", rms)
-    assert err < HIDDEN_TOL and rms < HIDDEN_RMS_TOL
+    _derived_check("group", got.float().cpu().numpy(), rounded, exact)
+
+
+def test_loop9b_end_to_end_prefill_and_decode():
+    """The full Loop-9B shape through the C ABI: 32 stored layers, block
+    [4, 28) run twice (56 executions, 14 full-attention and 42 linear, each
+    with its own per-pass cache or state), vocabulary 248,320, B = 2.  A
+    128-position prefill (last-row logits, and all rows for row 64), then two
+    decode steps, against the stored oracle logits (tests/golden/make_golden.py)
+    at the derived bar against exact arithmetic (at this depth bf16 storage
+    alone moves the oracle's logits 2.8-3.9e-2 max-row from exact)."""
+    L = need_gpu()
+    import json
+    from gpu_common import lib_config
+    g = np.load(os.path.join(GOLDEN, "loop9b_logits.npz"))
+    meta = json.loads(str(g["meta"]))
+    toks, rows = g["tokens"], [int(r) for r in g["rows"]]
+    B, T, P = meta["B"], meta["T"], meta["prefill"]
+    ocfg = oracle.nine_b_config()
+    assert np.array_equal(toks, tokens(B, T, ocfg.vocab, seed=1))
+    gcfg = lib_config(ocfg)
+    _say("Loop-9B end to end: B", B, "prefill", P, "decode", T - P)
+    model = L.LoopModel(gcfg, L.random_weights(gcfg, 0))
+    assert len(model.schedule()) == 56
+    st = model.new_state(B, 256)
+    allr = model.prefill(st, to_dev_tokens(toks[:, :P]), all_logits=True)
+    got = {r: allr[:, r].cpu().numpy() for r in rows if r < P}
+    del allr
+    st2 = model.new_state(B, 256)
+    last = model.prefill(st2, to_dev_tokens(toks[:, :P])).cpu().numpy()
+    assert rel(last, got[P - 1]) < 1e-6          # last-row head = that row of the all-rows head
+    for t in range(P, T):
+        got[t] = model.decode_step(st2, to_dev_tokens(toks[:, t])).cpu().numpy()
+    assert st2.lengths == [T] * B
+    G = np.stack([got[r] for r in rows], axis=1)            # [B, rows, V]
+    rounded, exact = g["rounded"].astype(np.float64), g["unrounded"].astype(np.float64)
+    for i, r in enumerate(rows):
+        _say("row", r, "GPU vs bf16 oracle", rel(G[:, i], rounded[:, i]), "GPU vs exact", rel(G[:, i], exact[:, i]),
+             "bf16 oracle vs exact", rel(rounded[:, i], exact[:, i]))
+    _derived_check("Loop-9B logits", G, rounded, exact)
 
 
 @pytest.mark.parametrize("shape,S", [((1, 0, 1, 1, 4), 160), ((4, 3, 4, 1, 4), 160), ((1, 0, 1, 1, 1), 2900)],
@@ -503,3 +559,28 @@ def test_error_paths():
         st.check()
     assert e.value.code == -8
     st.check()   # cleared
+
+
+def test_last_row_head_with_long_rows_and_wide_batch():
+    """Last-position logits of B = 65 sequences of S = 2048 at hidden 4096: the
+    head reads one row per sequence, S x 4096 elements apart, past the 32-bit
+    row offsets of a 256-row GEMM tile.  The rows are gathered into a
+    contiguous block first, so the call succeeds (it used to fail only after
+    every layer had run and written the state).  Sequences 0 and 64 against
+    the oracle; all 65 rows equal the matching rows of LOOP_ALL_LOGITS."""
+    L = need_gpu()
+    ocfg = oracle.group_config(vocab=256, ffn=128, n_layers=1, loop_start=0, loop_end=0, n_passes=1)
+    model, Wo = build_pair(ocfg)
+    B, S = 65, 2048
+    toks = tokens(B, S, ocfg.vocab, seed=61)
+    _say("last-row head B=65 S=2048 hidden 4096")
+    st = model.new_state(B, S)
+    last = model.prefill(st, to_dev_tokens(toks)).cpu().numpy()
+    assert st.lengths == [S] * B
+    allr = model.prefill(st, to_dev_tokens(toks), all_logits=True)[:, -1].cpu().numpy()
+    assert rel(last, allr) < 1e-6
+    for b in (0, 64):
+        ref = oracle.forward(ocfg, Wo, toks[b:b + 1])
+        err = rel(last[b:b + 1], ref)
+        _say("sequence", b, "rel err", err)
+        assert err < BF16_TOL
