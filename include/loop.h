@@ -215,6 +215,23 @@ int loop_prefill_rows(loop_model* m, loop_state* st, void* workspace, size_t ws_
 int loop_decode_step(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes,
                      const int32_t* tokens_dev, int B, float* logits_dev, void* stream);
 
+/* loop_decode_step for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the workspace is the library's own device array of
+ * LOOP_NOALLOC_WORKSPACE_BYTES (64 MiB), one per GPU, held until the process
+ * ends; its address on a device is looked up once (loop_model_create, or the
+ * first call on that device).  The call allocates nothing and computes what
+ * loop_decode_step computes with the same kernels.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (on different
+ * streams, or from several threads without ordering) race and give wrong
+ * results.  No kernel relies on the array's previous contents.
+ * Errors: as loop_decode_step; WORKSPACE (nothing launched) when the step
+ * needs more than the array holds, that is when
+ * loop_workspace_bytes(m, B, B, max_seq) > LOOP_NOALLOC_WORKSPACE_BYTES. */
+enum { LOOP_NOALLOC_WORKSPACE_BYTES = 64 << 20 };
+int loop_decode_step_noalloc(loop_model* m, loop_state* st, const int32_t* tokens_dev, int B, float* logits_dev,
+                             void* stream);
+
 /* Decode with the passes of the looped block co-scheduled over cohorts, so
  * that every call reads each shared layer's weights once for several tokens'
  * passes.  One page expects the shared block's weights to be fetched once

@@ -12,6 +12,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -21,7 +22,20 @@
 
 namespace {
 thread_local std::string g_err;
+
+// Workspace of loop_decode_step_noalloc, for callers that cannot allocate.
+// Every GPU the library runs on holds its own copy of this array until the
+// process ends.  Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in symbol): it uses the device address that
+// hipGetSymbolAddress returned for the current device, kept per device below.
+constexpr size_t NOALLOC_WS_BYTES = (size_t)64 << 20;
+constexpr int MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[MAX_DEVICES] = {};
+
 }  // namespace
+
+static __device__ __align__(256) unsigned char scratch[NOALLOC_WS_BYTES];
 
 int lp_fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -145,6 +159,23 @@ int check_hip(hipError_t e, const char* what) {
   return lp_fail(LOOP_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.
+int noalloc_scratch(void** out) {
+  int dev = -1;
+  if (int r = check_hip(hipGetDevice(&dev), "hipGetDevice")) return r;
+  if (dev < 0 || dev >= MAX_DEVICES)
+    return lp_fail(LOOP_ERR_NO_DEVICE, "device %d outside the library's table of %d devices", dev, MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (int r = check_hip(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)")) return r;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return LOOP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -246,6 +277,12 @@ int loop_model_create(const loop_config* cfg, const loop_weights* w, loop_model*
   for (int i = c.loop_end; i < c.n_layers; ++i) push(i, 0);
   m->cu = lk::device_cu_count();
   if (m->cu <= 0) m->cu = 256;
+  // set-up of loop_decode_step_noalloc: the static workspace's address on this device
+  void* ws = nullptr;
+  if (int r = noalloc_scratch(&ws)) {
+    delete m;
+    return r;
+  }
   *out = m;
   return LOOP_OK;
 }
@@ -949,6 +986,23 @@ int loop_decode_step(loop_model* m, loop_state* st, void* workspace, size_t ws_b
   if (!m) return lp_fail(LOOP_ERR_INVALID_ARG, "null model");
   if (!tokens_dev) return lp_fail(LOOP_ERR_INVALID_ARG, "null tokens");
   return forward(m, st, workspace, ws_bytes, 0, tokens_dev, nullptr, B, 1, 0, logits_dev, (hipStream_t)stream, true);
+}
+
+int loop_decode_step_noalloc(loop_model* m, loop_state* st, const int32_t* tokens_dev, int B, float* logits_dev,
+                             void* stream) {
+  if (!m) return lp_fail(LOOP_ERR_INVALID_ARG, "null model");
+  if (!tokens_dev) return lp_fail(LOOP_ERR_INVALID_ARG, "null tokens");
+  if (!st || st->m != m) return lp_fail(LOOP_ERR_STATE, "state does not belong to this model");
+  if (B <= 0) return lp_fail(LOOP_ERR_INVALID_ARG, "B must be positive");
+  const size_t need = ws_layout(m, B, B, st->max_seq).total;
+  if (need > NOALLOC_WS_BYTES)
+    return lp_fail(LOOP_ERR_WORKSPACE,
+                   "a decode step of %d sequences (max_seq %d) needs %zu workspace bytes; the library's static "
+                   "workspace holds %zu (use loop_decode_step with a caller workspace)",
+                   B, st->max_seq, need, NOALLOC_WS_BYTES);
+  void* ws = nullptr;
+  if (int r = noalloc_scratch(&ws)) return r;
+  return forward(m, st, ws, NOALLOC_WS_BYTES, 0, tokens_dev, nullptr, B, 1, 0, logits_dev, (hipStream_t)stream, true);
 }
 
 int loop_decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, const int32_t* tokens_dev,

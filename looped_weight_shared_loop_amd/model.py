@@ -240,6 +240,15 @@ class LoopModel:
                            out.data_ptr(), self._stream())
         return out
 
+    def decode_step_noalloc(self, state: LoopState, tokens: torch.Tensor, out: torch.Tensor) -> torch.Tensor:
+        """decode_step on the library's own static device workspace: the call
+        allocates nothing (the caller passes the logits buffer)."""
+        B = int(tokens.shape[0])
+        assert tokens.dtype == torch.int32 and tokens.is_contiguous()
+        assert out.dtype == torch.float32 and out.is_contiguous() and out.numel() >= B * self.cfg.vocab
+        A.loop_decode_step_noalloc(self.handle, state.handle, tokens.data_ptr(), B, out.data_ptr(), self._stream())
+        return out
+
     def decode_pipelined(self, state: LoopState, tokens: Optional[torch.Tensor], out: Optional[torch.Tensor] = None):
         """One call of the pass-pipelined decode (the state holds n_passes
         cohorts of B sequences).  tokens: int32 [B] for the entering cohort, or
