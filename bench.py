@@ -504,6 +504,160 @@ def profile_run(L, torch, args):
     print(json.dumps({"profile": mode, "done": True, "copy_bytes": 1 << 30}), flush=True)
 
 
+# ------------------------------------------------------------------ rocprofv3 summaries
+def _prof_rows(d, suffix):
+    """Rows of the rocprofv3 CSV under directory d whose name ends in suffix,
+    in dispatch order."""
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit(f"no *{suffix} under {d}")
+    rows = []
+    for f in files:
+        with open(f, newline="") as fh:
+            rows += list(csv.DictReader(fh))
+    rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+    return rows
+
+
+def _kname(n):
+    n = n.split("(")[0] if not n.startswith("(") else n.split(")::", 1)[-1].split("(")[0]
+    return n.replace("void ", "").strip()
+
+
+_ATTN_OR_LIN = ("attn_prefill_dma", "attn_decode_mfma", "attn_combine", "lin_out_bf", "lin_decode_kernel",
+                "lin_output", "attn_f32", "kv_append")
+
+
+def _labels(names):
+    """Names the projection of each GEMM launch from the driver's launch order:
+    a plain-store GEMM after a norm or mHC kernel is the QKV projection of a
+    linear-attention layer, after attention it is the O projection, after the
+    gate/up GEMM (or its split-K reduction) it is the down projection."""
+    out, prev = [], ""
+    for n in names:
+        lab = n
+        if "gemm_w4_kernel<" in n or "gemm_skinny_rs_kernel<" in n or "gemm_dma_kernel<" in n:
+            epi = n.split("<")[1].split(",")[0].split(">")[0]
+            kind = "256-row tiles" if "w4" in n or "dma" in n else "skinny, weights streamed once"
+            if epi == "3":
+                lab = f"gemm gate/up + SwiGLU ({kind}) {n}"
+            elif epi == "2":
+                lab = f"gemm QKV, full-attention layers ({kind}) {n}"
+            elif epi == "1":
+                lab = f"gemm head ({kind}) {n}"
+            elif any(k in prev for k in _ATTN_OR_LIN):
+                lab = f"gemm o ({kind}) {n}"
+            elif "<3" in prev and "gemm" in prev:
+                lab = f"gemm down ({kind}) {n}"
+            else:
+                lab = f"gemm QKV, linear-attention layers ({kind}) {n}"
+        out.append(lab)
+        if not n.startswith("at::") and "rocclr" not in n:
+            prev = n
+    return out
+
+
+def _scope(names, scope, marker):
+    """Index range summarized: everything after the 1 GiB reference copy
+    ('all'), or from the last launch of the marker kernel on ('last')."""
+    first = next(i for i, n in enumerate(names) if n == "__amd_rocclr_copyBuffer") + 1
+    if scope == "all":
+        return first, len(names)
+    idx = [i for i, n in enumerate(names) if marker in n and i >= first]
+    return (idx[-1] if idx else first), len(names)
+
+
+def summarize(kind, dirs, scope, marker, title):
+    import collections
+    lines = [f"# {title}"]
+    if kind == "trace":
+        rows = _prof_rows(dirs[0], "kernel_trace.csv")
+        names = [_kname(r["Kernel_Name"]) for r in rows]
+        a, b = _scope(names, scope, marker)
+        labs = _labels(names)
+        agg = collections.OrderedDict()
+        for i in range(a, b):
+            if names[i].startswith("at::") or "rocclr" in names[i]:
+                continue
+            dt = (int(rows[i]["End_Timestamp"]) - int(rows[i]["Start_Timestamp"])) / 1e6
+            e = agg.setdefault(labs[i], [0, 0.0])
+            e[0] += 1
+            e[1] += dt
+        tot = sum(v[1] for v in agg.values())
+        span = (int(rows[b - 1]["End_Timestamp"]) - int(rows[a]["Start_Timestamp"])) / 1e6
+        lines.append(f"# library kernels: {tot:.3f} ms of kernel time; first start to last end {span:.3f} ms")
+        lines.append("# kernel (projection named from the launch order) | launches | average ms | total ms | share")
+        for k, (c, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+            lines.append(f"{k[:96]:96s} | {c:5d} | {t / c:9.4f} | {t:9.3f} | {100 * t / tot:5.1f}%")
+    elif kind == "mfma":
+        rows = _prof_rows(dirs[0], "counter_collection.csv")
+        per = collections.OrderedDict()
+        for r in rows:
+            e = per.setdefault(int(r["Dispatch_Id"]), {"name": _kname(r["Kernel_Name"]),
+                                                        "t": (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))})
+            e[r["Counter_Name"]] = float(r["Counter_Value"])
+        disp = list(per.values())
+        names = [e["name"] for e in disp]
+        a, b = _scope(names, scope, marker)
+        labs = _labels(names)
+        agg = collections.OrderedDict()
+        for i in range(a, b):
+            e = disp[i]
+            if e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) == 0:
+                continue
+            g = agg.setdefault(labs[i], collections.defaultdict(float))
+            g["n"] += 1
+            for c in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_VALU",
+                      "GRBM_GUI_ACTIVE"):
+                g[c] += e.get(c, 0.0)
+            g["t"] += e["t"]
+        lines.append("# MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE per XCC x 1024 SIMDs); VALUBusy ="
+                     " SQ_ACTIVE_INST_VALU / 256 CUs / GRBM_GUI_ACTIVE per XCC (rocprofv3's derived metrics);"
+                     " GRBM_GUI_ACTIVE is the sum over the 8 XCCs")
+        lines.append("# clock = GUI-active cycles per XCC / kernel duration under counter collection")
+        lines.append("# kernel | launches | bf16 MFMA FLOP per launch (MOPS_BF16 x 512) | MfmaUtil | VALUBusy | clock GHz")
+        tot_f = 0.0
+        for k, g in sorted(agg.items(), key=lambda kv: -kv[1]["SQ_INSTS_VALU_MFMA_MOPS_BF16"]):
+            n, gui = g["n"], g["GRBM_GUI_ACTIVE"] / 8
+            tot_f += g["SQ_INSTS_VALU_MFMA_MOPS_BF16"] * 512
+            lines.append(f"{k[:96]:96s} | {int(n):5d} | {g['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / n:10.4e} | "
+                         f"{g['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * 1024):6.3f} | "
+                         f"{g['SQ_ACTIVE_INST_VALU'] / 256 / gui:6.3f} | {gui / g['t']:5.2f}")
+        lines.append(f"# bf16 MFMA FLOP counted in the scope: {tot_f:.4e}")
+    elif kind == "hbm":
+        f = _prof_rows(dirs[0], "counter_collection.csv")
+        w = _prof_rows(dirs[1], "counter_collection.csv")
+        f = [(_kname(r["Kernel_Name"]), float(r["Counter_Value"])) for r in f if r["Counter_Name"] == "FETCH_SIZE"]
+        w = [(_kname(r["Kernel_Name"]), float(r["Counter_Value"])) for r in w if r["Counter_Name"] == "WRITE_SIZE"]
+        names = [n for n, _ in f]
+        assert names == [n for n, _ in w], "the two runs launched different kernels"
+        cf = next(v for n, v in f if n == "__amd_rocclr_copyBuffer")
+        cw = next(v for n, v in w if n == "__amd_rocclr_copyBuffer")
+        sf, sw = (1 << 30) / (cf * 1024), (1 << 30) / (cw * 1024)
+        lines.append(f"# reference: a plain 1 GiB device copy reads FETCH_SIZE {cf:.1f} KiB (scale {sf:.4f}) and "
+                     f"WRITE_SIZE {cw:.1f} KiB (scale {sw:.4f})")
+        a, b = _scope(names, scope, marker)
+        labs = _labels(names)
+        agg = collections.OrderedDict()
+        for i in range(a, b):
+            if names[i].startswith("at::") or "rocclr" in names[i]:
+                continue
+            e = agg.setdefault(labs[i], [0, 0.0, 0.0])
+            e[0] += 1
+            e[1] += f[i][1] * 1024 * sf
+            e[2] += w[i][1] * 1024 * sw
+        tf = sum(v[1] for v in agg.values())
+        tw = sum(v[2] for v in agg.values())
+        lines.append(f"# library kernels in the scope: fetched {tf / 1e9:.3f} GB, written {tw / 1e9:.3f} GB, "
+                     f"total {(tf + tw) / 1e9:.3f} GB")
+        lines.append("# kernel | launches | fetched GB | written GB | GB per launch")
+        for k, (c, x, y) in sorted(agg.items(), key=lambda kv: -(kv[1][1] + kv[1][2])):
+            lines.append(f"{k[:96]:96s} | {c:5d} | {x / 1e9:9.3f} | {y / 1e9:8.3f} | {(x + y) / c / 1e9:8.4f}")
+    return "\n".join(lines)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -527,7 +681,18 @@ def main():
     ap.add_argument("--profile", choices=PROFILE_MODES, default=None,
                     help="only a 1 GiB device copy (counter scale reference) and ONE run of this workload, "
                          "for rocprofv3 kernel traces and counters per configuration")
+    ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
+                    help="print a summary of rocprofv3 CSV output instead of running: trace DIR | mfma DIR | "
+                         "hbm FETCH_DIR WRITE_DIR (no GPU needed)")
+    ap.add_argument("--scope", choices=("last", "all"), default="last",
+                    help="with --summarize: the last run of the workload (from the last --marker launch) or "
+                         "everything after the reference copy")
+    ap.add_argument("--marker", default="embed_kernel", help="with --summarize: the kernel that starts a run")
+    ap.add_argument("--title", default="rocprofv3 summary")
     args = ap.parse_args()
+    if args.summarize:
+        print(summarize(args.summarize[0], args.summarize[1:], args.scope, args.marker, args.title))
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: the looped-decoder path runs on one GPU (it has no cross-GPU path); run with --gpus 1", flush=True)
         sys.exit(2)
