@@ -149,7 +149,9 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
     const bf16_t* vs = smem + (kt % AQ_NS) * AQ_STAGE + PK * PD;
     // st[c][r]: key kt*64 + 32c + 16(r/8) + 8h + r%8, query column `col`
     const bool diag = kt * PK + PK - 1 > a.pos0 + q0;
-    float tmax = -INFINITY;
+    // four independent partial maxima (and sums below), so that a wave
+    // alone on its SIMD's vector ALU is not held up by one dependent chain
+    float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     if (diag) {
 #pragma unroll
       for (int c = 0; c < 2; ++c)
@@ -158,29 +160,31 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
           const int key = kt * PK + c * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
           const float v = (key <= qpos && key < kv_end) ? st[c][r] : -INFINITY;
           st[c][r] = v;
-          tmax = fmaxf(tmax, v);
+          tm[r & 3] = fmaxf(tm[r & 3], v);
         }
     } else {
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, st[c][r]);
+        for (int r = 0; r < 16; ++r) tm[r & 3] = fmaxf(tm[r & 3], st[c][r]);
     }
+    float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
     tmax = x32_max(tmax) * sc;     // scaled (base-2) units
     // the running max moves only when the tile's max exceeds it by more than
     // 8: the probabilities stay below 2^8 and the result is the same softmax,
     // with fewer rescales of O
     const float mnew = tmax > mrun + 8.f ? tmax : mrun;
     const float mfin = (mnew == -INFINITY) ? 0.f : mnew;
-    float psum = 0.f;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = exp2_hw(fmaf(st[c][r], sc, -mfin));
         st[c][r] = p;
-        psum += p;
+        ps[r & 3] += p;
       }
+    const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
     if (__any(mnew > mrun)) {
       const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(mrun - mnew);
       lrun *= alpha;
