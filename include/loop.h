@@ -154,13 +154,34 @@ int loop_workspace_bytes(const loop_model* m, int batch, int max_tokens, int max
  * loop_state_check(). */
 int loop_state_create(const loop_model* m, void* state_dev, size_t bytes, int batch, int max_seq, loop_state** out);
 int loop_state_destroy(loop_state* st);
+/* Paged KV caches, for serving.  Serving shared-weight loops is the gap one
+ * page names ("SenseTime Open-Sources Loop-9B: Same Layers, Run Twice", its
+ * closing paragraphs on costs): a looped model needs one cache per (layer,
+ * pass), so a paged state gives every full-attention (layer, pass) slot its
+ * own pool of n_pages pages of 64 positions, K [n_pages][Hkv][64][d] and V^T
+ * [n_pages][Hkv][d][64], and one block table maps each sequence's positions
+ * to pages for all slots at once: positions [64 j, 64 j + 64) of sequence b
+ * live in page block_table_dev[b * ceil(max_seq / 64) + j] of every pool.
+ * block_table_dev is caller-owned device memory, int32 [batch][ceil(max_seq /
+ * 64)], read by the kernels of every call (the caller may change entries
+ * between calls, for example to give a growing sequence its next page); an
+ * entry outside [0, n_pages) is clamped into it, so a bad entry gives wrong
+ * results but no access outside the pools.  Two sequences that write the
+ * same page race; sharing pages that no call writes (a common prefix) is
+ * allowed.  Everything else (linear states, lengths, ragged batches, every
+ * prefill and decode entry point) is as for loop_state_create.
+ * loop_state_bytes_paged: device bytes of such a state (the pools replace the
+ * per-sequence slots; the rest as loop_state_bytes).  loop_state_create_paged:
+ * max_seq <= 524,288.  Errors: INVALID_ARG (n_pages <= 0, null table), ALIGN,
+ * CAPACITY. */
+int loop_state_bytes_paged(const loop_model* m, int batch, int max_seq, int n_pages, size_t* bytes);
+int loop_state_create_paged(const loop_model* m, void* state_dev, size_t bytes, int batch, int max_seq, int n_pages,
+                            const int32_t* block_table_dev, loop_state** out);
+
 /* Every sequence of a state has its own length (the positions its KV caches
  * and linear states hold).  Sequences of one state may differ (a ragged
  * batch): loop_prefill_rows fills a subset, and loop_decode_step advances
- * each sequence from its own length.  Ragged serving is the gap one page
- * names for shared-weight loops ("SenseTime Open-Sources Loop-9B: Same
- * Layers, Run Twice" (nvdium.com), its closing paragraphs on costs); the
- * caches stay one contiguous slot per sequence (no paging).
+ * each sequence from its own length (contiguous or paged caches).
  *
  * loop_state_length: the shortest sequence's length (the common length when
  * all agree).  loop_state_seq_length: sequence `seq`'s length. */
@@ -178,8 +199,9 @@ int loop_state_seq_length(const loop_state* st, int seq, int* length);
 int loop_state_set_length(loop_state* st, int length);
 int loop_state_set_seq_length(loop_state* st, int seq, int length);
 /* Device pointer and byte size of one region of the state: kind 0 = K, 1 = V^T
- * (slot = full-attention execution index), 2 = S, 3 = z (slot = linear
- * execution index), 4 = header (slot ignored; word 0 = error flags). */
+ * (slot = full-attention execution index; a page pool for a paged state),
+ * 2 = S, 3 = z (slot = linear execution index), 4 = header (slot ignored;
+ * word 0 = error flags). */
 int loop_state_region(const loop_state* st, int kind, int slot, void** ptr, size_t* bytes);
 /* Synchronises the stream, reads and clears the device error word.
  * Returns LOOP_OK or LOOP_ERR_DEVICE_FLAG (token id out of range: row 0 used). */

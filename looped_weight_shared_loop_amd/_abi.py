@@ -65,6 +65,9 @@ SYMBOLS = {
     "loop_state_bytes": (c_int, [c_void_p, c_int, c_int, POINTER(c_size_t)]),
     "loop_workspace_bytes": (c_int, [c_void_p, c_int, c_int, c_int, POINTER(c_size_t)]),
     "loop_state_create": (c_int, [c_void_p, c_void_p, c_size_t, c_int, c_int, POINTER(c_void_p)]),
+    "loop_state_bytes_paged": (c_int, [c_void_p, c_int, c_int, c_int, POINTER(c_size_t)]),
+    "loop_state_create_paged": (c_int, [c_void_p, c_void_p, c_size_t, c_int, c_int, c_int, c_void_p,
+                                        POINTER(c_void_p)]),
     "loop_state_destroy": (c_int, [c_void_p]),
     "loop_state_length": (c_int, [c_void_p, POINTER(c_int)]),
     "loop_state_set_length": (c_int, [c_void_p, c_int]),
@@ -174,6 +177,20 @@ def loop_state_create(m, state_ptr: int, nbytes: int, batch: int, max_seq: int) 
     h = c_void_p()
     _check(lib().loop_state_create(m, c_void_p(state_ptr), nbytes, batch, max_seq, ctypes.byref(h)),
            "loop_state_create")
+    return h
+
+
+def loop_state_bytes_paged(m, batch: int, max_seq: int, n_pages: int) -> int:
+    b = c_size_t()
+    _check(lib().loop_state_bytes_paged(m, batch, max_seq, n_pages, ctypes.byref(b)), "loop_state_bytes_paged")
+    return b.value
+
+
+def loop_state_create_paged(m, state_ptr: int, nbytes: int, batch: int, max_seq: int, n_pages: int,
+                            table_ptr: int) -> c_void_p:
+    h = c_void_p()
+    _check(lib().loop_state_create_paged(m, c_void_p(state_ptr), nbytes, batch, max_seq, n_pages,
+                                         c_void_p(table_ptr), ctypes.byref(h)), "loop_state_create_paged")
     return h
 
 

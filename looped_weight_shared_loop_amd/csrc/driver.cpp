@@ -81,6 +81,18 @@ struct loop_state {
   size_t bytes;
   int batch, max_seq, S_max;
   std::vector<int> seq_len;     // positions each sequence holds (sequences may differ: ragged batch)
+  // paged KV: each full-attention slot is a pool of n_pages pages of 64
+  // positions; table [batch][table_stride] (caller-owned device memory) maps a
+  // sequence's 64-position block to its page in every slot's pool
+  int n_pages = 0;
+  const int32_t* table = nullptr;
+  int table_stride = 0;
+  // the page table of the sequences from seq0 on (empty for a contiguous state)
+  lk::KvPages pages(int seq0) const {
+    return table ? lk::KvPages{table + (size_t)seq0 * table_stride, table_stride, n_pages} : lk::KvPages{};
+  }
+  // byte offset of sequence seq0's part of a K or V^T slot (0 for a paged pool, which all share)
+  size_t kv_seq_off(int seq0, size_t per_seq) const { return table ? 0 : (size_t)seq0 * per_seq; }
   size_t pos_off = 0;           // int32 [batch] device copy of a ragged call's start positions
   std::vector<size_t> koff, voff, soff, zoff;
   // pipelined decode: cohort g holds sequences [g B, (g + 1) B), B = batch / n_passes.
@@ -304,11 +316,13 @@ int loop_model_schedule(const loop_model* m, int max, int* layer, int* pass, int
   return LOOP_OK;
 }
 
-static void state_offsets(const loop_model* m, int batch, int max_seq, std::vector<size_t>* k, std::vector<size_t>* v,
-                          std::vector<size_t>* s, std::vector<size_t>* z, size_t* total, size_t* park = nullptr) {
+static void state_offsets(const loop_model* m, int batch, int max_seq, int n_pages, std::vector<size_t>* k,
+                          std::vector<size_t>* v, std::vector<size_t>* s, std::vector<size_t>* z, size_t* total,
+                          size_t* park = nullptr) {
   const loop_config& c = m->cfg;
   const size_t S_max = ((size_t)max_seq + 63) / 64 * 64;
-  const size_t kv = (size_t)batch * c.n_kv_heads * S_max * c.head_dim * m->es;
+  // contiguous: K [batch][Hkv][S_max][d] per slot; paged: a pool K [n_pages][Hkv][64][d]
+  const size_t kv = (n_pages > 0 ? (size_t)n_pages * 64 : (size_t)batch * S_max) * c.n_kv_heads * c.head_dim * m->es;
   const size_t sb = (size_t)batch * c.n_kv_heads * c.head_dim * c.head_dim * sizeof(float);
   const size_t zb = (size_t)batch * c.n_kv_heads * c.head_dim * sizeof(float);
   size_t off = 256;
@@ -341,7 +355,7 @@ static void state_offsets(const loop_model* m, int batch, int max_seq, std::vect
 int loop_state_bytes(const loop_model* m, int batch, int max_seq, size_t* bytes) {
   if (!m || !bytes) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
   if (batch <= 0 || max_seq <= 0) return lp_fail(LOOP_ERR_INVALID_ARG, "batch and max_seq must be positive");
-  state_offsets(m, batch, max_seq, nullptr, nullptr, nullptr, nullptr, bytes);
+  state_offsets(m, batch, max_seq, 0, nullptr, nullptr, nullptr, nullptr, bytes);
   return LOOP_OK;
 }
 
@@ -352,14 +366,32 @@ int loop_workspace_bytes(const loop_model* m, int batch, int max_tokens, int max
   return LOOP_OK;
 }
 
-int loop_state_create(const loop_model* m, void* state_dev, size_t bytes, int batch, int max_seq, loop_state** out) {
+// Largest cache length of a paged state: the prefill attention keeps the page
+// numbers of a workgroup's tiles (up to 8,192) in LDS next to its ring.
+constexpr int PAGED_MAX_SEQ = 8192 * 64;
+
+int loop_state_bytes_paged(const loop_model* m, int batch, int max_seq, int n_pages, size_t* bytes) {
+  if (!m || !bytes) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
+  if (batch <= 0 || max_seq <= 0 || n_pages <= 0)
+    return lp_fail(LOOP_ERR_INVALID_ARG, "batch, max_seq and n_pages must be positive");
+  state_offsets(m, batch, max_seq, n_pages, nullptr, nullptr, nullptr, nullptr, bytes);
+  return LOOP_OK;
+}
+
+static int state_create(const loop_model* m, void* state_dev, size_t bytes, int batch, int max_seq, int n_pages,
+                        const int32_t* table, loop_state** out) {
   if (!m || !state_dev || !out) return lp_fail(LOOP_ERR_INVALID_ARG, "null argument");
   *out = nullptr;
   if (batch <= 0 || max_seq <= 0) return lp_fail(LOOP_ERR_INVALID_ARG, "batch and max_seq must be positive");
   if (misaligned(state_dev)) return lp_fail(LOOP_ERR_ALIGN, "state not 16-byte aligned");
+  if (n_pages > 0) {
+    if (!table) return lp_fail(LOOP_ERR_INVALID_ARG, "null block table");
+    if ((uintptr_t)table % 4) return lp_fail(LOOP_ERR_ALIGN, "block table not 4-byte aligned");
+    if (max_seq > PAGED_MAX_SEQ) return lp_fail(LOOP_ERR_CAPACITY, "paged state: max_seq %d above %d", max_seq, PAGED_MAX_SEQ);
+  }
   auto* st = new loop_state();
   size_t need = 0, park[4] = {0, 0, 0, 0};
-  state_offsets(m, batch, max_seq, &st->koff, &st->voff, &st->soff, &st->zoff, &need, park);
+  state_offsets(m, batch, max_seq, n_pages, &st->koff, &st->voff, &st->soff, &st->zoff, &need, park);
   if (bytes < need) {
     delete st;
     return lp_fail(LOOP_ERR_CAPACITY, "state has %zu bytes, needs %zu", bytes, need);
@@ -376,8 +408,23 @@ int loop_state_create(const loop_model* m, void* state_dev, size_t bytes, int ba
   st->park_maps = park[2];
   st->pos_off = park[3];
   st->pipe_next.assign(m->cfg.n_passes, 0);
+  if (n_pages > 0) {
+    st->n_pages = n_pages;
+    st->table = table;
+    st->table_stride = (max_seq + 63) / 64;
+  }
   *out = st;
   return LOOP_OK;
+}
+
+int loop_state_create(const loop_model* m, void* state_dev, size_t bytes, int batch, int max_seq, loop_state** out) {
+  return state_create(m, state_dev, bytes, batch, max_seq, 0, nullptr, out);
+}
+
+int loop_state_create_paged(const loop_model* m, void* state_dev, size_t bytes, int batch, int max_seq, int n_pages,
+                            const int32_t* block_table_dev, loop_state** out) {
+  if (n_pages <= 0) return lp_fail(LOOP_ERR_INVALID_ARG, "n_pages must be positive");
+  return state_create(m, state_dev, bytes, batch, max_seq, n_pages, block_table_dev, out);
 }
 
 int loop_state_destroy(loop_state* st) {
@@ -421,7 +468,8 @@ int loop_state_region(const loop_state* st, int kind, int slot, void** ptr, size
   const loop_model* m = st->m;
   const loop_config& c = m->cfg;
   size_t off = 0, sz = 0;
-  const size_t kv = (size_t)st->batch * c.n_kv_heads * st->S_max * c.head_dim * m->es;
+  const size_t kv = (st->table ? (size_t)st->n_pages * 64 : (size_t)st->batch * st->S_max) * c.n_kv_heads *
+                    c.head_dim * m->es;
   switch (kind) {
     case 0: case 1:
       if (slot < 0 || slot >= m->n_full) return lp_fail(LOOP_ERR_INVALID_ARG, "full slot %d out of range", slot);
@@ -519,7 +567,8 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, int
   const int qkv_rows = m->qkv_rows();
   const int mhc_grid = T < 2 * m->cu ? T : 2 * m->cu;
   // per-sequence slices of the slots: the kernels index sequences from the base
-  const size_t kv_skip = (size_t)seq0 * Hkv * st->S_max * d * m->es;
+  const size_t kv_skip = st->kv_seq_off(seq0, (size_t)Hkv * st->S_max * d * m->es);
+  const lk::KvPages pages = st->pages(seq0);
   const size_t s_skip = (size_t)seq0 * Hkv * d * d, z_skip = (size_t)seq0 * Hkv * d;
   const int* pos_dev = nullptr;
   if (ragged) {
@@ -603,11 +652,11 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, int
       g.q_cols = Hq * d; g.n_kv = Hkv; g.head_dim = d;
       g.kcache = st->base + st->koff[ex.slot] + kv_skip;
       g.vcache = st->base + st->voff[ex.slot] + kv_skip;
-      g.S_call = S; g.pos0 = pos0; g.S_max = st->S_max; g.pos_dev = pos_dev;
+      g.S_call = S; g.pos0 = pos0; g.S_max = st->S_max; g.pos_dev = pos_dev; g.pages = pages;
       LAUNCH(run_gemm(g), "qkv gemm");
       lk::AttnArgs a{};
       a.dt = dt; a.B = B; a.S_call = S; a.pos0 = pos0; a.S_max = st->S_max; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
-      a.pos_dev = pos_dev;
+      a.pos_dev = pos_dev; a.pages = pages;
       a.q = qkv; a.ldq = qkv_rows; a.kcache = g.kcache; a.vcache = g.vcache; a.out = attn; a.ldo = Hq * d;
       if (decode && dt == lk::DT_BF16) {
         const lk::DecodePlan dp = lk::decode_plan(B, Hkv, pos0 + S, m->cu);
@@ -812,9 +861,9 @@ int decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_b
       const int g = coh[0];
       lk::GemmArgs q = gemm(lk::EPI_QKV, rows(u, r0, C), C, n, W.qkv, qkv_rows, C, rows(qkv, r0, qkv_rows), qkv_rows);
       q.q_cols = Hq * d; q.n_kv = Hkv; q.head_dim = d;
-      q.kcache = st->base + st->koff[exs[0]->slot] + (size_t)g * B * Hkv * st->S_max * d * es;
-      q.vcache = st->base + st->voff[exs[0]->slot] + (size_t)g * B * Hkv * d * st->S_max * es;
-      q.S_call = 1; q.pos0 = st->seq_len[g * B]; q.S_max = st->S_max;
+      q.kcache = st->base + st->koff[exs[0]->slot] + st->kv_seq_off(g * B, (size_t)Hkv * st->S_max * d * es);
+      q.vcache = st->base + st->voff[exs[0]->slot] + st->kv_seq_off(g * B, (size_t)Hkv * d * st->S_max * es);
+      q.S_call = 1; q.pos0 = st->seq_len[g * B]; q.S_max = st->S_max; q.pages = st->pages(g * B);
       LAUNCH(run_gemm(q, false), "qkv gemm");
     } else {
       LAUNCH(run_gemm(gemm(lk::EPI_STORE, rows(u, r0, C), C, n, W.qkv, qkv_rows, C, rows(qkv, r0, qkv_rows),
@@ -826,12 +875,14 @@ int decode_pipelined(loop_model* m, loop_state* st, void* workspace, size_t ws_b
       const int pos = st->seq_len[g * B];
       char* qrow = rows(qkv, g * B, qkv_rows);
       if (full) {
-        char* kc = st->base + st->koff[ex.slot] + (size_t)g * B * Hkv * st->S_max * d * es;
-        char* vc = st->base + st->voff[ex.slot] + (size_t)g * B * Hkv * d * st->S_max * es;
+        char* kc = st->base + st->koff[ex.slot] + st->kv_seq_off(g * B, (size_t)Hkv * st->S_max * d * es);
+        char* vc = st->base + st->voff[ex.slot] + st->kv_seq_off(g * B, (size_t)Hkv * d * st->S_max * es);
+        const lk::KvPages pg = st->pages(g * B);
         if (!fused)
-          LAUNCH(lk::kv_append(dt, qrow, qkv_rows, Hq * d, B, Hkv, d, kc, vc, st->S_max, pos, s), "kv append");
+          LAUNCH(lk::kv_append(dt, qrow, qkv_rows, Hq * d, B, Hkv, d, kc, vc, st->S_max, pos, pg, s), "kv append");
         lk::AttnArgs a{};
         a.dt = dt; a.B = B; a.S_call = 1; a.pos0 = pos; a.S_max = st->S_max; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
+        a.pages = pg;
         a.q = qrow; a.ldq = qkv_rows; a.kcache = kc; a.vcache = vc; a.out = rows(attn, g * B, Hq * d);
         a.ldo = Hq * d;
         if (dt == lk::DT_BF16) {

@@ -45,6 +45,7 @@ DEV int vq_sw(int r, int u) { return r * PK + ((u ^ ((r >> 1) & 7)) << 3); }
 constexpr int AQ_NW = 8;                       // waves per workgroup
 constexpr int AQ_NS = 4;                       // LDS stages
 constexpr int AQ_LDS = AQ_NS * AQ_STAGE * 2;   // 128 KB
+constexpr int AQ_LDS_MAX = 160 * 1024;          // the CU's LDS: with a paged cache, up to 8,192 tile pages
 
 __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
   constexpr int NW = AQ_NW, AHEAD = AQ_NS - 1;
@@ -65,13 +66,22 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
   const int ntiles = (kv_end + PK - 1) / PK;
   const int wave_last = a.pos0 + min(q0 + 31, a.S_call - 1);       // last key this wave can see
 
+  // paged cache: the page of every tile the workgroup reads, kept in LDS past the ring
+  const bool paged = a.pages.table != nullptr;
+  int* pglist = reinterpret_cast<int*>(smem + AQ_NS * AQ_STAGE);
+  if (paged) {
+    for (int t = tid; t < ntiles; t += 64 * NW) pglist[t] = kv_page(a.pages, b, t * PK);
+    __syncthreads();
+  }
+
   const bf16_t* Q = (const bf16_t*)a.q + (size_t)(b * a.S_call + min(m, a.S_call - 1)) * a.ldq + j * PD;
   bf16x8_t qf[8];
 #pragma unroll
   for (int ds = 0; ds < 8; ++ds) qf[ds] = as_bf16x8(ldv4(Q + ds * 16 + h * 8));
 
-  const bf16_t* Kg = (const bf16_t*)a.kcache + ((size_t)(b * a.Hkv + kvh) * a.S_max) * PD;
-  const bf16_t* Vg = (const bf16_t*)a.vcache + ((size_t)(b * a.Hkv + kvh) * PD) * a.S_max;
+  const bf16_t* Kg = (const bf16_t*)a.kcache + (paged ? 0 : ((size_t)(b * a.Hkv + kvh) * a.S_max) * PD);
+  const bf16_t* Vg = (const bf16_t*)a.vcache + (paged ? 0 : ((size_t)(b * a.Hkv + kvh) * PD) * a.S_max);
+  const int vstride = kv_vstride(a.pages, a.S_max);
   // DMA: per tile 16 K blocks of 4 rows and 16 V^T blocks of 8 rows; wave w
   // issues blocks 2w and 2w + 1 of each.  Lane l writes LDS bytes 16 l .. of
   // the block, so it fetches the global unit that the swizzle puts there.
@@ -83,17 +93,27 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
     koff[i] = kr * PD + ((ks ^ (kr & 15)) << 3);
     kl[i] = blk * 512;
     const int vr = 8 * blk + (lane >> 3), vs = lane & 7;
-    voff[i] = vr * a.S_max + ((vs ^ ((vr >> 1) & 7)) << 3);
+    voff[i] = vr * vstride + ((vs ^ ((vr >> 1) & 7)) << 3);
     vl[i] = PK * PD + blk * 512;
   }
   auto issue = [&](int kt) {
     bf16_t* st = smem + (kt % AQ_NS) * AQ_STAGE;
-    const int k0 = min(kt, ntiles - 1) * PK;
+    const int tile = min(kt, ntiles - 1);
+    const bf16_t* Kt;
+    const bf16_t* Vt;
+    if (paged) {
+      const int pg = __builtin_amdgcn_readfirstlane(pglist[tile]);
+      Kt = Kg + (((size_t)pg * a.Hkv + kvh) * KV_PAGE) * PD;
+      Vt = Vg + ((size_t)pg * a.Hkv + kvh) * PD * KV_PAGE;
+    } else {
+      Kt = Kg + (size_t)tile * PK * PD;
+      Vt = Vg + tile * PK;
+    }
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Kg + (size_t)k0 * PD + koff[i]),
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Kt + koff[i]),
                                        (void __attribute__((address_space(3)))*)(st + kl[i]), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Vg + k0 + voff[i]),
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Vt + voff[i]),
                                        (void __attribute__((address_space(3)))*)(st + vl[i]), 16, 0, 0);
     }
   };
@@ -325,8 +345,10 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
 #pragma unroll
   for (int ds = 0; ds < 4; ++ds) qf[ds] = as_bf16x8(cvalid ? ldv4(Q + ds * 32 + g * 8) : zero);
 
-  const bf16_t* Kg = (const bf16_t*)a.kcache + ((size_t)(b * a.Hkv + kvh) * a.S_max) * PD;
-  const bf16_t* Vg = (const bf16_t*)a.vcache + ((size_t)(b * a.Hkv + kvh) * PD) * a.S_max;
+  const bool paged = a.pages.table != nullptr;
+  const bf16_t* Kg = (const bf16_t*)a.kcache + (paged ? 0 : ((size_t)(b * a.Hkv + kvh) * a.S_max) * PD);
+  const bf16_t* Vg = (const bf16_t*)a.vcache + (paged ? 0 : ((size_t)(b * a.Hkv + kvh) * PD) * a.S_max);
+  const int vstride = kv_vstride(a.pages, a.S_max);
   const float sc = LOG2E / sqrtf((float)PD);
 
   f32x4_t o[8];
@@ -334,21 +356,28 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
   for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lrun = 0.f;
 
+  // a round is 64 keys starting at a multiple of 64: one page of a paged
+  // cache, whose number is read one round ahead
+  int pg = (paged && k_begin + wid * 64 < k_end) ? kv_page(a.pages, b, k_begin + wid * 64) : 0;
   for (int k0 = k_begin + wid * 64; k0 < k_end; k0 += DW * 64) {
+    const int pg_next = (paged && k0 + DW * 64 < k_end) ? kv_page(a.pages, b, k0 + DW * 64) : 0;
+    const bf16_t* Kround = paged ? Kg + (((size_t)pg * a.Hkv + kvh) * KV_PAGE) * PD : Kg + (size_t)k0 * PD;
+    const bf16_t* Vround = paged ? Vg + ((size_t)pg * a.Hkv + kvh) * PD * KV_PAGE : Vg + k0;
+    pg = pg_next;
     // loads of the whole round first: K rows (S^T operand) and V^T (PV operand).
-    // Keys past k_end stay inside the slot (S_max % 64 == 0) and are masked.
+    // Keys past k_end stay inside the slot or page (S_max % 64 == 0) and are masked.
     u32x4_t kf[4][4], vf[2][8];
 #pragma unroll
     for (int sb = 0; sb < 4; ++sb) {
-      const int key = k0 + 32 * (sb >> 1) + (c >> 2) * 8 + (sb & 1) * 4 + (c & 3);
-      const bf16_t* kr = Kg + (size_t)key * PD + g * 8;
+      const int key = 32 * (sb >> 1) + (c >> 2) * 8 + (sb & 1) * 4 + (c & 3);   // within the round
+      const bf16_t* kr = Kround + (size_t)key * PD + g * 8;
 #pragma unroll
       for (int ds = 0; ds < 4; ++ds) kf[sb][ds] = ldv4(kr + ds * 32);
     }
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int db = 0; db < 8; ++db) vf[kk][db] = ldv4(Vg + (size_t)(db * 16 + c) * a.S_max + k0 + 32 * kk + 8 * g);
+      for (int db = 0; db < 8; ++db) vf[kk][db] = ldv4(Vround + (size_t)(db * 16 + c) * vstride + 32 * kk + 8 * g);
 
     f32x4_t st[4];
 #pragma unroll
@@ -485,8 +514,9 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a) {
   if (t >= a.S_call) return;
   const int G = a.Hq / a.Hkv, kvh = j / G;
   const float* q = (const float*)a.q + (size_t)(b * a.S_call + t) * a.ldq + j * D;
-  const float* K = (const float*)a.kcache + ((size_t)(b * a.Hkv + kvh) * a.S_max) * D;
-  const float* V = (const float*)a.vcache + ((size_t)(b * a.Hkv + kvh) * D) * a.S_max;
+  const float* K = (const float*)a.kcache;
+  const float* V = (const float*)a.vcache;
+  const int vstride = kv_vstride(a.pages, a.S_max);
   float qr[D], o[D];
   const float sc = 1.0f / sqrtf((float)D);
 #pragma unroll
@@ -494,15 +524,17 @@ __global__ __launch_bounds__(64) void attn_f32(AttnArgs a) {
   float m = -INFINITY, l = 0.f;
   const int last = (a.pos_dev ? min(max(a.pos_dev[b], 0), a.pos0) : a.pos0) + t;
   for (int key = 0; key <= last; ++key) {
+    const float* Kr = K + kv_k_off(a.pages, a.Hkv, a.S_max, D, b, kvh, key);
+    const float* Vc = V + kv_v_off(a.pages, a.Hkv, a.S_max, D, b, kvh, key);
     float s = 0.f;
 #pragma unroll
-    for (int i = 0; i < D; ++i) s += qr[i] * K[(size_t)key * D + i];
+    for (int i = 0; i < D; ++i) s += qr[i] * Kr[i];
     s *= sc;
     const float mn = fmaxf(m, s);
     const float al = expf(m - mn), p = expf(s - mn);
     l = l * al + p;
 #pragma unroll
-    for (int i = 0; i < D; ++i) o[i] = o[i] * al + p * V[(size_t)i * a.S_max + key];
+    for (int i = 0; i < D; ++i) o[i] = o[i] * al + p * Vc[(size_t)i * vstride];
     m = mn;
   }
   float* out = (float*)a.out + (size_t)(b * a.S_call + t) * a.ldo + j * D;
@@ -525,15 +557,20 @@ hipError_t attn_prefill(const AttnArgs& a, hipStream_t s) {
   const int G = a.Hq / a.Hkv;
   if (a.d != PD || a.Hq % a.Hkv || !(G == 1 || G == 2 || G == 4 || G == 8) || a.S_max % 64)
     return hipErrorInvalidValue;
+  // a paged cache keeps the page numbers of the workgroup's tiles in LDS past the ring
+  const long tiles = ((long)a.pos0 + a.S_call + PK - 1) / PK;
+  const size_t lds = AQ_LDS + (a.pages.table ? (size_t)tiles * sizeof(int) : 0);
+  if (lds > AQ_LDS_MAX) return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_dma, hipFuncAttributeMaxDynamicSharedMemorySize, AQ_LDS);
+    hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_dma, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       AQ_LDS_MAX);
     if (e != hipSuccess) return e;
     attr = true;
   }
   const int qpw = 32 * (AQ_NW / G);   // queries per workgroup
   dim3 grid((a.S_call + qpw - 1) / qpw, a.Hkv, a.B);
-  attn_prefill_dma<<<grid, 64 * AQ_NW, AQ_LDS, s>>>(a);
+  attn_prefill_dma<<<grid, 64 * AQ_NW, lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -560,27 +597,28 @@ hipError_t attn_decode(const AttnArgs& a, hipStream_t s) {
 template <typename T>
 __global__ __launch_bounds__(256) void kv_append_kernel(const T* __restrict__ qkv, long ld, int q_cols, int B,
                                                         int Hkv, int d, T* __restrict__ kc, T* __restrict__ vc,
-                                                        int S_max, int pos) {
+                                                        int S_max, int pos, KvPages pages) {
   const int n = B * Hkv * d;
+  const int vstride = kv_vstride(pages, S_max);
   for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) {
     const int b = i / (Hkv * d), r = i - b * Hkv * d, hk = r / d, dd = r - hk * d;
     const T* row = qkv + (size_t)b * ld + q_cols;
-    kc[(((size_t)b * Hkv + hk) * S_max + pos) * d + dd] = row[hk * d + dd];
-    vc[(((size_t)b * Hkv + hk) * d + dd) * S_max + pos] = row[Hkv * d + hk * d + dd];
+    kc[kv_k_off(pages, Hkv, S_max, d, b, hk, pos) + dd] = row[hk * d + dd];
+    vc[kv_v_off(pages, Hkv, S_max, d, b, hk, pos) + (size_t)dd * vstride] = row[Hkv * d + hk * d + dd];
   }
 }
 
 hipError_t kv_append(int dt, const void* qkv, long ld, int q_cols, int B, int Hkv, int d, void* kcache,
-                     void* vcache, int S_max, int pos, hipStream_t s) {
+                     void* vcache, int S_max, int pos, KvPages pages, hipStream_t s) {
   const int n = B * Hkv * d;
   if (n <= 0) return hipSuccess;
   const int grid = (n + 255) / 256;
   if (dt == DT_BF16)
     kv_append_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)qkv, ld, q_cols, B, Hkv, d, (bf16_t*)kcache,
-                                                  (bf16_t*)vcache, S_max, pos);
+                                                  (bf16_t*)vcache, S_max, pos, pages);
   else
     kv_append_kernel<float><<<grid, 256, 0, s>>>((const float*)qkv, ld, q_cols, B, Hkv, d, (float*)kcache,
-                                                 (float*)vcache, S_max, pos);
+                                                 (float*)vcache, S_max, pos, pages);
   return hipGetLastError();
 }
 

@@ -35,11 +35,12 @@ DEV void epi_qkv(const GemmArgs& a, int row, int col, float v) {
   const int pos = (a.pos_dev ? min(max(a.pos_dev[b], 0), a.pos0) : a.pos0) + row % a.S_call;
   if (cc < kvn) {
     const int hk = cc / a.head_dim, dd = cc % a.head_dim;
-    st1((T*)a.kcache + (((size_t)b * a.n_kv + hk) * a.S_max + pos) * a.head_dim + dd, v);
+    st1((T*)a.kcache + kv_k_off(a.pages, a.n_kv, a.S_max, a.head_dim, b, hk, pos) + dd, v);
   } else {
     cc -= kvn;
     const int hk = cc / a.head_dim, dd = cc % a.head_dim;
-    st1((T*)a.vcache + (((size_t)b * a.n_kv + hk) * a.head_dim + dd) * a.S_max + pos, v);
+    st1((T*)a.vcache + kv_v_off(a.pages, a.n_kv, a.S_max, a.head_dim, b, hk, pos) +
+            (size_t)dd * kv_vstride(a.pages, a.S_max), v);
   }
 }
 
@@ -490,7 +491,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
     // plain row-major block, stored like the q tiles
     int ksq = -1;
     if (EPI == EPI_QKV && n0 >= a.q_cols && n0 + TBN <= a.q_cols + a.n_kv * a.head_dim && a.head_dim == WCOL &&
-        !a.pos_dev && m0 / a.S_call == (min(m0 + TBM, a.M) - 1) / a.S_call)
+        !a.pos_dev && !a.pages.table && m0 / a.S_call == (min(m0 + TBM, a.M) - 1) / a.S_call)
       ksq = m0 / a.S_call;
     if (EPI == EPI_SWIGLU || EPI == EPI_STORE || EPI == EPI_F32 || n0 + TBN <= a.q_cols || ksq >= 0) {
       constexpr int ES = EPI == EPI_F32 ? 4 : 2;      // output element bytes
@@ -533,8 +534,8 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
       // they go out as one 8-byte store (same sequence and 4-aligned positions
       // when S_call and pos0 are multiples of 4)
       const int kvn = a.n_kv * a.head_dim;
-      const bool vtile = EPI == EPI_QKV && n0 >= a.q_cols + kvn && !a.pos_dev && a.S_call % 4 == 0 &&
-                         a.pos0 % 4 == 0 && (a.head_dim & 31) == 0;
+      const bool vtile = EPI == EPI_QKV && n0 >= a.q_cols + kvn && !a.pos_dev && !a.pages.table &&
+                         a.S_call % 4 == 0 && a.pos0 % 4 == 0 && (a.head_dim & 31) == 0;
       if (vtile) {
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib)

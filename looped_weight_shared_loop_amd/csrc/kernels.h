@@ -67,6 +67,33 @@ hipError_t mhc(const MhcArgs& a, hipStream_t s);
 
 // ---------------------------------------------------------------- GEMM
 enum Epi { EPI_STORE = 0, EPI_F32 = 1, EPI_QKV = 2, EPI_SWIGLU = 3 };
+// Paged KV cache of one full-attention slot: positions [64 j, 64 j + 64) of
+// sequence b live in page table[b * stride + j] of the slot's page pool, K
+// [n_pages][Hkv][64][d] and V^T [n_pages][Hkv][d][64] (every slot has its own
+// pool; the table is shared).  Page numbers are clamped to [0, n_pages), so no
+// table entry can make an access leave the pool.  table null: the contiguous
+// layout K [B][Hkv][S_max][d], V^T [B][Hkv][d][S_max].
+constexpr int KV_PAGE = 64;
+struct KvPages {
+  const int32_t* table;
+  int stride, n_pages;
+};
+__device__ inline int kv_page(const KvPages& p, int b, int pos) {
+  const int pg = p.table[(size_t)b * p.stride + (pos >> 6)];
+  return min(max(pg, 0), p.n_pages - 1);
+}
+// element offset of K[b][hk][pos][0]
+__device__ inline size_t kv_k_off(const KvPages& p, int Hkv, int S_max, int d, int b, int hk, int pos) {
+  if (!p.table) return (((size_t)b * Hkv + hk) * S_max + pos) * d;
+  return (((size_t)kv_page(p, b, pos) * Hkv + hk) * KV_PAGE + (pos & (KV_PAGE - 1))) * d;
+}
+// element offset of V^T[b][hk][0][pos]; rows of V^T are kv_vstride() apart
+__device__ inline size_t kv_v_off(const KvPages& p, int Hkv, int S_max, int d, int b, int hk, int pos) {
+  if (!p.table) return ((size_t)b * Hkv + hk) * d * S_max + pos;
+  return ((size_t)kv_page(p, b, pos) * Hkv + hk) * d * KV_PAGE + (pos & (KV_PAGE - 1));
+}
+__host__ __device__ inline int kv_vstride(const KvPages& p, int S_max) { return p.table ? KV_PAGE : S_max; }
+
 struct GemmArgs {
   int dt, epi;
   int M, N, K;          // C[M, N] = A[M, K] . B[N, K]^T; SWIGLU: N = 2F B rows, F outputs
@@ -80,6 +107,7 @@ struct GemmArgs {
   int S_call, pos0, S_max;  // row m is sequence m / S_call at position pos0 + m % S_call
   const int* pos_dev;    // non-null: sequence b starts at pos_dev[b] (ragged batch), read clamped
                          // to [0, pos0]: pos0 then holds the largest start, which bounds the writes
+  KvPages pages;         // EPI_QKV, table non-null: kcache / vcache are page pools
   int F;                 // EPI_SWIGLU: up rows start at row F of B
   // M <= 64: split-K plan (skinny_plan) and its scratch; ksplit 1 needs none.
   int ksplit;
@@ -106,13 +134,14 @@ struct AttnArgs {
   const int* pos_dev;              // decode: non-null: sequence b's new tokens start at pos_dev[b]
                                    // (ragged batch), read clamped to [0, pos0]: pos0 then holds
                                    // the largest start, which the split plan covers
+  KvPages pages;                   // table non-null: kcache / vcache are page pools
 };
 hipError_t attn_prefill(const AttnArgs& a, hipStream_t s);
 hipError_t attn_decode(const AttnArgs& a, hipStream_t s);
 // K and V columns of B q|k|v rows (row stride ld, K from column q_cols) into a
 // cache slot at position pos (one new position per sequence).
 hipError_t kv_append(int dt, const void* qkv, long ld, int q_cols, int B, int Hkv, int d, void* kcache,
-                     void* vcache, int S_max, int pos, hipStream_t s);
+                     void* vcache, int S_max, int pos, KvPages pages, hipStream_t s);
 // Decode split of the cache: as few splits as fill `cu` workgroups over the
 // B * Hkv (sequence, KV head) pairs, each a multiple of 64 keys.
 struct DecodePlan { int split_len, n_split; };

@@ -105,14 +105,30 @@ def weights_from_arrays(cfg: ModelConfig, arrays: Dict[str, "object"], device="c
 class LoopState:
     """Caller-owned device state (per-(layer, pass) KV caches and linear states)."""
 
-    def __init__(self, model: "LoopModel", batch: int, max_seq: int):
+    def __init__(self, model: "LoopModel", batch: int, max_seq: int, n_pages: Optional[int] = None):
+        """n_pages: a paged state (every full-attention slot a pool of n_pages
+        pages of 64 positions); its block table is ``self.block_table``, int32
+        [batch][ceil(max_seq / 64)] on the device, initially page b * blocks + j
+        for block j of sequence b (fill it before use if there are fewer pages)."""
         self.model = model
         self.batch = batch
         self.max_seq = max_seq
-        self.nbytes = A.loop_state_bytes(model.handle, batch, max_seq)
+        self.n_pages = n_pages
+        self.block_table = None
+        if n_pages is None:
+            self.nbytes = A.loop_state_bytes(model.handle, batch, max_seq)
+        else:
+            self.nbytes = A.loop_state_bytes_paged(model.handle, batch, max_seq, n_pages)
+            blocks = (max_seq + 63) // 64
+            self.block_table = torch.arange(batch * blocks, dtype=torch.int32,
+                                            device=model.device).reshape(batch, blocks) % n_pages
         self.buf = torch.empty(self.nbytes, dtype=torch.uint8, device=model.device)
         self.buf[:256].zero_()
-        self.handle = A.loop_state_create(model.handle, self.buf.data_ptr(), self.nbytes, batch, max_seq)
+        if n_pages is None:
+            self.handle = A.loop_state_create(model.handle, self.buf.data_ptr(), self.nbytes, batch, max_seq)
+        else:
+            self.handle = A.loop_state_create_paged(model.handle, self.buf.data_ptr(), self.nbytes, batch, max_seq,
+                                                    n_pages, self.block_table.data_ptr())
 
     @property
     def length(self) -> int:
@@ -187,8 +203,8 @@ class LoopModel:
     def schedule(self):
         return A.loop_model_schedule(self.handle)
 
-    def new_state(self, batch: int, max_seq: int) -> LoopState:
-        return LoopState(self, batch, max_seq)
+    def new_state(self, batch: int, max_seq: int, n_pages: Optional[int] = None) -> LoopState:
+        return LoopState(self, batch, max_seq, n_pages)
 
     def workspace(self, batch: int, max_tokens: int, max_seq: int) -> torch.Tensor:
         n = A.loop_workspace_bytes(self.handle, batch, max_tokens, max_seq)
