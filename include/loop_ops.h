@@ -51,7 +51,7 @@ int loop_op_add_rmsnorm(int dtype, int T, int C, const void* y, void* h, const f
  *  ENTER: X = [h + y, h + y] (y may be NULL); maps_out, u for site (w, b, gamma).
  *  MID:   X <- H_res X + H_post y with maps_in; then maps_out and u for (w, b, gamma).
  *  EXIT:  X' = H_res X + H_post y; h = (X'0 + X'1) / 2; u = RMSNorm(h; gamma).
- * C <= 4096, C % 8 == 0.  With bf16, C % 256 == 0 and T >= 256, ENTER and
+ * C <= 4096, C % 8 == 0.  With bf16, C % 512 == 0 and T >= 256, ENTER and
  * MID run the projection W x on the matrix cores when `scratch` (>=
  * loop_op_mhc_bytes(C)) is given: W is split there into three bf16 parts
  * (high, middle, low; together within 2^-27 of W, so the projection equals a

@@ -636,7 +636,10 @@ hipError_t mhc(const MhcArgs& a, hipStream_t s) {
   // 16-token tiles on the matrix cores pay off once there are enough tiles;
   // decode-sized calls split the channels over waves (below); otherwise one
   // workgroup per token with W in registers
-  if (a.dt == DT_BF16 && a.mode != MHC_EXIT && a.C % 256 == 0 && a.wsplit && a.T >= MHC_MFMA_MIN_T) {
+  // (C % 512: a wave's channel range, C / 8, is a whole number of two-step
+  // load groups of 32 channels; at C = 256 a group would reach into the next
+  // wave's channels and count them twice)
+  if (a.dt == DT_BF16 && a.mode != MHC_EXIT && a.C % 512 == 0 && a.wsplit && a.T >= MHC_MFMA_MIN_T) {
     if (a.yp.part) return hipErrorInvalidValue;   // the tiled path reads y itself
     const int n = 8 * 2 * a.C;
     mhc_split_w<<<(n + 255) / 256, 256, 0, s>>>(a.w, a.wsplit, n);

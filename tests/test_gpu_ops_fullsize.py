@@ -387,3 +387,49 @@ def test_linear_attention_decode_prefilled_state():
     err = np.abs(got - ref).max(-1) / np.abs(ref).max(-1)
     assert err.max() < 2e-2, err.max()
     assert np.abs(S0.cpu().numpy() - Sf).max() <= 1e-5 * np.abs(Sf).max()
+
+
+@pytest.mark.parametrize("Cn", [256, 512])
+def test_mhc_narrow_streams(Cn):
+    """The mHC site on narrow streams (512 tokens): at C = 512 the tiled MFMA
+    path, at C = 256 the per-token path (a wave's C / 8 = 32 channels are one
+    32-channel step, less than the tiled path's two-step load group).  Maps
+    of the kernel's own X' against the float64 definition, X' and u."""
+    need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    T = 512
+    X = _dev_normal((T, 2, Cn), 71)
+    X0 = X.clone()
+    y = _dev_normal((T, Cn), 72)
+    logits_in = synth.normal_f32(SEED, 73, (T, 8))
+    pre_i = 1 / (1 + np.exp(-logits_in[:, 0:2].astype(np.float64)))
+    post_i = 2 / (1 + np.exp(-logits_in[:, 2:4].astype(np.float64)))
+    R = logits_in[:, 4:8].astype(np.float64).reshape(T, 2, 2)
+    res_i = M.sinkhorn(np.exp(R - R.max(axis=(1, 2), keepdims=True)), 20)
+    maps_in = np.concatenate([pre_i, post_i, res_i.reshape(T, 4)], 1).astype(np.float32)
+    mi = torch.from_numpy(maps_in).cuda()
+    mo = torch.empty(T, 8, dtype=torch.float32, device="cuda")
+    w = _dev_normal((8, 2 * Cn), 74, 0.02, torch.float32)
+    bb = _dev_normal((8,), 75, 0.02, torch.float32)
+    gamma = torch.ones(Cn, dtype=torch.float32, device="cuda")
+    u = torch.empty(T, Cn, dtype=torch.bfloat16, device="cuda")
+    nb = A.loop_op_mhc_bytes(Cn)
+    scr = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    A.loop_op_mhc(A.LOOP_BF16, A.LOOP_MHC_MID, T, Cn, 20, 1e-6, y.data_ptr(), None, X.data_ptr(), mi.data_ptr(),
+                  mo.data_ptr(), w.data_ptr(), bb.data_ptr(), gamma.data_ptr(), u.data_ptr(), scr.data_ptr(), nb,
+                  _stream())
+    torch.cuda.synchronize()
+    x_old, y_h, gX = _bf16(X0), _bf16(y), _bf16(X)
+    mi_s = maps_in.astype(np.float64)
+    Xn = M.round_bf16(np.einsum("tij,tjc->tic", mi_s[:, 4:8].reshape(-1, 2, 2), x_old)
+                      + mi_s[:, 2:4, None] * y_h[:, None, :])
+    terms = (np.abs(mi_s[:, 4:8].reshape(-1, 2, 2)) @ np.abs(x_old)) + np.abs(mi_s[:, 2:4, None] * y_h[:, None, :])
+    assert np.all(np.abs(gX - Xn) <= 2.0 ** -7 * np.abs(Xn) + 4 * 2.0 ** -24 * terms)
+    W, Bv = w.cpu().numpy().astype(np.float64), bb.cpu().numpy().astype(np.float64)
+    pre, post, res, _ = M.mhc_maps(gX, W, Bv, 20, 1e-6)
+    ref = np.concatenate([pre, post, res.reshape(-1, 4)], 1)
+    err = float(np.abs(mo.cpu().numpy().astype(np.float64) - ref).max())
+    print(f"mhc C={Cn}: maps max |diff| {err:.2e}", flush=True)
+    assert err < 2e-6
+    u_ref = M.rmsnorm(pre[:, 0:1] * gX[:, 0] + pre[:, 1:2] * gX[:, 1], np.ones(Cn), 1e-6)
+    assert np.all(np.abs(_bf16(u) - u_ref) <= 2.0 ** -6 * np.abs(u_ref) + 1e-3)
