@@ -28,7 +28,7 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 
 # HBM traffic of the dominant kernel per launch, from two rocprofv3 --pmc runs
-# of `bench.py --profile-dominant` (FETCH_SIZE, then WRITE_SIZE, KiB per
+# of `bench.py --profile dominant` (FETCH_SIZE, then WRITE_SIZE, KiB per
 # dispatch), each scaled by the same counter's reading for a plain 1 GiB
 # device copy in that run.  Valid only for the kernel source it was taken on:
 # the hash of k_gemm.hip + common.h must match, else traffic is reported null.
