@@ -653,7 +653,16 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, int
       g.kcache = st->base + st->koff[ex.slot] + kv_skip;
       g.vcache = st->base + st->voff[ex.slot] + kv_skip;
       g.S_call = S; g.pos0 = pos0; g.S_max = st->S_max; g.pos_dev = pos_dev; g.pages = pages;
-      LAUNCH(run_gemm(g), "qkv gemm");
+      if (pages.table && dt == lk::DT_BF16 && T > 64) {
+        // the 256-row tile GEMM stores contiguous caches only: plain rows, then the pages
+        g.epi = lk::EPI_STORE;
+        LAUNCH(run_gemm(g), "qkv gemm");
+        LAUNCH(lk::kv_scatter(dt, qkv, qkv_rows, Hq * d, B, S, pos0, pos_dev, Hkv, d, g.kcache, g.vcache, st->S_max,
+                              pages, s),
+               "kv scatter");
+      } else {
+        LAUNCH(run_gemm(g), "qkv gemm");
+      }
       lk::AttnArgs a{};
       a.dt = dt; a.B = B; a.S_call = S; a.pos0 = pos0; a.S_max = st->S_max; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
       a.pos_dev = pos_dev; a.pages = pages;

@@ -10,10 +10,13 @@
 //   computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16), which leaves
 //   each lane with one query column; the probabilities feed O^T = V^T P^T
 //   directly from registers.  Online softmax in fp32 (base 2).
-// * attn_decode_mfma (bf16, d = 128, up to 16 query columns = heads x new
-//   tokens): eight waves per (split, KV head, sequence), splits only as many
-//   as needed to fill the device, v_mfma_f32_16x16x32_bf16, operands read
-//   straight from the cache; a combine kernel when there are several splits.
+// * attn_prefill_d256 (bf16, d = 256, Hq / Hkv in 1, 2, 4): the same scheme
+//   with four waves (one per SIMD), two-stage K and V^T rings.
+// * attn_decode_mfma<D> (bf16, d = 128 or 256, up to 16 query columns =
+//   heads x new tokens): eight waves per (split, KV head, sequence), splits
+//   only as many as needed to fill the device, v_mfma_f32_16x16x32_bf16,
+//   operands read straight from the cache; a combine kernel when there are
+//   several splits.
 // * attn_f32: plain kernel for the fp32 configuration.
 #include "common.h"
 #include "kernels.h"
@@ -292,17 +295,316 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ prefill, bf16, d = 256
+// Four waves per workgroup, one per SIMD: wave w serves query head kvh*G + w % G
+// for the query sub-block w / G (32 queries), so one K / V^T tile of 64 keys
+// serves 32 * 4 / G queries of each of the G heads (G in 1, 2, 4).  At d = 256
+// a wave's O (32 queries x 256) takes 128 accumulators and its Q fragments 64
+// registers: that fits only with a SIMD's whole register file, so there is no
+// second wave on the SIMD to fill the vector ALU while the matrix core runs.
+// Instead the wave itself overlaps them: the score MFMAs of tile kt + 1 are
+// issued before the softmax of tile kt.  K and V^T live in separate rings of
+// two 32 KB stages each (K of tiles kt + 1 and kt + 2, V^T of tiles kt and
+// kt + 1), so the loads of one tile have a whole tile's work to land in.
+// LDS layouts (16-byte units, swizzled against the 64 banks):
+//   K   [64 keys][256 d]:  unit c (0..31) of row r at c ^ (r & 15)
+//   V^T [256 d][64 keys]:  as for d = 128
+// Scores use the same key permutation as the d = 128 kernel, and the score
+// contraction runs as two 128-deep halves with their own accumulators (four
+// independent chains per tile), summed before the softmax.
+constexpr int PD2 = 256;
+constexpr int A2_NW = 4;
+constexpr int A2_KST = PK * PD2;                // elements per K stage (32 KB)
+constexpr int A2_LDS = 4 * A2_KST * 2;          // two K stages + two V^T stages: 128 KB
+
+DEV int kq2_sw(int r, int c) { return r * PD2 + ((c ^ (r & 15)) << 3); }
+
+__global__ __launch_bounds__(64 * A2_NW, 1) void attn_prefill_d256(AttnArgs a) {
+  constexpr int NW = A2_NW;
+  constexpr int NB = 32 / NW;                  // DMA blocks of 1 KB per wave per operand and tile
+  extern __shared__ __align__(16) bf16_t smem[];
+  bf16_t* kring = smem;                        // [2][64][256]
+  bf16_t* vring = smem + 2 * A2_KST;           // [2][256][64]
+  const int G = a.Hq / a.Hkv;                  // 1, 2 or 4
+  const int QS = NW / G;                       // query sub-blocks per workgroup
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int qb = gridDim.x - 1 - blockIdx.x;   // long rows first
+  const int kvh = blockIdx.y, b = blockIdx.z;
+  const int j = kvh * G + wid % G;
+  const int q0 = qb * 32 * QS + (wid / G) * 32;
+  const int h = lane >> 5, col = lane & 31;
+  const int m = q0 + col;
+  const bool qvalid = m < a.S_call;
+  const int qpos = a.pos0 + m;
+  const int kv_end = a.pos0 + min((qb + 1) * 32 * QS, a.S_call);
+  const int ntiles = (kv_end + PK - 1) / PK;
+
+  const bool paged = a.pages.table != nullptr;
+  int* pglist = reinterpret_cast<int*>(smem + 4 * A2_KST);
+  if (paged) {
+    for (int t = tid; t < ntiles; t += 64 * NW) pglist[t] = kv_page(a.pages, b, t * PK);
+    __syncthreads();
+  }
+
+  const bf16_t* Q = (const bf16_t*)a.q + (size_t)(b * a.S_call + min(m, a.S_call - 1)) * a.ldq + j * PD2;
+  bf16x8_t qf[16];
+#pragma unroll
+  for (int ds = 0; ds < 16; ++ds) qf[ds] = as_bf16x8(ldv4(Q + ds * 16 + h * 8));
+  // Register classes: O (128) and Q (64) live in the accumulation registers
+  // (MFMA operands may come from there), leaving the vector registers to the
+  // scores, the fragments and the softmax.  Everything that touches O is an
+  // MFMA or the in-place rescale below, so the compiler keeps it there.
+#pragma unroll
+  for (int ds = 0; ds < 16; ++ds) asm volatile("" : "+a"(qf[ds]));
+
+  const bf16_t* Kg = (const bf16_t*)a.kcache + (paged ? 0 : ((size_t)(b * a.Hkv + kvh) * a.S_max) * PD2);
+  const bf16_t* Vg = (const bf16_t*)a.vcache + (paged ? 0 : ((size_t)(b * a.Hkv + kvh) * PD2) * a.S_max);
+  const int vstride = kv_vstride(a.pages, a.S_max);
+  // K: 32 blocks of 2 rows, V^T: 32 blocks of 8 rows; wave w issues blocks
+  // NB w .. NB w + NB - 1 of each.  Lane l writes LDS bytes 16 l .. of the
+  // block, so it fetches the global unit that the swizzle puts there.
+  const int kr_l = lane >> 5, ks_l = lane & 31, vr_l = lane >> 3, vs_l = lane & 7;
+  auto tile_src = [&](int tile, const bf16_t*& Kt, const bf16_t*& Vt) {
+    if (paged) {
+      const int pg = __builtin_amdgcn_readfirstlane(pglist[tile]);
+      Kt = Kg + (((size_t)pg * a.Hkv + kvh) * KV_PAGE) * PD2;
+      Vt = Vg + ((size_t)pg * a.Hkv + kvh) * PD2 * KV_PAGE;
+    } else {
+      Kt = Kg + (size_t)tile * PK * PD2;
+      Vt = Vg + tile * PK;
+    }
+  };
+  auto issue_k = [&](int kt) {
+    const bf16_t *Kt, *Vt;
+    tile_src(min(kt, ntiles - 1), Kt, Vt);
+    bf16_t* st = kring + (kt & 1) * A2_KST;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int blk = NB * wid + i;
+      const int kr = 2 * blk + kr_l;
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(Kt + kr * PD2 + ((ks_l ^ (kr & 15)) << 3)),
+          (void __attribute__((address_space(3)))*)(st + blk * 512), 16, 0, 0);
+    }
+  };
+  auto issue_v = [&](int kt) {
+    const bf16_t *Kt, *Vt;
+    tile_src(min(kt, ntiles - 1), Kt, Vt);
+    bf16_t* st = vring + (kt & 1) * A2_KST;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int blk = NB * wid + i;
+      const int vr = 8 * blk + vr_l;
+      __builtin_amdgcn_global_load_lds(
+          (const void __attribute__((address_space(1)))*)(Vt + (size_t)vr * vstride + ((vs_l ^ ((vr >> 1) & 7)) << 3)),
+          (void __attribute__((address_space(3)))*)(st + blk * 512), 16, 0, 0);
+    }
+  };
+  auto sync = [&]() {
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+
+  f32x16_t o[8];
+#pragma unroll
+  for (int db = 0; db < 8; ++db)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+#pragma unroll
+  for (int db = 0; db < 8; ++db) asm volatile("" : "+a"(o[db]));
+  float mrun = -INFINITY, lrun = 0.f;
+  const float sc = LOG2E / sqrtf((float)PD2);
+  const int krow = (col & 0x13) | ((col & 4) << 1) | ((col & 8) >> 1);
+
+  // LDS read addresses: only the swizzled part depends on the lane; the key
+  // block, the d half, the O block and the stage are constant offsets, which
+  // the reads take as immediates.  K unit 2 ds + h (+ 16 for the upper d half)
+  // of row r = 32 c + krow sits at unit (2 ds + h) ^ (krow & 15); V^T unit
+  // 2 mm + h of row 32 db + col at (2 mm + h) ^ ((col >> 1) & 7).
+  const int kx = krow & 15, vy = (col >> 1) & 7;
+  int kofs[8], vofs[4];
+#pragma unroll
+  for (int ds = 0; ds < 8; ++ds) kofs[ds] = krow * PD2 + (((2 * ds + h) ^ kx) << 3);
+#pragma unroll
+  for (int mm = 0; mm < 4; ++mm) vofs[mm] = col * PK + (((2 * mm + h) ^ vy) << 3);
+
+  f32x16_t sa[2], sb[2];
+  auto scores = [&](int kstage, f32x16_t (&st)[2]) {
+    const bf16_t* ks = kring + kstage * A2_KST;
+    f32x16_t lo[2], hi[2];
+#pragma unroll
+    for (int ds = 0; ds < 8; ++ds) {
+      const bf16_t* kp = ks + kofs[ds];
+      bf16x8_t kf[2][2];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        kf[c][0] = as_bf16x8(ldv4(kp + c * 32 * PD2));
+        kf[c][1] = as_bf16x8(ldv4(kp + c * 32 * PD2 + 128));
+      }
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        lo[c] = mfma32(kf[c][0], qf[ds], ds == 0 ? f32x16_t{} : lo[c]);
+        hi[c] = mfma32(kf[c][1], qf[8 + ds], ds == 0 ? f32x16_t{} : hi[c]);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // bounded register use: one step's fragments at a time
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) st[c] = lo[c] + hi[c];
+  };
+  auto softmax_pv = [&](int kt, int vstage, f32x16_t (&st)[2]) {
+    const bf16_t* vs = vring + vstage * A2_KST;
+    const bool diag = kt * PK + PK - 1 > a.pos0 + q0;
+    float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (diag) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = kt * PK + c * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
+          const float v = (key <= qpos && key < kv_end) ? st[c][r] : -INFINITY;
+          st[c][r] = v;
+          tm[r & 3] = fmaxf(tm[r & 3], v);
+        }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tm[r & 3] = fmaxf(tm[r & 3], st[c][r]);
+    }
+    float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+    tmax = x32_max(tmax) * sc;
+    // lazy rescaling, as in the d = 128 kernel
+    const float mnew = tmax > mrun + 8.f ? tmax : mrun;
+    const float mfin = (mnew == -INFINITY) ? 0.f : mnew;
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = exp2_hw(fmaf(st[c][r], sc, -mfin));
+        st[c][r] = p;
+        ps[r & 3] += p;
+      }
+    const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    if (__any(mnew > mrun)) {
+      const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(mrun - mnew);
+      lrun *= alpha;
+      // O scaled in place in the accumulation registers (a copy through the
+      // vector registers would make the compiler keep O there, at 128
+      // registers and two copies per tile).  The last MFMA writing O was
+      // issued a whole tile of work earlier; the nops cover the read-after-
+      // MFMA, read -> VALU and write -> MFMA source wait states all the same.
+      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float t;
+          asm volatile(
+              "v_accvgpr_read_b32 %1, %0\n\t"
+              "s_nop 1\n\t"
+              "v_mul_f32 %1, %1, %2\n\t"
+              "v_accvgpr_write_b32 %0, %1\n\t"
+              "s_nop 3"
+              : "+a"(o[db][r]), "=&v"(t)
+              : "v"(alpha));
+        }
+    }
+    lrun += psum;
+    mrun = mnew;
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const int c = mm >> 1, half = mm & 1;
+      uint32_t pw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(st[c][half * 8 + 2 * e], st[c][half * 8 + 2 * e + 1]);
+      const bf16x8_t pf = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
+      const bf16_t* vp = vs + vofs[mm];
+#pragma unroll
+      for (int db = 0; db < 8; ++db) {
+        const bf16x8_t vf = as_bf16x8(ldv4(vp + db * 32 * PK));
+        o[db] = mfma32(vf, pf, o[db]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // keys kv_end .. of the last tile hold arbitrary bits: clear V^T there
+  auto mask_tail = [&]() {
+    const int kt = ntiles - 1;
+    bf16_t* vs = vring + (kt & 1) * A2_KST;
+    const int lim = kv_end - kt * PK;
+    for (int idx = tid; idx < PD2 * 8; idx += 64 * NW) {
+      const int r = idx >> 3, u = idx & 7;
+      if (8 * u + 8 > lim) {
+        bf16_t* p = vs + vq_sw(r, u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (8 * u + e >= lim) p[e] = 0;
+      }
+    }
+  };
+  const bool ragged = kv_end % PK != 0;
+  // prologue: K of tiles 0 and 1, V^T of tile 0; scores of tile 0
+  issue_k(0);
+  if (ntiles > 1) issue_k(1);
+  issue_v(0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  sync();
+  scores(0, sa);
+  // step kt: K of tile kt + 1 and V^T of tile kt are in LDS; K of tile kt + 2
+  // and V^T of tile kt + 1 go into the stages that tiles kt and kt - 1 used
+  // (every wave is past them at the barrier)
+  // (par = kt & 1, a constant in each unrolled half, so stage offsets are immediates)
+  auto step = [&](int kt, int par, f32x16_t (&cur)[2], f32x16_t (&nxt)[2]) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    sync();
+    if (kt + 2 < ntiles) issue_k(kt + 2);
+    if (kt + 1 < ntiles) issue_v(kt + 1);
+    if (kt == ntiles - 1 && ragged) {
+      mask_tail();
+      __syncthreads();
+    }
+    // no branches around these (a branch would make O a merged value, which
+    // the compiler keeps in vector registers): past the last tile the scores
+    // read a stale stage and go unused; a tile past the wave's last query is
+    // masked out whole, so its probabilities are 0
+    scores(par ^ 1, nxt);
+    softmax_pv(kt, par, cur);
+  };
+  for (int kt = 0; kt < ntiles; kt += 2) {
+    step(kt, 0, sa, sb);
+    if (kt + 1 >= ntiles) break;
+    step(kt + 1, 1, sb, sa);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
+  if (qvalid) {
+    const float ltot = x32_sum(lrun);
+    const float inv = 1.0f / ltot;
+    bf16_t* O = (bf16_t*)a.out + (size_t)(b * a.S_call + m) * a.ldo + j * PD2;
+#pragma unroll
+    for (int db = 0; db < 8; ++db)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + g4 * 8 + h * 4;
+        const uint32_t w0 = pack_bf16x2(o[db][g4 * 4] * inv, o[db][g4 * 4 + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(o[db][g4 * 4 + 2] * inv, o[db][g4 * 4 + 3] * inv);
+        *(u32x2_t*)(O + d0) = u32x2_t{w0, w1};
+      }
+  }
+}
+
 // ------------------------------------------------------------------ decode, bf16
-// One workgroup of DW waves per (split, KV head, sequence); wave w takes the
-// 64-key rounds w, w + DW, ... of the split, so the waves stream neighbouring
-// cache lines together.  Query columns c < ncol are (token t = c / G, head
-// kvh*G + c % G).  A round loads its K rows and its V^T columns at once
-// (32 KB per wave in flight), then computes four S^T blocks of 16 keys whose
-// rows are ordered so that, for PV step kk, lane group g holds the
-// probabilities of keys 32kk + 8g + 0..7, matching a contiguous 16-byte read
-// of V^T.  The waves' (max, sum, O) are merged in LDS by a fixed tree
-// (w + 4 into w, then w + 2, then w + 1).  A single split writes the output;
-// several splits write fp32 partials for attn_combine.
+// One workgroup of DW waves (d = 128; DW / 2 at d = 256) per (split, KV head,
+// sequence); wave w takes the rounds w, w + DW, ... of the split (64 keys at
+// d = 128, 32 at d = 256), so the waves stream neighbouring cache lines
+// together.  Query columns c < ncol are (token t = c / G, head kvh*G + c % G).
+// A round loads its K rows and its V^T columns at once (32 KB per wave in
+// flight), then computes S^T blocks of 16 keys whose rows are ordered so
+// that, for PV step kk, lane group g holds the probabilities of keys
+// 32kk + 8g + 0..7, matching a contiguous 16-byte read of V^T.  The waves'
+// (max, sum, O) are merged in LDS by a fixed tree (w + 4 into w, then w + 2,
+// then w + 1).  A single split writes the output; several splits write fp32
+// partials for attn_combine.
 constexpr int DW = 8;
 
 DecodePlan decode_plan(int B, int Hkv, int kv_len, int cu) {
@@ -325,8 +627,21 @@ int decode_max_splits(int B, int Hkv, int S_max, int cu) {
   return want < 1 ? 1 : (want < cap ? want : cap);
 }
 
-__global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
-  __shared__ float mrg[DW / 2][16][PD + 2];   // o[0..127], max, sum per column
+// d = 128 takes rounds of 64 keys, d = 256 rounds of 32 keys (the same
+// registers per round: K rows and V^T columns of a round in flight at once).
+template <int D>
+constexpr int decode_waves() { return D == 128 ? DW : DW / 2; }
+
+template <int D>
+__global__ __launch_bounds__(64 * decode_waves<D>()) void attn_decode_mfma(AttnArgs a) {
+  constexpr int NWV = decode_waves<D>();    // waves: four at d = 256, each with a whole SIMD's registers
+  constexpr int RK = D == 128 ? 64 : 32;     // keys per round
+  constexpr int NSB = RK / 16;               // S^T blocks of 16 keys
+  constexpr int NKK = RK / 32;               // PV steps of 32 keys
+  constexpr int NQ = D / 32;                 // 32-deep q fragments
+  constexpr int NO = D / 16;                 // O blocks of 16 rows
+  constexpr int NCH = NQ > 4 ? 2 : 1;        // independent score chains per block
+  extern __shared__ float mrg[];             // [NWV / 2][16][D + 2]: o, max, sum per column
   const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
   const int ncol = G * a.S_call;
@@ -339,57 +654,66 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
   const int k_begin = s * a.split_len;
   const int k_end = min(k_begin + a.split_len, kv_len);
 
-  const bf16_t* Q = (const bf16_t*)a.q + (size_t)(b * a.S_call + tq) * a.ldq + jq * PD;
-  bf16x8_t qf[4];
+  const bf16_t* Q = (const bf16_t*)a.q + (size_t)(b * a.S_call + tq) * a.ldq + jq * D;
+  bf16x8_t qf[NQ];
   const u32x4_t zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int ds = 0; ds < 4; ++ds) qf[ds] = as_bf16x8(cvalid ? ldv4(Q + ds * 32 + g * 8) : zero);
+  for (int ds = 0; ds < NQ; ++ds) qf[ds] = as_bf16x8(cvalid ? ldv4(Q + ds * 32 + g * 8) : zero);
 
   const bool paged = a.pages.table != nullptr;
-  const bf16_t* Kg = (const bf16_t*)a.kcache + (paged ? 0 : ((size_t)(b * a.Hkv + kvh) * a.S_max) * PD);
-  const bf16_t* Vg = (const bf16_t*)a.vcache + (paged ? 0 : ((size_t)(b * a.Hkv + kvh) * PD) * a.S_max);
+  const bf16_t* Kg = (const bf16_t*)a.kcache + (paged ? 0 : ((size_t)(b * a.Hkv + kvh) * a.S_max) * D);
+  const bf16_t* Vg = (const bf16_t*)a.vcache + (paged ? 0 : ((size_t)(b * a.Hkv + kvh) * D) * a.S_max);
   const int vstride = kv_vstride(a.pages, a.S_max);
-  const float sc = LOG2E / sqrtf((float)PD);
+  const float sc = LOG2E / sqrtf((float)D);
 
-  f32x4_t o[8];
+  f32x4_t o[NO];
 #pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int db = 0; db < NO; ++db) o[db] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float mrun = -INFINITY, lrun = 0.f;
 
-  // a round is 64 keys starting at a multiple of 64: one page of a paged
-  // cache, whose number is read one round ahead
-  int pg = (paged && k_begin + wid * 64 < k_end) ? kv_page(a.pages, b, k_begin + wid * 64) : 0;
-  for (int k0 = k_begin + wid * 64; k0 < k_end; k0 += DW * 64) {
-    const int pg_next = (paged && k0 + DW * 64 < k_end) ? kv_page(a.pages, b, k0 + DW * 64) : 0;
-    const bf16_t* Kround = paged ? Kg + (((size_t)pg * a.Hkv + kvh) * KV_PAGE) * PD : Kg + (size_t)k0 * PD;
-    const bf16_t* Vround = paged ? Vg + ((size_t)pg * a.Hkv + kvh) * PD * KV_PAGE : Vg + k0;
+  // rounds start at multiples of RK (k_begin is a multiple of 64), so a round
+  // lies in one page of a paged cache; its page number is read one round ahead
+  int pg = (paged && k_begin + wid * RK < k_end) ? kv_page(a.pages, b, k_begin + wid * RK) : 0;
+  for (int k0 = k_begin + wid * RK; k0 < k_end; k0 += NWV * RK) {
+    const int pg_next = (paged && k0 + NWV * RK < k_end) ? kv_page(a.pages, b, k0 + NWV * RK) : 0;
+    const int in_pg = k0 & (KV_PAGE - 1);
+    const bf16_t* Kround = paged ? Kg + (((size_t)pg * a.Hkv + kvh) * KV_PAGE + in_pg) * D : Kg + (size_t)k0 * D;
+    const bf16_t* Vround = paged ? Vg + ((size_t)pg * a.Hkv + kvh) * D * KV_PAGE + in_pg : Vg + k0;
     pg = pg_next;
     // loads of the whole round first: K rows (S^T operand) and V^T (PV operand).
     // Keys past k_end stay inside the slot or page (S_max % 64 == 0) and are masked.
-    u32x4_t kf[4][4], vf[2][8];
+    u32x4_t kf[NSB][NQ], vf[NKK][NO];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
+    for (int sb = 0; sb < NSB; ++sb) {
       const int key = 32 * (sb >> 1) + (c >> 2) * 8 + (sb & 1) * 4 + (c & 3);   // within the round
-      const bf16_t* kr = Kround + (size_t)key * PD + g * 8;
+      const bf16_t* kr = Kround + (size_t)key * D + g * 8;
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) kf[sb][ds] = ldv4(kr + ds * 32);
+      for (int ds = 0; ds < NQ; ++ds) kf[sb][ds] = ldv4(kr + ds * 32);
     }
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < NKK; ++kk)
 #pragma unroll
-      for (int db = 0; db < 8; ++db) vf[kk][db] = ldv4(Vround + (size_t)(db * 16 + c) * vstride + 32 * kk + 8 * g);
+      for (int db = 0; db < NO; ++db) vf[kk][db] = ldv4(Vround + (size_t)(db * 16 + c) * vstride + 32 * kk + 8 * g);
 
-    f32x4_t st[4];
+    f32x4_t st[NSB];
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb) {
-      st[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int sb = 0; sb < NSB; ++sb) {
+      f32x4_t part[NCH];
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) st[sb] = mfma16(as_bf16x8(kf[sb][ds]), qf[ds], st[sb]);
+      for (int ch = 0; ch < NCH; ++ch) {
+        part[ch] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = ch * NQ / NCH; ds < (ch + 1) * NQ / NCH; ++ds)
+          part[ch] = mfma16(as_bf16x8(kf[sb][ds]), qf[ds], part[ch]);
+      }
+      st[sb] = part[0];
+#pragma unroll
+      for (int ch = 1; ch < NCH; ++ch) st[sb] += part[ch];
     }
     // st[sb][i]: column c, key k0 + 32*(sb/2) + 8g + 4*(sb%2) + i
     float tmax = -INFINITY;
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb)
+    for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int key = k0 + 32 * (sb >> 1) + 8 * g + 4 * (sb & 1) + i;
@@ -402,7 +726,7 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
     const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(mrun - mnew);
     float psum = 0.f;
 #pragma unroll
-    for (int sb = 0; sb < 4; ++sb)
+    for (int sb = 0; sb < NSB; ++sb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = (mnew == -INFINITY) ? 0.f : exp2_hw(st[sb][i] - mnew);
@@ -412,9 +736,9 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
     lrun = lrun * alpha + psum;
     mrun = mnew;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) o[db] *= alpha;
+    for (int db = 0; db < NO; ++db) o[db] *= alpha;
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < NKK; ++kk) {
       uint32_t pw[4];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
@@ -426,7 +750,7 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
       const bf16x8_t pf = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
       const int key0 = k0 + 32 * kk + 8 * g;
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
+      for (int db = 0; db < NO; ++db) {
         u32x4_t v = vf[kk][db];
         if (key0 + 8 > k_end) {
 #pragma unroll
@@ -440,25 +764,25 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
   // full row sum of a column (its four lane groups)
   float ltot = x32_sum(x16_sum(lrun));
 
-  // merge waves: step h = 4, 2, 1: waves [h, 2h) hand their state to w - h
-  for (int h = DW / 2; h >= 1; h >>= 1) {
+  // merge waves: step h = NWV / 2, ..., 1: waves [h, 2h) hand their state to w - h
+  for (int h = NWV / 2; h >= 1; h >>= 1) {
     if (wid >= h && wid < 2 * h) {
-      float* slot = &mrg[wid - h][c][0];
+      float* slot = mrg + ((size_t)(wid - h) * 16 + c) * (D + 2);
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+      for (int db = 0; db < NO; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) slot[db * 16 + g * 4 + i] = o[db][i];
-      if (g == 0) { slot[PD] = mrun; slot[PD + 1] = ltot; }
+      if (g == 0) { slot[D] = mrun; slot[D + 1] = ltot; }
     }
     __syncthreads();
     if (wid < h) {
-      const float* slot = &mrg[wid][c][0];
-      const float m2 = slot[PD], l2 = slot[PD + 1];
+      const float* slot = mrg + ((size_t)wid * 16 + c) * (D + 2);
+      const float m2 = slot[D], l2 = slot[D + 1];
       const float M = fmaxf(mrun, m2);
       const float a1 = (mrun == -INFINITY) ? 0.f : exp2_hw(mrun - M);
       const float a2 = (m2 == -INFINITY) ? 0.f : exp2_hw(m2 - M);
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+      for (int db = 0; db < NO; ++db)
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[db][i] = o[db][i] * a1 + slot[db * 16 + g * 4 + i] * a2;
       ltot = ltot * a1 + l2 * a2;
@@ -469,21 +793,24 @@ __global__ __launch_bounds__(64 * DW) void attn_decode_mfma(AttnArgs a) {
   if (wid != 0 || !cvalid) return;
   if (a.n_split == 1) {
     const float inv = 1.f / ltot;
-    bf16_t* O = (bf16_t*)a.out + (size_t)(b * a.S_call + tq) * a.ldo + jq * PD;
+    bf16_t* O = (bf16_t*)a.out + (size_t)(b * a.S_call + tq) * a.ldo + jq * D;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
+    for (int db = 0; db < NO; ++db) {
       const uint32_t w0 = pack_bf16x2(o[db][0] * inv, o[db][1] * inv);
       const uint32_t w1 = pack_bf16x2(o[db][2] * inv, o[db][3] * inv);
       *(u32x2_t*)(O + db * 16 + g * 4) = u32x2_t{w0, w1};
     }
     return;
   }
-  float* P = a.part + ((((size_t)(b * a.S_call + tq) * a.Hq + jq) * a.n_split) + s) * (PD + 2);
+  float* P = a.part + ((((size_t)(b * a.S_call + tq) * a.Hq + jq) * a.n_split) + s) * (D + 2);
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < NO; ++db)
     *(float4*)(P + db * 16 + g * 4) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
-  if (g == 0) { P[PD] = mrun; P[PD + 1] = ltot; }
+  if (g == 0) { P[D] = mrun; P[D + 1] = ltot; }
 }
+
+template <int D>
+constexpr size_t decode_lds() { return (size_t)(decode_waves<D>() / 2) * 16 * (D + 2) * sizeof(float); }
 
 // out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
 template <typename T>
@@ -555,11 +882,26 @@ hipError_t attn_prefill(const AttnArgs& a, hipStream_t s) {
   if (a.dt == DT_F32) return launch_f32(a, s);
   if (a.pos_dev) return hipErrorInvalidValue;   // one start position per call
   const int G = a.Hq / a.Hkv;
-  if (a.d != PD || a.Hq % a.Hkv || !(G == 1 || G == 2 || G == 4 || G == 8) || a.S_max % 64)
-    return hipErrorInvalidValue;
+  if (a.Hq % a.Hkv || a.S_max % 64) return hipErrorInvalidValue;
   // a paged cache keeps the page numbers of the workgroup's tiles in LDS past the ring
   const long tiles = ((long)a.pos0 + a.S_call + PK - 1) / PK;
-  const size_t lds = AQ_LDS + (a.pages.table ? (size_t)tiles * sizeof(int) : 0);
+  const size_t pgl = a.pages.table ? (size_t)tiles * sizeof(int) : 0;
+  if (a.d == PD2) {
+    if (!(G == 1 || G == 2 || G == 4) || A2_LDS + pgl > AQ_LDS_MAX) return hipErrorInvalidValue;
+    static bool attr2 = false;
+    if (!attr2) {
+      hipError_t e = hipFuncSetAttribute((const void*)attn_prefill_d256, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                         AQ_LDS_MAX);
+      if (e != hipSuccess) return e;
+      attr2 = true;
+    }
+    const int qpw = 32 * (A2_NW / G);
+    dim3 grid((a.S_call + qpw - 1) / qpw, a.Hkv, a.B);
+    attn_prefill_d256<<<grid, 64 * A2_NW, A2_LDS + pgl, s>>>(a);
+    return hipGetLastError();
+  }
+  if (a.d != PD || !(G == 1 || G == 2 || G == 4 || G == 8)) return hipErrorInvalidValue;
+  const size_t lds = AQ_LDS + pgl;
   if (lds > AQ_LDS_MAX) return hipErrorInvalidValue;
   static bool attr = false;
   if (!attr) {
@@ -578,11 +920,23 @@ hipError_t attn_decode(const AttnArgs& a, hipStream_t s) {
   if (a.S_call <= 0 || a.B <= 0) return hipSuccess;
   if (a.dt == DT_F32) return launch_f32(a, s);
   const int G = a.Hq / a.Hkv;
-  if (a.d != PD || a.Hq % a.Hkv || G * a.S_call > 16 || a.S_max % 64 || a.split_len % 64) return hipErrorInvalidValue;
+  if ((a.d != PD && a.d != PD2) || a.Hq % a.Hkv || G * a.S_call > 16 || a.S_max % 64 || a.split_len % 64)
+    return hipErrorInvalidValue;
   const int kv_len = a.pos0 + a.S_call;
   if ((long)a.n_split * a.split_len < kv_len) return hipErrorInvalidValue;
   dim3 grid(a.n_split, a.Hkv, a.B);
-  attn_decode_mfma<<<grid, 64 * DW, 0, s>>>(a);
+  if (a.d == 128) {
+    attn_decode_mfma<128><<<grid, 64 * decode_waves<128>(), decode_lds<128>(), s>>>(a);
+  } else {
+    static bool attr = false;
+    if (!attr) {
+      hipError_t e = hipFuncSetAttribute((const void*)attn_decode_mfma<256>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)decode_lds<256>());
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    attn_decode_mfma<256><<<grid, 64 * decode_waves<256>(), decode_lds<256>(), s>>>(a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   attn_combine<bf16_t><<<a.B * a.S_call * a.Hq, 128, 0, s>>>(a);
@@ -619,6 +973,59 @@ hipError_t kv_append(int dt, const void* qkv, long ld, int q_cols, int B, int Hk
   else
     kv_append_kernel<float><<<grid, 256, 0, s>>>((const float*)qkv, ld, q_cols, B, Hkv, d, (float*)kcache,
                                                  (float*)vcache, S_max, pos, pages);
+  return hipGetLastError();
+}
+
+// One workgroup per (64-position block, KV head, sequence): K rows go
+// straight to the cache; V goes through LDS so that V^T is written as runs of
+// consecutive positions.  Only positions pos0 .. pos0 + S - 1 are written (a
+// continued chunk shares its first block with earlier positions).  With
+// per-sequence start positions (pos_dev, clamped to [0, pos0]) S must be 1.
+template <typename T>
+__global__ __launch_bounds__(256) void kv_scatter_kernel(const T* __restrict__ qkv, long ld, int q_cols, int S,
+                                                         int pos0, const int* __restrict__ pos_dev, int Hkv, int d,
+                                                         T* __restrict__ kc, T* __restrict__ vc, int S_max,
+                                                         KvPages pages) {
+  extern __shared__ __align__(16) unsigned char kvs_raw[];
+  T* vl = reinterpret_cast<T*>(kvs_raw);        // [64][d + 1]
+  const int dp = d + 1;
+  const int hk = blockIdx.y, b = blockIdx.z;
+  const int ps = pos_dev ? min(max(pos_dev[b], 0), pos0) : pos0;   // this sequence's first position
+  const int p0 = (ps & ~(KV_PAGE - 1)) + KV_PAGE * blockIdx.x;
+  const int lo = max(p0, ps), hi = min(p0 + KV_PAGE, ps + S);
+  for (int idx = threadIdx.x; idx < KV_PAGE * d; idx += 256) {
+    const int r = idx / d, dd = idx - r * d;
+    const int pos = p0 + r;
+    if (pos >= lo && pos < hi) {
+      const T* row = qkv + (size_t)(b * S + pos - ps) * ld + q_cols;
+      kc[kv_k_off(pages, Hkv, S_max, d, b, hk, pos) + dd] = row[hk * d + dd];
+      vl[r * dp + dd] = row[Hkv * d + hk * d + dd];
+    }
+  }
+  __syncthreads();
+  const int vstride = kv_vstride(pages, S_max);
+  for (int idx = threadIdx.x; idx < KV_PAGE * d; idx += 256) {
+    const int dd = idx / KV_PAGE, r = idx - dd * KV_PAGE;
+    const int pos = p0 + r;
+    if (pos >= lo && pos < hi) vc[kv_v_off(pages, Hkv, S_max, d, b, hk, pos) + (size_t)dd * vstride] = vl[r * dp + dd];
+  }
+}
+
+hipError_t kv_scatter(int dt, const void* qkv, long ld, int q_cols, int B, int S, int pos0, const int* pos_dev,
+                      int Hkv, int d, void* kcache, void* vcache, int S_max, KvPages pages, hipStream_t s) {
+  if (B <= 0 || S <= 0) return hipSuccess;
+  if (pos_dev && S != 1) return hipErrorInvalidValue;
+  const int blocks = (pos0 + S + KV_PAGE - 1) / KV_PAGE - pos0 / KV_PAGE;
+  const dim3 grid(blocks, Hkv, B);
+  const size_t es = dt == DT_BF16 ? 2 : 4;
+  const size_t lds = (size_t)KV_PAGE * (d + 1) * es;
+  if (lds > 64 * 1024) return hipErrorInvalidValue;
+  if (dt == DT_BF16)
+    kv_scatter_kernel<bf16_t><<<grid, 256, lds, s>>>((const bf16_t*)qkv, ld, q_cols, S, pos0, pos_dev, Hkv, d,
+                                                     (bf16_t*)kcache, (bf16_t*)vcache, S_max, pages);
+  else
+    kv_scatter_kernel<float><<<grid, 256, lds, s>>>((const float*)qkv, ld, q_cols, S, pos0, pos_dev, Hkv, d, (float*)kcache,
+                                                    (float*)vcache, S_max, pages);
   return hipGetLastError();
 }
 

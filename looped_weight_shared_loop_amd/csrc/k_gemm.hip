@@ -23,7 +23,10 @@
 namespace lk {
 
 // ------------------------------------------------------------------ epilogue
-template <typename T>
+// PG: the cache may be paged.  The 256-row tile kernels take contiguous caches
+// only (page addressing there costs the k loop registers); the host stores
+// their QKV rows plainly and scatters K / V into the pages (kv_scatter).
+template <typename T, bool PG>
 DEV void epi_qkv(const GemmArgs& a, int row, int col, float v) {
   if (col < a.q_cols) {
     st1((T*)a.C + (size_t)row * a.ldc + col, v);
@@ -35,20 +38,23 @@ DEV void epi_qkv(const GemmArgs& a, int row, int col, float v) {
   const int pos = (a.pos_dev ? min(max(a.pos_dev[b], 0), a.pos0) : a.pos0) + row % a.S_call;
   if (cc < kvn) {
     const int hk = cc / a.head_dim, dd = cc % a.head_dim;
-    st1((T*)a.kcache + kv_k_off(a.pages, a.n_kv, a.S_max, a.head_dim, b, hk, pos) + dd, v);
+    if (PG) st1((T*)a.kcache + kv_k_off(a.pages, a.n_kv, a.S_max, a.head_dim, b, hk, pos) + dd, v);
+    else st1((T*)a.kcache + (((size_t)b * a.n_kv + hk) * a.S_max + pos) * a.head_dim + dd, v);
   } else {
     cc -= kvn;
     const int hk = cc / a.head_dim, dd = cc % a.head_dim;
-    st1((T*)a.vcache + kv_v_off(a.pages, a.n_kv, a.S_max, a.head_dim, b, hk, pos) +
-            (size_t)dd * kv_vstride(a.pages, a.S_max), v);
+    if (PG)
+      st1((T*)a.vcache + kv_v_off(a.pages, a.n_kv, a.S_max, a.head_dim, b, hk, pos) +
+              (size_t)dd * kv_vstride(a.pages, a.S_max), v);
+    else st1((T*)a.vcache + (((size_t)b * a.n_kv + hk) * a.head_dim + dd) * a.S_max + pos, v);
   }
 }
 
-template <typename T, int EPI>
+template <typename T, int EPI, bool PG = true>
 DEV void epi_one(const GemmArgs& a, int row, int col, float v) {
   if (EPI == EPI_STORE) st1((T*)a.C + (size_t)row * a.ldc + col, v);
   else if (EPI == EPI_F32) ((float*)a.C)[(size_t)row * a.ldc + col] = v;
-  else if (EPI == EPI_QKV) epi_qkv<T>(a, row, col, v);
+  else if (EPI == EPI_QKV) epi_qkv<T, PG>(a, row, col, v);
 }
 
 // ------------------------------------------------------------------ MFMA tile kernel
@@ -240,7 +246,7 @@ __global__ __launch_bounds__(128 * WN_, 1) void gemm_dma_kernel(GemmArgs a) {
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wm * 128 + ib * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
           const int col = n0 + wn * WCOL + jb * 32 + (lane & 31);
-          if (row < a.M) epi_one<bf16_t, EPI>(a, row, col, acc[ib][jb][r]);
+          if (row < a.M) epi_one<bf16_t, EPI, false>(a, row, col, acc[ib][jb][r]);
         }
   }
 }
@@ -491,7 +497,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
     // plain row-major block, stored like the q tiles
     int ksq = -1;
     if (EPI == EPI_QKV && n0 >= a.q_cols && n0 + TBN <= a.q_cols + a.n_kv * a.head_dim && a.head_dim == WCOL &&
-        !a.pos_dev && !a.pages.table && m0 / a.S_call == (min(m0 + TBM, a.M) - 1) / a.S_call)
+        !a.pos_dev && m0 / a.S_call == (min(m0 + TBM, a.M) - 1) / a.S_call)
       ksq = m0 / a.S_call;
     if (EPI == EPI_SWIGLU || EPI == EPI_STORE || EPI == EPI_F32 || n0 + TBN <= a.q_cols || ksq >= 0) {
       constexpr int ES = EPI == EPI_F32 ? 4 : 2;      // output element bytes
@@ -534,8 +540,8 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
       // they go out as one 8-byte store (same sequence and 4-aligned positions
       // when S_call and pos0 are multiples of 4)
       const int kvn = a.n_kv * a.head_dim;
-      const bool vtile = EPI == EPI_QKV && n0 >= a.q_cols + kvn && !a.pos_dev && !a.pages.table &&
-                         a.S_call % 4 == 0 && a.pos0 % 4 == 0 && (a.head_dim & 31) == 0;
+      const bool vtile = EPI == EPI_QKV && n0 >= a.q_cols + kvn && !a.pos_dev && a.S_call % 4 == 0 &&
+                         a.pos0 % 4 == 0 && (a.head_dim & 31) == 0;
       if (vtile) {
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib)
@@ -556,7 +562,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                   if (row + e < a.M)
-                    epi_one<bf16_t, EPI>(a, row + e, n0 + wn * WCOL + jb * 32 + lcol, acc[ib][jb][g * 4 + e]);
+                    epi_one<bf16_t, EPI, false>(a, row + e, n0 + wn * WCOL + jb * 32 + lcol, acc[ib][jb][g * 4 + e]);
               }
             }
           }
@@ -569,7 +575,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
             for (int r = 0; r < 16; ++r) {
               const int row = m0 + lrow + ib * 32 + (r >> 2) * 8 + (r & 3);
               const int col = n0 + wn * WCOL + jb * 32 + lcol;
-              if (row < a.M) epi_one<bf16_t, EPI>(a, row, col, acc[ib][jb][r]);
+              if (row < a.M) epi_one<bf16_t, EPI, false>(a, row, col, acc[ib][jb][r]);
             }
       }
     }
@@ -909,7 +915,7 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
     if (a.ksplit > 1 && !a.part) return hipErrorInvalidValue;
     return a.M > 32 ? launch_skinny_rs<EPI, 2>(a, s) : launch_skinny_rs<EPI, 1>(a, s);
   }
-  if (a.K % DBK) return hipErrorInvalidValue;
+  if (a.K % DBK || (EPI == EPI_QKV && a.pages.table)) return hipErrorInvalidValue;
   if ((long)TBM * a.lda >= (1L << 31) || (long)(EPI == EPI_SWIGLU ? 2 * a.F : a.N) * a.ldb >= (1L << 31) ||
       (long)TBM * a.ldc * 4 >= (1L << 31))
     return hipErrorInvalidValue;

@@ -142,6 +142,10 @@ hipError_t attn_decode(const AttnArgs& a, hipStream_t s);
 // cache slot at position pos (one new position per sequence).
 hipError_t kv_append(int dt, const void* qkv, long ld, int q_cols, int B, int Hkv, int d, void* kcache,
                      void* vcache, int S_max, int pos, KvPages pages, hipStream_t s);
+// K and V of S rows per sequence (positions pos0 ..) from plainly stored
+// q|k|v rows into a cache slot (paged or contiguous), V transposed.
+hipError_t kv_scatter(int dt, const void* qkv, long ld, int q_cols, int B, int S, int pos0, const int* pos_dev,
+                      int Hkv, int d, void* kcache, void* vcache, int S_max, KvPages pages, hipStream_t s);
 // Decode split of the cache: as few splits as fill `cu` workgroups over the
 // B * Hkv (sequence, KV head) pairs, each a multiple of 64 keys.
 struct DecodePlan { int split_len, n_split; };
