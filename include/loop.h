@@ -88,8 +88,8 @@ typedef struct loop_config {
   int hidden;          /* C; a multiple of 8, at most 4096 */
   int ffn;             /* F (SwiGLU width) */
   int n_heads;         /* Hq query heads */
-  int n_kv_heads;      /* Hkv KV heads; Hq % Hkv == 0, Hq / Hkv <= 8 (bf16: 1, 2, 4 or 8) */
-  int head_dim;        /* d: 64 or 128 (bf16 needs 128) */
+  int n_kv_heads;      /* Hkv KV heads; Hq % Hkv == 0, Hq / Hkv <= 8 (bf16: 1, 2, 4 or 8; 1, 2, 4 at d 256) */
+  int head_dim;        /* d: float32 64 or 128; bf16 128 or 256 */
   int n_layers;        /* stored layers */
   int loop_start;      /* first looped layer */
   int loop_end;        /* one past the last looped layer */

@@ -66,12 +66,15 @@ int loop_op_mhc(int dtype, int mode, int T, int C, int sinkhorn_iters, float eps
  * pos0+S-1) of B sequences over a cache slot: K [B][Hkv][S_max][d],
  * V^T [B][Hkv][d][S_max] holding positions 0 .. pos0+S-1.  q: token (b, s) at
  * q + (b*S + s)*ldq, head j at + j*d; out likewise with ldo.  Query head j
- * reads KV head j / (Hq / Hkv); scale 1/sqrt(d).  bf16 needs d == 128,
- * Hq / Hkv in {1, 2, 4, 8} and S_max % 64 == 0. */
+ * reads KV head j / (Hq / Hkv); scale 1/sqrt(d).  bf16 needs d == 128 with
+ * Hq / Hkv in {1, 2, 4, 8}, or d == 256 with Hq / Hkv in {1, 2, 4} (the 16
+ * query / 4 KV heads of 256 in "How Does SenseNova-Loop Get More Depth Without
+ * More Parameters?", section on the hybrid attention pattern), and
+ * S_max % 64 == 0. */
 int loop_op_attention(int dtype, int B, int S, int pos0, int S_max, int Hq, int Hkv, int d, const void* q, long ldq,
                       const void* kcache, const void* vcache, void* out, long ldo, void* stream);
 
-/* The decode form: same contract, for Hq / Hkv * S <= 16.  The cache is split
+/* The decode form: same contract (bf16: d 128 or 256), for Hq / Hkv * S <= 16.  The cache is split
  * over workgroups only as far as needed to fill the device (none at B * Hkv >=
  * the CU count); several splits are merged by a second kernel through
  * `scratch` (caller-owned, loop_op_attention_decode_bytes() bytes, an upper
@@ -96,7 +99,8 @@ int loop_op_attention_decode_ragged(int dtype, int B, int S, const int32_t* pos_
  * float32 state S [B][Hkv][d][d], z [B][Hkv][d] (ignored and treated as zero
  * when init_zero), which is replaced by the state after the last position.
  * chunked = 1: chunk-parallel form (needs scratch of loop_op_linear_bytes());
- * chunked = 0: the recurrence, one position after another. */
+ * chunked = 0: the recurrence, one position after another.  d: 64 or 128
+ * (float32), 64, 128 or 256 (bf16). */
 size_t loop_op_linear_bytes(int B, int S, int Hkv, int d);
 int loop_op_linear(int dtype, int chunked, int B, int S, int Hq, int Hkv, int d, float eps, const void* qkv, long ld,
                    float* S_state, float* z_state, int init_zero, void* out, long ldo, void* scratch,

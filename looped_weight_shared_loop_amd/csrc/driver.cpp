@@ -227,12 +227,12 @@ int loop_model_create(const loop_config* cfg, const loop_weights* w, loop_model*
   if (c.n_heads % c.n_kv_heads || c.n_heads / c.n_kv_heads > 8)
     return lp_fail(LOOP_ERR_SHAPE, "n_heads must be a multiple of n_kv_heads, at most 8 per group");
   if (c.hidden % 8 || c.hidden > 4096) return lp_fail(LOOP_ERR_SHAPE, "hidden must be a multiple of 8, <= 4096");
-  if (c.head_dim != 64 && c.head_dim != 128) return lp_fail(LOOP_ERR_SHAPE, "head_dim must be 64 or 128");
   const int qkv_rows = (c.n_heads + 2 * c.n_kv_heads) * c.head_dim;
   if (c.dtype == LOOP_BF16) {
-    if (c.head_dim != 128) return lp_fail(LOOP_ERR_SHAPE, "bf16 needs head_dim 128");
+    if (c.head_dim != 128 && c.head_dim != 256) return lp_fail(LOOP_ERR_SHAPE, "bf16 needs head_dim 128 or 256");
     const int G = c.n_heads / c.n_kv_heads;
-    if (G != 1 && G != 2 && G != 4 && G != 8) return lp_fail(LOOP_ERR_SHAPE, "bf16 needs n_heads / n_kv_heads in 1, 2, 4, 8");
+    if (G != 1 && G != 2 && G != 4 && (G != 8 || c.head_dim != 128))
+      return lp_fail(LOOP_ERR_SHAPE, "bf16 needs n_heads / n_kv_heads in 1, 2, 4 (or 8 with head_dim 128)");
     if (c.hidden % 256 || qkv_rows % 256 || c.vocab % 256 || (c.n_heads * c.head_dim) % 128 || c.ffn % 128)
       return lp_fail(LOOP_ERR_SHAPE, "bf16 GEMM tiles need hidden, qkv rows, vocab %% 256 == 0 and ffn %% 128 == 0");
     // The bf16 GEMM tiles address a weight matrix and 256 rows of an operand
@@ -244,6 +244,7 @@ int loop_model_create(const loop_config* cfg, const loop_weights* w, loop_model*
         256L * std::max(F, Q) >= lim || 256L * c.vocab * 4 >= lim)
       return lp_fail(LOOP_ERR_SHAPE, "bf16 weight matrices need fewer than 2^31 elements and vocab < 2^21");
   } else {
+    if (c.head_dim != 64 && c.head_dim != 128) return lp_fail(LOOP_ERR_SHAPE, "fp32 needs head_dim 64 or 128");
     if (c.ffn % 8 || (c.n_heads * c.head_dim) % 8) return lp_fail(LOOP_ERR_SHAPE, "fp32 widths must be multiples of 8");
   }
   int ndev = 0;

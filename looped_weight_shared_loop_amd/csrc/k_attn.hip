@@ -812,23 +812,28 @@ __global__ __launch_bounds__(64 * decode_waves<D>()) void attn_decode_mfma(AttnA
 template <int D>
 constexpr size_t decode_lds() { return (size_t)(decode_waves<D>() / 2) * 16 * (D + 2) * sizeof(float); }
 
-// out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M)
+// out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M); thread t takes the
+// dimensions t, t + 128, ... of one (token, head) row
 template <typename T>
 __global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
   const int row = blockIdx.x;                   // (b * S_call + t) * Hq + j
-  const int dd = threadIdx.x;
   const float* P = a.part + (size_t)row * a.n_split * (a.d + 2);
   float M = -INFINITY;
   for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, P[s * (a.d + 2) + a.d]);
-  float L = 0.f, acc = 0.f;
+  float L = 0.f;
   for (int s = 0; s < a.n_split; ++s) {
     const float ms = P[s * (a.d + 2) + a.d];
-    const float w = (ms == -INFINITY) ? 0.f : exp2_hw(ms - M);
-    L += P[s * (a.d + 2) + a.d + 1] * w;
-    if (dd < a.d) acc += P[s * (a.d + 2) + dd] * w;
+    L += P[s * (a.d + 2) + a.d + 1] * ((ms == -INFINITY) ? 0.f : exp2_hw(ms - M));
   }
   const int tok = row / a.Hq, j = row % a.Hq;
-  if (dd < a.d) st1((T*)a.out + (size_t)tok * a.ldo + j * a.d + dd, acc / L);
+  for (int dd = threadIdx.x; dd < a.d; dd += 128) {
+    float acc = 0.f;
+    for (int s = 0; s < a.n_split; ++s) {
+      const float ms = P[s * (a.d + 2) + a.d];
+      acc += P[s * (a.d + 2) + dd] * ((ms == -INFINITY) ? 0.f : exp2_hw(ms - M));
+    }
+    st1((T*)a.out + (size_t)tok * a.ldo + j * a.d + dd, acc / L);
+  }
 }
 
 // ------------------------------------------------------------------ fp32

@@ -6,6 +6,8 @@ nothing here touches the GPU library.  Run from the repository root:
     python tests/golden/make_golden.py loop9b   # ~6 min, ~30 GB of host memory
     python tests/golden/make_golden.py group    # ~5 min
 
+    python tests/golden/make_golden.py group256 # ~2 min
+
 loop9b -> tests/golden/loop9b_logits.npz
     The full Loop-9B shape (32 stored layers, block [4, 28) run twice: 56
     layer executions; vocabulary 248,320; pages: "SenseTime's Loop-9B runs its
@@ -27,6 +29,12 @@ group -> tests/golden/group9b_hidden.npz
     as float32.  Also how far the rounded oracle moves when one input element
     is moved by one bf16 ulp, at eight sites spread over positions and
     channels (max-row and row-RMS relative change per site).
+
+group256 -> tests/golden/group9b_d256_hidden.npz
+    The same group with the attention heads as one page gives them, 16 query
+    and 4 KV heads of 256 ("How Does SenseNova-Loop Get More Depth Without
+    More Parameters?", section on the hybrid attention pattern; the projection
+    sizes equal those of 32 / 8 heads of 128): rounded and unrounded results.
 """
 from __future__ import annotations
 
@@ -90,9 +98,10 @@ def make_loop9b():
                         meta=np.array(json.dumps(meta)))
 
 
-def make_group():
-    cfg = oracle.group_config()
-    cfg_exact = oracle.group_config(round_storage=False)
+def make_group(heads=None):
+    kw = dict(n_heads=heads[0], n_kv_heads=heads[1], head_dim=heads[2]) if heads else {}
+    cfg = oracle.group_config(**kw)
+    cfg_exact = oracle.group_config(round_storage=False, **kw)
     W = M.make_weights(cfg, 0, cache_layers=4)
     emb = synth.normal_bf16_as_f32(1, synth.TID_EMBEDS_IN, (1, GROUP_S, cfg.hidden))
     t0 = time.time()
@@ -100,6 +109,16 @@ def make_group():
     exact = M.forward(cfg_exact, W, embeds=emb, hidden_out=True)
     print(f"group: {time.time() - t0:.0f} s", flush=True)
     assert np.array_equal(M.round_bf16(ref), ref)
+    bits = synth.f32_to_bf16_bits(ref.astype(np.float32))
+    if heads:
+        meta = dict(config=f"one 9B-width group [lin, lin, lin, full] looped twice, {heads[0]} q / {heads[1]} kv "
+                    f"heads of {heads[2]}, bf16, weights seed 0, inputs seed 1",
+                    S=GROUP_S, heads=list(heads), rounded_vs_unrounded_max_row=float(row_max_rel(ref, exact).max()),
+                    rounded_vs_unrounded_row_rms=float(row_rms_rel(ref, exact).mean()))
+        print(json.dumps(meta, indent=1), flush=True)
+        np.savez_compressed(os.path.join(HERE, f"group9b_d{heads[2]}_hidden.npz"), rounded_bf16_bits=bits,
+                            unrounded=exact.astype(np.float32), meta=np.array(json.dumps(meta)))
+        return
     sens = []
     for (t, c) in SENS_SITES:
         e2 = emb.copy()
@@ -114,7 +133,6 @@ def make_group():
                 S=GROUP_S, rounded_vs_unrounded_max_row=float(row_max_rel(ref, exact).max()),
                 rounded_vs_unrounded_row_rms=float(row_rms_rel(ref, exact).mean()), one_ulp_sensitivity=sens)
     print(json.dumps(meta, indent=1), flush=True)
-    bits = synth.f32_to_bf16_bits(ref.astype(np.float32))
     np.savez_compressed(os.path.join(HERE, "group9b_hidden.npz"), rounded_bf16_bits=bits,
                         unrounded=exact.astype(np.float32), meta=np.array(json.dumps(meta)))
 
@@ -122,4 +140,4 @@ def make_group():
 if __name__ == "__main__":
     which = sys.argv[1:] or ["group", "loop9b"]
     for w in which:
-        {"loop9b": make_loop9b, "group": make_group}[w]()
+        {"loop9b": make_loop9b, "group": make_group, "group256": lambda: make_group((16, 4, 256))}[w]()

@@ -67,9 +67,11 @@ def _create(cfg, n_layers=None):
     (dict(hidden=260), -2),
     (dict(hidden=8192), -2),
     (dict(head_dim=96), -2),
-    (dict(dtype="bf16"), -2),                 # bf16 needs head_dim 128
+    (dict(dtype="bf16"), -2),                 # bf16 needs head_dim 128 or 256
     (dict(dtype="bf16", head_dim=128, hidden=200), -2),
     (dict(dtype="bf16", head_dim=128, hidden=256, n_heads=6, n_kv_heads=2), -2),   # group of 3 heads
+    (dict(dtype="bf16", head_dim=256, hidden=256, n_heads=8, n_kv_heads=1), -2),   # 8 heads of 256 per group
+    (dict(head_dim=256), -2),                 # float32 needs head_dim 64 or 128
 ])
 def test_create_rejects_bad_configs(kw, code):
     from looped_weight_shared_loop_amd import LoopError

@@ -21,14 +21,14 @@ from gpu_common import need_gpu, torch
 
 pytestmark = pytest.mark.gpu
 
-D, HQ, HKV = 128, 8, 2
+HQ, HKV = 8, 2
 LOG2E = 1.4426950408889634
 # per-tile step of the score level, base 2 (the first tile sets the level)
 STEPS2 = [0.0, 7.0, 9.0, 7.5, 8.5, 30.0, -25.0, 7.2, 9.5, 2.0, 7.8, 8.4, 40.0, 0.5, 7.6, 9.2,
           8.0, 8.1, 7.9, 12.0, -3.0, 8.6, 7.4, 16.0]
 
 
-def _inputs(L, rng):
+def _inputs(L, rng, D):
     u = rng.standard_normal(D)
     u /= np.linalg.norm(u)
     level2 = np.cumsum(STEPS2)[np.arange(L) // 64] + rng.uniform(-0.3, 0.3, L)   # base 2
@@ -42,18 +42,19 @@ def _inputs(L, rng):
     return u, M.round_bf16(K), M.round_bf16(V)
 
 
+@pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("pos0,S", [(0, 1536), (600, 936)], ids=["from_zero", "continued_chunk"])
-def test_prefill_attention_rising_scores(pos0, S):
+def test_prefill_attention_rising_scores(pos0, S, D):
     L = need_gpu()
     from looped_weight_shared_loop_amd import _abi as A
     rng = np.random.default_rng(1234 + pos0)
     Lk = pos0 + S
     assert Lk <= 64 * len(STEPS2)
     Smax = (Lk + 63) // 64 * 64
-    u, K, V = _inputs(Lk, rng)
+    u, K, V = _inputs(Lk, rng, D)
     a = rng.uniform(0.85, 1.15, (S, HQ))
     q = M.round_bf16(a[:, :, None] * np.sqrt(D) * u[None, None, :] + 0.01 * rng.standard_normal((S, HQ, D)))
-    print(f"rising-score attention pos0={pos0} S={S}", flush=True)
+    print(f"rising-score attention d={D} pos0={pos0} S={S}", flush=True)
     kc = np.zeros((1, HKV, Smax, D), np.float32)
     vt = np.zeros((1, HKV, D, Smax), np.float32)
     kc[0, :, :Lk] = K

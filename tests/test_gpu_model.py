@@ -340,12 +340,15 @@ def test_ragged_batch_subset_decode_and_rules():
 
 
 # ------------------------------------------------------------------ bf16 (MFMA kernels)
-def test_mini_bf16_prefill_decode():
-    ocfg = mini_bf16_config()
+@pytest.mark.parametrize("heads", [None, (4, 1, 256)], ids=["4x128", "4x256"])
+def test_mini_bf16_prefill_decode(heads):
+    """bf16 kernels at the smallest width, heads of 128 (2 KV) or of 256 (one
+    KV head for four query heads, the group size of the 16 / 4 layout)."""
+    ocfg = mini_bf16_config(**(dict(n_heads=heads[0], n_kv_heads=heads[1], head_dim=heads[2]) if heads else {}))
     model, Wo = build_pair(ocfg)
     B, S, K = 2, 100, 3
     toks = tokens(B, S + K, ocfg.vocab, seed=5)
-    _say("mini bf16 B=2 S=100")
+    _say("mini bf16 B=2 S=100, heads", ocfg.n_heads, ocfg.n_kv_heads, ocfg.head_dim)
     ost = oracle.State()
     ref = oracle.forward(ocfg, Wo, toks[:, :S], state=ost, all_logits=True)
     st = model.new_state(B, 256)
@@ -427,20 +430,25 @@ def _derived_check(tag, got, rounded, exact):
     assert e_rms <= DERIVED_FACTOR * base_rms, (e_rms, base_rms)
 
 
-def test_group_9b_width_hidden_out():
-    """One [linear x3, full] group at hidden 4096 / FFN 12288 / 32q-8kv x 128,
+@pytest.mark.parametrize("layout", ["32x128", "16x256"])
+def test_group_9b_width_hidden_out(layout):
+    """One [linear x3, full] group at hidden 4096 / FFN 12288, heads 32q-8kv x
+    128 or 16q-4kv x 256 (the page's layout: "How Does SenseNova-Loop Get More
+    Depth Without More Parameters?", section on the hybrid attention pattern),
     looped twice under two-stream mHC (8 executions), inputs N(0, 1), S=200,
     against the stored oracle results at the derived bar."""
     L = need_gpu()
     import json
     from gpu_common import lib_config
-    g = np.load(os.path.join(GOLDEN, "group9b_hidden.npz"))
+    name, kw = {"32x128": ("group9b_hidden.npz", {}),
+                "16x256": ("group9b_d256_hidden.npz", dict(n_heads=16, n_kv_heads=4, head_dim=256))}[layout]
+    g = np.load(os.path.join(GOLDEN, name))
     rounded = synth.bf16_bits_to_f32(g["rounded_bf16_bits"]).astype(np.float64)
     exact = g["unrounded"].astype(np.float64)
     meta = json.loads(str(g["meta"]))
-    ocfg = oracle.group_config()
+    ocfg = oracle.group_config(**kw)
     S = meta["S"]
-    _say("group 9B width S=", S)
+    _say("group 9B width S=", S, "heads", layout)
     model = L.LoopModel(lib_config(ocfg), L.random_weights(lib_config(ocfg), 0))
     emb = synth.normal_bf16_as_f32(1, synth.TID_EMBEDS_IN, (1, S, ocfg.hidden))
     st = model.new_state(1, S)

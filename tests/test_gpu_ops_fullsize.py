@@ -25,6 +25,15 @@ C, F, V = 4096, 12288, 248320
 HQ, HKV, D = 32, 8, 128
 QKV = (HQ + 2 * HKV) * D
 SEED = 7
+# attention head layouts at 9B width: 32 query / 8 KV heads of 128, and the
+# 16 / 4 heads of 256 of "How Does SenseNova-Loop Get More Depth Without More
+# Parameters?" (section on the hybrid attention pattern); same projection sizes
+LAYOUTS = {"32x128": (32, 8, 128), "16x256": (16, 4, 256)}
+
+
+def _lay(layout):
+    hq, hkv, d = LAYOUTS[layout]
+    return hq, hkv, d, (hq + 2 * hkv) * d
 
 
 def _stream():
@@ -172,8 +181,10 @@ def test_mhc_isolated_full_size_sampled():
 
 
 # ------------------------------------------------------------------ attention
-def test_full_attention_prefill_full_size_sampled():
-    """One full-attention execution of the 32K prefill: B=1, S=32768, 32 q / 8 kv heads."""
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+def test_full_attention_prefill_full_size_sampled(layout):
+    """One full-attention execution of the 32K prefill: B=1, S=32768, 32 q / 8 kv heads of 128 or 16 / 4 of 256."""
+    HQ, HKV, D, QKV = _lay(layout)
     need_gpu()
     from looped_weight_shared_loop_amd import _abi as A
     S = 32768
@@ -188,6 +199,7 @@ def test_full_attention_prefill_full_size_sampled():
                         out.data_ptr(), HQ * D, _stream())
     torch.cuda.synchronize()
     for pos, head in [(0, 0), (31, 5), (4095, 13), (20000, 30), (S - 1, 31), (S - 1, 2)]:
+        head %= HQ
         kvh = head // (HQ // HKV)
         qr = synth.normal_bf16_as_f32(SEED, 31, (QKV,), start=pos * QKV)[head * D:(head + 1) * D]
         K = synth.normal_bf16_as_f32(SEED, 32, (pos + 1, D), start=(kvh * S) * D)
@@ -199,9 +211,11 @@ def test_full_attention_prefill_full_size_sampled():
         assert err < 2e-2
 
 
-def test_full_attention_chunk_continuation_sampled():
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+def test_full_attention_chunk_continuation_sampled(layout):
     """A prefill chunk that continues a long cache (chunked prefill): 700 new
     positions at pos0 = 30000 (not a tile multiple) over S_max = 30720, B=2."""
+    HQ, HKV, D, QKV = _lay(layout)
     need_gpu()
     from looped_weight_shared_loop_amd import _abi as A
     from synth import device as sd
@@ -222,6 +236,7 @@ def test_full_attention_chunk_continuation_sampled():
                         out.data_ptr(), HQ * D, _stream())
     torch.cuda.synchronize()
     for b, t, head in [(0, 0, 0), (0, 63, 7), (1, 64, 12), (1, 699, 31), (0, 350, 20)]:
+        head %= HQ
         kvh = head // (HQ // HKV)
         row = b * S + t
         qr = synth.normal_bf16_as_f32(SEED, 34, (QKV,), start=row * QKV)[head * D:(head + 1) * D]
@@ -240,8 +255,10 @@ def test_full_attention_chunk_continuation_sampled():
     (2, 5001, [(0, 0), (1, 13), (1, 31)]),                # several splits, ragged last split
     (1, 37, [(0, 0), (0, 30)]),                           # fewer keys than one round
 ])
-def test_decode_attention_full_size_sampled(B, ctx, samples):
-    """B sequences of ctx cached positions + 1 new, 8 KV heads of 128."""
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+def test_decode_attention_full_size_sampled(B, ctx, samples, layout):
+    """B sequences of ctx cached positions + 1 new, 8 KV heads of 128 or 4 of 256."""
+    HQ, HKV, D, QKV = _lay(layout)
     need_gpu()
     from looped_weight_shared_loop_amd import _abi as A
     from synth import device as sd
@@ -262,6 +279,7 @@ def test_decode_attention_full_size_sampled(B, ctx, samples):
                                vt.data_ptr(), out.data_ptr(), HQ * D, scr.data_ptr(), nb, _stream())
     torch.cuda.synchronize()
     for b, head in samples:
+        head %= HQ
         kvh = head // (HQ // HKV)
         qr = synth.normal_bf16_as_f32(SEED, 43, (QKV,), start=b * QKV)[head * D:(head + 1) * D]
         base = ((b * HKV + kvh) * L) * D
@@ -281,9 +299,11 @@ def test_decode_attention_full_size_sampled(B, ctx, samples):
     # two sequences: the short one has keys in the first of many splits only
     ([5000, 3], [(0, 0), (0, 22), (1, 0), (1, 31)]),
 ])
-def test_decode_attention_ragged_full_size_sampled(pos, samples):
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+def test_decode_attention_ragged_full_size_sampled(pos, samples, layout):
     """Sequence b attends to its own pos[b] + 1 keys; slots hold NaN past
     each sequence's keys, which the kernel must neither weigh nor multiply."""
+    HQ, HKV, D, QKV = _lay(layout)
     need_gpu()
     from looped_weight_shared_loop_amd import _abi as A
     from synth import device as sd
@@ -311,6 +331,7 @@ def test_decode_attention_ragged_full_size_sampled(pos, samples):
     torch.cuda.synchronize()
     assert torch.isfinite(out.float()).all().item()
     for b, head in samples:
+        head %= HQ
         kvh = head // (HQ // HKV)
         n = pos[b] + 1
         qr = synth.normal_bf16_as_f32(SEED, 53, (QKV,), start=b * QKV)[head * D:(head + 1) * D]
@@ -325,10 +346,12 @@ def test_decode_attention_ragged_full_size_sampled(pos, samples):
 
 
 # ------------------------------------------------------------------ linear attention
-def test_linear_attention_chunked_full_size_sampled():
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+def test_linear_attention_chunked_full_size_sampled(layout):
     """One linear-attention execution of the 32K prefill, fresh state: outputs
     of one KV group at sampled positions, and the final state of that group,
     against the oracle's recurrence."""
+    HQ, HKV, D, QKV = _lay(layout)
     need_gpu()
     from looped_weight_shared_loop_amd import _abi as A
     S = 32768
@@ -341,10 +364,11 @@ def test_linear_attention_chunked_full_size_sampled():
     A.loop_op_linear(A.LOOP_BF16, 1, 1, S, HQ, HKV, D, 1e-6, qkv.data_ptr(), QKV, St.data_ptr(), zt.data_ptr(), 1,
                      out.data_ptr(), HQ * D, scr.data_ptr(), nb, _stream())
     torch.cuda.synchronize()
-    kvh = 5
-    heads = list(range(kvh * 4, kvh * 4 + 4))
+    kvh = 5 % HKV
+    G = HQ // HKV
+    heads = list(range(kvh * G, kvh * G + G))
     rows = synth.normal_bf16_as_f32(SEED, 51, (S, QKV))
-    q = rows[:, [h * D + i for h in heads for i in range(D)]].reshape(1, S, 4, D)
+    q = rows[:, [h * D + i for h in heads for i in range(D)]].reshape(1, S, G, D)
     k = rows[:, (HQ + kvh) * D:(HQ + kvh + 1) * D].reshape(1, S, 1, D)
     v = rows[:, (HQ + HKV + kvh) * D:(HQ + HKV + kvh + 1) * D].reshape(1, S, 1, D)
     del rows
@@ -360,8 +384,10 @@ def test_linear_attention_chunked_full_size_sampled():
     assert np.abs(zt[kvh].cpu().numpy() - zf[0, 0]).max() <= 1e-4 * np.abs(zf[0, 0]).max()
 
 
-def test_linear_attention_decode_prefilled_state():
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+def test_linear_attention_decode_prefilled_state(layout):
     """B=32 decode with pre-filled states S ~ N(0, 1), z = |N(0, 1)| (all outputs)."""
+    HQ, HKV, D, QKV = _lay(layout)
     need_gpu()
     from looped_weight_shared_loop_amd import _abi as A
     B = 32

@@ -38,13 +38,15 @@ def assign_pages(state, lengths, seed):
     state.block_table.copy_(torch.from_numpy(table.astype(np.int32)))
 
 
-@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("dtype", ["fp32", "bf16", "bf16_d256"])
 def test_paged_ragged_prefill_decode_matches_contiguous(dtype):
     """Ragged rows (prefill subsets, a continued chunk), then decode steps, on a
     paged and on a contiguous state: equal logits; the fp32 case also against
-    the oracle."""
+    the oracle.  Prefills of more than 64 rows store plain QKV rows and
+    scatter K / V into the pages; shorter ones write the pages directly."""
     need_gpu()
-    ocfg = oracle.tiny_config(n_kv_heads=2) if dtype == "fp32" else mini_bf16_config()
+    ocfg = {"fp32": lambda: oracle.tiny_config(n_kv_heads=2), "bf16": mini_bf16_config,
+            "bf16_d256": lambda: mini_bf16_config(n_heads=4, n_kv_heads=1, head_dim=256)}[dtype]()
     model, Wo = build_pair(ocfg)
     lens, K = [70, 70, 133, 20], 3
     toks = tokens(4, max(lens) + K, ocfg.vocab, seed=81)
@@ -107,13 +109,16 @@ def test_paged_pipelined_decode_matches_contiguous():
 
 
 @pytest.mark.parametrize("S", [2900])
-def test_paged_9b_width_full_attention_prefill_and_decode(S):
-    """One looped full-attention layer at 9B width (32q / 8kv x 128) over 2,900
-    positions (46 pages per sequence, B=2): prefill through the fused QKV
-    epilogue and the DMA-fed prefill attention, then decode steps through the
-    decode attention, paged against contiguous, bit for bit; and the oracle."""
+@pytest.mark.parametrize("heads", [(32, 8, 128), (16, 4, 256)], ids=["32x128", "16x256"])
+def test_paged_9b_width_full_attention_prefill_and_decode(S, heads):
+    """One looped full-attention layer at 9B width (32q / 8kv x 128 or 16q /
+    4kv x 256) over 2,900 positions (46 pages per sequence, B=2): prefill
+    through the QKV projection, the page scatter and the DMA-fed prefill
+    attention, then decode steps through the decode attention, paged against
+    contiguous, bit for bit; and the oracle."""
     need_gpu()
-    ocfg = oracle.group_config(vocab=1024, n_layers=1, loop_start=0, loop_end=1, n_passes=1, attn_period=1)
+    ocfg = oracle.group_config(vocab=1024, n_layers=1, loop_start=0, loop_end=1, n_passes=1, attn_period=1,
+                               n_heads=heads[0], n_kv_heads=heads[1], head_dim=heads[2])
     model, Wo = build_pair(ocfg, cache_layers=4)
     B, K = 2, 3
     toks = tokens(B, S + K, ocfg.vocab, seed=85)
@@ -131,7 +136,7 @@ def test_paged_9b_width_full_attention_prefill_and_decode(S):
         assert np.array_equal(a, b)
     ref = oracle.forward(ocfg, Wo, toks[:1], all_logits=True)[0]     # sequence 0
     err = rel(outs["paged"][0][:1], ref[S - 1][None])
-    _say("paged 9B-width prefill rel err", err)
+    _say("paged 9B-width prefill rel err", heads, err)
     assert err < 2e-2
     for k in range(K):
         assert rel(outs["paged"][1 + k][:1], ref[S + k][None]) < 2e-2
