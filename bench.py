@@ -32,11 +32,15 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # dispatch), each scaled by the same counter's reading for a plain 1 GiB
 # device copy in that run.  Valid only for the kernel source it was taken on:
 # the hash of k_gemm.hip + common.h must match, else traffic is reported null.
-DOMINANT_COUNTERS = {"source_sha256_16": "101a8993efe0f4c4", "fetch_kib": 4930203.2, "write_kib": 807168.0,
-                     "copy_fetch_kib": 524315.6, "copy_write_kib": 1048576.0}
+DOMINANT_COUNTERS = {"source_sha256_16": "1b9ed5dc71955733", "fetch_kib": 4929590.5, "write_kib": 807168.0,
+                     "copy_fetch_kib": 524308.4, "copy_write_kib": 1048576.0}
 
 NINE_B = dict(vocab=248320, hidden=4096, ffn=12288, n_heads=32, n_kv_heads=8, head_dim=128,
               n_layers=32, loop_start=4, loop_end=28, n_passes=2, dtype="bf16")
+# the same model with the attention heads one page gives (16 query / 4 KV heads
+# of 256: "How Does SenseNova-Loop Get More Depth Without More Parameters?",
+# section on the hybrid attention pattern); equal projection sizes
+NINE_B_D256 = dict(NINE_B, n_heads=16, n_kv_heads=4, head_dim=256)
 
 
 def log(*a):
@@ -381,6 +385,30 @@ TINY = dict(vocab=512, hidden=256, ffn=768, n_heads=4, n_kv_heads=4, head_dim=64
             loop_end=6, n_passes=2, dtype="fp32")
 
 
+def time_d256(L, torch, args):
+    """The 9B shape with the page's head layout (16 query / 4 KV heads of 256):
+    prefill at the bench length and the B=32 decode step."""
+    cfg = L.ModelConfig(**NINE_B_D256)
+    log("generating random-init 9B-shape weights, 16 x 256 heads")
+    model = L.LoopModel(cfg, L.random_weights(cfg, 0))
+    torch.cuda.synchronize()
+    S = args.seq
+    ms = time_prefill(L, torch, model, S, 2, 1)
+    flops, _, attn_f, _ = prefill_flops(NINE_B_D256, S)
+    out = {"heads": "16 q / 4 kv x 256", "prefill_ms": round(ms, 3), "prefill_tokens_per_s": round(S / (ms / 1e3), 1),
+           "prefill_tflops": round(flops / (ms / 1e3) / 1e12, 1),
+           "prefill_mfma_frac": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    if not args.no_decode:
+        dms = time_decode(L, torch, model, args.decode_batch, args.decode_ctx, args.decode_steps, 3)
+        tot, _, _, _ = decode_bytes(NINE_B_D256, args.decode_batch, args.decode_ctx)
+        gbs = tot / (dms / 1e3) / 1e9
+        out.update({"decode_ms_per_step": round(dms, 3), "decode_tokens_per_s": round(args.decode_batch / (dms / 1e3), 1),
+                    "decode_algorithmic_gb_per_step": round(tot / 1e9, 2), "decode_hbm_frac": round(gbs / PEAK_HBM_GBS, 4)})
+    del model
+    torch.cuda.empty_cache()
+    return out
+
+
 def time_tiny(L, torch, S=128, iters=20):
     """The tiny looped decoder (8 stored layers, block [2, 6) twice: 12
     executions; fp32): latency of one B=1 prefill of S=128 tokens (last-row
@@ -463,7 +491,7 @@ def cpu_baseline(seq=128):
                      "oracle_s": round(tiny_s, 3), "tokens_per_s": round(128 / tiny_s, 1)}}
 
 
-PROFILE_MODES = ("dominant", "prefill", "decode", "mhc", "group", "long")
+PROFILE_MODES = ("dominant", "prefill", "decode", "mhc", "group", "long", "prefill_d256", "decode_d256")
 
 
 def profile_run(L, torch, args):
@@ -475,6 +503,7 @@ def profile_run(L, torch, args):
       mhc       the mHC site alone, 65,536 tokens, 3 launches
       group     one 9B-width group looped twice, S=8,192 (after one warm-up call)
       long      one chunked prefill of 262,144 positions (8 chunks of 32,768)
+      prefill_d256, decode_d256   prefill / decode with 16 query / 4 KV heads of 256
     Prints the step it is in before each one, so a profiled run shows progress."""
     src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")     # 1 GiB
     dst = torch.empty_like(src)
@@ -490,13 +519,13 @@ def profile_run(L, torch, args):
     elif mode == "group":
         time_group(L, torch, iters=1)
     else:
-        cfg = L.ModelConfig(**NINE_B)
+        cfg = L.ModelConfig(**(NINE_B_D256 if mode.endswith("_d256") else NINE_B))
         model = L.LoopModel(cfg, L.random_weights(cfg, 0))
         torch.cuda.synchronize()
         log(f"profile {mode}: weights ready")
-        if mode == "prefill":
+        if mode in ("prefill", "prefill_d256"):
             time_prefill(L, torch, model, args.seq, 1, 1)
-        elif mode == "decode":
+        elif mode in ("decode", "decode_d256"):
             time_decode(L, torch, model, args.decode_batch, args.decode_ctx, 1, 2)
         elif mode == "long":
             time_long_prefill(L, torch, model, args.long_seq, args.long_chunk)
@@ -526,7 +555,7 @@ def _kname(n):
     return n.replace("void ", "").strip()
 
 
-_ATTN_OR_LIN = ("attn_prefill_dma", "attn_decode_mfma", "attn_combine", "lin_out_bf", "lin_decode_kernel",
+_ATTN_OR_LIN = ("attn_prefill_dma", "attn_prefill_d256", "attn_decode_mfma", "attn_combine", "lin_out_bf", "lin_decode_kernel",
                 "lin_output", "attn_f32", "kv_append")
 
 
@@ -676,6 +705,7 @@ def main():
     ap.add_argument("--no-parts", action="store_true",
                     help="skip the mHC-isolated and one-group measurements")
     ap.add_argument("--cpu-seq", type=int, default=1536)
+    ap.add_argument("--no-d256", action="store_true", help="skip the 16 x 256 head layout")
     ap.add_argument("--profile-dominant", action="store_true",
                     help="only a 1 GiB device copy (counter scale reference) and 3 launches of the dominant kernel")
     ap.add_argument("--profile", choices=PROFILE_MODES, default=None,
@@ -788,6 +818,11 @@ def main():
                               "algorithmic_tflop": round(gf / 1e12, 2),
                               "tflops": round(gf / (gms / 1e3) / 1e12, 1),
                               "mfma_frac": round(gf / (gms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+    if not args.no_d256:
+        if "model" in locals():
+            del model
+        torch.cuda.empty_cache()
+        result["heads_16x256"] = time_d256(L, torch, args)
     if not args.no_parts:
         tp, td = time_tiny(L, torch)
         result["tiny"] = {"config": "tiny looped decoder (8 stored layers, block [2,6) x2 = 12 executions, fp32), "

@@ -429,24 +429,33 @@ __global__ __launch_bounds__(64 * A2_NW, 1) void attn_prefill_d256(AttnArgs a) {
   for (int mm = 0; mm < 4; ++mm) vofs[mm] = col * PK + (((2 * mm + h) ^ vy) << 3);
 
   f32x16_t sa[2], sb[2];
+  // With one wave per SIMD nothing else hides the LDS latency: the K
+  // fragments of step ds + 2 and the V^T fragments of step mm + 1 are read
+  // while the MFMAs of the current step run (scheduling walls keep that order).
   auto scores = [&](int kstage, f32x16_t (&st)[2]) {
     const bf16_t* ks = kring + kstage * A2_KST;
     f32x16_t lo[2], hi[2];
+    bf16x8_t kf[3][4];
+    auto ldk = [&](int ds, bf16x8_t (&f)[4]) {
+      const bf16_t* kp = ks + kofs[ds];
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        f[2 * c] = as_bf16x8(ldv4(kp + c * 32 * PD2));
+        f[2 * c + 1] = as_bf16x8(ldv4(kp + c * 32 * PD2 + 128));
+      }
+    };
+    ldk(0, kf[0]);
+    ldk(1, kf[1]);
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) {
-      const bf16_t* kp = ks + kofs[ds];
-      bf16x8_t kf[2][2];
+      if (ds + 2 < 8) ldk(ds + 2, kf[(ds + 2) % 3]);
+      const bf16x8_t(&f)[4] = kf[ds % 3];
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        kf[c][0] = as_bf16x8(ldv4(kp + c * 32 * PD2));
-        kf[c][1] = as_bf16x8(ldv4(kp + c * 32 * PD2 + 128));
+        lo[c] = mfma32(f[2 * c], qf[ds], ds == 0 ? f32x16_t{} : lo[c]);
+        hi[c] = mfma32(f[2 * c + 1], qf[8 + ds], ds == 0 ? f32x16_t{} : hi[c]);
       }
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        lo[c] = mfma32(kf[c][0], qf[ds], ds == 0 ? f32x16_t{} : lo[c]);
-        hi[c] = mfma32(kf[c][1], qf[8 + ds], ds == 0 ? f32x16_t{} : hi[c]);
-      }
-      __builtin_amdgcn_sched_barrier(0);   // bounded register use: one step's fragments at a time
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) st[c] = lo[c] + hi[c];
@@ -512,19 +521,23 @@ __global__ __launch_bounds__(64 * A2_NW, 1) void attn_prefill_d256(AttnArgs a) {
     }
     lrun += psum;
     mrun = mnew;
+    bf16x8_t vfr[2][8];
+    auto ldv = [&](int mm, bf16x8_t (&f)[8]) {
+      const bf16_t* vp = vs + vofs[mm];
+#pragma unroll
+      for (int db = 0; db < 8; ++db) f[db] = as_bf16x8(ldv4(vp + db * 32 * PK));
+    };
+    ldv(0, vfr[0]);
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
+      if (mm + 1 < 4) ldv(mm + 1, vfr[(mm + 1) & 1]);
       const int c = mm >> 1, half = mm & 1;
       uint32_t pw[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(st[c][half * 8 + 2 * e], st[c][half * 8 + 2 * e + 1]);
       const bf16x8_t pf = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
-      const bf16_t* vp = vs + vofs[mm];
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const bf16x8_t vf = as_bf16x8(ldv4(vp + db * 32 * PK));
-        o[db] = mfma32(vf, pf, o[db]);
-      }
+      for (int db = 0; db < 8; ++db) o[db] = mfma32(vfr[mm & 1][db], pf, o[db]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
