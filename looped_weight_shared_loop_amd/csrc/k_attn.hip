@@ -429,72 +429,109 @@ __global__ __launch_bounds__(64 * A2_NW, 1) void attn_prefill_d256(AttnArgs a) {
   for (int mm = 0; mm < 4; ++mm) vofs[mm] = col * PK + (((2 * mm + h) ^ vy) << 3);
 
   f32x16_t sa[2], sb[2];
-  // With one wave per SIMD nothing else hides the LDS latency: the K
-  // fragments of step ds + 2 and the V^T fragments of step mm + 1 are read
-  // while the MFMAs of the current step run (scheduling walls keep that order).
+  // With one wave per SIMD nothing else hides the LDS latency or fills the
+  // vector ALU while the matrix core runs, so the wave interleaves its own
+  // work: the K fragments of score step ds + 2 are read during step ds, and
+  // the softmax of tile kt runs in eight slices between the eight score steps
+  // of tile kt + 1 (scheduling walls keep each slice beside its MFMAs).
+  bf16x8_t kf[3][4];
+  auto ldk = [&](const bf16_t* ks, int ds, bf16x8_t (&f)[4]) {
+    const bf16_t* kp = ks + kofs[ds];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      f[2 * c] = as_bf16x8(ldv4(kp + c * 32 * PD2));
+      f[2 * c + 1] = as_bf16x8(ldv4(kp + c * 32 * PD2 + 128));
+    }
+  };
+  // one score step: MFMAs of chunk ds (and the reads of chunk ds + 2)
+  auto score_step = [&](const bf16_t* ks, int ds, f32x16_t (&lo)[2], f32x16_t (&hi)[2]) {
+    if (ds + 2 < 8) ldk(ks, ds + 2, kf[(ds + 2) % 3]);
+    const bf16x8_t(&f)[4] = kf[ds % 3];
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      lo[c] = mfma32(f[2 * c], qf[ds], ds == 0 ? f32x16_t{} : lo[c]);
+      hi[c] = mfma32(f[2 * c + 1], qf[8 + ds], ds == 0 ? f32x16_t{} : hi[c]);
+    }
+  };
   auto scores = [&](int kstage, f32x16_t (&st)[2]) {
     const bf16_t* ks = kring + kstage * A2_KST;
     f32x16_t lo[2], hi[2];
-    bf16x8_t kf[3][4];
-    auto ldk = [&](int ds, bf16x8_t (&f)[4]) {
-      const bf16_t* kp = ks + kofs[ds];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        f[2 * c] = as_bf16x8(ldv4(kp + c * 32 * PD2));
-        f[2 * c + 1] = as_bf16x8(ldv4(kp + c * 32 * PD2 + 128));
-      }
-    };
-    ldk(0, kf[0]);
-    ldk(1, kf[1]);
+    ldk(ks, 0, kf[0]);
+    ldk(ks, 1, kf[1]);
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) {
-      if (ds + 2 < 8) ldk(ds + 2, kf[(ds + 2) % 3]);
-      const bf16x8_t(&f)[4] = kf[ds % 3];
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        lo[c] = mfma32(f[2 * c], qf[ds], ds == 0 ? f32x16_t{} : lo[c]);
-        hi[c] = mfma32(f[2 * c + 1], qf[8 + ds], ds == 0 ? f32x16_t{} : hi[c]);
-      }
+      score_step(ks, ds, lo, hi);
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int c = 0; c < 2; ++c) st[c] = lo[c] + hi[c];
   };
-  auto softmax_pv = [&](int kt, int vstage, f32x16_t (&st)[2]) {
-    const bf16_t* vs = vring + vstage * A2_KST;
-    const bool diag = kt * PK + PK - 1 > a.pos0 + q0;
-    float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    if (diag) {
+  // the masked scores of a tile that reaches past the wave's first query
+  auto mask_diag = [&](int kt, f32x16_t (&st)[2]) {
+    if (kt * PK + PK - 1 > a.pos0 + q0) {
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = kt * PK + c * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
-          const float v = (key <= qpos && key < kv_end) ? st[c][r] : -INFINITY;
-          st[c][r] = v;
-          tm[r & 3] = fmaxf(tm[r & 3], v);
+          if (!(key <= qpos && key < kv_end)) st[c][r] = -INFINITY;
         }
-    } else {
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tm[r & 3] = fmaxf(tm[r & 3], st[c][r]);
     }
-    float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
-    tmax = x32_max(tmax) * sc;
-    // lazy rescaling, as in the d = 128 kernel
-    const float mnew = tmax > mrun + 8.f ? tmax : mrun;
-    const float mfin = (mnew == -INFINITY) ? 0.f : mnew;
+  };
+  // scores of the next tile (nxt) fused with the softmax of this one (cur):
+  // cur becomes its probabilities; returns the new running max and the sum
+  uint32_t pw[4][4];
+  auto scores_softmax = [&](int kstage, f32x16_t (&nxt)[2], f32x16_t (&cur)[2], float& mnew, float& psum) {
+    const bf16_t* ks = kring + kstage * A2_KST;
+    f32x16_t lo[2], hi[2];
+    ldk(ks, 0, kf[0]);
+    ldk(ks, 1, kf[1]);
+    float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    float mfin = 0.f;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int ds = 0; ds < 8; ++ds) {
+      score_step(ks, ds, lo, hi);
+      if (ds < 2) {                     // partial maxima of one 32-key block
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_hw(fmaf(st[c][r], sc, -mfin));
-        st[c][r] = p;
-        ps[r & 3] += p;
+        for (int r = 0; r < 16; ++r) tm[r & 3] = fmaxf(tm[r & 3], cur[ds][r]);
       }
-    const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+      if (ds == 1) {
+        float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+        tmax = x32_max(tmax) * sc;
+        // lazy rescaling, as in the d = 128 kernel
+        mnew = tmax > mrun + 8.f ? tmax : mrun;
+        mfin = (mnew == -INFINITY) ? 0.f : mnew;
+      }
+      if (ds >= 2 && ds < 6) {          // eight probabilities per step
+        const int c = (ds - 2) >> 1, r0 = ((ds - 2) & 1) * 8;
+#pragma unroll
+        for (int r = r0; r < r0 + 8; ++r) {
+          const float p = exp2_hw(fmaf(cur[c][r], sc, -mfin));
+          cur[c][r] = p;
+          ps[r & 3] += p;
+        }
+        // formed here, beside this step's MFMAs (the compiler would otherwise
+        // sink them to their uses after the rescale branch)
+        asm volatile("" : "+v"(ps[0]), "+v"(ps[1]), "+v"(ps[2]), "+v"(ps[3]));
+      }
+      if (ds >= 6) {                    // bf16 pairs for two PV steps
+#pragma unroll
+        for (int mm = 2 * (ds - 6); mm < 2 * (ds - 6) + 2; ++mm) {
+          const int c = mm >> 1, half = mm & 1;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) pw[mm][e] = pack_bf16x2(cur[c][half * 8 + 2 * e], cur[c][half * 8 + 2 * e + 1]);
+          asm volatile("" : "+v"(pw[mm][0]), "+v"(pw[mm][1]), "+v"(pw[mm][2]), "+v"(pw[mm][3]));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+#pragma unroll
+    for (int c = 0; c < 2; ++c) nxt[c] = lo[c] + hi[c];
+  };
+  auto rescale_pv = [&](int vstage, float mnew, float psum) {
+    const bf16_t* vs = vring + vstage * A2_KST;
     if (__any(mnew > mrun)) {
       const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(mrun - mnew);
       lrun *= alpha;
@@ -531,11 +568,7 @@ __global__ __launch_bounds__(64 * A2_NW, 1) void attn_prefill_d256(AttnArgs a) {
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) {
       if (mm + 1 < 4) ldv(mm + 1, vfr[(mm + 1) & 1]);
-      const int c = mm >> 1, half = mm & 1;
-      uint32_t pw[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(st[c][half * 8 + 2 * e], st[c][half * 8 + 2 * e + 1]);
-      const bf16x8_t pf = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
+      const bf16x8_t pf = as_bf16x8(u32x4_t{pw[mm][0], pw[mm][1], pw[mm][2], pw[mm][3]});
 #pragma unroll
       for (int db = 0; db < 8; ++db) o[db] = mfma32(vfr[mm & 1][db], pf, o[db]);
       __builtin_amdgcn_sched_barrier(0);
@@ -581,8 +614,10 @@ __global__ __launch_bounds__(64 * A2_NW, 1) void attn_prefill_d256(AttnArgs a) {
     // the compiler keeps in vector registers): past the last tile the scores
     // read a stale stage and go unused; a tile past the wave's last query is
     // masked out whole, so its probabilities are 0
-    scores(par ^ 1, nxt);
-    softmax_pv(kt, par, cur);
+    mask_diag(kt, cur);
+    float mnew, psum;
+    scores_softmax(par ^ 1, nxt, cur, mnew, psum);
+    rescale_pv(par, mnew, psum);
   };
   for (int kt = 0; kt < ntiles; kt += 2) {
     step(kt, 0, sa, sb);
