@@ -1,0 +1,225 @@
+"""Inputs the seeded draws of the other tests do not give.
+
+1. Integer-valued bf16 inputs.  Every product and every partial sum of the
+   bf16 matrix-core kernels is then an integer below 2^24, exact in float32
+   whatever the summation order, so the kernels must reproduce the integer
+   results exactly: the GEMM tiles, k steps and split-K partials bit for bit
+   (float32 output) or to the bf16 rounding of the exact value (bf16 output),
+   and the chunked linear attention's outgoing state (S, z) bit for bit (its
+   bf16 high / low operand split carries integers below 2^16 exactly).  These
+   pins sit far below the bf16 tolerance of the random-input tests.
+2. Gaussian tails (numpy normal draws, not the bounded Irwin-Hall sums):
+   attention scores with a standard deviation of 9 (tails past +-40), and mHC
+   projection logits with a standard deviation near 18, where the sigmoids
+   saturate and 20 Sinkhorn iterations are far from converged.
+
+Operations: the projections and linear attention of "How Does SenseNova-Loop
+Get More Depth Without More Parameters?" (section on the hybrid attention
+pattern); the mHC maps of the same page (section on two-stream mHC).
+"""
+import zlib
+
+import numpy as np
+import pytest
+
+from oracle import model as M
+from gpu_common import need_gpu, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(x, dtype=torch.bfloat16):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(dtype).cuda()
+
+
+# ------------------------------------------------------------------ GEMM, exact
+@pytest.mark.parametrize("name,Mr,N,K,epi,split", [
+    ("prefill_f32_rows1000", 1000, 768, 4096, 1, False),      # 256-row tiles, ragged last tile
+    ("prefill_bf16", 700, 1024, 4096, 0, False),
+    ("prefill_f32_k4064", 300, 512, 4064, 1, False),           # the 32-deep eight-wave kernel
+    ("decode_f32_split", 32, 1024, 4096, 1, True),            # split-K partials summed by the reduce kernel
+    ("decode_bf16_split_m7", 7, 2048, 12288, 0, True),
+    ("decode64_f32_split", 64, 1024, 4096, 1, True),          # two token blocks per weight read
+])
+def test_gemm_integer_inputs_exact(name, Mr, N, K, epi, split):
+    need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    print(f"exact gemm {name}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(name.encode()))
+    a = rng.integers(-3, 4, (Mr, K))
+    b = rng.integers(-3, 4, (N, K))
+    ref = (a @ b.T).astype(np.float64)                     # |entries| <= 9 K < 2^24: exact in float32
+    assert np.abs(ref).max() < 2 ** 24
+    ad, bd = _dev(a), _dev(b)
+    c = torch.empty(Mr, N, dtype=torch.float32 if epi == 1 else torch.bfloat16, device="cuda")
+    nbytes = A.loop_op_gemm_bytes(A.LOOP_BF16, epi, Mr, N, K, 0) if split else 0
+    if split:
+        assert nbytes > 0
+    scr = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+    A.loop_op_gemm(A.LOOP_BF16, epi, Mr, N, K, ad.data_ptr(), K, bd.data_ptr(), K, c.data_ptr(), N, 0, _stream(),
+                   scr.data_ptr() if nbytes else None, nbytes)
+    torch.cuda.synchronize()
+    got = c.float().cpu().numpy().astype(np.float64)
+    want = ref if epi == 1 else M.round_bf16(ref)
+    bad = int((got != want).sum())
+    print(f"  mismatches {bad} of {got.size}", flush=True)
+    assert bad == 0
+
+
+# ------------------------------------------------------------------ linear attention, exact state
+@pytest.mark.parametrize("Hq,Hkv,D,S", [(8, 2, 128, 2000), (4, 1, 256, 2000)], ids=["d128", "d256"])
+def test_linear_attention_integer_inputs_state_exact(Hq, Hkv, D, S):
+    """q, k in {0, 1, 2} (so phi = x + 1 in {1, 2, 3}, exact on both sides),
+    v in {-2 .. 2}; 2,000 positions (31 chunks and a ragged one) from a
+    state of small integers.  The outgoing S and z are integers below 2^16:
+    bit for bit.  The outputs are quotients of exact integers, rounded to
+    bf16 once: within one bf16 rounding of the float64 quotient."""
+    need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    print(f"exact linear attention d={D}", flush=True)
+    rng = np.random.default_rng(D)
+    QKV = (Hq + 2 * Hkv) * D
+    rows = np.empty((S, QKV))
+    rows[:, :(Hq + Hkv) * D] = rng.integers(0, 3, (S, (Hq + Hkv) * D))
+    rows[:, (Hq + Hkv) * D:] = rng.integers(-2, 3, (S, Hkv * D))
+    S0 = rng.integers(-4, 5, (Hkv, D, D)).astype(np.float64)
+    z0 = rng.integers(0, 5, (Hkv, D)).astype(np.float64)
+    qkv = _dev(rows)
+    St = _dev(S0, torch.float32)
+    zt = _dev(z0, torch.float32)
+    out = torch.empty(S, Hq * D, dtype=torch.bfloat16, device="cuda")
+    nb = A.loop_op_linear_bytes(1, S, Hkv, D)
+    scr = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    A.loop_op_linear(A.LOOP_BF16, 1, 1, S, Hq, Hkv, D, 1e-6, qkv.data_ptr(), QKV, St.data_ptr(), zt.data_ptr(), 0,
+                     out.data_ptr(), Hq * D, scr.data_ptr(), nb, _stream())
+    torch.cuda.synchronize()
+    q = rows[:, :Hq * D].reshape(1, S, Hq, D)
+    k = rows[:, Hq * D:(Hq + Hkv) * D].reshape(1, S, Hkv, D)
+    v = rows[:, (Hq + Hkv) * D:].reshape(1, S, Hkv, D)
+    o, Sf, zf = M.linear_attention(q, k, v, S0[None], z0[None], 1e-6)
+    assert np.abs(Sf).max() < 2 ** 16 and np.abs(zf).max() < 2 ** 16
+    assert np.array_equal(St.cpu().numpy().astype(np.float64), Sf[0])
+    assert np.array_equal(zt.cpu().numpy().astype(np.float64), zf[0])
+    got = out.float().cpu().numpy().astype(np.float64).reshape(S, Hq, D)
+    ref = o[0]
+    err = np.abs(got - ref) / np.maximum(np.abs(ref), 1e-30)
+    print(f"  output max rel {err.max():.2e}", flush=True)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+
+
+# ------------------------------------------------------------------ attention, Gaussian tails
+@pytest.mark.parametrize("Hq,Hkv,D", [(32, 8, 128), (16, 4, 256)], ids=["32x128", "16x256"])
+def test_attention_gaussian_tails(Hq, Hkv, D):
+    """q, k ~ 3 N(0, 1) (scores with standard deviation 9), v ~ N(0, 1):
+    prefill of 2,048 positions from 0, and decode of 4 sequences over 3,000
+    cached positions; sampled rows against the float64 softmax attention at
+    the bf16 bar (probabilities are rounded to bf16 before P V)."""
+    need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    print(f"gaussian-tail attention d={D}", flush=True)
+    rng = np.random.default_rng(11 + D)
+    G = Hq // Hkv
+    # prefill
+    S = 2048
+    q = M.round_bf16(3.0 * rng.standard_normal((S, Hq, D)))
+    K = M.round_bf16(3.0 * rng.standard_normal((Hkv, S, D)))
+    V = M.round_bf16(rng.standard_normal((Hkv, S, D)))
+    qd = _dev(q.reshape(S, Hq * D))
+    kd = _dev(K[None])
+    vd = _dev(V.transpose(0, 2, 1)[None])
+    out = torch.empty(S, Hq * D, dtype=torch.bfloat16, device="cuda")
+    A.loop_op_attention(A.LOOP_BF16, 1, S, 0, S, Hq, Hkv, D, qd.data_ptr(), Hq * D, kd.data_ptr(), vd.data_ptr(),
+                        out.data_ptr(), Hq * D, _stream())
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy().reshape(S, Hq, D)
+    worst = 0.0
+    for t in sorted(set([0, 1, 63, 64, 1000, S - 1] + list(rng.integers(0, S, 10)))):
+        for j in (0, G - 1, Hq - 1):
+            kv = j // G
+            ref = M.full_attention(q[t, j][None, None, None, :], K[kv][None, :, None, :], V[kv][None, :, None, :],
+                                   t)[0, 0, 0]
+            err = np.abs(got[t, j] - ref).max() / np.abs(ref).max()
+            worst = max(worst, err)
+            assert err < 2e-2, (t, j, err)
+    # decode: 4 sequences, 3,000 cached positions + 1 new
+    B, ctx = 4, 3000
+    Smax = (ctx + 1 + 63) // 64 * 64
+    Kc = M.round_bf16(3.0 * rng.standard_normal((B, Hkv, ctx + 1, D)))
+    Vc = M.round_bf16(rng.standard_normal((B, Hkv, ctx + 1, D)))
+    qn = M.round_bf16(3.0 * rng.standard_normal((B, Hq, D)))
+    kc = np.zeros((B, Hkv, Smax, D), np.float32)
+    vt = np.zeros((B, Hkv, D, Smax), np.float32)
+    kc[:, :, :ctx + 1] = Kc
+    vt[:, :, :, :ctx + 1] = Vc.transpose(0, 1, 3, 2)
+    kcd, vtd, qnd = _dev(kc), _dev(vt), _dev(qn.reshape(B, Hq * D))
+    outd = torch.empty(B, Hq * D, dtype=torch.bfloat16, device="cuda")
+    nb = A.loop_op_attention_decode_bytes(B, 1, Hq, D, Smax)
+    scr = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    A.loop_op_attention_decode(A.LOOP_BF16, B, 1, ctx, Smax, Hq, Hkv, D, qnd.data_ptr(), Hq * D, kcd.data_ptr(),
+                               vtd.data_ptr(), outd.data_ptr(), Hq * D, scr.data_ptr(), nb, _stream())
+    torch.cuda.synchronize()
+    gd = outd.float().cpu().numpy().reshape(B, Hq, D)
+    for b in range(B):
+        for j in (0, Hq // 2, Hq - 1):
+            kv = j // G
+            ref = M.full_attention(qn[b, j][None, None, None, :], Kc[b, kv][None, :, None, :],
+                                   Vc[b, kv][None, :, None, :], ctx)[0, 0, 0]
+            err = np.abs(gd[b, j] - ref).max() / np.abs(ref).max()
+            worst = max(worst, err)
+            assert err < 2e-2, (b, j, err)
+    print(f"  worst row error {worst:.2e}", flush=True)
+
+
+# ------------------------------------------------------------------ mHC, extreme logits
+@pytest.mark.parametrize("T", [512, 32], ids=["tiled", "decode_slices"])
+def test_mhc_extreme_logits(T):
+    """W ~ 0.2 N(0, 1) over 2C = 8,192 inputs: the 8 logits have a standard
+    deviation near 18, so the pre/post sigmoids saturate and the Sinkhorn
+    iterates of the 2x2 residual map are far from their limit after 20 steps.
+    Maps of the X' the kernel wrote, against the float64 definition, within
+    a bound from the arithmetic: the float32 projection of 8,192 exact
+    products (W in three bf16 parts on the tiled path, float32 on the decode
+    path) carries at most a few float32 ulps of sum |w x_hat| per logit, and
+    every map moves by at most that much per unit of logit error."""
+    need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    print(f"mhc extreme logits T={T}", flush=True)
+    C = 4096
+    rng = np.random.default_rng(T)
+    X = _dev(rng.standard_normal((T, 2, C)))
+    y = _dev(rng.standard_normal((T, C)))
+    maps_in = np.tile(np.array([0.5, 0.5, 1.0, 1.0, 0.5, 0.5, 0.5, 0.5], np.float32), (T, 1))
+    mi = torch.from_numpy(maps_in).cuda()
+    mo = torch.empty(T, 8, dtype=torch.float32, device="cuda")
+    Wh = (0.2 * rng.standard_normal((8, 2 * C))).astype(np.float32)
+    bh = (0.2 * rng.standard_normal(8)).astype(np.float32)
+    w, bb = torch.from_numpy(Wh).cuda(), torch.from_numpy(bh).cuda()
+    gamma = torch.ones(C, dtype=torch.float32, device="cuda")
+    u = torch.empty(T, C, dtype=torch.bfloat16, device="cuda")
+    nb = A.loop_op_mhc_bytes(C)
+    scr = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    A.loop_op_mhc(A.LOOP_BF16, A.LOOP_MHC_MID, T, C, 20, 1e-6, y.data_ptr(), None, X.data_ptr(), mi.data_ptr(),
+                  mo.data_ptr(), w.data_ptr(), bb.data_ptr(), gamma.data_ptr(), u.data_ptr(), scr.data_ptr(), nb,
+                  _stream())
+    torch.cuda.synchronize()
+    gX = X.float().cpu().numpy().astype(np.float64)
+    W64, b64 = Wh.astype(np.float64), bh.astype(np.float64)
+    pre, post, res, _ = M.mhc_maps(gX, W64, b64, 20, 1e-6)
+    ref = np.concatenate([pre, post, res.reshape(-1, 4)], 1)
+    got = mo.cpu().numpy().astype(np.float64)
+    assert np.isfinite(got).all()
+    xh = gX.reshape(T, -1)
+    xh = xh / np.sqrt((xh ** 2).mean(1, keepdims=True) + 1e-6)
+    logits = xh @ W64.T + b64
+    print(f"  logit std {logits.std():.1f}, max |logit| {np.abs(logits).max():.1f}", flush=True)
+    scale = np.abs(xh) @ np.abs(W64).T                      # sum |w x_hat| per token and logit
+    bound = 64 * 2.0 ** -24 * scale.max(1, keepdims=True) + 1e-6
+    err = np.abs(got - ref)
+    print(f"  maps max |diff| {err.max():.2e}, max bound {bound.max():.2e}", flush=True)
+    assert np.all(err <= bound)
+    # the columns of the residual map sum to 1 after the last (column) step
+    assert np.abs(got[:, 4:8].reshape(-1, 2, 2).sum(1) - 1).max() < 1e-5
