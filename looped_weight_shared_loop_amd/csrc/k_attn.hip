@@ -172,50 +172,77 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
     const bf16_t* vs = smem + (kt % AQ_NS) * AQ_STAGE + PK * PD;
     // st[c][r]: key kt*64 + 32c + 16(r/8) + 8h + r%8, query column `col`
     const bool diag = kt * PK + PK - 1 > a.pos0 + q0;
-    // four independent partial maxima (and sums below), so that a wave
-    // alone on its SIMD's vector ALU is not held up by one dependent chain
-    float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-    if (diag) {
+    auto mask = [&]() {
+      if (diag) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt * PK + c * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
+            if (!(key <= qpos && key < kv_end)) st[c][r] = -INFINITY;
+          }
+      }
+    };
+    mask();
+    // Probabilities against the running max, without the tile's own max:
+    // bf16 keeps its relative precision at any magnitude, so p may grow far
+    // past 1 before anything is lost.  Only when a lane's partial sum passes
+    // 2^64 (a score 64 past the running max in base-2 units; 2^64 times 2^18
+    // keys stays far inside float32), and at tile 0, where there is no running
+    // max yet, is the tile's max taken: from the scores recomputed out of the
+    // K tile, which is still in LDS.  Four independent partial sums (and maxima
+    // below), so that a wave alone on its SIMD's vector ALU is not held up by
+    // one dependent chain.
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    bool slow = kt == 0;                   // every wave starts at tile 0
+    if (!slow) {
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = kt * PK + c * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
-          const float v = (key <= qpos && key < kv_end) ? st[c][r] : -INFINITY;
-          st[c][r] = v;
-          tm[r & 3] = fmaxf(tm[r & 3], v);
+          const float p = exp2_hw(fmaf(st[c][r], sc, -mrun));
+          st[c][r] = p;
+          ps[r & 3] += p;
         }
-    } else {
+      slow = __any(!((ps[0] + ps[1]) + (ps[2] + ps[3]) <= 0x1p64f));
+    }
+    float mnew = mrun;
+    if (slow) {
+      if (kt != 0) {
+        scores(kt, st);
+        mask();
+      }
+      float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
       for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) tm[r & 3] = fmaxf(tm[r & 3], st[c][r]);
-    }
-    float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
-    tmax = x32_max(tmax) * sc;     // scaled (base-2) units
-    // the running max moves only when the tile's max exceeds it by more than
-    // 8: the probabilities stay below 2^8 and the result is the same softmax,
-    // with fewer rescales of O
-    const float mnew = tmax > mrun + 8.f ? tmax : mrun;
-    const float mfin = (mnew == -INFINITY) ? 0.f : mnew;
-    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+      float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+      tmax = x32_max(tmax) * sc;     // scaled (base-2) units
+      // the running max moves only when the tile's max exceeds it by more
+      // than 8, so O is rescaled rarely
+      mnew = tmax > mrun + 8.f ? tmax : mrun;
+      const float mfin = (mnew == -INFINITY) ? 0.f : mnew;
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+      for (int i = 0; i < 4; ++i) ps[i] = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float p = exp2_hw(fmaf(st[c][r], sc, -mfin));
-        st[c][r] = p;
-        ps[r & 3] += p;
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_hw(fmaf(st[c][r], sc, -mfin));
+          st[c][r] = p;
+          ps[r & 3] += p;
+        }
+      if (__any(mnew > mrun)) {
+        const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(mrun - mnew);
+        lrun *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       }
-    const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
-    if (__any(mnew > mrun)) {
-      const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(mrun - mnew);
-      lrun *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
     }
+    const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
     lrun += psum;
     mrun = mnew;
 #pragma unroll

@@ -7,7 +7,10 @@ and every query q_t = a_t sqrt(d) u.  The score q_t . k_tau / sqrt(d) is then
 a_t (s_tau + e_tau): a per-tile level s (steps just under, just over and far
 over the threshold, and drops) plus a small spread e inside the tile.  The
 query scales a_t in [0.85, 1.15] put a step of 8.5 on either side of 8 for
-different queries.  Sampled rows are checked against the oracle's causal
+different queries.  The level climbs past 64 (base 2) above the first tile's
+within a dozen tiles, so the kernels' fast path (probabilities against the
+running max, no per-tile max) and their recompute path (a lane's partial sum
+past 2^64: the tile's max taken from recomputed scores) both run.  Sampled rows are checked against the oracle's causal
 softmax attention (pages: "How Does SenseNova-Loop Get More Depth Without More
 Parameters?", section "How does the hybrid attention pattern work?"), per row
 at 2e-2 of the row's largest value, for a chunk from position 0 and a chunk
