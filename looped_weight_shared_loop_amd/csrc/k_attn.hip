@@ -505,49 +505,43 @@ __global__ __launch_bounds__(64 * A2_NW, 1) void attn_prefill_d256(AttnArgs a) {
         }
     }
   };
-  // scores of the next tile (nxt) fused with the softmax of this one (cur):
-  // cur becomes its probabilities; returns the new running max and the sum
+  // Scores of the next tile (nxt) fused with the softmax of this one (cur):
+  // its probabilities pc against the running max, without the tile's own max
+  // (bf16 keeps its relative precision at any magnitude).  Returns whether
+  // some lane's partial sum passed 2^64 or is not finite (always at tile 0,
+  // where the running max is -inf): then rescale_pv takes the tile's max from
+  // the raw scores cur, which are kept for that.
+  float pc[2][16];
   uint32_t pw[4][4];
-  auto scores_softmax = [&](int kstage, f32x16_t (&nxt)[2], f32x16_t (&cur)[2], float& mnew, float& psum) {
+  auto pack = [&](int mm) {
+    const int c = mm >> 1, half = mm & 1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pw[mm][e] = pack_bf16x2(pc[c][half * 8 + 2 * e], pc[c][half * 8 + 2 * e + 1]);
+  };
+  auto scores_softmax = [&](int kstage, f32x16_t (&nxt)[2], const f32x16_t (&cur)[2], float& psum) {
     const bf16_t* ks = kring + kstage * A2_KST;
     f32x16_t lo[2], hi[2];
     ldk(ks, 0, kf[0]);
     ldk(ks, 1, kf[1]);
-    float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     float ps[4] = {0.f, 0.f, 0.f, 0.f};
-    float mfin = 0.f;
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) {
       score_step(ks, ds, lo, hi);
-      if (ds < 2) {                     // partial maxima of one 32-key block
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tm[r & 3] = fmaxf(tm[r & 3], cur[ds][r]);
-      }
-      if (ds == 1) {
-        float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
-        tmax = x32_max(tmax) * sc;
-        // lazy rescaling, as in the d = 128 kernel
-        mnew = tmax > mrun + 8.f ? tmax : mrun;
-        mfin = (mnew == -INFINITY) ? 0.f : mnew;
-      }
-      if (ds >= 2 && ds < 6) {          // eight probabilities per step
-        const int c = (ds - 2) >> 1, r0 = ((ds - 2) & 1) * 8;
+      if (ds < 4) {                     // eight probabilities per step
+        const int c = ds >> 1, r0 = (ds & 1) * 8;
 #pragma unroll
         for (int r = r0; r < r0 + 8; ++r) {
-          const float p = exp2_hw(fmaf(cur[c][r], sc, -mfin));
-          cur[c][r] = p;
+          const float p = exp2_hw(fmaf(cur[c][r], sc, -mrun));
+          pc[c][r] = p;
           ps[r & 3] += p;
         }
         // formed here, beside this step's MFMAs (the compiler would otherwise
         // sink them to their uses after the rescale branch)
         asm volatile("" : "+v"(ps[0]), "+v"(ps[1]), "+v"(ps[2]), "+v"(ps[3]));
-      }
-      if (ds >= 6) {                    // bf16 pairs for two PV steps
+      } else if (ds < 6) {              // bf16 pairs for two PV steps
 #pragma unroll
-        for (int mm = 2 * (ds - 6); mm < 2 * (ds - 6) + 2; ++mm) {
-          const int c = mm >> 1, half = mm & 1;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) pw[mm][e] = pack_bf16x2(cur[c][half * 8 + 2 * e], cur[c][half * 8 + 2 * e + 1]);
+        for (int mm = 2 * (ds - 4); mm < 2 * (ds - 4) + 2; ++mm) {
+          pack(mm);
           asm volatile("" : "+v"(pw[mm][0]), "+v"(pw[mm][1]), "+v"(pw[mm][2]), "+v"(pw[mm][3]));
         }
       }
@@ -557,31 +551,56 @@ __global__ __launch_bounds__(64 * A2_NW, 1) void attn_prefill_d256(AttnArgs a) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) nxt[c] = lo[c] + hi[c];
   };
-  auto rescale_pv = [&](int vstage, float mnew, float psum) {
+  auto rescale_pv = [&](int vstage, const f32x16_t (&cur)[2], float psum) {
     const bf16_t* vs = vring + vstage * A2_KST;
-    if (__any(mnew > mrun)) {
-      const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(mrun - mnew);
-      lrun *= alpha;
-      // O scaled in place in the accumulation registers (a copy through the
-      // vector registers would make the compiler keep O there, at 128
-      // registers and two copies per tile).  The last MFMA writing O was
-      // issued a whole tile of work earlier; the nops cover the read-after-
-      // MFMA, read -> VALU and write -> MFMA source wait states all the same.
-      asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    float mnew = mrun;
+    if (__any(!(psum <= 0x1p64f))) {
+      float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tm[r & 3] = fmaxf(tm[r & 3], cur[c][r]);
+      float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+      tmax = x32_max(tmax) * sc;
+      // lazy rescaling, as in the d = 128 kernel
+      mnew = tmax > mrun + 8.f ? tmax : mrun;
+      const float mfin = (mnew == -INFINITY) ? 0.f : mnew;
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float t;
-          asm volatile(
-              "v_accvgpr_read_b32 %1, %0\n\t"
-              "s_nop 1\n\t"
-              "v_mul_f32 %1, %1, %2\n\t"
-              "v_accvgpr_write_b32 %0, %1\n\t"
-              "s_nop 3"
-              : "+a"(o[db][r]), "=&v"(t)
-              : "v"(alpha));
+          const float p = exp2_hw(fmaf(cur[c][r], sc, -mfin));
+          pc[c][r] = p;
+          ps[r & 3] += p;
         }
+      psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) pack(mm);
+      if (__any(mnew > mrun)) {
+        const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(mrun - mnew);
+        lrun *= alpha;
+        // O scaled in place in the accumulation registers (a copy through the
+        // vector registers would make the compiler keep O there, at 128
+        // registers and two copies per tile).  The last MFMA writing O was
+        // issued a whole tile of work earlier; the nops cover the read-after-
+        // MFMA, read -> VALU and write -> MFMA source wait states all the same.
+        asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+        for (int db = 0; db < 8; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float t;
+            asm volatile(
+                "v_accvgpr_read_b32 %1, %0\n\t"
+                "s_nop 1\n\t"
+                "v_mul_f32 %1, %1, %2\n\t"
+                "v_accvgpr_write_b32 %0, %1\n\t"
+                "s_nop 3"
+                : "+a"(o[db][r]), "=&v"(t)
+                : "v"(alpha));
+          }
+      }
     }
     lrun += psum;
     mrun = mnew;
@@ -642,9 +661,9 @@ __global__ __launch_bounds__(64 * A2_NW, 1) void attn_prefill_d256(AttnArgs a) {
     // read a stale stage and go unused; a tile past the wave's last query is
     // masked out whole, so its probabilities are 0
     mask_diag(kt, cur);
-    float mnew, psum;
-    scores_softmax(par ^ 1, nxt, cur, mnew, psum);
-    rescale_pv(par, mnew, psum);
+    float psum;
+    scores_softmax(par ^ 1, nxt, cur, psum);
+    rescale_pv(par, cur, psum);
   };
   for (int kt = 0; kt < ntiles; kt += 2) {
     step(kt, 0, sa, sb);
