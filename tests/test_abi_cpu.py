@@ -72,6 +72,10 @@ def _create(cfg, n_layers=None):
     (dict(dtype="bf16", head_dim=128, hidden=256, n_heads=6, n_kv_heads=2), -2),   # group of 3 heads
     (dict(dtype="bf16", head_dim=256, hidden=256, n_heads=8, n_kv_heads=1), -2),   # 8 heads of 256 per group
     (dict(head_dim=256), -2),                 # float32 needs head_dim 64 or 128
+    # weight matrices the 256-row GEMM tiles cannot address with 32-bit offsets: refused at
+    # creation, before any call could fail part-way through a forward
+    (dict(dtype="bf16", head_dim=128, hidden=4096, n_heads=32, n_kv_heads=8, ffn=12288, vocab=1 << 20), -2),
+    (dict(dtype="bf16", head_dim=128, hidden=4096, n_heads=32, n_kv_heads=8, ffn=1 << 18, vocab=1024), -2),
 ])
 def test_create_rejects_bad_configs(kw, code):
     from looped_weight_shared_loop_amd import LoopError
