@@ -567,9 +567,9 @@ def _labels(names):
     out, prev = [], ""
     for n in names:
         lab = n
-        if "gemm_w4_kernel<" in n or "gemm_skinny_rs_kernel<" in n or "gemm_dma_kernel<" in n:
+        if any(k in n for k in ("gemm_w4_kernel<", "gemm_w16_kernel<", "gemm_skinny_rs_kernel<", "gemm_dma_kernel<")):
             epi = n.split("<")[1].split(",")[0].split(">")[0]
-            kind = "256-row tiles" if "w4" in n or "dma" in n else "skinny, weights streamed once"
+            kind = "skinny, weights streamed once" if "skinny" in n else "256-row tiles"
             if epi == "3":
                 lab = f"gemm gate/up + SwiGLU ({kind}) {n}"
             elif epi == "2":
@@ -760,7 +760,7 @@ def main():
         "prefill": {"tflops": round(tflops, 1), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                     "algorithmic_tflop": round(flops / 1e12, 2), "gemm_tflop": round(gemm_f / 1e12, 2),
                     "attention_tflop": round(attn_f / 1e12, 2), "linear_tflop": round(lin_f / 1e12, 3)},
-        "roofline": {"kernel": "gemm_w4_kernel<EPI_SWIGLU> (gate/up, M=%d N=24576 K=4096)" % S, "bound": "mfma",
+        "roofline": {"kernel": "gemm_w16_kernel<EPI_SWIGLU> (gate/up, M=%d N=24576 K=4096)" % S, "bound": "mfma",
                      "achieved": round(g_tflops, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(g_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": (None if S != 32768 or traffic is None else round(traffic)),

@@ -4,7 +4,9 @@
 //                workgroup tile, 4 waves of 128x128 (v_mfma_f32_32x32x16_bf16),
 //                64-deep k steps of whole-line global -> LDS DMA into two
 //                stages, persistent workgroups, XCD-aware tile order.  fp32
-//                accumulation.
+//                accumulation.  Taken for operand rows longer than 8 KB.
+// * gemm_w16:    the same tile on v_mfma_f32_16x16x32_bf16 with one barrier
+//                per step; taken for operand rows up to 8 KB.
 // * gemm_dma:    bf16, M > 64, other K % 32 == 0.  The same tile with 8 waves of
 //                128x64 and 32-deep steps through five LDS stages.
 // * gemm_skinny: bf16, M <= 64 (decode): streams B (the weights) once for up to
@@ -599,6 +601,249 @@ __global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
 }
 
+// ------------------------------------------------------------------ MFMA tile kernel, 16x16x32
+// The persistent 256x256 tile of gemm_w4 (same LDS layout, stages, tile order
+// and load cursor) on v_mfma_f32_16x16x32_bf16: a wave's 128x128 is 8 x 8
+// blocks of 16x16 (64 four-register accumulators) and a 64-deep step is two
+// 32-deep substeps of 64 MFMAs.  The step's one barrier sits between its
+// substeps.  Every fragment of the second substep is read during the first
+// (two register sets), so no wave reads the stage after the barrier; the
+// second substep reads the next step's first fragments from the other stage,
+// which landed before the barrier, and issues the 16 loads of step s + 2 into
+// this stage, one after every fourth MFMA.  The MFMAs are in-place
+// instructions on the accumulation registers: through the builtin the
+// compiler lets the registers of the 64 accumulators drift between loop
+// iterations and copies them every step.  The two kernels' outputs agree bit
+// for bit on every shape measured.  Against gemm_w4 on the Loop-9B shapes
+// (M = 32768) this one is 4-8% faster with 8 KB operand rows (K = 4096) and
+// 20-25% slower with 24 KB rows (the down projection), so the host picks by
+// row pitch.
+template <int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_w16_kernel(GemmArgs a) {
+  constexpr int NB = 8;                    // DMA instructions per wave per operand per step
+  extern __shared__ __align__(16) bf16_t smem[];
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wid >> 1, wn = wid & 1;
+  const int num_m = (a.M + TBM - 1) / TBM;
+  const int out_n = (EPI == EPI_SWIGLU) ? 128 : TBN;
+  const int num_n = (EPI == EPI_SWIGLU ? a.F : a.N) / out_n;
+  const int nblk = num_m * num_n;
+  const int G = gridDim.x;
+  const int GM = num_n <= 16 ? 4 : 8;
+  auto tile_mn = [&](int t, int& m0, int& n0) __attribute__((always_inline)) {
+    int id = t;
+    if (nblk % 8 == 0) id = (id & 7) * (nblk >> 3) + (id >> 3);
+    const int group = GM * num_n;
+    const int first_m = (id / group) * GM;
+    const int gsz = min(num_m - first_m, GM);
+    m0 = (first_m + (id % group) % gsz) * TBM;
+    n0 = ((id % group) / gsz) * out_n;
+  };
+  const int KT = a.K / WBK;
+  // One load cursor (tile c_t, step c_kt), two steps ahead of the MFMAs.
+  // Wave w loads rows 64 w .. 64 w + 63 of both operand tiles: block i is
+  // rows 64 w + 8 i + lane / 8, whose swizzle depends on i only through its
+  // parity, so a lane keeps two vector offsets per operand and a block adds
+  // a scalar one.  Rows past M lie past the end of the A view and read zeros.
+  int c_t = blockIdx.x, c_kt = 0;
+  __amdgpu_buffer_rsrc_t Ar;
+  const __amdgpu_buffer_rsrc_t Br = buf_rsrc(a.B, 0xFFFFFFF0u);
+  const int lda2 = (int)a.lda * 2, ldb2 = (int)a.ldb * 2;
+  int av[2], bv[2], a_s = 0, b_s = 0;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int r = p * 8 + (lane >> 3);
+    const int cs = ((lane & 7) ^ ((r >> 1) & 7)) * 16;
+    av[p] = (lane >> 3) * lda2 + cs;
+    bv[p] = (lane >> 3) * ldb2 + cs;
+  }
+  auto set_ab = [&](int t) __attribute__((always_inline)) {
+    int m0, n0;
+    tile_mn(t, m0, n0);
+    Ar = buf_rsrc((const bf16_t*)a.A + (long)m0 * a.lda, (unsigned)(min(TBM, a.M - m0) * a.lda * 2));
+    // B row of tile row r: n0 + r; SwiGLU: rows 128 w' + x are gate rows
+    // n0 + 64 w' + x (x < 64), then the up rows of the same outputs
+    int brow0;
+    if (EPI == EPI_SWIGLU) brow0 = ((wid & 1) ? a.F : 0) + n0 + (wid >> 1) * 64;
+    else brow0 = n0 + wid * 64;
+    a_s = wid * 64 * lda2;
+    b_s = brow0 * ldb2;
+  };
+  auto next = [&]() __attribute__((always_inline)) {
+    if (++c_kt == KT) {
+      if (c_t + G < nblk) {
+        c_t += G;
+        c_kt = 0;
+        set_ab(c_t);
+      } else {
+        c_kt = KT - 1;      // past the last tile: re-read into the stage nobody reads again
+      }
+    }
+  };
+  set_ab(c_t);
+  // load L of a step: L < 8 block L of A, else block L - 8 of B
+  auto dma = [&](int L, int par) __attribute__((always_inline)) {
+    const int i = L % NB;
+    if (L < NB)
+      dma16_buf(Ar, av[i & 1], a_s + i * 8 * lda2 + c_kt * WBK * 2, smem + par * WSTAGE + (wid * NB + i) * 512);
+    else
+      dma16_buf(Br, bv[i & 1], b_s + i * 8 * ldb2 + c_kt * WBK * 2,
+                smem + par * WSTAGE + TBM * WBK + (wid * NB + i) * 512);
+  };
+  f32x4_t acc[8][8];
+  const int arow = wm * 128 + (lane & 15);
+  const int brow = wn * 128 + (lane & 15);
+  bf16x8_t fa[2][8], fb[2][8];
+  // the fragment of 16 rows x 32 k: lane l holds row l % 16, k 8 (l / 16) .. + 7 of substep j
+  auto read_frags = [&](int par, int j, bf16x8_t (&xa)[8], bf16x8_t (&xb)[8]) __attribute__((always_inline)) {
+    const bf16_t* as = smem + par * WSTAGE;
+    const bf16_t* bs = as + TBM * WBK;
+    const int ch = j * 4 + (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      xa[i] = as_bf16x8(ldv4(as + wswz(arow + i * 16, ch)));
+      xb[i] = as_bf16x8(ldv4(bs + wswz(brow + i * 16, ch)));
+    }
+  };
+  // One substep: 64 MFMAs; after every fourth, one fragment read of the other
+  // register set (rd >= 0: substep rd of stage rpar; B blocks first) and, when
+  // lpar >= 0, one load into stage lpar.  Scheduling walls keep this order.
+  auto substep = [&](const bf16x8_t (&xa)[8], const bf16x8_t (&xb)[8], bool first, int rpar, int rd,
+                     bf16x8_t (&ya)[8], bf16x8_t (&yb)[8], int lpar) __attribute__((always_inline)) {
+    const bf16_t* as = smem + rpar * WSTAGE;
+    const bf16_t* bs = as + TBM * WBK;
+    const int ch = rd * 4 + (lane >> 4);
+#pragma unroll
+    for (int q = 0; q < 64; ++q) {
+      const int ib = q >> 3, jb = q & 7;
+      if (first)
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, 0" : "=a"(acc[ib][jb]) : "v"(xa[ib]), "v"(xb[jb]));
+      else
+        asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc[ib][jb]) : "v"(xa[ib]), "v"(xb[jb]));
+      if (rd >= 0 && q % 4 == 0) {
+        const int f = q / 4;
+        if (f < 8) yb[f] = as_bf16x8(ldv4(bs + wswz(brow + f * 16, ch)));
+        else ya[f - 8] = as_bf16x8(ldv4(as + wswz(arow + (f - 8) * 16, ch)));
+      }
+      if (lpar >= 0 && q % 4 == 0) dma(q / 4, lpar);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto sync = [&]() __attribute__((always_inline)) {
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  };
+  // step 0 into stage 0; step 1 into stage 1 (lands before step 0's barrier)
+#pragma unroll
+  for (int L = 0; L < 2 * NB; ++L) dma(L, 0);
+  next();
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  sync();
+#pragma unroll
+  for (int L = 0; L < 2 * NB; ++L) dma(L, 1);
+  next();
+  read_frags(0, 0, fa[0], fb[0]);
+  // Step s on stage par: substep 0 reads substep 1's fragments; the barrier
+  // (this wave's loads of step s + 1 landed, every read of this stage
+  // returned); substep 1 reads the first fragments of step s + 1 (last: of
+  // the next tile, after its epilogue instead) and loads step s + 2 here.
+  auto step = [&](int par, bool first, bool last) __attribute__((always_inline)) {
+    substep(fa[0], fb[0], first, par, 1, fa[1], fb[1], -1);
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+    sync();
+    substep(fa[1], fb[1], false, par ^ 1, last ? -1 : 0, fa[0], fb[0], par);
+    next();
+  };
+
+  // Epilogue.  acc[ib][jb][r]: row wm*128 + 16 ib + 4 (lane / 16) + r, column
+  // wn*128 + 16 jb + lane % 16 (SwiGLU: gate block jb < 4 pairs with up block
+  // jb + 4, output column wn*64 + 16 jb + lane % 16).  Plain stores go through
+  // a buffer view of the tile's rows that ends at row M, as in gemm_w4.
+  auto epilogue = [&](int m0, int n0) __attribute__((always_inline)) {
+    const int lrow = wm * 128 + (lane >> 4) * 4, lcol = lane & 15;
+    int ksq = -1;
+    if (EPI == EPI_QKV && n0 >= a.q_cols && n0 + TBN <= a.q_cols + a.n_kv * a.head_dim && a.head_dim == 128 &&
+        !a.pos_dev && m0 / a.S_call == (min(m0 + TBM, a.M) - 1) / a.S_call)
+      ksq = m0 / a.S_call;
+    if (EPI == EPI_SWIGLU || EPI == EPI_STORE || EPI == EPI_F32 || n0 + TBN <= a.q_cols || ksq >= 0) {
+      constexpr int ES = EPI == EPI_F32 ? 4 : 2;
+      int ldcb = (int)(ksq >= 0 ? a.head_dim : a.ldc) * ES;
+      asm volatile("" : "+s"(ldcb));
+      const char* base = (const char*)a.C + (size_t)m0 * ldcb;
+      int lb = lrow * ldcb + (n0 + wn * (EPI == EPI_SWIGLU ? 64 : 128) + lcol) * ES;
+      if (ksq >= 0) {
+        const int hk = (n0 - a.q_cols) / 128 + wn;
+        base = (const char*)a.kcache +
+               (((size_t)ksq * a.n_kv + hk) * a.S_max + a.pos0 + (m0 - ksq * a.S_call)) * (size_t)ldcb;
+        lb = lrow * ldcb + lcol * ES;
+      }
+      const __amdgpu_buffer_rsrc_t Cr = buf_rsrc(base, (unsigned)(min(TBM, a.M - m0) * ldcb));
+#pragma unroll
+      for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int vo = lb + (ib * 16 + r) * ldcb;
+          if (EPI == EPI_SWIGLU) {
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb)
+              __builtin_amdgcn_raw_buffer_store_b16(f2bf(silu(acc[ib][jb][r]) * acc[ib][jb + 4][r]), Cr,
+                                                    vo + jb * 16 * ES, 0, 0);
+          } else if (EPI == EPI_F32) {
+#pragma unroll
+            for (int jb = 0; jb < 8; ++jb)
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[ib][jb][r]), Cr, vo + jb * 16 * ES, 0, 0);
+          } else {
+#pragma unroll
+            for (int jb = 0; jb < 8; ++jb)
+              __builtin_amdgcn_raw_buffer_store_b16(f2bf(acc[ib][jb][r]), Cr, vo + jb * 16 * ES, 0, 0);
+          }
+        }
+    } else {
+      // QKV tile wholly in the V columns: a lane's four rows of a block are
+      // four consecutive positions of one V^T row, one 8-byte store (as in gemm_w4)
+      const int kvn = a.n_kv * a.head_dim;
+      const bool vtile = EPI == EPI_QKV && n0 >= a.q_cols + kvn && !a.pos_dev && a.S_call % 4 == 0 &&
+                         a.pos0 % 4 == 0 && (a.head_dim & 31) == 0;
+#pragma unroll
+      for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb) {
+          const int row = m0 + lrow + ib * 16;      // rows row .. row + 3
+          const int col = n0 + wn * 128 + jb * 16 + lcol;
+          if (vtile && row + 3 < a.M) {
+            const int cc = col - a.q_cols - kvn;
+            const int hk = cc / a.head_dim, dd = cc - hk * a.head_dim;
+            const int b = row / a.S_call, pos = a.pos0 + row - b * a.S_call;
+            bf16_t* dst = (bf16_t*)a.vcache + (((size_t)b * a.n_kv + hk) * a.head_dim + dd) * a.S_max + pos;
+            *(u32x2_t*)dst = u32x2_t{pack_bf16x2(acc[ib][jb][0], acc[ib][jb][1]),
+                                     pack_bf16x2(acc[ib][jb][2], acc[ib][jb][3])};
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (row + r < a.M) epi_one<bf16_t, EPI, false>(a, row + r, col, acc[ib][jb][r]);
+          }
+        }
+    }
+  };
+
+  for (int t = blockIdx.x; t < nblk; t += G) {
+    step(0, true, false);
+    for (int kt = 1; kt + 2 < KT; kt += 2) {
+      step(1, false, false);
+      step(0, false, false);
+    }
+    step(1, false, true);
+    int m0, n0;
+    tile_mn(t, m0, n0);
+    // the in-place MFMAs are opaque to the compiler's hazard checks: wait out
+    // their write latency before the accumulators are read
+    asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
+    epilogue(m0, n0);
+    read_frags(0, 0, fa[0], fb[0]);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
+}
+
 // ------------------------------------------------------------------ skinny (M <= 64)
 // Decode shape: the weights are streamed once; the <= 64 token rows (one or two
 // blocks of 32) are the MFMA's other operand (gemm_skinny_rs_kernel below).
@@ -909,6 +1154,19 @@ static hipError_t launch_w4(const GemmArgs& a, int blocks, hipStream_t s) {
 }
 
 template <int EPI>
+static hipError_t launch_w16(const GemmArgs& a, int blocks, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_w16_kernel<EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       GEMM_W4_LDS);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  gemm_w16_kernel<EPI><<<blocks, 256, GEMM_W4_LDS, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int EPI>
 static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   if (a.M <= 64) {
     if (a.ksplit < 1 || a.K % (a.ksplit * 64)) return hipErrorInvalidValue;
@@ -924,9 +1182,12 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   if (ncols % out_n) return hipErrorInvalidValue;
   const int blocks = ((a.M + TBM - 1) / TBM) * (ncols / out_n);
   if (a.K % (2 * WBK) == 0) {
-    // persistent: one workgroup per CU (a multiple of 8, for the XCD order)
+    // persistent: one workgroup per CU (a multiple of 8, for the XCD order);
+    // 16x16x32 MFMAs for operand rows up to 8 KB, 32x32x16 beyond (measured)
     const int cu = device_cu_count() & ~7;
-    return launch_w4<EPI>(a, (cu > 0 && blocks > cu) ? cu : blocks, s);
+    const int g = (cu > 0 && blocks > cu) ? cu : blocks;
+    if (a.lda <= 4096 && a.ldb <= 4096) return launch_w16<EPI>(a, g, s);
+    return launch_w4<EPI>(a, g, s);
   }
   return launch_dma<EPI, 4>(a, blocks, s);
 }
