@@ -32,8 +32,8 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 # dispatch), each scaled by the same counter's reading for a plain 1 GiB
 # device copy in that run.  Valid only for the kernel source it was taken on:
 # the hash of k_gemm.hip + common.h must match, else traffic is reported null.
-DOMINANT_COUNTERS = {"source_sha256_16": "1b9ed5dc71955733", "fetch_kib": 4929590.5, "write_kib": 807168.0,
-                     "copy_fetch_kib": 524308.4, "copy_write_kib": 1048576.0}
+DOMINANT_COUNTERS = {"source_sha256_16": "4133fdefaf0ea73c", "fetch_kib": 4728479.6, "write_kib": 786688.0,
+                     "copy_fetch_kib": 524308.0, "copy_write_kib": 1048576.0}
 
 NINE_B = dict(vocab=248320, hidden=4096, ffn=12288, n_heads=32, n_kv_heads=8, head_dim=128,
               n_layers=32, loop_start=4, loop_end=28, n_passes=2, dtype="bf16")
@@ -590,11 +590,15 @@ def _labels(names):
 
 def _scope(names, scope, marker):
     """Index range summarized: everything after the 1 GiB reference copy
-    ('all'), or from the last launch of the marker kernel on ('last')."""
+    ('all'), from the last launch of the marker kernel on ('last'), or from
+    its launch N + 1 on ('after:N', e.g. past N untimed warm-up launches)."""
     first = next(i for i, n in enumerate(names) if n == "__amd_rocclr_copyBuffer") + 1
     if scope == "all":
         return first, len(names)
     idx = [i for i, n in enumerate(names) if marker in n and i >= first]
+    if scope.startswith("after:"):
+        k = int(scope.split(":")[1])
+        return (idx[k] if k < len(idx) else len(names)), len(names)
     return (idx[-1] if idx else first), len(names)
 
 
@@ -714,9 +718,9 @@ def main():
     ap.add_argument("--summarize", nargs="+", metavar=("KIND", "DIR"),
                     help="print a summary of rocprofv3 CSV output instead of running: trace DIR | mfma DIR | "
                          "hbm FETCH_DIR WRITE_DIR (no GPU needed)")
-    ap.add_argument("--scope", choices=("last", "all"), default="last",
-                    help="with --summarize: the last run of the workload (from the last --marker launch) or "
-                         "everything after the reference copy")
+    ap.add_argument("--scope", default="last",
+                    help="with --summarize: last (from the last --marker launch), all (everything after the "
+                         "reference copy) or after:N (from --marker launch N + 1 on)")
     ap.add_argument("--marker", default="embed_kernel", help="with --summarize: the kernel that starts a run")
     ap.add_argument("--title", default="rocprofv3 summary")
     args = ap.parse_args()
