@@ -1,12 +1,10 @@
 // Dense contractions of the looped decoder: C[M, N] = A[M, K] . B[N, K]^T.
 //
-// * gemm_w4:     bf16, M > 64, K % 128 == 0 (every model shape).  256x256
-//                workgroup tile, 4 waves of 128x128 (v_mfma_f32_32x32x16_bf16),
+// * gemm_w16:    bf16, M > 64, K % 128 == 0 (every model shape).  256x256
+//                workgroup tile, 4 waves of 128x128 (v_mfma_f32_16x16x32_bf16),
 //                64-deep k steps of whole-line global -> LDS DMA into two
 //                stages, persistent workgroups, XCD-aware tile order.  fp32
-//                accumulation.  Taken for operand rows longer than 8 KB.
-// * gemm_w16:    the same tile on v_mfma_f32_16x16x32_bf16 with one barrier
-//                per step; taken for operand rows up to 8 KB.
+//                accumulation.
 // * gemm_dma:    bf16, M > 64, other K % 32 == 0.  The same tile with 8 waves of
 //                128x64 and 32-deep steps through five LDS stages.
 // * gemm_skinny: bf16, M <= 64 (decode): streams B (the weights) once for up to
@@ -255,34 +253,37 @@ __global__ __launch_bounds__(128 * WN_, 1) void gemm_dma_kernel(GemmArgs a) {
 
 // ------------------------------------------------------------------ MFMA tile kernel, 64-deep
 // 256x256 workgroup tile, four waves as 2 (M) x 2 (N), each owning 128x128 =
-// 4x4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).
-// A k step is 64 deep, so every operand row of a step is one whole 128-byte
-// line: a DMA instruction moves 8 rows (1 KB, lane l to +16 l), and the row's
-// eight 16-byte chunks sit at c ^ ((row >> 1) & 7): a fragment read takes one
-// chunk of 16 consecutive rows per 16 lanes, and with 64 four-byte banks two
-// rows span all banks, so the rows of one parity must use 8 distinct
-// positions.  Two 64 KB stages.  Within a step the fragments of substep
-// j + 1 are read while the MFMAs of substep j run, one read after each of
-// the first eight MFMAs.  The step's one barrier sits before its last
-// substep, whose fragments are already in registers: by then every read of
-// the stage has returned and the next step has landed, so the next step's
-// first reads overlap the last MFMAs.  The loads are issued one after every
-// second MFMA rather than in a burst (a burst stalls the wave on a full load
-// queue while its MFMA pipe idles): A of step kt + 2 during the last substep
-// of step kt, into the stage just released, and B of step kt + 2 during the
-// first substep of step kt + 1.  Scheduling walls after every MFMA fix this
-// order.  The kernel is persistent: workgroup b takes tiles b, b + G, ...
-// (G a multiple of 8, at most the CU count) as one stream of k steps, so
-// the loads of a tile's first steps go out during the previous tile's last
-// steps and the epilogue (branch-free buffer stores) runs with them in
-// flight.
+// 8x8 blocks of v_mfma_f32_16x16x32_bf16 (64 four-register fp32 accumulators,
+// 256 per lane).  A k step is 64 deep, so every operand row of a step is one
+// whole 128-byte line: a DMA instruction moves 8 rows (1 KB, lane l to
+// +16 l), and the row's eight 16-byte chunks sit at c ^ ((row >> 1) & 7): a
+// fragment read takes one chunk of 16 consecutive rows per 16 lanes, and with
+// 64 four-byte banks two rows span all banks, so the rows of one parity must
+// use 8 distinct positions.  Two 64 KB stages; a step is two 32-deep
+// substeps of 64 MFMAs with the step's one barrier between them.  Every
+// fragment of the second substep is read during the first (two register
+// sets, one read after every fourth MFMA), so no wave reads the stage after
+// the barrier: the second substep reads the next step's first fragments from
+// the other stage, which landed before the barrier, and issues the 16 loads
+// of step s + 2 into this stage, one after every fourth MFMA rather than in a
+// burst (a burst stalls the wave on a full load queue while its MFMA pipe
+// idles).  Scheduling walls after every MFMA fix this order.  The kernel is
+// persistent: workgroup b takes tiles b, b + G, ... (G a multiple of 8, at
+// most the CU count) as one stream of k steps, so the loads of a tile's
+// first steps go out during the previous tile's last steps and the epilogue
+// (branch-free buffer stores) runs with them in flight.
+// The MFMAs are in-place instructions on the accumulation registers: through
+// the builtin the compiler let the registers of the 64 accumulators drift
+// between loop iterations and copied them every step.  Against the same tile
+// on 32x32x16 MFMAs (sixteen 16-register accumulators, four 16-deep
+// substeps) this kernel runs at a higher shader clock under load (1.85
+// against 1.69 GHz on the gate/up shape) and was 4-8% faster on every
+// Loop-9B projection, with outputs bit for bit equal.
 // Against the eight-wave, 32-deep kernel above this halves the L2 requests
 // (whole lines) and cuts LDS fragment reads by a third (128x128 per wave).
-// MFMA j of a step contracts k 16 j .. 16 j + 15 (lane half h reads chunk
-// 2 j + h), the same k sets in the same order as the kernel above.
 constexpr int WBK = 64, WST = 2;
 constexpr int WSTAGE = (TBM + TBN) * WBK;             // elements per stage (64 KB)
-constexpr int GEMM_W4_LDS = WST * WSTAGE * 2;         // 128 KB
+constexpr int GEMM_W16_LDS = WST * WSTAGE * 2;        // 128 KB
 
 DEV int wswz(int row, int chunk) { return row * WBK + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
@@ -295,329 +296,6 @@ DEV __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, unsigned bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
-template <int EPI>
-__global__ __launch_bounds__(256, 1) void gemm_w4_kernel(GemmArgs a) {
-  constexpr int JB = 4, WCOL = 128;
-  constexpr int NB = 8;                    // DMA instructions per wave per operand per step
-  extern __shared__ __align__(16) bf16_t smem[];
-  // the wave index is uniform: as a scalar it keeps every LDS destination of
-  // the DMA (the M0 operand) in scalar registers, with no per-load readfirstlane
-  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wid >> 1, wn = wid & 1;
-  const int num_m = (a.M + TBM - 1) / TBM;
-  const int out_n = (EPI == EPI_SWIGLU) ? 128 : TBN;
-  const int num_n = (EPI == EPI_SWIGLU ? a.F : a.N) / out_n;
-  const int nblk = num_m * num_n;
-  const int G = gridDim.x;                 // workgroup b takes tiles b, b + G, b + 2 G, ...
-  const int GM = num_n <= 16 ? 4 : 8;     // measured: 4 suits the 4096-wide outputs, 8 the wider ones
-  // Launch-order tile t -> output block.  XCD-aware as in the kernel above:
-  // workgroup b runs on XCD b % 8 and G is a multiple of 8 (or covers every
-  // tile), so tile t runs on XCD t % 8 and each XCD walks a contiguous range.
-  auto tile_mn = [&](int t, int& m0, int& n0) {
-    int id = t;
-    if (nblk % 8 == 0) id = (id & 7) * (nblk >> 3) + (id >> 3);
-    const int group = GM * num_n;
-    const int first_m = (id / group) * GM;
-    const int gsz = min(num_m - first_m, GM);
-    m0 = (first_m + (id % group) % gsz) * TBM;
-    n0 = ((id % group) / gsz) * out_n;
-  };
-  const int KT = a.K / WBK;
-
-  // The workgroup's steps form one stream over its tiles; the loads run ahead
-  // of the MFMAs on two cursors (A two steps ahead, B one), so the first
-  // steps of the next tile are in LDS by the time this tile's last MFMAs end
-  // and its epilogue runs.  A cursor past the last tile re-reads the last
-  // step into the stage nobody reads again, so the loop has no branch around
-  // its loads.
-  // Wave w issues DMA blocks 8 w .. 8 w + 7 of each operand: rows 8 blk + lane / 8,
-  // LDS chunk lane % 8 holds global chunk (lane % 8) ^ ((row >> 1) & 7).
-  // Buffer views of the tile's A rows and of B: byte offsets fit in 32 bits
-  // (the host checks 256 lda and the B rows against 2^31 elements).
-  int a_t = blockIdx.x, a_kt = 0, b_t = blockIdx.x, b_kt = 0;
-  __amdgpu_buffer_rsrc_t Ar;
-  const __amdgpu_buffer_rsrc_t Br = buf_rsrc(a.B, 0xFFFFFFF0u);
-  int aoff[NB], boff[NB];
-  auto set_a = [&](int t) {
-    int m0, n0;
-    tile_mn(t, m0, n0);
-    const int mlast = a.M - 1 - m0;
-    Ar = buf_rsrc((const bf16_t*)a.A + (long)m0 * a.lda, (unsigned)(min(TBM, a.M - m0) * a.lda * 2));
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int r = (wid * NB + i) * 8 + (lane >> 3);
-      aoff[i] = (min(r, mlast) * (int)a.lda + ((lane & 7) ^ ((r >> 1) & 7)) * 8) * 2;
-    }
-  };
-  auto set_b = [&](int t) {
-    int m0, n0;
-    tile_mn(t, m0, n0);
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int r = (wid * NB + i) * 8 + (lane >> 3);
-      int br;
-      if (EPI == EPI_SWIGLU) {
-        const int w = r / WCOL, j = (r % WCOL) / 32, cc = r & 31;
-        const int oc = n0 + w * (WCOL / 2) + (j % (JB / 2)) * 32 + cc;
-        br = (j < JB / 2) ? oc : (a.F + oc);
-      } else {
-        br = n0 + r;
-      }
-      boff[i] = (br * (int)a.ldb + ((lane & 7) ^ ((r >> 1) & 7)) * 8) * 2;
-    }
-  };
-  auto next_a = [&]() {
-    if (++a_kt == KT) {
-      if (a_t + G < nblk) {
-        a_t += G;
-        a_kt = 0;
-        set_a(a_t);
-      } else {
-        a_kt = KT - 1;
-      }
-    }
-  };
-  auto next_b = [&]() {
-    if (++b_kt == KT) {
-      if (b_t + G < nblk) {
-        b_t += G;
-        b_kt = 0;
-        set_b(b_t);
-      } else {
-        b_kt = KT - 1;
-      }
-    }
-  };
-  set_a(a_t);
-  set_b(b_t);
-  // one operand (op 0: A, op 1: B) at its cursor, NB loads per wave, into stage par
-  auto issue = [&](int par, int op) {
-    bf16_t* st = smem + par * WSTAGE + op * TBM * WBK;
-    if (op == 0) {
-#pragma unroll
-      for (int i = 0; i < NB; ++i) dma16_buf(Ar, aoff[i], a_kt * WBK * 2, st + (wid * NB + i) * 512);
-    } else {
-#pragma unroll
-      for (int i = 0; i < NB; ++i) dma16_buf(Br, boff[i], b_kt * WBK * 2, st + (wid * NB + i) * 512);
-    }
-  };
-  f32x16_t acc[4][JB];
-
-  const int arow = wm * 128 + (lane & 31);
-  const int brow = wn * WCOL + (lane & 31);
-  bf16x8_t fa[2][4], fb[2][JB];
-  // par: the stage, step & 1, passed as a constant so LDS addresses fold into offsets
-  auto read_frags = [&](int par, int j, bf16x8_t (&xa)[4], bf16x8_t (&xb)[JB]) {
-    const bf16_t* as = smem + par * WSTAGE;
-    const bf16_t* bs = as + TBM * WBK;
-    const int ch = j * 2 + (lane >> 5);
-#pragma unroll
-    for (int ib = 0; ib < 4; ++ib) xa[ib] = as_bf16x8(ldv4(as + wswz(arow + ib * 32, ch)));
-#pragma unroll
-    for (int jb = 0; jb < JB; ++jb) xb[jb] = as_bf16x8(ldv4(bs + wswz(brow + jb * 32, ch)));
-  };
-  // Load L of a step (L < 8: A block L, else B block L - 8) goes out after
-  // MFMA w of the step's load window: the last substep of the step two
-  // before (w 0..15, after that step's barrier has freed the stage), then
-  // the substeps of the step before (w 16..).  One load per LSP MFMAs; with
-  // LSP = 2 the A blocks fill the first part and the B blocks the first
-  // substep of the step before, so every load has at least two substeps to
-  // land before the barrier that waits for it (spreading them one per three
-  // MFMAs, into the second substep, measured slower on the wide shapes).
-  constexpr int LSP = 2;
-  static_assert(LSP >= 2 && LSP * (2 * NB - 1) < 48, "every load needs a slot before the third substep");
-  auto load_slot = [](int w) { return (w % LSP == 0 && w / LSP < 2 * NB) ? w / LSP : -1; };
-  // One substep: its 16 MFMAs (first: from zero accumulators), after MFMA
-  // q < 8 the fragment read q of the next substep (rd >= 0: substep rd of
-  // stage rpar), and the loads of window slots w0 + q (w0 >= 0) into stage
-  // lpar.  Scheduling walls keep this order.
-  auto substep = [&](const bf16x8_t (&xa)[4], const bf16x8_t (&xb)[JB], bool first, int rpar, int rd,
-                     bf16x8_t (&ya)[4], bf16x8_t (&yb)[JB], int w0, int lpar) {
-    const bf16_t* as = smem + rpar * WSTAGE;
-    const bf16_t* bs = as + TBM * WBK;
-    const int ch = rd * 2 + (lane >> 5);
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int ib = q >> 2, jb = q & 3;
-      acc[ib][jb] = mfma32(xa[ib], xb[jb], first ? f32x16_t{} : acc[ib][jb]);
-      if (rd >= 0 && q < 4) ya[q] = as_bf16x8(ldv4(as + wswz(arow + q * 32, ch)));
-      if (rd >= 0 && q >= 4 && q < 4 + JB) yb[q - 4] = as_bf16x8(ldv4(bs + wswz(brow + (q - 4) * 32, ch)));
-      const int L = w0 >= 0 ? load_slot(w0 + q) : -1;
-      if (L >= 0 && L < NB)
-        dma16_buf(Ar, aoff[L], a_kt * WBK * 2, smem + lpar * WSTAGE + (wid * NB + L) * 512);
-      if (L >= NB)
-        dma16_buf(Br, boff[L - NB], b_kt * WBK * 2, smem + lpar * WSTAGE + TBM * WBK + (wid * NB + L - NB) * 512);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  };
-  auto sync = [&]() {
-    __builtin_amdgcn_s_barrier();
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  };
-  // A and B of stream step 0 into stage 0, then the loads of step 1 that
-  // belong to the window's first part (A blocks) into stage 1
-  issue(0, 0);
-  next_a();
-  issue(0, 1);
-  next_b();
-  constexpr int NA0 = (16 + LSP - 1) / LSP;    // slots w < 16
-#pragma unroll
-  for (int L = 0; L < NA0; ++L)
-    dma16_buf(Ar, aoff[L], a_kt * WBK * 2, smem + WSTAGE + (wid * NB + L) * 512);
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(NA0) : "memory");   // step 0 landed
-  sync();
-  read_frags(0, 0, fa[0], fb[0]);
-  // Stream step s of the stage par = s & 1.  The loads of step s + 1 (into
-  // the other stage, free since the last barrier) finish in the first two
-  // substeps; after the barrier the stage of step s takes the first loads of
-  // step s + 2 while the last substep's MFMAs run.  The first substep of
-  // step s + 1 is read during those MFMAs, except after a tile's last step
-  // (last), where it is read after the epilogue so that it does not hold
-  // registers across it.
-  auto step = [&](int par, bool first, bool last) {
-    substep(fa[0], fb[0], first, par, 1, fa[1], fb[1], 16, par ^ 1);
-    substep(fa[1], fb[1], false, par, 2, fa[0], fb[0], 32, par ^ 1);
-    next_a();
-    next_b();
-    substep(fa[0], fb[0], false, par, 3, fa[1], fb[1], -1, 0);
-    // Every read of this stage has returned (their registers feed the MFMAs
-    // below) and this wave's loads of step s + 1 have landed.
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
-    sync();
-    substep(fa[1], fb[1], false, par ^ 1, last ? -1 : 0, fa[0], fb[0], 0, par);
-  };
-
-  // Epilogue.  Plain stores (SwiGLU, bf16 or fp32 output, and QKV tiles
-  // wholly in the q columns) go through a buffer view of the tile's rows that
-  // ends at row M, so the hardware drops the rows past M and the stores need
-  // no branches: a lane's offset is its own column plus a row step that is
-  // the same for the whole wave.
-  auto epilogue = [&](int m0, int n0) {
-    const int lrow = wm * 128 + (lane >> 5) * 4, lcol = lane & 31;
-    // QKV tile wholly in the K columns, head_dim 128 (a wave's 128 columns are
-    // one KV head) and rows in one sequence: its K-cache rows [pos][d] are a
-    // plain row-major block, stored like the q tiles
-    int ksq = -1;
-    if (EPI == EPI_QKV && n0 >= a.q_cols && n0 + TBN <= a.q_cols + a.n_kv * a.head_dim && a.head_dim == WCOL &&
-        !a.pos_dev && m0 / a.S_call == (min(m0 + TBM, a.M) - 1) / a.S_call)
-      ksq = m0 / a.S_call;
-    if (EPI == EPI_SWIGLU || EPI == EPI_STORE || EPI == EPI_F32 || n0 + TBN <= a.q_cols || ksq >= 0) {
-      constexpr int ES = EPI == EPI_F32 ? 4 : 2;      // output element bytes
-      int ldcb = (int)(ksq >= 0 ? a.head_dim : a.ldc) * ES;
-      // opaque here, so the 64 row offsets below are formed per tile rather
-      // than hoisted out of the tile loop, where they would hold registers
-      asm volatile("" : "+s"(ldcb));
-      const char* base = (const char*)a.C + (size_t)m0 * ldcb;
-      int lb = lrow * ldcb + (n0 + wn * (EPI == EPI_SWIGLU ? WCOL / 2 : WCOL) + lcol) * ES;
-      if (ksq >= 0) {
-        const int hk = (n0 - a.q_cols) / WCOL + wn;
-        base = (const char*)a.kcache +
-               (((size_t)ksq * a.n_kv + hk) * a.S_max + a.pos0 + (m0 - ksq * a.S_call)) * (size_t)ldcb;
-        lb = lrow * ldcb + lcol * ES;
-      }
-      const __amdgpu_buffer_rsrc_t Cr = buf_rsrc(base, (unsigned)(min(TBM, a.M - m0) * ldcb));
-#pragma unroll
-      for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int vo = lb + (ib * 32 + (r >> 2) * 8 + (r & 3)) * ldcb;
-          if (EPI == EPI_SWIGLU) {
-#pragma unroll
-            for (int jb = 0; jb < JB / 2; ++jb)
-              __builtin_amdgcn_raw_buffer_store_b16(f2bf(silu(acc[ib][jb][r]) * acc[ib][jb + JB / 2][r]), Cr,
-                                                    vo + jb * 32 * ES, 0, 0);
-          } else if (EPI == EPI_F32) {
-#pragma unroll
-            for (int jb = 0; jb < JB; ++jb)
-              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[ib][jb][r]), Cr, vo + jb * 32 * ES, 0, 0);
-          } else {
-#pragma unroll
-            for (int jb = 0; jb < JB; ++jb)
-              __builtin_amdgcn_raw_buffer_store_b16(f2bf(acc[ib][jb][r]), Cr, vo + jb * 32 * ES, 0, 0);
-          }
-        }
-    } else {
-      // QKV: a tile wholly in the V columns writes V^T [.., d][S_max]: a lane's
-      // four consecutive rows are four consecutive positions of one column, so
-      // they go out as one 8-byte store (same sequence and 4-aligned positions
-      // when S_call and pos0 are multiples of 4)
-      const int kvn = a.n_kv * a.head_dim;
-      const bool vtile = EPI == EPI_QKV && n0 >= a.q_cols + kvn && !a.pos_dev && a.S_call % 4 == 0 &&
-                         a.pos0 % 4 == 0 && (a.head_dim & 31) == 0;
-      if (vtile) {
-#pragma unroll
-        for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-          for (int jb = 0; jb < JB; ++jb) {
-            const int cc = n0 + wn * WCOL + jb * 32 + lcol - a.q_cols - kvn;
-            const int hk = cc / a.head_dim, dd = cc - hk * a.head_dim;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-              const int row = m0 + lrow + ib * 32 + g * 8;     // rows row .. row + 3
-              if (row + 3 < a.M) {
-                const int b = row / a.S_call, pos = a.pos0 + row - b * a.S_call;
-                bf16_t* dst = (bf16_t*)a.vcache + (((size_t)b * a.n_kv + hk) * a.head_dim + dd) * a.S_max + pos;
-                const uint32_t w0 = pack_bf16x2(acc[ib][jb][g * 4], acc[ib][jb][g * 4 + 1]);
-                const uint32_t w1 = pack_bf16x2(acc[ib][jb][g * 4 + 2], acc[ib][jb][g * 4 + 3]);
-                *(u32x2_t*)dst = u32x2_t{w0, w1};
-              } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                  if (row + e < a.M)
-                    epi_one<bf16_t, EPI, false>(a, row + e, n0 + wn * WCOL + jb * 32 + lcol, acc[ib][jb][g * 4 + e]);
-              }
-            }
-          }
-      } else {
-#pragma unroll
-        for (int ib = 0; ib < 4; ++ib)
-#pragma unroll
-          for (int jb = 0; jb < JB; ++jb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = m0 + lrow + ib * 32 + (r >> 2) * 8 + (r & 3);
-              const int col = n0 + wn * WCOL + jb * 32 + lcol;
-              if (row < a.M) epi_one<bf16_t, EPI, false>(a, row, col, acc[ib][jb][r]);
-            }
-      }
-    }
-  };
-
-  // Tiles of this workgroup; KT is even (the host checks), so every tile
-  // starts on stage 0 and two steps per trip keep the stage of each a
-  // constant.
-  for (int t = blockIdx.x; t < nblk; t += G) {
-    step(0, true, false);
-    for (int kt = 1; kt + 2 < KT; kt += 2) {
-      step(1, false, false);
-      step(0, false, false);
-    }
-    step(1, false, true);
-    int m0, n0;
-    tile_mn(t, m0, n0);
-    epilogue(m0, n0);
-    read_frags(0, 0, fa[0], fb[0]);
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
-}
-
-// ------------------------------------------------------------------ MFMA tile kernel, 16x16x32
-// The persistent 256x256 tile of gemm_w4 (same LDS layout, stages, tile order
-// and load cursor) on v_mfma_f32_16x16x32_bf16: a wave's 128x128 is 8 x 8
-// blocks of 16x16 (64 four-register accumulators) and a 64-deep step is two
-// 32-deep substeps of 64 MFMAs.  The step's one barrier sits between its
-// substeps.  Every fragment of the second substep is read during the first
-// (two register sets), so no wave reads the stage after the barrier; the
-// second substep reads the next step's first fragments from the other stage,
-// which landed before the barrier, and issues the 16 loads of step s + 2 into
-// this stage, one after every fourth MFMA.  The MFMAs are in-place
-// instructions on the accumulation registers: through the builtin the
-// compiler lets the registers of the 64 accumulators drift between loop
-// iterations and copies them every step.  The two kernels' outputs agree bit
-// for bit on every shape measured.  Against gemm_w4 on the Loop-9B shapes
-// (M = 32768) this one is 4-8% faster with 8 KB operand rows (K = 4096) and
-// 20-25% slower with 24 KB rows (the down projection), so the host picks by
-// row pitch.
 template <int EPI>
 __global__ __launch_bounds__(256, 1) void gemm_w16_kernel(GemmArgs a) {
   constexpr int NB = 8;                    // DMA instructions per wave per operand per step
@@ -642,21 +320,17 @@ __global__ __launch_bounds__(256, 1) void gemm_w16_kernel(GemmArgs a) {
   const int KT = a.K / WBK;
   // One load cursor (tile c_t, step c_kt), two steps ahead of the MFMAs.
   // Wave w loads rows 64 w .. 64 w + 63 of both operand tiles: block i is
-  // rows 64 w + 8 i + lane / 8, whose swizzle depends on i only through its
-  // parity, so a lane keeps two vector offsets per operand and a block adds
-  // a scalar one.  Rows past M lie past the end of the A view and read zeros.
+  // rows 64 w + 8 i + lane / 8.  A lane's whole byte offset of each block
+  // sits in a vector register and the scalar offset carries only the k step:
+  // with the block's row offset in the scalar operand instead, the kernel ran
+  // 25% slower on 24 KB rows (measured).  Rows past M lie past the end of the
+  // A view and read zeros.  Offsets fit in 32 bits unsigned (the host checks
+  // 256 lda and the B rows against 2^31 elements).
   int c_t = blockIdx.x, c_kt = 0;
   __amdgpu_buffer_rsrc_t Ar;
   const __amdgpu_buffer_rsrc_t Br = buf_rsrc(a.B, 0xFFFFFFF0u);
-  const int lda2 = (int)a.lda * 2, ldb2 = (int)a.ldb * 2;
-  int av[2], bv[2], a_s = 0, b_s = 0;
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int r = p * 8 + (lane >> 3);
-    const int cs = ((lane & 7) ^ ((r >> 1) & 7)) * 16;
-    av[p] = (lane >> 3) * lda2 + cs;
-    bv[p] = (lane >> 3) * ldb2 + cs;
-  }
+  const unsigned lda2 = (unsigned)a.lda * 2u, ldb2 = (unsigned)a.ldb * 2u;
+  unsigned aoff[NB], boff[NB];
   auto set_ab = [&](int t) __attribute__((always_inline)) {
     int m0, n0;
     tile_mn(t, m0, n0);
@@ -666,8 +340,13 @@ __global__ __launch_bounds__(256, 1) void gemm_w16_kernel(GemmArgs a) {
     int brow0;
     if (EPI == EPI_SWIGLU) brow0 = ((wid & 1) ? a.F : 0) + n0 + (wid >> 1) * 64;
     else brow0 = n0 + wid * 64;
-    a_s = wid * 64 * lda2;
-    b_s = brow0 * ldb2;
+#pragma unroll
+    for (int i = 0; i < NB; ++i) {
+      const int r = 8 * i + (lane >> 3);                          // row within the wave's 64
+      const unsigned cs = (unsigned)(((lane & 7) ^ ((r >> 1) & 7)) * 16);
+      aoff[i] = (unsigned)(wid * 64 + r) * lda2 + cs;
+      boff[i] = (unsigned)(brow0 + r) * ldb2 + cs;
+    }
   };
   auto next = [&]() __attribute__((always_inline)) {
     if (++c_kt == KT) {
@@ -684,11 +363,8 @@ __global__ __launch_bounds__(256, 1) void gemm_w16_kernel(GemmArgs a) {
   // load L of a step: L < 8 block L of A, else block L - 8 of B
   auto dma = [&](int L, int par) __attribute__((always_inline)) {
     const int i = L % NB;
-    if (L < NB)
-      dma16_buf(Ar, av[i & 1], a_s + i * 8 * lda2 + c_kt * WBK * 2, smem + par * WSTAGE + (wid * NB + i) * 512);
-    else
-      dma16_buf(Br, bv[i & 1], b_s + i * 8 * ldb2 + c_kt * WBK * 2,
-                smem + par * WSTAGE + TBM * WBK + (wid * NB + i) * 512);
+    if (L < NB) dma16_buf(Ar, (int)aoff[i], c_kt * WBK * 2, smem + par * WSTAGE + (wid * NB + i) * 512);
+    else dma16_buf(Br, (int)boff[i], c_kt * WBK * 2, smem + par * WSTAGE + TBM * WBK + (wid * NB + i) * 512);
   };
   f32x4_t acc[8][8];
   const int arow = wm * 128 + (lane & 15);
@@ -757,10 +433,16 @@ __global__ __launch_bounds__(256, 1) void gemm_w16_kernel(GemmArgs a) {
 
   // Epilogue.  acc[ib][jb][r]: row wm*128 + 16 ib + 4 (lane / 16) + r, column
   // wn*128 + 16 jb + lane % 16 (SwiGLU: gate block jb < 4 pairs with up block
-  // jb + 4, output column wn*64 + 16 jb + lane % 16).  Plain stores go through
-  // a buffer view of the tile's rows that ends at row M, as in gemm_w4.
+  // jb + 4, output column wn*64 + 16 jb + lane % 16).  Plain stores (SwiGLU,
+  // bf16 or fp32 output, and QKV tiles wholly in the q columns) go through a
+  // buffer view of the tile's rows that ends at row M, so the hardware drops
+  // the rows past M and the stores need no branches: a lane's offset is its
+  // own column plus a row step that is the same for the whole wave.
   auto epilogue = [&](int m0, int n0) __attribute__((always_inline)) {
     const int lrow = wm * 128 + (lane >> 4) * 4, lcol = lane & 15;
+    // QKV tile wholly in the K columns, head_dim 128 (a wave's 128 columns are
+    // one KV head) and rows in one sequence: its K-cache rows [pos][d] are a
+    // plain row-major block, stored like the q tiles
     int ksq = -1;
     if (EPI == EPI_QKV && n0 >= a.q_cols && n0 + TBN <= a.q_cols + a.n_kv * a.head_dim && a.head_dim == 128 &&
         !a.pos_dev && m0 / a.S_call == (min(m0 + TBM, a.M) - 1) / a.S_call)
@@ -768,6 +450,8 @@ __global__ __launch_bounds__(256, 1) void gemm_w16_kernel(GemmArgs a) {
     if (EPI == EPI_SWIGLU || EPI == EPI_STORE || EPI == EPI_F32 || n0 + TBN <= a.q_cols || ksq >= 0) {
       constexpr int ES = EPI == EPI_F32 ? 4 : 2;
       int ldcb = (int)(ksq >= 0 ? a.head_dim : a.ldc) * ES;
+      // opaque here, so the 32 row offsets below are formed per tile rather
+      // than hoisted out of the tile loop, where they would hold registers
       asm volatile("" : "+s"(ldcb));
       const char* base = (const char*)a.C + (size_t)m0 * ldcb;
       int lb = lrow * ldcb + (n0 + wn * (EPI == EPI_SWIGLU ? 64 : 128) + lcol) * ES;
@@ -799,8 +483,10 @@ __global__ __launch_bounds__(256, 1) void gemm_w16_kernel(GemmArgs a) {
           }
         }
     } else {
-      // QKV tile wholly in the V columns: a lane's four rows of a block are
-      // four consecutive positions of one V^T row, one 8-byte store (as in gemm_w4)
+      // QKV: a tile wholly in the V columns writes V^T [.., d][S_max]: a lane's
+      // four rows of a block are four consecutive positions of one column, so
+      // they go out as one 8-byte store (same sequence and 4-aligned positions
+      // when S_call and pos0 are multiples of 4); other tiles element by element
       const int kvn = a.n_kv * a.head_dim;
       const bool vtile = EPI == EPI_QKV && n0 >= a.q_cols + kvn && !a.pos_dev && a.S_call % 4 == 0 &&
                          a.pos0 % 4 == 0 && (a.head_dim & 31) == 0;
@@ -1141,28 +827,15 @@ static hipError_t launch_dma(const GemmArgs& a, int blocks, hipStream_t s) {
 }
 
 template <int EPI>
-static hipError_t launch_w4(const GemmArgs& a, int blocks, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_w4_kernel<EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       GEMM_W4_LDS);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  gemm_w4_kernel<EPI><<<blocks, 256, GEMM_W4_LDS, s>>>(a);
-  return hipGetLastError();
-}
-
-template <int EPI>
 static hipError_t launch_w16(const GemmArgs& a, int blocks, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute((const void*)gemm_w16_kernel<EPI>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       GEMM_W4_LDS);
+                                       GEMM_W16_LDS);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  gemm_w16_kernel<EPI><<<blocks, 256, GEMM_W4_LDS, s>>>(a);
+  gemm_w16_kernel<EPI><<<blocks, 256, GEMM_W16_LDS, s>>>(a);
   return hipGetLastError();
 }
 
@@ -1182,12 +855,9 @@ static hipError_t launch_bf16(const GemmArgs& a, hipStream_t s) {
   if (ncols % out_n) return hipErrorInvalidValue;
   const int blocks = ((a.M + TBM - 1) / TBM) * (ncols / out_n);
   if (a.K % (2 * WBK) == 0) {
-    // persistent: one workgroup per CU (a multiple of 8, for the XCD order);
-    // 16x16x32 MFMAs for operand rows up to 8 KB, 32x32x16 beyond (measured)
+    // persistent: one workgroup per CU (a multiple of 8, for the XCD order)
     const int cu = device_cu_count() & ~7;
-    const int g = (cu > 0 && blocks > cu) ? cu : blocks;
-    if (a.lda <= 4096 && a.ldb <= 4096) return launch_w16<EPI>(a, g, s);
-    return launch_w4<EPI>(a, g, s);
+    return launch_w16<EPI>(a, (cu > 0 && blocks > cu) ? cu : blocks, s);
   }
   return launch_dma<EPI, 4>(a, blocks, s);
 }

@@ -58,15 +58,15 @@ def _write(path, rows, fields):
 SEQ = ["__amd_rocclr_copyBuffer",
        "void lk::embed_kernel<unsigned short>(lk::EmbArgs)",
        "void lk::add_rmsnorm_kernel<unsigned short, 4>(lk::NormArgs)",
-       "void lk::gemm_w4_kernel<0>(lk::GemmArgs)",            # QKV of a linear layer
+       "void lk::gemm_w16_kernel<0>(lk::GemmArgs)",           # QKV of a linear layer
        "lk::lin_out_bf<4, 128>(lk::LinArgs)",
-       "void lk::gemm_w4_kernel<0>(lk::GemmArgs)",            # o
+       "void lk::gemm_w16_kernel<0>(lk::GemmArgs)",           # o
        "void lk::add_rmsnorm_kernel<unsigned short, 4>(lk::NormArgs)",
        "void lk::gemm_w16_kernel<3>(lk::GemmArgs)",           # gate/up
-       "void lk::gemm_w4_kernel<0>(lk::GemmArgs)",            # down
+       "void lk::gemm_w16_kernel<0>(lk::GemmArgs)",           # down
        "void lk::gemm_w16_kernel<2>(lk::GemmArgs)",           # QKV of a full layer
        "lk::attn_prefill_dma(lk::AttnArgs)",
-       "void lk::gemm_w4_kernel<0>(lk::GemmArgs)",            # o
+       "void lk::gemm_w16_kernel<0>(lk::GemmArgs)",           # o
        "void lk::gemm_skinny_rs_kernel<1, 1, 4>(lk::GemmArgs)"]
 
 
