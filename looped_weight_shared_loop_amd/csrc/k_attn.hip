@@ -7,9 +7,9 @@
 //   One workgroup of eight waves per (256 / G queries, KV head, sequence);
 //   the G heads of a group and 8 / G query blocks of 32 share every K / V^T
 //   tile, which global -> LDS DMA brings in three tiles ahead.  Scores are
-//   computed transposed, S^T = K Q^T (v_mfma_f32_16x16x32_bf16), which leaves
-//   each lane with a quarter of two query columns; the probabilities feed
-//   O^T = V^T P^T directly from registers.  Online softmax in fp32 (base 2).
+//   computed transposed, S^T = K Q^T (v_mfma_f32_32x32x16_bf16), which leaves
+//   each lane with one query column; the probabilities feed O^T = V^T P^T
+//   directly from registers.  Online softmax in fp32 (base 2).
 // * attn_prefill_d256 (bf16, d = 256, Hq / Hkv in 1, 2, 4): the same scheme
 //   with four waves (one per SIMD), two-stage K and V^T rings.
 // * attn_decode_mfma<D> (bf16, d = 128 or 256, up to 16 query columns =
@@ -35,24 +35,14 @@ constexpr int PD = 128;   // head dim
 // 32 * 8 / G queries of each of the G heads.  Tiles move global -> LDS with
 // global_load_lds_dwordx4 into a ring of four stages, three tiles ahead.
 // LDS layouts (16-byte units, swizzled against the 64 banks):
-//   K   [64 keys][128 d]:  unit c of row r at c ^ kf16(r)
+//   K   [64 keys][128 d]:  unit c of row r at c ^ (r & 15)
 //   V^T [128 d][64 keys]:  unit u (keys 8u .. 8u + 7) of row r at u ^ ((r >> 1) & 7)
-// Products on v_mfma_f32_16x16x32_bf16: a wave's scores S^T (64 keys x 32
-// queries) are 4 x 2 blocks of 16 keys x 16 queries (eight independent
-// accumulation chains of four 32-deep steps), and O^T (128 d x 32 queries)
-// 8 x 2 blocks.  MFMA row i of key block kb = 2 m + e reads key
-// 32 m + 8 (i / 4) + 4 e + i % 4: lane group g then holds keys
-// 32 m + 8 g + 4 e .. + 3 of block kb, so blocks 2 m and 2 m + 1 give the eight
-// consecutive keys 32 m + 8 g .. + 7 that the PV step of chunk m takes from
-// lane group g (the B operand of O^T = V^T P^T, straight from registers), and
-// its V^T fragment is one 16-byte read.  kf16 makes the 16 rows of one K
-// fragment read land on 16 different units.  Against the same kernel on
-// 32x32x16 MFMAs (two chains of eight steps per wave) this ran 4-8% faster
-// at S = 32,768.
+// The score MFMA takes its K rows in the order kappa(rho), which swaps bits 2
+// and 3 of the row index, so that a lane's probabilities for PV step mm are the
+// eight consecutive keys 16 mm + 8 h .. + 7: one 16-byte read of V^T.
 constexpr int AQ_STAGE = 2 * PK * PD;          // elements per stage (K + V^T, 32 KB)
 
-DEV int kf16(int r) { return (r & 3) | (((r >> 3) & 3) << 2); }
-DEV int kq16(int r, int c) { return r * PD + ((c ^ kf16(r)) << 3); }
+DEV int kq_sw(int r, int c) { return r * PD + ((c ^ (r & 15)) << 3); }
 DEV int vq_sw(int r, int u) { return r * PK + ((u ^ ((r >> 1) & 7)) << 3); }
 
 constexpr int AQ_NW = 8;                       // waves per workgroup
@@ -63,47 +53,47 @@ constexpr int AQ_LDS_MAX = 160 * 1024;          // the CU's LDS: with a paged ca
 __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
   constexpr int NW = AQ_NW, AHEAD = AQ_NS - 1;
   extern __shared__ __align__(16) bf16_t smem[];
-  constexpr int NB = 16 / NW;
-  const int G = a.Hq / a.Hkv;
-  const int QS = NW / G;
+  constexpr int NB = 16 / NW;                  // DMA blocks per wave per operand and tile
+  const int G = a.Hq / a.Hkv;                  // 1, 2, 4 or 8
+  const int QS = NW / G;                       // query sub-blocks per workgroup
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qblk = gridDim.x - 1 - blockIdx.x;
+  const int qb = gridDim.x - 1 - blockIdx.x;   // long rows first
   const int kvh = blockIdx.y, b = blockIdx.z;
   const int j = kvh * G + wid % G;
-  const int q0 = qblk * 32 * QS + (wid / G) * 32;
-  const int g = lane >> 4, li = lane & 15;
-  const int kv_end = a.pos0 + min((qblk + 1) * 32 * QS, a.S_call);
+  const int q0 = qb * 32 * QS + (wid / G) * 32; // this wave's first query
+  const int h = lane >> 5, col = lane & 31;
+  const int m = q0 + col;
+  const bool qvalid = m < a.S_call;
+  const int qpos = a.pos0 + m;
+  const int kv_end = a.pos0 + min((qb + 1) * 32 * QS, a.S_call);   // keys the workgroup needs
   const int ntiles = (kv_end + PK - 1) / PK;
-  const int wave_last = a.pos0 + min(q0 + 31, a.S_call - 1);
-  // this lane's queries: q0 + 16 qb + li, qb = 0, 1
-  int qpos[2];
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) qpos[qb] = a.pos0 + q0 + 16 * qb + li;
+  const int wave_last = a.pos0 + min(q0 + 31, a.S_call - 1);       // last key this wave can see
 
+  // paged cache: the page of every tile the workgroup reads, kept in LDS past the ring
   const bool paged = a.pages.table != nullptr;
   int* pglist = reinterpret_cast<int*>(smem + AQ_NS * AQ_STAGE);
   if (paged) {
     for (int t = tid; t < ntiles; t += 64 * NW) pglist[t] = kv_page(a.pages, b, t * PK);
     __syncthreads();
   }
-  // B operand of S^T = K Q^T: lane holds Q[q0 + 16 qb + li][32 ds + 8 g .. + 7]
-  bf16x8_t qf[2][4];
+
+  const bf16_t* Q = (const bf16_t*)a.q + (size_t)(b * a.S_call + min(m, a.S_call - 1)) * a.ldq + j * PD;
+  bf16x8_t qf[8];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int m = min(q0 + 16 * qb + li, a.S_call - 1);
-    const bf16_t* Q = (const bf16_t*)a.q + (size_t)(b * a.S_call + m) * a.ldq + j * PD;
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds) qf[qb][ds] = as_bf16x8(ldv4(Q + ds * 32 + g * 8));
-  }
+  for (int ds = 0; ds < 8; ++ds) qf[ds] = as_bf16x8(ldv4(Q + ds * 16 + h * 8));
+
   const bf16_t* Kg = (const bf16_t*)a.kcache + (paged ? 0 : ((size_t)(b * a.Hkv + kvh) * a.S_max) * PD);
   const bf16_t* Vg = (const bf16_t*)a.vcache + (paged ? 0 : ((size_t)(b * a.Hkv + kvh) * PD) * a.S_max);
   const int vstride = kv_vstride(a.pages, a.S_max);
+  // DMA: per tile 16 K blocks of 4 rows and 16 V^T blocks of 8 rows; wave w
+  // issues blocks 2w and 2w + 1 of each.  Lane l writes LDS bytes 16 l .. of
+  // the block, so it fetches the global unit that the swizzle puts there.
   int koff[NB], voff[NB], kl[NB], vl[NB];
 #pragma unroll
   for (int i = 0; i < NB; ++i) {
     const int blk = NB * wid + i;
     const int kr = 4 * blk + (lane >> 4), ks = lane & 15;
-    koff[i] = kr * PD + ((ks ^ kf16(kr)) << 3);
+    koff[i] = kr * PD + ((ks ^ (kr & 15)) << 3);
     kl[i] = blk * 512;
     const int vr = 8 * blk + (lane >> 3), vs = lane & 7;
     voff[i] = vr * vstride + ((vs ^ ((vr >> 1) & 7)) << 3);
@@ -134,147 +124,138 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
-  f32x4_t o[8][2];
+
+  f32x16_t o[4];
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) o[db][qb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float mrun[2] = {-INFINITY, -INFINITY}, lrun[2] = {0.f, 0.f};
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
+  float mrun = -INFINITY, lrun = 0.f;
   const float sc = LOG2E / sqrtf((float)PD);
-  // key of MFMA row li in block kb: 32 (kb / 2) + 4 (kb % 2) + krow0 (see above)
-  const int krow0 = 8 * (li >> 2) + (li & 3);
+  // MFMA row rho of the score block reads K row kappa(rho) (bits 2 and 3 swapped)
+  const int krow = (col & 0x13) | ((col & 4) << 1) | ((col & 8) >> 1);
+
   static_assert(AQ_NS == 4 && NW == 8 && NB == 2, "wait counts below");
   // Software pipeline: the score MFMAs of tile kt + 1 are issued before the
   // softmax and PV of tile kt, so the softmax VALU work runs while they execute.
   // The two waves of a SIMD reach the same phase together after each barrier;
   // a wave raises its issue priority for its score MFMAs (and keeps a middle
   // one through softmax and PV), so the SIMD's other wave fills the VALU
-  // slots rather than both waves alternating instruction by instruction.
-  f32x4_t sa[4][2], sb[4][2];                // scores of the current / next tile
-  // The K fragments of step ds + 1 are read while the eight MFMAs of step ds
-  // run (scheduling walls keep that order).
-  auto scores = [&](int kt, f32x4_t (&st)[4][2]) {
+  // slots rather than both waves alternating instruction by instruction
+  // (measured: 3% over equal priorities; results are unchanged).
+  f32x16_t sa[2], sb[2];                     // scores of the current / next tile
+  // The two 32-key blocks alternate, so consecutive MFMAs are independent;
+  // the K fragments of chunk ds + SA are read while the MFMAs of chunk ds
+  // run (scheduling walls keep that order), so the MFMAs do not wait on the
+  // LDS latency.
+  constexpr int SA = 2;
+  auto scores = [&](int kt, f32x16_t (&st)[2]) {
     const bf16_t* ks = smem + (kt % AQ_NS) * AQ_STAGE;
-    bf16x8_t kf[2][4];
+    bf16x8_t kf[SA + 1][2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) kf[0][kb] = as_bf16x8(ldv4(ks + kq16(32 * (kb >> 1) + 4 * (kb & 1) + krow0, g)));
+    for (int ds = 0; ds < SA; ++ds)
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds) {
-      if (ds + 1 < 4) {
+      for (int c = 0; c < 2; ++c) kf[ds][c] = as_bf16x8(ldv4(ks + kq_sw(c * 32 + krow, ds * 2 + h)));
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          kf[(ds + 1) & 1][kb] = as_bf16x8(ldv4(ks + kq16(32 * (kb >> 1) + 4 * (kb & 1) + krow0, 4 * (ds + 1) + g)));
+    for (int ds = 0; ds < 8; ++ds) {
+      if (ds + SA < 8) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          kf[(ds + SA) % (SA + 1)][c] = as_bf16x8(ldv4(ks + kq_sw(c * 32 + krow, (ds + SA) * 2 + h)));
       }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-          st[kb][qb] = mfma16(kf[ds & 1][kb], qf[qb][ds], ds == 0 ? f32x4_t{0.f, 0.f, 0.f, 0.f} : st[kb][qb]);
+      for (int c = 0; c < 2; ++c) st[c] = mfma32(kf[ds % (SA + 1)][c], qf[ds], ds == 0 ? f32x16_t{} : st[c]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto softmax_pv = [&](int kt, f32x4_t (&st)[4][2]) {
+  auto softmax_pv = [&](int kt, f32x16_t (&st)[2]) {
     const bf16_t* vs = smem + (kt % AQ_NS) * AQ_STAGE + PK * PD;
+    // st[c][r]: key kt*64 + 32c + 16(r/8) + 8h + r%8, query column `col`
     const bool diag = kt * PK + PK - 1 > a.pos0 + q0;
-    // st[kb][qb][r]: key kt*64 + 32 (kb / 2) + 8 g + 4 (kb % 2) + r, query q0 + 16 qb + li
     auto mask = [&]() {
       if (diag) {
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int key = kt * PK + 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + r;
-              if (!(key <= qpos[qb] && key < kv_end)) st[kb][qb][r] = -INFINITY;
-            }
+          for (int r = 0; r < 16; ++r) {
+            const int key = kt * PK + c * 32 + (r >> 3) * 16 + h * 8 + (r & 7);
+            if (!(key <= qpos && key < kv_end)) st[c][r] = -INFINITY;
+          }
       }
     };
     mask();
     // Probabilities against the running max, without the tile's own max:
     // bf16 keeps its relative precision at any magnitude, so p may grow far
-    // past 1 before anything is lost.  Only when a query's partial sum passes
-    // its bound (a lane holds a quarter of each query's keys, so 2^62 per lane
-    // keeps the four quarters within 2^64; 2^64 times 2^18 keys stays far
-    // inside float32), and at tile 0, where there is no running max yet, is
-    // the tile's max taken: from the scores recomputed out of the K tile, which
-    // is still in LDS.  Two partial sums per query, so that a wave alone on
-    // its SIMD's vector ALU is not held up by one dependent chain.
-    float ps[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
-    bool slow = kt == 0;
+    // past 1 before anything is lost.  Only when a lane's partial sum passes
+    // 2^64 (a score 64 past the running max in base-2 units; 2^64 times 2^18
+    // keys stays far inside float32), and at tile 0, where there is no running
+    // max yet, is the tile's max taken: from the scores recomputed out of the
+    // K tile, which is still in LDS.  Four independent partial sums (and maxima
+    // below), so that a wave alone on its SIMD's vector ALU is not held up by
+    // one dependent chain.
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
+    bool slow = kt == 0;                   // every wave starts at tile 0
     if (!slow) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = exp2_hw(fmaf(st[kb][qb][r], sc, -mrun[qb]));
-            st[kb][qb][r] = p;
-            ps[qb][r & 1] += p;
-          }
-      slow = __any(!(ps[0][0] + ps[0][1] <= 0x1p62f) || !(ps[1][0] + ps[1][1] <= 0x1p62f));
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_hw(fmaf(st[c][r], sc, -mrun));
+          st[c][r] = p;
+          ps[r & 3] += p;
+        }
+      slow = __any(!((ps[0] + ps[1]) + (ps[2] + ps[3]) <= 0x1p64f));
     }
-    float mnew[2] = {mrun[0], mrun[1]};
+    float mnew = mrun;
     if (slow) {
       if (kt != 0) {
         scores(kt, st);
         mask();
       }
+      float tm[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float t0 = -INFINITY, t1 = -INFINITY;
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          t0 = fmaxf(t0, fmaxf(st[kb][qb][0], st[kb][qb][1]));
-          t1 = fmaxf(t1, fmaxf(st[kb][qb][2], st[kb][qb][3]));
+        for (int r = 0; r < 16; ++r) tm[r & 3] = fmaxf(tm[r & 3], st[c][r]);
+      float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
+      tmax = x32_max(tmax) * sc;     // scaled (base-2) units
+      // the running max moves only when the tile's max exceeds it by more
+      // than 8, so O is rescaled rarely
+      mnew = tmax > mrun + 8.f ? tmax : mrun;
+      const float mfin = (mnew == -INFINITY) ? 0.f : mnew;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ps[i] = 0.f;
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = exp2_hw(fmaf(st[c][r], sc, -mfin));
+          st[c][r] = p;
+          ps[r & 3] += p;
         }
-        const float tmax = x32_max(x16_max(fmaxf(t0, t1))) * sc;   // the query's four lane groups
-        // the running max moves only when the tile's max exceeds it by more
-        // than 8, so O is rescaled rarely
-        mnew[qb] = tmax > mrun[qb] + 8.f ? tmax : mrun[qb];
-        const float mfin = (mnew[qb] == -INFINITY) ? 0.f : mnew[qb];
-        ps[qb][0] = ps[qb][1] = 0.f;
+      if (__any(mnew > mrun)) {
+        const float alpha = (mnew == -INFINITY) ? 1.f : exp2_hw(mrun - mnew);
+        lrun *= alpha;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = exp2_hw(fmaf(st[kb][qb][r], sc, -mfin));
-            st[kb][qb][r] = p;
-            ps[qb][r & 1] += p;
-          }
-      }
-      if (__any(mnew[0] > mrun[0] || mnew[1] > mrun[1])) {
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          const float alpha = (mnew[qb] == -INFINITY) ? 1.f : exp2_hw(mrun[qb] - mnew[qb]);
-          lrun[qb] *= alpha;
-#pragma unroll
-          for (int db = 0; db < 8; ++db) o[db][qb] *= alpha;
-        }
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       }
     }
+    const float psum = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    lrun += psum;
+    mrun = mnew;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      lrun[qb] += ps[qb][0] + ps[qb][1];
-      mrun[qb] = mnew[qb];
-    }
-    // PV: O^T[16 d][16 q] += V^T[16 d][32 keys] P^T[32 keys][16 q] for each
-    // 32-key chunk m; lane group g holds the probabilities of keys 32 m + 8 g .. + 7
+    for (int mm = 0; mm < 4; ++mm) {
+      const int c = mm >> 1, half = mm & 1;
+      uint32_t pw[4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      bf16x8_t pf[2];
+      for (int e = 0; e < 4; ++e) pw[e] = pack_bf16x2(st[c][half * 8 + 2 * e], st[c][half * 8 + 2 * e + 1]);
+      const bf16x8_t pf = as_bf16x8(u32x4_t{pw[0], pw[1], pw[2], pw[3]});
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-        pf[qb] = as_bf16x8(u32x4_t{pack_bf16x2(st[2 * m][qb][0], st[2 * m][qb][1]),
-                                   pack_bf16x2(st[2 * m][qb][2], st[2 * m][qb][3]),
-                                   pack_bf16x2(st[2 * m + 1][qb][0], st[2 * m + 1][qb][1]),
-                                   pack_bf16x2(st[2 * m + 1][qb][2], st[2 * m + 1][qb][3])});
-#pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const bf16x8_t vf = as_bf16x8(ldv4(vs + vq_sw(db * 16 + li, 4 * m + g)));
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb) o[db][qb] = mfma16(vf, pf[qb], o[db][qb]);
+      for (int db = 0; db < 4; ++db) {
+        const bf16x8_t vf = as_bf16x8(ldv4(vs + vq_sw(db * 32 + col, 2 * mm + h)));
+        o[db] = mfma32(vf, pf, o[db]);
       }
     }
   };
@@ -325,19 +306,19 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
     __builtin_amdgcn_s_setprio(0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load may still target LDS at exit
-  // o[db][qb][r]: O[q0 + 16 qb + li][16 db + 4 g + r]; the query's sum over its four lane groups
+  if (qvalid) {
+    const float ltot = x32_sum(lrun);
+    const float inv = 1.0f / ltot;
+    bf16_t* O = (bf16_t*)a.out + (size_t)(b * a.S_call + m) * a.ldo + j * PD;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int m = q0 + 16 * qb + li;
-    const float ltot = x32_sum(x16_sum(lrun[qb]));
-    if (m < a.S_call) {
-      const float inv = 1.0f / ltot;
-      bf16_t* O = (bf16_t*)a.out + (size_t)(b * a.S_call + m) * a.ldo + j * PD;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 8; ++db)
-        *(u32x2_t*)(O + db * 16 + 4 * g) = u32x2_t{pack_bf16x2(o[db][qb][0] * inv, o[db][qb][1] * inv),
-                                                   pack_bf16x2(o[db][qb][2] * inv, o[db][qb][3] * inv)};
-    }
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int d0 = db * 32 + g4 * 8 + h * 4;
+        const uint32_t w0 = pack_bf16x2(o[db][g4 * 4] * inv, o[db][g4 * 4 + 1] * inv);
+        const uint32_t w1 = pack_bf16x2(o[db][g4 * 4 + 2] * inv, o[db][g4 * 4 + 3] * inv);
+        *(u32x2_t*)(O + d0) = u32x2_t{w0, w1};
+      }
   }
 }
 
@@ -355,12 +336,9 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
 // LDS layouts (16-byte units, swizzled against the 64 banks):
 //   K   [64 keys][256 d]:  unit c (0..31) of row r at c ^ (r & 15)
 //   V^T [256 d][64 keys]:  as for d = 128
-// Scores are on v_mfma_f32_32x32x16_bf16: MFMA row rho of a 32-key block reads
-// K row kappa(rho), which swaps bits 2 and 3 of the row index, so that a
-// lane's probabilities for PV step mm are the eight consecutive keys
-// 16 mm + 8 h .. + 7 (one 16-byte read of V^T); the score contraction runs as
-// two 128-deep halves with their own accumulators (four independent chains
-// per tile), summed before the softmax.
+// Scores use the same key permutation as the d = 128 kernel, and the score
+// contraction runs as two 128-deep halves with their own accumulators (four
+// independent chains per tile), summed before the softmax.
 constexpr int PD2 = 256;
 constexpr int A2_NW = 4;
 constexpr int A2_KST = PK * PD2;                // elements per K stage (32 KB)
@@ -584,7 +562,7 @@ __global__ __launch_bounds__(64 * A2_NW, 1) void attn_prefill_d256(AttnArgs a) {
         for (int r = 0; r < 16; ++r) tm[r & 3] = fmaxf(tm[r & 3], cur[c][r]);
       float tmax = fmaxf(fmaxf(tm[0], tm[1]), fmaxf(tm[2], tm[3]));
       tmax = x32_max(tmax) * sc;
-      // lazy rescaling: the running max moves only past +8 (as at d = 128)
+      // lazy rescaling, as in the d = 128 kernel
       mnew = tmax > mrun + 8.f ? tmax : mrun;
       const float mfin = (mnew == -INFINITY) ? 0.f : mnew;
       float ps[4] = {0.f, 0.f, 0.f, 0.f};
