@@ -41,6 +41,9 @@ def _dev(x, dtype=torch.bfloat16):
     ("prefill_f32_rows1000", 1000, 768, 4096, 1, False),      # 256-row tiles, ragged last tile
     ("prefill_bf16", 700, 1024, 4096, 0, False),
     ("prefill_f32_k12288", 300, 512, 12288, 1, False),        # 24 KB operand rows (the down projection's)
+    ("prefill_f32_m65_k128", 65, 256, 128, 1, False),          # smallest tile-kernel shape: two k steps, one tile
+    ("prefill_bf16_tiles4", 300, 512, 4096, 0, False),        # 4 tiles: fewer workgroups than CUs, no XCD order
+    ("prefill_f32_tiles260", 3328, 5120, 256, 1, False),       # 260 tiles on 256 workgroups: some take two
     ("prefill_f32_k4064", 300, 512, 4064, 1, False),           # the 32-deep eight-wave kernel
     ("decode_f32_split", 32, 1024, 4096, 1, True),            # split-K partials summed by the reduce kernel
     ("decode_bf16_split_m7", 7, 2048, 12288, 0, True),
