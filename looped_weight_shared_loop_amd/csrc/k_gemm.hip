@@ -307,7 +307,7 @@ __global__ __launch_bounds__(256, 1) void gemm_w16_kernel(GemmArgs a) {
   const int num_n = (EPI == EPI_SWIGLU ? a.F : a.N) / out_n;
   const int nblk = num_m * num_n;
   const int G = gridDim.x;
-  const int GM = num_n <= 16 ? 4 : 8;
+  constexpr int GM = 4;                    // row tiles per group (measured in the whole prefill: 4 over 8 or 16)
   auto tile_mn = [&](int t, int& m0, int& n0) __attribute__((always_inline)) {
     int id = t;
     if (nblk % 8 == 0) id = (id & 7) * (nblk >> 3) + (id >> 3);
