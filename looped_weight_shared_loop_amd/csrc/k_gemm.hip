@@ -522,8 +522,14 @@ __global__ __launch_bounds__(256, 1) void gemm_w16_kernel(GemmArgs a) {
     int m0, n0;
     tile_mn(t, m0, n0);
     // the in-place MFMAs are opaque to the compiler's hazard checks: wait out
-    // their write latency before the accumulators are read
+    // their write latency before the accumulators are read.  The empty
+    // statements after the wait redefine every accumulator, so no read of one
+    // can be scheduled above the wait.
     asm volatile("s_nop 7\n s_nop 7\n s_nop 7" ::: "memory");
+#pragma unroll
+    for (int ib = 0; ib < 8; ++ib)
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb) asm volatile("" : "+a"(acc[ib][jb]));
     epilogue(m0, n0);
     read_frags(0, 0, fa[0], fb[0]);
   }
