@@ -547,7 +547,10 @@ constexpr int SK_THREADS = 256;
 
 // Tiles of 128 weight rows (SwiGLU: 64 output columns).  K is split in powers
 // of two (at most 16) while the grid has fewer than two workgroups per CU and
-// each workgroup keeps at least eight 64-wide k steps.
+// each workgroup keeps a multiple of four 64-wide k steps, at least sixteen, or
+// at least eight while the grid is still under one workgroup per CU (the
+// streaming rate of a workgroup falls with fewer steps: the first loads'
+// latency is paid once per workgroup).
 SkinnyPlan skinny_plan(int epi, int M, int N, int K, int F, int cu) {
   SkinnyPlan p{};
   auto tiles_of = [&](int rb) {
@@ -558,9 +561,13 @@ SkinnyPlan skinny_plan(int epi, int M, int N, int K, int F, int cu) {
   p.rb = 4;
   p.tiles = tiles_of(p.rb);
   p.ksplit = 1;
-  while (p.ksplit < 16 && (long)p.tiles * p.ksplit < 2L * cu && K % (p.ksplit * 2 * 4 * 64) == 0 &&
-         K / (p.ksplit * 2) >= 512)
-    p.ksplit *= 2;
+  for (;;) {
+    const int ks2 = 2 * p.ksplit;
+    if (p.ksplit >= 16 || (long)p.tiles * p.ksplit >= 2L * cu || K % (ks2 * 4 * 64)) break;
+    const int steps2 = K / (ks2 * 64);
+    if (!(steps2 >= 16 || (steps2 >= 8 && (long)p.tiles * p.ksplit < cu))) break;
+    p.ksplit = ks2;
+  }
   if (p.ksplit > 1) p.bytes = (size_t)p.tiles * p.ksplit * 32 * p.tb * 32 * p.rb * sizeof(float);
   return p;
 }
@@ -602,39 +609,51 @@ __global__ __launch_bounds__(256) void gemm_skinny_reduce(GemmArgs a) {
 // Decode shape with the token operand shared: a workgroup owns 128 weight rows
 // (SwiGLU: 64 gate and the 64 matching up rows) and a k range; each of its four
 // waves owns one 32-row MFMA block (SwiGLU: 16 gate rows, then their 16 up
-// rows) over the whole range, so all four read the same token operand, which
-// moves global -> LDS once per 64-k step (DMA into a ring of D + 1 stages).
-// The weight rows stream into registers D steps ahead, as in the kernel above,
-// with the same k order inside a step (lane half h: k + 32 h .. + 31; MFMA j
-// takes chunk j of both halves, the token fragment the same chunks).
-// Token rows [TOK][64 k] in LDS: 16-byte unit c of row t at c ^ ((t >> 1) & 7).
+// rows) over the whole range, so all four read the same token operand.
+// Both operands move global -> LDS by DMA in whole 128-byte lines, D steps of
+// 64 k ahead: the tokens into a ring shared by the workgroup, the weights into
+// a ring private to each wave (one DMA instruction moves 8 rows x 128 B).
+// Reading the weights straight into registers would have each load touch 64
+// lines (32 rows x two 16-byte pieces) and caps a workgroup near 20 GB/s.
+// k order inside a step: lane half h takes k + 32 h .. + 31; MFMA j takes
+// 16-byte chunk 4 h + j of both operands.  Rows [n][64 k] in LDS (tokens and
+// weights alike): chunk c of row n at slot c ^ ((n >> 1) & 7).
 // ksplit > 1: fp32 partial tiles [blockIdx][TOK][128] in the logical column
 // order (SwiGLU: gate columns, then up columns), read by gemm_skinny_reduce<.., 4, TB>
 // or a YPart consumer; ksplit == 1: the epilogue is applied directly.
 template <int EPI, int TB, int D>
 __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_rs_kernel(GemmArgs a) {
   constexpr int R = 128, TOK = 32 * TB, NS = D + 1;
-  constexpr int RING = NS * TOK * 64 * 2, STAGE_OUT = TOK * (R + 1) * 4;
+  constexpr int TSTAGE = TOK * 64, WSTAGE = 32 * 64;             // elements per stage
+  constexpr int RING = NS * (TSTAGE + 4 * WSTAGE) * 2, STAGE_OUT = TOK * (R + 1) * 4;
   __shared__ __align__(16) char lds[RING > STAGE_OUT ? RING : STAGE_OUT];
-  bf16_t* As = (bf16_t*)lds;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  bf16_t* As = (bf16_t*)lds;                                      // [NS][TOK][64]
+  bf16_t* Ws = As + NS * TSTAGE + wid * NS * WSTAGE;              // this wave's [NS][32][64]
   const int ks = a.ksplit;
   const int tile = blockIdx.x / ks, kpart = blockIdx.x - tile * ks;
   const int r = lane & 31, h = lane >> 5;
   const int Kw = a.K / ks, kb = kpart * Kw;
   const int nsteps = Kw / 64;
-  int n;
-  if (EPI == EPI_SWIGLU) {
-    const int j = tile * 64 + wid * 16 + (r & 15);                  // output column
-    n = j < a.F ? (r < 16 ? j : a.F + j) : 0;
-  } else {
-    n = tile * R + wid * 32 + r;
-    n = n < a.N ? n : 0;
+  // weight DMA i: rows 8 i .. 8 i + 7 of the wave's block; lane l writes slot
+  // l % 8 of row 8 i + l / 8, so it fetches the chunk the swizzle puts there
+  const bf16_t* Bg[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rl = 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ ((rl >> 1) & 7);
+    int n;
+    if (EPI == EPI_SWIGLU) {
+      const int j = tile * 64 + wid * 16 + (rl & 15);               // output column
+      n = j < a.F ? (rl < 16 ? j : a.F + j) : 0;
+    } else {
+      n = tile * R + wid * 32 + rl;
+      n = n < a.N ? n : 0;
+    }
+    Bg[i] = (const bf16_t*)a.B + (size_t)n * a.ldb + kb + c * 8;
   }
-  const bf16_t* Bp = (const bf16_t*)a.B + (size_t)n * a.ldb + kb + h * 32;
   // token DMA: per step TOK rows of 128 B = 4 TB blocks of 8 rows; wave w
-  // issues blocks w + 4 i.  Lane l of a block writes LDS unit l % 8 of row
-  // 8 blk + l / 8, so it fetches the global unit the swizzle puts there.
+  // issues blocks w + 4 i, with the same lane-to-slot rule
   const bf16_t* Ag[TB];
   int Al[TB];
 #pragma unroll
@@ -644,15 +663,20 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_rs_kernel(GemmArgs a) 
     Ag[i] = (const bf16_t*)a.A + (size_t)min(t, a.M - 1) * a.lda + kb + c * 8;
     Al[i] = blk * 512;
   }
-  u32x4_t bw[D][4];
-  auto issue = [&](int st, u32x4_t (&w)[4]) {      // weights and tokens of step st
+  auto dma = [](const bf16_t* g, bf16_t* l) {
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)g,
+                                     (void __attribute__((address_space(3)))*)l, 16, 0, 0);
+  };
+  auto issue = [&](int st) {      // weights and tokens of step st
+    // the stage refilled here was last read by this wave's fragment loads of
+    // step st - D - 1 ... st - 1; every such read has returned before the DMA
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    bf16_t* wd = Ws + (st % NS) * WSTAGE;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = ldv4(Bp + st * 64 + j * 8);
-    bf16_t* dst = As + (st % NS) * (TOK * 64);
+    for (int i = 0; i < 4; ++i) dma(Bg[i] + st * 64, wd + i * 512);
+    bf16_t* td = As + (st % NS) * TSTAGE;
 #pragma unroll
-    for (int i = 0; i < TB; ++i)
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(Ag[i] + st * 64),
-                                       (void __attribute__((address_space(3)))*)(dst + Al[i]), 16, 0, 0);
+    for (int i = 0; i < TB; ++i) dma(Ag[i] + st * 64, td + Al[i]);
   };
   f32x16_t acc[TB];
 #pragma unroll
@@ -663,8 +687,12 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_rs_kernel(GemmArgs a) 
     __builtin_amdgcn_s_barrier();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
   };
-  auto compute = [&](int st, const u32x4_t (&w)[4]) {
-    const bf16_t* src = As + (st % NS) * (TOK * 64);
+  auto compute = [&](int st) {
+    const bf16_t* ws = Ws + (st % NS) * WSTAGE;
+    const bf16_t* src = As + (st % NS) * TSTAGE;
+    u32x4_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = ldv4(ws + r * 64 + (((4 * h + j) ^ ((r >> 1) & 7)) << 3));
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int t = tb * 32 + r;
@@ -675,10 +703,10 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_rs_kernel(GemmArgs a) 
       }
     }
   };
-  // Group of step st = 4 weight loads then TB token DMAs.  Waiting until at
+  // Group of step st = 4 weight DMAs then TB token DMAs.  Waiting until at
   // most (D - 1 - q) groups are outstanding lands the oldest one; the barrier
   // then makes every wave's token rows of that step visible, and also orders
-  // all reads of step st - 1 before the DMA that refills its stage.
+  // all reads of step st - 1 before the DMA that refills its token stage.
   constexpr int GS = 4 + TB;
   static_assert(GS * (D - 1) <= 63, "vmcnt range");
   auto wait_groups = [&](auto q) {
@@ -686,26 +714,26 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_rs_kernel(GemmArgs a) 
     asm volatile("s_waitcnt vmcnt(%0)" :: "n"(N) : "memory");
   };
 #pragma unroll
-  for (int d = 0; d < D; ++d) issue(d, bw[d]);
+  for (int d = 0; d < D; ++d) issue(d);
   int st = 0;
   for (; st + D < nsteps; st += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       wait_groups(std::integral_constant<int, 0>{});
       sync();
-      compute(st + d, bw[d]);
-      issue(st + d + D, bw[d]);    // stage of step st + d - 1, read before the barrier above
+      compute(st + d);
+      issue(st + d + D);          // stages of step st + d - 1, read before the barrier above
     }
   }
   // last D steps: no more loads, the outstanding groups drain one by one
-  wait_groups(std::integral_constant<int, 0>{}); sync(); compute(st, bw[0]);
-  if constexpr (D > 1) { wait_groups(std::integral_constant<int, 1>{}); sync(); compute(st + 1, bw[1]); }
-  if constexpr (D > 2) { wait_groups(std::integral_constant<int, 2>{}); sync(); compute(st + 2, bw[2]); }
-  if constexpr (D > 3) { wait_groups(std::integral_constant<int, 3>{}); sync(); compute(st + 3, bw[3]); }
+  wait_groups(std::integral_constant<int, 0>{}); sync(); compute(st);
+  if constexpr (D > 1) { wait_groups(std::integral_constant<int, 1>{}); sync(); compute(st + 1); }
+  if constexpr (D > 2) { wait_groups(std::integral_constant<int, 2>{}); sync(); compute(st + 2); }
+  if constexpr (D > 3) { wait_groups(std::integral_constant<int, 3>{}); sync(); compute(st + 3); }
   static_assert(D <= 4, "drain above");
 
   // accumulators -> LDS in the logical column order, then coalesced output
-  sync();                              // every wave is done with the token ring
+  sync();                              // every wave is done with both rings
   float* out = (float*)lds;            // [TOK][R + 1]
 #pragma unroll
   for (int tb = 0; tb < TB; ++tb)
@@ -738,13 +766,19 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_rs_kernel(GemmArgs a) 
   }
 }
 
+// Four steps in flight (a 100-120 KB ring, one workgroup per CU) while the
+// grid has at most one workgroup per CU or each workgroup streams at least 32
+// steps; two (60-72 KB, two per CU) otherwise.
 template <int EPI, int TB>
 static hipError_t launch_skinny_rs(const GemmArgs& a, hipStream_t s) {
   const int tiles = (EPI == EPI_SWIGLU) ? (a.F + 63) / 64 : (a.N + 127) / 128;
   const int steps = a.K / (a.ksplit * 64);
-  if (steps % 4 == 0) gemm_skinny_rs_kernel<EPI, TB, 4><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
-  else if (steps % 2 == 0) gemm_skinny_rs_kernel<EPI, TB, 2><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
-  else gemm_skinny_rs_kernel<EPI, TB, 1><<<tiles * a.ksplit, SK_THREADS, 0, s>>>(a);
+  const int grid = tiles * a.ksplit;
+  static int cu = 0;
+  if (cu == 0) cu = device_cu_count() > 0 ? device_cu_count() : 256;
+  if (steps % 4 == 0 && (grid <= cu || steps >= 32)) gemm_skinny_rs_kernel<EPI, TB, 4><<<grid, SK_THREADS, 0, s>>>(a);
+  else if (steps % 2 == 0) gemm_skinny_rs_kernel<EPI, TB, 2><<<grid, SK_THREADS, 0, s>>>(a);
+  else gemm_skinny_rs_kernel<EPI, TB, 1><<<grid, SK_THREADS, 0, s>>>(a);
   if (a.ksplit > 1 && !(a.defer_reduce && EPI == EPI_STORE)) {
     const long outs = (long)a.M * tiles * (EPI == EPI_SWIGLU ? 64 : 128);
     gemm_skinny_reduce<EPI, 4, TB><<<(int)((outs + 255) / 256), 256, 0, s>>>(a);
