@@ -77,14 +77,13 @@ DEV void block_sum(float* v, float (*red)[16][12], int par) {
 // ------------------------------------------------------------------ add + RMSNorm
 // 8 channels c0 .. c0 + 7 (one GEMM tile) of token t of a sublayer output:
 // from y, or summed from the split-K partials and rounded like the stored y.
-template <typename T>
+template <typename T, int PG = 4>
 DEV void ld8_y(const T* y, const YPart& yp, int t, int C, int c0, float* v) {
   if (yp.part) {
     const int R = yp.rows, tile = c0 / R, j = c0 - tile * R;
 #pragma unroll
     for (int e = 0; e < 8; ++e) v[e] = 0.f;
-    // partial loads issued four at a time ahead of their sums (index order kept)
-    constexpr int PG = 4;
+    // partial loads issued PG at a time ahead of their sums (index order kept)
     for (int p0 = 0; p0 < yp.ks; p0 += PG) {
       float4 lo[PG], hi[PG];
 #pragma unroll
@@ -338,12 +337,20 @@ __global__ __launch_bounds__(64) void mhc_slice_a(MhcArgs a, float* __restrict__
   const int c0 = sl * MHC_SLICE + lane * 8;
   T* X = (T*)a.X;
   const T* y = (const T*)a.y;
+  // the slice of W first: no load of the slice waits for another's result
+  // or for the X' stores
+  float w0[8][8], w1[8][8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    ld8(a.w + (size_t)j * 2 * C + c0, w0[j]);
+    ld8(a.w + (size_t)j * 2 * C + C + c0, w1[j]);
+  }
   float x0[8], x1[8];
   if (a.mode == MHC_ENTER) {
     ld8((const T*)a.h + (size_t)t * C + c0, x0);
     if (y || a.yp.part) {
       float yv[8];
-      ld8_y(y, a.yp, t, C, c0, yv);
+      ld8_y<T, 16>(y, a.yp, t, C, c0, yv);
 #pragma unroll
       for (int e = 0; e < 8; ++e) x0[e] = round_to(x0[e] + yv[e], (T*)nullptr);
     }
@@ -353,7 +360,7 @@ __global__ __launch_bounds__(64) void mhc_slice_a(MhcArgs a, float* __restrict__
     float p[8], q[8], yv[8];
     ld8(X + ((size_t)t * 2) * C + c0, p);
     ld8(X + ((size_t)t * 2 + 1) * C + c0, q);
-    ld8_y(y, a.yp, t, C, c0, yv);
+    ld8_y<T, 16>(y, a.yp, t, C, c0, yv);
     const float* mi = a.maps_in + (size_t)t * 8;
     const float po0 = mi[2], po1 = mi[3], r00 = mi[4], r01 = mi[5], r10 = mi[6], r11 = mi[7];
 #pragma unroll
@@ -374,12 +381,9 @@ __global__ __launch_bounds__(64) void mhc_slice_a(MhcArgs a, float* __restrict__
   }
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    float w0[8], w1[8];
-    ld8(a.w + (size_t)j * 2 * C + c0, w0);
-    ld8(a.w + (size_t)j * 2 * C + C + c0, w1);
     float sj = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sj += w0[e] * x0[e] + w1[e] * x1[e];
+    for (int e = 0; e < 8; ++e) sj += w0[j][e] * x0[e] + w1[j][e] * x1[e];
     acc[3 + j] = sj;
   }
 #pragma unroll
@@ -397,6 +401,11 @@ __global__ __launch_bounds__(64) void mhc_slice_b(MhcArgs a, const float* __rest
   const int C = a.C, nsl = C / MHC_SLICE;
   const int sl = blockIdx.x, t = blockIdx.y, lane = threadIdx.x;
   const int c0 = sl * MHC_SLICE + lane * 8;
+  // the slice's X' and gain do not depend on the maps: in flight during them
+  float x0[8], x1[8], g[8], o[8];
+  ld8((const T*)a.X + ((size_t)t * 2) * C + c0, x0);
+  ld8((const T*)a.X + ((size_t)t * 2 + 1) * C + c0, x1);
+  ld8(a.gamma + c0, g);
   float acc[11];
 #pragma unroll
   for (int i = 0; i < 11; ++i) acc[i] = 0.f;
@@ -418,10 +427,6 @@ __global__ __launch_bounds__(64) void mhc_slice_b(MhcArgs a, const float* __rest
   const float p0 = m[0], p1 = m[1];
   const float ssin = p0 * p0 * acc[0] + 2.f * p0 * p1 * acc[2] + p1 * p1 * acc[1];
   const float invu = 1.0f / sqrtf(fmaxf(ssin, 0.f) / (float)C + a.eps);
-  float x0[8], x1[8], g[8], o[8];
-  ld8((const T*)a.X + ((size_t)t * 2) * C + c0, x0);
-  ld8((const T*)a.X + ((size_t)t * 2 + 1) * C + c0, x1);
-  ld8(a.gamma + c0, g);
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = g[e] * (p0 * x0[e] + p1 * x1[e]) * invu;
   st8((T*)a.u + (size_t)t * C + c0, o);
