@@ -48,6 +48,9 @@ def _dev(x, dtype=torch.bfloat16):
     ("decode_f32_split", 32, 1024, 4096, 1, True),            # split-K partials summed by the reduce kernel
     ("decode_bf16_split_m7", 7, 2048, 12288, 0, True),
     ("decode64_f32_split", 64, 1024, 4096, 1, True),          # two token blocks per weight read
+    ("decode_f32_split_768wg", 32, 24576, 4096, 1, True),     # more workgroups than CUs: two steps in flight
+    ("decode_f32_odd_steps", 5, 300, 192, 1, False),          # three k steps (one in flight), ragged last tile
+    ("decode_f32_512wg_long", 3, 65536, 4096, 1, False),      # no split, 64 steps per workgroup, four in flight
 ])
 def test_gemm_integer_inputs_exact(name, Mr, N, K, epi, split):
     need_gpu()
