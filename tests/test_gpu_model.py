@@ -281,6 +281,31 @@ def test_ragged_batch_prefill_rows_and_decode(dtype):
     assert st.lengths == [l + K for l in lens]
 
 
+def test_ragged_decode_lengths_far_apart_bf16():
+    """Ragged decode with lengths from 64 to 1,000: the decode attention then
+    splits every sequence's keys into up to 16 parts of one length (the shorter
+    sequences' later parts are empty) and merges the parts per row.  Every
+    logit row equals the oracle's forward over that sequence alone."""
+    ocfg = mini_bf16_config()
+    model, Wo = build_pair(ocfg)
+    lens, K = [700, 64, 1000, 333], 2
+    toks = tokens(4, max(lens) + K, ocfg.vocab, seed=61)
+    _say("ragged decode, lengths", lens)
+    ref = [oracle.forward(ocfg, Wo, toks[b:b + 1, :lens[b] + K], all_logits=True)[0] for b in range(4)]
+    st = model.new_state(4, max(lens) + K)
+    for b in range(4):
+        model.prefill(st, to_dev_tokens(toks[b:b + 1, :lens[b]]), seq0=b)
+    assert st.lengths == lens
+    for k in range(K):
+        step = np.array([toks[b, lens[b] + k] for b in range(4)], np.int32)
+        d = model.decode_step(st, to_dev_tokens(step)).cpu().numpy()
+        for b in range(4):
+            err = rel(d[b:b + 1], ref[b][lens[b] + k][None])
+            _say("step", k, "sequence", b, "position", lens[b] + k, "rel err", err)
+            assert err < BF16_TOL
+    assert st.lengths == [l + K for l in lens]
+
+
 def test_ragged_batch_subset_decode_and_rules():
     """A decode step over the first B sequences of a ragged state leaves the
     rest untouched; continued prefills need equal lengths; sequence ranges and
