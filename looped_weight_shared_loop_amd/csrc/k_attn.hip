@@ -57,8 +57,11 @@ __global__ __launch_bounds__(64 * AQ_NW, 1) void attn_prefill_dma(AttnArgs a) {
   const int G = a.Hq / a.Hkv;                  // 1, 2, 4 or 8
   const int QS = NW / G;                       // query sub-blocks per workgroup
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qb = gridDim.x - 1 - blockIdx.x;   // long rows first
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  // query blocks slowest in the dispatch order, longest first: every KV head's
+  // long rows start before any short ones, and with one sequence workgroup n
+  // serves KV head n % Hkv (the XCD a workgroup lands on follows n % 8)
+  const int qb = gridDim.z - 1 - blockIdx.z;
+  const int kvh = blockIdx.x, b = blockIdx.y;
   const int j = kvh * G + wid % G;
   const int q0 = qb * 32 * QS + (wid / G) * 32; // this wave's first query
   const int h = lane >> 5, col = lane & 31;
@@ -355,8 +358,11 @@ __global__ __launch_bounds__(64 * A2_NW, 1) void attn_prefill_d256(AttnArgs a) {
   const int G = a.Hq / a.Hkv;                  // 1, 2 or 4
   const int QS = NW / G;                       // query sub-blocks per workgroup
   const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int qb = gridDim.x - 1 - blockIdx.x;   // long rows first
-  const int kvh = blockIdx.y, b = blockIdx.z;
+  // query blocks slowest in the dispatch order, longest first: every KV head's
+  // long rows start before any short ones, and with one sequence workgroup n
+  // serves KV head n % Hkv (the XCD a workgroup lands on follows n % 8)
+  const int qb = gridDim.z - 1 - blockIdx.z;
+  const int kvh = blockIdx.x, b = blockIdx.y;
   const int j = kvh * G + wid % G;
   const int q0 = qb * 32 * QS + (wid / G) * 32;
   const int h = lane >> 5, col = lane & 31;
@@ -995,7 +1001,8 @@ hipError_t attn_prefill(const AttnArgs& a, hipStream_t s) {
       attr2 = true;
     }
     const int qpw = 32 * (A2_NW / G);
-    dim3 grid((a.S_call + qpw - 1) / qpw, a.Hkv, a.B);
+    if ((a.S_call + qpw - 1) / qpw > 65535) return hipErrorInvalidValue;
+    dim3 grid(a.Hkv, a.B, (a.S_call + qpw - 1) / qpw);
     attn_prefill_d256<<<grid, 64 * A2_NW, A2_LDS + pgl, s>>>(a);
     return hipGetLastError();
   }
@@ -1010,7 +1017,8 @@ hipError_t attn_prefill(const AttnArgs& a, hipStream_t s) {
     attr = true;
   }
   const int qpw = 32 * (AQ_NW / G);   // queries per workgroup
-  dim3 grid((a.S_call + qpw - 1) / qpw, a.Hkv, a.B);
+  if ((a.S_call + qpw - 1) / qpw > 65535) return hipErrorInvalidValue;
+  dim3 grid(a.Hkv, a.B, (a.S_call + qpw - 1) / qpw);
   attn_prefill_dma<<<grid, 64 * AQ_NW, lds, s>>>(a);
   return hipGetLastError();
 }
