@@ -668,8 +668,9 @@ __global__ __launch_bounds__(SK_THREADS) void gemm_skinny_rs_kernel(GemmArgs a) 
                                      (void __attribute__((address_space(3)))*)l, 16, 0, 0);
   };
   auto issue = [&](int st) {      // weights and tokens of step st
-    // the stage refilled here was last read by this wave's fragment loads of
-    // step st - D - 1 ... st - 1; every such read has returned before the DMA
+    // the weight stage refilled here last held step st - D - 1; the wait makes
+    // every LDS read this wave has issued (those of that step included) return
+    // before the DMA can overwrite it
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     bf16_t* wd = Ws + (st % NS) * WSTAGE;
 #pragma unroll
