@@ -120,7 +120,7 @@ struct loop_state {
 namespace {
 
 struct WsLayout {
-  size_t h, X, u, y, qkv, attn, inter, maps, lin, dec, wsplit, skinny, skinny_bytes, total;
+  size_t h, X, u, y, qkv, attn, inter, maps, lin, dec, dec_meta, wsplit, skinny, skinny_bytes, total;
 };
 
 WsLayout ws_layout(const loop_model* m, int batch, int max_tokens, int max_seq) {
@@ -145,7 +145,11 @@ WsLayout ws_layout(const loop_model* m, int batch, int max_tokens, int max_seq) 
   size_t dec_rows = 0;
   for (int b = 1; b <= batch; ++b)
     dec_rows = std::max(dec_rows, (size_t)b * c.n_heads * lk::decode_max_splits(b, c.n_kv_heads, S_max, m->cu));
+  // a ragged decode step (two sequences or more) splits stream-K: up to
+  // decode_sk_slots partials per row, and the padded key prefix
+  if (batch >= 2) dec_rows = std::max(dec_rows, (size_t)batch * c.n_heads * lk::decode_sk_slots(c.n_kv_heads, m->cu));
   w.dec = take(dec_rows * (c.head_dim + 2) * sizeof(float));
+  w.dec_meta = take((size_t)(batch + 1) * sizeof(int32_t));
   w.wsplit = take((size_t)lk::MHC_WSPLIT_ROWS * 2 * C * sizeof(uint16_t));
   // split-K scratch of the decode-shaped GEMMs (the largest plan of the five projections)
   size_t sk = 0;
@@ -546,6 +550,9 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, int
   // pos0: the (largest) first new position; ragged decode rows read their own
   const int pos0 = (decode || (flags & LOOP_CONTINUE)) ? len_max : 0;
   const bool ragged = decode && len_min != len_max;
+  // lengths far apart (the shortest under 7/8 of the longest): the bf16 decode
+  // attention splits the keys of all sequences stream-K
+  const bool ragged_sk = ragged && c.dtype == LOOP_BF16 && (long)(len_max - len_min) * 8 > len_max;
   if ((long)pos0 + S > st->max_seq)
     return lp_fail(LOOP_ERR_CAPACITY, "positions %d + %d exceed max_seq %d", pos0, S, st->max_seq);
   const int T = B * S;
@@ -576,6 +583,16 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, int
     int32_t* p = (int32_t*)(st->base + st->pos_off) + seq0;
     LAUNCH(lk::set_i32(p, st->seq_len.data() + seq0, B, s), "positions");
     pos_dev = p;
+  }
+  lk::StreamKPlan sk{};
+  const int32_t* sk_pref = nullptr;
+  if (ragged_sk) {
+    std::vector<int32_t> pref(B + 1, 0);
+    for (int b = 0; b < B; ++b) pref[b + 1] = pref[b] + (st->seq_len[seq0 + b] + S + 63) / 64 * 64;
+    sk = lk::decode_plan_sk(pref[B], Hkv, m->cu);
+    int32_t* p = (int32_t*)(ws + L.dec_meta);
+    LAUNCH(lk::set_i32(p, pref.data(), B + 1, s), "key prefix");
+    sk_pref = p;
   }
 
   // embedding
@@ -668,7 +685,10 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, int
       a.dt = dt; a.B = B; a.S_call = S; a.pos0 = pos0; a.S_max = st->S_max; a.Hq = Hq; a.Hkv = Hkv; a.d = d;
       a.pos_dev = pos_dev; a.pages = pages;
       a.q = qkv; a.ldq = qkv_rows; a.kcache = g.kcache; a.vcache = g.vcache; a.out = attn; a.ldo = Hq * d;
-      if (decode && dt == lk::DT_BF16) {
+      if (decode && sk_pref) {
+        a.part = dec_part;
+        LAUNCH(lk::attn_decode_sk(a, sk_pref, sk, s), "decode attention (stream-K)");
+      } else if (decode && dt == lk::DT_BF16) {
         const lk::DecodePlan dp = lk::decode_plan(B, Hkv, pos0 + S, m->cu);
         a.part = dec_part; a.split_len = dp.split_len; a.n_split = dp.n_split;
         LAUNCH(lk::attn_decode(a, s), "decode attention");

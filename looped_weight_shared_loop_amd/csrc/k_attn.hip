@@ -720,6 +720,22 @@ DecodePlan decode_plan(int B, int Hkv, int kv_len, int cu) {
   return p;
 }
 
+int decode_sk_slots(int Hkv, int cu) {
+  const int n = cu / (Hkv > 0 ? Hkv : 1);
+  return n > 1 ? n : 1;
+}
+
+// about one piece per CU: cu / Hkv pieces per KV head
+StreamKPlan decode_plan_sk(int total, int Hkv, int cu) {
+  StreamKPlan p{};
+  p.slots = decode_sk_slots(Hkv, cu);
+  int chunk = (total + p.slots - 1) / p.slots;
+  chunk = (chunk + 63) / 64 * 64;
+  p.chunk = chunk < 64 ? 64 : chunk;
+  p.n_wg = (total + p.chunk - 1) / p.chunk;
+  return p;
+}
+
 int decode_max_splits(int B, int Hkv, int S_max, int cu) {
   const int groups = B * Hkv > 0 ? B * Hkv : 1;
   const int want = (cu + groups - 1) / groups;
@@ -732,8 +748,12 @@ int decode_max_splits(int B, int Hkv, int S_max, int cu) {
 template <int D>
 constexpr int decode_waves() { return D == 128 ? DW : DW / 2; }
 
+// Keys [k_begin, min(k_end, kv_len)) of sequence b for KV head kvh: the
+// workgroup's waves take the rounds in turn and merge their (max, sum, O) in
+// LDS; wave 0 then writes the output (nslot == 1) or the fp32 partial in slot
+// `slot` of nslot per row.  Every wave of the workgroup calls this together.
 template <int D>
-__global__ __launch_bounds__(64 * decode_waves<D>()) void attn_decode_mfma(AttnArgs a) {
+DEV void decode_range(const AttnArgs& a, float* mrg, int b, int kvh, int k_begin, int k_end_cap, int slot, int nslot) {
   constexpr int NWV = decode_waves<D>();    // waves: four at d = 256, each with a whole SIMD's registers
   constexpr int RK = D == 128 ? 64 : 32;     // keys per round
   constexpr int NSB = RK / 16;               // S^T blocks of 16 keys
@@ -741,8 +761,6 @@ __global__ __launch_bounds__(64 * decode_waves<D>()) void attn_decode_mfma(AttnA
   constexpr int NQ = D / 32;                 // 32-deep q fragments
   constexpr int NO = D / 16;                 // O blocks of 16 rows
   constexpr int NCH = NQ > 4 ? 2 : 1;        // independent score chains per block
-  extern __shared__ float mrg[];             // [NWV / 2][16][D + 2]: o, max, sum per column
-  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
   const int ncol = G * a.S_call;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63, g = lane >> 4, c = lane & 15;
@@ -751,8 +769,7 @@ __global__ __launch_bounds__(64 * decode_waves<D>()) void attn_decode_mfma(AttnA
   const int pos0 = a.pos_dev ? min(max(a.pos_dev[b], 0), a.pos0) : a.pos0;   // this sequence's first new position
   const int kv_len = pos0 + a.S_call;              // keys [0, kv_len) exist
   const int lim = pos0 + tq + 1;                   // visible to this column
-  const int k_begin = s * a.split_len;
-  const int k_end = min(k_begin + a.split_len, kv_len);
+  const int k_end = min(k_end_cap, kv_len);
 
   const bf16_t* Q = (const bf16_t*)a.q + (size_t)(b * a.S_call + tq) * a.ldq + jq * D;
   bf16x8_t qf[NQ];
@@ -891,7 +908,7 @@ __global__ __launch_bounds__(64 * decode_waves<D>()) void attn_decode_mfma(AttnA
     __syncthreads();
   }
   if (wid != 0 || !cvalid) return;
-  if (a.n_split == 1) {
+  if (nslot == 1) {
     const float inv = 1.f / ltot;
     bf16_t* O = (bf16_t*)a.out + (size_t)(b * a.S_call + tq) * a.ldo + jq * D;
 #pragma unroll
@@ -902,38 +919,80 @@ __global__ __launch_bounds__(64 * decode_waves<D>()) void attn_decode_mfma(AttnA
     }
     return;
   }
-  float* P = a.part + ((((size_t)(b * a.S_call + tq) * a.Hq + jq) * a.n_split) + s) * (D + 2);
+  float* P = a.part + ((((size_t)(b * a.S_call + tq) * a.Hq + jq) * nslot) + slot) * (D + 2);
 #pragma unroll
   for (int db = 0; db < NO; ++db)
     *(float4*)(P + db * 16 + g * 4) = make_float4(o[db][0], o[db][1], o[db][2], o[db][3]);
   if (g == 0) { P[D] = mrun; P[D + 1] = ltot; }
 }
 
+// One workgroup of DW waves (d = 128; DW / 2 at d = 256) per (split, KV head,
+// sequence): split s covers keys [s split_len, (s + 1) split_len).
+template <int D>
+__global__ __launch_bounds__(64 * decode_waves<D>()) void attn_decode_mfma(AttnArgs a) {
+  extern __shared__ float mrg[];             // [NWV / 2][16][D + 2]: o, max, sum per column
+  const int s = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  decode_range<D>(a, mrg, b, kvh, s * a.split_len, s * a.split_len + a.split_len, s, a.n_split);
+}
+
+// Stream-K split of a ragged batch: the sequences' keys, each padded to a
+// multiple of 64, are laid end to end (sequence b at [pref[b], pref[b + 1]))
+// and cut into pieces of `chunk` keys (a multiple of 64), one workgroup per
+// (piece, KV head), so the work per workgroup is the same whatever the
+// lengths.  A piece that spans several sequences yields one partial per
+// sequence; sequence b's pieces are pref[b] / chunk .. (pref[b + 1] - 1) /
+// chunk, its partial slots 0, 1, ... in that order (a.n_split slots per row).
+template <int D>
+__global__ __launch_bounds__(64 * decode_waves<D>()) void attn_decode_sk(AttnArgs a, const int32_t* __restrict__ pref,
+                                                                         int chunk) {
+  extern __shared__ float mrg[];
+  const int p = blockIdx.x, kvh = blockIdx.y;
+  const int rs = p * chunk, re = min(rs + chunk, pref[a.B]);
+  int b = 0;
+  while (b < a.B - 1 && pref[b + 1] <= rs) ++b;
+  for (; b < a.B && pref[b] < re; ++b) {
+    const int base = pref[b];
+    decode_range<D>(a, mrg, b, kvh, max(rs, base) - base, min(re, pref[b + 1]) - base, p - base / chunk, a.n_split);
+  }
+}
+
 template <int D>
 constexpr size_t decode_lds() { return (size_t)(decode_waves<D>() / 2) * 16 * (D + 2) * sizeof(float); }
 
-// out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M); thread t takes the
-// dimensions t, t + 128, ... of one (token, head) row
+// out = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M) over the ns partials of
+// one (token, head) row (stored a.n_split apart); thread t takes the
+// dimensions t, t + 128, ...
 template <typename T>
-__global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
-  const int row = blockIdx.x;                   // (b * S_call + t) * Hq + j
+DEV void combine_row(const AttnArgs& a, int row, int ns) {
   const float* P = a.part + (size_t)row * a.n_split * (a.d + 2);
   float M = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, P[s * (a.d + 2) + a.d]);
+  for (int s = 0; s < ns; ++s) M = fmaxf(M, P[s * (a.d + 2) + a.d]);
   float L = 0.f;
-  for (int s = 0; s < a.n_split; ++s) {
+  for (int s = 0; s < ns; ++s) {
     const float ms = P[s * (a.d + 2) + a.d];
     L += P[s * (a.d + 2) + a.d + 1] * ((ms == -INFINITY) ? 0.f : exp2_hw(ms - M));
   }
   const int tok = row / a.Hq, j = row % a.Hq;
   for (int dd = threadIdx.x; dd < a.d; dd += 128) {
     float acc = 0.f;
-    for (int s = 0; s < a.n_split; ++s) {
+    for (int s = 0; s < ns; ++s) {
       const float ms = P[s * (a.d + 2) + a.d];
       acc += P[s * (a.d + 2) + dd] * ((ms == -INFINITY) ? 0.f : exp2_hw(ms - M));
     }
     st1((T*)a.out + (size_t)tok * a.ldo + j * a.d + dd, acc / L);
   }
+}
+
+template <typename T>
+__global__ __launch_bounds__(128) void attn_combine(AttnArgs a) {
+  combine_row<T>(a, blockIdx.x, a.n_split);     // row (b * S_call + t) * Hq + j
+}
+
+// rows of sequence b: its pieces of the stream-K split
+template <typename T>
+__global__ __launch_bounds__(128) void attn_combine_sk(AttnArgs a, const int32_t* __restrict__ pref, int chunk) {
+  const int row = blockIdx.x, b = row / (a.S_call * a.Hq);
+  combine_row<T>(a, row, (pref[b + 1] - 1) / chunk - pref[b] / chunk + 1);
 }
 
 // ------------------------------------------------------------------ fp32
@@ -1047,6 +1106,33 @@ hipError_t attn_decode(const AttnArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_split == 1) return e;
   attn_combine<bf16_t><<<a.B * a.S_call * a.Hq, 128, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t attn_decode_sk(const AttnArgs& a0, const int32_t* pref, const StreamKPlan& p, hipStream_t s) {
+  const int G = a0.Hkv > 0 ? a0.Hq / a0.Hkv : 0;
+  if (a0.dt != DT_BF16 || (a0.d != PD && a0.d != PD2) || !a0.pos_dev || !pref || a0.Hkv <= 0 || a0.Hq % a0.Hkv ||
+      G * a0.S_call > 16 || a0.S_max % 64 || p.chunk % 64 || p.n_wg < 1 || p.slots < p.n_wg)
+    return hipErrorInvalidValue;
+  if (a0.S_call <= 0 || a0.B <= 0) return hipSuccess;
+  AttnArgs a = a0;
+  a.n_split = p.slots;                 // partial slots per row
+  dim3 grid(p.n_wg, a.Hkv);
+  if (a.d == 128) {
+    attn_decode_sk<128><<<grid, 64 * decode_waves<128>(), decode_lds<128>(), s>>>(a, pref, p.chunk);
+  } else {
+    static bool attr = false;
+    if (!attr) {
+      hipError_t e = hipFuncSetAttribute((const void*)attn_decode_sk<256>,
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)decode_lds<256>());
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    attn_decode_sk<256><<<grid, 64 * decode_waves<256>(), decode_lds<256>(), s>>>(a, pref, p.chunk);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  attn_combine_sk<bf16_t><<<a.B * a.S_call * a.Hq, 128, 0, s>>>(a, pref, p.chunk);
   return hipGetLastError();
 }
 

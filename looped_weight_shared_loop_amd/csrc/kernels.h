@@ -150,6 +150,14 @@ hipError_t kv_scatter(int dt, const void* qkv, long ld, int q_cols, int B, int S
 // B * Hkv (sequence, KV head) pairs, each a multiple of 64 keys.
 struct DecodePlan { int split_len, n_split; };
 DecodePlan decode_plan(int B, int Hkv, int kv_len, int cu);
+// Stream-K split of a ragged decode batch (attn_decode_sk): the sequences'
+// keys, each padded to a multiple of 64, laid end to end (`total` keys) and
+// cut into n_wg pieces of `chunk` keys per KV head; `slots` partials per row.
+struct StreamKPlan { int chunk, n_wg, slots; };
+int decode_sk_slots(int Hkv, int cu);
+StreamKPlan decode_plan_sk(int total, int Hkv, int cu);
+// pref: int32 [B + 1] device copy of the padded key prefix; a.pos_dev set.
+hipError_t attn_decode_sk(const AttnArgs& a, const int32_t* pref, const StreamKPlan& p, hipStream_t s);
 // upper bound of n_split over kv_len <= S_max
 int decode_max_splits(int B, int Hkv, int S_max, int cu);
 

@@ -306,6 +306,33 @@ def test_ragged_decode_lengths_far_apart_bf16():
     assert st.lengths == [l + K for l in lens]
 
 
+def test_ragged_decode_stream_k_pieces_span_sequences_bf16():
+    """Stream-K decode attention where pieces cross sequence boundaries: four
+    KV heads leave 64 pieces per head on 256 CUs, so the 4,864 padded keys of
+    lengths 1,450 / 190 / 2,450 / 700 fall into pieces of 128 keys; the piece
+    at 1,408 holds the last 64 keys of sequence 0 and the first 64 of
+    sequence 1, the one at 4,096 the end of sequence 2 and the start of
+    sequence 3.  Every logit row equals the oracle's forward over that
+    sequence alone."""
+    ocfg = mini_bf16_config(n_kv_heads=4)
+    model, Wo = build_pair(ocfg)
+    lens, K = [1450, 190, 2450, 700], 2
+    toks = tokens(4, max(lens) + K, ocfg.vocab, seed=67)
+    _say("stream-K ragged decode, lengths", lens)
+    ref = [oracle.forward(ocfg, Wo, toks[b:b + 1, :lens[b] + K], all_logits=True)[0] for b in range(4)]
+    st = model.new_state(4, max(lens) + K)
+    for b in range(4):
+        model.prefill(st, to_dev_tokens(toks[b:b + 1, :lens[b]]), seq0=b)
+    for k in range(K):
+        step = np.array([toks[b, lens[b] + k] for b in range(4)], np.int32)
+        d = model.decode_step(st, to_dev_tokens(step)).cpu().numpy()
+        for b in range(4):
+            err = rel(d[b:b + 1], ref[b][lens[b] + k][None])
+            _say("step", k, "sequence", b, "position", lens[b] + k, "rel err", err)
+            assert err < BF16_TOL
+    assert st.lengths == [l + K for l in lens]
+
+
 def test_ragged_batch_subset_decode_and_rules():
     """A decode step over the first B sequences of a ragged state leaves the
     rest untouched; continued prefills need equal lengths; sequence ranges and
