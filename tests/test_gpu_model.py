@@ -281,12 +281,14 @@ def test_ragged_batch_prefill_rows_and_decode(dtype):
     assert st.lengths == [l + K for l in lens]
 
 
-def test_ragged_decode_lengths_far_apart_bf16():
-    """Ragged decode with lengths from 64 to 1,000: the decode attention then
-    splits every sequence's keys into up to 16 parts of one length (the shorter
-    sequences' later parts are empty) and merges the parts per row.  Every
-    logit row equals the oracle's forward over that sequence alone."""
-    ocfg = mini_bf16_config()
+@pytest.mark.parametrize("heads", [None, (4, 1, 256)], ids=["4x128", "4x256"])
+def test_ragged_decode_lengths_far_apart_bf16(heads):
+    """Ragged decode with lengths from 64 to 1,000 (heads of 128, or of 256
+    with one KV head): the decode attention splits the sequences' keys,
+    laid end to end, into pieces of one length per KV head and merges each
+    row's pieces.  Every logit row equals the oracle's forward over that
+    sequence alone."""
+    ocfg = mini_bf16_config(**(dict(n_heads=heads[0], n_kv_heads=heads[1], head_dim=heads[2]) if heads else {}))
     model, Wo = build_pair(ocfg)
     lens, K = [700, 64, 1000, 333], 2
     toks = tokens(4, max(lens) + K, ocfg.vocab, seed=61)
