@@ -94,6 +94,21 @@ int loop_op_attention_decode_ragged(int dtype, int B, int S, const int32_t* pos_
                                     int Hkv, int d, const void* q, long ldq, const void* kcache, const void* vcache,
                                     void* out, long ldo, void* scratch, size_t scratch_bytes, void* stream);
 
+/* Decode attention for a ragged batch split stream-K (the split the model's
+ * decode step uses when its sequences' lengths are far apart): the keys of
+ * sequence b are positions 0 .. starts[b] + S - 1 (starts: host int32 [B]);
+ * all sequences' keys, each padded to a multiple of 64, are laid end to end
+ * and cut into pieces of one length per KV head, one workgroup per piece, and
+ * a second kernel merges each (token, head) row's pieces.  bf16 only, d 128
+ * or 256, (Hq / Hkv) * S <= 16, starts[b] + S <= S_max, S_max % 64 == 0.
+ * `scratch` (caller-owned, loop_op_attention_decode_stream_k_bytes() bytes)
+ * takes the partials and device copies of the starts and of the key prefix,
+ * written on `stream` before the kernels run. */
+size_t loop_op_attention_decode_stream_k_bytes(int B, int S, int Hq, int Hkv, int d);
+int loop_op_attention_decode_stream_k(int dtype, int B, int S, const int32_t* starts, int S_max, int Hq, int Hkv,
+                                      int d, const void* q, long ldq, const void* kcache, const void* vcache,
+                                      void* out, long ldo, void* scratch, size_t scratch_bytes, void* stream);
+
 /* Causal elu+1 linear attention for S new positions of B sequences from
  * qkv [B*S][ld] (q at column 0, k at Hq*d, v at (Hq+Hkv)*d), continuing the
  * float32 state S [B][Hkv][d][d], z [B][Hkv][d] (ignored and treated as zero

@@ -102,6 +102,10 @@ SYMBOLS = {
     "loop_op_attention_decode_ragged": (c_int, [c_int, c_int, c_int, c_void_p, c_int, c_int, c_int, c_int, c_int,
                                                 c_void_p, ctypes.c_long, c_void_p, c_void_p, c_void_p, ctypes.c_long,
                                                 c_void_p, c_size_t, c_void_p]),
+    "loop_op_attention_decode_stream_k_bytes": (c_size_t, [c_int, c_int, c_int, c_int, c_int]),
+    "loop_op_attention_decode_stream_k": (c_int, [c_int, c_int, c_int, c_void_p, c_int, c_int, c_int, c_int,
+                                                  c_void_p, ctypes.c_long, c_void_p, c_void_p, c_void_p,
+                                                  ctypes.c_long, c_void_p, c_size_t, c_void_p]),
     "loop_op_linear_bytes": (c_size_t, [c_int, c_int, c_int, c_int]),
     "loop_op_linear": (c_int, [c_int, c_int, c_int, c_int, c_int, c_int, c_int, c_float, c_void_p, ctypes.c_long,
                                c_void_p, c_void_p, c_int, c_void_p, ctypes.c_long, c_void_p, c_size_t, c_void_p]),
@@ -314,6 +318,18 @@ def loop_op_attention_decode_ragged(dtype, B, S, pos, max_pos0, S_max, Hq, Hkv, 
     _check(lib().loop_op_attention_decode_ragged(dtype, B, S, _p(pos), max_pos0, S_max, Hq, Hkv, d, _p(q), ldq, _p(k),
                                                  _p(v), _p(out), ldo, _p(scratch), nbytes, _p(stream)),
            "loop_op_attention_decode_ragged")
+
+
+def loop_op_attention_decode_stream_k_bytes(B, S, Hq, Hkv, d) -> int:
+    return lib().loop_op_attention_decode_stream_k_bytes(B, S, Hq, Hkv, d)
+
+
+def loop_op_attention_decode_stream_k(dtype, B, S, starts, S_max, Hq, Hkv, d, q, ldq, k, v, out, ldo, scratch, nbytes,
+                                      stream) -> None:
+    """starts: host address of an int32 array of the B first new positions (e.g. numpy `a.ctypes.data`)."""
+    _check(lib().loop_op_attention_decode_stream_k(dtype, B, S, _p(starts), S_max, Hq, Hkv, d, _p(q), ldq, _p(k),
+                                                   _p(v), _p(out), ldo, _p(scratch), nbytes, _p(stream)),
+           "loop_op_attention_decode_stream_k")
 
 
 def loop_op_linear_bytes(B, S, Hkv, d) -> int:

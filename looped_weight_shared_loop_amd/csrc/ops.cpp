@@ -5,6 +5,7 @@
 #include "../../include/loop_ops.h"
 #include "abi_util.h"
 #include "kernels.h"
+#include <vector>
 
 namespace {
 
@@ -164,6 +165,44 @@ int loop_op_attention_decode_ragged(int dtype, int B, int S, const int32_t* pos_
   a.split_len = dp.split_len;
   a.n_split = dp.n_split;
   return launched(lk::attn_decode(a, (hipStream_t)stream), "decode attention");
+}
+
+size_t loop_op_attention_decode_stream_k_bytes(int B, int S, int Hq, int Hkv, int d) {
+  if (B <= 0 || S <= 0 || Hq <= 0 || Hkv <= 0 || d <= 0) return 0;
+  const size_t slots = (size_t)lk::decode_sk_slots(Hkv, lk::device_cu_count());
+  const size_t part = ((size_t)B * S * Hq * slots * (d + 2) * sizeof(float) + 255) / 256 * 256;
+  return part + (size_t)(2 * B + 1) * sizeof(int32_t);
+}
+
+int loop_op_attention_decode_stream_k(int dtype, int B, int S, const int32_t* starts, int S_max, int Hq, int Hkv,
+                                      int d, const void* q, long ldq, const void* kcache, const void* vcache,
+                                      void* out, long ldo, void* scratch, size_t scratch_bytes, void* stream) {
+  if (!starts) return lp_fail(LOOP_ERR_INVALID_ARG, "null starts");
+  if (dtype != LOOP_BF16) return lp_fail(LOOP_ERR_INVALID_ARG, "the stream-K split runs bf16 only");
+  int mx = 0;
+  for (int b = 0; b < B; ++b) {
+    if (starts[b] < 0) return lp_fail(LOOP_ERR_INVALID_ARG, "negative start");
+    mx = starts[b] > mx ? starts[b] : mx;
+  }
+  lk::AttnArgs a;
+  if (int r = attn_common(dtype, B, S, mx, S_max, Hq, Hkv, d, q, ldq, kcache, vcache, out, ldo, &a)) return r;
+  if ((d != 128 && d != 256) || (Hq / Hkv) * S > 16 || S_max % 64)
+    return lp_fail(LOOP_ERR_INVALID_ARG, "head size, group or S_max");
+  const size_t need = loop_op_attention_decode_stream_k_bytes(B, S, Hq, Hkv, d);
+  if (!scratch || scratch_bytes < need) return lp_fail(LOOP_ERR_WORKSPACE, "stream-K scratch too small");
+  if (lp_misaligned(scratch)) return lp_fail(LOOP_ERR_ALIGN, "misaligned scratch");
+  // scratch: partials, then the starts [B], then the padded key prefix [B + 1]
+  int32_t* pos_dev = (int32_t*)((char*)scratch + need - (size_t)(2 * B + 1) * sizeof(int32_t));
+  int32_t* pref_dev = pos_dev + B;
+  std::vector<int32_t> pref(B + 1, 0);
+  for (int b = 0; b < B; ++b) pref[b + 1] = pref[b] + (starts[b] + S + 63) / 64 * 64;
+  const lk::StreamKPlan plan = lk::decode_plan_sk(pref[B], Hkv, lk::device_cu_count());
+  hipStream_t s = (hipStream_t)stream;
+  if (int r = launched(lk::set_i32(pos_dev, starts, B, s), "starts")) return r;
+  if (int r = launched(lk::set_i32(pref_dev, pref.data(), B + 1, s), "key prefix")) return r;
+  a.pos_dev = pos_dev;
+  a.part = (float*)scratch;
+  return launched(lk::attn_decode_sk(a, pref_dev, plan, s), "decode attention (stream-K)");
 }
 
 size_t loop_op_linear_bytes(int B, int S, int Hkv, int d) {

@@ -145,3 +145,14 @@ def test_op_level_validation_without_device():
     nb = A.loop_op_attention_decode_bytes(32, 1, 32, 128, 32832)
     assert 32 * 32 * 130 * 4 <= nb <= 32 * 32 * (32832 // 64) * 130 * 4 and nb % (32 * 32 * 130 * 4) == 0
     assert A.loop_op_linear_bytes(1, 100, 8, 128) == 2 * 8 * (128 * 128 + 128) * 4
+    # stream-K decode attention: bf16 only, starts present and inside S_max; the scratch holds at
+    # least one partial slot per row plus the starts and the key prefix
+    import numpy as np
+    starts = np.array([100, 7000], np.int32)
+    args = (2, 1, starts.ctypes.data, 8192, 32, 8, 128, 16, 6144, 16, 16, 16, 4096, 16, 1 << 24, None)
+    assert lib.loop_op_attention_decode_stream_k(0, *args) == A.LOOP_ERR_INVALID_ARG          # float32
+    assert lib.loop_op_attention_decode_stream_k(1, 2, 1, None, *args[3:]) == A.LOOP_ERR_INVALID_ARG
+    bad = np.array([100, 9000], np.int32)                                                      # past S_max
+    assert lib.loop_op_attention_decode_stream_k(1, 2, 1, bad.ctypes.data, *args[3:]) == A.LOOP_ERR_INVALID_ARG
+    nbs = A.loop_op_attention_decode_stream_k_bytes(2, 1, 32, 8, 128)
+    assert nbs >= 2 * 32 * 130 * 4 + 5 * 4

@@ -293,6 +293,60 @@ def test_decode_attention_full_size_sampled(B, ctx, samples, layout):
 
 
 @pytest.mark.parametrize("pos,samples", [
+    # 32 sequences from 1 to 32,768 keys: pieces span several short sequences
+    ([32767, 0, 63, 64, 65, 1, 31000, 12345] + [(b * 7919) % 32768 for b in range(8, 32)],
+     [(0, 0), (1, 5), (2, 31), (3, 8), (4, 17), (5, 2), (6, 30), (9, 12), (31, 7)]),
+    ([5000, 3], [(0, 0), (0, 22), (1, 0), (1, 31)]),
+])
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+def test_decode_attention_stream_k_full_size_sampled(pos, samples, layout):
+    """The stream-K split of the ragged decode (sequences' keys laid end to end
+    and cut into equal pieces per KV head, partials merged per row) at the 9B
+    layouts: sequence b attends to its own pos[b] + 1 keys; slots hold NaN past
+    each sequence's keys."""
+    HQ, HKV, D, QKV = _lay(layout)
+    need_gpu()
+    from looped_weight_shared_loop_amd import _abi as A
+    from synth import device as sd
+    B, mx = len(pos), max(pos)
+    print(f"stream-K decode attention B={B} max start {mx}", flush=True)
+    Smax = (mx + 1 + 63) // 64 * 64
+    L = mx + 1
+    kc = torch.zeros(B, HKV, Smax, D, dtype=torch.bfloat16, device="cuda")
+    vt = torch.zeros(B, HKV, D, Smax, dtype=torch.bfloat16, device="cuda")
+    sd.fill_normal4(kc.data_ptr(), True, (B, HKV, L, D), (HKV * Smax * D, Smax * D, D, 1), SEED, 51, 1.0,
+                    stream=_stream())
+    sd.fill_normal4(vt.data_ptr(), True, (B, HKV, L, D), (HKV * D * Smax, D * Smax, 1, Smax), SEED, 52, 1.0,
+                    stream=_stream())
+    for b, p in enumerate(pos):
+        kc[b, :, p + 1:, :] = float("nan")
+        vt[b, :, :, p + 1:] = float("nan")
+    q = _dev_normal((B, QKV), 53)
+    starts = np.array(pos, np.int32)
+    out = torch.empty(B, HQ * D, dtype=torch.bfloat16, device="cuda")
+    nb = A.loop_op_attention_decode_stream_k_bytes(B, 1, HQ, HKV, D)
+    scr = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    A.loop_op_attention_decode_stream_k(A.LOOP_BF16, B, 1, starts.ctypes.data, Smax, HQ, HKV, D, q.data_ptr(), QKV,
+                                        kc.data_ptr(), vt.data_ptr(), out.data_ptr(), HQ * D, scr.data_ptr(), nb,
+                                        _stream())
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all().item()
+    for b, head in samples:
+        head %= HQ
+        kvh = head // (HQ // HKV)
+        n = pos[b] + 1
+        qr = synth.normal_bf16_as_f32(SEED, 53, (QKV,), start=b * QKV)[head * D:(head + 1) * D]
+        base = ((b * HKV + kvh) * L) * D
+        K = synth.normal_bf16_as_f32(SEED, 51, (n, D), start=base)
+        Vv = synth.normal_bf16_as_f32(SEED, 52, (n, D), start=base)
+        ref = M.full_attention(qr[None, None, None, :], K[None, :, None, :], Vv[None, :, None, :], pos[b])[0, 0, 0]
+        got = out[b, head * D:(head + 1) * D].float().cpu().numpy()
+        err = np.abs(got - ref).max() / np.abs(ref).max()
+        print("stream-K decode attn", b, pos[b], head, err, flush=True)
+        assert err < 2e-2
+
+
+@pytest.mark.parametrize("pos,samples", [
     # 32 sequences of the decode batch at lengths up to the 32K context: one split each
     ([32767, 0, 63, 64, 65, 1, 31000, 12345] + [(b * 7919) % 32768 for b in range(8, 32)],
      [(0, 0), (1, 5), (2, 31), (3, 8), (4, 17), (5, 2), (6, 30), (9, 12)]),
