@@ -51,6 +51,8 @@ def _dev(x, dtype=torch.bfloat16):
     ("decode_f32_split_768wg", 32, 24576, 4096, 1, True),     # more workgroups than CUs: two steps in flight
     ("decode_f32_odd_steps", 5, 300, 192, 1, False),          # three k steps (one in flight), ragged last tile
     ("decode_f32_512wg_long", 3, 65536, 4096, 1, False),      # no split, 64 steps per workgroup, four in flight
+    ("decode_f32_300wg", 9, 38400, 256, 1, False),            # no split, 300 workgroups of four k steps
+    ("decode_f32_split_600wg", 32, 19200, 4096, 1, True),     # 600 split-K workgroups: more than two per CU
 ])
 def test_gemm_integer_inputs_exact(name, Mr, N, K, epi, split):
     need_gpu()
