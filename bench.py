@@ -491,7 +491,8 @@ def cpu_baseline(seq=128):
                      "oracle_s": round(tiny_s, 3), "tokens_per_s": round(128 / tiny_s, 1)}}
 
 
-PROFILE_MODES = ("dominant", "prefill", "decode", "mhc", "group", "long", "prefill_d256", "decode_d256")
+PROFILE_MODES = ("dominant", "prefill", "decode", "mhc", "group", "long", "prefill_d256", "decode_d256",
+                 "decode_pipelined", "decode_ragged")
 
 
 def profile_run(L, torch, args):
@@ -504,6 +505,9 @@ def profile_run(L, torch, args):
       group     one 9B-width group looped twice, S=8,192 (after one warm-up call)
       long      one chunked prefill of 262,144 positions (8 chunks of 32,768)
       prefill_d256, decode_d256   prefill / decode with 16 query / 4 KV heads of 256
+      decode_pipelined  one pass-pipelined call, 2 cohorts x 32 sequences at 32,768 positions
+                (after the pipeline fill and 2 warm-up calls)
+      decode_ragged     one decode step of the ragged batch (B=32, lengths 16,384-32,483)
     Prints the step it is in before each one, so a profiled run shows progress."""
     src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda")     # 1 GiB
     dst = torch.empty_like(src)
@@ -527,6 +531,11 @@ def profile_run(L, torch, args):
             time_prefill(L, torch, model, args.seq, 1, 1)
         elif mode in ("decode", "decode_d256"):
             time_decode(L, torch, model, args.decode_batch, args.decode_ctx, 1, 2)
+        elif mode == "decode_pipelined":
+            time_decode_pipelined(L, torch, model, args.decode_batch, args.decode_ctx, 1, 2)
+        elif mode == "decode_ragged":
+            time_decode(L, torch, model, args.decode_batch, args.decode_ctx, 1, 2,
+                        lengths=ragged_lengths(args.decode_batch, args.decode_ctx))
         elif mode == "long":
             time_long_prefill(L, torch, model, args.long_seq, args.long_chunk)
     torch.cuda.synchronize()
