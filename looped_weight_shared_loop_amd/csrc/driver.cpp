@@ -121,6 +121,7 @@ namespace {
 
 struct WsLayout {
   size_t h, X, u, y, qkv, attn, inter, maps, lin, dec, dec_meta, wsplit, skinny, skinny_bytes, total;
+  int wsplit_sites;   // mHC sites whose W split a call keeps (0: one scratch split per site visit)
 };
 
 WsLayout ws_layout(const loop_model* m, int batch, int max_tokens, int max_seq) {
@@ -150,7 +151,11 @@ WsLayout ws_layout(const loop_model* m, int batch, int max_tokens, int max_seq) 
   if (batch >= 2) dec_rows = std::max(dec_rows, (size_t)batch * c.n_heads * lk::decode_sk_slots(c.n_kv_heads, m->cu));
   w.dec = take(dec_rows * (c.head_dim + 2) * sizeof(float));
   w.dec_meta = take((size_t)(batch + 1) * sizeof(int32_t));
-  w.wsplit = take((size_t)lk::MHC_WSPLIT_ROWS * 2 * C * sizeof(uint16_t));
+  // bf16 calls whose mHC sites run tiled keep each site's split of W (both
+  // passes read it), plus one scratch split for a W seen beyond that count
+  const bool site_splits = c.dtype == LOOP_BF16 && C % 512 == 0 && max_tokens >= lk::MHC_MFMA_MIN_T;
+  w.wsplit_sites = site_splits ? 2 * (c.loop_end - c.loop_start) : 0;
+  w.wsplit = take((size_t)(w.wsplit_sites + 1) * lk::MHC_WSPLIT_ROWS * 2 * C * sizeof(uint16_t));
   // split-K scratch of the decode-shaped GEMMs (the largest plan of the five projections)
   size_t sk = 0;
   if (c.dtype == LOOP_BF16 && max_tokens <= 64) {
@@ -613,6 +618,7 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, int
     return lk::add_rmsnorm(a, s);
   };
   int mp = 0;   // maps[mp] holds the maps of the current mHC site
+  std::vector<const float*> split_w;   // W of the sites whose split is in the workspace, by slot
   auto mhc = [&](int mode, const void* yin, const float* w, const float* b, const float* gamma) {
     lk::MhcArgs a{};
     a.dt = dt; a.mode = mode; a.T = T; a.C = C; a.iters = c.sinkhorn_iters; a.eps = c.rms_eps;
@@ -623,6 +629,14 @@ int forward(loop_model* m, loop_state* st, void* workspace, size_t ws_bytes, int
     a.maps_out = maps[mp ^ 1];
     a.w = w; a.b = b; a.gamma = gamma; a.u = u; a.grid = mhc_grid;
     a.wsplit = (lk::bf16_t*)(ws + L.wsplit);
+    if (L.wsplit_sites > 0 && w && mode != lk::MHC_EXIT) {
+      // the second pass (and a site met again) reuses the split made at the first visit
+      size_t k = 0;
+      while (k < split_w.size() && split_w[k] != w) ++k;
+      if (k < split_w.size()) a.wsplit_ready = 1;
+      else if (k < (size_t)L.wsplit_sites) split_w.push_back(w);
+      a.wsplit += k * (size_t)lk::MHC_WSPLIT_ROWS * 2 * C;
+    }
     hipError_t e = lk::mhc(a, s);
     if (mode != lk::MHC_EXIT) mp ^= 1;
     return e;

@@ -633,8 +633,6 @@ __global__ __launch_bounds__(512) void mhc_mfma_kernel(MhcArgs a, const bf16_t* 
   }
 }
 
-constexpr int MHC_MFMA_MIN_T = 256;
-
 hipError_t mhc(const MhcArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   if (a.C % 8 || a.C / 8 > 512) return hipErrorInvalidValue;
@@ -646,10 +644,12 @@ hipError_t mhc(const MhcArgs& a, hipStream_t s) {
   // wave's channels and count them twice)
   if (a.dt == DT_BF16 && a.mode != MHC_EXIT && a.C % 512 == 0 && a.wsplit && a.T >= MHC_MFMA_MIN_T) {
     if (a.yp.part) return hipErrorInvalidValue;   // the tiled path reads y itself
-    const int n = 8 * 2 * a.C;
-    mhc_split_w<<<(n + 255) / 256, 256, 0, s>>>(a.w, a.wsplit, n);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (!a.wsplit_ready) {
+      const int n = 8 * 2 * a.C;
+      mhc_split_w<<<(n + 255) / 256, 256, 0, s>>>(a.w, a.wsplit, n);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
     const int ntiles = (a.T + 15) / 16;
     // Persistent grid: exactly the resident workgroups (a second wave of
     // workgroups would start only after the first finished its tiles), then

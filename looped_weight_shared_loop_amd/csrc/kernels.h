@@ -46,6 +46,7 @@ hipError_t add_rmsnorm(const NormArgs& a, hipStream_t s);
 enum MhcMode { MHC_ENTER = 0, MHC_MID = 1, MHC_EXIT = 2 };
 // rows of the bf16 split of an mHC projection W [8][2C]: high, middle and low parts
 constexpr int MHC_WSPLIT_ROWS = 24;
+constexpr int MHC_MFMA_MIN_T = 256;   // bf16 sites of at least this many tokens run tiled on MFMA
 
 struct MhcArgs {
   int dt, mode, T, C, iters;
@@ -62,6 +63,7 @@ struct MhcArgs {
   void* u;               // [T][C] normed input of the next sublayer
   int grid;              // persistent grid size (0: one block per token)
   bf16_t* wsplit;        // bf16 ENTER/MID: scratch of MHC_WSPLIT_ROWS x 2C bf16 for [W_hi; W_mid; W_lo]
+  int wsplit_ready;      // the tiled path: wsplit already holds this W's split (no split launch)
 };
 hipError_t mhc(const MhcArgs& a, hipStream_t s);
 
