@@ -434,7 +434,8 @@ __global__ __launch_bounds__(64) void mhc_slice_b(MhcArgs a, const float* __rest
 
 // ------------------------------------------------------------------ mHC, MFMA (bf16)
 // For bf16 streams the 8 projections l = W vec(X') run on the matrix cores:
-// W (float32 [8][2C]) is split once per call into W_hi = bf16(W),
+// W (float32 [8][2C]) is split (once per call, or kept by the caller across
+// calls with the same W: wsplit_ready) into W_hi = bf16(W),
 // W_mid = bf16(W - W_hi) and W_lo = bf16(W - W_hi - W_mid), 24 bf16 rows
 // that carry W to within 2^-27 of its value (finer than float32's own
 // rounding): X' is bf16, so each product is exact and the projection equals
