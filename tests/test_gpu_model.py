@@ -447,6 +447,36 @@ def test_mini_bf16_deterministic_and_looped_equals_unrolled():
     assert torch.equal(model.decode_step(st, nt), un.decode_step(stu, nt))
 
 
+def test_mini_bf16_site_splits_reused_across_passes():
+    """At 2 x 160 positions per call the mHC sites run tiled on the matrix
+    cores.  The looped model then splits each site's W once per call and its
+    second pass reuses that split.  The unrolled model gets copies of the
+    repeated layers' weights at other addresses, so none of its splits are
+    reused.  Both must give bitwise-equal logits, over two calls (the second
+    continues the first)."""
+    L = need_gpu()
+    ocfg = mini_bf16_config()
+    gcfg = L.ModelConfig(**vars_of(ocfg))
+    W = L.random_weights(gcfg, 0)
+    model = L.LoopModel(gcfg, W)
+    ucfg = L.ModelConfig(**{**vars_of(ocfg), "n_layers": 12, "loop_start": 2, "loop_end": 10, "n_passes": 1})
+    Wu = {"embed": W["embed"], "head": W["head"], "final_norm": W["final_norm"]}
+    for j in range(12):
+        src = j if j < 2 else (2 + (j - 2) % 4 if j < 10 else j - 4)
+        for k, v in W.items():
+            if k.startswith(f"layers.{src}."):
+                Wu[f"layers.{j}." + k.split(".", 2)[2]] = v.clone() if 6 <= j < 10 else v
+    un = L.LoopModel(ucfg, Wu)
+    toks = to_dev_tokens(tokens(2, 320, ocfg.vocab, seed=11))
+    st, stu = model.new_state(2, 320), un.new_state(2, 320)
+    for i, sl in enumerate((slice(0, 160), slice(160, 320))):
+        part = toks[:, sl].contiguous()
+        a = model.prefill(st, part, all_logits=True, cont=i > 0)
+        c = un.prefill(stu, part, all_logits=True, cont=i > 0)
+        print(f"call {i}: max |looped - unrolled| {(a - c).abs().max().item():.3g}", flush=True)
+        assert torch.equal(a, c)
+
+
 def vars_of(ocfg):
     return dict(vocab=ocfg.vocab, hidden=ocfg.hidden, ffn=ocfg.ffn, n_heads=ocfg.n_heads,
                 n_kv_heads=ocfg.n_kv_heads, head_dim=ocfg.head_dim, n_layers=ocfg.n_layers,
